@@ -1,0 +1,282 @@
+#!/usr/bin/env python3
+"""Benchmark of the fp32 matrix product and implicit-GEMM convolution on one MI355X.
+
+A step is one fast-mode 4096^3 matrix product (N(0,1) inputs with 0.1% special
+values at seeded positions) through the C ABI, inputs resident in HBM.  After
+W untimed steps, K steps are timed back to back between HIP events on the
+stream the kernels run on; the JSON line reports GFLOP/s, the roofline
+fraction of the dominant kernel, and the CPU oracle timed on a bounded
+sample.  The other workloads (exact mode at 4096^3, 256^3, the ragged,
+prefill and skinny products, the ResNet-50 convolution chain at batch 1 and
+8, the grouped/dilated and 1-D convolutions) are timed in both modes under
+"extra": 2 warm-up calls, calls repeated for at least 80 ms between events,
+the median of 3 such repetitions.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fp32 GFLOP/s (exact & fast) at 4096^3 + ResNet-50 conv chain ms; % fp32 peak"
+PEAK_FP32_TFLOPS = 157.3        # MI355X dense fp32 (matrix and packed vector)
+EXACT_CEILING_TFLOPS = 78.65    # one separately rounded VALU add per term
+HBM_GBPS = 8000.0
+PAGES_RESNET_CPU_MS = {"16 threads": 12.3, "32 threads": 11.1}  # 16-core Zen 4, fast mode
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default=None,
+                    help="time one workload only (for profiling): gemm4096_fast, gemm4096_exact, "
+                         "resnet_b1, resnet_b8, skinny, prefill, grouped, conv1d, ragged, gemm256")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+class Timer:
+    """HIP events on the current torch stream (the stream libog launches on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def time_calls(self, fn, calls: int) -> float:
+        t = self.torch
+        s = t.cuda.current_stream()
+        e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        t.cuda.synchronize()
+        e0.record(s)
+        for _ in range(calls):
+            fn()
+        e1.record(s)
+        t.cuda.synchronize()
+        return e0.elapsed_time(e1) / calls  # ms per call
+
+    def spike(self, fn, min_ms: float = 80.0, reps: int = 3) -> float:
+        """2 warm-ups; calls repeated for >= min_ms; median of `reps` means (ms per call)."""
+        fn()
+        fn()
+        one = self.time_calls(fn, 1)
+        calls = max(1, int(min_ms / max(one, 1e-3)) + 1)
+        return statistics.median(self.time_calls(fn, calls) for _ in range(reps))
+
+
+def dev_strided(torch, case_A, ld):
+    rows, cols = case_A.shape
+    buf = torch.empty((rows, ld), dtype=torch.float32, device="cuda")
+    buf[:, :cols] = torch.from_numpy(case_A).cuda()
+    return buf[:, :cols]
+
+
+def gemm_workload(torch, og, case):
+    A = dev_strided(torch, case.A, case.lda)
+    B = dev_strided(torch, case.B, case.ldb)
+    C = torch.empty((case.m, case.ldc), dtype=torch.float32, device="cuda")[:, :case.n]
+    return A, B, C
+
+
+def conv_chain(torch, og, synth, batch):
+    layers = []
+    for i, s in enumerate(synth.resnet50_convs(batch)):
+        x, w = synth.conv_inputs(s, synth.seed_for(4, i + (0 if batch == 1 else 100)))
+        dx, dw = torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda()
+        y = og.conv2d(dx, dw, stride=s.stride, pad=s.pad, dil=s.dil, groups=s.groups)
+        layers.append((s, dx, dw, y))
+    return layers
+
+
+def conv_macs(og, s):
+    oh = og.conv2d_out_size(s.H, s.KH, s.stride[0], s.pad[0], s.pad[2], s.dil[0])
+    ow = og.conv2d_out_size(s.W, s.KW, s.stride[1], s.pad[1], s.pad[3], s.dil[1])
+    return s.N * s.Cout * oh * ow * (s.Cin // s.groups) * s.KH * s.KW
+
+
+def run_chain(og, layers, mode):
+    for s, dx, dw, y in layers:
+        og.conv2d(dx, dw, stride=s.stride, pad=s.pad, dil=s.dil, groups=s.groups, mode=mode,
+                  out=y)
+
+
+def extras(torch, og, synth, timer, only=None):
+    out = {}
+
+    def want(name):
+        return only is None or only == name
+
+    def gemm_entry(case, modes=("fast", "exact"), bytes_moved=None):
+        A, B, C = gemm_workload(torch, og, case)
+        ent = {"m": case.m, "n": case.n, "k": case.k, "lda": case.lda, "ldb": case.ldb,
+               "ldc": case.ldc}
+        for mode in modes:
+            ms = timer.spike(lambda: og.gemm(A, B, mode, out=C))
+            ent[mode] = {"us": round(ms * 1e3, 2),
+                         "gflops": round(case.flops / (ms * 1e-3) / 1e9, 1),
+                         "frac_peak": round(case.flops / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4)}
+            if mode == "exact":
+                ent[mode]["frac_exact_ceiling"] = round(
+                    case.flops / (ms * 1e-3) / 1e12 / EXACT_CEILING_TFLOPS, 4)
+            if bytes_moved:
+                ent[mode]["hbm_gbps_hot"] = round(bytes_moved / (ms * 1e-3) / 1e9, 1)
+        del A, B, C
+        return ent
+
+    if want("gemm4096_exact") and only is not None:
+        out["gemm_4096"] = gemm_entry(synth.gemm_4096(), modes=("exact",))
+        return out
+    if want("gemm256"):
+        log("extra: gemm 256^3")
+        out["gemm_256"] = gemm_entry(synth.gemm_square256())
+    if want("ragged"):
+        log("extra: ragged")
+        out["gemm_1000x777x1531_ld13"] = gemm_entry(synth.gemm_ragged())
+    if want("prefill"):
+        log("extra: prefill")
+        out["gemm_prefill_512x11008x4096"] = gemm_entry(synth.gemm_prefill())
+    if want("skinny"):
+        log("extra: skinny")
+        c = synth.gemm_skinny()
+        out["gemm_skinny_1x4096x4096"] = gemm_entry(c, bytes_moved=4.0 * (c.k * c.n + c.k + c.n))
+    for batch in (1, 8):
+        name = f"resnet_b{batch}"
+        if not want(name):
+            continue
+        log(f"extra: resnet50 chain batch {batch}")
+        layers = conv_chain(torch, og, synth, batch)
+        macs = sum(conv_macs(og, s) for s, *_ in layers)
+        ent = {"layers": len(layers), "gflop": round(2 * macs / 1e9, 3)}
+        for mode in ("fast", "exact"):
+            ms = timer.spike(lambda: run_chain(og, layers, mode))
+            ent[mode] = {"ms": round(ms, 4), "gflops": round(2 * macs / (ms * 1e-3) / 1e9, 1),
+                         "frac_peak": round(2 * macs / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4)}
+        if batch == 1:
+            ent["pages_cpu_context_ms"] = PAGES_RESNET_CPU_MS
+        out[f"resnet50_chain_b{batch}"] = ent
+        del layers
+    for name, shape_fn, dist in (("grouped", synth.grouped_dilated, "uniform"),
+                                 ("conv1d", synth.conv1d_h1, "uniform")):
+        if not want(name):
+            continue
+        log(f"extra: {name}")
+        s = shape_fn()
+        x, w = synth.conv_inputs(s, synth.seed_for(5, 0), dist)
+        dx, dw = torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda()
+        y = og.conv2d(dx, dw, stride=s.stride, pad=s.pad, dil=s.dil, groups=s.groups)
+        macs = conv_macs(og, s)
+        nbytes = 4.0 * (x.size + w.size + y.numel())
+        ent = {"shape": repr(s), "gflop": round(2 * macs / 1e9, 4)}
+        for mode in ("fast", "exact"):
+            ms = timer.spike(lambda: og.conv2d(dx, dw, stride=s.stride, pad=s.pad, dil=s.dil,
+                                               groups=s.groups, mode=mode, out=y))
+            ent[mode] = {"us": round(ms * 1e3, 2), "gflops": round(2 * macs / (ms * 1e-3) / 1e9, 1),
+                         "tensor_gbps_hot": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+        out[s.name] = ent
+    return out
+
+
+def cpu_baseline(synth, seconds):
+    """The oracle (fast mode, its row-wise loop) on a bounded sample of the 4096^3 rows."""
+    import oracle
+    orc = oracle.get()
+    c = synth.gemm_4096()
+    rows = 8
+    t0 = time.perf_counter()
+    orc.gemm(c.A[:rows], c.B, 1, rowwise=True)
+    dt = time.perf_counter() - t0
+    rows = int(min(c.m, max(rows, rows * seconds / max(dt, 1e-6))))
+    t0 = time.perf_counter()
+    orc.gemm(c.A[:rows], c.B, 1, rowwise=True)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * c.n * c.k
+    return {"value": round(flops / dt / 1e9, 3), "unit": "GFLOP/s", "cores": orc.num_threads(),
+            "kind": "oracle",
+            "sample": f"fast mode, rows 0..{rows - 1} of the 4096^3 product (all 4096 columns, "
+                      f"k = 4096), one call of the oracle's row-wise loop, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for "
+              f"--gpus {args.gpus}); the matrix product and convolution shard without any "
+              "exchange, by rows/columns of C or by image/group, each GPU running the one-GPU "
+              "kernel on its share.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import fp32_blocked_gemm_amd as og
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    og.lib()
+    timer = Timer(torch)
+
+    if args.only not in (None, "gemm4096_fast"):
+        log(f"only: {args.only}")
+        res = extras(torch, og, synth, timer, only=args.only)
+        print(json.dumps({"only": args.only, "extra": res}), flush=True)
+        return
+
+    log("headline: fast-mode 4096^3 matrix product")
+    case = synth.gemm_4096()
+    A, B, C = gemm_workload(torch, og, case)
+    for _ in range(args.warmup):
+        og.gemm(A, B, "fast", out=C)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ms = timer.time_calls(lambda: og.gemm(A, B, "fast", out=C), args.steps)
+    wall = time.perf_counter() - wall0
+    flops = case.flops
+    value = flops / (ms * 1e-3) / 1e9
+    achieved = flops / (ms * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "fp32 GEMM m=n=k=4096, fast mode (ordered FMA), row-major, "
+                               "N(0,1) with 0.1% special values", "m": 4096, "n": 4096, "k": 4096,
+                   "mode": "fast", "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
+                     "traffic": None, "kernel": "og::mfma_kernel<fast, 128x256, matrix B>",
+                     "wall_s_timed_region": round(wall, 3)},
+    }
+    del A, B, C
+    if args.only is None and not args.no_extra:
+        line["extra"] = extras(torch, og, synth, timer)
+        g = line["extra"]
+        g_exact = extras(torch, og, synth, timer, only="gemm4096_exact")["gemm_4096"]["exact"]
+        line["extra"]["gemm_4096_exact"] = g_exact
+    if args.only is None and not args.no_cpu:
+        log("cpu baseline: oracle on a bounded sample")
+        line["cpu_baseline"] = cpu_baseline(synth, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,289 @@
+// og_api.hip -- the C ABI of libog (declared in include/og.h): argument
+// checks, the choice of kernel and tile from the shape alone, and launches.
+//
+// The tile is a function of the shape only, never of the device or of the
+// load ("Matrix product and convolution kernels", section "Fixed chunks and
+// thread independence"); the results do not depend on it anyway, because
+// every output is summed whole, in one order, by one lane.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "og.h"
+#include "og_kernels.hpp"
+
+namespace {
+
+thread_local hipStream_t t_stream = nullptr;
+thread_local int t_variant = 0;
+thread_local std::string t_error;
+
+og_status fail(og_status code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  t_error = buf;
+  return code;
+}
+
+og_status ok() {
+  t_error.clear();
+  return OG_OK;
+}
+
+constexpr int kMaxDevices = 64;
+int g_device_state[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
+
+// The current device must be a gfx950.
+og_status check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(OG_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(OG_ERR_DEVICE, "device index %d", dev);
+  int st = __atomic_load_n(&g_device_state[dev], __ATOMIC_ACQUIRE);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return fail(OG_ERR_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    __atomic_store_n(&g_device_state[dev], st, __ATOMIC_RELEASE);
+    if (st < 0)
+      return fail(OG_ERR_DEVICE, "device %d is %s; this library runs on gfx950 only", dev,
+                  prop.gcnArchName);
+  }
+  if (st < 0) return fail(OG_ERR_DEVICE, "device %d is not gfx950", dev);
+  return OG_OK;
+}
+
+og_status check_launch(const char *what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(OG_ERR_DEVICE, "%s launch: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+constexpr int64_t kI32Max = 2147483647;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Kernel variants (og_set_variant): 1 VALU 64x64; 2..5 matrix core.
+struct Tile {
+  int variant, bm, bn;
+};
+constexpr Tile kTiles[] = {{1, 64, 64}, {2, 128, 256}, {3, 128, 128}, {4, 64, 128}, {5, 32, 256}};
+
+const Tile &tile_for_variant(int v) {
+  for (const Tile &t : kTiles)
+    if (t.variant == v) return t;
+  return kTiles[1];
+}
+
+// The tile chosen from the shape alone: the largest matrix-core tile that
+// still gives at least one workgroup per CU, weighed by the number of
+// rounds of 256 workgroups it needs.
+const Tile &choose_tile(int64_t M, int64_t N, int64_t groups) {
+  if (M <= 32) return tile_for_variant(5);
+  struct Cand {
+    int variant;
+    double eff;  // relative throughput of one CU running the tile
+  };
+  const Cand cands[] = {{2, 1.0}, {3, 0.9}, {4, 0.75}};
+  int best = 3;
+  double best_cost = 1e300;
+  for (const Cand &c : cands) {
+    const Tile &t = tile_for_variant(c.variant);
+    const int64_t blocks = ceil_div(M, t.bm) * ceil_div(N, t.bn) * groups;
+    const double rounds = (double)ceil_div(blocks, 256);
+    const double cost = rounds * t.bm * t.bn / c.eff;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = c.variant;
+    }
+  }
+  return tile_for_variant(best);
+}
+
+template <int MODE, int KIND>
+void launch_tile(const Tile &t, og::Problem p, hipStream_t s) {
+  p.tiles_m = (int)ceil_div(p.M, t.bm);
+  p.tiles_n = (int)ceil_div(p.N, t.bn);
+  const unsigned blocks = (unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)p.groups;
+  const dim3 grid(blocks), block(256);
+  switch (t.variant) {
+    case 1: hipLaunchKernelGGL((og::valu_kernel<MODE, KIND>), grid, block, 0, s, p); break;
+    case 2: hipLaunchKernelGGL((og::mfma_kernel<MODE, 128, 256, 2, 2, KIND>), grid, block, 0, s, p); break;
+    case 3: hipLaunchKernelGGL((og::mfma_kernel<MODE, 128, 128, 2, 2, KIND>), grid, block, 0, s, p); break;
+    case 4: hipLaunchKernelGGL((og::mfma_kernel<MODE, 64, 128, 2, 2, KIND>), grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL((og::mfma_kernel<MODE, 32, 256, 1, 4, KIND>), grid, block, 0, s, p); break;
+  }
+}
+
+template <int KIND>
+void launch(int mode, const Tile &t, const og::Problem &p, hipStream_t s) {
+  if (mode == OG_MODE_EXACT)
+    launch_tile<og::kExact, KIND>(t, p, s);
+  else
+    launch_tile<og::kFast, KIND>(t, p, s);
+}
+
+const Tile &pick(int64_t M, int64_t N, int64_t groups) {
+  return t_variant == 0 ? choose_tile(M, N, groups) : tile_for_variant(t_variant);
+}
+
+bool grid_fits(const Tile &t, int64_t M, int64_t N, int64_t groups) {
+  return ceil_div(M, t.bm) * ceil_div(N, t.bn) * groups <= kI32Max;
+}
+
+}  // namespace
+
+extern "C" {
+
+og_status og_gemm_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_t lda,
+                      const float *B, int64_t ldb, float *C, int64_t ldc, int mode) {
+  if (mode != OG_MODE_EXACT && mode != OG_MODE_FAST)
+    return fail(OG_ERR_INVALID_ARG, "og_gemm_f32: mode %d is not 0 (exact) or 1 (fast)", mode);
+  if (m < 0 || n < 0 || k < 0)
+    return fail(OG_ERR_INVALID_ARG, "og_gemm_f32: negative size m=%lld n=%lld k=%lld",
+                (long long)m, (long long)n, (long long)k);
+  if (lda < (k > 1 ? k : 1) || ldb < (n > 1 ? n : 1) || ldc < (n > 1 ? n : 1))
+    return fail(OG_ERR_INVALID_ARG,
+                "og_gemm_f32: leading dimension too small (lda=%lld k=%lld ldb=%lld ldc=%lld "
+                "n=%lld)",
+                (long long)lda, (long long)k, (long long)ldb, (long long)ldc, (long long)n);
+  if (m == 0 || n == 0) return ok();
+  if (C == nullptr) return fail(OG_ERR_INVALID_ARG, "og_gemm_f32: C is null");
+  if (k > 0 && (A == nullptr || B == nullptr))
+    return fail(OG_ERR_INVALID_ARG, "og_gemm_f32: A or B is null");
+  if (m > kI32Max || n > kI32Max || k > kI32Max)
+    return fail(OG_ERR_TOO_LARGE, "og_gemm_f32: a dimension exceeds 2^31-1");
+  const Tile &t = pick(m, n, 1);
+  if (!grid_fits(t, m, n, 1)) return fail(OG_ERR_TOO_LARGE, "og_gemm_f32: too many tiles");
+  og_status st = check_device();
+  if (st != OG_OK) return st;
+
+  og::Problem p{};
+  p.A = A;
+  p.lda = lda;
+  p.B = B;
+  p.ldb = ldb;
+  p.C = C;
+  p.ldc = ldc;
+  p.M = (int)m;
+  p.N = (int)n;
+  p.K = (int)k;
+  p.groups = 1;
+  launch<og::kBMatrix>(mode, t, p, t_stream);
+  return check_launch("og_gemm_f32");
+}
+
+int64_t og_conv2d_out_size(int64_t size, int64_t k, int64_t stride, int64_t padBefore,
+                           int64_t padAfter, int64_t dil) {
+  if (size < 1 || k < 1 || stride < 1 || dil < 1 || padBefore < 0 || padAfter < 0) return 0;
+  const int64_t span = size + padBefore + padAfter - dil * (k - 1) - 1;
+  if (span < 0) return 0;  // floor of a negative quotient plus one is < 1
+  return span / stride + 1;
+}
+
+og_status og_conv2d_f32_ex(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout,
+                           int64_t G, int64_t KH, int64_t KW, int64_t strideH, int64_t strideW,
+                           int64_t padTop, int64_t padLeft, int64_t padBottom, int64_t padRight,
+                           int64_t dilH, int64_t dilW, const float *x, const float *w, float *y,
+                           int mode) {
+  if (mode != OG_MODE_EXACT && mode != OG_MODE_FAST)
+    return fail(OG_ERR_INVALID_ARG, "og_conv2d_f32: mode %d is not 0 (exact) or 1 (fast)", mode);
+  if (N < 1 || Cin < 1 || H < 1 || W < 1 || Cout < 1 || G < 1 || KH < 1 || KW < 1)
+    return fail(OG_ERR_INVALID_ARG, "og_conv2d_f32: sizes must be >= 1");
+  if (strideH < 1 || strideW < 1 || dilH < 1 || dilW < 1)
+    return fail(OG_ERR_INVALID_ARG, "og_conv2d_f32: strides and dilations must be >= 1");
+  if (padTop < 0 || padLeft < 0 || padBottom < 0 || padRight < 0)
+    return fail(OG_ERR_INVALID_ARG, "og_conv2d_f32: pads must be >= 0");
+  if (Cin % G != 0 || Cout % G != 0)
+    return fail(OG_ERR_INVALID_ARG, "og_conv2d_f32: Cin=%lld and Cout=%lld must be multiples of "
+                "G=%lld", (long long)Cin, (long long)Cout, (long long)G);
+  const int64_t OH = og_conv2d_out_size(H, KH, strideH, padTop, padBottom, dilH);
+  const int64_t OW = og_conv2d_out_size(W, KW, strideW, padLeft, padRight, dilW);
+  if (OH < 1 || OW < 1)
+    return fail(OG_ERR_INVALID_ARG, "og_conv2d_f32: the window does not fit the padded input");
+  if (x == nullptr || w == nullptr || y == nullptr)
+    return fail(OG_ERR_INVALID_ARG, "og_conv2d_f32: null pointer");
+  const int64_t cin_g = Cin / G, cout_g = Cout / G;
+  const int64_t K = cin_g * KH * KW, ncols = N * OH * OW;
+  // every index the kernels form in 32 bits must fit
+  const int64_t dims[] = {K, ncols, cout_g, H, W, OH * OW, KH * KW,
+                          (H + padTop + padBottom) * strideH, (W + padLeft + padRight) * strideW,
+                          KH * dilH + H, KW * dilW + W};
+  for (int64_t d : dims)
+    if (d > kI32Max) return fail(OG_ERR_TOO_LARGE, "og_conv2d_f32: a dimension exceeds 2^31-1");
+  const bool planes = KH == 1 && KW == 1 && strideH == 1 && strideW == 1 && padTop == 0 &&
+                      padLeft == 0 && padBottom == 0 && padRight == 0;
+  const Tile &t = pick(cout_g, ncols, G);
+  if (!grid_fits(t, cout_g, ncols, G)) return fail(OG_ERR_TOO_LARGE, "og_conv2d_f32: too many tiles");
+  og_status st = check_device();
+  if (st != OG_OK) return st;
+
+  og::Problem p{};
+  p.A = w;
+  p.lda = K;
+  p.a_gstride = cout_g * K;
+  p.B = x;
+  p.C = y;
+  p.M = (int)cout_g;
+  p.N = (int)ncols;
+  p.K = (int)K;
+  p.groups = (int)G;
+  p.H = (int)H;
+  p.W = (int)W;
+  p.OW = (int)OW;
+  p.OHW = (int)(OH * OW);
+  p.KW = (int)KW;
+  p.KHW = (int)(KH * KW);
+  p.sH = (int)strideH;
+  p.sW = (int)strideW;
+  p.pT = (int)padTop;
+  p.pL = (int)padLeft;
+  p.dH = (int)dilH;
+  p.dW = (int)dilW;
+  p.x_img = Cin * H * W;
+  p.x_grp = cin_g * H * W;
+  p.y_img = Cout * OH * OW;
+  p.y_grp = cout_g * OH * OW;
+  if (planes)
+    launch<og::kBPlanes>(mode, t, p, t_stream);
+  else
+    launch<og::kBGather>(mode, t, p, t_stream);
+  return check_launch("og_conv2d_f32");
+}
+
+og_status og_conv2d_f32(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout, int64_t G,
+                        int64_t KH, int64_t KW, int64_t stride, int64_t pad, int64_t dil,
+                        const float *x, const float *w, float *y, int mode) {
+  return og_conv2d_f32_ex(N, Cin, H, W, Cout, G, KH, KW, stride, stride, pad, pad, pad, pad, dil,
+                          dil, x, w, y, mode);
+}
+
+og_status og_set_stream(void *hip_stream) {
+  t_stream = static_cast<hipStream_t>(hip_stream);
+  return ok();
+}
+
+void *og_get_stream(void) { return t_stream; }
+
+og_status og_set_variant(int variant) {
+  if (variant < 0 || variant > 5)
+    return fail(OG_ERR_INVALID_ARG, "og_set_variant: %d is not in 0..5", variant);
+  t_variant = variant;
+  return ok();
+}
+
+int og_get_variant(void) { return t_variant; }
+
+const char *og_last_error(void) { return t_error.c_str(); }
+
+const char *og_version(void) { return "0.1.0"; }
+
+}  // extern "C"

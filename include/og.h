@@ -1,0 +1,145 @@
+/*
+ * og.h -- exact and fast fp32 matrix product and NCHW convolution on AMD
+ * Instinct MI355X (gfx950).  C ABI of libog.so.
+ *
+ * What the library computes is defined by two pages of the OneModel
+ * documentation:
+ *  - "Exact mode", sections "Rules every exact kernel follows", "Matrix
+ *    product" and "Convolution": every output is one accumulator that starts
+ *    at +0 and receives its terms in increasing index (for a convolution:
+ *    channel, then kernel row, then kernel column), each product and each sum
+ *    rounded to binary32 on its own (round to nearest even, subnormals kept);
+ *    a NaN result is stored as 0x7FC00000; an empty sum is +0; no bias.
+ *  - "Matrix product and convolution kernels", section "Fast mode", and
+ *    "Convolution (fast mode)", section "What each output is": the same
+ *    accumulator and order with one fused multiply-add per term.  This
+ *    library also stores a NaN result of fast mode as 0x7FC00000, so both
+ *    modes have exactly one correct bit pattern per output.
+ * Results do not depend on tile shapes, kernel variant, stream or device:
+ * every output is computed whole by one GPU lane over all of k, and k is
+ * never split ("Matrix product and convolution kernels", section "Fixed
+ * chunks and thread independence").
+ *
+ * Conventions of every entry point below:
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *    library allocates nothing, keeps no pointer after it returns and frees
+ *    nothing.  Outputs must not overlap inputs.
+ *  - Work is queued on the calling thread's current stream (og_set_stream)
+ *    and the call returns without waiting for it.  Argument errors are
+ *    returned before anything is queued; a fault inside a kernel surfaces at
+ *    the caller's next synchronisation.
+ *  - On an error nothing is written, and og_last_error() describes it.
+ *  - Only gfx950 is supported: on any other device a compute call returns
+ *    OG_ERR_DEVICE (there is no fallback path).
+ */
+#ifndef OG_H
+#define OG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int og_status;
+
+#define OG_OK 0
+#define OG_ERR_INVALID_ARG (-1) /* a size, stride, pointer or mode is out of range           */
+#define OG_ERR_NOT_EXACT (-2)   /* exact mode asked of a kernel variant that has no exact form
+                                   ("Exact mode": reported, never approximated)              */
+#define OG_ERR_DEVICE (-3)      /* HIP error, or the current device is not gfx950            */
+#define OG_ERR_TOO_LARGE (-4)   /* a dimension does not fit the kernels' 32-bit counters     */
+
+#define OG_MODE_EXACT 0 /* separately rounded multiply and add ("Exact mode")              */
+#define OG_MODE_FAST 1  /* one fused multiply-add per term, same order ("Fast mode")        */
+
+/*
+ * Matrix product, row-major ("Matrix product and convolution kernels",
+ * first paragraph; "Exact mode", section "Matrix product"):
+ *
+ *     C[i*ldc + j] = sum over p = 0..k-1 of A[i*lda + p] * B[p*ldb + j]
+ *
+ * for 0 <= i < m, 0 <= j < n, summed by the mode's rule.  C is overwritten
+ * (there is no alpha, beta or bias); the gaps C[i*ldc + j], n <= j < ldc, are
+ * never written.  Requirements: m, n, k >= 0; lda >= max(1,k),
+ * ldb >= max(1,n), ldc >= max(1,n); A and B non-null when m, n and k are all
+ * positive, C non-null when m and n are positive.  m == 0 or n == 0: nothing
+ * is done.  k == 0: every output is +0 and A, B are not read.
+ */
+og_status og_gemm_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_t lda,
+                      const float *B, int64_t ldb, float *C, int64_t ldc, int mode);
+
+/*
+ * 2-D convolution, NCHW, per-axis stride, padding and dilation ("Exact mode",
+ * section "Convolution"; "Convolution (fast mode)", sections "What each output
+ * is" and "Layout of the work"):
+ *
+ *   x [N, Cin, H, W], w [Cout, Cin/G, KH, KW], y [N, Cout, OH, OW], contiguous;
+ *   output (n, oc, oy, ox) of group g = oc / (Cout/G) sums, over c in
+ *   [0, Cin/G), then ky in [0, KH), then kx in [0, KW), the products
+ *   w[oc][c][ky][kx] * v, where v is x[n][g*Cin/G + c][iy][ix] with
+ *   iy = oy*strideH - padTop + ky*dilH and ix = ox*strideW - padLeft + kx*dilW
+ *   when 0 <= iy < H and 0 <= ix < W, and +0 otherwise.  Taps in the padding
+ *   are real products with +0 (an infinite or NaN weight there gives NaN).
+ *   OH and OW follow og_conv2d_out_size.  No bias.
+ *
+ * It runs as an implicit matrix product per group: the weights are A and the
+ * input patches are gathered into on-chip tiles of B, the zero padding written
+ * during the gather and never stored in memory.  A one-dimensional
+ * convolution is H = 1, KH = 1 with padTop = padBottom = 0.
+ * Requirements: N, Cin, H, W, Cout, G, KH, KW >= 1; strides and dilations
+ * >= 1; pads >= 0; Cin and Cout multiples of G; OH, OW >= 1; pointers
+ * non-null.
+ */
+og_status og_conv2d_f32_ex(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout,
+                           int64_t G, int64_t KH, int64_t KW, int64_t strideH, int64_t strideW,
+                           int64_t padTop, int64_t padLeft, int64_t padBottom, int64_t padRight,
+                           int64_t dilH, int64_t dilW, const float *x, const float *w, float *y,
+                           int mode);
+
+/*
+ * The same convolution with one stride, one symmetric padding and one
+ * dilation for both axes: og_conv2d_f32_ex(..., stride, stride, pad, pad,
+ * pad, pad, dil, dil, ...).
+ */
+og_status og_conv2d_f32(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout, int64_t G,
+                        int64_t KH, int64_t KW, int64_t stride, int64_t pad, int64_t dil,
+                        const float *x, const float *w, float *y, int mode);
+
+/*
+ * Output length of one axis ("Exact mode", section "Convolution"):
+ * floor((size + padBefore + padAfter - dil*(k-1) - 1) / stride) + 1.
+ * Returns a value < 1 when the window does not fit or an argument is out of
+ * range (size, k, stride, dil < 1 or a pad < 0).  Host-only, no device use.
+ */
+int64_t og_conv2d_out_size(int64_t size, int64_t k, int64_t stride, int64_t padBefore,
+                           int64_t padAfter, int64_t dil);
+
+/*
+ * Stream for the calling thread's later calls (a hipStream_t; NULL = the
+ * default stream).  The library does not take ownership.  Always OG_OK.
+ */
+og_status og_set_stream(void *hip_stream);
+void *og_get_stream(void);
+
+/*
+ * Kernel variant for the calling thread's later calls, for tests that check
+ * the results do not depend on it ("Exact mode", rule 5): 0 = chosen from
+ * the shape (the default); 1 = the VALU tile kernel; 2, 3, 4 = the matrix-core
+ * kernel with 128x256, 128x128 and 64x128 output tiles; 5 = the matrix-core
+ * kernel with 32x256 tiles.  A value outside 0..5 returns OG_ERR_INVALID_ARG.
+ * Shapes a variant cannot run fall back to the automatic choice.
+ */
+og_status og_set_variant(int variant);
+int og_get_variant(void);
+
+/* Description of the calling thread's last error ("" after a success). */
+const char *og_last_error(void);
+
+/* Library version, "major.minor.patch". */
+const char *og_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,121 @@
+"""The C-ABI library on a host without a GPU: it loads, exports every symbol
+``include/og.h`` declares, and rejects invalid arguments before touching the
+device.  No compute call is made here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import fp32_blocked_gemm_amd as og
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "og.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(og_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return og.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert {"og_gemm_f32", "og_conv2d_f32", "og_conv2d_f32_ex", "og_set_stream",
+            "og_last_error"} <= set(names)
+    for name in names:
+        assert hasattr(L, name), f"{name} is declared in og.h but not exported"
+
+
+def test_version(L):
+    assert re.fullmatch(r"\d+\.\d+\.\d+", og.version())
+
+
+NULL = None
+P = ctypes.c_void_p(16)  # a non-null pointer that is never dereferenced (arguments fail first)
+
+
+@pytest.mark.parametrize("args,why", [
+    ((4, 4, 4, P, 4, P, 4, P, 4, 7), "mode"),
+    ((-1, 4, 4, P, 4, P, 4, P, 4, 0), "negative m"),
+    ((4, -1, 4, P, 4, P, 4, P, 4, 0), "negative n"),
+    ((4, 4, -1, P, 4, P, 4, P, 4, 0), "negative k"),
+    ((4, 4, 5, P, 4, P, 4, P, 4, 0), "lda < k"),
+    ((4, 5, 4, P, 4, P, 4, P, 5, 0), "ldb < n"),
+    ((4, 5, 4, P, 4, P, 5, P, 4, 1), "ldc < n"),
+    ((4, 4, 4, NULL, 4, P, 4, P, 4, 0), "A null"),
+    ((4, 4, 4, P, 4, NULL, 4, P, 4, 0), "B null"),
+    ((4, 4, 4, P, 4, P, 4, NULL, 4, 1), "C null"),
+    ((4, 4, 0, P, 0, P, 4, P, 4, 0), "lda must be >= 1 even for k = 0"),
+])
+def test_gemm_rejects_before_launch(L, args, why):
+    assert L.og_gemm_f32(*args) == og.OG_ERR_INVALID_ARG, why
+    assert L.og_last_error()
+
+
+def test_gemm_empty_is_a_no_op(L):
+    assert L.og_gemm_f32(0, 4, 4, NULL, 4, NULL, 4, NULL, 4, 0) == og.OG_OK
+    assert L.og_gemm_f32(3, 0, 4, NULL, 4, NULL, 1, NULL, 1, 1) == og.OG_OK
+    assert L.og_last_error() == b""
+
+
+def test_too_large(L):
+    assert L.og_gemm_f32(1 << 31, 1, 1, P, 1, P, 1, P, 1, 0) == og.OG_ERR_TOO_LARGE
+
+
+def _conv(L, N=1, Cin=4, H=5, W=5, Cout=4, G=1, KH=3, KW=3, s=(1, 1), p=(0, 0, 0, 0), d=(1, 1),
+          x=P, w=P, y=P, mode=0):
+    return L.og_conv2d_f32_ex(N, Cin, H, W, Cout, G, KH, KW, s[0], s[1], p[0], p[1], p[2], p[3],
+                              d[0], d[1], x, w, y, mode)
+
+
+@pytest.mark.parametrize("kw,why", [
+    (dict(mode=2), "mode"),
+    (dict(N=0), "N"), (dict(Cin=0), "Cin"), (dict(H=0), "H"), (dict(KW=0), "KW"),
+    (dict(G=3), "Cin % G"), (dict(Cin=6, G=3, Cout=4), "Cout % G"),
+    (dict(s=(0, 1)), "stride"), (dict(d=(1, 0)), "dilation"), (dict(p=(0, -1, 0, 0)), "pad"),
+    (dict(KH=7), "window larger than the input"),
+    (dict(x=NULL), "x null"), (dict(w=NULL), "w null"), (dict(y=NULL), "y null"),
+])
+def test_conv_rejects_before_launch(L, kw, why):
+    assert _conv(L, **kw) == og.OG_ERR_INVALID_ARG, why
+    assert L.og_last_error()
+
+
+def test_out_size_matches_the_formula():
+    orc = oracle.get()
+    rng = np.random.default_rng(0)
+    for _ in range(2000):
+        size, k, stride, pb, pa, dil = (int(v) for v in rng.integers(1, 9, size=6))
+        pb -= 1
+        pa -= 1
+        want = orc.conv_out_size(size, k, stride, pb, pa, dil)
+        got = og.conv2d_out_size(size, k, stride, pb, pa, dil)
+        assert (got if got >= 1 else 0) == (want if want >= 1 else 0), (size, k, stride, pb, pa,
+                                                                        dil)
+
+
+def test_variant_and_stream_state(L):
+    assert L.og_set_variant(9) == og.OG_ERR_INVALID_ARG
+    assert L.og_set_variant(3) == og.OG_OK and L.og_get_variant() == 3
+    assert L.og_set_variant(0) == og.OG_OK
+    assert L.og_set_stream(None) == og.OG_OK and L.og_get_stream() is None
+
+
+def test_no_device_is_reported_not_hidden(L):
+    """With valid arguments and no usable gfx950 device, the call reports
+    OG_ERR_DEVICE (there is no CPU fallback)."""
+    try:
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("a GPU is present")
+    except ImportError:
+        pass
+    assert L.og_gemm_f32(2, 2, 2, P, 2, P, 2, P, 2, 0) == og.OG_ERR_DEVICE

@@ -1,0 +1,160 @@
+"""GPU parity of the implicit-GEMM convolution: libog (through its C ABI)
+against the CPU oracle's direct convolution, bit for bit, exact and fast.
+
+Cases: small random shapes covering stride, asymmetric padding, dilation,
+groups (depthwise included) and batch, with special values; the 53 layers of
+ResNet-50 v1.5 at batch 1 in full and at batch 8 on sampled outputs; the
+grouped dilated strided convolution in full; the 1-D convolution (H = 1) on
+sampled outputs and whole rows.
+"""
+import numpy as np
+import pytest
+
+import fp32_blocked_gemm_amd as og
+import oracle
+import synth
+from gpu_util import assert_same_bits, say, sha256, to_host, torch
+
+pytestmark = pytest.mark.gpu
+MODES = (og.EXACT, og.FAST)
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+@pytest.fixture(autouse=True)
+def auto_variant():
+    og.set_variant(0)
+    yield
+    og.set_variant(0)
+
+
+def _gpu_conv(x, w, s: synth.ConvShape, mode):
+    t = torch()
+    dx = t.from_numpy(x).cuda()
+    dw = t.from_numpy(w).cuda()
+    y = og.conv2d(dx, dw, stride=s.stride, pad=s.pad, dil=s.dil, groups=s.groups, mode=mode)
+    return to_host(y)
+
+
+def _oracle(orc, x, w, s, mode):
+    return orc.conv2d(x, w, mode, groups=s.groups, stride=s.stride, pad=s.pad, dil=s.dil)
+
+
+def _random_shapes(rng, count):
+    shapes = []
+    while len(shapes) < count:
+        G = int(rng.choice([1, 1, 2, 3, 4]))
+        cin_g = int(rng.integers(1, 9))
+        cout_g = int(rng.integers(1, 40))
+        KH, KW = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+        H, W = int(rng.integers(1, 23)), int(rng.integers(1, 23))
+        st = (int(rng.integers(1, 4)), int(rng.integers(1, 4)))
+        dl = (int(rng.integers(1, 4)), int(rng.integers(1, 4)))
+        pad = tuple(int(p) for p in rng.integers(0, 4, size=4))
+        if H + pad[0] + pad[2] - dl[0] * (KH - 1) - 1 < 0:
+            continue
+        if W + pad[1] + pad[3] - dl[1] * (KW - 1) - 1 < 0:
+            continue
+        shapes.append(synth.ConvShape(f"rand{len(shapes)}", int(rng.integers(1, 4)), G * cin_g,
+                                      H, W, G * cout_g, KH, KW, st, pad, dl, G))
+    return shapes
+
+
+def _with_specials(a, rng, frac):
+    a = a.copy()
+    synth.inject_specials(a.reshape(a.shape[0], -1), frac, int(rng.integers(1 << 30)))
+    return a
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_random_shapes(orc, mode):
+    rng = np.random.default_rng(200 + mode)
+    for s in _random_shapes(rng, 60):
+        x, w = synth.conv_inputs(s, int(rng.integers(1 << 30)), "uniform")
+        x = _with_specials(x, rng, 0.01)
+        w = _with_specials(w, rng, 0.01)
+        say(f"conv {s} mode {mode}")
+        assert_same_bits(_gpu_conv(x, w, s, mode), _oracle(orc, x, w, s, mode), f"{s} mode {mode}")
+
+
+@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5])
+def test_variants_agree(orc, variant):
+    rng = np.random.default_rng(300)
+    og.set_variant(variant)
+    shapes = [synth.ConvShape("v3x3", 2, 24, 13, 11, 40, 3, 3, (1, 2), (1, 0, 2, 1), (2, 1), 2),
+              synth.ConvShape("v1x1", 3, 20, 9, 7, 70, 1, 1)]
+    for s in shapes:
+        x, w = synth.conv_inputs(s, int(rng.integers(1 << 30)), "uniform")
+        for mode in MODES:
+            say(f"conv variant {variant} {s} mode {mode}")
+            assert_same_bits(_gpu_conv(x, w, s, mode), _oracle(orc, x, w, s, mode),
+                             f"variant {variant} {s} mode {mode}")
+
+
+def test_padding_tap_meets_infinite_weight(orc):
+    """An infinite weight on a padding tap gives NaN (padding taps are real products)."""
+    s = synth.ConvShape("w8", 1, 1, 1, 1, 1, 3, 3, (1, 1), (1, 1, 1, 1))
+    x = np.array([[[[2.0]]]], np.float32)
+    w = np.ones((1, 1, 3, 3), np.float32)
+    w[0, 0, 0, 0] = np.inf
+    for mode in MODES:
+        y = _gpu_conv(x, w, s, mode)
+        assert y.view(np.uint32).ravel()[0] == 0x7FC00000
+
+
+def test_resnet50_batch1_all_layers(orc):
+    """All 53 layers of the chain at batch 1, every output, both modes."""
+    for i, s in enumerate(synth.resnet50_convs(1)):
+        x, w = synth.conv_inputs(s, synth.seed_for(4, i))
+        for mode in MODES:
+            say(f"resnet50 b1 layer {i} {s} mode {mode}")
+            got = _gpu_conv(x, w, s, mode)
+            want = _oracle(orc, x, w, s, mode)
+            assert sha256(got) == sha256(want), f"layer {i} {s.name} mode {mode}"
+
+
+def _flat_sample(rng, shape, count):
+    total = int(np.prod(shape))
+    idx = rng.integers(0, total, size=count)
+    return np.concatenate([idx, [0, total - 1]])
+
+
+def test_resnet50_batch8_sampled(orc):
+    rng = np.random.default_rng(8)
+    for i, s in enumerate(synth.resnet50_convs(8)):
+        x, w = synth.conv_inputs(s, synth.seed_for(4, 100 + i))
+        for mode in MODES:
+            say(f"resnet50 b8 layer {i} {s} mode {mode}")
+            got = _gpu_conv(x, w, s, mode)
+            flat = _flat_sample(rng, got.shape, 600)
+            want = orc.conv2d_at(x, w, flat, mode, groups=s.groups, stride=s.stride, pad=s.pad,
+                                 dil=s.dil)
+            assert_same_bits(got.ravel()[flat], want, f"b8 layer {i} {s.name} mode {mode}")
+
+
+def test_grouped_dilated_full(orc):
+    s = synth.grouped_dilated()
+    x, w = synth.conv_inputs(s, synth.seed_for(5, 0), "uniform")
+    for mode in MODES:
+        say(f"grouped dilated mode {mode}")
+        assert_same_bits(_gpu_conv(x, w, s, mode), _oracle(orc, x, w, s, mode),
+                         f"grouped mode {mode}")
+
+
+def test_conv1d_h1_sampled(orc):
+    s = synth.conv1d_h1()
+    x, w = synth.conv_inputs(s, synth.seed_for(5, 10), "uniform")
+    rng = np.random.default_rng(10)
+    for mode in MODES:
+        say(f"conv1d mode {mode}")
+        got = _gpu_conv(x, w, s, mode)
+        assert got.shape == (8, 512, 1, 4096)
+        flat = _flat_sample(rng, got.shape, 3000)
+        want = orc.conv2d_at(x, w, flat, mode, groups=1, stride=s.stride, pad=s.pad, dil=s.dil)
+        assert_same_bits(got.ravel()[flat], want, f"conv1d sampled mode {mode}")
+        # one whole image against the oracle on that image alone (batch invariance)
+        want0 = orc.conv2d(np.ascontiguousarray(x[:1]), w, mode, pad=s.pad)
+        assert_same_bits(got[:1], want0, f"conv1d image 0 mode {mode}")

@@ -1,0 +1,197 @@
+"""GPU parity of the matrix product: libog (through its C ABI) against the CPU
+oracle, bit for bit, in exact and fast mode.
+
+Sizes: every dimension swept over 0..70 with the others fixed (the sweep the
+exact-mode page describes under "Checking it"), random row strides and
+pointer offsets, special values; the 256^3 exact case in full; the ragged
+1000x777x1531 case with row strides dim+13 in full; 4096^3, the prefill
+shape and the skinny m = 1 shape at full size on sampled outputs (and whole
+rows) in the launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+
+import fp32_blocked_gemm_amd as og
+import oracle
+import synth
+from gpu_util import assert_same_bits, bits, say, sha256, to_device_strided, to_host, torch
+
+pytestmark = pytest.mark.gpu
+MODES = (og.EXACT, og.FAST)
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+@pytest.fixture(autouse=True)
+def auto_variant():
+    og.set_variant(0)
+    yield
+    og.set_variant(0)
+
+
+def _mixed(rng, shape, special_frac):
+    """N(0,1) values with a fraction of special values (NaN kinds, +-inf, subnormal, -0)."""
+    v = rng.standard_normal(shape).astype(np.float32)
+    if special_frac > 0 and v.size:
+        synth.inject_specials(v.reshape(shape[0], -1), special_frac, int(rng.integers(1 << 30)))
+    return v
+
+
+def _run_gpu(A, B, mode, lda, ldb, ldc, offs=(0, 0, 0)):
+    m, k = A.shape
+    n = B.shape[1]
+    dA, _ = to_device_strided(A, lda, offs[0])
+    dB, _ = to_device_strided(B, ldb, offs[1])
+    fill = np.full((m, n), synth.GAP_OUT_BITS, np.uint32).view(np.float32)
+    dC, flatC = to_device_strided(fill, ldc, offs[2], gap_bits=synth.GAP_OUT_BITS)
+    og.gemm(dA, dB, mode, out=dC)
+    torch().cuda.synchronize()
+    return to_host(dC), to_host(flatC)
+
+
+def _check_gaps(flatC, m, n, ldc, off):
+    u = flatC.view(np.uint32)
+    mask = np.ones(u.shape, bool)
+    if m and n:
+        idx = off + np.arange(m)[:, None] * ldc + np.arange(n)[None, :]
+        mask[idx.ravel()] = False
+    assert np.all(u[mask] == synth.GAP_OUT_BITS), "an element outside C was written"
+
+
+def test_square_256_exact_config(orc):
+    """m = n = k = 256, uniform[-1,1] from seed 0: bit for bit, exact and fast."""
+    c = synth.gemm_square256()
+    for mode in MODES:
+        say(f"gemm 256^3 mode {mode}")
+        got, _ = _run_gpu(c.A, c.B, mode, 256, 256, 256)
+        want = orc.gemm(c.A, c.B, mode, rowwise=True)
+        assert sha256(got) == sha256(want)
+        assert_same_bits(got, want, f"256^3 mode {mode}")
+
+
+SWEEP = [(d, 37, 45) for d in range(71)] + [(19, d, 45) for d in range(71)] + \
+        [(19, 37, d) for d in range(71)]
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_size_sweep_0_to_70(orc, mode):
+    """Every size 0..70 in each dimension, random strides, offsets and special values."""
+    rng = np.random.default_rng(100 + mode)
+    say(f"gemm sweep mode {mode}")
+    for (m, n, k) in SWEEP:
+        A = _mixed(rng, (m, k), 0.02)
+        B = _mixed(rng, (k, n), 0.02)
+        lda = max(1, k) + int(rng.integers(0, 5))
+        ldb = max(1, n) + int(rng.integers(0, 5))
+        ldc = max(1, n) + int(rng.integers(0, 5))
+        offs = tuple(int(o) for o in rng.integers(0, 7, size=3))
+        got, flatC = _run_gpu(A, B, mode, lda, ldb, ldc, offs)
+        want = orc.gemm(A, B, mode)
+        assert_same_bits(got, want, f"sweep {m}x{n}x{k} mode {mode}")
+        _check_gaps(flatC, m, n, ldc, offs[2])
+
+
+@pytest.mark.parametrize("specials", [True, False])
+def test_ragged_ld13_full(orc, specials):
+    """1000x777x1531 with row strides dim+13 and 0.1% special values: every output."""
+    c = synth.gemm_ragged(specials)
+    for mode in MODES:
+        say(f"gemm ragged specials={specials} mode {mode}")
+        got, flatC = _run_gpu(c.A, c.B, mode, c.lda, c.ldb, c.ldc)
+        want = orc.gemm(c.A, c.B, mode, rowwise=True)
+        assert_same_bits(got, want, f"ragged mode {mode}")
+        _check_gaps(flatC, c.m, c.n, c.ldc, 0)
+
+
+@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5])
+def test_variants_agree(orc, variant):
+    """Every kernel variant gives the oracle's bits (no dependence on tiles)."""
+    rng = np.random.default_rng(7)
+    m, n, k = 131, 301, 97
+    A = _mixed(rng, (m, k), 0.01)
+    B = _mixed(rng, (k, n), 0.01)
+    og.set_variant(variant)
+    for mode in MODES:
+        say(f"gemm variant {variant} mode {mode}")
+        got, _ = _run_gpu(A, B, mode, k + 3, n + 1, n + 2, (1, 2, 3))
+        assert_same_bits(got, orc.gemm(A, B, mode), f"variant {variant} mode {mode}")
+
+
+def _sample(rng, m, n, count):
+    rows = rng.integers(0, m, size=count)
+    cols = rng.integers(0, n, size=count)
+    # the four corners and the last row/column, where tile edges are
+    rows = np.concatenate([rows, [0, 0, m - 1, m - 1]])
+    cols = np.concatenate([cols, [0, n - 1, 0, n - 1]])
+    return rows, cols
+
+
+def _full_size(orc, c, whole_rows):
+    rng = np.random.default_rng(5)
+    for mode in MODES:
+        say(f"gemm {c.name} mode {mode}")
+        dA, _ = to_device_strided(c.A, c.lda)
+        dB, _ = to_device_strided(c.B, c.ldb)
+        dC = torch().empty((c.m, c.ldc), dtype=torch().float32, device="cuda")[:, :c.n]
+        og.gemm(dA, dB, mode, out=dC)
+        got = to_host(dC)
+        rows, cols = _sample(rng, c.m, c.n, 3000)
+        want = orc.gemm_at(c.A, c.B, rows, cols, mode)
+        assert_same_bits(got[rows, cols], want, f"{c.name} sampled mode {mode}")
+        for r in whole_rows:
+            wr = orc.gemm(c.A[r:r + 1], c.B, mode, rowwise=True)
+            assert_same_bits(got[r:r + 1], wr, f"{c.name} row {r} mode {mode}")
+        # run twice: the same bits
+        og.gemm(dA, dB, mode, out=dC)
+        assert np.array_equal(bits(to_host(dC)), bits(got)), "second run differs"
+
+
+@pytest.mark.parametrize("specials", [True, False])
+def test_4096_cubed_sampled(orc, specials):
+    _full_size(orc, synth.gemm_4096(specials), whole_rows=[0, 2047, 4095])
+
+
+def test_prefill_sampled(orc):
+    _full_size(orc, synth.gemm_prefill(), whole_rows=[0, 511])
+
+
+def test_skinny_full(orc):
+    c = synth.gemm_skinny()
+    for mode in MODES:
+        say(f"gemm skinny mode {mode}")
+        got, _ = _run_gpu(c.A, c.B, mode, c.lda, c.ldb, c.ldc)
+        assert_same_bits(got, orc.gemm(c.A, c.B, mode, rowwise=True), f"skinny mode {mode}")
+
+
+def test_k_zero_and_empty():
+    """k = 0 stores +0 everywhere; m = 0 or n = 0 does nothing."""
+    t = torch()
+    C = t.full((3, 5), float("nan"), device="cuda")
+    A = t.empty((3, 0), device="cuda")
+    B = t.empty((0, 5), device="cuda")
+    for mode in MODES:
+        say(f"gemm k=0 mode {mode}")
+        og.gemm(A, B, mode, out=C)
+        assert np.all(bits(to_host(C)) == 0)
+    og.gemm(t.empty((0, 4), device="cuda"), t.ones((4, 5), device="cuda"), "exact",
+            out=t.empty((0, 5), device="cuda"))
+    t.cuda.synchronize()
+
+
+def test_stream_is_honoured(orc):
+    """Work goes to the current torch stream and is ordered on it."""
+    t = torch()
+    rng = np.random.default_rng(9)
+    A = rng.standard_normal((300, 200)).astype(np.float32)
+    B = rng.standard_normal((200, 400)).astype(np.float32)
+    s = t.cuda.Stream()
+    with t.cuda.stream(s):
+        dA = t.from_numpy(A).cuda()
+        dB = t.from_numpy(B).cuda()
+        C = og.gemm(dA, dB, "fast")
+        got = C.cpu().numpy()
+    assert og.lib().og_get_stream() == s.cuda_stream
+    assert_same_bits(got, orc.gemm(A, B, 1), "gemm on a side stream")
