@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <string>
 
 #include "og.h"
@@ -71,11 +72,17 @@ constexpr int64_t kI32Max = 2147483647;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Kernel variants (og_set_variant): 1 VALU 64x64; 2..5 matrix core.
+// Kernel variants (og_set_variant): 1 VALU 64x64 tile; 2..5 matrix core with
+// (bm, bn) output tiles; 6..9 the lane kernel with R = 1, 2, 4, 8 rows per
+// wave and 4 waves (so bm = 4R, bn = 64).
 struct Tile {
   int variant, bm, bn;
+  int per_wave;  // matrix core: 32x64 blocks per wave; lane kernel: rows per wave
 };
-constexpr Tile kTiles[] = {{1, 64, 64}, {2, 128, 256}, {3, 128, 128}, {4, 64, 128}, {5, 32, 256}};
+constexpr Tile kTiles[] = {{1, 64, 64, 0},  {2, 128, 256, 4}, {3, 128, 128, 2}, {4, 64, 128, 1},
+                           {5, 32, 256, 1}, {6, 4, 64, 1},    {7, 8, 64, 2},    {8, 16, 64, 4},
+                           {9, 32, 64, 8}};
+constexpr int kNumVariants = 9;
 
 const Tile &tile_for_variant(int v) {
   for (const Tile &t : kTiles)
@@ -83,26 +90,46 @@ const Tile &tile_for_variant(int v) {
   return kTiles[1];
 }
 
-// The tile chosen from the shape alone: the largest matrix-core tile that
-// still gives at least one workgroup per CU, weighed by the number of
-// rounds of 256 workgroups it needs.
-const Tile &choose_tile(int64_t M, int64_t N, int64_t groups) {
-  if (M <= 32) return tile_for_variant(5);
-  struct Cand {
-    int variant;
-    double eff;  // relative throughput of one CU running the tile
-  };
-  const Cand cands[] = {{2, 1.0}, {3, 0.9}, {4, 0.75}};
+bool is_lane(const Tile &t) { return t.variant >= 6; }
+
+// Estimated cycles of one launch, from the shape alone.  The constants are
+// fitted to launches measured on MI355X: the matrix-core kernel sustains one
+// 32x32x1 MFMA per ~94 cycles per SIMD in fast mode (188 in exact mode) when
+// its tiles fill the chip, and ~300 cycles per k step when a few tiles run
+// alone (the loads of the next k-chunk are then exposed); the lane kernel
+// takes ~70 cycles per k step (~135 with the padded gather) while it has at
+// most one wave per SIMD.
+double estimate(const Tile &t, int64_t M, int64_t N, int64_t K, int64_t groups, int mode,
+                bool gather) {
+  const double cus = 256.0, simds = 1024.0;
+  const int64_t blocks = ceil_div(M, t.bm) * ceil_div(N, t.bn) * groups;
+  const double kk = (double)(K > 0 ? K : 1);
+  if (is_lane(t)) {
+    const double waves = 4.0 * blocks;
+    const double step = (gather ? 135.0 : 70.0) * (mode == OG_MODE_EXACT ? 1.1 : 1.0) *
+                        (1.0 + 0.15 * (t.per_wave - 1));
+    return kk * step * std::max(1.0, waves / simds) + 3000.0;
+  }
+  const double per_mfma = mode == OG_MODE_EXACT ? 188.0 : 94.0;
+  const double lone = std::max(per_mfma * t.per_wave, 300.0);
+  const double full = per_mfma * t.per_wave;
+  const double rounds = (double)ceil_div(blocks, (int64_t)cus);
+  const double t_block = kk * (blocks < (int64_t)cus ? lone : full) + 3000.0;
+  return t_block * rounds;
+}
+
+// The kernel chosen from the shape alone: the lowest estimate.
+const Tile &choose_tile(int64_t M, int64_t N, int64_t K, int64_t groups, int mode,
+                        bool gather) {
+  const int cands[] = {2, 3, 4, 5, 6, 7, 8, 9};
   int best = 3;
   double best_cost = 1e300;
-  for (const Cand &c : cands) {
-    const Tile &t = tile_for_variant(c.variant);
-    const int64_t blocks = ceil_div(M, t.bm) * ceil_div(N, t.bn) * groups;
-    const double rounds = (double)ceil_div(blocks, 256);
-    const double cost = rounds * t.bm * t.bn / c.eff;
-    if (cost < best_cost) {
-      best_cost = cost;
-      best = c.variant;
+  for (int v : cands) {
+    if (v == 9 && mode == OG_MODE_EXACT) continue;  // eight rows per lane: VALU-bound in exact mode
+    const double c = estimate(tile_for_variant(v), M, N, K, groups, mode, gather);
+    if (c < best_cost) {
+      best_cost = c;
+      best = v;
     }
   }
   return tile_for_variant(best);
@@ -119,7 +146,11 @@ void launch_tile(const Tile &t, og::Problem p, hipStream_t s) {
     case 2: hipLaunchKernelGGL((og::mfma_kernel<MODE, 128, 256, 2, 2, KIND>), grid, block, 0, s, p); break;
     case 3: hipLaunchKernelGGL((og::mfma_kernel<MODE, 128, 128, 2, 2, KIND>), grid, block, 0, s, p); break;
     case 4: hipLaunchKernelGGL((og::mfma_kernel<MODE, 64, 128, 2, 2, KIND>), grid, block, 0, s, p); break;
-    default: hipLaunchKernelGGL((og::mfma_kernel<MODE, 32, 256, 1, 4, KIND>), grid, block, 0, s, p); break;
+    case 5: hipLaunchKernelGGL((og::mfma_kernel<MODE, 32, 256, 1, 4, KIND>), grid, block, 0, s, p); break;
+    case 6: hipLaunchKernelGGL((og::lane_kernel<MODE, KIND, 1, 4>), grid, block, 0, s, p, p.A); break;
+    case 7: hipLaunchKernelGGL((og::lane_kernel<MODE, KIND, 2, 4>), grid, block, 0, s, p, p.A); break;
+    case 8: hipLaunchKernelGGL((og::lane_kernel<MODE, KIND, 4, 4>), grid, block, 0, s, p, p.A); break;
+    default: hipLaunchKernelGGL((og::lane_kernel<MODE, KIND, 8, 4>), grid, block, 0, s, p, p.A); break;
   }
 }
 
@@ -131,8 +162,8 @@ void launch(int mode, const Tile &t, const og::Problem &p, hipStream_t s) {
     launch_tile<og::kFast, KIND>(t, p, s);
 }
 
-const Tile &pick(int64_t M, int64_t N, int64_t groups) {
-  return t_variant == 0 ? choose_tile(M, N, groups) : tile_for_variant(t_variant);
+const Tile &pick(int64_t M, int64_t N, int64_t K, int64_t groups, int mode, bool gather) {
+  return t_variant == 0 ? choose_tile(M, N, K, groups, mode, gather) : tile_for_variant(t_variant);
 }
 
 bool grid_fits(const Tile &t, int64_t M, int64_t N, int64_t groups) {
@@ -161,7 +192,7 @@ og_status og_gemm_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_t l
     return fail(OG_ERR_INVALID_ARG, "og_gemm_f32: A or B is null");
   if (m > kI32Max || n > kI32Max || k > kI32Max)
     return fail(OG_ERR_TOO_LARGE, "og_gemm_f32: a dimension exceeds 2^31-1");
-  const Tile &t = pick(m, n, 1);
+  const Tile &t = pick(m, n, k, 1, mode, false);
   if (!grid_fits(t, m, n, 1)) return fail(OG_ERR_TOO_LARGE, "og_gemm_f32: too many tiles");
   og_status st = check_device();
   if (st != OG_OK) return st;
@@ -221,7 +252,7 @@ og_status og_conv2d_f32_ex(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t
     if (d > kI32Max) return fail(OG_ERR_TOO_LARGE, "og_conv2d_f32: a dimension exceeds 2^31-1");
   const bool planes = KH == 1 && KW == 1 && strideH == 1 && strideW == 1 && padTop == 0 &&
                       padLeft == 0 && padBottom == 0 && padRight == 0;
-  const Tile &t = pick(cout_g, ncols, G);
+  const Tile &t = pick(cout_g, ncols, K, G, mode, !planes);
   if (!grid_fits(t, cout_g, ncols, G)) return fail(OG_ERR_TOO_LARGE, "og_conv2d_f32: too many tiles");
   og_status st = check_device();
   if (st != OG_OK) return st;
@@ -274,8 +305,8 @@ og_status og_set_stream(void *hip_stream) {
 void *og_get_stream(void) { return t_stream; }
 
 og_status og_set_variant(int variant) {
-  if (variant < 0 || variant > 5)
-    return fail(OG_ERR_INVALID_ARG, "og_set_variant: %d is not in 0..5", variant);
+  if (variant < 0 || variant > kNumVariants)
+    return fail(OG_ERR_INVALID_ARG, "og_set_variant: %d is not in 0..%d", variant, kNumVariants);
   t_variant = variant;
   return ok();
 }

@@ -418,4 +418,99 @@ __global__ void __launch_bounds__(256) valu_kernel(Problem p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Lane kernel, for shapes with few outputs and long k (the deep layers of a
+// convolution network at batch 1, short matrix products): the matrix-core
+// instructions take 64 (32x32x1) or ~13 (4x4x1) cycles per dependent k step,
+// a VALU fused multiply-add about 5.  Lane l of a wave owns output column
+// n0 + l for the wave's R output rows; the R weights of a k step are the
+// same for every lane and come through the scalar cache into SGPRs; the B
+// value of the step is read from the LDS tile all W waves of the block
+// share (staged like the matrix-core kernel's, zero padding included).
+// ---------------------------------------------------------------------------
+template <int MODE, int KIND, int R, int W>
+__global__ void __launch_bounds__(64 * W) lane_kernel(Problem p, const float *__restrict__ Aw) {
+  constexpr int NT = 64 * W, BK = 32, BN = 64;
+  __shared__ __align__(16) float Bs[2][BK * BN];
+
+  const TileCoord tc = tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = tc.tn * BN;
+  const int row0 = tc.tm * (R * W) + wave * R;
+
+  BLoader<BN, BK, NT, KIND> bl;
+  bl.init(p, tc.g, n0, tid);
+  float rb[BLoader<BN, BK, NT, KIND>::kPer];
+
+  // Weight rows of this wave; a row beyond M reads row M-1 and is never stored.
+  const float *arow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int row = min(row0 + r, p.M - 1);
+    arow[r] = Aw + tc.g * p.a_gstride + (int64_t)row * p.lda;
+  }
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+
+  const int nchunks = (p.K + BK - 1) / BK;
+  if (nchunks > 0) {
+    bl.load(p, 0, rb);
+    bl.store(Bs[0], rb);
+  }
+  __syncthreads();
+  for (int kc = 0; kc < nchunks; ++kc) {
+    const int cur = kc & 1;
+    const bool more = kc + 1 < nchunks;
+    if (more) bl.load(p, (kc + 1) * BK, rb);
+    const int k0 = kc * BK;
+    const float *bs = Bs[cur];
+    if (k0 + BK <= p.K) {
+#pragma unroll
+      for (int kk = 0; kk < BK; ++kk) {
+        const float b = bs[kk * BN + lane];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float a = arow[r][k0 + kk];
+          if (MODE == kFast) {
+            acc[r] = __builtin_fmaf(a, b, acc[r]);
+          } else {
+            const float prod = a * b;
+            acc[r] = acc[r] + prod;
+          }
+        }
+      }
+    } else {
+      // last, partial chunk: taps at or beyond K are +0 in both operands
+#pragma unroll
+      for (int kk = 0; kk < BK; ++kk) {
+        const float b = bs[kk * BN + lane];
+        const bool kin = k0 + kk < p.K;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float av = arow[r][kin ? k0 + kk : 0];
+          const float a = kin ? av : 0.0f;
+          if (MODE == kFast) {
+            acc[r] = __builtin_fmaf(a, b, acc[r]);
+          } else {
+            const float prod = a * b;
+            acc[r] = acc[r] + prod;
+          }
+        }
+      }
+    }
+    if (more) bl.store(Bs[cur ^ 1], rb);
+    __syncthreads();
+  }
+  const int col = n0 + lane;
+  if (col < p.N) {
+    float *base = out_ptr<KIND>(p, tc.g, 0, col);
+    const int64_t rstride = KIND == kBMatrix ? p.ldc : (int64_t)p.OHW;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (row0 + r < p.M) base[(row0 + r) * rstride] = canonical(acc[r]);
+  }
+}
+
 }  // namespace og

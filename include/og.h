@@ -124,11 +124,12 @@ void *og_get_stream(void);
 
 /*
  * Kernel variant for the calling thread's later calls, for tests that check
- * the results do not depend on it ("Exact mode", rule 5): 0 = chosen from
- * the shape (the default); 1 = the VALU tile kernel; 2, 3, 4 = the matrix-core
- * kernel with 128x256, 128x128 and 64x128 output tiles; 5 = the matrix-core
- * kernel with 32x256 tiles.  A value outside 0..5 returns OG_ERR_INVALID_ARG.
- * Shapes a variant cannot run fall back to the automatic choice.
+ * that the results do not depend on it ("Exact mode", rule 5): 0 = chosen
+ * from the shape (the default); 1 = the VALU tile kernel (64x64 tiles);
+ * 2, 3, 4, 5 = the matrix-core kernel with 128x256, 128x128, 64x128 and
+ * 32x256 output tiles; 6, 7, 8, 9 = the lane kernel (one output column per
+ * lane) with 1, 2, 4, 8 output rows per wave.  Every variant runs every
+ * shape.  A value outside 0..9 returns OG_ERR_INVALID_ARG.
  */
 og_status og_set_variant(int variant);
 int og_get_variant(void);
