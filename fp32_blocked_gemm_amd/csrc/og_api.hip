@@ -135,32 +135,80 @@ const Tile &choose_tile(int64_t M, int64_t N, int64_t K, int64_t groups, int mod
   return tile_for_variant(best);
 }
 
-template <int MODE, int KIND>
+// Lane variants of a 3x3 or a 1x1 (strided or padded) convolution run the
+// lane kernel specialised for that kernel size; its column tiles are 64
+// output pixels of one image.
+template <int MODE, int KH, int KW>
+void launch_lane_conv(int variant, og::Problem p, hipStream_t s) {
+  const int tpi = (int)ceil_div(p.OHW, 64);
+  const int rpb = 4 * (variant == 6 ? 1 : variant == 7 ? 2 : variant == 8 ? 4 : 8);
+  p.tiles_m = (int)ceil_div(p.M, rpb);
+  p.tiles_n = (p.N / p.OHW) * tpi;
+  const unsigned blocks = (unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)p.groups;
+  const dim3 grid(blocks), block(256);
+  switch (variant) {
+    case 6: hipLaunchKernelGGL((og::lane_conv_kernel<MODE, KH, KW, 1, 4, 8>), grid, block, 0, s, p); break;
+    case 7: hipLaunchKernelGGL((og::lane_conv_kernel<MODE, KH, KW, 2, 4, 8>), grid, block, 0, s, p); break;
+    case 8: hipLaunchKernelGGL((og::lane_conv_kernel<MODE, KH, KW, 4, 4, 2>), grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL((og::lane_conv_kernel<MODE, KH, KW, 8, 4, 2>), grid, block, 0, s, p); break;
+  }
+}
+
+// D: register-ring depth of the staged loads (chunks in flight).
+template <int MODE, int KIND, bool AV, bool BV>
 void launch_tile(const Tile &t, og::Problem p, hipStream_t s) {
-  p.tiles_m = (int)ceil_div(p.M, t.bm);
-  p.tiles_n = (int)ceil_div(p.N, t.bn);
+  if (KIND == og::kBGather && is_lane(t)) {
+    if (p.KH == 3 && p.KW == 3) return launch_lane_conv<MODE, 3, 3>(t.variant, p, s);
+    if (p.KH == 1 && p.KW == 1) return launch_lane_conv<MODE, 1, 1>(t.variant, p, s);
+  }
+  const Tile &tt = (MODE == og::kExact && t.variant == 2) ? tile_for_variant(3) : t;
+  p.tiles_m = (int)ceil_div(p.M, tt.bm);
+  p.tiles_n = (int)ceil_div(p.N, tt.bn);
   const unsigned blocks = (unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)p.groups;
   const dim3 grid(blocks), block(256);
   switch (t.variant) {
     case 1: hipLaunchKernelGGL((og::valu_kernel<MODE, KIND>), grid, block, 0, s, p); break;
-    case 2: hipLaunchKernelGGL((og::mfma_kernel<MODE, 128, 256, 2, 2, KIND>), grid, block, 0, s, p); break;
-    case 3: hipLaunchKernelGGL((og::mfma_kernel<MODE, 128, 128, 2, 2, KIND>), grid, block, 0, s, p); break;
-    case 4: hipLaunchKernelGGL((og::mfma_kernel<MODE, 64, 128, 2, 2, KIND>), grid, block, 0, s, p); break;
-    case 5: hipLaunchKernelGGL((og::mfma_kernel<MODE, 32, 256, 1, 4, KIND>), grid, block, 0, s, p); break;
-    case 6: hipLaunchKernelGGL((og::lane_kernel<MODE, KIND, 1, 4>), grid, block, 0, s, p, p.A); break;
-    case 7: hipLaunchKernelGGL((og::lane_kernel<MODE, KIND, 2, 4>), grid, block, 0, s, p, p.A); break;
-    case 8: hipLaunchKernelGGL((og::lane_kernel<MODE, KIND, 4, 4>), grid, block, 0, s, p, p.A); break;
-    default: hipLaunchKernelGGL((og::lane_kernel<MODE, KIND, 8, 4>), grid, block, 0, s, p, p.A); break;
+    case 2:
+      // exact mode keeps its products beside 128 accumulators per lane: with
+      // 128x256 tiles that leaves one wave per SIMD, so it runs 128x128 tiles
+      if constexpr (MODE == og::kExact)
+        hipLaunchKernelGGL((og::mfma_kernel<MODE, 128, 128, 2, 2, KIND, AV, BV, 2>), grid, block, 0, s, p);
+      else
+        hipLaunchKernelGGL((og::mfma_kernel<MODE, 128, 256, 2, 2, KIND, AV, BV, 2>), grid, block, 0, s, p);
+      break;
+    case 3: hipLaunchKernelGGL((og::mfma_kernel<MODE, 128, 128, 2, 2, KIND, AV, BV, 2>), grid, block, 0, s, p); break;
+    case 4: hipLaunchKernelGGL((og::mfma_kernel<MODE, 64, 128, 2, 2, KIND, AV, BV, 4>), grid, block, 0, s, p); break;
+    case 5: hipLaunchKernelGGL((og::mfma_kernel<MODE, 32, 256, 1, 4, KIND, AV, BV, 4>), grid, block, 0, s, p); break;
+    case 6: hipLaunchKernelGGL((og::lane_kernel<MODE, KIND, 1, 4, 8>), grid, block, 0, s, p); break;
+    case 7: hipLaunchKernelGGL((og::lane_kernel<MODE, KIND, 2, 4, 8>), grid, block, 0, s, p); break;
+    case 8: hipLaunchKernelGGL((og::lane_kernel<MODE, KIND, 4, 4, 4>), grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL((og::lane_kernel<MODE, KIND, 8, 4, 2>), grid, block, 0, s, p); break;
   }
 }
 
-template <int KIND>
-void launch(int mode, const Tile &t, const og::Problem &p, hipStream_t s) {
-  if (mode == OG_MODE_EXACT)
-    launch_tile<og::kExact, KIND>(t, p, s);
+// AV / BV: 16-byte loads of A rows / B rows (every address and every
+// row length a multiple of 16 bytes, so no load crosses the end of a row).
+template <int MODE, int KIND>
+void launch_vec(bool av, bool bv, const Tile &t, const og::Problem &p, hipStream_t s) {
+  if (av && bv)
+    launch_tile<MODE, KIND, true, true>(t, p, s);
+  else if (av)
+    launch_tile<MODE, KIND, true, false>(t, p, s);
+  else if (bv)
+    launch_tile<MODE, KIND, false, true>(t, p, s);
   else
-    launch_tile<og::kFast, KIND>(t, p, s);
+    launch_tile<MODE, KIND, false, false>(t, p, s);
 }
+
+template <int KIND>
+void launch(int mode, bool av, bool bv, const Tile &t, const og::Problem &p, hipStream_t s) {
+  if (mode == OG_MODE_EXACT)
+    launch_vec<og::kExact, KIND>(av, bv, t, p, s);
+  else
+    launch_vec<og::kFast, KIND>(av, bv, t, p, s);
+}
+
+bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15) == 0; }
 
 const Tile &pick(int64_t M, int64_t N, int64_t K, int64_t groups, int mode, bool gather) {
   return t_variant == 0 ? choose_tile(M, N, K, groups, mode, gather) : tile_for_variant(t_variant);
@@ -192,6 +240,9 @@ og_status og_gemm_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_t l
     return fail(OG_ERR_INVALID_ARG, "og_gemm_f32: A or B is null");
   if (m > kI32Max || n > kI32Max || k > kI32Max)
     return fail(OG_ERR_TOO_LARGE, "og_gemm_f32: a dimension exceeds 2^31-1");
+  // the kernels address a tile's rows with 32-bit byte offsets
+  if (lda > (int64_t(1) << 22) || ldb > (int64_t(1) << 22))
+    return fail(OG_ERR_TOO_LARGE, "og_gemm_f32: lda or ldb exceeds 2^22");
   const Tile &t = pick(m, n, k, 1, mode, false);
   if (!grid_fits(t, m, n, 1)) return fail(OG_ERR_TOO_LARGE, "og_gemm_f32: too many tiles");
   og_status st = check_device();
@@ -208,7 +259,9 @@ og_status og_gemm_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_t l
   p.N = (int)n;
   p.K = (int)k;
   p.groups = 1;
-  launch<og::kBMatrix>(mode, t, p, t_stream);
+  const bool av = aligned16(A) && lda % 4 == 0 && k % 4 == 0;
+  const bool bv = aligned16(B) && ldb % 4 == 0 && n % 4 == 0;
+  launch<og::kBMatrix>(mode, av, bv, t, p, t_stream);
   return check_launch("og_gemm_f32");
 }
 
@@ -250,6 +303,9 @@ og_status og_conv2d_f32_ex(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t
                           KH * dilH + H, KW * dilW + W};
   for (int64_t d : dims)
     if (d > kI32Max) return fail(OG_ERR_TOO_LARGE, "og_conv2d_f32: a dimension exceeds 2^31-1");
+  // the kernels address the input with 32-bit byte offsets
+  if (N * Cin * H * W > (int64_t(1) << 29))
+    return fail(OG_ERR_TOO_LARGE, "og_conv2d_f32: the input exceeds 2^29 elements");
   const bool planes = KH == 1 && KW == 1 && strideH == 1 && strideW == 1 && padTop == 0 &&
                       padLeft == 0 && padBottom == 0 && padRight == 0;
   const Tile &t = pick(cout_g, ncols, K, G, mode, !planes);
@@ -272,6 +328,8 @@ og_status og_conv2d_f32_ex(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t
   p.OW = (int)OW;
   p.OHW = (int)(OH * OW);
   p.KW = (int)KW;
+  p.KH = (int)KH;
+  p.HW = (int)(H * W);
   p.KHW = (int)(KH * KW);
   p.sH = (int)strideH;
   p.sW = (int)strideW;
@@ -283,10 +341,11 @@ og_status og_conv2d_f32_ex(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t
   p.x_grp = cin_g * H * W;
   p.y_img = Cout * OH * OW;
   p.y_grp = cout_g * OH * OW;
+  const bool av = aligned16(w) && K % 4 == 0 && (cout_g * K) % 4 == 0;
   if (planes)
-    launch<og::kBPlanes>(mode, t, p, t_stream);
+    launch<og::kBPlanes>(mode, av, false, t, p, t_stream);
   else
-    launch<og::kBGather>(mode, t, p, t_stream);
+    launch<og::kBGather>(mode, av, false, t, p, t_stream);
   return check_launch("og_conv2d_f32");
 }
 

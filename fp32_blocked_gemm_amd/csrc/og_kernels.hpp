@@ -23,18 +23,23 @@
 // acc + prod because acc is never -0) and adds it on the VALU with a
 // separately rounded v_add_f32.
 //
-// Operands are staged through LDS in k-chunks of BK: the A tile (weights, or
-// the left matrix) and the B tile (the right matrix, or the convolution's
-// input patches gathered on the fly with the zero padding written during the
-// gather; "Convolution (fast mode)", section "Layout of the work").  Rows,
-// columns and taps beyond the problem are staged as +0 in BOTH operands, so
-// the extra terms are fma(+0, +0, acc) = acc and acc + round(+0 * +0) = acc.
+// Operands are staged through LDS in k-chunks: the A tile (weights, or the
+// left matrix) and the B tile (the right matrix, or the convolution's input
+// patches gathered on the fly with the zero padding written during the
+// gather; "Convolution (fast mode)", section "Layout of the work").  The
+// global loads of a chunk are issued D-1 chunks ahead into a ring of
+// registers, so their latency hides behind the products of the chunks in
+// between.  Rows, columns and taps beyond the problem are staged as +0 in
+// BOTH operands, so the extra terms are fma(+0, +0, acc) = acc and
+// acc + round(+0 * +0) = acc.
 //
 // All code is compiled with -ffp-contract=off and with fp32 denormals on.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <utility>
 
 namespace og {
 
@@ -63,10 +68,20 @@ struct Problem {
   int M, N, K, groups;
   int tiles_m, tiles_n;
   // convolution only
-  int H, W, OW, OHW, KW, KHW, sH, sW, pT, pL, dH, dW;
+  int H, W, HW, OW, OHW, KH, KW, KHW, sH, sW, pT, pL, dH, dW;
   int64_t x_img, x_grp;  // element strides of x between images and between groups
   int64_t y_img, y_grp;  // element strides of y between images and between groups
 };
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = 0..N-1.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // ---------------------------------------------------------------------------
 // Workgroup -> tile.  Workgroups are handed to the 8 XCDs of the chip in
@@ -104,108 +119,210 @@ __device__ inline float canonical(float v) {
 }
 
 // ---------------------------------------------------------------------------
-// Staging of one k-chunk.  A: thread -> (row r0 + q*rstep, tap c); coalesced
-// along k.  B: thread -> (column, taps kk0 + q*kstep); coalesced along the
-// columns.  Values go to registers first, then to the LDS buffer not being
-// read, so the global loads of chunk c+1 overlap the products of chunk c.
+// Loads.  Every staged operand is read with raw buffer loads: a 32-bit byte
+// offset from a base held in scalar registers.  A load whose element lies
+// outside the problem uses the offset kOutside, beyond the buffer's range,
+// and the hardware returns +0 for it; no select after the load, and no
+// branch around it, so every chunk issues the same loads and the waits for
+// them can be counted exactly D-1 chunks later.
 // ---------------------------------------------------------------------------
-template <int BM, int BK, int NT>
-struct ALoader {
-  static constexpr int kPer = BM * BK / NT;
-  static constexpr int kRstep = NT / BK;
-  const float *ptr;  // row r0, tap c of chunk 0
-  int64_t row_step;  // kRstep rows
-  int c, r0, rows_left;
+// kOutside + 16 must not wrap around 2^32, or a 16-byte load would pass the
+// range check.
+constexpr uint32_t kRange = 0xFFFFFF00u;    // range of a staging buffer, in bytes
+constexpr uint32_t kOutside = kRange;       // an offset at or past the range: the load returns +0
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_at(const float *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ float load1(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+}
+// The whole vector is reinterpreted before its elements are taken: taking
+// them one by one from the integer vector made this compiler shrink the load
+// to a single dword.
+__device__ __forceinline__ void load4(__amdgpu_buffer_rsrc_t rs, uint32_t off, float *r) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+  r[0] = v.x;
+  r[1] = v.y;
+  r[2] = v.z;
+  r[3] = v.w;
+}
+
+// ---------------------------------------------------------------------------
+// A staging: rows of A (k contiguous), BM rows x BK taps per chunk, into a
+// k-major LDS tile As[kk*LDA + row].  VEC: 16-byte loads of 4 taps (A
+// 16-byte aligned, lda, the group stride and K multiples of 4, so a load is
+// wholly inside or wholly outside the problem).
+// ---------------------------------------------------------------------------
+template <int BM, int BK, int NT, bool VEC>
+struct AStage {
+  static constexpr int KV = VEC ? 4 : 1;      // taps per load
+  static constexpr int LPR = BK / KV;         // loads per row and chunk
+  static constexpr int RSTEP = NT / LPR;      // rows between a thread's loads
+  static constexpr int NQ = BM / RSTEP;       // loads per thread and chunk
+  static constexpr int kRegs = NQ * KV;
+  static_assert(NT % LPR == 0 && BM % RSTEP == 0 && NQ >= 1, "A staging shape");
+
+  const float *blk;     // A_g row m0, tap 0
+  uint32_t voff[NQ];    // byte offset of (row r0 + q*RSTEP, tap kc) from blk; kOutside past M
+  int kc, r0;
 
   __device__ void init(const Problem &p, int g, int m0, int tid) {
-    c = tid % BK;
-    r0 = tid / BK;
-    rows_left = p.M - m0 - r0;  // row q is valid when q*kRstep < rows_left
-    ptr = p.A + g * p.a_gstride + (int64_t)(m0 + r0) * p.lda + c;
-    row_step = (int64_t)kRstep * p.lda;
-  }
-  __device__ void load(const Problem &p, int k0, float (&r)[kPer]) const {
-    const bool kin = k0 + c < p.K;
+    kc = (tid % LPR) * KV;
+    r0 = tid / LPR;
+    blk = p.A + g * p.a_gstride + (int64_t)m0 * p.lda;
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      const bool ok = kin && q * kRstep < rows_left;
-      const float v = *(ok ? ptr + q * row_step + k0 : p.A);  // p.A: any readable element
-      r[q] = ok ? v : 0.0f;
+    for (int q = 0; q < NQ; ++q)
+      voff[q] = m0 + r0 + q * RSTEP < p.M ? (uint32_t)(4 * ((r0 + q * RSTEP) * p.lda + kc))
+                                          : kOutside;
+  }
+  __device__ void load(const Problem &p, int k0, float (&r)[kRegs]) const {
+    const __amdgpu_buffer_rsrc_t rs = buffer_at(blk + k0, kRange);
+    const bool kin = k0 + kc < p.K;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const uint32_t o = kin ? voff[q] : kOutside;
+      if (VEC)
+        load4(rs, o, &r[q * 4]);
+      else
+        r[q] = load1(rs, o);
     }
   }
-  template <int LDA_STRIDE>
-  __device__ void store(float *lds, const float (&r)[kPer]) const {
+  template <int LDA>
+  __device__ void store(float *lds, const float (&r)[kRegs]) const {
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) lds[c * LDA_STRIDE + r0 + q * kRstep] = r[q];
+    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+      for (int e = 0; e < KV; ++e) lds[(kc + e) * LDA + r0 + q * RSTEP] = r[q * KV + e];
   }
 };
 
-template <int BN, int BK, int NT, int KIND>
-struct BLoader {
-  static constexpr int kPer = BN * BK / NT;
-  static constexpr int kKstep = NT / BN;
-  int col, kk0;
+// ---------------------------------------------------------------------------
+// B staging: BK taps x BN columns per chunk into Bs[kk*BN + col].
+//  * matrix, VEC: 16-byte loads of 4 columns (B 16-byte aligned, ldb and N
+//    multiples of 4);
+//  * matrix scalar, planes, gather: thread -> one column and TPG consecutive
+//    taps.  The gather decodes its first tap (c, ky, kx) once per chunk with
+//    wave-uniform (scalar) arithmetic and steps the following taps
+//    incrementally; a tap outside the input plane reads +0.
+// ---------------------------------------------------------------------------
+template <int BN, int BK, int NT, int KIND, bool VEC>
+struct BStage {
+  static constexpr bool V = VEC && KIND == kBMatrix;
+  static constexpr int C4 = BN / 4;                       // float4 per k-row
+  static constexpr int VRSTEP = V ? NT / C4 : 1;          // k-rows between a thread's loads
+  static constexpr int VNQ = V ? BK / VRSTEP : 1;
+  static constexpr int TPG = BK * BN / NT;                // scalar: taps per thread
+  static constexpr int NV = V ? VNQ : (KIND == kBMatrix ? TPG : 1);
+  static constexpr int kRegs = V ? VNQ * 4 : TPG;
+  static_assert(V ? (NT % C4 == 0 && BK % VRSTEP == 0) : (NT % BN == 0 && TPG >= 1),
+                "B staging shape");
+
+  int col, t0;        // column in the tile; first tap (scalar) or k-row (vector) of this thread
   bool col_ok;
-  int64_t base;  // per-thread element offset of the column's data
-  int iy0, ix0;  // gather: top-left input position of the column's window
+  const float *base;  // matrix: B + n0; conv: x + g*x_grp
+  uint32_t voff[NV];  // matrix: byte offsets of this thread's elements of a chunk; kOutside past N
+  int e0;             // conv: element offset of this column's (image, window origin) in base
+  int iy0, ix0;       // gather: window origin of this column's output pixel
 
   __device__ void init(const Problem &p, int g, int n0, int tid) {
+    if (V) {
+      col = 4 * (tid % C4);
+      t0 = tid / C4;
+      col_ok = n0 + col < p.N;
+      base = p.B + n0;
+#pragma unroll
+      for (int q = 0; q < VNQ; ++q)
+        voff[q] = col_ok ? (uint32_t)(4 * ((t0 + q * VRSTEP) * p.ldb + col)) : kOutside;
+      return;
+    }
     col = tid % BN;
-    kk0 = __builtin_amdgcn_readfirstlane(tid / BN);  // uniform in a wave (BN >= 64)
+    t0 = __builtin_amdgcn_readfirstlane((tid / BN) * TPG);  // wave-uniform (BN >= 64)
     const int j = n0 + col;
     col_ok = j < p.N;
     if (KIND == kBMatrix) {
-      base = j;
+      base = p.B + n0;
+#pragma unroll
+      for (int q = 0; q < TPG; ++q)
+        voff[q] = col_ok ? (uint32_t)(4 * ((t0 + q) * p.ldb + col)) : kOutside;
+      return;
+    }
+    const int jj = col_ok ? j : 0;
+    const int img = jj / p.OHW;
+    const int pix = jj - img * p.OHW;
+    base = p.B + g * p.x_grp;
+    if (KIND == kBPlanes) {
+      e0 = (int)(img * p.x_img) + pix;
     } else {
-      const int jj = col_ok ? j : 0;
-      const int img = jj / p.OHW;
-      const int pix = jj - img * p.OHW;
-      if (KIND == kBPlanes) {
-        base = img * p.x_img + g * p.x_grp + pix;
-      } else {
-        const int oy = pix / p.OW;
-        const int ox = pix - oy * p.OW;
-        iy0 = oy * p.sH - p.pT;
-        ix0 = ox * p.sW - p.pL;
-        base = img * p.x_img + g * p.x_grp + (int64_t)iy0 * p.W + ix0;
+      const int oy = pix / p.OW;
+      const int ox = pix - oy * p.OW;
+      iy0 = oy * p.sH - p.pT;
+      ix0 = ox * p.sW - p.pL;
+      e0 = (int)(img * p.x_img) + iy0 * p.W + ix0;
+    }
+  }
+
+  __device__ void load(const Problem &p, int k0, float (&r)[kRegs]) const {
+    if (V) {
+      const __amdgpu_buffer_rsrc_t rs = buffer_at(base + (int64_t)k0 * p.ldb, kRange);
+#pragma unroll
+      for (int q = 0; q < VNQ; ++q)
+        load4(rs, k0 + t0 + q * VRSTEP < p.K ? voff[q] : kOutside, &r[q * 4]);
+      return;
+    }
+    const int t = k0 + t0;  // first tap of this thread (wave-uniform)
+    if (KIND == kBMatrix) {
+      const __amdgpu_buffer_rsrc_t rs = buffer_at(base + (int64_t)k0 * p.ldb, kRange);
+#pragma unroll
+      for (int q = 0; q < TPG; ++q) r[q] = load1(rs, t + q < p.K ? voff[q] : kOutside);
+      return;
+    }
+    const __amdgpu_buffer_rsrc_t rs = buffer_at(base, kRange);
+    if (KIND == kBPlanes) {
+#pragma unroll
+      for (int q = 0; q < TPG; ++q) {
+        const bool ok = col_ok && t + q < p.K;  // plane t+q of the group
+        r[q] = load1(rs, ok ? (uint32_t)(4 * (e0 + (t + q) * p.HW)) : kOutside);
+      }
+      return;
+    }
+    // gather: tap t -> (c, ky, kx) once, then step through the following taps
+    int c = t / p.KHW;
+    const int rr = t - c * p.KHW;
+    int ky = rr / p.KW;
+    int kx = rr - ky * p.KW;
+#pragma unroll
+    for (int q = 0; q < TPG; ++q) {
+      const int dy = ky * p.dH, dx = kx * p.dW;
+      const bool ok = col_ok && t + q < p.K && (unsigned)(iy0 + dy) < (unsigned)p.H &&
+                      (unsigned)(ix0 + dx) < (unsigned)p.W;  // outside the plane: padding, +0
+      r[q] = load1(rs, ok ? (uint32_t)(4 * (e0 + c * p.HW + dy * p.W + dx)) : kOutside);
+      if (++kx == p.KW) {
+        kx = 0;
+        if (++ky == p.KH) {
+          ky = 0;
+          ++c;
+        }
       }
     }
   }
-  __device__ void load(const Problem &p, int k0, float (&r)[kPer]) const {
+
+  __device__ void store(float *lds, const float (&r)[kRegs]) const {
+    if (V) {
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      const int t = k0 + kk0 + q * kKstep;  // wave-uniform tap index
-      // The load always runs, from p.B (any readable element) when the
-      // element is outside the problem, and its value is then replaced by +0.
-      bool ok = col_ok && t < p.K;
-      int64_t off = 0;
-      if (KIND == kBMatrix) {
-        off = base + (int64_t)t * p.ldb;
-      } else if (KIND == kBPlanes) {
-        off = base + (int64_t)t * p.OHW;  // plane t of the group
-      } else {
-        // tap t -> (c, ky, kx): channel, kernel row, kernel column
-        const int c = t / p.KHW;
-        const int rr = t - c * p.KHW;
-        const int ky = rr / p.KW;
-        const int kx = rr - ky * p.KW;
-        const int dy = ky * p.dH, dx = kx * p.dW;
-        const bool inside = (unsigned)(iy0 + dy) < (unsigned)p.H &&
-                            (unsigned)(ix0 + dx) < (unsigned)p.W;
-        ok = ok && inside;  // outside the plane: a padding tap, +0
-        off = base + (int64_t)c * p.H * p.W + (int64_t)dy * p.W + dx;
-      }
-      const float v = p.B[ok ? off : 0];
-      r[q] = ok ? v : 0.0f;
+      for (int q = 0; q < VNQ; ++q)
+        *reinterpret_cast<float4 *>(&lds[(t0 + q * VRSTEP) * BN + col]) =
+            make_float4(r[q * 4 + 0], r[q * 4 + 1], r[q * 4 + 2], r[q * 4 + 3]);
+      return;
     }
-  }
-  __device__ void store(float *lds, const float (&r)[kPer]) const {
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) lds[(kk0 + q * kKstep) * BN + col] = r[q];
+    for (int q = 0; q < TPG; ++q) lds[(t0 + q) * BN + col] = r[q];
   }
 };
 
-// Pointer to output (row, col) of group g, or nullptr outside the problem.
+// Pointer to output (row, col) of group g.
 template <int KIND>
 __device__ inline float *out_ptr(const Problem &p, int g, int row, int col) {
   if (KIND == kBMatrix) return p.C + (int64_t)row * p.ldc + col;
@@ -215,12 +332,50 @@ __device__ inline float *out_ptr(const Problem &p, int g, int row, int col) {
 }
 
 // ---------------------------------------------------------------------------
+// The staging pipeline.  Chunk c's loads go to register slot c % D, D-1
+// chunks ahead of its use; at its turn the slot is written to LDS buffer
+// c % 2, one barrier, then the chunk's products.  One barrier per chunk is
+// enough with two LDS buffers: a wave writing buffer c % 2 has passed the
+// barrier of chunk c-1, so every wave has finished reading chunk c-2 there.
+// The main loop runs whole groups of D chunks and issues every load
+// unconditionally (past the last chunk it reloads the last one), so each
+// wait is for loads issued D-1 chunks earlier; the remaining chunks are
+// consumed without further loads.
+// ---------------------------------------------------------------------------
+template <int D, class Load, class Store, class Compute>
+__device__ __forceinline__ void run_pipeline(int nchunks, Load &&load, Store &&store,
+                                             Compute &&compute) {
+  static_assert(D >= 2 && D % 2 == 0, "pipeline depth");
+  if (nchunks <= 0) return;
+  const int last = nchunks - 1;
+  static_for<D - 1>([&](auto j) { load(min((int)decltype(j)::value, last), j); });
+  const int full = nchunks - nchunks % D;
+  for (int c0 = 0; c0 < full; c0 += D) {
+    static_for<D>([&](auto j) {
+      constexpr int J = decltype(j)::value;
+      load(min(c0 + J + D - 1, last), std::integral_constant<int, (J + D - 1) % D>{});
+      store(j, std::integral_constant<int, J % 2>{});
+      __syncthreads();
+      compute(c0 + J, std::integral_constant<int, J % 2>{}, j);
+    });
+  }
+  static_for<D - 1>([&](auto j) {
+    constexpr int J = decltype(j)::value;
+    if (full + J < nchunks) {
+      store(j, std::integral_constant<int, J % 2>{});
+      __syncthreads();
+      compute(full + J, std::integral_constant<int, J % 2>{}, j);
+    }
+  });
+}
+
+// ---------------------------------------------------------------------------
 // Matrix-core kernel.  256 threads = 4 waves arranged WM x WN; a wave owns a
 // (TM*32) x (TN*64) sub-tile as TM x TN blocks of 32 x 64 outputs, each block
 // one 32x32x1 MFMA pair-of-blocks: lanes 0-31 and 32-63 both carry the 32 A
 // rows, lanes 0-31 carry B columns 0-31 and lanes 32-63 columns 32-63.
 // ---------------------------------------------------------------------------
-template <int MODE, int BM, int BN, int WM, int WN, int KIND>
+template <int MODE, int BM, int BN, int WM, int WN, int KIND, bool AVEC, bool BVEC, int D>
 __global__ void __launch_bounds__(256) mfma_kernel(Problem p) {
   constexpr int NT = 256, BK = 16;
   constexpr int TM = BM / WM / 32, TN = BN / WN / 64;
@@ -228,92 +383,94 @@ __global__ void __launch_bounds__(256) mfma_kernel(Problem p) {
   constexpr int LDA = BM + 1;  // k-major A tile, padded against bank conflicts of the transposing store
   __shared__ __align__(16) float As[2][BK * LDA];
   __shared__ __align__(16) float Bs[2][BK * BN];
+  // 16-byte loads only where every thread has at least one of them
+  using AS = AStage<BM, BK, NT, AVEC && (BM * BK / 4 >= NT)>;
+  using BS = BStage<BN, BK, NT, KIND, BVEC && (BN * BK / 4 >= NT)>;
 
   const TileCoord tc = tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n);
   const int m0 = tc.tm * BM, n0 = tc.tn * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
-  ALoader<BM, BK, NT> al;
-  BLoader<BN, BK, NT, KIND> bl;
-  al.init(p, tc.g, m0, tid);
-  bl.init(p, tc.g, n0, tid);
-  float ra[ALoader<BM, BK, NT>::kPer];
-  float rb[BLoader<BN, BK, NT, KIND>::kPer];
+  AS as;
+  BS bs;
+  as.init(p, tc.g, m0, tid);
+  bs.init(p, tc.g, n0, tid);
+  float ra[D][AS::kRegs];
+  float rb[D][BS::kRegs];
 
   f32x32 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x32{};
-
-  const int nchunks = (p.K + BK - 1) / BK;
-  if (nchunks > 0) {
-    al.load(p, 0, ra);
-    bl.load(p, 0, rb);
-    al.template store<LDA>(As[0], ra);
-    bl.store(Bs[0], rb);
-  }
-  __syncthreads();
+  f32x32 pend = f32x32{};  // exact mode: the last product made, added one MFMA later
 
   const int a_off = wm * TM * 32 + (lane & 31);
   const int b_off = wn * TN * 64 + lane;
-  for (int kc = 0; kc < nchunks; ++kc) {
-    const int cur = kc & 1;
-    const bool more = kc + 1 < nchunks;
-    if (more) {
-      al.load(p, (kc + 1) * BK, ra);
-      bl.load(p, (kc + 1) * BK, rb);
-    }
-    const float *as = As[cur];
-    const float *bs = Bs[cur];
-    if (MODE == kFast) {
-      float a[2][TM], b[2][TN];
+
+  run_pipeline<D>(
+      (p.K + BK - 1) / BK,
+      [&](int c, auto slot) {
+        as.load(p, c * BK, ra[decltype(slot)::value]);
+        bs.load(p, c * BK, rb[decltype(slot)::value]);
+      },
+      [&](auto slot, auto buf) {
+        as.template store<LDA>(As[decltype(buf)::value], ra[decltype(slot)::value]);
+        bs.store(Bs[decltype(buf)::value], rb[decltype(slot)::value]);
+      },
+      [&](int, auto buf, auto) {
+        const float *al = As[decltype(buf)::value];
+        const float *bl = Bs[decltype(buf)::value];
+        if (MODE == kExact) {
+          // Exact: a rolled k loop, so only one k's products are live at a
+          // time (unrolled, the compiler makes every product of the chunk
+          // first; they do not depend on the accumulators).  The product
+          // made one MFMA earlier is added while the next one is made.
+#pragma unroll 2
+          for (int kk = 0; kk < BK; ++kk) {
+            float a[TM], b[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) a[0][i] = as[a_off + i * 32];
+            for (int i = 0; i < TM; ++i) a[i] = al[kk * LDA + a_off + i * 32];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) b[0][j] = bs[b_off + j * 64];
+            for (int j = 0; j < TN; ++j) b[j] = bl[kk * BN + b_off + j * 64];
 #pragma unroll
-      for (int kk = 0; kk < BK; ++kk) {
-        const int u = kk & 1;
-        if (kk + 1 < BK) {  // operands of the next k, read while this k's MFMAs run
+            for (int i = 0; i < TM; ++i)
 #pragma unroll
-          for (int i = 0; i < TM; ++i) a[u ^ 1][i] = as[(kk + 1) * LDA + a_off + i * 32];
-#pragma unroll
-          for (int j = 0; j < TN; ++j) b[u ^ 1][j] = bs[(kk + 1) * BN + b_off + j * 64];
-        }
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x1f32(a[u][i], b[u][j], acc[i][j], 0, 0, 0);
-      }
-    } else {
-      // Exact: the rolled k loop keeps the products of one k live at a time
-      // (an unrolled loop lets the compiler make every product of the chunk
-      // first); waves sharing a SIMD overlap one another's MFMAs and adds.
-#pragma unroll 1
-      for (int kk = 0; kk < BK; ++kk) {
-        float a[TM], b[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) a[i] = as[kk * LDA + a_off + i * 32];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) b[j] = bs[kk * BN + b_off + j * 64];
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            const f32x32 prod = __builtin_amdgcn_mfma_f32_32x32x1f32(a[i], b[j], f32x32{}, 0, 0, 0);
-            acc[i][j] += prod;
+              for (int j = 0; j < TN; ++j) {
+                const f32x32 prod =
+                    __builtin_amdgcn_mfma_f32_32x32x1f32(a[i], b[j], f32x32{}, 0, 0, 0);
+                const int s = i * TN + j;
+                const int pi = s == 0 ? TM - 1 : (s - 1) / TN;
+                const int pj = s == 0 ? TN - 1 : (s - 1) % TN;
+                acc[pi][pj] += pend;  // the first pend is +0: acc stays +0
+                pend = prod;
+              }
           }
-      }
-    }
-    if (more) {
-      al.template store<LDA>(As[cur ^ 1], ra);
-      bl.store(Bs[cur ^ 1], rb);
-    }
-    __syncthreads();
-  }
+          return;
+        }
+        float a[2][TM], b[2][TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) a[0][i] = al[a_off + i * 32];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) b[0][j] = bl[b_off + j * 64];
+#pragma unroll
+        for (int kk = 0; kk < BK; ++kk) {
+          const int u = kk & 1;
+          if (kk + 1 < BK) {  // operands of the next k, read while this k's MFMAs run
+#pragma unroll
+            for (int i = 0; i < TM; ++i) a[u ^ 1][i] = al[(kk + 1) * LDA + a_off + i * 32];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) b[u ^ 1][j] = bl[(kk + 1) * BN + b_off + j * 64];
+          }
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x1f32(a[u][i], b[u][j], acc[i][j], 0, 0, 0);
+        }
+      });
+  if (MODE == kExact) acc[TM - 1][TN - 1] += pend;
 
   // Epilogue: accumulator register r of lane l in block pair half h = r/16
   // holds row 8*((r%16)/4) + 4*(l/32) + r%4 and column h*32 + l%32 of the
@@ -343,21 +500,23 @@ __global__ void __launch_bounds__(256) mfma_kernel(Problem p) {
 // ---------------------------------------------------------------------------
 template <int MODE, int KIND>
 __global__ void __launch_bounds__(256) valu_kernel(Problem p) {
-  constexpr int NT = 256, BK = 16, BM = 64, BN = 64;
+  constexpr int NT = 256, BK = 16, BM = 64, BN = 64, D = 2;
   constexpr int LDA = BM + 4;
   __shared__ __align__(16) float As[2][BK * LDA];
   __shared__ __align__(16) float Bs[2][BK * BN];
+  using AS = AStage<BM, BK, NT, false>;
+  using BS = BStage<BN, BK, NT, KIND, false>;
 
   const TileCoord tc = tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n);
   const int m0 = tc.tm * BM, n0 = tc.tn * BN;
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
 
-  ALoader<BM, BK, NT> al;
-  BLoader<BN, BK, NT, KIND> bl;
-  al.init(p, tc.g, m0, tid);
-  bl.init(p, tc.g, n0, tid);
-  float ra[ALoader<BM, BK, NT>::kPer];
-  float rb[BLoader<BN, BK, NT, KIND>::kPer];
+  AS as;
+  BS bs;
+  as.init(p, tc.g, m0, tid);
+  bs.init(p, tc.g, n0, tid);
+  float ra[D][AS::kRegs];
+  float rb[D][BS::kRegs];
 
   float acc[4][4];
 #pragma unroll
@@ -365,45 +524,38 @@ __global__ void __launch_bounds__(256) valu_kernel(Problem p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
 
-  const int nchunks = (p.K + BK - 1) / BK;
-  if (nchunks > 0) {
-    al.load(p, 0, ra);
-    bl.load(p, 0, rb);
-    al.template store<LDA>(As[0], ra);
-    bl.store(Bs[0], rb);
-  }
-  __syncthreads();
-  for (int kc = 0; kc < nchunks; ++kc) {
-    const int cur = kc & 1;
-    const bool more = kc + 1 < nchunks;
-    if (more) {
-      al.load(p, (kc + 1) * BK, ra);
-      bl.load(p, (kc + 1) * BK, rb);
-    }
+  run_pipeline<D>(
+      (p.K + BK - 1) / BK,
+      [&](int c, auto slot) {
+        as.load(p, c * BK, ra[decltype(slot)::value]);
+        bs.load(p, c * BK, rb[decltype(slot)::value]);
+      },
+      [&](auto slot, auto buf) {
+        as.template store<LDA>(As[decltype(buf)::value], ra[decltype(slot)::value]);
+        bs.store(Bs[decltype(buf)::value], rb[decltype(slot)::value]);
+      },
+      [&](int, auto buf, auto) {
+        const float *al = As[decltype(buf)::value];
+        const float *bl = Bs[decltype(buf)::value];
 #pragma unroll
-    for (int kk = 0; kk < BK; ++kk) {
-      const float4 a4 = *reinterpret_cast<const float4 *>(&As[cur][kk * LDA + ty * 4]);
-      const float4 b4 = *reinterpret_cast<const float4 *>(&Bs[cur][kk * BN + tx * 4]);
-      const float a[4] = {a4.x, a4.y, a4.z, a4.w};
-      const float b[4] = {b4.x, b4.y, b4.z, b4.w};
+        for (int kk = 0; kk < BK; ++kk) {
+          const float4 a4 = *reinterpret_cast<const float4 *>(&al[kk * LDA + ty * 4]);
+          const float4 b4 = *reinterpret_cast<const float4 *>(&bl[kk * BN + tx * 4]);
+          const float a[4] = {a4.x, a4.y, a4.z, a4.w};
+          const float b[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (MODE == kFast) {
-            acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
-          } else {
-            const float prod = a[i] * b[j];
-            acc[i][j] = acc[i][j] + prod;
-          }
+            for (int j = 0; j < 4; ++j) {
+              if (MODE == kFast) {
+                acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+              } else {
+                const float prod = a[i] * b[j];
+                acc[i][j] = acc[i][j] + prod;
+              }
+            }
         }
-    }
-    if (more) {
-      al.template store<LDA>(As[cur ^ 1], ra);
-      bl.store(Bs[cur ^ 1], rb);
-    }
-    __syncthreads();
-  }
+      });
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int col = n0 + tx * 4 + j;
@@ -418,20 +570,44 @@ __global__ void __launch_bounds__(256) valu_kernel(Problem p) {
   }
 }
 
+// One term for every lane, with the weight taken from lane U of the lane's
+// row of 16 (DPP row_newbcast on the first source operand), in one VOP2
+// instruction: fast mode v_fmac_f32 (acc += w*b, one rounding); exact mode
+// v_mul_f32 (the rounded product), then a separately rounded add.  The
+// weight register is written only by memory loads, never by a VALU
+// instruction, so the DPP read has no VALU-write hazard to wait out.
+template <int MODE, int U>
+__device__ __forceinline__ float step_bcast(float acc, float w, float b) {
+  if (MODE == kFast) {
+    asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+        : "+v"(acc)
+        : "v"(w), "v"(b), "n"(U));
+    return acc;
+  } else {
+    float prod;
+    asm("v_mul_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+        : "=v"(prod)
+        : "v"(w), "v"(b), "n"(U));
+    return acc + prod;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Lane kernel, for shapes with few outputs and long k (the deep layers of a
-// convolution network at batch 1, short matrix products): the matrix-core
-// instructions take 64 (32x32x1) or ~13 (4x4x1) cycles per dependent k step,
-// a VALU fused multiply-add about 5.  Lane l of a wave owns output column
-// n0 + l for the wave's R output rows; the R weights of a k step are the
-// same for every lane and come through the scalar cache into SGPRs; the B
-// value of the step is read from the LDS tile all W waves of the block
-// share (staged like the matrix-core kernel's, zero padding included).
+// convolution network at batch 1, short matrix products): a 32x32x1 MFMA
+// takes 64 cycles per dependent k step, a VALU fused multiply-add about 5.
+// Lane l of a wave owns output column n0 + l for the wave's R output rows.
+// The B value of a k step comes from the LDS tile all W waves of the block
+// share; the weight of a step is the same for every lane: a register holds
+// 16 taps of a row (lane l: tap l % 16, the same in each row of 16 lanes)
+// and a DPP row broadcast hands tap kk to all lanes.  Weights and B tiles
+// are loaded D-1 chunks ahead.
 // ---------------------------------------------------------------------------
-template <int MODE, int KIND, int R, int W>
-__global__ void __launch_bounds__(64 * W) lane_kernel(Problem p, const float *__restrict__ Aw) {
-  constexpr int NT = 64 * W, BK = 32, BN = 64;
+template <int MODE, int KIND, int R, int W, int D>
+__global__ void __launch_bounds__(64 * W) lane_kernel(Problem p) {
+  constexpr int NT = 64 * W, BK = 32, BN = 64, WR = BK / 16;
   __shared__ __align__(16) float Bs[2][BK * BN];
+  using BS = BStage<BN, BK, NT, KIND, false>;
 
   const TileCoord tc = tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -439,70 +615,57 @@ __global__ void __launch_bounds__(64 * W) lane_kernel(Problem p, const float *__
   const int n0 = tc.tn * BN;
   const int row0 = tc.tm * (R * W) + wave * R;
 
-  BLoader<BN, BK, NT, KIND> bl;
-  bl.init(p, tc.g, n0, tid);
-  float rb[BLoader<BN, BK, NT, KIND>::kPer];
+  BS bs;
+  bs.init(p, tc.g, n0, tid);
+  float rb[D][BS::kRegs];
+  float wv[D][R][WR];
 
-  // Weight rows of this wave; a row beyond M reads row M-1 and is never stored.
-  const float *arow[R];
+  // Weight row per output row (a row beyond M reads row M-1, never stored).
+  const float *wrow[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int row = min(row0 + r, p.M - 1);
-    arow[r] = Aw + tc.g * p.a_gstride + (int64_t)row * p.lda;
+    wrow[r] = p.A + tc.g * p.a_gstride + (int64_t)row * p.lda;
   }
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = 0.0f;
 
-  const int nchunks = (p.K + BK - 1) / BK;
-  if (nchunks > 0) {
-    bl.load(p, 0, rb);
-    bl.store(Bs[0], rb);
-  }
-  __syncthreads();
-  for (int kc = 0; kc < nchunks; ++kc) {
-    const int cur = kc & 1;
-    const bool more = kc + 1 < nchunks;
-    if (more) bl.load(p, (kc + 1) * BK, rb);
-    const int k0 = kc * BK;
-    const float *bs = Bs[cur];
-    if (k0 + BK <= p.K) {
+  run_pipeline<D>(
+      (p.K + BK - 1) / BK,
+      [&](int c, auto slot) {
+        constexpr int S = decltype(slot)::value;
+        const int k0 = c * BK;
+        bs.load(p, k0, rb[S]);
 #pragma unroll
-      for (int kk = 0; kk < BK; ++kk) {
-        const float b = bs[kk * BN + lane];
+        for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const float a = arow[r][k0 + kk];
-          if (MODE == kFast) {
-            acc[r] = __builtin_fmaf(a, b, acc[r]);
-          } else {
-            const float prod = a * b;
-            acc[r] = acc[r] + prod;
+          for (int h = 0; h < WR; ++h) {
+            const int t = 16 * h + (lane & 15);
+            wv[S][r][h] = load1(buffer_at(wrow[r] + k0, kRange),
+                                k0 + t < p.K ? (uint32_t)(4 * t) : kOutside);
           }
-        }
-      }
-    } else {
-      // last, partial chunk: taps at or beyond K are +0 in both operands
+      },
+      [&](auto slot, auto buf) { bs.store(Bs[decltype(buf)::value], rb[decltype(slot)::value]); },
+      [&](int, auto buf, auto slot) {
+        constexpr int S = decltype(slot)::value;
+        const float *bl = Bs[decltype(buf)::value];
+        // the chunk's B values first, all issued before the chains (the
+        // scheduling barrier keeps the compiler from sinking each read to
+        // just before its use, where its latency would stall the chain)
+        float bv[BK];
+        static_for<BK>([&](auto kk) {
+          constexpr int KK = decltype(kk)::value;
+          bv[KK] = bl[KK * BN + lane];
+        });
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<BK>([&](auto kk) {
+          constexpr int KK = decltype(kk)::value;
 #pragma unroll
-      for (int kk = 0; kk < BK; ++kk) {
-        const float b = bs[kk * BN + lane];
-        const bool kin = k0 + kk < p.K;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const float av = arow[r][kin ? k0 + kk : 0];
-          const float a = kin ? av : 0.0f;
-          if (MODE == kFast) {
-            acc[r] = __builtin_fmaf(a, b, acc[r]);
-          } else {
-            const float prod = a * b;
-            acc[r] = acc[r] + prod;
-          }
-        }
-      }
-    }
-    if (more) bl.store(Bs[cur ^ 1], rb);
-    __syncthreads();
-  }
+          for (int r = 0; r < R; ++r)
+            acc[r] = step_bcast<MODE, KK % 16>(acc[r], wv[S][r][KK / 16], bv[KK]);
+        });
+      });
   const int col = n0 + lane;
   if (col < p.N) {
     float *base = out_ptr<KIND>(p, tc.g, 0, col);
@@ -510,6 +673,119 @@ __global__ void __launch_bounds__(64 * W) lane_kernel(Problem p, const float *__
 #pragma unroll
     for (int r = 0; r < R; ++r)
       if (row0 + r < p.M) base[(row0 + r) * rstride] = canonical(acc[r]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Lane kernel for a KH x KW convolution known at compile time.  The columns
+// of a block are 64 output pixels of one image.  A k-chunk is CC whole input
+// channels (CC*KH*KW taps; every wave stages CPW channels).  Each lane keeps,
+// for every kernel position (ky, kx), the byte offset of its input pixel in
+// a plane, or an offset beyond the plane when the tap falls in the padding;
+// a tap's load then needs no arithmetic at all: a buffer load of the
+// channel's plane at that offset, which reads +0 outside the plane.  The
+// padding zeros are produced during the gather and never stored in memory.
+// ---------------------------------------------------------------------------
+template <int MODE, int KH, int KW, int R, int W, int D>
+__global__ void __launch_bounds__(64 * W) lane_conv_kernel(Problem p) {
+  constexpr int KHW = KH * KW;
+  constexpr int CPW = KHW >= 32 ? 1 : (32 / KHW + W - 1) / W;  // channels per wave and chunk
+  constexpr int CC = W * CPW;                                  // channels per chunk
+  constexpr int BK = CC * KHW, BN = 64, WR = (BK + 15) / 16, PER = CPW * KHW;
+  __shared__ __align__(16) float Bs[2][BK * BN];
+
+  const TileCoord tc = tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tpi = (p.OHW + BN - 1) / BN;  // column tiles per image
+  const int img = tc.tn / tpi;
+  const int pix = (tc.tn - img * tpi) * BN + lane;
+  const int row0 = tc.tm * (R * W) + wave * R;
+  const int cin_g = p.K / KHW;
+
+  // byte offsets of this lane's taps inside a plane
+  uint32_t voff[KHW];
+  {
+    const bool valid = pix < p.OHW;
+    const int oy = valid ? pix / p.OW : 0;
+    const int ox = valid ? pix - oy * p.OW : 0;
+    const int iy0 = oy * p.sH - p.pT, ix0 = ox * p.sW - p.pL;
+#pragma unroll
+    for (int ky = 0; ky < KH; ++ky)
+#pragma unroll
+      for (int kx = 0; kx < KW; ++kx) {
+        const int iy = iy0 + ky * p.dH, ix = ix0 + kx * p.dW;
+        const bool in = valid && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
+        voff[ky * KW + kx] = in ? (uint32_t)(4 * (iy * p.W + ix)) : kOutside;
+      }
+  }
+  const float *xg = p.B + img * p.x_img + tc.g * p.x_grp;  // channel 0 of (image, group)
+  const int plane_bytes = 4 * p.HW;
+
+  float rb[D][PER];
+  float wv[D][R][WR];
+  const float *wrow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int row = min(row0 + r, p.M - 1);  // a row beyond M is computed, never stored
+    wrow[r] = p.A + tc.g * p.a_gstride + (int64_t)row * p.lda;
+  }
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+
+  run_pipeline<D>(
+      (cin_g + CC - 1) / CC,
+      [&](int c, auto slot) {
+        constexpr int S = decltype(slot)::value;
+#pragma unroll
+        for (int cc = 0; cc < CPW; ++cc) {
+          const int ch = c * CC + wave * CPW + cc;  // wave-uniform
+          // a channel beyond K gets an empty range: its loads read +0
+          const __amdgpu_buffer_rsrc_t rs = buffer_at(
+              xg + (int64_t)min(ch, cin_g - 1) * p.HW, ch < cin_g ? (uint32_t)plane_bytes : 0u);
+#pragma unroll
+          for (int k = 0; k < KHW; ++k) rb[S][cc * KHW + k] = load1(rs, voff[k]);
+        }
+        const int k0 = c * BK;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int h = 0; h < WR; ++h) {
+            const int t = 16 * h + (lane & 15);
+            wv[S][r][h] = load1(buffer_at(wrow[r] + k0, kRange),
+                                k0 + t < p.K ? (uint32_t)(4 * t) : kOutside);
+          }
+      },
+      [&](auto slot, auto buf) {
+        float *bl = Bs[decltype(buf)::value];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) bl[(wave * PER + j) * BN + lane] = rb[decltype(slot)::value][j];
+      },
+      [&](int, auto buf, auto slot) {
+        constexpr int S = decltype(slot)::value;
+        const float *bl = Bs[decltype(buf)::value];
+        // the chunk's B values first, all issued before the chains (the
+        // scheduling barrier keeps the compiler from sinking each read to
+        // just before its use, where its latency would stall the chain)
+        float bv[BK];
+        static_for<BK>([&](auto kk) {
+          constexpr int KK = decltype(kk)::value;
+          bv[KK] = bl[KK * BN + lane];
+        });
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<BK>([&](auto kk) {
+          constexpr int KK = decltype(kk)::value;
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+            acc[r] = step_bcast<MODE, KK % 16>(acc[r], wv[S][r][KK / 16], bv[KK]);
+        });
+      });
+  if (pix < p.OHW) {
+    float *base = out_ptr<kBGather>(p, tc.g, 0, img * p.OHW + pix);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (row0 + r < p.M) base[(int64_t)(row0 + r) * p.OHW] = canonical(acc[r]);
   }
 }
 
