@@ -28,6 +28,12 @@ METRIC = "fp32 GFLOP/s (exact & fast) at 4096^3 + ResNet-50 conv chain ms; % fp3
 PEAK_FP32_TFLOPS = 157.3        # MI355X dense fp32 (matrix and packed vector)
 EXACT_CEILING_TFLOPS = 78.65    # one separately rounded VALU add per term
 HBM_GBPS = 8000.0
+# HBM bytes per launch of the headline kernel, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE runs scaled by a 1 GiB copy (factors 2.00 and 1.00; the
+# summary under profiles/ gives the commands and counts).  Valid only for
+# the kernel named here.
+HEADLINE_TRAFFIC = {"kernel": "og::mfma_kernel<1, 128, 256, 2, 2, 0, true, true, 2>",
+                    "bytes": (2.00 * 255186.9 + 1.00 * 65536.0) * 1024}
 PAGES_RESNET_CPU_MS = {"16 threads": 12.3, "32 threads": 11.1}  # 16-core Zen 4, fast mode
 
 
@@ -38,11 +44,12 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", default=None,
                     help="time one workload only (for profiling): gemm4096_fast, gemm4096_exact, "
-                         "resnet_b1, resnet_b8, skinny, prefill, grouped, conv1d, ragged, gemm256")
+                         "resnet_b1, resnet_b8, skinny, prefill, grouped, conv1d, ragged, gemm256, "
+                         "copy (a 1 GiB device copy, to scale the HBM byte counters)")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -66,6 +73,21 @@ class Timer:
         e1.record(s)
         t.cuda.synchronize()
         return e0.elapsed_time(e1) / calls  # ms per call
+
+    def graph(self, fn, calls: int = 1):
+        """`calls` calls of fn captured in one HIP graph (fn launches kernels only)."""
+        t = self.torch
+        fn()
+        t.cuda.synchronize()
+        s = t.cuda.Stream()
+        s.wait_stream(t.cuda.current_stream())
+        g = t.cuda.CUDAGraph()
+        with t.cuda.stream(s):
+            with t.cuda.graph(g, stream=s):
+                for _ in range(calls):
+                    fn()
+        t.cuda.synchronize()
+        return g
 
     def spike(self, fn, min_ms: float = 80.0, reps: int = 3) -> float:
         """2 warm-ups; calls repeated for >= min_ms; median of `reps` means (ms per call)."""
@@ -135,6 +157,15 @@ def extras(torch, og, synth, timer, only=None):
         del A, B, C
         return ent
 
+    if only == "copy":
+        x = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        x.fill_(1.0)
+        ms = timer.spike(lambda: y.copy_(x))
+        out["copy_1GiB"] = {"bytes_read": x.numel() * 4, "bytes_written": y.numel() * 4,
+                            "us": round(ms * 1e3, 1),
+                            "gbps": round(2 * x.numel() * 4 / (ms * 1e-3) / 1e9, 1)}
+        return out
     if want("gemm4096_exact") and only is not None:
         out["gemm_4096"] = gemm_entry(synth.gemm_4096(), modes=("exact",))
         return out
@@ -160,9 +191,15 @@ def extras(torch, og, synth, timer, only=None):
         macs = sum(conv_macs(og, s) for s, *_ in layers)
         ent = {"layers": len(layers), "gflop": round(2 * macs / 1e9, 3)}
         for mode in ("fast", "exact"):
-            ms = timer.spike(lambda: run_chain(og, layers, mode))
-            ent[mode] = {"ms": round(ms, 4), "gflops": round(2 * macs / (ms * 1e-3) / 1e9, 1),
+            # the 53 launches replayed from one HIP graph (no host time between
+            # kernels), and issued one by one from Python
+            g = timer.graph(lambda: run_chain(og, layers, mode))
+            ms = timer.spike(g.replay)
+            ms_eager = timer.spike(lambda: run_chain(og, layers, mode))
+            ent[mode] = {"ms": round(ms, 4), "ms_eager_launches": round(ms_eager, 4),
+                         "gflops": round(2 * macs / (ms * 1e-3) / 1e9, 1),
                          "frac_peak": round(2 * macs / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4)}
+            del g
         if batch == 1:
             ent["pages_cpu_context_ms"] = PAGES_RESNET_CPU_MS
         out[f"resnet50_chain_b{batch}"] = ent
@@ -198,14 +235,19 @@ def cpu_baseline(synth, seconds):
     orc.gemm(c.A[:rows], c.B, 1, rowwise=True)
     dt = time.perf_counter() - t0
     rows = int(min(c.m, max(rows, rows * seconds / max(dt, 1e-6))))
+    calls = 0
     t0 = time.perf_counter()
-    orc.gemm(c.A[:rows], c.B, 1, rowwise=True)
-    dt = time.perf_counter() - t0
-    flops = 2.0 * rows * c.n * c.k
+    while True:  # whole calls until the sample has run for `seconds`
+        orc.gemm(c.A[:rows], c.B, 1, rowwise=True)
+        calls += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            break
+    flops = 2.0 * calls * rows * c.n * c.k
     return {"value": round(flops / dt / 1e9, 3), "unit": "GFLOP/s", "cores": orc.num_threads(),
             "kind": "oracle",
             "sample": f"fast mode, rows 0..{rows - 1} of the 4096^3 product (all 4096 columns, "
-                      f"k = 4096), one call of the oracle's row-wise loop, {dt:.1f} s"}
+                      f"k = 4096), {calls} call(s) of the oracle's row-wise loop, {dt:.1f} s"}
 
 
 def main():
@@ -263,7 +305,9 @@ def main():
                    "mode": "fast", "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
-                     "traffic": None, "kernel": "og::mfma_kernel<fast, 128x256, matrix B>",
+                     "traffic": round(HEADLINE_TRAFFIC["bytes"]),
+                     "traffic_unit": "bytes per launch (HBM, counter-measured)",
+                     "kernel": HEADLINE_TRAFFIC["kernel"],
                      "wall_s_timed_region": round(wall, 3)},
     }
     del A, B, C

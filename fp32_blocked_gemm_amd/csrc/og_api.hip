@@ -79,10 +79,14 @@ struct Tile {
   int variant, bm, bn;
   int per_wave;  // matrix core: 32x64 blocks per wave; lane kernel: rows per wave
 };
+// 10..13 the chain kernel: (bn columns, compute waves, rows per lane) =
+// (64, 4, 1), (64, 2, 1), (16, 1, 1) and (64, 2, 2); its 3x3 convolution
+// form of variant 12 has 32 columns.
 constexpr Tile kTiles[] = {{1, 64, 64, 0},  {2, 128, 256, 4}, {3, 128, 128, 2}, {4, 64, 128, 1},
                            {5, 32, 256, 1}, {6, 4, 64, 1},    {7, 8, 64, 2},    {8, 16, 64, 4},
-                           {9, 32, 64, 8}};
-constexpr int kNumVariants = 9;
+                           {9, 32, 64, 8},  {10, 4, 64, 1},   {11, 2, 64, 1},   {12, 4, 16, 1},
+                           {13, 4, 64, 2}};
+constexpr int kNumVariants = 13;
 
 const Tile &tile_for_variant(int v) {
   for (const Tile &t : kTiles)
@@ -90,46 +94,67 @@ const Tile &tile_for_variant(int v) {
   return kTiles[1];
 }
 
-bool is_lane(const Tile &t) { return t.variant >= 6; }
+bool is_lane(const Tile &t) { return t.variant >= 6 && t.variant <= 9; }
+bool is_chain(const Tile &t) { return t.variant >= 10; }
 
-// Estimated cycles of one launch, from the shape alone.  The constants are
-// fitted to launches measured on MI355X: the matrix-core kernel sustains one
-// 32x32x1 MFMA per ~94 cycles per SIMD in fast mode (188 in exact mode) when
-// its tiles fill the chip, and ~300 cycles per k step when a few tiles run
-// alone (the loads of the next k-chunk are then exposed); the lane kernel
-// takes ~70 cycles per k step (~135 with the padded gather) while it has at
-// most one wave per SIMD.
-double estimate(const Tile &t, int64_t M, int64_t N, int64_t K, int64_t groups, int mode,
-                bool gather) {
-  const double cus = 256.0, simds = 1024.0;
-  const int64_t blocks = ceil_div(M, t.bm) * ceil_div(N, t.bn) * groups;
-  const double kk = (double)(K > 0 ? K : 1);
-  if (is_lane(t)) {
-    const double waves = 4.0 * blocks;
-    const double step = (gather ? 135.0 : 70.0) * (mode == OG_MODE_EXACT ? 1.1 : 1.0) *
-                        (1.0 + 0.15 * (t.per_wave - 1));
-    return kk * step * std::max(1.0, waves / simds) + 3000.0;
+// The shape the kernel choice sees: a group's product (M x N x K) and, for
+// a convolution, the pixels of one output image and the window size (the
+// lane and chain kernels tile columns per image for 1x1 and 3x3 windows).
+struct Shape {
+  int64_t M, N, K, groups;
+  int64_t ohw;  // output pixels per image; 0 for a matrix product
+  int64_t khw;  // KH * KW; 0 for a matrix product
+};
+
+// Launch time model, fitted to launches of every variant measured on MI355X
+// over the ResNet-50 layers at batch 1 and the matrix products the library
+// is benchmarked on: t = c * K * max(1, blocks / cap) + o microseconds, with
+// (cap, c in ns per k step, o) per variant and mode.
+struct Cost {
+  int variant;
+  double cap_fast, c_fast, o_fast, cap_exact, c_exact, o_exact;
+};
+constexpr Cost kCosts[] = {
+    {2, 384, 152.89, 7.2, 256, 226.15, 4.3},  {3, 384, 84.52, 4.4, 384, 222.18, 5.2},
+    {4, 384, 51.47, 3.7, 512, 133.74, 3.7},   {5, 512, 63.38, 4.6, 512, 152.77, 3.5},
+    {6, 384, 12.58, 6.6, 384, 14.08, 6.3},    {7, 384, 14.77, 6.3, 256, 17.43, 5.7},
+    {8, 384, 19.99, 4.7, 384, 29.56, 4.4},    {9, 384, 29.89, 4.5, 512, 52.56, 4.2},
+    {10, 128, 5.00, 7.9, 128, 5.86, 7.4},     {11, 128, 3.89, 9.4, 128, 4.35, 11.1},
+    {12, 384, 3.58, 7.8, 384, 4.41, 7.6},     {13, 128, 4.89, 7.6, 128, 6.57, 7.8},
+};
+
+// Blocks of a launch of variant t (columns per image where that kernel tiles so).
+int64_t launch_blocks(const Tile &t, const Shape &s) {
+  const bool per_image = s.ohw > 0 && (s.khw == 1 || s.khw == 9) && (is_lane(t) || is_chain(t));
+  int64_t bm = t.bm, bn = t.bn;
+  if (t.variant == 12 && s.khw == 9) bm = 2, bn = 32;  // the 3x3 form of variant 12
+  const int64_t ncol = per_image ? (s.N / s.ohw) * ceil_div(s.ohw, bn) : ceil_div(s.N, bn);
+  return ceil_div(s.M, bm) * ncol * s.groups;
+}
+
+double estimate(const Tile &t, const Shape &s, int mode) {
+  for (const Cost &c : kCosts) {
+    if (c.variant != t.variant) continue;
+    const bool ex = mode == OG_MODE_EXACT;
+    const double cap = ex ? c.cap_exact : c.cap_fast;
+    const double per = (ex ? c.c_exact : c.c_fast) * 1e-3;
+    const double o = ex ? c.o_exact : c.o_fast;
+    const double k = (double)(s.K > 0 ? s.K : 1);
+    return per * k * std::max(1.0, (double)launch_blocks(t, s) / cap) + o;
   }
-  const double per_mfma = mode == OG_MODE_EXACT ? 188.0 : 94.0;
-  const double lone = std::max(per_mfma * t.per_wave, 300.0);
-  const double full = per_mfma * t.per_wave;
-  const double rounds = (double)ceil_div(blocks, (int64_t)cus);
-  const double t_block = kk * (blocks < (int64_t)cus ? lone : full) + 3000.0;
-  return t_block * rounds;
+  return 1e300;
 }
 
 // The kernel chosen from the shape alone: the lowest estimate.
-const Tile &choose_tile(int64_t M, int64_t N, int64_t K, int64_t groups, int mode,
-                        bool gather) {
-  const int cands[] = {2, 3, 4, 5, 6, 7, 8, 9};
+const Tile &choose_tile(const Shape &s, int mode) {
   int best = 3;
   double best_cost = 1e300;
-  for (int v : cands) {
-    if (v == 9 && mode == OG_MODE_EXACT) continue;  // eight rows per lane: VALU-bound in exact mode
-    const double c = estimate(tile_for_variant(v), M, N, K, groups, mode, gather);
-    if (c < best_cost) {
-      best_cost = c;
-      best = v;
+  for (const Cost &c : kCosts) {
+    if (c.variant == 9 && mode == OG_MODE_EXACT) continue;  // eight rows per lane: VALU-bound in exact mode
+    const double e = estimate(tile_for_variant(c.variant), s, mode);
+    if (e < best_cost) {
+      best_cost = e;
+      best = c.variant;
     }
   }
   return tile_for_variant(best);
@@ -154,9 +179,41 @@ void launch_lane_conv(int variant, og::Problem p, hipStream_t s) {
   }
 }
 
+// The chain kernel of variant v for a matrix product (CONV false) or a
+// KH x KW convolution; its column tiles of a convolution are BN pixels of
+// one image.
+template <int MODE, bool CONV, int KH, int KW>
+void launch_chain(int v, og::Problem p, hipStream_t s) {
+  const int bn = v == 12 ? (KH * KW == 1 ? 16 : 32) : 64;
+  const int rows = v == 10 ? 4 : v == 11 ? 2 : v == 12 ? 64 / bn : 4;
+  const int threads = 64 * ((v == 10 ? 4 : v == 12 ? 1 : 2) + bn / 16);  // compute + producer waves
+  p.tiles_m = (int)ceil_div(p.M, rows);
+  p.tiles_n = CONV ? (int)((p.N / p.OHW) * ceil_div(p.OHW, bn)) : (int)ceil_div(p.N, bn);
+  const unsigned blocks = (unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)p.groups;
+  const dim3 grid(blocks), block(threads);
+  switch (v) {
+    case 10: hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, KH, KW, 64, 4, 1>), grid, block, 0, s, p); break;
+    case 11: hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, KH, KW, 64, 2, 1>), grid, block, 0, s, p); break;
+    case 12:
+      if constexpr (KH * KW == 1)
+        hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, KH, KW, 16, 1, 1>), grid, block, 0, s, p);
+      else
+        hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, KH, KW, 32, 1, 1>), grid, block, 0, s, p);
+      break;
+    default: hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, KH, KW, 64, 2, 2>), grid, block, 0, s, p); break;
+  }
+}
+
 // D: register-ring depth of the staged loads (chunks in flight).
 template <int MODE, int KIND, bool AV, bool BV>
 void launch_tile(const Tile &t, og::Problem p, hipStream_t s) {
+  if (is_chain(t)) {
+    if (KIND == og::kBMatrix) return launch_chain<MODE, false, 1, 1>(t.variant, p, s);
+    if (p.KH == 3 && p.KW == 3) return launch_chain<MODE, true, 3, 3>(t.variant, p, s);
+    if (p.KH == 1 && p.KW == 1) return launch_chain<MODE, true, 1, 1>(t.variant, p, s);
+    // other window sizes: the lane kernel with one row per wave
+    return launch_tile<MODE, KIND, AV, BV>(tile_for_variant(6), p, s);
+  }
   if (KIND == og::kBGather && is_lane(t)) {
     if (p.KH == 3 && p.KW == 3) return launch_lane_conv<MODE, 3, 3>(t.variant, p, s);
     if (p.KH == 1 && p.KW == 1) return launch_lane_conv<MODE, 1, 1>(t.variant, p, s);
@@ -210,8 +267,8 @@ void launch(int mode, bool av, bool bv, const Tile &t, const og::Problem &p, hip
 
 bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15) == 0; }
 
-const Tile &pick(int64_t M, int64_t N, int64_t K, int64_t groups, int mode, bool gather) {
-  return t_variant == 0 ? choose_tile(M, N, K, groups, mode, gather) : tile_for_variant(t_variant);
+const Tile &pick(const Shape &s, int mode) {
+  return t_variant == 0 ? choose_tile(s, mode) : tile_for_variant(t_variant);
 }
 
 bool grid_fits(const Tile &t, int64_t M, int64_t N, int64_t groups) {
@@ -243,7 +300,7 @@ og_status og_gemm_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_t l
   // the kernels address a tile's rows with 32-bit byte offsets
   if (lda > (int64_t(1) << 22) || ldb > (int64_t(1) << 22))
     return fail(OG_ERR_TOO_LARGE, "og_gemm_f32: lda or ldb exceeds 2^22");
-  const Tile &t = pick(m, n, k, 1, mode, false);
+  const Tile &t = pick(Shape{m, n, k, 1, 0, 0}, mode);
   if (!grid_fits(t, m, n, 1)) return fail(OG_ERR_TOO_LARGE, "og_gemm_f32: too many tiles");
   og_status st = check_device();
   if (st != OG_OK) return st;
@@ -308,7 +365,7 @@ og_status og_conv2d_f32_ex(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t
     return fail(OG_ERR_TOO_LARGE, "og_conv2d_f32: the input exceeds 2^29 elements");
   const bool planes = KH == 1 && KW == 1 && strideH == 1 && strideW == 1 && padTop == 0 &&
                       padLeft == 0 && padBottom == 0 && padRight == 0;
-  const Tile &t = pick(cout_g, ncols, K, G, mode, !planes);
+  const Tile &t = pick(Shape{cout_g, ncols, K, G, OH * OW, KH * KW}, mode);
   if (!grid_fits(t, cout_g, ncols, G)) return fail(OG_ERR_TOO_LARGE, "og_conv2d_f32: too many tiles");
   og_status st = check_device();
   if (st != OG_OK) return st;

@@ -789,4 +789,323 @@ __global__ void __launch_bounds__(64 * W) lane_conv_kernel(Problem p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Runs of 8 or 16 k steps of one or two rows in one asm block: the weight of
+// step u comes from lane u of the lane's row of 16 (DPP row_newbcast).  A
+// VALU write of a register read through DPP must be followed by two wait
+// states before that read; the weight registers are normally written by
+// loads, but the compiler may copy them (from AGPRs, say) on the VALU just
+// before the block, so every block starts with s_nop 1.  Inside a block the
+// DPP-read registers are never written.
+//   fast : acc = fma(w[u], b[u], acc)                       (v_fmac_f32_dpp)
+//   exact: p = round(w[u] * b[u]) (v_mul_f32_dpp); acc = round(acc + p); the
+//          product of step u+1 is formed while the sum of step u is pending.
+// ---------------------------------------------------------------------------
+#define OG_DPP(u) " row_newbcast:" #u " row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+// fast, one row: %0 acc, %1 weights, %2.. B values
+#define OG_F1(u, b) "v_fmac_f32_dpp %0, %1, %" #b OG_DPP(u)
+#define OG_FAST1_8                                                                     \
+  "s_nop 1\n" OG_F1(0, 2) OG_F1(1, 3) OG_F1(2, 4) OG_F1(3, 5) OG_F1(4, 6) OG_F1(5, 7) \
+      OG_F1(6, 8) OG_F1(7, 9)
+#define OG_FAST1_16                                                                   \
+  OG_FAST1_8 OG_F1(8, 10) OG_F1(9, 11) OG_F1(10, 12) OG_F1(11, 13) OG_F1(12, 14) \
+      OG_F1(13, 15) OG_F1(14, 16) OG_F1(15, 17)
+// fast, two rows: %0 %1 acc, %2 %3 weights, %4.. B values
+#define OG_F2(u, b) "v_fmac_f32_dpp %0, %2, %" #b OG_DPP(u) "v_fmac_f32_dpp %1, %3, %" #b OG_DPP(u)
+#define OG_FAST2_8                                                                      \
+  "s_nop 1\n" OG_F2(0, 4) OG_F2(1, 5) OG_F2(2, 6) OG_F2(3, 7) OG_F2(4, 8) OG_F2(5, 9) \
+      OG_F2(6, 10) OG_F2(7, 11)
+#define OG_FAST2_16                                                                    \
+  OG_FAST2_8 OG_F2(8, 12) OG_F2(9, 13) OG_F2(10, 14) OG_F2(11, 15) OG_F2(12, 16) \
+      OG_F2(13, 17) OG_F2(14, 18) OG_F2(15, 19)
+// exact, one row: %0 acc, %1 %2 products of even / odd steps, %3 weights,
+// %4.. B values
+#define OG_M1(t, u, b) "v_mul_f32_dpp %" #t ", %3, %" #b OG_DPP(u)
+#define OG_A1(t) "v_add_f32 %0, %0, %" #t "\n"
+#define OG_EXACT1_HEAD                                                                    \
+  "s_nop 1\n" OG_M1(1, 0, 4) OG_M1(2, 1, 5) OG_A1(1) OG_M1(1, 2, 6) OG_A1(2) OG_M1(2, 3, 7) \
+      OG_A1(1) OG_M1(1, 4, 8) OG_A1(2) OG_M1(2, 5, 9) OG_A1(1) OG_M1(1, 6, 10) OG_A1(2)     \
+          OG_M1(2, 7, 11) OG_A1(1)
+#define OG_EXACT1_8 OG_EXACT1_HEAD OG_A1(2)
+#define OG_EXACT1_16                                                                      \
+  OG_EXACT1_HEAD OG_M1(1, 8, 12) OG_A1(2) OG_M1(2, 9, 13) OG_A1(1) OG_M1(1, 10, 14) OG_A1(2) \
+      OG_M1(2, 11, 15) OG_A1(1) OG_M1(1, 12, 16) OG_A1(2) OG_M1(2, 13, 17) OG_A1(1)          \
+          OG_M1(1, 14, 18) OG_A1(2) OG_M1(2, 15, 19) OG_A1(1) OG_A1(2)
+// exact, two rows: %0 %1 acc, %2 %3 products of even steps, %4 %5 of odd
+// steps, %6 %7 weights, %8.. B values
+#define OG_M2(ta, tb, u, b) \
+  "v_mul_f32_dpp %" #ta ", %6, %" #b OG_DPP(u) "v_mul_f32_dpp %" #tb ", %7, %" #b OG_DPP(u)
+#define OG_A2(ta, tb) "v_add_f32 %0, %0, %" #ta "\n" "v_add_f32 %1, %1, %" #tb "\n"
+#define OG_EXACT2_HEAD                                                                   \
+  "s_nop 1\n" OG_M2(2, 3, 0, 8) OG_M2(4, 5, 1, 9) OG_A2(2, 3) OG_M2(2, 3, 2, 10)         \
+      OG_A2(4, 5) OG_M2(4, 5, 3, 11) OG_A2(2, 3) OG_M2(2, 3, 4, 12) OG_A2(4, 5)          \
+          OG_M2(4, 5, 5, 13) OG_A2(2, 3) OG_M2(2, 3, 6, 14) OG_A2(4, 5) OG_M2(4, 5, 7, 15) \
+              OG_A2(2, 3)
+#define OG_EXACT2_8 OG_EXACT2_HEAD OG_A2(4, 5)
+#define OG_EXACT2_16                                                                     \
+  OG_EXACT2_HEAD OG_M2(2, 3, 8, 16) OG_A2(4, 5) OG_M2(4, 5, 9, 17) OG_A2(2, 3)           \
+      OG_M2(2, 3, 10, 18) OG_A2(4, 5) OG_M2(4, 5, 11, 19) OG_A2(2, 3) OG_M2(2, 3, 12, 20) \
+          OG_A2(4, 5) OG_M2(4, 5, 13, 21) OG_A2(2, 3) OG_M2(2, 3, 14, 22) OG_A2(4, 5)     \
+              OG_M2(4, 5, 15, 23) OG_A2(2, 3) OG_A2(4, 5)
+
+#define OG_B8(b) "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]), "v"(b[4]), "v"(b[5]), "v"(b[6]), "v"(b[7])
+#define OG_B16(b)                                                                            \
+  OG_B8(b), "v"(b[8]), "v"(b[9]), "v"(b[10]), "v"(b[11]), "v"(b[12]), "v"(b[13]), "v"(b[14]), \
+      "v"(b[15])
+
+// N (8 or 16) steps of R (1 or 2) rows: acc[r] over b[0..N-1] with the
+// weights of row r in w[r] (lane u of each row of 16 holds step u's weight).
+template <int MODE, int R, int N>
+__device__ __forceinline__ void dpp_steps(float (&acc)[R], const float (&w)[R], const float *b) {
+  static_assert((R == 1 || R == 2) && (N == 8 || N == 16), "dpp_steps shape");
+  if constexpr (MODE == kFast && R == 1 && N == 8)
+    asm(OG_FAST1_8 : "+v"(acc[0]) : "v"(w[0]), OG_B8(b));
+  else if constexpr (MODE == kFast && R == 1)
+    asm(OG_FAST1_16 : "+v"(acc[0]) : "v"(w[0]), OG_B16(b));
+  else if constexpr (MODE == kFast && N == 8)
+    asm(OG_FAST2_8 : "+v"(acc[0]), "+v"(acc[1]) : "v"(w[0]), "v"(w[1]), OG_B8(b));
+  else if constexpr (MODE == kFast)
+    asm(OG_FAST2_16 : "+v"(acc[0]), "+v"(acc[1]) : "v"(w[0]), "v"(w[1]), OG_B16(b));
+  else if constexpr (R == 1) {
+    float t0, t1;
+    if constexpr (N == 8)
+      asm(OG_EXACT1_8 : "+v"(acc[0]), "=&v"(t0), "=&v"(t1) : "v"(w[0]), OG_B8(b));
+    else
+      asm(OG_EXACT1_16 : "+v"(acc[0]), "=&v"(t0), "=&v"(t1) : "v"(w[0]), OG_B16(b));
+  } else {
+    float t0, t1, t2, t3;
+    if constexpr (N == 8)
+      asm(OG_EXACT2_8
+          : "+v"(acc[0]), "+v"(acc[1]), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)
+          : "v"(w[0]), "v"(w[1]), OG_B8(b));
+    else
+      asm(OG_EXACT2_16
+          : "+v"(acc[0]), "+v"(acc[1]), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)
+          : "v"(w[0]), "v"(w[1]), OG_B16(b));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Chain kernel, for shapes whose outputs are too few to fill the chip and
+// whose k is long (the deep layers of a convolution network at batch 1, a
+// matrix-vector product, small square products).  There the time is the
+// length of one output's chain of k dependent operations, so the waves that
+// own outputs ("compute waves") do nothing but that chain: per k step one
+// DPP-broadcast fused multiply-add (fast) or multiply then add (exact), the
+// B values read from LDS four steps at a time and the weights loaded by the
+// wave itself 16 steps per register.  Separate "producer waves" of the same
+// block stream the B operand from memory into a ring of three LDS stages.
+//
+// B is read as a stack of "planes": the rows of a row-major matrix (GEMM),
+// or the input channels of one (image, group) of a convolution.  A k-chunk
+// is CH whole planes, CH*KHW taps in the order (plane, ky, kx).  Producer
+// lane groups of BN lanes own CPG planes of a chunk and one column each; a
+// lane keeps the byte offset of every one of its taps inside a chunk (its
+// column's pixel at each kernel position, or an offset past the buffer for
+// a padding tap or a column beyond the tile), so a tap is one buffer load
+// with no arithmetic and the padding zeros come from the load itself.  LDS
+// holds a chunk as [tap/4][column][tap%4], so a compute lane reads four
+// consecutive taps of its column with one 16-byte read.
+//
+// Barriers: iteration t (t = -1 .. chunks-1) ends with one block barrier.
+// In iteration t producers store chunk t+2 (t = -1 also stores chunk 0) in
+// stage (t+2) % 3, and compute waves read chunk t+1 from stage (t+1) % 3
+// into registers while they run the chain of chunk t.  A stage is thus
+// written two barriers after it was last read.  Loads past the last chunk
+// reload the last chunk (branch-free ring, exact wait counts) and their
+// stores go to a stage no one reads again.
+// ---------------------------------------------------------------------------
+template <int KHW, int BN>
+struct ChainShape {
+  static constexpr int PG = 4;                        // producer lane groups
+  static constexpr int PW = PG * BN / 64;             // producer waves
+  static constexpr int CPG = KHW == 1 ? 16 : 2;       // planes per group and chunk
+  static constexpr int CH = PG * CPG;                 // planes per chunk
+  static constexpr int BK = CH * KHW;                 // taps per chunk
+  static constexpr int TPG = CPG * KHW;               // taps per group and chunk
+  static constexpr int WU = TPG % 4 == 0 ? 4 : 2;     // taps per LDS store
+  static_assert(TPG % 2 == 0 && BK % 16 % 8 == 0 && BK <= 72, "chain chunk shape");
+};
+
+template <int MODE, bool CONV, int KH, int KW, int BN, int CW, int R>
+__global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN>::PW))
+    chain_kernel(Problem p) {
+  using CS = ChainShape<KH * KW, BN>;
+  constexpr int KHW = KH * KW, BK = CS::BK, NQ = BK / 4, WR = (BK + 15) / 16;
+  constexpr int TPG = CS::TPG, CPG = CS::CPG, CH = CS::CH, WU = CS::WU;
+  constexpr int NS = 3, DP = 4, DA = 8, U = 8;  // LDS stages, register ring depths, unroll
+  constexpr int RW = 64 / BN;                   // lane rows of a compute wave
+  constexpr int ROWS = CW * RW * R;             // output rows of a block
+  static_assert(U % DP == 0 && U % DA == 0 && U % 2 == 0, "unroll");
+  __shared__ __align__(16) float4 stage[NS][NQ * BN];
+
+  const TileCoord tc = tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int cl = lane % BN;
+
+  // the tile's columns: matrix columns, or output pixels of one image
+  int img = 0, cidx;
+  if (CONV) {
+    const int tpi = (p.OHW + BN - 1) / BN;
+    img = tc.tn / tpi;
+    cidx = (tc.tn - img * tpi) * BN + cl;
+  } else {
+    cidx = tc.tn * BN + cl;
+  }
+  const bool col_ok = cidx < (CONV ? p.OHW : p.N);
+
+  const float *pbase = CONV ? p.B + img * p.x_img + tc.g * p.x_grp : p.B;
+  const int64_t pstride = CONV ? (int64_t)p.HW : p.ldb;
+  const int pcount = CONV ? p.K / KHW : p.K;
+  const int nchunks = (pcount + CH - 1) / CH;
+  const int last = nchunks - 1;
+  if (nchunks == 0 && wave >= CW) return;  // k = 0: no barrier is ever reached
+
+  if (wave >= CW) {
+    // ---------------- producer ----------------
+    const int grp = (wave - CW) * (64 / BN) + lane / BN;
+    uint32_t off[TPG];
+    {
+      uint32_t voff[KHW];
+      if (CONV) {
+        const int oy = col_ok ? cidx / p.OW : 0;
+        const int ox = col_ok ? cidx - oy * p.OW : 0;
+        const int iy0 = oy * p.sH - p.pT, ix0 = ox * p.sW - p.pL;
+#pragma unroll
+        for (int ky = 0; ky < KH; ++ky)
+#pragma unroll
+          for (int kx = 0; kx < KW; ++kx) {
+            const int iy = iy0 + ky * p.dH, ix = ix0 + kx * p.dW;
+            const bool in = col_ok && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
+            voff[ky * KW + kx] = in ? (uint32_t)(4 * (iy * p.W + ix)) : kOutside;
+          }
+      } else {
+        voff[0] = col_ok ? (uint32_t)(4 * cidx) : kOutside;
+      }
+#pragma unroll
+      for (int j = 0; j < CPG; ++j)
+#pragma unroll
+        for (int t = 0; t < KHW; ++t) {
+          const int64_t o = (int64_t)(grp * CPG + j) * pstride * 4 + voff[t];
+          off[j * KHW + t] = (voff[t] == kOutside || o >= (int64_t)kOutside) ? kOutside : (uint32_t)o;
+        }
+    }
+    float rb[DP][TPG];
+    auto load = [&](int c, auto slot) {
+      constexpr int S = decltype(slot)::value;
+      const int valid = min(max(pcount - c * CH, 0), CH);  // planes of the chunk that exist
+      // (the range is uniform; readfirstlane keeps the descriptor in scalar
+      // registers where the compiler would otherwise clamp it on the VALU)
+      const uint32_t range =
+          __builtin_amdgcn_readfirstlane((uint32_t)((int64_t)valid * pstride * 4));
+      const __amdgpu_buffer_rsrc_t rs = buffer_at(pbase + (int64_t)c * CH * pstride, range);
+#pragma unroll
+      for (int e = 0; e < TPG; ++e) rb[S][e] = load1(rs, off[e]);
+    };
+    auto store = [&](auto slot, int st) {
+      constexpr int S = decltype(slot)::value;
+      float *st0 = reinterpret_cast<float *>(stage[st]);
+#pragma unroll
+      for (int u = 0; u < TPG / WU; ++u) {
+        const int kt = grp * TPG + u * WU;  // first tap of the store within the chunk
+        float *dst = st0 + ((kt / 4) * BN + cl) * 4 + kt % 4;
+        if constexpr (WU == 4)
+          *reinterpret_cast<float4 *>(dst) =
+              make_float4(rb[S][4 * u], rb[S][4 * u + 1], rb[S][4 * u + 2], rb[S][4 * u + 3]);
+        else
+          *reinterpret_cast<float2 *>(dst) = make_float2(rb[S][2 * u], rb[S][2 * u + 1]);
+      }
+    };
+    static_for<DP>([&](auto j) { load(min((int)decltype(j)::value, last), j); });
+    store(std::integral_constant<int, 0>{}, 0);
+    load(min(DP, last), std::integral_constant<int, 0>{});
+    for (int t0 = -1; t0 < nchunks; t0 += U) {
+      static_for<U>([&](auto j) {
+        constexpr int J = decltype(j)::value;
+        const int t = t0 + J;
+        if (t < nchunks) {
+          const int v = t + 2;  // the chunk stored now (slot (J + 1) % DP holds it)
+          store(std::integral_constant<int, (J + 1) % DP>{}, v % NS);
+          load(min(v + DP, last), std::integral_constant<int, (J + 1) % DP>{});
+          __syncthreads();
+        }
+      });
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    return;
+  }
+
+  // ---------------- compute ----------------
+  const int row_w = tc.tm * ROWS + wave * RW * R;  // first row of the wave
+  const int lrow = row_w + (lane / BN) * R;        // first row of the lane
+  const int mlast = p.M - 1;
+  const float *wbase = p.A + tc.g * p.a_gstride + (int64_t)min(row_w, mlast) * p.lda;
+  uint32_t woff[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    woff[r] = (uint32_t)((int64_t)(min(lrow + r, mlast) - min(row_w, mlast)) * p.lda * 4);
+  float wv[DA][R][WR];
+  auto wload = [&](int c, auto slot) {
+    constexpr int S = decltype(slot)::value;
+    const int k0 = c * BK;
+    const __amdgpu_buffer_rsrc_t rs = buffer_at(wbase + k0, kRange);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int h = 0; h < WR; ++h) {
+        const int t = 16 * h + (lane & 15);
+        wv[S][r][h] = load1(rs, k0 + t < p.K ? woff[r] + (uint32_t)(4 * t) : kOutside);
+      }
+  };
+  float4 bq[2][NQ];
+  auto read = [&](auto par, int st) {
+    constexpr int P = decltype(par)::value;
+    const float4 *src = stage[st] + cl;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) bq[P][q] = src[q * BN];
+  };
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+
+  if (nchunks > 0) {
+    static_for<DA - 1>([&](auto j) { wload(min((int)decltype(j)::value, last), j); });
+    __syncthreads();
+    read(std::integral_constant<int, 0>{}, 0);
+    for (int t0 = 0; t0 < nchunks; t0 += U) {
+      static_for<U>([&](auto j) {
+        constexpr int J = decltype(j)::value;
+        const int t = t0 + J;
+        if (t < nchunks) {
+          wload(min(t + DA - 1, last), std::integral_constant<int, (J + DA - 1) % DA>{});
+          read(std::integral_constant<int, (J + 1) % 2>{}, (t + 1) % NS);
+          __builtin_amdgcn_sched_barrier(0);
+          static_for<WR>([&](auto h) {
+            constexpr int H = decltype(h)::value;
+            constexpr int N = BK - 16 * H < 16 ? BK - 16 * H : 16;
+            float b[N];
+#pragma unroll
+            for (int u = 0; u < N; ++u) b[u] = bq[J % 2][(16 * H + u) / 4][u % 4];
+            float w[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) w[r] = wv[J % DA][r][H];
+            dpp_steps<MODE, R, N>(acc, w, b);
+          });
+          // the barrier waits for this wave's LDS reads: keep it after the chain
+          __builtin_amdgcn_sched_barrier(0);
+          __syncthreads();
+        }
+      });
+    }
+  }
+  if (col_ok) {
+    float *base = out_ptr<CONV ? kBGather : kBMatrix>(p, tc.g, 0, CONV ? img * p.OHW + cidx : cidx);
+    const int64_t rstride = CONV ? (int64_t)p.OHW : p.ldc;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (lrow + r < p.M) base[(int64_t)(lrow + r) * rstride] = canonical(acc[r]);
+  }
+}
+
 }  // namespace og

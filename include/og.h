@@ -65,6 +65,7 @@ typedef int og_status;
  * ldb >= max(1,n), ldc >= max(1,n); A and B non-null when m, n and k are all
  * positive, C non-null when m and n are positive.  m == 0 or n == 0: nothing
  * is done.  k == 0: every output is +0 and A, B are not read.
+ * OG_ERR_TOO_LARGE when m, n or k exceeds 2^31-1 or lda or ldb exceeds 2^22.
  */
 og_status og_gemm_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_t lda,
                       const float *B, int64_t ldb, float *C, int64_t ldc, int mode);
@@ -89,7 +90,8 @@ og_status og_gemm_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_t l
  * convolution is H = 1, KH = 1 with padTop = padBottom = 0.
  * Requirements: N, Cin, H, W, Cout, G, KH, KW >= 1; strides and dilations
  * >= 1; pads >= 0; Cin and Cout multiples of G; OH, OW >= 1; pointers
- * non-null.
+ * non-null.  OG_ERR_TOO_LARGE when the input holds more than 2^29 elements
+ * or a size does not fit 31 bits (the kernels form 32-bit offsets).
  */
 og_status og_conv2d_f32_ex(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout,
                            int64_t G, int64_t KH, int64_t KW, int64_t strideH, int64_t strideW,
@@ -127,9 +129,15 @@ void *og_get_stream(void);
  * that the results do not depend on it ("Exact mode", rule 5): 0 = chosen
  * from the shape (the default); 1 = the VALU tile kernel (64x64 tiles);
  * 2, 3, 4, 5 = the matrix-core kernel with 128x256, 128x128, 64x128 and
- * 32x256 output tiles; 6, 7, 8, 9 = the lane kernel (one output column per
- * lane) with 1, 2, 4, 8 output rows per wave.  Every variant runs every
- * shape.  A value outside 0..9 returns OG_ERR_INVALID_ARG.
+ * 32x256 output tiles (exact mode runs variant 2 with 128x128 tiles);
+ * 6, 7, 8, 9 = the lane kernel (one output column per lane) with 1, 2, 4, 8
+ * output rows per wave; 10, 11, 12, 13 = the chain kernel (compute waves
+ * that only run the k chain, producer waves that stage B) with 64 columns
+ * and 4 rows, 64 columns and 2 rows, 16 columns and 4 rows (a 3x3
+ * convolution: 32 columns and 2 rows), 64 columns and 4 rows as two rows
+ * per lane.  Every variant runs every shape (a convolution window other
+ * than 1x1 or 3x3 runs variants 10..13 as variant 6).  A value outside
+ * 0..13 returns OG_ERR_INVALID_ARG.
  */
 og_status og_set_variant(int variant);
 int og_get_variant(void);

@@ -80,7 +80,7 @@ def test_random_shapes(orc, mode):
         assert_same_bits(_gpu_conv(x, w, s, mode), _oracle(orc, x, w, s, mode), f"{s} mode {mode}")
 
 
-@pytest.mark.parametrize("variant", list(range(1, 10)))
+@pytest.mark.parametrize("variant", list(range(1, 14)))
 def test_variants_agree(orc, variant):
     rng = np.random.default_rng(300)
     og.set_variant(variant)
@@ -92,6 +92,27 @@ def test_variants_agree(orc, variant):
             say(f"conv variant {variant} {s} mode {mode}")
             assert_same_bits(_gpu_conv(x, w, s, mode), _oracle(orc, x, w, s, mode),
                              f"variant {variant} {s} mode {mode}")
+
+
+@pytest.mark.parametrize("variant", [10, 11, 12, 13])
+def test_chain_kernel_shapes(orc, variant):
+    """The chain kernel on 3x3 and 1x1 windows (strided, padded, dilated,
+    grouped, several chunks of channels) and its fallback for other windows."""
+    rng = np.random.default_rng(400 + variant)
+    og.set_variant(variant)
+    shapes = [synth.ConvShape("c3", 2, 40, 9, 11, 12, 3, 3, (2, 1), (1, 0, 2, 1), (2, 1)),
+              synth.ConvShape("c3g", 1, 34, 7, 7, 10, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), 2),
+              synth.ConvShape("c1s", 2, 70, 9, 8, 9, 1, 1, (2, 2)),
+              synth.ConvShape("c1p", 3, 130, 5, 6, 5, 1, 1),
+              synth.ConvShape("c5", 1, 6, 9, 9, 7, 5, 3, (1, 2), (2, 1, 2, 1))]
+    for s in shapes:
+        x, w = synth.conv_inputs(s, int(rng.integers(1 << 30)), "uniform")
+        x = _with_specials(x, rng, 0.01)
+        w = _with_specials(w, rng, 0.01)
+        for mode in MODES:
+            say(f"conv chain variant {variant} {s} mode {mode}")
+            assert_same_bits(_gpu_conv(x, w, s, mode), _oracle(orc, x, w, s, mode),
+                             f"chain {variant} {s} mode {mode}")
 
 
 def test_padding_tap_meets_infinite_weight(orc):

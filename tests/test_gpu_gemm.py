@@ -106,7 +106,7 @@ def test_ragged_ld13_full(orc, specials):
         _check_gaps(flatC, c.m, c.n, c.ldc, 0)
 
 
-@pytest.mark.parametrize("variant", list(range(1, 10)))
+@pytest.mark.parametrize("variant", list(range(1, 14)))
 def test_variants_agree(orc, variant):
     """Every kernel variant gives the oracle's bits (no dependence on tiles)."""
     rng = np.random.default_rng(7)
@@ -118,6 +118,22 @@ def test_variants_agree(orc, variant):
         say(f"gemm variant {variant} mode {mode}")
         got, _ = _run_gpu(A, B, mode, k + 3, n + 1, n + 2, (1, 2, 3))
         assert_same_bits(got, orc.gemm(A, B, mode), f"variant {variant} mode {mode}")
+
+
+@pytest.mark.parametrize("variant", [10, 11, 12, 13])
+def test_chain_kernel_lengths(orc, variant):
+    """The chain kernel over k from 0 to several chunks, with ragged tails,
+    rows and columns that end inside a tile, and special values."""
+    rng = np.random.default_rng(70 + variant)
+    og.set_variant(variant)
+    for m, n, k in ((5, 70, 0), (5, 70, 1), (9, 33, 64), (9, 33, 65), (3, 130, 517),
+                    (1, 301, 300), (6, 17, 129)):
+        A = _mixed(rng, (m, k), 0.01)
+        B = _mixed(rng, (k, n), 0.01)
+        for mode in MODES:
+            say(f"gemm chain variant {variant} {m}x{n}x{k} mode {mode}")
+            got, _ = _run_gpu(A, B, mode, k + 1, n + 3, n, (0, 1, 0))
+            assert_same_bits(got, orc.gemm(A, B, mode), f"chain {variant} {m}x{n}x{k} mode {mode}")
 
 
 def _sample(rng, m, n, count):
