@@ -109,18 +109,26 @@ struct Shape {
 // Launch time model, fitted to launches of every variant measured on MI355X
 // over the ResNet-50 layers at batch 1 and the matrix products the library
 // is benchmarked on: t = c * K * max(1, blocks / cap) + o microseconds, with
-// (cap, c in ns per k step, o) per variant and mode.
+// (cap, c in ns per k step, o) per variant and mode, and for the lane and
+// chain kernels separately for 3x3 windows (whose gathers cost more).  The
+// chain kernel's step cost is held at >= 2.5 ns when fitting (about six
+// cycles: its dependent chain cannot run faster), so the model does not
+// extrapolate a chain to no cost.
 struct Cost {
-  int variant;
+  int variant, win3;
   double cap_fast, c_fast, o_fast, cap_exact, c_exact, o_exact;
 };
 constexpr Cost kCosts[] = {
-    {2, 384, 152.89, 7.2, 256, 226.15, 4.3},  {3, 384, 84.52, 4.4, 384, 222.18, 5.2},
-    {4, 384, 51.47, 3.7, 512, 133.74, 3.7},   {5, 512, 63.38, 4.6, 512, 152.77, 3.5},
-    {6, 384, 12.58, 6.6, 384, 14.08, 6.3},    {7, 384, 14.77, 6.3, 256, 17.43, 5.7},
-    {8, 384, 19.99, 4.7, 384, 29.56, 4.4},    {9, 384, 29.89, 4.5, 512, 52.56, 4.2},
-    {10, 128, 5.00, 7.9, 128, 5.86, 7.4},     {11, 128, 3.89, 9.4, 128, 4.35, 11.1},
-    {12, 384, 3.58, 7.8, 384, 4.41, 7.6},     {13, 128, 4.89, 7.6, 128, 6.57, 7.8},
+    {2, 0, 256, 125.54, 9.4, 256, 232.36, 0.0}, {3, 0, 384, 84.05, 4.5, 384, 222.57, 4.7},
+    {4, 0, 384, 51.50, 3.8, 512, 134.27, 3.3},  {5, 0, 256, 38.34, 6.8, 384, 123.02, 4.7},
+    {6, 0, 384, 11.49, 7.1, 384, 12.80, 6.5},   {6, 1, 1024, 11.70, 15.1, 512, 14.61, 12.8},
+    {7, 0, 256, 17.09, 3.8, 256, 21.72, 3.8},   {7, 1, 384, 16.49, 6.2, 384, 21.24, 6.9},
+    {8, 0, 384, 19.36, 4.2, 384, 28.36, 4.6},   {8, 1, 256, 23.08, 1.9, 256, 32.03, 2.6},
+    {9, 0, 384, 29.72, 4.1, 512, 52.36, 4.2},   {9, 1, 128, 32.44, 1.8, 128, 54.15, 2.2},
+    {10, 0, 128, 4.44, 7.9, 128, 5.05, 8.9},    {10, 1, 256, 6.11, 17.7, 256, 5.48, 20.2},
+    {11, 0, 128, 3.55, 9.8, 128, 4.44, 10.5},   {11, 1, 256, 2.50, 33.4, 256, 2.50, 34.9},
+    {12, 0, 256, 2.50, 8.2, 384, 3.97, 9.0},    {12, 1, 512, 2.50, 29.3, 512, 2.50, 33.4},
+    {13, 0, 128, 4.62, 7.8, 128, 6.24, 8.2},    {13, 1, 256, 4.42, 18.8, 256, 5.89, 20.9},
 };
 
 // Blocks of a launch of variant t (columns per image where that kernel tiles so).
@@ -133,8 +141,9 @@ int64_t launch_blocks(const Tile &t, const Shape &s) {
 }
 
 double estimate(const Tile &t, const Shape &s, int mode) {
+  const int win3 = (is_lane(t) || is_chain(t)) && s.khw == 9 ? 1 : 0;
   for (const Cost &c : kCosts) {
-    if (c.variant != t.variant) continue;
+    if (c.variant != t.variant || c.win3 != win3) continue;
     const bool ex = mode == OG_MODE_EXACT;
     const double cap = ex ? c.cap_exact : c.cap_fast;
     const double per = (ex ? c.c_exact : c.c_fast) * 1e-3;
@@ -150,6 +159,7 @@ const Tile &choose_tile(const Shape &s, int mode) {
   int best = 3;
   double best_cost = 1e300;
   for (const Cost &c : kCosts) {
+    if (c.win3) continue;  // each variant once
     if (c.variant == 9 && mode == OG_MODE_EXACT) continue;  // eight rows per lane: VALU-bound in exact mode
     const double e = estimate(tile_for_variant(c.variant), s, mode);
     if (e < best_cost) {
@@ -179,28 +189,29 @@ void launch_lane_conv(int variant, og::Problem p, hipStream_t s) {
   }
 }
 
-// The chain kernel of variant v for a matrix product (CONV false) or a
-// KH x KW convolution; its column tiles of a convolution are BN pixels of
-// one image.
-template <int MODE, bool CONV, int KH, int KW>
+// The chain kernel of variant v for a matrix product (CONV false; VEC: B
+// rows 16-byte aligned, read 16 bytes per load) or a KH x KW convolution; its
+// column tiles of a convolution are BN pixels of one image.
+template <int MODE, bool CONV, bool VEC, int KH, int KW>
 void launch_chain(int v, og::Problem p, hipStream_t s) {
   const int bn = v == 12 ? (KH * KW == 1 ? 16 : 32) : 64;
-  const int rows = v == 10 ? 4 : v == 11 ? 2 : v == 12 ? 64 / bn : 4;
-  const int threads = 64 * ((v == 10 ? 4 : v == 12 ? 1 : 2) + bn / 16);  // compute + producer waves
+  const int cw = v == 10 ? 4 : v == 12 ? 1 : 2;  // compute waves
+  const int rows = cw * (64 / bn) * (v == 13 ? 2 : 1);
+  const int pw = 4 * bn / 64;  // B producer waves (and one weight wave)
   p.tiles_m = (int)ceil_div(p.M, rows);
   p.tiles_n = CONV ? (int)((p.N / p.OHW) * ceil_div(p.OHW, bn)) : (int)ceil_div(p.N, bn);
   const unsigned blocks = (unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)p.groups;
-  const dim3 grid(blocks), block(threads);
+  const dim3 grid(blocks), block(64 * (cw + pw + 1));
   switch (v) {
-    case 10: hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, KH, KW, 64, 4, 1>), grid, block, 0, s, p); break;
-    case 11: hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, KH, KW, 64, 2, 1>), grid, block, 0, s, p); break;
+    case 10: hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, VEC, KH, KW, 64, 4, 1>), grid, block, 0, s, p); break;
+    case 11: hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, VEC, KH, KW, 64, 2, 1>), grid, block, 0, s, p); break;
     case 12:
       if constexpr (KH * KW == 1)
-        hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, KH, KW, 16, 1, 1>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, VEC, KH, KW, 16, 1, 1>), grid, block, 0, s, p);
       else
-        hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, KH, KW, 32, 1, 1>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, VEC, KH, KW, 32, 1, 1>), grid, block, 0, s, p);
       break;
-    default: hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, KH, KW, 64, 2, 2>), grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, VEC, KH, KW, 64, 2, 2>), grid, block, 0, s, p); break;
   }
 }
 
@@ -208,9 +219,12 @@ void launch_chain(int v, og::Problem p, hipStream_t s) {
 template <int MODE, int KIND, bool AV, bool BV>
 void launch_tile(const Tile &t, og::Problem p, hipStream_t s) {
   if (is_chain(t)) {
-    if (KIND == og::kBMatrix) return launch_chain<MODE, false, 1, 1>(t.variant, p, s);
-    if (p.KH == 3 && p.KW == 3) return launch_chain<MODE, true, 3, 3>(t.variant, p, s);
-    if (p.KH == 1 && p.KW == 1) return launch_chain<MODE, true, 1, 1>(t.variant, p, s);
+    if (KIND == og::kBMatrix) {
+      if (BV) return launch_chain<MODE, false, true, 1, 1>(t.variant, p, s);
+      return launch_chain<MODE, false, false, 1, 1>(t.variant, p, s);
+    }
+    if (p.KH == 3 && p.KW == 3) return launch_chain<MODE, true, false, 3, 3>(t.variant, p, s);
+    if (p.KH == 1 && p.KW == 1) return launch_chain<MODE, true, false, 1, 1>(t.variant, p, s);
     // other window sizes: the lane kernel with one row per wave
     return launch_tile<MODE, KIND, AV, BV>(tile_for_variant(6), p, s);
   }

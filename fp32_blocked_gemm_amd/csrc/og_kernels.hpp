@@ -890,11 +890,13 @@ __device__ __forceinline__ void dpp_steps(float (&acc)[R], const float (&w)[R], 
 // whose k is long (the deep layers of a convolution network at batch 1, a
 // matrix-vector product, small square products).  There the time is the
 // length of one output's chain of k dependent operations, so the waves that
-// own outputs ("compute waves") do nothing but that chain: per k step one
+// own outputs ("compute waves") run nothing but that chain: per k step one
 // DPP-broadcast fused multiply-add (fast) or multiply then add (exact), the
-// B values read from LDS four steps at a time and the weights loaded by the
-// wave itself 16 steps per register.  Separate "producer waves" of the same
-// block stream the B operand from memory into a ring of three LDS stages.
+// B values read from LDS four steps per 16-byte read and the weights one
+// read per 16 steps.  A compute wave issues no global load and never waits
+// at a barrier for its own LDS reads.  "Producer waves" of the same block
+// stream B and a "weight wave" streams the block's weight rows from memory
+// into a ring of three LDS stages.
 //
 // B is read as a stack of "planes": the rows of a row-major matrix (GEMM),
 // or the input channels of one (image, group) of a convolution.  A k-chunk
@@ -903,41 +905,50 @@ __device__ __forceinline__ void dpp_steps(float (&acc)[R], const float (&w)[R], 
 // lane keeps the byte offset of every one of its taps inside a chunk (its
 // column's pixel at each kernel position, or an offset past the buffer for
 // a padding tap or a column beyond the tile), so a tap is one buffer load
-// with no arithmetic and the padding zeros come from the load itself.  LDS
-// holds a chunk as [tap/4][column][tap%4], so a compute lane reads four
-// consecutive taps of its column with one 16-byte read.
+// with no arithmetic and the padding zeros come from the load itself.  When
+// B is a matrix whose rows are 16-byte aligned, a producer lane instead
+// loads a 4x4 block (four rows of four columns, 16 bytes each) and stores
+// it transposed.  LDS holds a chunk as [tap/4][column][tap%4], so a compute
+// lane reads four consecutive taps of its column with one 16-byte read, and
+// the weights as [row][tap].
 //
 // Barriers: iteration t (t = -1 .. chunks-1) ends with one block barrier.
 // In iteration t producers store chunk t+2 (t = -1 also stores chunk 0) in
 // stage (t+2) % 3, and compute waves read chunk t+1 from stage (t+1) % 3
-// into registers while they run the chain of chunk t.  A stage is thus
-// written two barriers after it was last read.  Loads past the last chunk
-// reload the last chunk (branch-free ring, exact wait counts) and their
-// stores go to a stage no one reads again.
+// into registers while they run the chain of chunk t; they consume those
+// reads before the next barrier, so a stage is written two barriers after
+// its last read has completed.  Loads past the last chunk reload the last
+// chunk (branch-free rings, exact wait counts) and their stores go to a
+// stage no one reads again.
 // ---------------------------------------------------------------------------
-template <int KHW, int BN>
+template <int KHW, int BN, int ROWS>
 struct ChainShape {
-  static constexpr int PG = 4;                        // producer lane groups
-  static constexpr int PW = PG * BN / 64;             // producer waves
-  static constexpr int CPG = KHW == 1 ? 16 : 2;       // planes per group and chunk
-  static constexpr int CH = PG * CPG;                 // planes per chunk
-  static constexpr int BK = CH * KHW;                 // taps per chunk
-  static constexpr int TPG = CPG * KHW;               // taps per group and chunk
-  static constexpr int WU = TPG % 4 == 0 ? 4 : 2;     // taps per LDS store
-  static_assert(TPG % 2 == 0 && BK % 16 % 8 == 0 && BK <= 72, "chain chunk shape");
+  static constexpr int PG = 4;                         // B producer lane groups
+  static constexpr int PW = PG * BN / 64;              // B producer waves
+  static constexpr int CPG = KHW == 1 ? 32 : 4;        // planes per group and chunk
+  static constexpr int CH = PG * CPG;                  // planes per chunk
+  static constexpr int BK = CH * KHW;                  // taps per chunk (128 or 144)
+  static constexpr int TPG = CPG * KHW;                // taps per group and chunk
+  static constexpr int NW = (ROWS * BK + 63) / 64;     // weight loads per weight-wave lane
+  static_assert(PW >= 1 && TPG % 4 == 0 && BK % 16 == 0, "chain chunk shape");
 };
 
-template <int MODE, bool CONV, int KH, int KW, int BN, int CW, int R>
-__global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN>::PW))
+template <int MODE, bool CONV, bool VEC, int KH, int KW, int BN, int CW, int R>
+__global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, CW *(64 / BN) * R>::PW + 1))
     chain_kernel(Problem p) {
-  using CS = ChainShape<KH * KW, BN>;
-  constexpr int KHW = KH * KW, BK = CS::BK, NQ = BK / 4, WR = (BK + 15) / 16;
-  constexpr int TPG = CS::TPG, CPG = CS::CPG, CH = CS::CH, WU = CS::WU;
-  constexpr int NS = 3, DP = 4, DA = 8, U = 8;  // LDS stages, register ring depths, unroll
-  constexpr int RW = 64 / BN;                   // lane rows of a compute wave
-  constexpr int ROWS = CW * RW * R;             // output rows of a block
-  static_assert(U % DP == 0 && U % DA == 0 && U % 2 == 0, "unroll");
+  constexpr int KHW = KH * KW;
+  constexpr int RW = 64 / BN;       // lane rows of a compute wave
+  constexpr int ROWS = CW * RW * R;  // output rows of a block
+  using CS = ChainShape<KHW, BN, ROWS>;
+  constexpr int BK = CS::BK, NQ = BK / 4, NB = BK / 16;
+  constexpr int TPG = CS::TPG, CPG = CS::CPG, CH = CS::CH, PW = CS::PW, NW = CS::NW;
+  constexpr int NS = 3, DP = 2, DW = 4, U = 4;  // LDS stages, ring depths (B, weights), unroll
+  constexpr int RB = 4, LA = RB - 1, UC = 4;    // compute: register blocks, read-ahead, unroll
+  constexpr int NBL = VEC ? BK / 64 : 0;        // 4x4 blocks per producer lane (16-byte loads)
+  static_assert(U % DP == 0 && U % DW == 0 && (UC * NB) % RB == 0, "unroll");
+  static_assert(!VEC || (!CONV && KHW == 1 && BK % 64 == 0), "16-byte producer loads: matrix B only");
   __shared__ __align__(16) float4 stage[NS][NQ * BN];
+  __shared__ __align__(16) float wstage[NS][ROWS * BK];
 
   const TileCoord tc = tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n);
   const int lane = threadIdx.x & 63;
@@ -945,28 +956,94 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN>::PW))
   const int cl = lane % BN;
 
   // the tile's columns: matrix columns, or output pixels of one image
-  int img = 0, cidx;
+  int img = 0, cbase;
   if (CONV) {
     const int tpi = (p.OHW + BN - 1) / BN;
     img = tc.tn / tpi;
-    cidx = (tc.tn - img * tpi) * BN + cl;
+    cbase = (tc.tn - img * tpi) * BN;
   } else {
-    cidx = tc.tn * BN + cl;
+    cbase = tc.tn * BN;
   }
-  const bool col_ok = cidx < (CONV ? p.OHW : p.N);
+  const int ncols = CONV ? p.OHW : p.N;
+  const int cidx = cbase + cl;
+  const bool col_ok = cidx < ncols;
 
   const float *pbase = CONV ? p.B + img * p.x_img + tc.g * p.x_grp : p.B;
   const int64_t pstride = CONV ? (int64_t)p.HW : p.ldb;
   const int pcount = CONV ? p.K / KHW : p.K;
   const int nchunks = (pcount + CH - 1) / CH;
   const int last = nchunks - 1;
+  const int row0 = tc.tm * ROWS;  // first row of the block
+  const int mlast = p.M - 1;
   if (nchunks == 0 && wave >= CW) return;  // k = 0: no barrier is ever reached
 
+  if (wave == CW + PW) {
+    // ---------------- weight wave: the block's rows, [row][tap] ----------------
+    const float *wbase = p.A + tc.g * p.a_gstride + (int64_t)min(row0, mlast) * p.lda;
+    uint32_t woff[NW];
+    int wtap[NW];
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const int idx = i * 64 + lane;
+      const int r = idx / BK, t = idx - r * BK;
+      wtap[i] = idx < ROWS * BK ? t : -1;  // beyond the block's rows: never loaded
+      woff[i] = (uint32_t)((int64_t)(min(row0 + r, mlast) - min(row0, mlast)) * p.lda * 4 + 4 * t);
+    }
+    float rw[DW][NW];
+    auto load = [&](int c, auto slot) {
+      constexpr int S = decltype(slot)::value;
+      const int k0 = c * BK;
+      const __amdgpu_buffer_rsrc_t rs = buffer_at(wbase + k0, kRange);
+#pragma unroll
+      for (int i = 0; i < NW; ++i)
+        rw[S][i] = load1(rs, wtap[i] >= 0 && k0 + wtap[i] < p.K ? woff[i] : kOutside);
+    };
+    auto store = [&](auto slot, int st) {
+      constexpr int S = decltype(slot)::value;
+#pragma unroll
+      for (int i = 0; i < NW; ++i)
+        if (i * 64 + lane < ROWS * BK) wstage[st][i * 64 + lane] = rw[S][i];
+    };
+    static_for<DW>([&](auto j) { load(min((int)decltype(j)::value, last), j); });
+    store(std::integral_constant<int, 0>{}, 0);
+    load(min(DW, last), std::integral_constant<int, 0>{});
+    for (int t0 = -1; t0 < nchunks; t0 += U) {
+      static_for<U>([&](auto j) {
+        constexpr int J = decltype(j)::value;
+        const int t = t0 + J;
+        if (t < nchunks) {
+          const int v = t + 2;  // the chunk stored now (slot (J + 1) % DW holds it)
+          store(std::integral_constant<int, (J + 1) % DW>{}, v % NS);
+          load(min(v + DW, last), std::integral_constant<int, (J + 1) % DW>{});
+          __syncthreads();
+        }
+      });
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    return;
+  }
+
   if (wave >= CW) {
-    // ---------------- producer ----------------
-    const int grp = (wave - CW) * (64 / BN) + lane / BN;
-    uint32_t off[TPG];
-    {
+    // ---------------- B producers ----------------
+    const int pw = wave - CW;
+    constexpr int NL = VEC ? 4 * NBL : TPG;  // loads per lane and chunk
+    uint32_t off[NL];
+    int grp = 0, qb[VEC ? NBL : 1], cb[VEC ? NBL : 1];
+    if constexpr (VEC) {
+      // lane -> 4x4 blocks: taps 4qb..4qb+3 of columns 4cb..4cb+3
+#pragma unroll
+      for (int i = 0; i < NBL; ++i) {
+        const int id = i * 64 * PW + pw * 64 + lane;
+        qb[i] = id / (BN / 4);
+        cb[i] = id - qb[i] * (BN / 4);
+        const bool ok = cbase + 4 * cb[i] < ncols;  // ncols is a multiple of 4 here
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          off[4 * i + j] =
+              ok ? (uint32_t)(((int64_t)(4 * qb[i] + j) * pstride + cbase + 4 * cb[i]) * 4) : kOutside;
+      }
+    } else {
+      grp = pw * (64 / BN) + lane / BN;
       uint32_t voff[KHW];
       if (CONV) {
         const int oy = col_ok ? cidx / p.OW : 0;
@@ -991,7 +1068,7 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN>::PW))
           off[j * KHW + t] = (voff[t] == kOutside || o >= (int64_t)kOutside) ? kOutside : (uint32_t)o;
         }
     }
-    float rb[DP][TPG];
+    float rb[DP][VEC ? 16 * NBL : TPG];
     auto load = [&](int c, auto slot) {
       constexpr int S = decltype(slot)::value;
       const int valid = min(max(pcount - c * CH, 0), CH);  // planes of the chunk that exist
@@ -1000,21 +1077,31 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN>::PW))
       const uint32_t range =
           __builtin_amdgcn_readfirstlane((uint32_t)((int64_t)valid * pstride * 4));
       const __amdgpu_buffer_rsrc_t rs = buffer_at(pbase + (int64_t)c * CH * pstride, range);
+      if constexpr (VEC) {
 #pragma unroll
-      for (int e = 0; e < TPG; ++e) rb[S][e] = load1(rs, off[e]);
+        for (int j = 0; j < 4 * NBL; ++j) load4(rs, off[j], &rb[S][4 * j]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < TPG; ++e) rb[S][e] = load1(rs, off[e]);
+      }
     };
     auto store = [&](auto slot, int st) {
       constexpr int S = decltype(slot)::value;
-      float *st0 = reinterpret_cast<float *>(stage[st]);
+      if constexpr (VEC) {
+        // rb[16i + 4j + jj] is (tap 4qb + j, column 4cb + jj) of block i:
+        // store each column's four taps
 #pragma unroll
-      for (int u = 0; u < TPG / WU; ++u) {
-        const int kt = grp * TPG + u * WU;  // first tap of the store within the chunk
-        float *dst = st0 + ((kt / 4) * BN + cl) * 4 + kt % 4;
-        if constexpr (WU == 4)
-          *reinterpret_cast<float4 *>(dst) =
-              make_float4(rb[S][4 * u], rb[S][4 * u + 1], rb[S][4 * u + 2], rb[S][4 * u + 3]);
-        else
-          *reinterpret_cast<float2 *>(dst) = make_float2(rb[S][2 * u], rb[S][2 * u + 1]);
+        for (int i = 0; i < NBL; ++i) {
+          float4 *dst = stage[st] + qb[i] * BN + 4 * cb[i];
+          const float *v = &rb[S][16 * i];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) dst[jj] = make_float4(v[jj], v[4 + jj], v[8 + jj], v[12 + jj]);
+        }
+      } else {
+        float4 *dst = stage[st] + grp * (TPG / 4) * BN + cl;
+#pragma unroll
+        for (int q = 0; q < TPG / 4; ++q)
+          dst[q * BN] = make_float4(rb[S][4 * q], rb[S][4 * q + 1], rb[S][4 * q + 2], rb[S][4 * q + 3]);
       }
     };
     static_for<DP>([&](auto j) { load(min((int)decltype(j)::value, last), j); });
@@ -1037,64 +1124,56 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN>::PW))
   }
 
   // ---------------- compute ----------------
-  const int row_w = tc.tm * ROWS + wave * RW * R;  // first row of the wave
-  const int lrow = row_w + (lane / BN) * R;        // first row of the lane
-  const int mlast = p.M - 1;
-  const float *wbase = p.A + tc.g * p.a_gstride + (int64_t)min(row_w, mlast) * p.lda;
-  uint32_t woff[R];
+  // The chain runs in blocks of 16 taps; block L of the run (chunk L / NB,
+  // block L % NB of it) sits in register slot L % RB, read from LDS LA
+  // blocks before it is used.
+  const int lr = lane / BN;                 // lane row of the wave
+  const int rb0 = wave * RW * R + lr * R;   // the lane's first row within the block
+  float4 bq[RB][4];
+  float wq[RB][R];
+  auto read = [&](auto slot, int st, auto blk) {
+    constexpr int S = decltype(slot)::value, B = decltype(blk)::value;
+    const float4 *src = stage[st] + 4 * B * BN + cl;
 #pragma unroll
-  for (int r = 0; r < R; ++r)
-    woff[r] = (uint32_t)((int64_t)(min(lrow + r, mlast) - min(row_w, mlast)) * p.lda * 4);
-  float wv[DA][R][WR];
-  auto wload = [&](int c, auto slot) {
-    constexpr int S = decltype(slot)::value;
-    const int k0 = c * BK;
-    const __amdgpu_buffer_rsrc_t rs = buffer_at(wbase + k0, kRange);
+    for (int i = 0; i < 4; ++i) bq[S][i] = src[i * BN];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int h = 0; h < WR; ++h) {
-        const int t = 16 * h + (lane & 15);
-        wv[S][r][h] = load1(rs, k0 + t < p.K ? woff[r] + (uint32_t)(4 * t) : kOutside);
-      }
-  };
-  float4 bq[2][NQ];
-  auto read = [&](auto par, int st) {
-    constexpr int P = decltype(par)::value;
-    const float4 *src = stage[st] + cl;
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) bq[P][q] = src[q * BN];
+    for (int r = 0; r < R; ++r) wq[S][r] = wstage[st][(rb0 + r) * BK + 16 * B + (lane & 15)];
   };
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = 0.0f;
 
   if (nchunks > 0) {
-    static_for<DA - 1>([&](auto j) { wload(min((int)decltype(j)::value, last), j); });
-    __syncthreads();
-    read(std::integral_constant<int, 0>{}, 0);
-    for (int t0 = 0; t0 < nchunks; t0 += U) {
-      static_for<U>([&](auto j) {
+    // The compute waves write no LDS, so their barrier needs no fence and no
+    // wait for their own reads (the asm's memory clobber keeps the compiler
+    // from moving LDS reads across it).  Reads never run more than a chunk
+    // ahead, so they only touch stages complete at the previous barrier.
+    asm volatile("s_barrier" ::: "memory");
+    static_for<LA>([&](auto l) {
+      constexpr int L = decltype(l)::value;
+      read(std::integral_constant<int, L % RB>{}, 0, std::integral_constant<int, L % NB>{});
+    });
+    for (int t0 = 0; t0 < nchunks; t0 += UC) {
+      static_for<UC>([&](auto j) {
         constexpr int J = decltype(j)::value;
         const int t = t0 + J;
         if (t < nchunks) {
-          wload(min(t + DA - 1, last), std::integral_constant<int, (J + DA - 1) % DA>{});
-          read(std::integral_constant<int, (J + 1) % 2>{}, (t + 1) % NS);
-          __builtin_amdgcn_sched_barrier(0);
-          static_for<WR>([&](auto h) {
-            constexpr int H = decltype(h)::value;
-            constexpr int N = BK - 16 * H < 16 ? BK - 16 * H : 16;
-            float b[N];
+          static_for<NB>([&](auto bb) {
+            constexpr int L = J * NB + decltype(bb)::value;  // block of the unrolled run
+            constexpr int LN = L + LA;                        // the block read now
+            read(std::integral_constant<int, LN % RB>{}, (t0 + LN / NB) % NS,
+                 std::integral_constant<int, LN % NB>{});
+            __builtin_amdgcn_sched_barrier(0);
+            float b[16];
 #pragma unroll
-            for (int u = 0; u < N; ++u) b[u] = bq[J % 2][(16 * H + u) / 4][u % 4];
+            for (int u = 0; u < 16; ++u) b[u] = bq[L % RB][u / 4][u % 4];
             float w[R];
 #pragma unroll
-            for (int r = 0; r < R; ++r) w[r] = wv[J % DA][r][H];
-            dpp_steps<MODE, R, N>(acc, w, b);
+            for (int r = 0; r < R; ++r) w[r] = wq[L % RB][r];
+            dpp_steps<MODE, R, 16>(acc, w, b);
           });
-          // the barrier waits for this wave's LDS reads: keep it after the chain
           __builtin_amdgcn_sched_barrier(0);
-          __syncthreads();
+          asm volatile("s_barrier" ::: "memory");
         }
       });
     }
@@ -1103,8 +1182,10 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN>::PW))
     float *base = out_ptr<CONV ? kBGather : kBMatrix>(p, tc.g, 0, CONV ? img * p.OHW + cidx : cidx);
     const int64_t rstride = CONV ? (int64_t)p.OHW : p.ldc;
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (lrow + r < p.M) base[(int64_t)(lrow + r) * rstride] = canonical(acc[r]);
+    for (int r = 0; r < R; ++r) {
+      const int row = row0 + rb0 + r;
+      if (row < p.M) base[(int64_t)row * rstride] = canonical(acc[r]);
+    }
   }
 }
 

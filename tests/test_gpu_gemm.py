@@ -134,6 +134,15 @@ def test_chain_kernel_lengths(orc, variant):
             say(f"gemm chain variant {variant} {m}x{n}x{k} mode {mode}")
             got, _ = _run_gpu(A, B, mode, k + 1, n + 3, n, (0, 1, 0))
             assert_same_bits(got, orc.gemm(A, B, mode), f"chain {variant} {m}x{n}x{k} mode {mode}")
+    # B rows 16-byte aligned (ldb and n multiples of 4): the 16-byte producer loads
+    for m, n, k, ldb in ((5, 64, 200, 68), (3, 132, 517, 136), (1, 48, 64, 48), (6, 16, 1, 20)):
+        A = _mixed(rng, (m, k), 0.01)
+        B = _mixed(rng, (k, n), 0.01)
+        for mode in MODES:
+            say(f"gemm chain variant {variant} aligned {m}x{n}x{k} ldb {ldb} mode {mode}")
+            got, _ = _run_gpu(A, B, mode, k, ldb, n + 1, (0, 4, 0))
+            assert_same_bits(got, orc.gemm(A, B, mode),
+                             f"chain {variant} aligned {m}x{n}x{k} mode {mode}")
 
 
 def _sample(rng, m, n, count):
