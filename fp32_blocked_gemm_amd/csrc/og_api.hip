@@ -192,7 +192,7 @@ void launch_lane_conv(int variant, og::Problem p, hipStream_t s) {
 // The chain kernel of variant v for a matrix product (CONV false; VEC: B
 // rows 16-byte aligned, read 16 bytes per load) or a KH x KW convolution; its
 // column tiles of a convolution are BN pixels of one image.
-template <int MODE, bool CONV, bool VEC, int KH, int KW>
+template <int MODE, bool CONV, int LD, int KH, int KW>
 void launch_chain(int v, og::Problem p, hipStream_t s) {
   const int bn = v == 12 ? (KH * KW == 1 ? 16 : 32) : 64;
   const int cw = v == 10 ? 4 : v == 12 ? 1 : 2;  // compute waves
@@ -203,15 +203,15 @@ void launch_chain(int v, og::Problem p, hipStream_t s) {
   const unsigned blocks = (unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)p.groups;
   const dim3 grid(blocks), block(64 * (cw + pw + 1));
   switch (v) {
-    case 10: hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, VEC, KH, KW, 64, 4, 1>), grid, block, 0, s, p); break;
-    case 11: hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, VEC, KH, KW, 64, 2, 1>), grid, block, 0, s, p); break;
+    case 10: hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, LD, KH, KW, 64, 4, 1>), grid, block, 0, s, p); break;
+    case 11: hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, LD, KH, KW, 64, 2, 1>), grid, block, 0, s, p); break;
     case 12:
       if constexpr (KH * KW == 1)
-        hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, VEC, KH, KW, 16, 1, 1>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, LD, KH, KW, 16, 1, 1>), grid, block, 0, s, p);
       else
-        hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, VEC, KH, KW, 32, 1, 1>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, LD, KH, KW, 32, 1, 1>), grid, block, 0, s, p);
       break;
-    default: hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, VEC, KH, KW, 64, 2, 2>), grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, LD, KH, KW, 64, 2, 2>), grid, block, 0, s, p); break;
   }
 }
 
@@ -220,11 +220,17 @@ template <int MODE, int KIND, bool AV, bool BV>
 void launch_tile(const Tile &t, og::Problem p, hipStream_t s) {
   if (is_chain(t)) {
     if (KIND == og::kBMatrix) {
-      if (BV) return launch_chain<MODE, false, true, 1, 1>(t.variant, p, s);
-      return launch_chain<MODE, false, false, 1, 1>(t.variant, p, s);
+      if (BV) return launch_chain<MODE, false, og::kLdVec, 1, 1>(t.variant, p, s);
+      return launch_chain<MODE, false, og::kLdTap, 1, 1>(t.variant, p, s);
     }
-    if (p.KH == 3 && p.KW == 3) return launch_chain<MODE, true, false, 3, 3>(t.variant, p, s);
-    if (p.KH == 1 && p.KW == 1) return launch_chain<MODE, true, false, 1, 1>(t.variant, p, s);
+    if (p.KH == 3 && p.KW == 3) {
+      // a kernel row's three taps in one load: horizontal dilation 1, the
+      // row at least 3 wide, left and right pads at most 1
+      if (p.dW == 1 && p.W >= 3 && p.pL <= 1 && p.pR <= 1)
+        return launch_chain<MODE, true, og::kLdRow3, 3, 3>(t.variant, p, s);
+      return launch_chain<MODE, true, og::kLdTap, 3, 3>(t.variant, p, s);
+    }
+    if (p.KH == 1 && p.KW == 1) return launch_chain<MODE, true, og::kLdTap, 1, 1>(t.variant, p, s);
     // other window sizes: the lane kernel with one row per wave
     return launch_tile<MODE, KIND, AV, BV>(tile_for_variant(6), p, s);
   }
@@ -406,6 +412,7 @@ og_status og_conv2d_f32_ex(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t
   p.sW = (int)strideW;
   p.pT = (int)padTop;
   p.pL = (int)padLeft;
+  p.pR = (int)padRight;
   p.dH = (int)dilH;
   p.dW = (int)dilW;
   p.x_img = Cin * H * W;

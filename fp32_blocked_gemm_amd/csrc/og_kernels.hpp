@@ -68,7 +68,7 @@ struct Problem {
   int M, N, K, groups;
   int tiles_m, tiles_n;
   // convolution only
-  int H, W, HW, OW, OHW, KH, KW, KHW, sH, sW, pT, pL, dH, dW;
+  int H, W, HW, OW, OHW, KH, KW, KHW, sH, sW, pT, pL, pR, dH, dW;  // pR: right pad
   int64_t x_img, x_grp;  // element strides of x between images and between groups
   int64_t y_img, y_grp;  // element strides of y between images and between groups
 };
@@ -141,6 +141,14 @@ __device__ __forceinline__ float load1(__amdgpu_buffer_rsrc_t rs, uint32_t off) 
 // The whole vector is reinterpreted before its elements are taken: taking
 // them one by one from the integer vector made this compiler shrink the load
 // to a single dword.
+__device__ __forceinline__ void load3(__amdgpu_buffer_rsrc_t rs, uint32_t off, float *r) {
+  typedef float f32x3 __attribute__((ext_vector_type(3)));
+  const f32x3 v = __builtin_bit_cast(f32x3, __builtin_amdgcn_raw_buffer_load_b96(rs, off, 0, 0));
+  r[0] = v.x;
+  r[1] = v.y;
+  r[2] = v.z;
+}
+
 __device__ __forceinline__ void load4(__amdgpu_buffer_rsrc_t rs, uint32_t off, float *r) {
   typedef float f32x4 __attribute__((ext_vector_type(4)));
   const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
@@ -933,9 +941,15 @@ struct ChainShape {
   static_assert(PW >= 1 && TPG % 4 == 0 && BK % 16 == 0, "chain chunk shape");
 };
 
-template <int MODE, bool CONV, bool VEC, int KH, int KW, int BN, int CW, int R>
+// How the chain kernel's producers read B: one tap per load; 4x4 blocks of
+// a matrix with 16-byte loads; or, for a 3x3 window with horizontal dilation
+// 1, the three taps of a kernel row with one 12-byte load.
+enum ChainLoad { kLdTap = 0, kLdVec = 1, kLdRow3 = 2 };
+
+template <int MODE, bool CONV, int LD, int KH, int KW, int BN, int CW, int R>
 __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, CW *(64 / BN) * R>::PW + 1))
     chain_kernel(Problem p) {
+  constexpr bool VEC = LD == kLdVec, ROW3 = LD == kLdRow3;
   constexpr int KHW = KH * KW;
   constexpr int RW = 64 / BN;       // lane rows of a compute wave
   constexpr int ROWS = CW * RW * R;  // output rows of a block
@@ -947,6 +961,7 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, CW *(64 / B
   constexpr int NBL = VEC ? BK / 64 : 0;        // 4x4 blocks per producer lane (16-byte loads)
   static_assert(U % DP == 0 && U % DW == 0 && (UC * NB) % RB == 0, "unroll");
   static_assert(!VEC || (!CONV && KHW == 1 && BK % 64 == 0), "16-byte producer loads: matrix B only");
+  static_assert(!ROW3 || (CONV && KH == 3 && KW == 3), "row loads: 3x3 windows only");
   __shared__ __align__(16) float4 stage[NS][NQ * BN];
   __shared__ __align__(16) float wstage[NS][ROWS * BK];
 
@@ -1026,9 +1041,14 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, CW *(64 / B
   if (wave >= CW) {
     // ---------------- B producers ----------------
     const int pw = wave - CW;
-    constexpr int NL = VEC ? 4 * NBL : TPG;  // loads per lane and chunk
+    constexpr int NL = VEC ? 4 * NBL : ROW3 ? TPG / 3 : TPG;  // loads per lane and chunk
     uint32_t off[NL];
     int grp = 0, qb[VEC ? NBL : 1], cb[VEC ? NBL : 1];
+    // row loads: the load of kernel row ky starts at column s0 of the input
+    // row, s0 = clamp(ix0, 0, W-3); tap kx is component kx + d (d = ix0 - s0,
+    // -1, 0 or 1 with left and right pads <= 1) when its column is inside
+    bool kin[3] = {false, false, false};
+    int dsh = 0;
     if constexpr (VEC) {
       // lane -> 4x4 blocks: taps 4qb..4qb+3 of columns 4cb..4cb+3
 #pragma unroll
@@ -1042,6 +1062,28 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, CW *(64 / B
           off[4 * i + j] =
               ok ? (uint32_t)(((int64_t)(4 * qb[i] + j) * pstride + cbase + 4 * cb[i]) * 4) : kOutside;
       }
+    } else if constexpr (ROW3) {
+      grp = pw * (64 / BN) + lane / BN;
+      const int oy = col_ok ? cidx / p.OW : 0;
+      const int ox = col_ok ? cidx - oy * p.OW : 0;
+      const int iy0 = oy * p.sH - p.pT, ix0 = ox * p.sW - p.pL;
+      const int s0 = min(max(ix0, 0), p.W - 3);
+      dsh = ix0 - s0;
+#pragma unroll
+      for (int kx = 0; kx < 3; ++kx) kin[kx] = col_ok && (unsigned)(ix0 + kx) < (unsigned)p.W;
+      uint32_t roff[3];
+#pragma unroll
+      for (int ky = 0; ky < 3; ++ky) {
+        const int iy = iy0 + ky * p.dH;
+        roff[ky] = col_ok && (unsigned)iy < (unsigned)p.H ? (uint32_t)(4 * (iy * p.W + s0)) : kOutside;
+      }
+#pragma unroll
+      for (int j = 0; j < CPG; ++j)
+#pragma unroll
+        for (int ky = 0; ky < 3; ++ky) {
+          const int64_t o = (int64_t)(grp * CPG + j) * pstride * 4 + roff[ky];
+          off[j * 3 + ky] = (roff[ky] == kOutside || o >= (int64_t)kOutside) ? kOutside : (uint32_t)o;
+        }
     } else {
       grp = pw * (64 / BN) + lane / BN;
       uint32_t voff[KHW];
@@ -1080,6 +1122,9 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, CW *(64 / B
       if constexpr (VEC) {
 #pragma unroll
         for (int j = 0; j < 4 * NBL; ++j) load4(rs, off[j], &rb[S][4 * j]);
+      } else if constexpr (ROW3) {
+#pragma unroll
+        for (int e = 0; e < TPG / 3; ++e) load3(rs, off[e], &rb[S][3 * e]);
       } else {
 #pragma unroll
         for (int e = 0; e < TPG; ++e) rb[S][e] = load1(rs, off[e]);
@@ -1098,6 +1143,16 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, CW *(64 / B
           for (int jj = 0; jj < 4; ++jj) dst[jj] = make_float4(v[jj], v[4 + jj], v[8 + jj], v[12 + jj]);
         }
       } else {
+        if constexpr (ROW3) {
+          // the loaded row segments -> the three taps of each kernel row
+#pragma unroll
+          for (int e = 0; e < TPG / 3; ++e) {
+            const float c0 = rb[S][3 * e], c1 = rb[S][3 * e + 1], c2 = rb[S][3 * e + 2];
+            rb[S][3 * e] = kin[0] ? (dsh > 0 ? c1 : c0) : 0.0f;
+            rb[S][3 * e + 1] = kin[1] ? (dsh < 0 ? c0 : dsh > 0 ? c2 : c1) : 0.0f;
+            rb[S][3 * e + 2] = kin[2] ? (dsh < 0 ? c1 : c2) : 0.0f;
+          }
+        }
         float4 *dst = stage[st] + grp * (TPG / 4) * BN + cl;
 #pragma unroll
         for (int q = 0; q < TPG / 4; ++q)

@@ -104,7 +104,13 @@ def test_chain_kernel_shapes(orc, variant):
               synth.ConvShape("c3g", 1, 34, 7, 7, 10, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), 2),
               synth.ConvShape("c1s", 2, 70, 9, 8, 9, 1, 1, (2, 2)),
               synth.ConvShape("c1p", 3, 130, 5, 6, 5, 1, 1),
-              synth.ConvShape("c5", 1, 6, 9, 9, 7, 5, 3, (1, 2), (2, 1, 2, 1))]
+              synth.ConvShape("c5", 1, 6, 9, 9, 7, 5, 3, (1, 2), (2, 1, 2, 1)),
+              # 3x3 row loads: stride 2, the narrowest row, pads 0 and 1 on either side
+              synth.ConvShape("c3s2", 1, 20, 9, 8, 11, 3, 3, (2, 2), (1, 1, 1, 1)),
+              synth.ConvShape("c3w3", 2, 9, 5, 3, 6, 3, 3, (1, 1), (1, 1, 1, 1)),
+              synth.ConvShape("c3p01", 1, 18, 6, 10, 5, 3, 3, (1, 3), (0, 0, 1, 1)),
+              # pads of 2: the tap loads
+              synth.ConvShape("c3p2", 1, 10, 6, 7, 5, 3, 3, (1, 1), (2, 2, 2, 2))]
     for s in shapes:
         x, w = synth.conv_inputs(s, int(rng.integers(1 << 30)), "uniform")
         x = _with_specials(x, rng, 0.01)
