@@ -119,16 +119,16 @@ struct Cost {
   double cap_fast, c_fast, o_fast, cap_exact, c_exact, o_exact;
 };
 constexpr Cost kCosts[] = {
-    {2, 0, 256, 125.54, 9.4, 256, 232.36, 0.0}, {3, 0, 384, 84.05, 4.5, 384, 222.57, 4.7},
-    {4, 0, 384, 51.50, 3.8, 512, 134.27, 3.3},  {5, 0, 256, 38.34, 6.8, 384, 123.02, 4.7},
-    {6, 0, 384, 11.49, 7.1, 384, 12.80, 6.5},   {6, 1, 1024, 11.70, 15.1, 512, 14.61, 12.8},
-    {7, 0, 256, 17.09, 3.8, 256, 21.72, 3.8},   {7, 1, 384, 16.49, 6.2, 384, 21.24, 6.9},
-    {8, 0, 384, 19.36, 4.2, 384, 28.36, 4.6},   {8, 1, 256, 23.08, 1.9, 256, 32.03, 2.6},
-    {9, 0, 384, 29.72, 4.1, 512, 52.36, 4.2},   {9, 1, 128, 32.44, 1.8, 128, 54.15, 2.2},
-    {10, 0, 128, 4.44, 7.9, 128, 5.05, 8.9},    {10, 1, 256, 6.11, 17.7, 256, 5.48, 20.2},
-    {11, 0, 128, 3.55, 9.8, 128, 4.44, 10.5},   {11, 1, 256, 2.50, 33.4, 256, 2.50, 34.9},
-    {12, 0, 256, 2.50, 8.2, 384, 3.97, 9.0},    {12, 1, 512, 2.50, 29.3, 512, 2.50, 33.4},
-    {13, 0, 128, 4.62, 7.8, 128, 6.24, 8.2},    {13, 1, 256, 4.42, 18.8, 256, 5.89, 20.9},
+    {2, 0, 256, 125.78, 9.3, 256, 232.75, 0.0}, {3, 0, 256, 80.24, 5.4, 384, 222.99, 4.7},
+    {4, 0, 384, 51.26, 4.0, 512, 133.91, 3.7}, {5, 0, 256, 38.99, 6.6, 384, 123.49, 4.6},
+    {6, 0, 384, 11.65, 6.7, 384, 12.69, 7.0}, {6, 1, 768, 11.85, 14.9, 512, 14.84, 12.6},
+    {7, 0, 256, 17.00, 3.9, 256, 21.86, 3.8}, {7, 1, 384, 16.36, 6.9, 384, 21.62, 6.0},
+    {8, 0, 384, 19.51, 4.2, 384, 28.70, 4.5}, {8, 1, 256, 23.43, 1.6, 256, 32.17, 2.6},
+    {9, 0, 512, 31.82, 3.8, 512, 52.29, 4.1}, {9, 1, 128, 32.52, 1.5, 128, 54.32, 2.2},
+    {10, 0, 128, 4.48, 8.0, 128, 5.31, 8.0}, {10, 1, 256, 3.08, 14.2, 256, 3.51, 16.3},
+    {11, 0, 128, 3.61, 10.1, 128, 4.51, 10.5}, {11, 1, 256, 2.50, 21.1, 256, 2.50, 26.3},
+    {12, 0, 256, 2.50, 8.1, 384, 4.02, 9.1}, {12, 1, 512, 2.50, 22.5, 512, 2.50, 28.6},
+    {13, 0, 128, 4.67, 7.9, 128, 6.26, 8.2}, {13, 1, 256, 3.67, 14.9, 256, 6.06, 16.2},
 };
 
 // Blocks of a launch of variant t (columns per image where that kernel tiles so).
