@@ -107,28 +107,33 @@ struct Shape {
 };
 
 // Launch time model, fitted to launches of every variant measured on MI355X
-// over the ResNet-50 layers at batch 1 and the matrix products the library
+// over the ResNet-50 layers at batch 1 and 8 and the matrix products the library
 // is benchmarked on: t = c * K * max(1, blocks / cap) + o microseconds, with
 // (cap, c in ns per k step, o) per variant and mode, and for the lane and
-// chain kernels separately for 3x3 windows (whose gathers cost more).  The
+// chain kernels per family: matrix products, 3x3 windows (whose gathers
+// cost more) and other windows.  The
 // chain kernel's step cost is held at >= 2.5 ns when fitting (about six
 // cycles: its dependent chain cannot run faster), so the model does not
 // extrapolate a chain to no cost.
 struct Cost {
-  int variant, win3;
+  int variant, fam;
   double cap_fast, c_fast, o_fast, cap_exact, c_exact, o_exact;
 };
 constexpr Cost kCosts[] = {
-    {2, 0, 256, 125.78, 9.3, 256, 232.75, 0.0}, {3, 0, 256, 80.24, 5.4, 384, 222.99, 4.7},
-    {4, 0, 384, 51.26, 4.0, 512, 133.91, 3.7}, {5, 0, 256, 38.99, 6.6, 384, 123.49, 4.6},
-    {6, 0, 384, 11.65, 6.7, 384, 12.69, 7.0}, {6, 1, 768, 11.85, 14.9, 512, 14.84, 12.6},
-    {7, 0, 256, 17.00, 3.9, 256, 21.86, 3.8}, {7, 1, 384, 16.36, 6.9, 384, 21.62, 6.0},
-    {8, 0, 384, 19.51, 4.2, 384, 28.70, 4.5}, {8, 1, 256, 23.43, 1.6, 256, 32.17, 2.6},
-    {9, 0, 512, 31.82, 3.8, 512, 52.29, 4.1}, {9, 1, 128, 32.52, 1.5, 128, 54.32, 2.2},
-    {10, 0, 128, 4.48, 8.0, 128, 5.31, 8.0}, {10, 1, 256, 3.08, 14.2, 256, 3.51, 16.3},
-    {11, 0, 128, 3.61, 10.1, 128, 4.51, 10.5}, {11, 1, 256, 2.50, 21.1, 256, 2.50, 26.3},
-    {12, 0, 256, 2.50, 8.1, 384, 4.02, 9.1}, {12, 1, 512, 2.50, 22.5, 512, 2.50, 28.6},
-    {13, 0, 128, 4.67, 7.9, 128, 6.26, 8.2}, {13, 1, 256, 3.67, 14.9, 256, 6.06, 16.2},
+    {2, 0, 256, 148.84, 9.8, 128, 210.38, 8.0}, {3, 0, 256, 83.23, 5.6, 256, 216.45, 6.1},
+    {4, 0, 256, 50.83, 4.8, 384, 133.21, 4.9}, {5, 0, 384, 61.33, 6.8, 384, 146.47, 7.4},
+    {6, 0, 512, 12.37, 4.9, 512, 13.71, 6.6}, {6, 1, 384, 12.42, 11.0, 384, 14.86, 10.6},
+    {6, 2, 384, 11.75, 7.0, 384, 12.14, 7.4}, {7, 0, 384, 15.55, 6.2, 256, 15.26, 6.6},
+    {7, 1, 384, 17.18, 6.0, 384, 21.33, 6.3}, {7, 2, 384, 15.55, 6.2, 256, 15.26, 6.6},
+    {8, 0, 512, 20.62, 4.0, 512, 30.07, 4.6}, {8, 1, 384, 22.36, 2.1, 384, 30.59, 3.3},
+    {8, 2, 384, 20.08, 4.0, 384, 26.94, 4.7}, {9, 0, 512, 33.39, 2.8, 512, 53.47, 3.7},
+    {9, 1, 128, 32.52, 1.5, 128, 54.32, 2.2}, {9, 2, 256, 32.22, 3.5, 256, 53.68, 3.4},
+    {10, 0, 256, 7.22, 5.1, 256, 8.41, 4.8}, {10, 1, 128, 3.22, 8.3, 128, 3.68, 9.5},
+    {10, 2, 32, 2.50, 0.0, 128, 6.41, 8.4}, {11, 0, 256, 5.91, 6.6, 256, 7.40, 6.9},
+    {11, 1, 128, 2.98, 6.4, 256, 7.11, 6.6}, {11, 2, 32, 2.50, 0.0, 32, 2.50, 0.0},
+    {12, 0, 384, 2.97, 6.3, 512, 4.49, 6.0}, {12, 1, 512, 2.50, 22.5, 512, 2.50, 28.6},
+    {12, 2, 256, 2.87, 7.7, 256, 3.15, 9.3}, {13, 0, 256, 7.55, 5.0, 256, 10.43, 5.3},
+    {13, 1, 256, 7.25, 6.4, 256, 10.16, 6.7}, {13, 2, 64, 3.01, 7.0, 32, 2.50, 1.8},
 };
 
 // Blocks of a launch of variant t (columns per image where that kernel tiles so).
@@ -141,9 +146,10 @@ int64_t launch_blocks(const Tile &t, const Shape &s) {
 }
 
 double estimate(const Tile &t, const Shape &s, int mode) {
-  const int win3 = (is_lane(t) || is_chain(t)) && s.khw == 9 ? 1 : 0;
+  // window family of the lane and chain kernels: 0 matrix, 1 3x3, 2 other windows
+  const int fam = !(is_lane(t) || is_chain(t)) || s.khw == 0 ? 0 : s.khw == 9 ? 1 : 2;
   for (const Cost &c : kCosts) {
-    if (c.variant != t.variant || c.win3 != win3) continue;
+    if (c.variant != t.variant || c.fam != fam) continue;
     const bool ex = mode == OG_MODE_EXACT;
     const double cap = ex ? c.cap_exact : c.cap_fast;
     const double per = (ex ? c.c_exact : c.c_fast) * 1e-3;
@@ -159,7 +165,7 @@ const Tile &choose_tile(const Shape &s, int mode) {
   int best = 3;
   double best_cost = 1e300;
   for (const Cost &c : kCosts) {
-    if (c.win3) continue;  // each variant once
+    if (c.fam) continue;  // each variant once
     if (c.variant == 9 && mode == OG_MODE_EXACT) continue;  // eight rows per lane: VALU-bound in exact mode
     const double e = estimate(tile_for_variant(c.variant), s, mode);
     if (e < best_cost) {
