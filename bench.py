@@ -26,7 +26,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fp32 GFLOP/s (exact & fast) at 4096^3 + ResNet-50 conv chain ms; % fp32 peak"
 PEAK_FP32_TFLOPS = 157.3        # MI355X dense fp32 (matrix and packed vector)
-EXACT_CEILING_TFLOPS = 78.65    # one separately rounded VALU add per term
+# Exact mode: the matrix cores form each rounded product and a separately
+# rounded non-packed VALU add (32 lanes per clock per SIMD) takes each term;
+# on one SIMD the two do not overlap (measured), so a term costs 1/32 + 1/32
+# clock per SIMD: half the fp32 peak.
+EXACT_CEILING_TFLOPS = 78.65
 HBM_GBPS = 8000.0
 # HBM bytes per launch of the headline kernel, from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs scaled by a 1 GiB copy (factors 2.00 and 1.00; the

@@ -166,6 +166,8 @@ const Tile &choose_tile(const Shape &s, int mode) {
   double best_cost = 1e300;
   for (const Cost &c : kCosts) {
     if (c.fam) continue;  // each variant once
+    // the chain kernel runs windows other than 1x1 and 3x3 as variant 6
+    if (c.variant >= 10 && s.khw != 0 && s.khw != 1 && s.khw != 9) continue;
     if (c.variant == 9 && mode == OG_MODE_EXACT) continue;  // eight rows per lane: VALU-bound in exact mode
     const double e = estimate(tile_for_variant(c.variant), s, mode);
     if (e < best_cost) {
@@ -244,26 +246,41 @@ void launch_tile(const Tile &t, og::Problem p, hipStream_t s) {
     if (p.KH == 3 && p.KW == 3) return launch_lane_conv<MODE, 3, 3>(t.variant, p, s);
     if (p.KH == 1 && p.KW == 1) return launch_lane_conv<MODE, 1, 1>(t.variant, p, s);
   }
-  const Tile &tt = (MODE == og::kExact && t.variant == 2) ? tile_for_variant(3) : t;
+  // Exact mode keeps two k steps of products beside the accumulators: with
+  // two 32x64 blocks per wave (128x256 and 128x128 tiles) that no longer fits
+  // the registers of two waves per SIMD, so variants 2 and 3 run 64x128
+  // tiles.  With gathered B it keeps one product and runs 128x128 tiles.
+  const bool big = t.variant == 2 || t.variant == 3;
+  const Tile &tt = (MODE == og::kExact && big) ? tile_for_variant(KIND == og::kBGather ? 3 : 4) : t;
   p.tiles_m = (int)ceil_div(p.M, tt.bm);
   p.tiles_n = (int)ceil_div(p.N, tt.bn);
   const unsigned blocks = (unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)p.groups;
   const dim3 grid(blocks), block(256);
+  if constexpr (MODE == og::kExact) {
+    if (big) {
+      if constexpr (KIND == og::kBGather)
+        hipLaunchKernelGGL((og::mfma_kernel<MODE, 128, 128, 2, 2, KIND, AV, BV, 2>), grid, block, 0, s, p);
+      else
+        hipLaunchKernelGGL((og::mfma_kernel<MODE, 64, 128, 2, 2, KIND, AV, BV, 4>), grid, block, 0, s, p);
+      return;
+    }
+  }
   switch (t.variant) {
     case 1: hipLaunchKernelGGL((og::valu_kernel<MODE, KIND>), grid, block, 0, s, p); break;
     case 2:
-      // exact mode keeps its products beside 128 accumulators per lane: with
-      // 128x256 tiles that leaves one wave per SIMD, so it runs 128x128 tiles
-      if constexpr (MODE == og::kExact)
-        hipLaunchKernelGGL((og::mfma_kernel<MODE, 128, 128, 2, 2, KIND, AV, BV, 2>), grid, block, 0, s, p);
-      else
+      if constexpr (MODE == og::kFast)
         hipLaunchKernelGGL((og::mfma_kernel<MODE, 128, 256, 2, 2, KIND, AV, BV, 2>), grid, block, 0, s, p);
       break;
-    case 3: hipLaunchKernelGGL((og::mfma_kernel<MODE, 128, 128, 2, 2, KIND, AV, BV, 2>), grid, block, 0, s, p); break;
+    case 3:
+      if constexpr (MODE == og::kFast)
+        hipLaunchKernelGGL((og::mfma_kernel<MODE, 128, 128, 2, 2, KIND, AV, BV, 2>), grid, block, 0, s, p);
+      break;
     case 4: hipLaunchKernelGGL((og::mfma_kernel<MODE, 64, 128, 2, 2, KIND, AV, BV, 4>), grid, block, 0, s, p); break;
     case 5: hipLaunchKernelGGL((og::mfma_kernel<MODE, 32, 256, 1, 4, KIND, AV, BV, 4>), grid, block, 0, s, p); break;
     case 6: hipLaunchKernelGGL((og::lane_kernel<MODE, KIND, 1, 4, 8>), grid, block, 0, s, p); break;
-    case 7: hipLaunchKernelGGL((og::lane_kernel<MODE, KIND, 2, 4, 8>), grid, block, 0, s, p); break;
+    case 7:  // (exact mode: a shallower ring; eight chunks spill the gather's registers)
+      hipLaunchKernelGGL((og::lane_kernel<MODE, KIND, 2, 4, MODE == og::kExact ? 4 : 8>), grid, block, 0, s, p);
+      break;
     case 8: hipLaunchKernelGGL((og::lane_kernel<MODE, KIND, 4, 4, 4>), grid, block, 0, s, p); break;
     default: hipLaunchKernelGGL((og::lane_kernel<MODE, KIND, 8, 4, 2>), grid, block, 0, s, p); break;
   }

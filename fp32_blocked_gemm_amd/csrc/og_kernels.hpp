@@ -412,7 +412,21 @@ __global__ void __launch_bounds__(256) mfma_kernel(Problem p) {
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x32{};
-  f32x32 pend = f32x32{};  // exact mode: the last product made, added one MFMA later
+  // Exact mode, matrix B and input planes: the rounded products of the last
+  // two k steps (k % 2), a step's products added while the next step's are
+  // made.  Exact mode with gathered B: the last product made, added one
+  // MFMA later (two steps of products beside the gather's registers do not
+  // fit two waves per SIMD).
+  constexpr bool kPend = MODE == kExact && KIND == kBGather;
+  constexpr int NPB = MODE == kExact && !kPend ? 2 : 1;
+  f32x32 prod[NPB][TM][TN];
+#pragma unroll
+  for (int u = 0; u < NPB; ++u)
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) prod[u][i][j] = f32x32{};
+  f32x32 pend = f32x32{};
 
   const int a_off = wm * TM * 32 + (lane & 31);
   const int b_off = wn * TN * 64 + lane;
@@ -430,11 +444,8 @@ __global__ void __launch_bounds__(256) mfma_kernel(Problem p) {
       [&](int, auto buf, auto) {
         const float *al = As[decltype(buf)::value];
         const float *bl = Bs[decltype(buf)::value];
-        if (MODE == kExact) {
-          // Exact: a rolled k loop, so only one k's products are live at a
-          // time (unrolled, the compiler makes every product of the chunk
-          // first; they do not depend on the accumulators).  The product
-          // made one MFMA earlier is added while the next one is made.
+        if constexpr (kPend) {
+          // a rolled k loop, so only one k's products are live at a time
 #pragma unroll 2
           for (int kk = 0; kk < BK; ++kk) {
             float a[TM], b[TN];
@@ -446,15 +457,51 @@ __global__ void __launch_bounds__(256) mfma_kernel(Problem p) {
             for (int i = 0; i < TM; ++i)
 #pragma unroll
               for (int j = 0; j < TN; ++j) {
-                const f32x32 prod =
-                    __builtin_amdgcn_mfma_f32_32x32x1f32(a[i], b[j], f32x32{}, 0, 0, 0);
-                const int s = i * TN + j;
+                const f32x32 pr = __builtin_amdgcn_mfma_f32_32x32x1f32(a[i], b[j], f32x32{}, 0, 0, 0);
+                const int s = i * TN + j;  // the product before this one: block s - 1
                 const int pi = s == 0 ? TM - 1 : (s - 1) / TN;
                 const int pj = s == 0 ? TN - 1 : (s - 1) % TN;
                 acc[pi][pj] += pend;  // the first pend is +0: acc stays +0
-                pend = prod;
+                pend = pr;
               }
           }
+          return;
+        } else if constexpr (MODE == kExact) {
+          // Exact: per k the MFMAs form this k's rounded products (C = +0)
+          // in one product buffer while the VALU adds the previous k's
+          // products, from the other buffer, into the accumulators: the
+          // matrix pipe and the VALU work at the same time.  The add of a
+          // product waits a whole k step, past the MFMA's latency.  (The
+          // first adds take the zero-initialised buffer: acc stays +0.)
+          float a[2][TM], b[2][TN];
+#pragma unroll
+          for (int i = 0; i < TM; ++i) a[0][i] = al[a_off + i * 32];
+#pragma unroll
+          for (int j = 0; j < TN; ++j) b[0][j] = bl[b_off + j * 64];
+          auto step = [&](auto uq, int kk) {
+            constexpr int U = decltype(uq)::value;
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+              for (int j = 0; j < TN; ++j)
+                prod[U][i][j] = __builtin_amdgcn_mfma_f32_32x32x1f32(a[U][i], b[U][j], f32x32{}, 0, 0, 0);
+            if (kk + 1 < BK) {
+#pragma unroll
+              for (int i = 0; i < TM; ++i) a[U ^ 1][i] = al[(kk + 1) * LDA + a_off + i * 32];
+#pragma unroll
+              for (int j = 0; j < TN; ++j) b[U ^ 1][j] = bl[(kk + 1) * BN + b_off + j * 64];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+              for (int j = 0; j < TN; ++j) acc[i][j] += prod[U ^ 1][i][j];
+            __builtin_amdgcn_sched_barrier(0);
+          };
+          static_for<BK>([&](auto kq) {
+            constexpr int KK = decltype(kq)::value;
+            step(std::integral_constant<int, KK & 1>{}, KK);
+          });
           return;
         }
         float a[2][TM], b[2][TN];
@@ -478,7 +525,15 @@ __global__ void __launch_bounds__(256) mfma_kernel(Problem p) {
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x1f32(a[u][i], b[u][j], acc[i][j], 0, 0, 0);
         }
       });
-  if (MODE == kExact) acc[TM - 1][TN - 1] += pend;
+  if constexpr (kPend) {
+    acc[TM - 1][TN - 1] += pend;
+  } else if constexpr (MODE == kExact) {
+    // the products of the last k (BK is even: they sit in buffer 1)
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] += prod[NPB - 1][i][j];
+  }
 
   // Epilogue: accumulator register r of lane l in block pair half h = r/16
   // holds row 8*((r%16)/4) + 4*(l/32) + r%4 and column h*32 + l%32 of the

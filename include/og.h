@@ -129,7 +129,8 @@ void *og_get_stream(void);
  * that the results do not depend on it ("Exact mode", rule 5): 0 = chosen
  * from the shape (the default); 1 = the VALU tile kernel (64x64 tiles);
  * 2, 3, 4, 5 = the matrix-core kernel with 128x256, 128x128, 64x128 and
- * 32x256 output tiles (exact mode runs variant 2 with 128x128 tiles);
+ * 32x256 output tiles (exact mode runs variants 2 and 3 with 64x128 tiles,
+ * or 128x128 tiles for a gathered convolution);
  * 6, 7, 8, 9 = the lane kernel (one output column per lane) with 1, 2, 4, 8
  * output rows per wave; 10, 11, 12, 13 = the chain kernel (compute waves
  * that only run the k chain, producer waves that stage B) with 64 columns

@@ -1,9 +1,13 @@
-"""The built gfx950 code respects the DPP read hazard: a register read
-through DPP (the source of a v_*_dpp instruction) is never written by a VALU
-instruction fewer than two wait states before the read.  The compiler does
-not model this hazard through inline asm, so the library's asm blocks start
-with s_nop 1; this test scans the disassembly of the shipped libog.so (the
-library's own device code object) to confirm it."""
+"""Checks of the built gfx950 code object of libog.so (the library's own
+device code, extracted from the shared library):
+
+- the DPP read hazard: a register read through DPP (the source of a
+  v_*_dpp instruction) is never written by a VALU instruction fewer than two
+  wait states before the read.  The compiler does not model this hazard
+  through inline asm, so the library's asm blocks start with s_nop 1; the
+  disassembly confirms it;
+- no kernel spills registers to scratch memory (a spilling kernel is
+  correct but many times slower; the code-object metadata records it)."""
 import os
 import re
 import shutil
@@ -17,20 +21,44 @@ LIB = os.path.join(ROOT, "fp32_blocked_gemm_amd", "libog.so")
 LLVM = "/opt/rocm/llvm/bin"
 
 
-def _disassemble():
+def _code_object(d):
     bundler = os.path.join(LLVM, "clang-offload-bundler")
-    objdump = os.path.join(LLVM, "llvm-objdump")
-    if not (os.path.exists(LIB) and os.path.exists(bundler) and os.path.exists(objdump)
-            and shutil.which("objcopy")):
-        pytest.skip("libog.so or the ROCm binary tools are missing")
+    fat, co = os.path.join(d, "fat.bin"), os.path.join(d, "dev.co")
+    subprocess.run(["objcopy", "--dump-section", f".hip_fatbin={fat}", LIB], check=True)
+    subprocess.run([bundler, "--unbundle", "--type=o",
+                    "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--input={fat}",
+                    f"--output={co}"], check=True)
+    return co
+
+
+def _tools_or_skip():
+    for tool in ("clang-offload-bundler", "llvm-objdump", "llvm-readelf"):
+        if not os.path.exists(os.path.join(LLVM, tool)):
+            pytest.skip(f"{tool} is missing")
+    if not (os.path.exists(LIB) and shutil.which("objcopy")):
+        pytest.skip("libog.so or objcopy is missing")
+
+
+def test_no_kernel_spills():
+    _tools_or_skip()
     with tempfile.TemporaryDirectory() as d:
-        fat, co = os.path.join(d, "fat.bin"), os.path.join(d, "dev.co")
-        subprocess.run(["objcopy", "--dump-section", f".hip_fatbin={fat}", LIB], check=True)
-        subprocess.run([bundler, "--unbundle", "--type=o",
-                        "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--input={fat}",
-                        f"--output={co}"], check=True)
-        out = subprocess.run([objdump, "-d", "--mcpu=gfx950", co], check=True,
-                             capture_output=True, text=True).stdout
+        co = _code_object(d)
+        notes = subprocess.run([os.path.join(LLVM, "llvm-readelf"), "--notes", co], check=True,
+                               capture_output=True, text=True).stdout
+    names = re.findall(r"^\s*\.name:\s+(\S+)", notes, flags=re.M)
+    spills = [int(v) for v in re.findall(r"\.vgpr_spill_count:\s+(\d+)", notes)]
+    sspills = [int(v) for v in re.findall(r"\.sgpr_spill_count:\s+(\d+)", notes)]
+    assert spills and len(spills) == len(sspills)
+    bad = [n for n, v, s in zip(names, spills, sspills) if v or s]
+    assert not bad, f"kernels spilling registers: {bad[:5]}"
+
+
+def _disassemble():
+    _tools_or_skip()
+    with tempfile.TemporaryDirectory() as d:
+        co = _code_object(d)
+        out = subprocess.run([os.path.join(LLVM, "llvm-objdump"), "-d", "--mcpu=gfx950", co],
+                             check=True, capture_output=True, text=True).stdout
     return out
 
 
