@@ -7,6 +7,7 @@
 // every output is summed whole, in one order, by one lane.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -108,8 +109,9 @@ struct Shape {
 
 // Launch time model, fitted to launches of every variant measured on MI355X
 // over the ResNet-50 layers at batch 1 and 8 and the matrix products the library
-// is benchmarked on: t = c * K * max(1, blocks / cap) + o microseconds, with
-// (cap, c in ns per k step, o) per variant and mode, and for the lane and
+// is benchmarked on: t = c * K * rounds + o microseconds, rounds =
+// ceil(blocks / cap) or max(1, blocks / cap), whichever fits that variant
+// better, with (cap, c in ns per k step, o) per variant and mode, and for the lane and
 // chain kernels per family: matrix products, 3x3 windows (whose gathers
 // cost more) and other windows.  The
 // chain kernel's step cost is held at >= 2.5 ns when fitting (about six
@@ -117,23 +119,26 @@ struct Shape {
 // extrapolate a chain to no cost.
 struct Cost {
   int variant, fam;
-  double cap_fast, c_fast, o_fast, cap_exact, c_exact, o_exact;
+  int q_fast;  // 1: whole rounds of cap blocks, ceil(blocks / cap); 0: max(1, blocks / cap)
+  double cap_fast, c_fast, o_fast;
+  int q_exact;
+  double cap_exact, c_exact, o_exact;
 };
 constexpr Cost kCosts[] = {
-    {2, 0, 256, 148.84, 9.8, 128, 210.38, 8.0}, {3, 0, 256, 83.23, 5.6, 256, 216.45, 6.1},
-    {4, 0, 256, 50.83, 4.8, 384, 133.21, 4.9}, {5, 0, 384, 61.33, 6.8, 384, 146.47, 7.4},
-    {6, 0, 512, 12.37, 4.9, 512, 13.71, 6.6}, {6, 1, 384, 12.42, 11.0, 384, 14.86, 10.6},
-    {6, 2, 384, 11.75, 7.0, 384, 12.14, 7.4}, {7, 0, 384, 15.55, 6.2, 256, 15.26, 6.6},
-    {7, 1, 384, 17.18, 6.0, 384, 21.33, 6.3}, {7, 2, 384, 15.55, 6.2, 256, 15.26, 6.6},
-    {8, 0, 512, 20.62, 4.0, 512, 30.07, 4.6}, {8, 1, 384, 22.36, 2.1, 384, 30.59, 3.3},
-    {8, 2, 384, 20.08, 4.0, 384, 26.94, 4.7}, {9, 0, 512, 33.39, 2.8, 512, 53.47, 3.7},
-    {9, 1, 128, 32.52, 1.5, 128, 54.32, 2.2}, {9, 2, 256, 32.22, 3.5, 256, 53.68, 3.4},
-    {10, 0, 256, 7.22, 5.1, 256, 8.41, 4.8}, {10, 1, 128, 3.22, 8.3, 128, 3.68, 9.5},
-    {10, 2, 32, 2.50, 0.0, 128, 6.41, 8.4}, {11, 0, 256, 5.91, 6.6, 256, 7.40, 6.9},
-    {11, 1, 128, 2.98, 6.4, 256, 7.11, 6.6}, {11, 2, 32, 2.50, 0.0, 32, 2.50, 0.0},
-    {12, 0, 384, 2.97, 6.3, 512, 4.49, 6.0}, {12, 1, 512, 2.50, 22.5, 512, 2.50, 28.6},
-    {12, 2, 256, 2.87, 7.7, 256, 3.15, 9.3}, {13, 0, 256, 7.55, 5.0, 256, 10.43, 5.3},
-    {13, 1, 256, 7.25, 6.4, 256, 10.16, 6.7}, {13, 2, 64, 3.01, 7.0, 32, 2.50, 1.8},
+    {2, 0, 1, 256, 154.25, 8.3, 1, 128, 134.82, 3.2}, {3, 0, 1, 256, 82.34, 5.5, 1, 256, 134.09, 3.2},
+    {4, 0, 1, 384, 53.21, 4.1, 1, 384, 117.10, 3.9}, {5, 0, 1, 384, 65.20, 4.6, 1, 384, 132.29, 3.8},
+    {6, 0, 1, 512, 11.99, 5.0, 1, 512, 13.40, 4.7}, {6, 1, 0, 384, 11.83, 14.2, 0, 384, 14.12, 14.1},
+    {6, 2, 0, 384, 11.95, 6.9, 0, 384, 12.24, 7.3}, {7, 0, 1, 512, 14.07, 4.5, 1, 768, 21.12, 3.6},
+    {7, 1, 0, 384, 16.37, 8.5, 0, 384, 19.99, 10.4}, {7, 2, 1, 256, 10.73, 6.2, 1, 512, 20.26, 4.7},
+    {8, 0, 1, 768, 22.39, 3.2, 1, 768, 31.74, 3.8}, {8, 1, 0, 384, 20.99, 5.0, 0, 384, 29.54, 5.3},
+    {8, 2, 0, 384, 20.26, 4.1, 0, 384, 27.26, 4.6}, {9, 0, 1, 384, 23.22, 5.1, 0, 512, 53.04, 3.8},
+    {9, 1, 0, 256, 30.95, 1.9, 0, 384, 54.25, 3.9}, {9, 2, 1, 384, 27.56, 4.0, 0, 384, 50.41, 4.4},
+    {10, 0, 1, 256, 7.16, 5.1, 1, 256, 8.35, 4.8}, {10, 1, 0, 128, 3.19, 9.8, 0, 128, 3.64, 10.4},
+    {10, 2, 1, 32, 2.50, 0.0, 1, 32, 2.50, 0.0}, {11, 0, 1, 256, 5.86, 6.7, 1, 256, 7.23, 6.9},
+    {11, 1, 0, 128, 2.92, 8.4, 0, 128, 3.45, 8.8}, {11, 2, 0, 32, 2.50, 0.0, 0, 32, 2.50, 0.0},
+    {12, 0, 0, 384, 2.97, 6.3, 1, 512, 4.49, 6.0}, {12, 1, 0, 256, 2.89, 10.6, 0, 256, 3.61, 10.8},
+    {12, 2, 0, 256, 3.06, 7.4, 0, 128, 2.50, 1.1}, {13, 0, 1, 256, 7.43, 5.0, 1, 256, 10.35, 5.3},
+    {13, 1, 0, 128, 3.62, 9.3, 0, 128, 5.06, 10.6}, {13, 2, 0, 64, 3.03, 6.7, 1, 32, 2.50, 2.0},
 };
 
 // Blocks of a launch of variant t (columns per image where that kernel tiles so).
@@ -155,7 +160,9 @@ double estimate(const Tile &t, const Shape &s, int mode) {
     const double per = (ex ? c.c_exact : c.c_fast) * 1e-3;
     const double o = ex ? c.o_exact : c.o_fast;
     const double k = (double)(s.K > 0 ? s.K : 1);
-    return per * k * std::max(1.0, (double)launch_blocks(t, s) / cap) + o;
+    const double x = (double)launch_blocks(t, s) / cap;
+    const double rounds = (ex ? c.q_exact : c.q_fast) ? std::ceil(x) : std::max(1.0, x);
+    return per * k * rounds + o;
   }
   return 1e300;
 }
