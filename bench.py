@@ -32,6 +32,7 @@ PEAK_FP32_TFLOPS = 157.3        # MI355X dense fp32 (matrix and packed vector)
 # clock per SIMD: half the fp32 peak.
 EXACT_CEILING_TFLOPS = 78.65
 HBM_GBPS = 8000.0
+COLD_BYTES = 600 << 20  # rotated input copies beyond the 256 MB last-level cache and the L2s
 # HBM bytes per launch of the headline kernel, from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs scaled by a 1 GiB copy (factors 2.00 and 1.00; the
 # summary under profiles/ gives the commands and counts).  Valid only for
@@ -52,7 +53,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", default=None,
                     help="time one workload only (for profiling): gemm4096_fast, gemm4096_exact, "
-                         "resnet_b1, resnet_b8, skinny, prefill, grouped, conv1d, ragged, gemm256, "
+                         "resnet_b1, resnet_b8, skinny, prefill, grouped, conv1d, conv1x1, ragged, "
+                         "gemm256, "
                          "copy (a 1 GiB device copy, to scale the HBM byte counters)")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -144,13 +146,26 @@ def extras(torch, og, synth, timer, only=None):
     def want(name):
         return only is None or only == name
 
-    def gemm_entry(case, modes=("fast", "exact"), bytes_moved=None):
+    def graph_ms(calls):
+        """ms per call of `calls` (a list of closures) replayed from one HIP graph."""
+        g = timer.graph(lambda: [c() for c in calls])
+        ms = timer.spike(g.replay) / len(calls)
+        del g
+        return ms
+
+    def gemm_entry(case, modes=("fast", "exact"), bytes_moved=None, cold_copies=0):
         A, B, C = gemm_workload(torch, og, case)
+        # cold: each call reads its own copy of B, the copies together larger
+        # than the last-level cache, so B comes from HBM
+        Bs = [dev_strided(torch, case.B, case.ldb) for _ in range(cold_copies)]
         ent = {"m": case.m, "n": case.n, "k": case.k, "lda": case.lda, "ldb": case.ldb,
                "ldc": case.ldc}
         for mode in modes:
-            ms = timer.spike(lambda: og.gemm(A, B, mode, out=C))
-            ent[mode] = {"us": round(ms * 1e3, 2),
+            # kernel time: calls replayed from a HIP graph (no host time
+            # between launches); also the calls issued one by one from Python
+            ms = graph_ms([lambda: og.gemm(A, B, mode, out=C)] * 20)
+            ms_eager = timer.spike(lambda: og.gemm(A, B, mode, out=C))
+            ent[mode] = {"us": round(ms * 1e3, 2), "us_eager_launches": round(ms_eager * 1e3, 2),
                          "gflops": round(case.flops / (ms * 1e-3) / 1e9, 1),
                          "frac_peak": round(case.flops / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4)}
             if mode == "exact":
@@ -158,7 +173,34 @@ def extras(torch, og, synth, timer, only=None):
                     case.flops / (ms * 1e-3) / 1e12 / EXACT_CEILING_TFLOPS, 4)
             if bytes_moved:
                 ent[mode]["hbm_gbps_hot"] = round(bytes_moved / (ms * 1e-3) / 1e9, 1)
-        del A, B, C
+            if Bs:
+                ms_cold = graph_ms([(lambda b: lambda: og.gemm(A, b, mode, out=C))(b) for b in Bs])
+                ent[mode]["us_cold"] = round(ms_cold * 1e3, 2)
+                ent[mode]["hbm_gbps_cold"] = round(bytes_moved / (ms_cold * 1e-3) / 1e9, 1)
+        del A, B, C, Bs
+        return ent
+
+    def conv_entry(s, dist, seed, cold_bytes=0):
+        x, w = synth.conv_inputs(s, seed, dist)
+        dx, dw = torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda()
+        y = og.conv2d(dx, dw, stride=s.stride, pad=s.pad, dil=s.dil, groups=s.groups)
+        macs = conv_macs(og, s)
+        nbytes = 4.0 * (x.size + w.size + y.numel())
+        xs = [dx.clone() for _ in range(-(-cold_bytes // (4 * x.size)))] if cold_bytes else []
+        ent = {"shape": repr(s), "gflop": round(2 * macs / 1e9, 4)}
+        for mode in ("fast", "exact"):
+            call = lambda xx: og.conv2d(xx, dw, stride=s.stride, pad=s.pad, dil=s.dil,
+                                        groups=s.groups, mode=mode, out=y)
+            ms = graph_ms([lambda: call(dx)] * 20)
+            ms_eager = timer.spike(lambda: call(dx))
+            ent[mode] = {"us": round(ms * 1e3, 2), "us_eager_launches": round(ms_eager * 1e3, 2),
+                         "gflops": round(2 * macs / (ms * 1e-3) / 1e9, 1),
+                         "tensor_gbps_hot": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+            if xs:
+                ms_cold = graph_ms([(lambda xx: lambda: call(xx))(xx) for xx in xs])
+                ent[mode]["us_cold"] = round(ms_cold * 1e3, 2)
+                ent[mode]["tensor_gbps_cold"] = round(nbytes / (ms_cold * 1e-3) / 1e9, 1)
+        del dx, dw, y, xs
         return ent
 
     if only == "copy":
@@ -185,7 +227,8 @@ def extras(torch, og, synth, timer, only=None):
     if want("skinny"):
         log("extra: skinny")
         c = synth.gemm_skinny()
-        out["gemm_skinny_1x4096x4096"] = gemm_entry(c, bytes_moved=4.0 * (c.k * c.n + c.k + c.n))
+        out["gemm_skinny_1x4096x4096"] = gemm_entry(c, bytes_moved=4.0 * (c.k * c.n + c.k + c.n),
+                                                    cold_copies=10)
     for batch in (1, 8):
         name = f"resnet_b{batch}"
         if not want(name):
@@ -214,18 +257,19 @@ def extras(torch, og, synth, timer, only=None):
             continue
         log(f"extra: {name}")
         s = shape_fn()
-        x, w = synth.conv_inputs(s, synth.seed_for(5, 0), dist)
-        dx, dw = torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda()
-        y = og.conv2d(dx, dw, stride=s.stride, pad=s.pad, dil=s.dil, groups=s.groups)
-        macs = conv_macs(og, s)
-        nbytes = 4.0 * (x.size + w.size + y.numel())
-        ent = {"shape": repr(s), "gflop": round(2 * macs / 1e9, 4)}
-        for mode in ("fast", "exact"):
-            ms = timer.spike(lambda: og.conv2d(dx, dw, stride=s.stride, pad=s.pad, dil=s.dil,
-                                               groups=s.groups, mode=mode, out=y))
-            ent[mode] = {"us": round(ms * 1e3, 2), "gflops": round(2 * macs / (ms * 1e-3) / 1e9, 1),
-                         "tensor_gbps_hot": round(nbytes / (ms * 1e-3) / 1e9, 1)}
-        out[s.name] = ent
+        out[s.name] = conv_entry(s, dist, synth.seed_for(5, 0),
+                                 cold_bytes=COLD_BYTES if name == "grouped" else 0)
+    if want("conv1x1"):
+        # the 1x1 layers of the batch-8 chain, hot and cold (HBM-bound shapes)
+        log("extra: 1x1 layers of the batch-8 chain")
+        seen, ent = set(), {}
+        for i, s in enumerate(synth.resnet50_convs(8)):
+            key = (s.Cin, s.H, s.Cout, s.stride)
+            if s.KH != 1 or key in seen:
+                continue
+            seen.add(key)
+            ent[s.name] = conv_entry(s, "normal", synth.seed_for(4, 200 + i), cold_bytes=COLD_BYTES)
+        out["resnet50_b8_1x1_layers"] = ent
     return out
 
 

@@ -83,11 +83,13 @@ struct Tile {
 // 10..13 the chain kernel: (bn columns, compute waves, rows per lane) =
 // (64, 4, 1), (64, 2, 1), (16, 1, 1) and (64, 2, 2); its 3x3 convolution
 // form of variant 12 has 32 columns.
+// 14..16 the chain kernel with matrix-core chains of 4 rows x 64 columns:
+// (compute waves, chains per wave) = (4, 1), (2, 2), (2, 1).
 constexpr Tile kTiles[] = {{1, 64, 64, 0},  {2, 128, 256, 4}, {3, 128, 128, 2}, {4, 64, 128, 1},
                            {5, 32, 256, 1}, {6, 4, 64, 1},    {7, 8, 64, 2},    {8, 16, 64, 4},
                            {9, 32, 64, 8},  {10, 4, 64, 1},   {11, 2, 64, 1},   {12, 4, 16, 1},
-                           {13, 4, 64, 2}};
-constexpr int kNumVariants = 13;
+                           {13, 4, 64, 2},  {14, 16, 64, 1},  {15, 16, 64, 2},  {16, 8, 64, 1}};
+constexpr int kNumVariants = 16;
 
 const Tile &tile_for_variant(int v) {
   for (const Tile &t : kTiles)
@@ -109,36 +111,60 @@ struct Shape {
 
 // Launch time model, fitted to launches of every variant measured on MI355X
 // over the ResNet-50 layers at batch 1 and 8 and the matrix products the library
-// is benchmarked on: t = c * K * rounds + o microseconds, rounds =
+// is benchmarked on: t = (c * K + d) * rounds + o microseconds, rounds =
 // ceil(blocks / cap) or max(1, blocks / cap), whichever fits that variant
-// better, with (cap, c in ns per k step, o) per variant and mode, and for the lane and
-// chain kernels per family: matrix products, 3x3 windows (whose gathers
-// cost more) and other windows.  The
-// chain kernel's step cost is held at >= 2.5 ns when fitting (about six
-// cycles: its dependent chain cannot run faster), so the model does not
-// extrapolate a chain to no cost.
+// better, with (cap, c in ns per k step, d per round, o) per variant and
+// mode, and for the lane and chain kernels per family: matrix products,
+// 3x3 windows (whose gathers cost more) and other windows.  The chain
+// kernel's step cost is held at >= 2.5 ns when fitting (about six cycles:
+// its dependent chain cannot run faster), so the model does not extrapolate
+// a chain to no cost.  (The exact-mode fields of variants 14..16 are not
+// used: exact mode runs them as 10, 13 and 11.)
 struct Cost {
   int variant, fam;
   int q_fast;  // 1: whole rounds of cap blocks, ceil(blocks / cap); 0: max(1, blocks / cap)
-  double cap_fast, c_fast, o_fast;
+  double cap_fast, c_fast, d_fast, o_fast;
   int q_exact;
-  double cap_exact, c_exact, o_exact;
+  double cap_exact, c_exact, d_exact, o_exact;
 };
 constexpr Cost kCosts[] = {
-    {2, 0, 1, 256, 154.25, 8.3, 1, 128, 134.82, 3.2}, {3, 0, 1, 256, 82.34, 5.5, 1, 256, 134.09, 3.2},
-    {4, 0, 1, 384, 53.21, 4.1, 1, 384, 117.10, 3.9}, {5, 0, 1, 384, 65.20, 4.6, 1, 384, 132.29, 3.8},
-    {6, 0, 1, 512, 11.99, 5.0, 1, 512, 13.40, 4.7}, {6, 1, 0, 384, 11.83, 14.2, 0, 384, 14.12, 14.1},
-    {6, 2, 0, 384, 11.95, 6.9, 0, 384, 12.24, 7.3}, {7, 0, 1, 512, 14.07, 4.5, 1, 768, 21.12, 3.6},
-    {7, 1, 0, 384, 16.37, 8.5, 0, 384, 19.99, 10.4}, {7, 2, 1, 256, 10.73, 6.2, 1, 512, 20.26, 4.7},
-    {8, 0, 1, 768, 22.39, 3.2, 1, 768, 31.74, 3.8}, {8, 1, 0, 384, 20.99, 5.0, 0, 384, 29.54, 5.3},
-    {8, 2, 0, 384, 20.26, 4.1, 0, 384, 27.26, 4.6}, {9, 0, 1, 384, 23.22, 5.1, 0, 512, 53.04, 3.8},
-    {9, 1, 0, 256, 30.95, 1.9, 0, 384, 54.25, 3.9}, {9, 2, 1, 384, 27.56, 4.0, 0, 384, 50.41, 4.4},
-    {10, 0, 1, 256, 7.16, 5.1, 1, 256, 8.35, 4.8}, {10, 1, 0, 128, 3.19, 9.8, 0, 128, 3.64, 10.4},
-    {10, 2, 1, 32, 2.50, 0.0, 1, 32, 2.50, 0.0}, {11, 0, 1, 256, 5.86, 6.7, 1, 256, 7.23, 6.9},
-    {11, 1, 0, 128, 2.92, 8.4, 0, 128, 3.45, 8.8}, {11, 2, 0, 32, 2.50, 0.0, 0, 32, 2.50, 0.0},
-    {12, 0, 0, 384, 2.97, 6.3, 1, 512, 4.49, 6.0}, {12, 1, 0, 256, 2.89, 10.6, 0, 256, 3.61, 10.8},
-    {12, 2, 0, 256, 3.06, 7.4, 0, 128, 2.50, 1.1}, {13, 0, 1, 256, 7.43, 5.0, 1, 256, 10.35, 5.3},
-    {13, 1, 0, 128, 3.62, 9.3, 0, 128, 5.06, 10.6}, {13, 2, 0, 64, 3.03, 6.7, 1, 32, 2.50, 2.0},
+    {2, 0, 1, 256, 153.63, 8.34, 0.0, 1, 128, 132.52, 3.55, 0.0},
+    {3, 0, 0, 256, 83.13, 4.88, 0.3, 1, 256, 132.63, 3.53, 0.0},
+    {4, 0, 1, 384, 52.67, 3.45, 0.2, 0, 384, 121.19, 4.73, 0.0},
+    {5, 0, 1, 384, 64.17, 3.18, 1.1, 0, 384, 136.68, 5.19, 0.0},
+    {6, 0, 1, 512, 11.84, 0.00, 6.1, 1, 768, 16.25, 3.85, 0.0},
+    {6, 1, 0, 384, 11.56, 0.79, 12.1, 0, 384, 13.80, 1.18, 11.4},
+    {6, 2, 1, 512, 13.83, 0.67, 5.0, 1, 512, 14.40, 0.61, 5.4},
+    {7, 0, 1, 768, 16.61, 4.74, 0.0, 1, 768, 20.91, 0.00, 3.6},
+    {7, 1, 0, 384, 16.27, 1.91, 4.9, 0, 384, 20.13, 1.73, 6.6},
+    {7, 2, 0, 384, 14.36, 0.60, 5.5, 1, 512, 19.64, 0.00, 4.8},
+    {8, 0, 1, 768, 20.81, 4.40, 0.2, 1, 768, 31.11, 3.93, 0.0},
+    {8, 1, 0, 384, 21.67, 0.54, 2.8, 0, 384, 29.83, 0.21, 4.5},
+    {8, 2, 0, 384, 19.85, 0.06, 4.0, 0, 384, 26.91, 0.00, 4.7},
+    {9, 0, 1, 384, 23.42, 0.00, 5.1, 0, 512, 52.93, 0.00, 3.8},
+    {9, 1, 0, 256, 31.10, 0.00, 1.9, 0, 384, 54.46, 0.00, 3.2},
+    {9, 2, 1, 384, 27.37, 0.02, 4.0, 0, 384, 50.13, 0.00, 4.5},
+    {10, 0, 0, 256, 6.62, 2.16, 4.1, 1, 256, 7.75, 2.33, 2.7},
+    {10, 1, 0, 256, 4.30, 5.28, 4.8, 0, 256, 4.95, 5.53, 5.5},
+    {10, 2, 0, 256, 6.13, 3.62, 3.6, 1, 256, 7.84, 3.56, 1.6},
+    {11, 0, 0, 256, 5.52, 1.59, 4.0, 0, 256, 6.72, 2.16, 3.3},
+    {11, 1, 0, 256, 3.90, 4.49, 5.9, 0, 256, 4.74, 4.60, 7.2},
+    {11, 2, 1, 128, 2.62, 1.60, 2.0, 1, 128, 3.35, 1.63, 2.3},
+    {12, 0, 0, 768, 4.07, 4.25, 0.0, 0, 768, 5.38, 2.92, 2.2},
+    {12, 1, 0, 512, 4.23, 3.29, 8.1, 0, 256, 2.74, 1.79, 8.2},
+    {12, 2, 0, 512, 3.85, 1.16, 5.3, 0, 256, 2.50, 0.54, 5.3},
+    {13, 0, 0, 256, 6.80, 2.73, 2.5, 1, 256, 9.81, 2.43, 3.1},
+    {13, 1, 0, 256, 5.00, 5.32, 4.3, 0, 256, 7.71, 5.70, 5.2},
+    {13, 2, 1, 256, 7.32, 3.25, 1.5, 1, 256, 9.86, 3.40, 1.1},
+    {14, 0, 1, 256, 13.52, 3.18, 3.4, 1, 32, 3.97, 0.93, 3.1},
+    {14, 1, 0, 256, 9.37, 7.83, 0.0, 1, 64, 5.94, 3.62, 3.7},
+    {14, 2, 1, 256, 11.61, 4.62, 1.8, 1, 64, 7.81, 3.56, 1.5},
+    {15, 0, 1, 256, 12.33, 2.71, 3.1, 1, 64, 9.83, 2.34, 3.2},
+    {15, 1, 0, 256, 10.23, 7.62, 0.0, 1, 64, 9.19, 3.29, 2.5},
+    {15, 2, 1, 256, 11.35, 4.38, 1.4, 1, 64, 9.83, 3.39, 1.5},
+    {16, 0, 0, 256, 8.27, 5.27, 1.6, 1, 32, 3.36, 1.07, 3.3},
+    {16, 1, 0, 256, 7.71, 6.69, 1.4, 0, 64, 4.78, 4.58, 6.3},
+    {16, 2, 1, 256, 8.68, 3.54, 1.4, 1, 32, 3.34, 1.64, 2.0},
 };
 
 // Blocks of a launch of variant t (columns per image where that kernel tiles so).
@@ -158,11 +184,11 @@ double estimate(const Tile &t, const Shape &s, int mode) {
     const bool ex = mode == OG_MODE_EXACT;
     const double cap = ex ? c.cap_exact : c.cap_fast;
     const double per = (ex ? c.c_exact : c.c_fast) * 1e-3;
-    const double o = ex ? c.o_exact : c.o_fast;
+    const double d = ex ? c.d_exact : c.d_fast, o = ex ? c.o_exact : c.o_fast;
     const double k = (double)(s.K > 0 ? s.K : 1);
     const double x = (double)launch_blocks(t, s) / cap;
     const double rounds = (ex ? c.q_exact : c.q_fast) ? std::ceil(x) : std::max(1.0, x);
-    return per * k * rounds + o;
+    return (per * k + d) * rounds + o;
   }
   return 1e300;
 }
@@ -176,6 +202,7 @@ const Tile &choose_tile(const Shape &s, int mode) {
     // the chain kernel runs windows other than 1x1 and 3x3 as variant 6
     if (c.variant >= 10 && s.khw != 0 && s.khw != 1 && s.khw != 9) continue;
     if (c.variant == 9 && mode == OG_MODE_EXACT) continue;  // eight rows per lane: VALU-bound in exact mode
+    if (c.variant >= 14 && mode == OG_MODE_EXACT) continue;  // exact mode runs them as 10, 13, 11
     const double e = estimate(tile_for_variant(c.variant), s, mode);
     if (e < best_cost) {
       best_cost = e;
@@ -209,24 +236,40 @@ void launch_lane_conv(int variant, og::Problem p, hipStream_t s) {
 // column tiles of a convolution are BN pixels of one image.
 template <int MODE, bool CONV, int LD, int KH, int KW>
 void launch_chain(int v, og::Problem p, hipStream_t s) {
+  // Exact mode of the matrix-core chains (14..16) runs the DPP chains of
+  // the same block shape (10, 13, 11): its products made on the matrix
+  // cores would still need a VALU add each, and the compiler cannot keep
+  // their independent products from piling up in registers.
+  if (MODE == og::kExact && v >= 14) v = v == 14 ? 10 : v == 15 ? 13 : 11;
+  const bool mf = v >= 14;
   const int bn = v == 12 ? (KH * KW == 1 ? 16 : 32) : 64;
-  const int cw = v == 10 ? 4 : v == 12 ? 1 : 2;  // compute waves
-  const int rows = cw * (64 / bn) * (v == 13 ? 2 : 1);
+  const int cw = v == 10 || v == 14 ? 4 : v == 12 ? 1 : 2;  // compute waves
+  const int rows = mf ? cw * 4 * (v == 15 ? 2 : 1) : cw * (64 / bn) * (v == 13 ? 2 : 1);
   const int pw = 4 * bn / 64;  // B producer waves (and one weight wave)
   p.tiles_m = (int)ceil_div(p.M, rows);
   p.tiles_n = CONV ? (int)((p.N / p.OHW) * ceil_div(p.OHW, bn)) : (int)ceil_div(p.N, bn);
   const unsigned blocks = (unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)p.groups;
   const dim3 grid(blocks), block(64 * (cw + pw + 1));
   switch (v) {
-    case 10: hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, LD, KH, KW, 64, 4, 1>), grid, block, 0, s, p); break;
-    case 11: hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, LD, KH, KW, 64, 2, 1>), grid, block, 0, s, p); break;
+    case 10: hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, LD, KH, KW, 64, 4, 1, false>), grid, block, 0, s, p); break;
+    case 11: hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, LD, KH, KW, 64, 2, 1, false>), grid, block, 0, s, p); break;
     case 12:
       if constexpr (KH * KW == 1)
-        hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, LD, KH, KW, 16, 1, 1>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, LD, KH, KW, 16, 1, 1, false>), grid, block, 0, s, p);
       else
-        hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, LD, KH, KW, 32, 1, 1>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, LD, KH, KW, 32, 1, 1, false>), grid, block, 0, s, p);
       break;
-    default: hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, LD, KH, KW, 64, 2, 2>), grid, block, 0, s, p); break;
+    case 13: hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, LD, KH, KW, 64, 2, 2, false>), grid, block, 0, s, p); break;
+    default:
+      if constexpr (MODE == og::kFast) {
+        if (v == 14)
+          hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, LD, KH, KW, 64, 4, 1, true>), grid, block, 0, s, p);
+        else if (v == 15)
+          hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, LD, KH, KW, 64, 2, 2, true>), grid, block, 0, s, p);
+        else
+          hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, LD, KH, KW, 64, 2, 1, true>), grid, block, 0, s, p);
+      }
+      break;
   }
 }
 
@@ -367,6 +410,7 @@ og_status og_gemm_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_t l
   p.K = (int)k;
   p.groups = 1;
   const bool av = aligned16(A) && lda % 4 == 0 && k % 4 == 0;
+  p.a_vec = av ? 1 : 0;
   const bool bv = aligned16(B) && ldb % 4 == 0 && n % 4 == 0;
   launch<og::kBMatrix>(mode, av, bv, t, p, t_stream);
   return check_launch("og_gemm_f32");
@@ -450,6 +494,7 @@ og_status og_conv2d_f32_ex(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t
   p.y_img = Cout * OH * OW;
   p.y_grp = cout_g * OH * OW;
   const bool av = aligned16(w) && K % 4 == 0 && (cout_g * K) % 4 == 0;
+  p.a_vec = av ? 1 : 0;
   if (planes)
     launch<og::kBPlanes>(mode, av, false, t, p, t_stream);
   else

@@ -44,6 +44,7 @@
 namespace og {
 
 typedef float f32x32 __attribute__((ext_vector_type(32)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 enum Mode { kExact = 0, kFast = 1 };
 
@@ -71,9 +72,13 @@ struct Problem {
   int H, W, HW, OW, OHW, KH, KW, KHW, sH, sW, pT, pL, pR, dH, dW;  // pR: right pad
   int64_t x_img, x_grp;  // element strides of x between images and between groups
   int64_t y_img, y_grp;  // element strides of y between images and between groups
+  int a_vec;             // A rows 16-byte aligned (A, lda and K multiples of 4 floats)
 };
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I = 0..N-1.
+// Every lambda of the kernels is forced inline: a lambda left as a call
+// takes its captures by address, which puts the kernel's arguments in
+// scratch memory and its buffer descriptors in vector registers.
 template <class F, int... I>
 __device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
   (f(std::integral_constant<int, I>{}), ...);
@@ -150,7 +155,6 @@ __device__ __forceinline__ void load3(__amdgpu_buffer_rsrc_t rs, uint32_t off, f
 }
 
 __device__ __forceinline__ void load4(__amdgpu_buffer_rsrc_t rs, uint32_t off, float *r) {
-  typedef float f32x4 __attribute__((ext_vector_type(4)));
   const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
   r[0] = v.x;
   r[1] = v.y;
@@ -356,10 +360,10 @@ __device__ __forceinline__ void run_pipeline(int nchunks, Load &&load, Store &&s
   static_assert(D >= 2 && D % 2 == 0, "pipeline depth");
   if (nchunks <= 0) return;
   const int last = nchunks - 1;
-  static_for<D - 1>([&](auto j) { load(min((int)decltype(j)::value, last), j); });
+  static_for<D - 1>([&](auto j) __attribute__((always_inline)) { load(min((int)decltype(j)::value, last), j); });
   const int full = nchunks - nchunks % D;
   for (int c0 = 0; c0 < full; c0 += D) {
-    static_for<D>([&](auto j) {
+    static_for<D>([&](auto j) __attribute__((always_inline)) {
       constexpr int J = decltype(j)::value;
       load(min(c0 + J + D - 1, last), std::integral_constant<int, (J + D - 1) % D>{});
       store(j, std::integral_constant<int, J % 2>{});
@@ -367,7 +371,7 @@ __device__ __forceinline__ void run_pipeline(int nchunks, Load &&load, Store &&s
       compute(c0 + J, std::integral_constant<int, J % 2>{}, j);
     });
   }
-  static_for<D - 1>([&](auto j) {
+  static_for<D - 1>([&](auto j) __attribute__((always_inline)) {
     constexpr int J = decltype(j)::value;
     if (full + J < nchunks) {
       store(j, std::integral_constant<int, J % 2>{});
@@ -433,15 +437,15 @@ __global__ void __launch_bounds__(256) mfma_kernel(Problem p) {
 
   run_pipeline<D>(
       (p.K + BK - 1) / BK,
-      [&](int c, auto slot) {
+      [&](int c, auto slot) __attribute__((always_inline)) {
         as.load(p, c * BK, ra[decltype(slot)::value]);
         bs.load(p, c * BK, rb[decltype(slot)::value]);
       },
-      [&](auto slot, auto buf) {
+      [&](auto slot, auto buf) __attribute__((always_inline)) {
         as.template store<LDA>(As[decltype(buf)::value], ra[decltype(slot)::value]);
         bs.store(Bs[decltype(buf)::value], rb[decltype(slot)::value]);
       },
-      [&](int, auto buf, auto) {
+      [&](int, auto buf, auto) __attribute__((always_inline)) {
         const float *al = As[decltype(buf)::value];
         const float *bl = Bs[decltype(buf)::value];
         if constexpr (kPend) {
@@ -478,7 +482,7 @@ __global__ void __launch_bounds__(256) mfma_kernel(Problem p) {
           for (int i = 0; i < TM; ++i) a[0][i] = al[a_off + i * 32];
 #pragma unroll
           for (int j = 0; j < TN; ++j) b[0][j] = bl[b_off + j * 64];
-          auto step = [&](auto uq, int kk) {
+          auto step = [&](auto uq, int kk) __attribute__((always_inline)) {
             constexpr int U = decltype(uq)::value;
 #pragma unroll
             for (int i = 0; i < TM; ++i)
@@ -498,7 +502,7 @@ __global__ void __launch_bounds__(256) mfma_kernel(Problem p) {
               for (int j = 0; j < TN; ++j) acc[i][j] += prod[U ^ 1][i][j];
             __builtin_amdgcn_sched_barrier(0);
           };
-          static_for<BK>([&](auto kq) {
+          static_for<BK>([&](auto kq) __attribute__((always_inline)) {
             constexpr int KK = decltype(kq)::value;
             step(std::integral_constant<int, KK & 1>{}, KK);
           });
@@ -589,15 +593,15 @@ __global__ void __launch_bounds__(256) valu_kernel(Problem p) {
 
   run_pipeline<D>(
       (p.K + BK - 1) / BK,
-      [&](int c, auto slot) {
+      [&](int c, auto slot) __attribute__((always_inline)) {
         as.load(p, c * BK, ra[decltype(slot)::value]);
         bs.load(p, c * BK, rb[decltype(slot)::value]);
       },
-      [&](auto slot, auto buf) {
+      [&](auto slot, auto buf) __attribute__((always_inline)) {
         as.template store<LDA>(As[decltype(buf)::value], ra[decltype(slot)::value]);
         bs.store(Bs[decltype(buf)::value], rb[decltype(slot)::value]);
       },
-      [&](int, auto buf, auto) {
+      [&](int, auto buf, auto) __attribute__((always_inline)) {
         const float *al = As[decltype(buf)::value];
         const float *bl = Bs[decltype(buf)::value];
 #pragma unroll
@@ -696,7 +700,7 @@ __global__ void __launch_bounds__(64 * W) lane_kernel(Problem p) {
 
   run_pipeline<D>(
       (p.K + BK - 1) / BK,
-      [&](int c, auto slot) {
+      [&](int c, auto slot) __attribute__((always_inline)) {
         constexpr int S = decltype(slot)::value;
         const int k0 = c * BK;
         bs.load(p, k0, rb[S]);
@@ -709,20 +713,20 @@ __global__ void __launch_bounds__(64 * W) lane_kernel(Problem p) {
                                 k0 + t < p.K ? (uint32_t)(4 * t) : kOutside);
           }
       },
-      [&](auto slot, auto buf) { bs.store(Bs[decltype(buf)::value], rb[decltype(slot)::value]); },
-      [&](int, auto buf, auto slot) {
+      [&](auto slot, auto buf) __attribute__((always_inline)) { bs.store(Bs[decltype(buf)::value], rb[decltype(slot)::value]); },
+      [&](int, auto buf, auto slot) __attribute__((always_inline)) {
         constexpr int S = decltype(slot)::value;
         const float *bl = Bs[decltype(buf)::value];
         // the chunk's B values first, all issued before the chains (the
         // scheduling barrier keeps the compiler from sinking each read to
         // just before its use, where its latency would stall the chain)
         float bv[BK];
-        static_for<BK>([&](auto kk) {
+        static_for<BK>([&](auto kk) __attribute__((always_inline)) {
           constexpr int KK = decltype(kk)::value;
           bv[KK] = bl[KK * BN + lane];
         });
         __builtin_amdgcn_sched_barrier(0);
-        static_for<BK>([&](auto kk) {
+        static_for<BK>([&](auto kk) __attribute__((always_inline)) {
           constexpr int KK = decltype(kk)::value;
 #pragma unroll
           for (int r = 0; r < R; ++r)
@@ -799,7 +803,7 @@ __global__ void __launch_bounds__(64 * W) lane_conv_kernel(Problem p) {
 
   run_pipeline<D>(
       (cin_g + CC - 1) / CC,
-      [&](int c, auto slot) {
+      [&](int c, auto slot) __attribute__((always_inline)) {
         constexpr int S = decltype(slot)::value;
 #pragma unroll
         for (int cc = 0; cc < CPW; ++cc) {
@@ -820,24 +824,24 @@ __global__ void __launch_bounds__(64 * W) lane_conv_kernel(Problem p) {
                                 k0 + t < p.K ? (uint32_t)(4 * t) : kOutside);
           }
       },
-      [&](auto slot, auto buf) {
+      [&](auto slot, auto buf) __attribute__((always_inline)) {
         float *bl = Bs[decltype(buf)::value];
 #pragma unroll
         for (int j = 0; j < PER; ++j) bl[(wave * PER + j) * BN + lane] = rb[decltype(slot)::value][j];
       },
-      [&](int, auto buf, auto slot) {
+      [&](int, auto buf, auto slot) __attribute__((always_inline)) {
         constexpr int S = decltype(slot)::value;
         const float *bl = Bs[decltype(buf)::value];
         // the chunk's B values first, all issued before the chains (the
         // scheduling barrier keeps the compiler from sinking each read to
         // just before its use, where its latency would stall the chain)
         float bv[BK];
-        static_for<BK>([&](auto kk) {
+        static_for<BK>([&](auto kk) __attribute__((always_inline)) {
           constexpr int KK = decltype(kk)::value;
           bv[KK] = bl[KK * BN + lane];
         });
         __builtin_amdgcn_sched_barrier(0);
-        static_for<BK>([&](auto kk) {
+        static_for<BK>([&](auto kk) __attribute__((always_inline)) {
           constexpr int KK = decltype(kk)::value;
 #pragma unroll
           for (int r = 0; r < R; ++r)
@@ -1001,18 +1005,27 @@ struct ChainShape {
 // 1, the three taps of a kernel row with one 12-byte load.
 enum ChainLoad { kLdTap = 0, kLdVec = 1, kLdRow3 = 2 };
 
-template <int MODE, bool CONV, int LD, int KH, int KW, int BN, int CW, int R>
-__global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, CW *(64 / BN) * R>::PW + 1))
+// Output rows of a chain-kernel block: CW compute waves of (64/BN) lane rows
+// and R rows per lane; with the matrix-core compute (MF) a wave's R chains
+// are 4 rows each.
+constexpr int chain_rows(int CW, int BN, int R, bool MF) { return MF ? CW * 4 * R : CW * (64 / BN) * R; }
+
+template <int MODE, bool CONV, int LD, int KH, int KW, int BN, int CW, int R, bool MF>
+__global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, chain_rows(CW, BN, R, MF)>::PW + 1))
     chain_kernel(Problem p) {
   constexpr bool VEC = LD == kLdVec, ROW3 = LD == kLdRow3;
   constexpr int KHW = KH * KW;
-  constexpr int RW = 64 / BN;       // lane rows of a compute wave
-  constexpr int ROWS = CW * RW * R;  // output rows of a block
+  constexpr int RW = 64 / BN;                    // lane rows of a compute wave
+  constexpr int ROWS = chain_rows(CW, BN, R, MF);  // output rows of a block
+  static_assert(!MF || (BN == 64 && MODE == kFast), "matrix-core chains: 64 columns, fast mode");
   using CS = ChainShape<KHW, BN, ROWS>;
   constexpr int BK = CS::BK, NQ = BK / 4, NB = BK / 16;
   constexpr int TPG = CS::TPG, CPG = CS::CPG, CH = CS::CH, PW = CS::PW, NW = CS::NW;
-  constexpr int NS = 3, DP = 2, DW = 4, U = 4;  // LDS stages, ring depths (B, weights), unroll
-  constexpr int RB = 4, LA = RB - 1, UC = 4;    // compute: register blocks, read-ahead, unroll
+  constexpr int NWV = (ROWS * BK / 4 + 63) / 64;  // 16-byte weight loads per weight-wave lane
+  constexpr int NWM = NW > 4 * NWV ? NW : 4 * NWV;  // weight-wave registers per chunk
+  constexpr int NS = 3, DP = 2, DW = NWM > 20 ? 2 : 4, U = 4;  // LDS stages, ring depths, unroll
+  // compute: register blocks of 16 taps, read-ahead, unroll (in chunks)
+  constexpr int RB = MF ? 3 : 4, LA = RB - 1, UC = MF ? 3 : 4;
   constexpr int NBL = VEC ? BK / 64 : 0;        // 4x4 blocks per producer lane (16-byte loads)
   static_assert(U % DP == 0 && U % DW == 0 && (UC * NB) % RB == 0, "unroll");
   static_assert(!VEC || (!CONV && KHW == 1 && BK % 64 == 0), "16-byte producer loads: matrix B only");
@@ -1049,36 +1062,54 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, CW *(64 / B
 
   if (wave == CW + PW) {
     // ---------------- weight wave: the block's rows, [row][tap] ----------------
+    // With aligned rows (p.a_vec, uniform) each lane loads 16 bytes (4 taps)
+    // per load, NWV loads per chunk; else one tap per load, NW loads.
     const float *wbase = p.A + tc.g * p.a_gstride + (int64_t)min(row0, mlast) * p.lda;
-    uint32_t woff[NW];
-    int wtap[NW];
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
+    const bool wv = p.a_vec != 0;
+    // byte offset of load i of this lane inside a chunk (past the buffer when
+    // the load is beyond the block's rows or beyond k): tap-wise, element idx
+    // of [row][tap]; 16-byte, quad idx of [row][tap/4]
+    auto woffset = [&](int i, int k0, auto vec) __attribute__((always_inline)) -> uint32_t {
+      constexpr bool V = decltype(vec)::value;
+      constexpr int per = V ? BK / 4 : BK, width = V ? 4 : 1, lim = V ? ROWS * BK / 4 : ROWS * BK;
       const int idx = i * 64 + lane;
-      const int r = idx / BK, t = idx - r * BK;
-      wtap[i] = idx < ROWS * BK ? t : -1;  // beyond the block's rows: never loaded
-      woff[i] = (uint32_t)((int64_t)(min(row0 + r, mlast) - min(row0, mlast)) * p.lda * 4 + 4 * t);
-    }
-    float rw[DW][NW];
-    auto load = [&](int c, auto slot) {
+      const int r = idx / per, t = (idx - r * per) * width;
+      if (idx >= lim || k0 + t >= p.K) return kOutside;
+      return (uint32_t)((int64_t)(min(row0 + r, mlast) - min(row0, mlast)) * p.lda * 4 + 4 * t);
+    };
+    float rw[DW][NWM];
+    auto load = [&](int c, auto slot) __attribute__((always_inline)) {
       constexpr int S = decltype(slot)::value;
       const int k0 = c * BK;
       const __amdgpu_buffer_rsrc_t rs = buffer_at(wbase + k0, kRange);
+      if (wv) {
 #pragma unroll
-      for (int i = 0; i < NW; ++i)
-        rw[S][i] = load1(rs, wtap[i] >= 0 && k0 + wtap[i] < p.K ? woff[i] : kOutside);
+        for (int i = 0; i < NWV; ++i)
+          load4(rs, woffset(i, k0, std::true_type{}), &rw[S][4 * i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) rw[S][i] = load1(rs, woffset(i, k0, std::false_type{}));
+      }
     };
-    auto store = [&](auto slot, int st) {
+    auto store = [&](auto slot, int st) __attribute__((always_inline)) {
       constexpr int S = decltype(slot)::value;
+      if (wv) {
 #pragma unroll
-      for (int i = 0; i < NW; ++i)
-        if (i * 64 + lane < ROWS * BK) wstage[st][i * 64 + lane] = rw[S][i];
+        for (int i = 0; i < NWV; ++i)
+          if (i * 64 + lane < ROWS * BK / 4)
+            *reinterpret_cast<float4 *>(&wstage[st][4 * (i * 64 + lane)]) =
+                make_float4(rw[S][4 * i], rw[S][4 * i + 1], rw[S][4 * i + 2], rw[S][4 * i + 3]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < NW; ++i)
+          if (i * 64 + lane < ROWS * BK) wstage[st][i * 64 + lane] = rw[S][i];
+      }
     };
-    static_for<DW>([&](auto j) { load(min((int)decltype(j)::value, last), j); });
+    static_for<DW>([&](auto j) __attribute__((always_inline)) { load(min((int)decltype(j)::value, last), j); });
     store(std::integral_constant<int, 0>{}, 0);
     load(min(DW, last), std::integral_constant<int, 0>{});
     for (int t0 = -1; t0 < nchunks; t0 += U) {
-      static_for<U>([&](auto j) {
+      static_for<U>([&](auto j) __attribute__((always_inline)) {
         constexpr int J = decltype(j)::value;
         const int t = t0 + J;
         if (t < nchunks) {
@@ -1166,7 +1197,7 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, CW *(64 / B
         }
     }
     float rb[DP][VEC ? 16 * NBL : TPG];
-    auto load = [&](int c, auto slot) {
+    auto load = [&](int c, auto slot) __attribute__((always_inline)) {
       constexpr int S = decltype(slot)::value;
       const int valid = min(max(pcount - c * CH, 0), CH);  // planes of the chunk that exist
       // (the range is uniform; readfirstlane keeps the descriptor in scalar
@@ -1185,7 +1216,7 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, CW *(64 / B
         for (int e = 0; e < TPG; ++e) rb[S][e] = load1(rs, off[e]);
       }
     };
-    auto store = [&](auto slot, int st) {
+    auto store = [&](auto slot, int st) __attribute__((always_inline)) {
       constexpr int S = decltype(slot)::value;
       if constexpr (VEC) {
         // rb[16i + 4j + jj] is (tap 4qb + j, column 4cb + jj) of block i:
@@ -1214,11 +1245,11 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, CW *(64 / B
           dst[q * BN] = make_float4(rb[S][4 * q], rb[S][4 * q + 1], rb[S][4 * q + 2], rb[S][4 * q + 3]);
       }
     };
-    static_for<DP>([&](auto j) { load(min((int)decltype(j)::value, last), j); });
+    static_for<DP>([&](auto j) __attribute__((always_inline)) { load(min((int)decltype(j)::value, last), j); });
     store(std::integral_constant<int, 0>{}, 0);
     load(min(DP, last), std::integral_constant<int, 0>{});
     for (int t0 = -1; t0 < nchunks; t0 += U) {
-      static_for<U>([&](auto j) {
+      static_for<U>([&](auto j) __attribute__((always_inline)) {
         constexpr int J = decltype(j)::value;
         const int t = t0 + J;
         if (t < nchunks) {
@@ -1237,21 +1268,46 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, CW *(64 / B
   // The chain runs in blocks of 16 taps; block L of the run (chunk L / NB,
   // block L % NB of it) sits in register slot L % RB, read from LDS LA
   // blocks before it is used.
-  const int lr = lane / BN;                 // lane row of the wave
-  const int rb0 = wave * RW * R + lr * R;   // the lane's first row within the block
+  //
+  // DPP form: lane l owns column l % BN of lane row l / BN, R rows per lane;
+  // the weight register holds 16 taps of a row, one per lane of a row of 16.
+  // Matrix-core form (MF): each of the wave's R chains is 4 rows x 64
+  // columns in one v_mfma_f32_4x4x1_16b_f32 per k: its 16 blocks of 4x4
+  // share the 4 rows; lane l gives the B value of column l and the weight of
+  // row l % 4 (four taps per 16-byte read), and holds the 4 rows of column l
+  // (register i = row i).  Each output element of the instruction is one
+  // fused multiply-add, so a chain over increasing k is fast mode (the only
+  // mode this form runs).
+  const int lr = lane / BN;                 // lane row of the wave (DPP form)
+  const int rb0 = MF ? wave * 4 * R : wave * RW * R + lr * R;  // first row of the lane / wave
   float4 bq[RB][4];
-  float wq[RB][R];
-  auto read = [&](auto slot, int st, auto blk) {
+  float wq[RB][MF ? 1 : R];
+  float4 wa[RB][MF ? R : 1][4];
+  auto read = [&](auto slot, int st, auto blk) __attribute__((always_inline)) {
     constexpr int S = decltype(slot)::value, B = decltype(blk)::value;
     const float4 *src = stage[st] + 4 * B * BN + cl;
 #pragma unroll
     for (int i = 0; i < 4; ++i) bq[S][i] = src[i * BN];
+    if constexpr (MF) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) wq[S][r] = wstage[st][(rb0 + r) * BK + 16 * B + (lane & 15)];
+      for (int c = 0; c < R; ++c) {
+        const float4 *wrow =
+            reinterpret_cast<const float4 *>(&wstage[st][(rb0 + 4 * c + (lane & 3)) * BK + 16 * B]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) wa[S][c][q] = wrow[q];
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) wq[S][r] = wstage[st][(rb0 + r) * BK + 16 * B + (lane & 15)];
+    }
   };
   float acc[R];
+  f32x4 acc4[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+  for (int r = 0; r < R; ++r) {
+    acc[r] = 0.0f;
+    acc4[r] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
 
   if (nchunks > 0) {
     // The compute waves write no LDS, so their barrier needs no fence and no
@@ -1259,34 +1315,59 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, CW *(64 / B
     // from moving LDS reads across it).  Reads never run more than a chunk
     // ahead, so they only touch stages complete at the previous barrier.
     asm volatile("s_barrier" ::: "memory");
-    static_for<LA>([&](auto l) {
+    static_for<LA>([&](auto l) __attribute__((always_inline)) {
       constexpr int L = decltype(l)::value;
       read(std::integral_constant<int, L % RB>{}, 0, std::integral_constant<int, L % NB>{});
     });
     for (int t0 = 0; t0 < nchunks; t0 += UC) {
-      static_for<UC>([&](auto j) {
+      static_for<UC>([&](auto j) __attribute__((always_inline)) {
         constexpr int J = decltype(j)::value;
         const int t = t0 + J;
         if (t < nchunks) {
-          static_for<NB>([&](auto bb) {
+          static_for<NB>([&](auto bb) __attribute__((always_inline)) {
             constexpr int L = J * NB + decltype(bb)::value;  // block of the unrolled run
             constexpr int LN = L + LA;                        // the block read now
             read(std::integral_constant<int, LN % RB>{}, (t0 + LN / NB) % NS,
                  std::integral_constant<int, LN % NB>{});
             __builtin_amdgcn_sched_barrier(0);
-            float b[16];
+            if constexpr (MF) {
+              static_for<16>([&](auto uq) __attribute__((always_inline)) {
+                constexpr int u = decltype(uq)::value;
 #pragma unroll
-            for (int u = 0; u < 16; ++u) b[u] = bq[L % RB][u / 4][u % 4];
-            float w[R];
+                for (int c = 0; c < R; ++c) {
+                  const float a = wa[L % RB][c][u / 4][u % 4], b = bq[L % RB][u / 4][u % 4];
+                  acc4[c] = __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, acc4[c], 0, 0, 0);
+                }
+              });
+            } else {
+              float b[16];
 #pragma unroll
-            for (int r = 0; r < R; ++r) w[r] = wq[L % RB][r];
-            dpp_steps<MODE, R, 16>(acc, w, b);
+              for (int u = 0; u < 16; ++u) b[u] = bq[L % RB][u / 4][u % 4];
+              float w[R];
+#pragma unroll
+              for (int r = 0; r < R; ++r) w[r] = wq[L % RB][r];
+              dpp_steps<MODE, R, 16>(acc, w, b);
+            }
           });
           __builtin_amdgcn_sched_barrier(0);
           asm volatile("s_barrier" ::: "memory");
         }
       });
     }
+  }
+  if constexpr (MF) {
+    if (col_ok) {
+      float *base = out_ptr<CONV ? kBGather : kBMatrix>(p, tc.g, 0, CONV ? img * p.OHW + cidx : cidx);
+      const int64_t rstride = CONV ? (int64_t)p.OHW : p.ldc;
+#pragma unroll
+      for (int c = 0; c < R; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = row0 + rb0 + 4 * c + i;
+          if (row < p.M) base[(int64_t)row * rstride] = canonical(acc4[c][i]);
+        }
+    }
+    return;
   }
   if (col_ok) {
     float *base = out_ptr<CONV ? kBGather : kBMatrix>(p, tc.g, 0, CONV ? img * p.OHW + cidx : cidx);

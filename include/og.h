@@ -136,9 +136,13 @@ void *og_get_stream(void);
  * that only run the k chain, producer waves that stage B) with 64 columns
  * and 4 rows, 64 columns and 2 rows, 16 columns and 4 rows (a 3x3
  * convolution: 32 columns and 2 rows), 64 columns and 4 rows as two rows
- * per lane.  Every variant runs every shape (a convolution window other
- * than 1x1 or 3x3 runs variants 10..13 as variant 6).  A value outside
- * 0..13 returns OG_ERR_INVALID_ARG.
+ * per lane; 14, 15, 16 = the chain kernel whose compute waves run the k
+ * chain on the matrix cores (v_mfma_f32_4x4x1_16b_f32, 4 rows x 64
+ * columns per chain) with 4 waves of 4 rows, 2 waves of 2 x 4 rows and
+ * 2 waves of 4 rows (exact mode runs them as 10, 13 and 11).  Every
+ * variant runs every shape (a convolution window other than 1x1 or 3x3
+ * runs variants 10..16 as variant 6).  A value outside 0..16 returns
+ * OG_ERR_INVALID_ARG.
  */
 og_status og_set_variant(int variant);
 int og_get_variant(void);

@@ -6,8 +6,11 @@ device code, extracted from the shared library):
   wait states before the read.  The compiler does not model this hazard
   through inline asm, so the library's asm blocks start with s_nop 1; the
   disassembly confirms it;
-- no kernel spills registers to scratch memory (a spilling kernel is
-  correct but many times slower; the code-object metadata records it)."""
+- no kernel spills registers to scratch memory or keeps any other data
+  there (a kernel that does is correct but many times slower: a lambda the
+  compiler did not inline once put a kernel's argument block in scratch
+  and made its buffer descriptors non-uniform); the code-object metadata
+  records both."""
 import os
 import re
 import shutil
@@ -51,6 +54,10 @@ def test_no_kernel_spills():
     assert spills and len(spills) == len(sspills)
     bad = [n for n, v, s in zip(names, spills, sspills) if v or s]
     assert not bad, f"kernels spilling registers: {bad[:5]}"
+    private = [int(v) for v in re.findall(r"\.private_segment_fixed_size:\s+(\d+)", notes)]
+    assert len(private) == len(names)
+    bad = [n for n, v in zip(names, private) if v]
+    assert not bad, f"kernels using scratch memory: {bad[:5]}"
 
 
 def _disassemble():

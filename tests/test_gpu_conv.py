@@ -80,7 +80,7 @@ def test_random_shapes(orc, mode):
         assert_same_bits(_gpu_conv(x, w, s, mode), _oracle(orc, x, w, s, mode), f"{s} mode {mode}")
 
 
-@pytest.mark.parametrize("variant", list(range(1, 14)))
+@pytest.mark.parametrize("variant", list(range(1, 17)))
 def test_variants_agree(orc, variant):
     rng = np.random.default_rng(300)
     og.set_variant(variant)
@@ -94,7 +94,7 @@ def test_variants_agree(orc, variant):
                              f"variant {variant} {s} mode {mode}")
 
 
-@pytest.mark.parametrize("variant", [10, 11, 12, 13])
+@pytest.mark.parametrize("variant", [10, 11, 12, 13, 14, 15, 16])
 def test_chain_kernel_shapes(orc, variant):
     """The chain kernel on 3x3 and 1x1 windows (strided, padded, dilated,
     grouped, several chunks of channels) and its fallback for other windows."""

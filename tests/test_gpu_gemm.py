@@ -106,7 +106,7 @@ def test_ragged_ld13_full(orc, specials):
         _check_gaps(flatC, c.m, c.n, c.ldc, 0)
 
 
-@pytest.mark.parametrize("variant", list(range(1, 14)))
+@pytest.mark.parametrize("variant", list(range(1, 17)))
 def test_variants_agree(orc, variant):
     """Every kernel variant gives the oracle's bits (no dependence on tiles)."""
     rng = np.random.default_rng(7)
@@ -120,7 +120,7 @@ def test_variants_agree(orc, variant):
         assert_same_bits(got, orc.gemm(A, B, mode), f"variant {variant} mode {mode}")
 
 
-@pytest.mark.parametrize("variant", [10, 11, 12, 13])
+@pytest.mark.parametrize("variant", [10, 11, 12, 13, 14, 15, 16])
 def test_chain_kernel_lengths(orc, variant):
     """The chain kernel over k from 0 to several chunks, with ragged tails,
     rows and columns that end inside a tile, and special values."""
@@ -135,7 +135,8 @@ def test_chain_kernel_lengths(orc, variant):
             got, _ = _run_gpu(A, B, mode, k + 1, n + 3, n, (0, 1, 0))
             assert_same_bits(got, orc.gemm(A, B, mode), f"chain {variant} {m}x{n}x{k} mode {mode}")
     # B rows 16-byte aligned (ldb and n multiples of 4): the 16-byte producer loads
-    for m, n, k, ldb in ((5, 64, 200, 68), (3, 132, 517, 136), (1, 48, 64, 48), (6, 16, 1, 20)):
+    for m, n, k, ldb in ((5, 64, 200, 68), (3, 132, 517, 136), (1, 48, 64, 48), (6, 16, 1, 20),
+                         (7, 64, 1100, 64)):
         A = _mixed(rng, (m, k), 0.01)
         B = _mixed(rng, (k, n), 0.01)
         for mode in MODES:
@@ -143,6 +144,16 @@ def test_chain_kernel_lengths(orc, variant):
             got, _ = _run_gpu(A, B, mode, k, ldb, n + 1, (0, 4, 0))
             assert_same_bits(got, orc.gemm(A, B, mode),
                              f"chain {variant} aligned {m}x{n}x{k} mode {mode}")
+    # A rows 16-byte aligned (lda and k multiples of 4; k ends inside a chunk): the
+    # 16-byte weight loads; the last case (k not a multiple of 4) loads tap by tap
+    for m, n, k, lda in ((5, 70, 516, 520), (9, 64, 132, 132), (2, 33, 4, 4), (3, 40, 131, 132)):
+        A = _mixed(rng, (m, k), 0.01)
+        B = _mixed(rng, (k, n), 0.01)
+        for mode in MODES:
+            say(f"gemm chain variant {variant} A aligned {m}x{n}x{k} lda {lda} mode {mode}")
+            got, _ = _run_gpu(A, B, mode, lda, n + 1, n, (0, 0, 0))
+            assert_same_bits(got, orc.gemm(A, B, mode),
+                             f"chain {variant} A aligned {m}x{n}x{k} mode {mode}")
 
 
 def _sample(rng, m, n, count):
