@@ -247,6 +247,30 @@ def extras(torch, og, synth, timer, only=None):
                          "gflops": round(2 * macs / (ms * 1e-3) / 1e9, 1),
                          "frac_peak": round(2 * macs / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4)}
             del g
+        # per distinct shape: 20 calls of the layer replayed from a HIP graph;
+        # count x time summed over the shapes should agree with the chain
+        shapes = {}
+        for s, dx, dw, y in layers:
+            key = (s.Cin, s.H, s.Cout, s.KH, s.stride)
+            if key in shapes:
+                shapes[key][1] += 1
+            else:
+                shapes[key] = [(s, dx, dw, y), 1]
+        per = {}
+        for (s, dx, dw, y), cnt in shapes.values():
+            e = {"count": cnt, "shape": f"{s.Cin}->{s.Cout} {s.H}x{s.W} k{s.KH}x{s.KW} s{s.stride[0]}"}
+            for mode in ("fast", "exact"):
+                call = (lambda s_, dx_, dw_, y_, m_: lambda: og.conv2d(
+                    dx_, dw_, stride=s_.stride, pad=s_.pad, dil=s_.dil, groups=s_.groups, mode=m_,
+                    out=y_))(s, dx, dw, y, mode)
+                g = timer.graph(lambda: [call() for _ in range(20)])
+                e[f"{mode}_us"] = round(timer.spike(g.replay, min_ms=30.0) / 20 * 1e3, 2)
+                del g
+            per[s.name] = e
+        ent["per_shape"] = per
+        for mode in ("fast", "exact"):
+            ent[mode]["sum_count_x_shape_ms"] = round(
+                sum(e["count"] * e[f"{mode}_us"] for e in per.values()) / 1e3, 4)
         if batch == 1:
             ent["pages_cpu_context_ms"] = PAGES_RESNET_CPU_MS
         out[f"resnet50_chain_b{batch}"] = ent
@@ -271,6 +295,46 @@ def extras(torch, og, synth, timer, only=None):
             ent[s.name] = conv_entry(s, "normal", synth.seed_for(4, 200 + i), cold_bytes=COLD_BYTES)
         out["resnet50_b8_1x1_layers"] = ent
     return out
+
+
+def cpu_oracle_table(synth, seconds_each=2.0):
+    """The oracle at all threads and at 1 thread, exact and fast, each on the
+    first rows of the 4096^3 product (whole calls for >= seconds_each)."""
+    import oracle
+    orc = oracle.get()
+    c = synth.gemm_4096()
+    full = orc.num_threads()
+    out = {"cpu_model": cpu_model(), "logical_cpus": os.cpu_count(),
+           "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS"), "runs": []}
+    try:
+        for threads in (full, 1):
+            orc.set_num_threads(threads)
+            for mode, name in ((1, "fast"), (0, "exact")):
+                rows = 16 if threads > 1 else 2
+                orc.gemm(c.A[:rows], c.B, mode, rowwise=True)  # warm-up
+                calls, t0 = 0, time.perf_counter()
+                while True:
+                    orc.gemm(c.A[:rows], c.B, mode, rowwise=True)
+                    calls += 1
+                    dt = time.perf_counter() - t0
+                    if dt >= seconds_each:
+                        break
+                out["runs"].append({"threads": threads, "mode": name, "rows": rows, "calls": calls,
+                                    "gflops": round(2.0 * calls * rows * c.n * c.k / dt / 1e9, 3)})
+    finally:
+        orc.set_num_threads(full)
+    return out
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(synth, seconds):
@@ -367,6 +431,7 @@ def main():
     if args.only is None and not args.no_cpu:
         log("cpu baseline: oracle on a bounded sample")
         line["cpu_baseline"] = cpu_baseline(synth, args.cpu_seconds)
+        line.setdefault("extra", {})["cpu_oracle"] = cpu_oracle_table(synth)
     print(json.dumps(line), flush=True)
 
 

@@ -477,23 +477,30 @@ __global__ void __launch_bounds__(256) mfma_kernel(Problem p) {
           // matrix pipe and the VALU work at the same time.  The add of a
           // product waits a whole k step, past the MFMA's latency.  (The
           // first adds take the zero-initialised buffer: acc stays +0.)
-          float a[2][TM], b[2][TN];
+          // Operands are read RA k steps ahead (ring of RA + 1), so a
+          // step's LDS reads have a whole step of adds to return.
+          constexpr int RA = 2;
+          float a[RA + 1][TM], b[RA + 1][TN];
+          static_for<RA>([&](auto rq) __attribute__((always_inline)) {
+            constexpr int R0 = decltype(rq)::value;
 #pragma unroll
-          for (int i = 0; i < TM; ++i) a[0][i] = al[a_off + i * 32];
+            for (int i = 0; i < TM; ++i) a[R0][i] = al[R0 * LDA + a_off + i * 32];
 #pragma unroll
-          for (int j = 0; j < TN; ++j) b[0][j] = bl[b_off + j * 64];
-          auto step = [&](auto uq, int kk) __attribute__((always_inline)) {
-            constexpr int U = decltype(uq)::value;
+            for (int j = 0; j < TN; ++j) b[R0][j] = bl[R0 * BN + b_off + j * 64];
+          });
+          auto step = [&](auto uq, auto kq) __attribute__((always_inline)) {
+            constexpr int U = decltype(uq)::value, KK = decltype(kq)::value;
+            constexpr int S = KK % (RA + 1), SN = (KK + RA) % (RA + 1);
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
               for (int j = 0; j < TN; ++j)
-                prod[U][i][j] = __builtin_amdgcn_mfma_f32_32x32x1f32(a[U][i], b[U][j], f32x32{}, 0, 0, 0);
-            if (kk + 1 < BK) {
+                prod[U][i][j] = __builtin_amdgcn_mfma_f32_32x32x1f32(a[S][i], b[S][j], f32x32{}, 0, 0, 0);
+            if constexpr (KK + RA < BK) {
 #pragma unroll
-              for (int i = 0; i < TM; ++i) a[U ^ 1][i] = al[(kk + 1) * LDA + a_off + i * 32];
+              for (int i = 0; i < TM; ++i) a[SN][i] = al[(KK + RA) * LDA + a_off + i * 32];
 #pragma unroll
-              for (int j = 0; j < TN; ++j) b[U ^ 1][j] = bl[(kk + 1) * BN + b_off + j * 64];
+              for (int j = 0; j < TN; ++j) b[SN][j] = bl[(KK + RA) * BN + b_off + j * 64];
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -504,7 +511,7 @@ __global__ void __launch_bounds__(256) mfma_kernel(Problem p) {
           };
           static_for<BK>([&](auto kq) __attribute__((always_inline)) {
             constexpr int KK = decltype(kq)::value;
-            step(std::integral_constant<int, KK & 1>{}, KK);
+            step(std::integral_constant<int, KK & 1>{}, kq);
           });
           return;
         }

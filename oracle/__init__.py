@@ -80,8 +80,10 @@ class Oracle:
         L.ogref_conv_out_size.restype = _i64
         for name in ("ogref_gemm_f32", "ogref_gemm_f32_rowwise", "ogref_gemm_f32_at",
                      "ogref_conv2d_f32_ex", "ogref_conv2d_im2col_f32_ex",
-                     "ogref_conv2d_f32_at", "ogref_selftest", "ogref_num_threads"):
+                     "ogref_conv2d_f32_at", "ogref_selftest", "ogref_num_threads",
+                     "ogref_set_num_threads"):
             getattr(L, name).restype = ctypes.c_int
+        L.ogref_set_num_threads.argtypes = [ctypes.c_int]
         self.L = L
         if selftest:
             rc = L.ogref_selftest()
@@ -91,6 +93,10 @@ class Oracle:
 
     def num_threads(self) -> int:
         return int(self.L.ogref_num_threads())
+
+    def set_num_threads(self, n: int) -> int:
+        """Threads of later calls (over outputs only: results do not change)."""
+        return int(self.L.ogref_set_num_threads(int(n)))
 
     def gemm(self, A: np.ndarray, B: np.ndarray, mode: int, out: np.ndarray | None = None,
              rowwise: bool = False) -> np.ndarray:

@@ -365,3 +365,15 @@ int ogref_num_threads(void)
     return 1;
 #endif
 }
+
+int ogref_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1)
+        omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}

@@ -81,6 +81,11 @@ int ogref_selftest(void);
 /* Threads an OpenMP region of this library uses. */
 int ogref_num_threads(void);
 
+/* Sets the threads of the library's later OpenMP regions in the calling
+ * thread (n >= 1; other values change nothing) and returns the new count.
+ * The split is over outputs only, so results do not depend on it. */
+int ogref_set_num_threads(int n);
+
 #ifdef __cplusplus
 }
 #endif
