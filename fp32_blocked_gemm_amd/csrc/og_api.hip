@@ -128,43 +128,43 @@ struct Cost {
   double cap_exact, c_exact, d_exact, o_exact;
 };
 constexpr Cost kCosts[] = {
-    {2, 0, 1, 256, 153.63, 8.34, 0.0, 1, 128, 132.52, 3.55, 0.0},
-    {3, 0, 0, 256, 83.13, 4.88, 0.3, 1, 256, 132.63, 3.53, 0.0},
-    {4, 0, 1, 384, 52.67, 3.45, 0.2, 0, 384, 121.19, 4.73, 0.0},
-    {5, 0, 1, 384, 64.17, 3.18, 1.1, 0, 384, 136.68, 5.19, 0.0},
-    {6, 0, 1, 512, 11.84, 0.00, 6.1, 1, 768, 16.25, 3.85, 0.0},
-    {6, 1, 0, 384, 11.56, 0.79, 12.1, 0, 384, 13.80, 1.18, 11.4},
-    {6, 2, 1, 512, 13.83, 0.67, 5.0, 1, 512, 14.40, 0.61, 5.4},
-    {7, 0, 1, 768, 16.61, 4.74, 0.0, 1, 768, 20.91, 0.00, 3.6},
-    {7, 1, 0, 384, 16.27, 1.91, 4.9, 0, 384, 20.13, 1.73, 6.6},
-    {7, 2, 0, 384, 14.36, 0.60, 5.5, 1, 512, 19.64, 0.00, 4.8},
-    {8, 0, 1, 768, 20.81, 4.40, 0.2, 1, 768, 31.11, 3.93, 0.0},
-    {8, 1, 0, 384, 21.67, 0.54, 2.8, 0, 384, 29.83, 0.21, 4.5},
-    {8, 2, 0, 384, 19.85, 0.06, 4.0, 0, 384, 26.91, 0.00, 4.7},
-    {9, 0, 1, 384, 23.42, 0.00, 5.1, 0, 512, 52.93, 0.00, 3.8},
-    {9, 1, 0, 256, 31.10, 0.00, 1.9, 0, 384, 54.46, 0.00, 3.2},
-    {9, 2, 1, 384, 27.37, 0.02, 4.0, 0, 384, 50.13, 0.00, 4.5},
-    {10, 0, 0, 256, 6.62, 2.16, 4.1, 1, 256, 7.75, 2.33, 2.7},
-    {10, 1, 0, 256, 4.30, 5.28, 4.8, 0, 256, 4.95, 5.53, 5.5},
-    {10, 2, 0, 256, 6.13, 3.62, 3.6, 1, 256, 7.84, 3.56, 1.6},
-    {11, 0, 0, 256, 5.52, 1.59, 4.0, 0, 256, 6.72, 2.16, 3.3},
-    {11, 1, 0, 256, 3.90, 4.49, 5.9, 0, 256, 4.74, 4.60, 7.2},
-    {11, 2, 1, 128, 2.62, 1.60, 2.0, 1, 128, 3.35, 1.63, 2.3},
-    {12, 0, 0, 768, 4.07, 4.25, 0.0, 0, 768, 5.38, 2.92, 2.2},
-    {12, 1, 0, 512, 4.23, 3.29, 8.1, 0, 256, 2.74, 1.79, 8.2},
-    {12, 2, 0, 512, 3.85, 1.16, 5.3, 0, 256, 2.50, 0.54, 5.3},
-    {13, 0, 0, 256, 6.80, 2.73, 2.5, 1, 256, 9.81, 2.43, 3.1},
-    {13, 1, 0, 256, 5.00, 5.32, 4.3, 0, 256, 7.71, 5.70, 5.2},
-    {13, 2, 1, 256, 7.32, 3.25, 1.5, 1, 256, 9.86, 3.40, 1.1},
-    {14, 0, 1, 256, 13.52, 3.18, 3.4, 1, 32, 3.97, 0.93, 3.1},
-    {14, 1, 0, 256, 9.37, 7.83, 0.0, 1, 64, 5.94, 3.62, 3.7},
-    {14, 2, 1, 256, 11.61, 4.62, 1.8, 1, 64, 7.81, 3.56, 1.5},
-    {15, 0, 1, 256, 12.33, 2.71, 3.1, 1, 64, 9.83, 2.34, 3.2},
-    {15, 1, 0, 256, 10.23, 7.62, 0.0, 1, 64, 9.19, 3.29, 2.5},
-    {15, 2, 1, 256, 11.35, 4.38, 1.4, 1, 64, 9.83, 3.39, 1.5},
-    {16, 0, 0, 256, 8.27, 5.27, 1.6, 1, 32, 3.36, 1.07, 3.3},
-    {16, 1, 0, 256, 7.71, 6.69, 1.4, 0, 64, 4.78, 4.58, 6.3},
-    {16, 2, 1, 256, 8.68, 3.54, 1.4, 1, 32, 3.34, 1.64, 2.0},
+    {2, 0, 1, 256, 153.84, 8.25, 0.0, 1, 128, 132.12, 3.79, 0.0},
+    {3, 0, 0, 256, 83.30, 4.86, 0.3, 1, 256, 131.64, 3.95, 0.0},
+    {4, 0, 1, 384, 53.07, 3.33, 0.3, 0, 384, 121.31, 4.72, 0.0},
+    {5, 0, 1, 384, 64.48, 2.90, 1.4, 0, 384, 138.20, 4.77, 0.0},
+    {6, 0, 1, 768, 13.72, 3.41, 0.1, 1, 768, 15.63, 0.85, 2.2},
+    {6, 1, 0, 512, 13.71, 0.00, 9.2, 0, 512, 15.25, 0.00, 9.7},
+    {6, 2, 0, 512, 12.55, 0.08, 5.1, 0, 512, 13.25, 0.05, 5.9},
+    {7, 0, 1, 768, 16.16, 0.03, 3.8, 1, 768, 20.56, 0.00, 3.7},
+    {7, 1, 1, 768, 17.65, 1.20, 4.1, 1, 768, 20.99, 0.44, 7.0},
+    {7, 2, 1, 512, 14.93, 0.14, 4.2, 1, 512, 18.45, 0.00, 4.7},
+    {8, 0, 1, 768, 21.61, 3.40, 0.0, 1, 768, 31.43, 3.86, 0.0},
+    {8, 1, 0, 384, 21.40, 0.51, 3.0, 0, 384, 29.79, 0.00, 4.7},
+    {8, 2, 0, 384, 19.33, 0.13, 4.5, 0, 384, 26.98, 0.00, 4.7},
+    {9, 0, 1, 384, 23.29, 0.00, 5.1, 0, 512, 53.17, 0.00, 3.7},
+    {9, 1, 0, 256, 31.54, 0.00, 1.2, 0, 384, 54.72, 0.00, 3.1},
+    {9, 2, 0, 384, 31.33, 0.18, 4.2, 0, 384, 50.41, 0.00, 4.4},
+    {10, 0, 0, 256, 6.79, 1.97, 3.3, 1, 256, 7.76, 2.32, 2.7},
+    {10, 1, 0, 256, 4.26, 5.33, 4.8, 0, 256, 4.93, 5.56, 5.7},
+    {10, 2, 1, 256, 6.63, 3.49, 1.6, 1, 256, 7.96, 3.55, 1.5},
+    {11, 0, 0, 256, 5.39, 1.97, 3.3, 0, 256, 6.74, 2.19, 3.2},
+    {11, 1, 0, 256, 3.93, 4.50, 5.6, 0, 256, 4.78, 4.64, 5.9},
+    {11, 2, 1, 128, 2.60, 1.60, 2.0, 1, 128, 3.37, 1.63, 2.1},
+    {12, 0, 0, 768, 4.08, 4.25, 0.0, 0, 768, 5.38, 2.99, 2.2},
+    {12, 1, 1, 384, 3.03, 2.82, 0.0, 0, 384, 4.15, 2.66, 7.6},
+    {12, 2, 0, 384, 2.91, 0.89, 4.8, 0, 256, 2.50, 0.54, 5.3},
+    {13, 0, 1, 256, 7.01, 2.00, 3.2, 1, 256, 9.82, 2.51, 3.0},
+    {13, 1, 0, 256, 5.04, 5.34, 4.1, 0, 256, 7.72, 5.79, 4.8},
+    {13, 2, 1, 256, 7.21, 3.27, 1.2, 1, 256, 9.88, 3.38, 1.2},
+    {14, 0, 1, 256, 13.54, 2.85, 2.7, 1, 32, 3.88, 1.16, 2.7},
+    {14, 1, 0, 256, 9.38, 7.78, 0.0, 1, 64, 5.98, 3.67, 3.4},
+    {14, 2, 1, 256, 11.77, 4.65, 1.5, 1, 64, 7.79, 3.61, 1.0},
+    {15, 0, 1, 256, 12.33, 2.71, 3.1, 1, 32, 4.92, 1.17, 3.2},
+    {15, 1, 0, 256, 10.11, 7.88, 0.0, 1, 64, 9.23, 3.33, 2.3},
+    {15, 2, 1, 256, 11.13, 4.45, 1.3, 1, 64, 9.76, 3.43, 1.3},
+    {16, 0, 1, 256, 8.88, 2.38, 3.3, 1, 32, 3.37, 1.06, 3.3},
+    {16, 1, 0, 256, 7.75, 6.65, 1.4, 0, 64, 4.79, 4.58, 6.5},
+    {16, 2, 1, 256, 8.72, 3.52, 1.4, 1, 32, 3.34, 1.64, 2.2},
 };
 
 // Blocks of a launch of variant t (columns per image where that kernel tiles so).
@@ -224,8 +224,8 @@ void launch_lane_conv(int variant, og::Problem p, hipStream_t s) {
   const unsigned blocks = (unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)p.groups;
   const dim3 grid(blocks), block(256);
   switch (variant) {
-    case 6: hipLaunchKernelGGL((og::lane_conv_kernel<MODE, KH, KW, 1, 4, 8>), grid, block, 0, s, p); break;
-    case 7: hipLaunchKernelGGL((og::lane_conv_kernel<MODE, KH, KW, 2, 4, 8>), grid, block, 0, s, p); break;
+    case 6: hipLaunchKernelGGL((og::lane_conv_kernel<MODE, KH, KW, 1, 4, 2>), grid, block, 0, s, p); break;
+    case 7: hipLaunchKernelGGL((og::lane_conv_kernel<MODE, KH, KW, 2, 4, 2>), grid, block, 0, s, p); break;
     case 8: hipLaunchKernelGGL((og::lane_conv_kernel<MODE, KH, KW, 4, 4, 2>), grid, block, 0, s, p); break;
     default: hipLaunchKernelGGL((og::lane_conv_kernel<MODE, KH, KW, 8, 4, 2>), grid, block, 0, s, p); break;
   }
@@ -327,10 +327,10 @@ void launch_tile(const Tile &t, og::Problem p, hipStream_t s) {
       break;
     case 4: hipLaunchKernelGGL((og::mfma_kernel<MODE, 64, 128, 2, 2, KIND, AV, BV, 4>), grid, block, 0, s, p); break;
     case 5: hipLaunchKernelGGL((og::mfma_kernel<MODE, 32, 256, 1, 4, KIND, AV, BV, 4>), grid, block, 0, s, p); break;
-    case 6: hipLaunchKernelGGL((og::lane_kernel<MODE, KIND, 1, 4, 8>), grid, block, 0, s, p); break;
-    case 7:  // (exact mode: a shallower ring; eight chunks spill the gather's registers)
-      hipLaunchKernelGGL((og::lane_kernel<MODE, KIND, 2, 4, MODE == og::kExact ? 4 : 8>), grid, block, 0, s, p);
-      break;
+    // (rings of two chunks: deeper rings cost more in occupancy than they
+    // gain in hidden latency, measured on the ResNet-50 layers and products)
+    case 6: hipLaunchKernelGGL((og::lane_kernel<MODE, KIND, 1, 4, 2>), grid, block, 0, s, p); break;
+    case 7: hipLaunchKernelGGL((og::lane_kernel<MODE, KIND, 2, 4, 2>), grid, block, 0, s, p); break;
     case 8: hipLaunchKernelGGL((og::lane_kernel<MODE, KIND, 4, 4, 4>), grid, block, 0, s, p); break;
     default: hipLaunchKernelGGL((og::lane_kernel<MODE, KIND, 8, 4, 2>), grid, block, 0, s, p); break;
   }
