@@ -85,11 +85,13 @@ struct Tile {
 // form of variant 12 has 32 columns.
 // 14..16 the chain kernel with matrix-core chains of 4 rows x 64 columns:
 // (compute waves, chains per wave) = (4, 1), (2, 2), (2, 1).
+// 17 the matrix-core kernel with 256x256 tiles and eight waves.
 constexpr Tile kTiles[] = {{1, 64, 64, 0},  {2, 128, 256, 4}, {3, 128, 128, 2}, {4, 64, 128, 1},
                            {5, 32, 256, 1}, {6, 4, 64, 1},    {7, 8, 64, 2},    {8, 16, 64, 4},
                            {9, 32, 64, 8},  {10, 4, 64, 1},   {11, 2, 64, 1},   {12, 4, 16, 1},
-                           {13, 4, 64, 2},  {14, 16, 64, 1},  {15, 16, 64, 2},  {16, 8, 64, 1}};
-constexpr int kNumVariants = 16;
+                           {13, 4, 64, 2},  {14, 16, 64, 1},  {15, 16, 64, 2},  {16, 8, 64, 1},
+                           {17, 256, 256, 4}};
+constexpr int kNumVariants = 17;
 
 const Tile &tile_for_variant(int v) {
   for (const Tile &t : kTiles)
@@ -98,7 +100,7 @@ const Tile &tile_for_variant(int v) {
 }
 
 bool is_lane(const Tile &t) { return t.variant >= 6 && t.variant <= 9; }
-bool is_chain(const Tile &t) { return t.variant >= 10; }
+bool is_chain(const Tile &t) { return t.variant >= 10 && t.variant <= 16; }
 
 // The shape the kernel choice sees: a group's product (M x N x K) and, for
 // a convolution, the pixels of one output image and the window size (the
@@ -129,51 +131,54 @@ struct Cost {
   double cap_exact, c_exact, d_exact, o_exact;
 };
 constexpr Cost kCosts[] = {
-    {2, 0, 0, 256, 126.09, 0.00, 9.2, 1, 128, 107.95, 2.33, 0.0},
-    {2, 1, 0, 256, 197.97, 1.17, 7.2, 0, 256, 234.80, 12.34, 0.0},
-    {2, 2, 0, 128, 132.29, 0.00, 10.0, 0, 128, 116.37, 5.68, 0.0},
-    {3, 0, 1, 256, 64.21, 0.00, 7.0, 1, 256, 107.83, 2.36, 0.0},
-    {3, 1, 1, 384, 103.87, 3.00, 3.6, 1, 384, 237.90, 0.11, 7.3},
-    {3, 2, 1, 256, 77.04, 3.55, 2.3, 1, 256, 116.75, 5.18, 0.0},
-    {4, 0, 1, 384, 41.74, 3.34, 0.0, 1, 512, 107.78, 2.36, 0.0},
-    {4, 1, 1, 384, 73.69, 1.64, 5.2, 0, 384, 150.58, 2.04, 4.7},
-    {4, 2, 1, 256, 47.68, 0.94, 3.5, 0, 384, 113.15, 5.37, 0.0},
-    {5, 0, 1, 384, 46.41, 4.27, 0.0, 1, 512, 115.40, 2.48, 0.0},
-    {5, 1, 0, 384, 115.23, 5.94, 0.0, 0, 384, 216.28, 0.00, 5.3},
-    {5, 2, 1, 256, 59.07, 0.44, 3.5, 0, 256, 123.15, 0.00, 4.9},
-    {6, 0, 1, 768, 13.91, 2.85, 0.6, 1, 768, 16.06, 0.27, 2.6},
-    {6, 1, 0, 512, 13.62, 0.00, 8.6, 0, 512, 14.90, 0.00, 8.8},
-    {6, 2, 0, 512, 12.76, 0.06, 4.9, 0, 512, 13.13, 0.05, 5.9},
-    {7, 0, 1, 768, 16.28, 0.00, 3.8, 1, 768, 20.62, 0.00, 3.7},
-    {7, 1, 1, 768, 17.71, 0.91, 3.5, 1, 768, 21.37, 0.00, 5.9},
-    {7, 2, 1, 512, 14.49, 0.07, 4.5, 1, 512, 18.43, 0.00, 4.5},
-    {8, 0, 1, 768, 21.36, 2.82, 0.6, 1, 768, 32.03, 0.00, 3.7},
-    {8, 1, 0, 384, 21.39, 0.13, 3.3, 0, 384, 30.55, 0.00, 2.4},
-    {8, 2, 0, 512, 23.34, 0.34, 3.1, 0, 768, 37.74, 1.76, 1.5},
-    {9, 0, 1, 384, 23.35, 0.00, 5.1, 0, 512, 53.00, 0.00, 3.8},
-    {9, 1, 0, 384, 32.64, 0.31, 3.0, 0, 384, 55.75, 0.00, 0.8},
-    {9, 2, 0, 384, 31.50, 0.30, 3.5, 0, 384, 50.09, 0.00, 4.4},
-    {10, 0, 0, 256, 6.81, 1.87, 3.4, 1, 256, 7.78, 2.23, 2.8},
-    {10, 1, 0, 256, 4.22, 5.27, 5.0, 0, 256, 4.85, 5.54, 5.4},
-    {10, 2, 1, 256, 6.64, 3.48, 1.4, 1, 256, 7.88, 3.53, 1.4},
-    {11, 0, 0, 256, 5.38, 1.91, 3.4, 0, 256, 6.73, 2.16, 3.2},
-    {11, 1, 0, 256, 3.93, 4.47, 5.1, 0, 256, 4.80, 4.63, 5.3},
-    {11, 2, 1, 128, 2.64, 1.58, 1.6, 1, 128, 3.34, 1.65, 1.7},
-    {12, 0, 0, 768, 4.08, 4.25, 0.0, 1, 768, 5.79, 2.00, 1.1},
-    {12, 1, 0, 384, 3.19, 2.48, 7.1, 0, 256, 2.77, 1.79, 6.7},
-    {12, 2, 0, 384, 2.87, 0.88, 4.8, 0, 256, 2.50, 0.55, 4.6},
-    {13, 0, 1, 256, 7.04, 1.90, 3.3, 1, 256, 9.84, 2.42, 3.1},
-    {13, 1, 0, 256, 4.99, 5.34, 3.9, 0, 256, 7.71, 5.77, 4.5},
-    {13, 2, 0, 256, 6.70, 3.44, 2.6, 1, 256, 9.88, 3.40, 1.0},
-    {14, 0, 1, 256, 13.73, 2.69, 2.8, 1, 32, 3.89, 1.12, 2.8},
-    {14, 1, 0, 256, 9.31, 7.69, 0.0, 1, 64, 5.99, 3.51, 3.4},
-    {14, 2, 1, 256, 11.84, 4.54, 1.6, 1, 64, 7.75, 3.55, 1.4},
-    {15, 0, 1, 256, 12.55, 2.20, 3.6, 1, 64, 9.82, 2.51, 3.0},
-    {15, 1, 0, 256, 10.28, 7.43, 0.0, 1, 64, 9.25, 3.24, 2.3},
-    {15, 2, 1, 256, 11.08, 4.40, 1.4, 1, 64, 9.90, 3.37, 1.2},
-    {16, 0, 0, 256, 8.52, 4.44, 1.4, 1, 32, 3.36, 1.06, 3.3},
-    {16, 1, 0, 256, 7.68, 6.49, 1.6, 0, 64, 4.83, 4.51, 6.1},
-    {16, 2, 1, 256, 8.60, 3.52, 1.5, 1, 32, 3.34, 1.64, 1.8},
+    {2, 0, 0, 256, 125.31, 0.00, 9.4, 1, 128, 107.50, 2.46, 0.0},
+    {2, 1, 0, 256, 197.45, 0.00, 9.6, 0, 256, 234.52, 12.36, 0.0},
+    {2, 2, 0, 128, 131.95, 0.00, 10.2, 1, 128, 117.10, 5.28, 0.0},
+    {3, 0, 1, 256, 63.76, 0.00, 7.1, 1, 256, 107.61, 2.45, 0.0},
+    {3, 1, 1, 384, 103.58, 2.92, 3.9, 1, 384, 237.74, 0.13, 7.3},
+    {3, 2, 1, 256, 76.89, 3.56, 2.3, 1, 384, 117.04, 5.18, 0.0},
+    {4, 0, 1, 384, 41.11, 3.52, 0.0, 1, 512, 107.32, 2.49, 0.0},
+    {4, 1, 1, 384, 73.95, 1.87, 4.4, 0, 384, 150.49, 2.09, 4.5},
+    {4, 2, 1, 256, 47.75, 0.80, 3.6, 0, 256, 107.39, 0.63, 4.6},
+    {5, 0, 1, 384, 45.55, 4.49, 0.0, 1, 512, 114.71, 2.63, 0.0},
+    {5, 1, 0, 384, 115.18, 5.91, 0.0, 0, 384, 215.93, 0.45, 5.7},
+    {5, 2, 1, 256, 58.70, 0.37, 3.6, 0, 256, 122.63, 0.00, 4.9},
+    {6, 0, 1, 768, 13.57, 3.45, 0.1, 1, 768, 15.27, 1.87, 2.2},
+    {6, 1, 0, 512, 13.48, 0.00, 8.7, 0, 512, 14.85, 0.00, 8.9},
+    {6, 2, 1, 512, 12.49, 0.06, 4.5, 0, 512, 13.11, 0.04, 6.0},
+    {7, 0, 1, 768, 16.14, 0.00, 3.9, 1, 768, 20.41, 0.00, 3.8},
+    {7, 1, 1, 768, 17.58, 0.80, 3.8, 1, 768, 21.17, 0.00, 5.9},
+    {7, 2, 1, 512, 14.55, 0.04, 4.5, 1, 512, 18.33, 0.00, 4.6},
+    {8, 0, 1, 768, 21.41, 2.69, 0.8, 1, 768, 32.08, 0.70, 2.0},
+    {8, 1, 0, 384, 21.34, 0.00, 3.3, 0, 384, 30.40, 0.00, 2.7},
+    {8, 2, 1, 512, 22.65, 0.00, 3.4, 0, 768, 37.84, 1.55, 1.8},
+    {9, 0, 1, 384, 23.24, 0.00, 5.1, 0, 512, 53.02, 0.00, 3.8},
+    {9, 1, 0, 384, 32.64, 0.07, 3.2, 0, 384, 55.57, 0.00, 0.9},
+    {9, 2, 0, 384, 31.67, 0.23, 3.6, 0, 384, 50.09, 0.00, 4.4},
+    {10, 0, 0, 256, 6.81, 1.78, 3.5, 1, 256, 7.76, 2.24, 2.8},
+    {10, 1, 0, 256, 4.14, 5.33, 5.0, 0, 256, 4.79, 5.58, 5.3},
+    {10, 2, 1, 256, 6.54, 3.48, 1.7, 1, 256, 7.81, 3.55, 1.5},
+    {11, 0, 0, 256, 5.38, 1.94, 3.3, 0, 256, 6.73, 2.13, 3.3},
+    {11, 1, 0, 256, 3.92, 4.48, 5.0, 0, 256, 4.80, 4.58, 5.5},
+    {11, 2, 1, 128, 2.60, 1.59, 1.8, 1, 128, 3.33, 1.64, 1.8},
+    {12, 0, 0, 768, 4.06, 4.23, 0.0, 0, 768, 5.37, 2.80, 2.4},
+    {12, 1, 0, 384, 3.18, 2.49, 7.0, 0, 384, 4.14, 2.68, 6.9},
+    {12, 2, 0, 384, 2.83, 0.88, 5.0, 0, 256, 2.50, 0.54, 5.0},
+    {13, 0, 0, 256, 6.79, 2.74, 2.5, 1, 256, 9.99, 2.14, 2.3},
+    {13, 1, 0, 256, 4.95, 5.29, 4.3, 0, 256, 7.66, 5.79, 4.6},
+    {13, 2, 0, 256, 6.68, 3.45, 2.6, 1, 256, 9.85, 3.39, 1.2},
+    {14, 0, 1, 256, 13.53, 2.85, 2.7, 1, 32, 3.88, 1.08, 2.9},
+    {14, 1, 0, 256, 9.41, 7.59, 0.0, 1, 64, 5.91, 3.57, 3.5},
+    {14, 2, 1, 256, 11.72, 4.56, 1.6, 1, 64, 7.77, 3.56, 1.4},
+    {15, 0, 1, 256, 12.32, 2.71, 3.1, 1, 64, 9.80, 2.52, 3.0},
+    {15, 1, 0, 256, 10.21, 7.46, 0.0, 1, 64, 9.17, 3.22, 2.9},
+    {15, 2, 1, 256, 11.18, 4.34, 1.5, 1, 64, 9.87, 3.39, 1.3},
+    {16, 0, 1, 256, 8.88, 2.21, 3.5, 1, 32, 3.36, 1.04, 3.4},
+    {16, 1, 0, 256, 7.64, 6.56, 1.6, 0, 64, 4.78, 4.57, 6.3},
+    {16, 2, 1, 256, 8.58, 3.51, 1.5, 1, 32, 3.32, 1.64, 2.0},
+    {17, 0, 0, 256, 232.97, 8.57, 0.0, 1, 64, 107.62, 2.42, 0.0},
+    {17, 1, 0, 256, 285.99, 9.90, 0.0, 0, 256, 234.57, 12.35, 0.0},
+    {17, 2, 1, 256, 246.22, 9.35, 0.0, 0, 64, 113.24, 0.00, 4.5},
 };
 
 // Blocks of a launch of variant t (columns per image where that kernel tiles so).
@@ -209,9 +214,9 @@ const Tile &choose_tile(const Shape &s, int mode) {
   for (const Cost &c : kCosts) {
     if (c.fam) continue;  // each variant once
     // the chain kernel runs windows other than 1x1 and 3x3 as variant 6
-    if (c.variant >= 10 && s.khw != 0 && s.khw != 1 && s.khw != 9) continue;
+    if (is_chain(tile_for_variant(c.variant)) && s.khw != 0 && s.khw != 1 && s.khw != 9) continue;
     if (c.variant == 9 && mode == OG_MODE_EXACT) continue;  // eight rows per lane: VALU-bound in exact mode
-    if (c.variant >= 14 && mode == OG_MODE_EXACT) continue;  // exact mode runs them as 10, 13, 11
+    if (c.variant >= 14 && c.variant <= 16 && mode == OG_MODE_EXACT) continue;  // run as 10, 13, 11
     const double e = estimate(tile_for_variant(c.variant), s, mode);
     if (e < best_cost) {
       best_cost = e;
@@ -306,10 +311,11 @@ void launch_tile(const Tile &t, og::Problem p, hipStream_t s) {
     if (p.KH == 1 && p.KW == 1) return launch_lane_conv<MODE, 1, 1>(t.variant, p, s);
   }
   // Exact mode keeps two k steps of products beside the accumulators: with
-  // two 32x64 blocks per wave (128x256 and 128x128 tiles) that no longer fits
-  // the registers of two waves per SIMD, so variants 2 and 3 run 64x128
-  // tiles.  With gathered B it keeps one product and runs 128x128 tiles.
-  const bool big = t.variant == 2 || t.variant == 3;
+  // two 32x64 blocks per wave (128x256, 128x128 and 256x256 tiles) that no
+  // longer fits the registers of two waves per SIMD, so variants 2, 3 and 17
+  // run 64x128 tiles.  With gathered B it keeps one product and runs 128x128
+  // tiles.
+  const bool big = t.variant == 2 || t.variant == 3 || t.variant == 17;
   const Tile &tt = (MODE == og::kExact && big) ? tile_for_variant(KIND == og::kBGather ? 3 : 4) : t;
   p.tiles_m = (int)ceil_div(p.M, tt.bm);
   p.tiles_n = (int)ceil_div(p.N, tt.bn);
@@ -336,6 +342,10 @@ void launch_tile(const Tile &t, og::Problem p, hipStream_t s) {
       break;
     case 4: hipLaunchKernelGGL((og::mfma_kernel<MODE, 64, 128, 2, 2, KIND, AV, BV, 4>), grid, block, 0, s, p); break;
     case 5: hipLaunchKernelGGL((og::mfma_kernel<MODE, 32, 256, 1, 4, KIND, AV, BV, 2>), grid, block, 0, s, p); break;
+    case 17:  // eight waves: the B tile (and its gather) serves 256 rows
+      if constexpr (MODE == og::kFast)
+        hipLaunchKernelGGL((og::mfma_kernel<MODE, 256, 256, 4, 2, KIND, AV, BV, 2>), grid, dim3(512), 0, s, p);
+      break;
     // (rings of two chunks: deeper rings cost more in occupancy than they
     // gain in hidden latency, measured on the ResNet-50 layers and products)
     case 6: hipLaunchKernelGGL((og::lane_kernel<MODE, KIND, 1, 4, 2>), grid, block, 0, s, p); break;

@@ -382,16 +382,16 @@ __device__ __forceinline__ void run_pipeline(int nchunks, Load &&load, Store &&s
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core kernel.  256 threads = 4 waves arranged WM x WN; a wave owns a
+// Matrix-core kernel.  4 or 8 waves arranged WM x WN; a wave owns a
 // (TM*32) x (TN*64) sub-tile as TM x TN blocks of 32 x 64 outputs, each block
 // one 32x32x1 MFMA pair-of-blocks: lanes 0-31 and 32-63 both carry the 32 A
 // rows, lanes 0-31 carry B columns 0-31 and lanes 32-63 columns 32-63.
 // ---------------------------------------------------------------------------
 template <int MODE, int BM, int BN, int WM, int WN, int KIND, bool AVEC, bool BVEC, int D>
-__global__ void __launch_bounds__(256) mfma_kernel(Problem p) {
-  constexpr int NT = 256, BK = 16;
+__global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
+  constexpr int NT = 64 * WM * WN, BK = 16;
   constexpr int TM = BM / WM / 32, TN = BN / WN / 64;
-  static_assert(WM * WN == 4 && TM >= 1 && TN >= 1, "tile shape");
+  static_assert((WM * WN == 4 || WM * WN == 8) && TM >= 1 && TN >= 1, "tile shape");
   constexpr int LDA = BM + 1;  // k-major A tile, padded against bank conflicts of the transposing store
   __shared__ __align__(16) float As[2][BK * LDA];
   __shared__ __align__(16) float Bs[2][BK * BN];

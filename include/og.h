@@ -129,8 +129,8 @@ void *og_get_stream(void);
  * that the results do not depend on it ("Exact mode", rule 5): 0 = chosen
  * from the shape (the default); 1 = the VALU tile kernel (64x64 tiles);
  * 2, 3, 4, 5 = the matrix-core kernel with 128x256, 128x128, 64x128 and
- * 32x256 output tiles (exact mode runs variants 2 and 3 with 64x128 tiles,
- * or 128x128 tiles for a gathered convolution);
+ * 32x256 output tiles (exact mode runs variants 2, 3 and 17 with 64x128
+ * tiles, or 128x128 tiles for a gathered convolution);
  * 6, 7, 8, 9 = the lane kernel (one output column per lane) with 1, 2, 4, 8
  * output rows per wave; 10, 11, 12, 13 = the chain kernel (compute waves
  * that only run the k chain, producer waves that stage B) with 64 columns
@@ -139,10 +139,11 @@ void *og_get_stream(void);
  * per lane; 14, 15, 16 = the chain kernel whose compute waves run the k
  * chain on the matrix cores (v_mfma_f32_4x4x1_16b_f32, 4 rows x 64
  * columns per chain) with 4 waves of 4 rows, 2 waves of 2 x 4 rows and
- * 2 waves of 4 rows (exact mode runs them as 10, 13 and 11).  Every
- * variant runs every shape (a convolution window other than 1x1 or 3x3
- * runs variants 10..16 as variant 6).  A value outside 0..16 returns
- * OG_ERR_INVALID_ARG.
+ * 2 waves of 4 rows (exact mode runs them as 10, 13 and 11); 17 = the
+ * matrix-core kernel with 256x256 output tiles and 8 waves (exact mode runs
+ * it like variants 2 and 3).  Every variant runs every shape (a
+ * convolution window other than 1x1 or 3x3 runs variants 10..16 as
+ * variant 6).  A value outside 0..17 returns OG_ERR_INVALID_ARG.
  */
 og_status og_set_variant(int variant);
 int og_get_variant(void);

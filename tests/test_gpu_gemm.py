@@ -106,7 +106,7 @@ def test_ragged_ld13_full(orc, specials):
         _check_gaps(flatC, c.m, c.n, c.ldc, 0)
 
 
-@pytest.mark.parametrize("variant", list(range(1, 17)))
+@pytest.mark.parametrize("variant", list(range(1, 18)))
 def test_variants_agree(orc, variant):
     """Every kernel variant gives the oracle's bits (no dependence on tiles)."""
     rng = np.random.default_rng(7)
@@ -118,6 +118,14 @@ def test_variants_agree(orc, variant):
         say(f"gemm variant {variant} mode {mode}")
         got, _ = _run_gpu(A, B, mode, k + 3, n + 1, n + 2, (1, 2, 3))
         assert_same_bits(got, orc.gemm(A, B, mode), f"variant {variant} mode {mode}")
+    # several tiles of the largest tile shapes, each ending inside the problem
+    m, n, k = 300, 520, 40
+    A = _mixed(rng, (m, k), 0.01)
+    B = _mixed(rng, (k, n), 0.01)
+    for mode in MODES:
+        say(f"gemm variant {variant} {m}x{n}x{k} mode {mode}")
+        got, _ = _run_gpu(A, B, mode, k, n, n)
+        assert_same_bits(got, orc.gemm(A, B, mode), f"variant {variant} {m}x{n}x{k} mode {mode}")
 
 
 @pytest.mark.parametrize("variant", [10, 11, 12, 13, 14, 15, 16])
