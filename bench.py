@@ -365,7 +365,7 @@ def cpu_baseline(synth, seconds):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for "
               f"--gpus {args.gpus}); the matrix product and convolution shard without any "
               "exchange, by rows/columns of C or by image/group, each GPU running the one-GPU "
               "kernel on its share.", file=sys.stderr)

@@ -88,8 +88,8 @@ class Oracle:
         if selftest:
             rc = L.ogref_selftest()
             if rc != 0:
-                raise RuntimeError(f"oracle self-test failed ({rc}): this build does not tell "
-                                   "fused from unfused arithmetic")
+                raise RuntimeError(f"oracle self-test failed ({rc}): the compiled library does not "
+                                   "tell fused from unfused arithmetic")
 
     def num_threads(self) -> int:
         return int(self.L.ogref_num_threads())

@@ -73,7 +73,8 @@ int ogref_conv2d_f32_at(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Co
                         int64_t dilH, int64_t dilW, const float *x, const float *w,
                         int64_t npts, const int64_t *flat, float *out, int mode);
 
-/* Load-time check that this build separates fused from unfused arithmetic:
+/* Load-time check that the compiled library separates fused from unfused
+ * arithmetic:
  * the two-term sum [1+2^-11, -(1+2^-12)] . [1, 1+2^-12] is +0 exactly and
  * -2^-24 fused.  Returns 0 when both hold. */
 int ogref_selftest(void);
