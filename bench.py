@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--only", default=None,
                     help="time one workload only (for profiling): gemm4096_fast, gemm4096_exact, "
                          "resnet_b1, resnet_b8, skinny, prefill, grouped, conv1d, conv1x1, ragged, "
-                         "gemm256, "
+                         "gemm256, dw_b1, dw_b8, se, single_column, nt_prefill, nt_single_row, "
                          "copy (a 1 GiB device copy, to scale the HBM byte counters)")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -134,6 +134,45 @@ def conv_macs(og, s):
     return s.N * s.Cout * oh * ow * (s.Cin // s.groups) * s.KH * s.KW
 
 
+def chain_entry_impl(torch, og, synth, timer, shapes, config, seed0):
+    """A list of convolutions timed as one chain (HIP graph and eager launches)
+    and one by one, with their algorithmic bytes (x, w and y once each)."""
+    layers = []
+    for i, s in enumerate(shapes):
+        x, w = synth.conv_inputs(s, synth.seed_for(config, seed0 + i))
+        dx, dw = torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda()
+        y = og.conv2d(dx, dw, stride=s.stride, pad=s.pad, dil=s.dil, groups=s.groups)
+        layers.append((s, dx, dw, y))
+    macs = sum(conv_macs(og, s) for s, *_ in layers)
+    nbytes = sum(4.0 * (dx.numel() + dw.numel() + y.numel()) for _, dx, dw, y in layers)
+    ent = {"layers": len(layers), "gflop": round(2 * macs / 1e9, 4),
+           "mbytes": round(nbytes / 1e6, 3)}
+    for mode in ("fast", "exact"):
+        g = timer.graph(lambda: run_chain(og, layers, mode))
+        ms = timer.spike(g.replay)
+        ms_eager = timer.spike(lambda: run_chain(og, layers, mode))
+        ent[mode] = {"us": round(ms * 1e3, 2), "us_eager_launches": round(ms_eager * 1e3, 2),
+                     "gflops": round(2 * macs / (ms * 1e-3) / 1e9, 1),
+                     "tensor_gbps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+        del g
+    per = {}
+    for s, dx, dw, y in layers:
+        e = {"shape": repr(s), "mbytes": round(4.0 * (dx.numel() + dw.numel() + y.numel()) / 1e6, 3)}
+        for mode in ("fast", "exact"):
+            call = (lambda s_, dx_, dw_, y_, m_: lambda: og.conv2d(
+                dx_, dw_, stride=s_.stride, pad=s_.pad, dil=s_.dil, groups=s_.groups, mode=m_,
+                out=y_))(s, dx, dw, y, mode)
+            g = timer.graph(lambda: [call() for _ in range(20)])
+            us = timer.spike(g.replay, min_ms=30.0) / 20 * 1e3
+            e[f"{mode}_us"] = round(us, 2)
+            e[f"{mode}_gbps"] = round(e["mbytes"] * 1e6 / (us * 1e-6) / 1e9, 1)
+            del g
+        per[s.name] = e
+    ent["per_layer"] = per
+    del layers
+    return ent
+
+
 def run_chain(og, layers, mode):
     for s, dx, dw, y in layers:
         og.conv2d(dx, dw, stride=s.stride, pad=s.pad, dil=s.dil, groups=s.groups, mode=mode,
@@ -202,6 +241,9 @@ def extras(torch, og, synth, timer, only=None):
                 ent[mode]["tensor_gbps_cold"] = round(nbytes / (ms_cold * 1e-3) / 1e9, 1)
         del dx, dw, y, xs
         return ent
+
+    def chain_entry(shapes, config, seed0):
+        return chain_entry_impl(torch, og, synth, timer, shapes, config, seed0)
 
     if only == "copy":
         x = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
@@ -283,6 +325,37 @@ def extras(torch, og, synth, timer, only=None):
         s = shape_fn()
         out[s.name] = conv_entry(s, dist, synth.seed_for(5, 0),
                                  cold_bytes=COLD_BYTES if name == "grouped" else 0)
+    for batch in (1, 8):
+        name = f"dw_b{batch}"
+        if want(name):
+            log(f"extra: MobileNetV3-large depthwise convolutions, batch {batch}")
+            out[f"mobilenetv3_depthwise_b{batch}"] = chain_entry(
+                synth.mobilenetv3_large_depthwise(batch), 6, 100 * batch)
+    if want("se"):
+        log("extra: MobileNetV3-large squeeze-and-excitation convolutions, batch 1")
+        out["mobilenetv3_se_b1"] = chain_entry(synth.mobilenetv3_large_se(1), 7, 0)
+    if want("single_column"):
+        log("extra: single-column product")
+        c = synth.gemm_single_column()
+        out["gemm_single_column_4096x1x4096"] = gemm_entry(
+            c, bytes_moved=4.0 * (c.m * c.k + c.k + c.m))
+    for name, m in (("nt_prefill", 512), ("nt_single_row", 1)):
+        if not want(name):
+            continue
+        log(f"extra: {name}")
+        n = 11008 if m > 1 else 4096
+        A = torch.from_numpy(synth.normal((m, 4096), synth.seed_for(3, 20))).cuda()
+        Bt = torch.from_numpy(synth.normal((n, 4096), synth.seed_for(3, 21), 0.02)).cuda()
+        C = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        flops, nbytes = 2.0 * m * n * 4096, 4.0 * (m * 4096 + n * 4096 + m * n)
+        ent = {"m": m, "n": n, "k": 4096, "layout": "B given as n x k (weights N x K)"}
+        for mode in ("fast", "exact"):
+            ms = graph_ms([lambda: og.gemm_nt(A, Bt, mode, out=C)] * 20)
+            ent[mode] = {"us": round(ms * 1e3, 2), "gflops": round(flops / (ms * 1e-3) / 1e9, 1),
+                         "frac_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4),
+                         "hbm_gbps_hot": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+        out[f"gemm_nt_{m}x{n}x4096"] = ent
+        del A, Bt, C
     if want("conv1x1"):
         # the 1x1 layers of the batch-8 chain, hot and cold (HBM-bound shapes)
         log("extra: 1x1 layers of the batch-8 chain")

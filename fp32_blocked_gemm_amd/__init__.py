@@ -49,6 +49,8 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     L.og_gemm_f32.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, ctypes.c_int]
     L.og_gemm_f32.restype = ctypes.c_int
+    L.og_gemm_nt_f32.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, ctypes.c_int]
+    L.og_gemm_nt_f32.restype = ctypes.c_int
     L.og_conv2d_f32_ex.argtypes = [_i64] * 16 + [_vp, _vp, _vp, ctypes.c_int]
     L.og_conv2d_f32_ex.restype = ctypes.c_int
     L.og_conv2d_f32.argtypes = [_i64] * 11 + [_vp, _vp, _vp, ctypes.c_int]
@@ -111,6 +113,10 @@ def set_stream(stream_handle: int | None):
 
 def gemm_f32(m, n, k, A_ptr, lda, B_ptr, ldb, C_ptr, ldc, mode):
     _check(lib().og_gemm_f32(m, n, k, A_ptr, lda, B_ptr, ldb, C_ptr, ldc, _mode(mode)))
+
+
+def gemm_nt_f32(m, n, k, A_ptr, lda, B_ptr, ldb, C_ptr, ldc, mode):
+    _check(lib().og_gemm_nt_f32(m, n, k, A_ptr, lda, B_ptr, ldb, C_ptr, ldc, _mode(mode)))
 
 
 def conv2d_f32_ex(N, Cin, H, W, Cout, G, KH, KW, sH, sW, pT, pL, pB, pR, dH, dW, x_ptr, w_ptr,
@@ -177,6 +183,25 @@ def gemm(A, B, mode="exact", out=None):
         _use_stream_of(out)
         gemm_f32(m, n, k, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B), out.data_ptr(), _ld(out),
                  mode)
+    return out
+
+
+def gemm_nt(A, B, mode="exact", out=None):
+    """C = A @ B.T on 2-D float32 CUDA tensors, B given as n x k (row strides as lda/ldb/ldc)."""
+    torch = _torch()
+    m, k = A.shape
+    n, k2 = B.shape
+    if k != k2:
+        raise ValueError(f"inner sizes differ: {k} vs {k2}")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=A.device)
+    if tuple(out.shape) != (m, n):
+        raise ValueError("out has the wrong shape")
+    dev = _check_f32_cuda(A, B, out)
+    with torch.cuda.device(dev):
+        _use_stream_of(out)
+        gemm_nt_f32(m, n, k, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B), out.data_ptr(),
+                    _ld(out), mode)
     return out
 
 

@@ -91,7 +91,10 @@ constexpr Tile kTiles[] = {{1, 64, 64, 0},  {2, 128, 256, 4}, {3, 128, 128, 2}, 
                            {9, 32, 64, 8},  {10, 4, 64, 1},   {11, 2, 64, 1},   {12, 4, 16, 1},
                            {13, 4, 64, 2},  {14, 16, 64, 1},  {15, 16, 64, 2},  {16, 8, 64, 1},
                            {17, 256, 256, 4}};
-constexpr int kNumVariants = 17;
+constexpr int kNumVariants = 18;
+// 18 the depthwise kernel (Cin/G = 1, any multiplier): the automatic choice
+// for those shapes; forced on any other shape it runs the automatic choice.
+constexpr int kDepthwiseVariant = 18;
 
 const Tile &tile_for_variant(int v) {
   for (const Tile &t : kTiles)
@@ -380,7 +383,141 @@ void launch(int mode, bool av, bool bv, const Tile &t, const og::Problem &p, hip
 bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15) == 0; }
 
 const Tile &pick(const Shape &s, int mode) {
-  return t_variant == 0 ? choose_tile(s, mode) : tile_for_variant(t_variant);
+  return t_variant == 0 || t_variant == kDepthwiseVariant ? choose_tile(s, mode)
+                                                           : tile_for_variant(t_variant);
+}
+
+// The depthwise kernel with its window size compiled in where it is 3x3 or
+// 5x5 (the windows of depthwise layers), read at run time otherwise.  A lane
+// computes P outputs.  Measured on the MobileNetV3-large layers at batch 1
+// and 8: P = 4 (or 2) pays only for 3x3 windows at stride 1, whose taps are
+// contiguous loads, and only while the launch keeps at least 2048 waves;
+// strided and 5x5 windows are bound by their tap loads, and fewer waves
+// then only lengthen the launch.
+int dw_outputs_per_lane(int64_t planes, int64_t ohw, int64_t kh, int64_t kw, int64_t sh,
+                        int64_t sw) {
+  if (kh != 3 || kw != 3 || sh != 1 || sw != 1) return 1;
+  for (int per_lane : {4, 2})
+    if (planes * ceil_div(ohw, 64 * per_lane) >= 2048) return per_lane;
+  return 1;
+}
+
+template <int MODE, int KH, int KW>
+void launch_dw_window(og::Problem p, int per_lane, dim3 grid, hipStream_t s) {
+  if (per_lane == 4)
+    hipLaunchKernelGGL((og::dw_kernel<MODE, KH, KW, 4>), grid, dim3(256), 0, s, p);
+  else if (per_lane == 2)
+    hipLaunchKernelGGL((og::dw_kernel<MODE, KH, KW, 2>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((og::dw_kernel<MODE, KH, KW, 1>), grid, dim3(256), 0, s, p);
+}
+
+template <int MODE>
+void launch_dw(og::Problem p, int per_lane, hipStream_t s) {
+  const dim3 grid((unsigned)ceil_div((int64_t)p.tiles_m * p.tiles_n, 4));
+  if (p.KH == 3 && p.KW == 3)
+    launch_dw_window<MODE, 3, 3>(p, per_lane, grid, s);
+  else if (p.KH == 5 && p.KW == 5)
+    launch_dw_window<MODE, 5, 5>(p, per_lane, grid, s);
+  else
+    hipLaunchKernelGGL((og::dw_kernel<MODE, 0, 0, 1>), grid, dim3(256), 0, s, p);
+}
+
+// The row-dot kernel (single-column products): one wave of 64 rows per
+// block, a ring of 8 chunks of 16 taps; VEC: 16-byte loads of the rows.
+template <int MODE>
+void launch_rowdot_mode(og::Problem p, bool vec, hipStream_t s) {
+  p.tiles_m = (int)ceil_div(p.M, 64);
+  p.tiles_n = 1;
+  const dim3 grid((unsigned)p.tiles_m * (unsigned)p.groups), block(64);
+  if (vec)
+    hipLaunchKernelGGL((og::rowdot_kernel<MODE, true, 8>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((og::rowdot_kernel<MODE, false, 8>), grid, block, 0, s, p);
+}
+
+void launch_rowdot(int mode, og::Problem p, bool vec, hipStream_t s) {
+  if (mode == OG_MODE_EXACT)
+    launch_rowdot_mode<og::kExact>(p, vec, s);
+  else
+    launch_rowdot_mode<og::kFast>(p, vec, s);
+}
+
+// Longest rows for which a single-column product (n = 1, or a 1x1
+// convolution of a 1x1 input) runs the row-dot kernel: measured on the
+// squeeze-and-excitation layers and a 4096 x 4096 matrix, it halves the
+// time up to k = 480 and loses to the chain kernel from k = 672 on, where
+// its loads of 64 rows at once are bound by the texture units.
+constexpr int64_t kRowdotMaxK = 512;
+
+// Blocks of the row-dot kernel address 64 rows with 32-bit byte offsets.
+bool rowdot_fits(int64_t rows, int64_t ld, int64_t vstride, int64_t groups) {
+  return ld <= (int64_t(1) << 22) && vstride <= (int64_t(1) << 22) &&
+         ceil_div(rows, 64) * groups <= kI32Max;
+}
+
+// The product with a transposed B (N x K) runs the tile kernels that stage B
+// like A: the VALU kernel (variant 1) and the matrix-core kernel (2..5, 17,
+// with exact mode's 64x128 tiles for 2, 3 and 17).
+template <int MODE, bool AV, bool BV>
+void launch_nt_tile(const Tile &t, og::Problem p, hipStream_t s) {
+  constexpr int K = og::kBMatrixT;
+  const bool big = t.variant == 2 || t.variant == 3 || t.variant == 17;
+  const Tile &tt = (MODE == og::kExact && big) ? tile_for_variant(4) : t;
+  p.tiles_m = (int)ceil_div(p.M, tt.bm);
+  p.tiles_n = (int)ceil_div(p.N, tt.bn);
+  const dim3 grid((unsigned)p.tiles_m * (unsigned)p.tiles_n), block(256);
+  if (MODE == og::kExact && big) {
+    hipLaunchKernelGGL((og::mfma_kernel<MODE, 64, 128, 2, 2, K, AV, BV, 4>), grid, block, 0, s, p);
+    return;
+  }
+  switch (tt.variant) {
+    case 1: hipLaunchKernelGGL((og::valu_kernel<MODE, K>), grid, block, 0, s, p); break;
+    case 2:
+      if constexpr (MODE == og::kFast)
+        hipLaunchKernelGGL((og::mfma_kernel<MODE, 128, 256, 2, 2, K, AV, BV, 2>), grid, block, 0, s, p);
+      break;
+    case 3:
+      if constexpr (MODE == og::kFast)
+        hipLaunchKernelGGL((og::mfma_kernel<MODE, 128, 128, 2, 2, K, AV, BV, 2>), grid, block, 0, s, p);
+      break;
+    case 5: hipLaunchKernelGGL((og::mfma_kernel<MODE, 32, 256, 1, 4, K, AV, BV, 2>), grid, block, 0, s, p); break;
+    case 17:
+      if constexpr (MODE == og::kFast)
+        hipLaunchKernelGGL((og::mfma_kernel<MODE, 256, 256, 4, 2, K, AV, BV, 2>), grid, dim3(512), 0, s, p);
+      break;
+    default: hipLaunchKernelGGL((og::mfma_kernel<MODE, 64, 128, 2, 2, K, AV, BV, 4>), grid, block, 0, s, p); break;
+  }
+}
+
+template <int MODE>
+void launch_nt(bool av, bool bv, const Tile &t, const og::Problem &p, hipStream_t s) {
+  if (av && bv)
+    launch_nt_tile<MODE, true, true>(t, p, s);
+  else if (av)
+    launch_nt_tile<MODE, true, false>(t, p, s);
+  else if (bv)
+    launch_nt_tile<MODE, false, true>(t, p, s);
+  else
+    launch_nt_tile<MODE, false, false>(t, p, s);
+}
+
+// Tile of a product with a transposed B: the forced variant when it has a
+// form for it (1..5, 17), else the cheapest matrix-core tile by the launch
+// model of matrix products.
+const Tile &pick_nt(const Shape &sh, int mode) {
+  const int v = t_variant;
+  if ((v >= 1 && v <= 5) || v == 17) return tile_for_variant(v);
+  int best = 3;
+  double best_cost = 1e300;
+  for (int cand : {2, 3, 4, 5, 17}) {
+    const double e = estimate(tile_for_variant(cand), sh, mode);
+    if (e < best_cost) {
+      best_cost = e;
+      best = cand;
+    }
+  }
+  return tile_for_variant(best);
 }
 
 bool grid_fits(const Tile &t, int64_t M, int64_t N, int64_t groups) {
@@ -430,9 +567,77 @@ og_status og_gemm_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_t l
   p.groups = 1;
   const bool av = aligned16(A) && lda % 4 == 0 && k % 4 == 0;
   p.a_vec = av ? 1 : 0;
+  if (n == 1 && k <= kRowdotMaxK && t_variant == 0 && rowdot_fits(m, lda, ldb, 1)) {
+    // a single column: the rows of A against the column of B
+    launch_rowdot(mode, p, av, t_stream);
+    return check_launch("og_gemm_f32");
+  }
   const bool bv = aligned16(B) && ldb % 4 == 0 && n % 4 == 0;
   launch<og::kBMatrix>(mode, av, bv, t, p, t_stream);
   return check_launch("og_gemm_f32");
+}
+
+og_status og_gemm_nt_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_t lda,
+                         const float *B, int64_t ldb, float *C, int64_t ldc, int mode) {
+  if (mode != OG_MODE_EXACT && mode != OG_MODE_FAST)
+    return fail(OG_ERR_INVALID_ARG, "og_gemm_nt_f32: mode %d is not 0 (exact) or 1 (fast)", mode);
+  if (m < 0 || n < 0 || k < 0)
+    return fail(OG_ERR_INVALID_ARG, "og_gemm_nt_f32: negative size m=%lld n=%lld k=%lld",
+                (long long)m, (long long)n, (long long)k);
+  if (lda < (k > 1 ? k : 1) || ldb < (k > 1 ? k : 1) || ldc < (n > 1 ? n : 1))
+    return fail(OG_ERR_INVALID_ARG,
+                "og_gemm_nt_f32: leading dimension too small (lda=%lld ldb=%lld k=%lld ldc=%lld "
+                "n=%lld)",
+                (long long)lda, (long long)ldb, (long long)k, (long long)ldc, (long long)n);
+  if (m == 0 || n == 0) return ok();
+  if (C == nullptr) return fail(OG_ERR_INVALID_ARG, "og_gemm_nt_f32: C is null");
+  if (k > 0 && (A == nullptr || B == nullptr))
+    return fail(OG_ERR_INVALID_ARG, "og_gemm_nt_f32: A or B is null");
+  if (m > kI32Max || n > kI32Max || k > kI32Max)
+    return fail(OG_ERR_TOO_LARGE, "og_gemm_nt_f32: a dimension exceeds 2^31-1");
+  if (lda > (int64_t(1) << 22) || ldb > (int64_t(1) << 22))
+    return fail(OG_ERR_TOO_LARGE, "og_gemm_nt_f32: lda or ldb exceeds 2^22");
+  const Shape sh{m, n, k, 1, 0, 0};
+  const bool single_row = m == 1 && t_variant == 0;
+  const Tile &t = pick_nt(sh, mode);
+  if (!single_row && !grid_fits(t, m, n, 1))
+    return fail(OG_ERR_TOO_LARGE, "og_gemm_nt_f32: too many tiles");
+  og_status st = check_device();
+  if (st != OG_OK) return st;
+
+  og::Problem p{};
+  p.groups = 1;
+  if (single_row) {
+    // one row of A against the n rows of B: out[j] = sum_p B[j][p] * A[0][p]
+    p.A = B;
+    p.lda = ldb;
+    p.B = A;
+    p.ldb = 1;
+    p.C = C;
+    p.ldc = 1;
+    p.M = (int)n;
+    p.K = (int)k;
+    const bool vec = aligned16(B) && ldb % 4 == 0 && k % 4 == 0;
+    launch_rowdot(mode, p, vec, t_stream);
+    return check_launch("og_gemm_nt_f32");
+  }
+  p.A = A;
+  p.lda = lda;
+  p.B = B;
+  p.ldb = ldb;
+  p.C = C;
+  p.ldc = ldc;
+  p.M = (int)m;
+  p.N = (int)n;
+  p.K = (int)k;
+  const bool av = aligned16(A) && lda % 4 == 0 && k % 4 == 0;
+  const bool bv = aligned16(B) && ldb % 4 == 0 && k % 4 == 0;
+  p.a_vec = av ? 1 : 0;
+  if (mode == OG_MODE_EXACT)
+    launch_nt<og::kExact>(av, bv, t, p, t_stream);
+  else
+    launch_nt<og::kFast>(av, bv, t, p, t_stream);
+  return check_launch("og_gemm_nt_f32");
 }
 
 int64_t og_conv2d_out_size(int64_t size, int64_t k, int64_t stride, int64_t padBefore,
@@ -512,8 +717,30 @@ og_status og_conv2d_f32_ex(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t
   p.x_grp = cin_g * H * W;
   p.y_img = Cout * OH * OW;
   p.y_grp = cout_g * OH * OW;
+  if (cin_g == 1 && (t_variant == 0 || t_variant == kDepthwiseVariant)) {
+    // depthwise: one wave per 64 * per_lane output pixels of an (image, output channel) plane
+    const int per_lane = dw_outputs_per_lane(N * Cout, OH * OW, KH, KW, strideH, strideW);
+    const int64_t per_plane = ceil_div(OH * OW, 64 * per_lane), nplanes = N * Cout;
+    if (per_plane * nplanes > kI32Max - 3)
+      return fail(OG_ERR_TOO_LARGE, "og_conv2d_f32: too many output planes");
+    p.tiles_m = (int)per_plane;
+    p.tiles_n = (int)nplanes;
+    if (mode == OG_MODE_EXACT)
+      launch_dw<og::kExact>(p, per_lane, t_stream);
+    else
+      launch_dw<og::kFast>(p, per_lane, t_stream);
+    return check_launch("og_conv2d_f32");
+  }
   const bool av = aligned16(w) && K % 4 == 0 && (cout_g * K) % 4 == 0;
   p.a_vec = av ? 1 : 0;
+  if (planes && ncols == 1 && K <= kRowdotMaxK && t_variant == 0 && rowdot_fits(cout_g, K, 1, G)) {
+    // a 1x1 convolution of one 1x1 input: per group, the weight rows against
+    // the group's input channels
+    p.ldb = 1;
+    p.ldc = 1;
+    launch_rowdot(mode, p, av, t_stream);
+    return check_launch("og_conv2d_f32");
+  }
   if (planes)
     launch<og::kBPlanes>(mode, av, false, t, p, t_stream);
   else

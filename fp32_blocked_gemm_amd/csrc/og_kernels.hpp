@@ -39,6 +39,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
 #include <utility>
 
 namespace og {
@@ -53,6 +54,7 @@ enum BKind {
   kBMatrix = 0,   // row-major matrix, element (t, j) at B[t*ldb + j]
   kBGather = 1,   // convolution patches, gathered with zero padding
   kBPlanes = 2,   // 1x1 / stride 1 / no padding: input planes read in place
+  kBMatrixT = 3,  // B given as its transpose, N x K row-major: element (t, j) at B[j*ldb + t]
 };
 
 // One launch: an implicit matrix product C_g = A_g * B_g for each group g.
@@ -168,7 +170,10 @@ __device__ __forceinline__ void load4(__amdgpu_buffer_rsrc_t rs, uint32_t off, f
 // 16-byte aligned, lda, the group stride and K multiples of 4, so a load is
 // wholly inside or wholly outside the problem).
 // ---------------------------------------------------------------------------
-template <int BM, int BK, int NT, bool VEC>
+// OPB: the same staging for a B operand given as its transpose (N x K
+// row-major, k contiguous like A's rows): BM columns of B per chunk, stored
+// k-major as Bs[kk*LDB + col].
+template <int BM, int BK, int NT, bool VEC, bool OPB = false>
 struct AStage {
   static constexpr int KV = VEC ? 4 : 1;      // taps per load
   static constexpr int LPR = BK / KV;         // loads per row and chunk
@@ -184,10 +189,12 @@ struct AStage {
   __device__ void init(const Problem &p, int g, int m0, int tid) {
     kc = (tid % LPR) * KV;
     r0 = tid / LPR;
-    blk = p.A + g * p.a_gstride + (int64_t)m0 * p.lda;
+    const int64_t ld = OPB ? p.ldb : p.lda;
+    const int lim = OPB ? p.N : p.M;
+    blk = OPB ? p.B + (int64_t)m0 * ld : p.A + g * p.a_gstride + (int64_t)m0 * ld;
 #pragma unroll
     for (int q = 0; q < NQ; ++q)
-      voff[q] = m0 + r0 + q * RSTEP < p.M ? (uint32_t)(4 * ((r0 + q * RSTEP) * p.lda + kc))
+      voff[q] = m0 + r0 + q * RSTEP < lim ? (uint32_t)(4 * ((r0 + q * RSTEP) * ld + kc))
                                           : kOutside;
   }
   __device__ void load(const Problem &p, int k0, float (&r)[kRegs]) const {
@@ -337,7 +344,7 @@ struct BStage {
 // Pointer to output (row, col) of group g.
 template <int KIND>
 __device__ inline float *out_ptr(const Problem &p, int g, int row, int col) {
-  if (KIND == kBMatrix) return p.C + (int64_t)row * p.ldc + col;
+  if (KIND == kBMatrix || KIND == kBMatrixT) return p.C + (int64_t)row * p.ldc + col;
   const int img = col / p.OHW;
   const int pix = col - img * p.OHW;
   return p.C + img * p.y_img + g * p.y_grp + (int64_t)row * p.OHW + pix;
@@ -393,11 +400,15 @@ __global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
   constexpr int TM = BM / WM / 32, TN = BN / WN / 64;
   static_assert((WM * WN == 4 || WM * WN == 8) && TM >= 1 && TN >= 1, "tile shape");
   constexpr int LDA = BM + 1;  // k-major A tile, padded against bank conflicts of the transposing store
+  // a transposed B (N x K) is staged like A, its k-major tile padded by 4
+  constexpr bool BT = KIND == kBMatrixT;
+  constexpr int LDB = BT ? BN + 4 : BN;
   __shared__ __align__(16) float As[2][BK * LDA];
-  __shared__ __align__(16) float Bs[2][BK * BN];
+  __shared__ __align__(16) float Bs[2][BK * LDB];
   // 16-byte loads only where every thread has at least one of them
   using AS = AStage<BM, BK, NT, AVEC && (BM * BK / 4 >= NT)>;
-  using BS = BStage<BN, BK, NT, KIND, BVEC && (BN * BK / 4 >= NT)>;
+  using BS = std::conditional_t<BT, AStage<BN, BK, NT, BVEC && (BN * BK / 4 >= NT), true>,
+                                BStage<BN, BK, NT, BT ? kBMatrix : KIND, BVEC && (BN * BK / 4 >= NT)>>;
 
   const TileCoord tc = tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n);
   const int m0 = tc.tm * BM, n0 = tc.tn * BN;
@@ -443,7 +454,10 @@ __global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
       },
       [&](auto slot, auto buf) __attribute__((always_inline)) {
         as.template store<LDA>(As[decltype(buf)::value], ra[decltype(slot)::value]);
-        bs.store(Bs[decltype(buf)::value], rb[decltype(slot)::value]);
+        if constexpr (BT)
+          bs.template store<LDB>(Bs[decltype(buf)::value], rb[decltype(slot)::value]);
+        else
+          bs.store(Bs[decltype(buf)::value], rb[decltype(slot)::value]);
       },
       [&](int, auto buf, auto) __attribute__((always_inline)) {
         const float *al = As[decltype(buf)::value];
@@ -456,7 +470,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
 #pragma unroll
             for (int i = 0; i < TM; ++i) a[i] = al[kk * LDA + a_off + i * 32];
 #pragma unroll
-            for (int j = 0; j < TN; ++j) b[j] = bl[kk * BN + b_off + j * 64];
+            for (int j = 0; j < TN; ++j) b[j] = bl[kk * LDB + b_off + j * 64];
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -486,7 +500,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
 #pragma unroll
             for (int i = 0; i < TM; ++i) a[R0][i] = al[R0 * LDA + a_off + i * 32];
 #pragma unroll
-            for (int j = 0; j < TN; ++j) b[R0][j] = bl[R0 * BN + b_off + j * 64];
+            for (int j = 0; j < TN; ++j) b[R0][j] = bl[R0 * LDB + b_off + j * 64];
           });
           auto step = [&](auto uq, auto kq) __attribute__((always_inline)) {
             constexpr int U = decltype(uq)::value, KK = decltype(kq)::value;
@@ -500,7 +514,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
 #pragma unroll
               for (int i = 0; i < TM; ++i) a[SN][i] = al[(KK + RA) * LDA + a_off + i * 32];
 #pragma unroll
-              for (int j = 0; j < TN; ++j) b[SN][j] = bl[(KK + RA) * BN + b_off + j * 64];
+              for (int j = 0; j < TN; ++j) b[SN][j] = bl[(KK + RA) * LDB + b_off + j * 64];
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -527,7 +541,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
 #pragma unroll
             for (int i = 0; i < TM; ++i) a[u ^ 1][i] = al[(kk + 1) * LDA + a_off + i * 32];
 #pragma unroll
-            for (int j = 0; j < TN; ++j) b[u ^ 1][j] = bl[(kk + 1) * BN + b_off + j * 64];
+            for (int j = 0; j < TN; ++j) b[u ^ 1][j] = bl[(kk + 1) * LDB + b_off + j * 64];
           }
 #pragma unroll
           for (int i = 0; i < TM; ++i)
@@ -558,7 +572,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
         const int col = n0 + wn * TN * 64 + j * 64 + h * 32 + (lane & 31);
         if (col >= p.N) continue;
         float *base = out_ptr<KIND>(p, tc.g, 0, col);
-        const int64_t rstride = KIND == kBMatrix ? p.ldc : (int64_t)p.OHW;
+        const int64_t rstride = KIND == kBMatrix || KIND == kBMatrixT ? p.ldc : (int64_t)p.OHW;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = m0 + wm * TM * 32 + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r & 3);
@@ -577,9 +591,12 @@ __global__ void __launch_bounds__(256) valu_kernel(Problem p) {
   constexpr int NT = 256, BK = 16, BM = 64, BN = 64, D = 2;
   constexpr int LDA = BM + 4;
   __shared__ __align__(16) float As[2][BK * LDA];
-  __shared__ __align__(16) float Bs[2][BK * BN];
+  constexpr bool BT = KIND == kBMatrixT;  // a transposed B is staged like A
+  constexpr int LDB = BT ? BN + 4 : BN;
+  __shared__ __align__(16) float Bs[2][BK * LDB];
   using AS = AStage<BM, BK, NT, false>;
-  using BS = BStage<BN, BK, NT, KIND, false>;
+  using BS = std::conditional_t<BT, AStage<BN, BK, NT, false, true>,
+                                BStage<BN, BK, NT, BT ? kBMatrix : KIND, false>>;
 
   const TileCoord tc = tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n);
   const int m0 = tc.tm * BM, n0 = tc.tn * BN;
@@ -606,7 +623,10 @@ __global__ void __launch_bounds__(256) valu_kernel(Problem p) {
       },
       [&](auto slot, auto buf) __attribute__((always_inline)) {
         as.template store<LDA>(As[decltype(buf)::value], ra[decltype(slot)::value]);
-        bs.store(Bs[decltype(buf)::value], rb[decltype(slot)::value]);
+        if constexpr (BT)
+          bs.template store<LDB>(Bs[decltype(buf)::value], rb[decltype(slot)::value]);
+        else
+          bs.store(Bs[decltype(buf)::value], rb[decltype(slot)::value]);
       },
       [&](int, auto buf, auto) __attribute__((always_inline)) {
         const float *al = As[decltype(buf)::value];
@@ -614,7 +634,7 @@ __global__ void __launch_bounds__(256) valu_kernel(Problem p) {
 #pragma unroll
         for (int kk = 0; kk < BK; ++kk) {
           const float4 a4 = *reinterpret_cast<const float4 *>(&al[kk * LDA + ty * 4]);
-          const float4 b4 = *reinterpret_cast<const float4 *>(&bl[kk * BN + tx * 4]);
+          const float4 b4 = *reinterpret_cast<const float4 *>(&bl[kk * LDB + tx * 4]);
           const float a[4] = {a4.x, a4.y, a4.z, a4.w};
           const float b[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
@@ -635,7 +655,7 @@ __global__ void __launch_bounds__(256) valu_kernel(Problem p) {
     const int col = n0 + tx * 4 + j;
     if (col >= p.N) continue;
     float *base = out_ptr<KIND>(p, tc.g, 0, col);
-    const int64_t rstride = KIND == kBMatrix ? p.ldc : (int64_t)p.OHW;
+    const int64_t rstride = KIND == kBMatrix || KIND == kBMatrixT ? p.ldc : (int64_t)p.OHW;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = m0 + ty * 4 + i;
@@ -1385,6 +1405,172 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, chain_rows(
       if (row < p.M) base[(int64_t)row * rstride] = canonical(acc[r]);
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Depthwise kernel: Cin/G = 1, any channel multiplier Cout/G.  The pages run
+// depthwise convolutions on a kernel of their own that computes the
+// convolution expression directly ("Matrix product and convolution
+// kernels", section "Convolution"; "Exact mode", section "Convolution"):
+// output (n, oc, oy, ox) of group g = oc / (Cout/G) is the sum over (ky, kx),
+// kernel row then kernel column, of w[oc][0][ky][kx] * x[n][g][iy][ix], +0
+// outside the plane.  With only KH*KW terms per output the work is bound by
+// moving x and y, not by arithmetic, so there are no matrix cores and no LDS
+// tiles here: a wave owns 64 consecutive output pixels of one (image, output
+// channel) plane, its channel's weights are wave-uniform (read once into
+// registers), and each lane runs its own output's terms in order, a tap being
+// one buffer load of the input plane at a byte offset that lies past the
+// plane's range for a padding tap (read as +0, never stored).  Neighbouring
+// lanes read neighbouring input pixels, so the taps of a window come from the
+// same cache lines.  KH_ = KW_ = 0: the window size is read at run time.
+// A lane computes P outputs 64 pixels apart (P = 2 or 4 on larger planes), so
+// one round of resident waves covers a layer and each wave has P*KH*KW loads
+// in flight.  Launch: tiles_m = waves per output plane (64*P pixels each),
+// tiles_n = N*Cout planes, four waves per block, blocks numbered so that each
+// XCD runs a contiguous range of waves (the waves of a plane share its input
+// rows in one L2).
+// ---------------------------------------------------------------------------
+__device__ inline int xcd_contiguous(int bid, int nblocks) {
+  const int xcd = bid % kXcds, local = bid / kXcds;
+  const int per = nblocks / kXcds, rem = nblocks % kXcds;
+  return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+
+template <int MODE>
+__device__ __forceinline__ float term(float acc, float w, float v) {
+  if (MODE == kFast) return __builtin_fmaf(w, v, acc);
+  const float prod = w * v;
+  return acc + prod;
+}
+
+template <int MODE, int KH_, int KW_, int P>
+__global__ void __launch_bounds__(256) dw_kernel(Problem p) {
+  static_assert(P == 1 || (KH_ > 0 && KW_ > 0), "several outputs per lane: compiled windows only");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(xcd_contiguous(blockIdx.x, gridDim.x) * 4 + (tid >> 6));
+  const int plane = wv / p.tiles_m;  // image * Cout + output channel
+  if (plane >= p.tiles_n) return;    // whole waves past the last plane
+  const int cout = p.groups * p.M;
+  const int img = plane / cout, oc = plane - img * cout, g = oc / p.M;
+  const __amdgpu_buffer_rsrc_t rs =
+      buffer_at(p.B + img * p.x_img + (int64_t)g * p.HW, 4u * (uint32_t)p.HW);
+  const float *wp = p.A + (int64_t)oc * p.KHW;  // row oc of the weights, KH*KW taps
+  // output j of this lane: pixel pix0 + 64 j of the plane
+  const int pix0 = (wv - plane * p.tiles_m) * (64 * P) + lane;
+  int iy0[P], ix0[P];
+  bool valid[P];
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const int pix = pix0 + 64 * j;
+    valid[j] = pix < p.OHW;
+    const int oy = valid[j] ? pix / p.OW : 0, ox = valid[j] ? pix - oy * p.OW : 0;
+    iy0[j] = oy * p.sH - p.pT;
+    ix0[j] = ox * p.sW - p.pL;
+  }
+  // byte offset of tap (ky, kx) of output j in the plane, or past its range
+  auto offset = [&](int j, int ky, int kx) __attribute__((always_inline)) {
+    const int iy = iy0[j] + ky * p.dH, ix = ix0[j] + kx * p.dW;
+    const bool in = valid[j] & ((unsigned)iy < (unsigned)p.H) & ((unsigned)ix < (unsigned)p.W);
+    // unsigned: for a tap outside the plane the product may wrap, and is not used
+    const uint32_t o = 4u * ((uint32_t)iy * (uint32_t)p.W + (uint32_t)ix);
+    return in ? o : kOutside;
+  };
+  float acc[P];
+#pragma unroll
+  for (int j = 0; j < P; ++j) acc[j] = 0.0f;
+  if constexpr (KH_ > 0) {
+    constexpr int T = KH_ * KW_;
+    float w[T], v[P][T];
+#pragma unroll
+    for (int j = 0; j < P; ++j)
+#pragma unroll
+      for (int ky = 0; ky < KH_; ++ky)
+#pragma unroll
+        for (int kx = 0; kx < KW_; ++kx) v[j][ky * KW_ + kx] = load1(rs, offset(j, ky, kx));
+#pragma unroll
+    for (int t = 0; t < T; ++t) w[t] = wp[t];
+#pragma unroll
+    for (int j = 0; j < P; ++j)
+#pragma unroll
+      for (int t = 0; t < T; ++t) acc[j] = term<MODE>(acc[j], w[t], v[j][t]);
+  } else {
+    for (int ky = 0; ky < p.KH; ++ky)
+      for (int kx = 0; kx < p.KW; ++kx)
+        acc[0] = term<MODE>(acc[0], wp[ky * p.KW + kx], load1(rs, offset(0, ky, kx)));
+  }
+  float *yp = p.C + img * p.y_img + (int64_t)oc * p.OHW;
+#pragma unroll
+  for (int j = 0; j < P; ++j)
+    if (valid[j]) yp[pix0 + 64 * j] = canonical(acc[j]);
+}
+
+// ---------------------------------------------------------------------------
+// Row-dot kernel: out_g[r] = sum over p of W_g[r][p] * v_g[p], p increasing,
+// for rows W whose k taps are contiguous.  It serves the single-column
+// products: one row times the transpose of an N x K matrix (m = 1), and,
+// with short rows, a matrix times one column (n = 1) and the 1x1
+// convolutions of a 1x1 input at batch 1, the squeeze-and-excitation layers
+// ("Convolution (fast mode)", section "Single-column products").  Every
+// output is still one lane's chain over the whole of k from +0 ("Exact
+// mode", matrix product).  A lane owns one row and streams it in chunks of
+// 16 taps through a ring of D chunks of registers (16-byte loads when rows
+// are 16-byte aligned); lane u of each row of 16 lanes holds tap k0 + u of
+// v, which the DPP broadcast of dpp_steps hands to every lane, so a chunk is
+// 16 dependent steps with no LDS and no barrier.  Taps past k read +0 on both
+// sides.  One wave per block (64 rows), blocks spread over the XCDs.  Each
+// load instruction reads 16 bytes of 64 different rows, which holds a long
+// row's stream to the texture units' rate of distinct lines.
+//   W_g row r at A + g*a_gstride + r*lda;  v_g tap t at B + g*x_grp + t*ldb;
+//   out_g[r] at C + g*y_grp + r*ldc.
+// ---------------------------------------------------------------------------
+template <int MODE, bool VEC, int D>
+__global__ void __launch_bounds__(64) rowdot_kernel(Problem p) {
+  const TileCoord tc = tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, 1);
+  const int lane = threadIdx.x;
+  const int row0 = tc.tm * 64;  // the wave's first row
+  const bool ok = row0 + lane < p.M;
+  const float *wbase = p.A + tc.g * p.a_gstride + (int64_t)row0 * p.lda;
+  const float *vbase = p.B + tc.g * p.x_grp;
+  const uint32_t roff = ok ? (uint32_t)(4 * (int64_t)lane * p.lda) : kOutside;
+  const uint32_t voff = (uint32_t)(4 * (int64_t)(lane & 15) * p.ldb);
+  const int nchunks = (p.K + 15) / 16, last = nchunks - 1;
+  float wr[D][16], vr[D];
+  float acc[1] = {0.0f};
+  auto load = [&](int c, auto slot) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot)::value;
+    const int k0 = c * 16;
+    const __amdgpu_buffer_rsrc_t rw = buffer_at(wbase + k0, kRange);
+    if constexpr (VEC) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        load4(rw, ok && k0 + 4 * q < p.K ? roff + 16 * q : kOutside, &wr[S][4 * q]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) wr[S][t] = load1(rw, ok && k0 + t < p.K ? roff + 4 * t : kOutside);
+    }
+    const __amdgpu_buffer_rsrc_t rv = buffer_at(vbase + (int64_t)k0 * p.ldb, kRange);
+    vr[S] = load1(rv, k0 + (lane & 15) < p.K ? voff : kOutside);
+  };
+  auto compute = [&](auto slot) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot)::value;
+    const float w1[1] = {vr[S]};
+    dpp_steps<MODE, 1, 16>(acc, w1, wr[S]);
+  };
+  if (nchunks > 0) {
+    static_for<D - 1>([&](auto j) __attribute__((always_inline)) { load(min((int)decltype(j)::value, last), j); });
+    const int full = nchunks - nchunks % D;
+    for (int c0 = 0; c0 < full; c0 += D) {
+      static_for<D>([&](auto j) __attribute__((always_inline)) {
+        constexpr int J = decltype(j)::value;
+        load(min(c0 + J + D - 1, last), std::integral_constant<int, (J + D - 1) % D>{});
+        compute(j);
+      });
+    }
+    static_for<D - 1>([&](auto j) __attribute__((always_inline)) {
+      if (full + (int)decltype(j)::value < nchunks) compute(j);
+    });
+  }
+  if (ok) p.C[tc.g * p.y_grp + (int64_t)(row0 + lane) * p.ldc] = canonical(acc[0]);
 }
 
 }  // namespace og

@@ -71,6 +71,25 @@ og_status og_gemm_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_t l
                       const float *B, int64_t ldb, float *C, int64_t ldc, int mode);
 
 /*
+ * Matrix product with the right operand given as its transpose: B is n x k,
+ * row-major, so that each of its rows holds the k weights of one output
+ * column (the weights-as-N-x-K layout of the dotLLM pull request "F32
+ * outer-product tiled GEMM kernel for prefill", section "Kernel design"):
+ *
+ *     C[i*ldc + j] = sum over p = 0..k-1 of A[i*lda + p] * B[j*ldb + p]
+ *
+ * that is, C = A * B^T, each output summed by the mode's rule in increasing p
+ * from +0 ("Exact mode", section "Matrix product": the product of two
+ * elements commutes, so this is the matrix product of A and B^T, bit for
+ * bit).  Same contract as og_gemm_f32 except that ldb >= max(1,k).  With
+ * m == 1 it is a single-row product against the rows of B, streamed once
+ * ("Convolution (fast mode)", section "Single-column products").  Every
+ * kernel variant 1..5 and 17 has a form for it; other variants run as 0.
+ */
+og_status og_gemm_nt_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_t lda,
+                         const float *B, int64_t ldb, float *C, int64_t ldc, int mode);
+
+/*
  * 2-D convolution, NCHW, per-axis stride, padding and dilation ("Exact mode",
  * section "Convolution"; "Convolution (fast mode)", sections "What each output
  * is" and "Layout of the work"):
@@ -141,9 +160,14 @@ void *og_get_stream(void);
  * columns per chain) with 4 waves of 4 rows, 2 waves of 2 x 4 rows and
  * 2 waves of 4 rows (exact mode runs them as 10, 13 and 11); 17 = the
  * matrix-core kernel with 256x256 output tiles and 8 waves (exact mode runs
- * it like variants 2 and 3).  Every variant runs every shape (a
- * convolution window other than 1x1 or 3x3 runs variants 10..16 as
- * variant 6).  A value outside 0..17 returns OG_ERR_INVALID_ARG.
+ * it like variants 2 and 3); 18 = the depthwise kernel (a convolution with
+ * Cin/G = 1, any channel multiplier Cout/G: each output's KH*KW terms run
+ * directly, one output per lane; "Matrix product and convolution kernels",
+ * section "Convolution"), which is also what 0 picks for such a shape.
+ * Every variant runs every shape (a convolution window other than 1x1 or
+ * 3x3 runs variants 10..16 as variant 6; variant 18 runs any shape with
+ * Cin/G > 1, and any matrix product, as 0 does).  A value outside 0..18
+ * returns OG_ERR_INVALID_ARG.
  */
 og_status og_set_variant(int variant);
 int og_get_variant(void);

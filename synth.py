@@ -232,3 +232,46 @@ def conv_inputs(shape: ConvShape, seed: int, dist: str = "normal") -> tuple[np.n
         return uniform(xs, seed), uniform(ws, seed + 1)
     fan_in = ws[1] * ws[2] * ws[3]
     return normal(xs, seed), normal(ws, seed + 1, math.sqrt(2.0 / fan_in))
+
+
+def mobilenetv3_large_depthwise(batch: int = 1) -> list[ConvShape]:
+    """The 15 depthwise convolutions of MobileNetV3-large at 224x224, in order.
+
+    Each bottleneck's depthwise convolution runs over its expanded channels
+    (groups = channels, multiplier 1) with a 3x3 or 5x5 window, padding
+    window // 2 and stride 1 or 2 (Howard et al. 2019, "Searching for
+    MobileNetV3", table 1).
+    """
+    # (channels, input size, window, stride)
+    spec = ((16, 112, 3, 1), (64, 112, 3, 2), (72, 56, 3, 1), (72, 56, 5, 2), (120, 28, 5, 1),
+            (120, 28, 5, 1), (240, 28, 3, 2), (200, 14, 3, 1), (184, 14, 3, 1), (184, 14, 3, 1),
+            (480, 14, 3, 1), (672, 14, 3, 1), (672, 14, 5, 2), (960, 7, 5, 1), (960, 7, 5, 1))
+    out = []
+    for i, (c, hw, k, s) in enumerate(spec):
+        p = k // 2
+        out.append(ConvShape(f"dw{i + 1}", batch, c, hw, hw, c, k, k, (s, s), (p, p, p, p),
+                             (1, 1), c))
+    return out
+
+
+def mobilenetv3_large_se(batch: int = 1) -> list[ConvShape]:
+    """The 16 squeeze-and-excitation convolutions of MobileNetV3-large, in order.
+
+    Each of the 8 blocks with squeeze-and-excitation pools its C expanded
+    channels to 1x1 and runs two 1x1 convolutions, C -> S and S -> C, with S
+    the quarter of C rounded up to a multiple of 8 (24, 32, 32, 120, 168,
+    168, 240, 240): at batch 1 each is a matrix-vector product.
+    """
+    out = []
+    for i, (c, s) in enumerate(((72, 24), (120, 32), (120, 32), (480, 120), (672, 168),
+                                (672, 168), (960, 240), (960, 240))):
+        out.append(ConvShape(f"se{i + 1}.reduce", batch, c, 1, 1, s, 1, 1))
+        out.append(ConvShape(f"se{i + 1}.expand", batch, s, 1, 1, c, 1, 1))
+    return out
+
+
+def gemm_single_column() -> GemmCase:
+    """m = k = 4096, n = 1: a 4096x4096 row-major matrix times one column (N(0,0.02) x N(0,1))."""
+    A = normal((4096, 4096), seed_for(3, 10), 0.02)
+    B = normal((4096, 1), seed_for(3, 11))
+    return GemmCase("gemm_single_column_4096x1x4096", 4096, 1, 4096, 4096, 1, 1, A, B)

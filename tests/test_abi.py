@@ -60,6 +60,33 @@ def test_gemm_rejects_before_launch(L, args, why):
     assert L.og_last_error()
 
 
+@pytest.mark.parametrize("args,why", [
+    ((4, 4, 4, P, 4, P, 4, P, 4, 2), "mode"),
+    ((-1, 4, 4, P, 4, P, 4, P, 4, 0), "negative m"),
+    ((4, 4, 5, P, 4, P, 5, P, 4, 0), "lda < k"),
+    ((4, 5, 6, P, 6, P, 5, P, 5, 0), "ldb < k (B is n x k)"),
+    ((4, 5, 4, P, 4, P, 4, P, 4, 1), "ldc < n"),
+    ((4, 4, 4, P, 4, NULL, 4, P, 4, 0), "B null"),
+    ((4, 4, 4, P, 4, P, 4, NULL, 4, 1), "C null"),
+])
+def test_gemm_nt_rejects_before_launch(L, args, why):
+    assert L.og_gemm_nt_f32(*args) == og.OG_ERR_INVALID_ARG, why
+    assert L.og_last_error()
+
+
+def test_gemm_nt_ldb_is_checked_against_k_not_n(L):
+    """n = 9 > ldb = 5 >= k: valid arguments, so with no GPU the call gets as far
+    as the device check."""
+    try:
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("a GPU is present")
+    except ImportError:
+        pass
+    assert L.og_gemm_nt_f32(2, 9, 5, P, 5, P, 5, P, 9, 0) == og.OG_ERR_DEVICE
+    assert L.og_gemm_nt_f32(0, 9, 5, NULL, 5, NULL, 5, NULL, 9, 0) == og.OG_OK
+
+
 def test_gemm_empty_is_a_no_op(L):
     assert L.og_gemm_f32(0, 4, 4, NULL, 4, NULL, 4, NULL, 4, 0) == og.OG_OK
     assert L.og_gemm_f32(3, 0, 4, NULL, 4, NULL, 1, NULL, 1, 1) == og.OG_OK
@@ -103,7 +130,8 @@ def test_out_size_matches_the_formula():
 
 
 def test_variant_and_stream_state(L):
-    assert L.og_set_variant(18) == og.OG_ERR_INVALID_ARG
+    assert L.og_set_variant(19) == og.OG_ERR_INVALID_ARG
+    assert L.og_set_variant(-1) == og.OG_ERR_INVALID_ARG
     assert L.og_set_variant(3) == og.OG_OK and L.og_get_variant() == 3
     assert L.og_set_variant(0) == og.OG_OK
     assert L.og_set_stream(None) == og.OG_OK and L.og_get_stream() is None
