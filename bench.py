@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--only", default=None,
                     help="time one workload only (for profiling): gemm4096_fast, gemm4096_exact, "
                          "resnet_b1, resnet_b8, skinny, prefill, grouped, conv1d, conv1x1, ragged, "
-                         "gemm256, dw_b1, dw_b8, se, single_column, nt_prefill, nt_single_row, "
+                         "gemm256, dw_b1, dw_b8, se, single_column, nt_prefill, nt_single_row, nt_rows8, "
                          "copy (a 1 GiB device copy, to scale the HBM byte counters)")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -339,11 +339,11 @@ def extras(torch, og, synth, timer, only=None):
         c = synth.gemm_single_column()
         out["gemm_single_column_4096x1x4096"] = gemm_entry(
             c, bytes_moved=4.0 * (c.m * c.k + c.k + c.m))
-    for name, m in (("nt_prefill", 512), ("nt_single_row", 1)):
+    for name, m in (("nt_prefill", 512), ("nt_single_row", 1), ("nt_rows8", 8)):
         if not want(name):
             continue
         log(f"extra: {name}")
-        n = 11008 if m > 1 else 4096
+        n = 11008 if m == 512 else 4096
         A = torch.from_numpy(synth.normal((m, 4096), synth.seed_for(3, 20))).cuda()
         Bt = torch.from_numpy(synth.normal((n, 4096), synth.seed_for(3, 21), 0.02)).cuda()
         C = torch.empty((m, n), dtype=torch.float32, device="cuda")

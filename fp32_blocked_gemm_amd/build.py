@@ -29,8 +29,25 @@ FLAGS = [
 ]
 
 
+def _digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in SOURCES + HEADERS:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
 def build(verbose: bool = False) -> str:
-    """Compile libog.so (always; about ten seconds)."""
+    """Compile libog.so (always; a few minutes).
+
+    hipcc reads the sources once for the device code and again for the host
+    code; a source edited in between would give a library whose host side
+    launches kernels its device code does not have.  The sources are hashed
+    before and after, and a library built from sources that changed meanwhile
+    is rejected.
+    """
+    before = _digest()
     cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, *SOURCES, "-o", LIB + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -42,6 +59,9 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if msgs and verbose:
         print("\n".join(msgs), file=sys.stderr)
+    if _digest() != before:
+        os.remove(LIB + ".tmp")
+        raise RuntimeError("the sources changed during the build; build again")
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

@@ -412,6 +412,36 @@ void launch_dw_window(og::Problem p, int per_lane, dim3 grid, hipStream_t s) {
     hipLaunchKernelGGL((og::dw_kernel<MODE, KH, KW, 1>), grid, dim3(256), 0, s, p);
 }
 
+// The band form of the depthwise kernel (input rows staged in LDS) for
+// strided or 5x5 windows on planes at least 28 pixels wide: bands of at
+// most 1024 outputs, enough bands for at least 1024 blocks, every band at
+// least 128 outputs, the staged rows within 32 KB.  Returns false (and
+// launches nothing) where the shape does not qualify.
+template <int MODE>
+bool launch_dw_band(og::Problem p, int64_t planes, int64_t OH, int64_t OW, hipStream_t s) {
+  const bool w3 = p.KH == 3 && p.KW == 3, w5 = p.KH == 5 && p.KW == 5;
+  if (!(w3 || w5) || (w3 && p.sH == 1 && p.sW == 1) || OW < 28) return false;
+  const int64_t iw = (OW - 1) * p.sW + (int64_t)(p.KW - 1) * p.dW + 1;
+  int64_t nb = std::max(ceil_div(OH * OW, 1024), ceil_div(1024, planes));
+  nb = std::min(nb, OH);
+  const int64_t bh = ceil_div(OH, nb);
+  nb = ceil_div(OH, bh);
+  const int64_t ih = (bh - 1) * p.sH + (int64_t)(p.KH - 1) * p.dH + 1;
+  if (planes * nb < 1024 || bh * OW < 128 || ih * iw > 8192 || planes * nb > kI32Max) return false;
+  p.bh = (int)bh;
+  p.ih = (int)ih;
+  p.iw = (int)iw;
+  p.tiles_m = (int)nb;
+  p.tiles_n = (int)planes;
+  const dim3 grid((unsigned)(planes * nb)), block(256);
+  const size_t lds = (size_t)(4 * ih * iw);
+  if (w3)
+    hipLaunchKernelGGL((og::dw_band_kernel<MODE, 3, 3>), grid, block, lds, s, p);
+  else
+    hipLaunchKernelGGL((og::dw_band_kernel<MODE, 5, 5>), grid, block, lds, s, p);
+  return true;
+}
+
 template <int MODE>
 void launch_dw(og::Problem p, int per_lane, hipStream_t s) {
   const dim3 grid((unsigned)ceil_div((int64_t)p.tiles_m * p.tiles_n, 4));
@@ -443,12 +473,47 @@ void launch_rowdot(int mode, og::Problem p, bool vec, hipStream_t s) {
     launch_rowdot_mode<og::kFast>(p, vec, s);
 }
 
-// Longest rows for which a single-column product (n = 1, or a 1x1
-// convolution of a 1x1 input) runs the row-dot kernel: measured on the
-// squeeze-and-excitation layers and a 4096 x 4096 matrix, it halves the
-// time up to k = 480 and loses to the chain kernel from k = 672 on, where
-// its loads of 64 rows at once are bound by the texture units.
+// Single-column products (n = 1, m = 1 against an N x K operand, a 1x1
+// convolution of a 1x1 input): rows of more than kStreamMinK taps that can
+// be read 16 bytes at a time are streamed through the chain kernel; other
+// rows of up to kRowdotMaxK taps run the row-dot kernel; the rest the
+// implicit product.  Measured on the squeeze-and-excitation layers and
+// 4096 x 4096 matrices: the row-dot kernel halves the tile kernels' time up
+// to k = 480 but its loads of 64 rows at once are bound by the texture units
+// for longer rows, where the streamed form is two to three times faster.
 constexpr int64_t kRowdotMaxK = 512;
+constexpr int64_t kStreamMinK = 256;
+
+// One row against the rows of an N x K matrix (k-contiguous, 16-byte
+// aligned, k a multiple of 4) on the chain kernel in its single-row form
+// (variant 12's shape: blocks of 16 columns, one compute wave of 4 lane rows,
+// one producer wave, one weight wave): the N x K operand streamed once
+// through LDS, 16 bytes of one column per load and no transpose.
+// p: A = the row (M = 1), B = the N x K operand (ldb its row stride), C = the
+// n outputs (contiguous), N = n, K = k.
+template <int MODE>
+void launch_chain_vt_mode(og::Problem p, hipStream_t s) {
+  constexpr int BN = 16, CW = 1, R = 1, ROWS = og::chain_rows(CW, BN, R, false);
+  using CS = og::ChainShape<1, BN, ROWS>;
+  p.tiles_m = (int)ceil_div(p.M, ROWS);
+  p.tiles_n = (int)ceil_div(p.N, BN);
+  p.groups = 1;
+  const dim3 grid((unsigned)p.tiles_m * (unsigned)p.tiles_n), block(64 * (CW + CS::PW + 1));
+  hipLaunchKernelGGL((og::chain_kernel<MODE, false, og::kLdVecT, 1, 1, BN, CW, R, false>), grid,
+                     block, 0, s, p);
+}
+
+void launch_chain_vt(int mode, og::Problem p, hipStream_t s) {
+  if (mode == OG_MODE_EXACT)
+    launch_chain_vt_mode<og::kExact>(p, s);
+  else
+    launch_chain_vt_mode<og::kFast>(p, s);
+}
+
+// The N x K operand can be streamed by 16-byte loads of its rows.
+bool vt_ok(const float *w, int64_t ldw, int64_t k) {
+  return aligned16(w) && ldw % 4 == 0 && k % 4 == 0 && k > 0 && ldw <= (int64_t(1) << 22);
+}
 
 // Blocks of the row-dot kernel address 64 rows with 32-bit byte offsets.
 bool rowdot_fits(int64_t rows, int64_t ld, int64_t vstride, int64_t groups) {
@@ -567,9 +632,27 @@ og_status og_gemm_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_t l
   p.groups = 1;
   const bool av = aligned16(A) && lda % 4 == 0 && k % 4 == 0;
   p.a_vec = av ? 1 : 0;
-  if (n == 1 && k <= kRowdotMaxK && t_variant == 0 && rowdot_fits(m, lda, ldb, 1)) {
+  const bool stream_col = n == 1 && k > kStreamMinK && ldb == 1 && ldc == 1 && vt_ok(A, lda, k);
+  if (n == 1 && !stream_col && k <= kRowdotMaxK && t_variant == 0 && rowdot_fits(m, lda, ldb, 1)) {
     // a single column: the rows of A against the column of B
     launch_rowdot(mode, p, av, t_stream);
+    return check_launch("og_gemm_f32");
+  }
+  if (stream_col && t_variant == 0) {
+    // a long single column: B's column (contiguous) against the rows of A,
+    // streamed through the chain kernel; the m outputs are C's column
+    og::Problem q{};
+    q.A = B;
+    q.lda = k;
+    q.a_vec = aligned16(B) ? 1 : 0;
+    q.B = A;
+    q.ldb = lda;
+    q.C = C;
+    q.ldc = m;
+    q.M = 1;
+    q.N = (int)m;
+    q.K = (int)k;
+    launch_chain_vt(mode, q, t_stream);
     return check_launch("og_gemm_f32");
   }
   const bool bv = aligned16(B) && ldb % 4 == 0 && n % 4 == 0;
@@ -607,6 +690,24 @@ og_status og_gemm_nt_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_
 
   og::Problem p{};
   p.groups = 1;
+  if (m <= 16 && t_variant == 0 && vt_ok(B, ldb, k) && (m > 1 || k > kStreamMinK)) {
+    // a few rows of A (a single row with a long k, or up to 16) streamed
+    // against the rows of B through the chain kernel, 4 rows x 16 columns
+    // per block
+    og::Problem q{};
+    q.A = A;
+    q.lda = lda;
+    q.a_vec = aligned16(A) && lda % 4 == 0 ? 1 : 0;
+    q.B = B;
+    q.ldb = ldb;
+    q.C = C;
+    q.ldc = ldc;
+    q.M = (int)m;
+    q.N = (int)n;
+    q.K = (int)k;
+    launch_chain_vt(mode, q, t_stream);
+    return check_launch("og_gemm_nt_f32");
+  }
   if (single_row) {
     // one row of A against the n rows of B: out[j] = sum_p B[j][p] * A[0][p]
     p.A = B;
@@ -723,6 +824,9 @@ og_status og_conv2d_f32_ex(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t
     const int64_t per_plane = ceil_div(OH * OW, 64 * per_lane), nplanes = N * Cout;
     if (per_plane * nplanes > kI32Max - 3)
       return fail(OG_ERR_TOO_LARGE, "og_conv2d_f32: too many output planes");
+    if (mode == OG_MODE_EXACT ? launch_dw_band<og::kExact>(p, nplanes, OH, OW, t_stream)
+                              : launch_dw_band<og::kFast>(p, nplanes, OH, OW, t_stream))
+      return check_launch("og_conv2d_f32");
     p.tiles_m = (int)per_plane;
     p.tiles_n = (int)nplanes;
     if (mode == OG_MODE_EXACT)
@@ -733,12 +837,31 @@ og_status og_conv2d_f32_ex(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t
   }
   const bool av = aligned16(w) && K % 4 == 0 && (cout_g * K) % 4 == 0;
   p.a_vec = av ? 1 : 0;
-  if (planes && ncols == 1 && K <= kRowdotMaxK && t_variant == 0 && rowdot_fits(cout_g, K, 1, G)) {
+  const bool stream_se = planes && ncols == 1 && G == 1 && K > kStreamMinK && vt_ok(w, K, K);
+  if (planes && ncols == 1 && !stream_se && K <= kRowdotMaxK && t_variant == 0 &&
+      rowdot_fits(cout_g, K, 1, G)) {
     // a 1x1 convolution of one 1x1 input: per group, the weight rows against
     // the group's input channels
     p.ldb = 1;
     p.ldc = 1;
     launch_rowdot(mode, p, av, t_stream);
+    return check_launch("og_conv2d_f32");
+  }
+  if (stream_se && t_variant == 0) {
+    // a long 1x1 convolution of one 1x1 input: the input channels against
+    // the weight rows, streamed through the chain kernel
+    og::Problem q{};
+    q.A = x;
+    q.lda = K;
+    q.a_vec = aligned16(x) ? 1 : 0;
+    q.B = w;
+    q.ldb = K;
+    q.C = y;
+    q.ldc = Cout;
+    q.M = 1;
+    q.N = (int)Cout;
+    q.K = (int)K;
+    launch_chain_vt(mode, q, t_stream);
     return check_launch("og_conv2d_f32");
   }
   if (planes)

@@ -75,6 +75,7 @@ struct Problem {
   int64_t x_img, x_grp;  // element strides of x between images and between groups
   int64_t y_img, y_grp;  // element strides of y between images and between groups
   int a_vec;             // A rows 16-byte aligned (A, lda and K multiples of 4 floats)
+  int bh, ih, iw;        // depthwise band kernel: output rows per band, staged input rows, columns
 };
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I = 0..N-1.
@@ -1030,7 +1031,9 @@ struct ChainShape {
 // How the chain kernel's producers read B: one tap per load; 4x4 blocks of
 // a matrix with 16-byte loads; or, for a 3x3 window with horizontal dilation
 // 1, the three taps of a kernel row with one 12-byte load.
-enum ChainLoad { kLdTap = 0, kLdVec = 1, kLdRow3 = 2 };
+// kLdVecT: B given as its transpose (N x K, each column's taps contiguous),
+// 16 bytes (4 taps of one column) per load, stored as they are.
+enum ChainLoad { kLdTap = 0, kLdVec = 1, kLdRow3 = 2, kLdVecT = 3 };
 
 // Output rows of a chain-kernel block: CW compute waves of (64/BN) lane rows
 // and R rows per lane; with the matrix-core compute (MF) a wave's R chains
@@ -1040,7 +1043,7 @@ constexpr int chain_rows(int CW, int BN, int R, bool MF) { return MF ? CW * 4 * 
 template <int MODE, bool CONV, int LD, int KH, int KW, int BN, int CW, int R, bool MF>
 __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, chain_rows(CW, BN, R, MF)>::PW + 1))
     chain_kernel(Problem p) {
-  constexpr bool VEC = LD == kLdVec, ROW3 = LD == kLdRow3;
+  constexpr bool VEC = LD == kLdVec, ROW3 = LD == kLdRow3, VT = LD == kLdVecT;
   constexpr int KHW = KH * KW;
   constexpr int RW = 64 / BN;                    // lane rows of a compute wave
   constexpr int ROWS = chain_rows(CW, BN, R, MF);  // output rows of a block
@@ -1053,9 +1056,10 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, chain_rows(
   constexpr int NS = 3, DP = 2, DW = NWM > 20 ? 2 : 4, U = 4;  // LDS stages, ring depths, unroll
   // compute: register blocks of 16 taps, read-ahead, unroll (in chunks)
   constexpr int RB = MF ? 3 : 4, LA = RB - 1, UC = MF ? 3 : 4;
-  constexpr int NBL = VEC ? BK / 64 : 0;        // 4x4 blocks per producer lane (16-byte loads)
+  constexpr int NBL = VEC || VT ? BK / 64 : 0;  // 4x4 blocks per producer lane (16-byte loads)
   static_assert(U % DP == 0 && U % DW == 0 && (UC * NB) % RB == 0, "unroll");
-  static_assert(!VEC || (!CONV && KHW == 1 && BK % 64 == 0), "16-byte producer loads: matrix B only");
+  static_assert(!(VEC || VT) || (!CONV && KHW == 1 && BK % 64 == 0),
+                "16-byte producer loads: matrix B only");
   static_assert(!ROW3 || (CONV && KH == 3 && KW == 3), "row loads: 3x3 windows only");
   __shared__ __align__(16) float4 stage[NS][NQ * BN];
   __shared__ __align__(16) float wstage[NS][ROWS * BK];
@@ -1154,8 +1158,9 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, chain_rows(
   if (wave >= CW) {
     // ---------------- B producers ----------------
     const int pw = wave - CW;
-    constexpr int NL = VEC ? 4 * NBL : ROW3 ? TPG / 3 : TPG;  // loads per lane and chunk
+    constexpr int NL = VEC || VT ? 4 * NBL : ROW3 ? TPG / 3 : TPG;  // loads per lane and chunk
     uint32_t off[NL];
+    int qv[VT ? NL : 1];  // transposed B: the tap quad of each load
     int grp = 0, qb[VEC ? NBL : 1], cb[VEC ? NBL : 1];
     // row loads: the load of kernel row ky starts at column s0 of the input
     // row, s0 = clamp(ix0, 0, W-3); tap kx is component kx + d (d = ix0 - s0,
@@ -1174,6 +1179,18 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, chain_rows(
         for (int j = 0; j < 4; ++j)
           off[4 * i + j] =
               ok ? (uint32_t)(((int64_t)(4 * qb[i] + j) * pstride + cbase + 4 * cb[i]) * 4) : kOutside;
+      }
+    } else if constexpr (VT) {
+      // lane -> (column, tap quad) pairs, columns fastest: a load instruction
+      // reads 16 bytes of each of BN columns (rows of the N x K operand),
+      // and a wave's LDS stores are contiguous.  Offsets are from column
+      // cbase of the chunk's first tap.
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        const int id = j * 64 * PW + pw * 64 + lane;
+        const int col = id % BN;
+        qv[j] = id / BN;
+        off[j] = cbase + col < ncols ? (uint32_t)(((int64_t)col * pstride + 4 * qv[j]) * 4) : kOutside;
       }
     } else if constexpr (ROW3) {
       grp = pw * (64 / BN) + lane / BN;
@@ -1223,9 +1240,18 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, chain_rows(
           off[j * KHW + t] = (voff[t] == kOutside || o >= (int64_t)kOutside) ? kOutside : (uint32_t)o;
         }
     }
-    float rb[DP][VEC ? 16 * NBL : TPG];
+    float rb[DP][VEC || VT ? 16 * NBL : TPG];
     auto load = [&](int c, auto slot) __attribute__((always_inline)) {
       constexpr int S = decltype(slot)::value;
+      if constexpr (VT) {
+        // k is a multiple of 4 here: a tap quad is wholly inside or past k
+        const __amdgpu_buffer_rsrc_t rt =
+            buffer_at(pbase + (int64_t)cbase * pstride + (int64_t)c * CH, kRange);
+        const int kleft = pcount - c * CH;
+#pragma unroll
+        for (int j = 0; j < NL; ++j) load4(rt, 4 * qv[j] < kleft ? off[j] : kOutside, &rb[S][4 * j]);
+        return;
+      }
       const int valid = min(max(pcount - c * CH, 0), CH);  // planes of the chunk that exist
       // (the range is uniform; readfirstlane keeps the descriptor in scalar
       // registers where the compiler would otherwise clamp it on the VALU)
@@ -1245,6 +1271,17 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, chain_rows(
     };
     auto store = [&](auto slot, int st) __attribute__((always_inline)) {
       constexpr int S = decltype(slot)::value;
+      if constexpr (VT) {
+        // load j holds taps 4 qv[j] .. + 3 of column (lane-order) j: already
+        // the [tap/4][column] layout
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+          const int id = j * 64 * PW + pw * 64 + lane;
+          stage[st][qv[j] * BN + id % BN] =
+              make_float4(rb[S][4 * j], rb[S][4 * j + 1], rb[S][4 * j + 2], rb[S][4 * j + 3]);
+        }
+        return;
+      }
       if constexpr (VEC) {
         // rb[16i + 4j + jj] is (tap 4qb + j, column 4cb + jj) of block i:
         // store each column's four taps
@@ -1502,6 +1539,71 @@ __global__ void __launch_bounds__(256) dw_kernel(Problem p) {
 #pragma unroll
   for (int j = 0; j < P; ++j)
     if (valid[j]) yp[pix0 + 64 * j] = canonical(acc[j]);
+}
+
+// ---------------------------------------------------------------------------
+// Depthwise kernel, band form (planes at least 28 pixels wide, 3x3 or 5x5
+// windows).  A block of 256 threads owns BH output rows of one (image,
+// output channel) plane.  It first stages the input rows those outputs read
+// (IH = (BH-1)*sH + (KH-1)*dH + 1 rows of IW = (OW-1)*sW + (KW-1)*dW + 1
+// columns, starting at the band's first window origin) in LDS, each element
+// one load of a contiguous row segment, +0 for the padding (written into
+// LDS, never stored in memory); then each thread runs the chains of its
+// outputs, taps read from LDS in (ky, kx) order.  Every input element is
+// loaded once per band instead of once per tap, which is what the strided
+// and 5x5 windows are bound by in the one-wave-per-64-pixels form.
+// Launch: tiles_m = bands per plane, tiles_n = N*Cout planes, dynamic LDS
+// 4*IH*IW bytes.
+// ---------------------------------------------------------------------------
+template <int MODE, int KH, int KW>
+__global__ void __launch_bounds__(256) dw_band_kernel(Problem p) {
+  extern __shared__ float tile[];
+  const int tid = threadIdx.x;
+  const int blk = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int plane = blk / p.tiles_m, band = blk - plane * p.tiles_m;
+  const int cout = p.groups * p.M;
+  const int img = plane / cout, oc = plane - img * cout, g = oc / p.M;
+  const int oy0 = band * p.bh;
+  const int iy0 = oy0 * p.sH - p.pT, ix0 = -p.pL;
+  const __amdgpu_buffer_rsrc_t rs =
+      buffer_at(p.B + img * p.x_img + (int64_t)g * p.HW, 4u * (uint32_t)p.HW);
+  // stage the band, 8 elements per thread per batch (all loads of a batch in flight)
+  const int total = p.ih * p.iw;
+  for (int e0 = 0; e0 < total; e0 += 8 * 256) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = e0 + i * 256 + tid;
+      const int r = e / p.iw, c = e - r * p.iw;
+      const int iy = iy0 + r, ix = ix0 + c;
+      const bool in = (e < total) & ((unsigned)iy < (unsigned)p.H) & ((unsigned)ix < (unsigned)p.W);
+      v[i] = load1(rs, in ? 4u * ((uint32_t)iy * (uint32_t)p.W + (uint32_t)ix) : kOutside);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = e0 + i * 256 + tid;
+      if (e < total) tile[e] = v[i];
+    }
+  }
+  __syncthreads();
+  const float *wp = p.A + (int64_t)oc * p.KHW;
+  float w[KH * KW];
+#pragma unroll
+  for (int t = 0; t < KH * KW; ++t) w[t] = wp[t];
+  const int rows = min(p.bh, p.OHW / p.OW - oy0);
+  const int nout = rows * p.OW;
+  float *yp = p.C + img * p.y_img + (int64_t)oc * p.OHW + (int64_t)oy0 * p.OW;
+  for (int o = tid; o < nout; o += 256) {
+    const int oyl = o / p.OW, ox = o - oyl * p.OW;
+    const float *t = tile + oyl * p.sH * p.iw + ox * p.sW;
+    float acc = 0.0f;
+#pragma unroll
+    for (int ky = 0; ky < KH; ++ky)
+#pragma unroll
+      for (int kx = 0; kx < KW; ++kx)
+        acc = term<MODE>(acc, w[ky * KW + kx], t[ky * p.dH * p.iw + kx * p.dW]);
+    yp[o] = canonical(acc);
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -60,6 +60,27 @@ def test_no_kernel_spills():
     assert not bad, f"kernels using scratch memory: {bad[:5]}"
 
 
+def test_every_host_kernel_has_device_code():
+    """Each kernel the host code can launch (its mangled name registered in
+    the library) is in the gfx950 code object.  A library whose host and
+    device passes saw different sources would launch a kernel that does not
+    exist, which the HIP runtime turns into an abort."""
+    _tools_or_skip()
+    with tempfile.TemporaryDirectory() as d:
+        co = _code_object(d)
+        notes = subprocess.run([os.path.join(LLVM, "llvm-readelf"), "--notes", co], check=True,
+                               capture_output=True, text=True).stdout
+    device = set(re.findall(r"^\s*\.name:\s+(\S+)", notes, flags=re.M))
+    with open(LIB, "rb") as f:
+        blob = f.read()
+    host = {m.decode() for m in re.findall(rb"_ZN2og\d+[a-z_]+kernelI[0-9A-Za-z_]*?EEvNS_7ProblemE",
+                                            blob)}
+    host = {n for n in host if "__device_stub__" not in n}  # the host-side launch stubs
+    assert host, "no kernel names found in the library"
+    missing = sorted(host - device)
+    assert not missing, f"{len(missing)} kernels registered on the host have no device code: {missing[:3]}"
+
+
 def _disassemble():
     _tools_or_skip()
     with tempfile.TemporaryDirectory() as d:

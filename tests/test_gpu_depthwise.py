@@ -114,6 +114,24 @@ def test_several_outputs_per_lane(orc):
             assert_same_bits(_gpu(x, w, s, mode), _oracle(orc, x, w, s, mode), f"{s} mode {mode}")
 
 
+def test_band_form(orc):
+    """Strided 3x3 and 5x5 windows on planes 28+ wide with enough planes run
+    the band form (input rows staged in LDS): ragged last bands, padding on
+    every side, dilation, a multiplier of 2."""
+    rng = np.random.default_rng(670)
+    for s in (synth.ConvShape("b3s2", 8, 64, 112, 112, 64, 3, 3, (2, 2), (1, 1, 1, 1), (1, 1), 64),
+              synth.ConvShape("b5s1", 8, 120, 28, 28, 120, 5, 5, (1, 1), (2, 2, 2, 2), (1, 1), 120),
+              synth.ConvShape("b5s2", 8, 72, 57, 58, 72, 5, 5, (2, 2), (2, 1, 3, 2), (1, 1), 72),
+              synth.ConvShape("b3d2", 4, 300, 30, 60, 600, 3, 3, (1, 2), (2, 2, 2, 2), (2, 2), 300),
+              synth.ConvShape("b5big", 2, 600, 40, 61, 600, 5, 5, (1, 1), (0, 4, 1, 0), (1, 1), 600)):
+        x, w = synth.conv_inputs(s, int(rng.integers(1 << 30)), "uniform")
+        x = _specials(x, rng, 0.0005)
+        w = _specials(w, rng, 0.002)
+        for mode in MODES:
+            say(f"depthwise band {s} mode {mode}")
+            assert_same_bits(_gpu(x, w, s, mode), _oracle(orc, x, w, s, mode), f"{s} mode {mode}")
+
+
 def test_padding_tap_meets_infinite_weight():
     """A depthwise output whose only non-padding tap is finite still turns NaN
     when an infinite weight meets a padding tap (padding taps are real products)."""

@@ -140,6 +140,52 @@ def test_single_row_nt(orc, mode):
 
 
 @pytest.mark.parametrize("mode", MODES)
+def test_single_row_nt_streamed(orc, mode):
+    """m = 1 with 16-byte aligned rows (k a multiple of 4): the row streamed
+    against the N x K operand through the chain kernel; ragged n, k across
+    chunk boundaries, padded row strides, every output."""
+    rng = np.random.default_rng(875 + mode)
+    for (n, k, ldb) in ((1, 4, 4), (15, 516, 520), (16, 128, 128), (17, 132, 136),
+                        (300, 1000, 1004), (1000, 4096, 4096), (4096, 4096, 4096)):
+        A = _mixed(rng, (1, k), 0.01)
+        Bt = _mixed(rng, (n, k), 0.001, 0.02)
+        say(f"gemm_nt single row (aligned) n {n} k {k} ldb {ldb} mode {mode}")
+        got, flatC = _nt_gpu(A, Bt, mode, k, ldb, n + 2, (0, 0, 3))
+        assert_same_bits(got, _nt_oracle(orc, A, Bt, mode), f"nt aligned 1x{n}x{k} mode {mode}")
+        _check_gaps(flatC, 1, n, n + 2, 3)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_few_rows_nt_streamed(orc, mode):
+    """2 to 16 rows against an aligned N x K operand (the chain kernel, 4 rows
+    per block): row counts not a multiple of 4, strided A and C."""
+    rng = np.random.default_rng(878 + mode)
+    for (m, n, k, lda, ldb) in ((2, 33, 64, 64, 64), (3, 100, 260, 263, 264), (5, 16, 128, 130, 132),
+                                (8, 517, 1000, 1000, 1004), (16, 4096, 4096, 4096, 4096)):
+        A = _mixed(rng, (m, k), 0.01)
+        Bt = _mixed(rng, (n, k), 0.001, 0.02)
+        say(f"gemm_nt few rows {m}x{n}x{k} lda {lda} ldb {ldb} mode {mode}")
+        got, flatC = _nt_gpu(A, Bt, mode, lda, ldb, n + 5, (1, 0, 2))
+        assert_same_bits(got, _nt_oracle(orc, A, Bt, mode), f"nt few rows {m}x{n}x{k} mode {mode}")
+        _check_gaps(flatC, m, n, n + 5, 2)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_single_column_streamed(orc, mode):
+    """n = 1 with aligned rows of A, B and C contiguous, k > 512: the column
+    streamed against the rows of A through the chain kernel."""
+    rng = np.random.default_rng(885 + mode)
+    for (m, k, lda) in ((1, 516, 516), (17, 1000, 1004), (333, 700, 704), (4096, 4096, 4096)):
+        A = _mixed(rng, (m, k), 0.002, 0.02)
+        B = _mixed(rng, (k, 1), 0.01)
+        say(f"gemm single column (streamed) {m}x1x{k} lda {lda} mode {mode}")
+        dA, _ = to_device_strided(A, lda, 0)
+        dB = torch().from_numpy(B).cuda()
+        got = to_host(og.gemm(dA, dB, mode))
+        assert_same_bits(got, orc.gemm(A, B, mode), f"streamed {m}x1x{k} mode {mode}")
+
+
+@pytest.mark.parametrize("mode", MODES)
 def test_single_column(orc, mode):
     """n = 1: the rows of A against one column of B (strided), every output;
     rows 16-byte aligned or not, k not a multiple of 16, k = 0."""
