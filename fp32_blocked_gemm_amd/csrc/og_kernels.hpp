@@ -1567,17 +1567,25 @@ __global__ void __launch_bounds__(256) dw_band_kernel(Problem p) {
   const int iy0 = oy0 * p.sH - p.pT, ix0 = -p.pL;
   const __amdgpu_buffer_rsrc_t rs =
       buffer_at(p.B + img * p.x_img + (int64_t)g * p.HW, 4u * (uint32_t)p.HW);
-  // stage the band, 8 elements per thread per batch (all loads of a batch in flight)
+  // stage the band, 8 elements per thread per batch (all loads of a batch in
+  // flight); element e = (r, c) of the tile, stepped by 256 without division
   const int total = p.ih * p.iw;
+  const int dr = 256 / p.iw, dc = 256 - dr * p.iw;
+  int r = tid / p.iw, c = tid - r * p.iw;
   for (int e0 = 0; e0 < total; e0 += 8 * 256) {
     float v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int e = e0 + i * 256 + tid;
-      const int r = e / p.iw, c = e - r * p.iw;
       const int iy = iy0 + r, ix = ix0 + c;
-      const bool in = (e < total) & ((unsigned)iy < (unsigned)p.H) & ((unsigned)ix < (unsigned)p.W);
+      const bool in = (e0 + i * 256 + tid < total) & ((unsigned)iy < (unsigned)p.H) &
+                      ((unsigned)ix < (unsigned)p.W);
       v[i] = load1(rs, in ? 4u * ((uint32_t)iy * (uint32_t)p.W + (uint32_t)ix) : kOutside);
+      r += dr;
+      c += dc;
+      if (c >= p.iw) {
+        c -= p.iw;
+        ++r;
+      }
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -1593,8 +1601,10 @@ __global__ void __launch_bounds__(256) dw_band_kernel(Problem p) {
   const int rows = min(p.bh, p.OHW / p.OW - oy0);
   const int nout = rows * p.OW;
   float *yp = p.C + img * p.y_img + (int64_t)oc * p.OHW + (int64_t)oy0 * p.OW;
+  // output o = (oyl, ox) of the band, stepped by 256 without division
+  const int qr = 256 / p.OW, qc = 256 - qr * p.OW;
+  int oyl = tid / p.OW, ox = tid - oyl * p.OW;
   for (int o = tid; o < nout; o += 256) {
-    const int oyl = o / p.OW, ox = o - oyl * p.OW;
     const float *t = tile + oyl * p.sH * p.iw + ox * p.sW;
     float acc = 0.0f;
 #pragma unroll
@@ -1603,6 +1613,12 @@ __global__ void __launch_bounds__(256) dw_band_kernel(Problem p) {
       for (int kx = 0; kx < KW; ++kx)
         acc = term<MODE>(acc, w[ky * KW + kx], t[ky * p.dH * p.iw + kx * p.dW]);
     yp[o] = canonical(acc);
+    oyl += qr;
+    ox += qc;
+    if (ox >= p.OW) {
+      ox -= p.OW;
+      ++oyl;
+    }
   }
 }
 
