@@ -91,10 +91,14 @@ constexpr Tile kTiles[] = {{1, 64, 64, 0},  {2, 128, 256, 4}, {3, 128, 128, 2}, 
                            {9, 32, 64, 8},  {10, 4, 64, 1},   {11, 2, 64, 1},   {12, 4, 16, 1},
                            {13, 4, 64, 2},  {14, 16, 64, 1},  {15, 16, 64, 2},  {16, 8, 64, 1},
                            {17, 256, 256, 4}};
-constexpr int kNumVariants = 18;
+constexpr int kNumVariants = 19;
 // 18 the depthwise kernel (Cin/G = 1, any multiplier): the automatic choice
 // for those shapes; forced on any other shape it runs the automatic choice.
 constexpr int kDepthwiseVariant = 18;
+// 19 the grouped direct kernel (grouped 3x3 convolutions with 2 <= Cin/G <= 64
+// and Cout/G <= 8): the automatic choice for those shapes; forced on any
+// other shape it runs the automatic choice.
+constexpr int kGroupedVariant = 19;
 
 const Tile &tile_for_variant(int v) {
   for (const Tile &t : kTiles)
@@ -383,7 +387,7 @@ void launch(int mode, bool av, bool bv, const Tile &t, const og::Problem &p, hip
 bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15) == 0; }
 
 const Tile &pick(const Shape &s, int mode) {
-  return t_variant == 0 || t_variant == kDepthwiseVariant ? choose_tile(s, mode)
+  return t_variant == 0 || t_variant >= kDepthwiseVariant ? choose_tile(s, mode)
                                                            : tile_for_variant(t_variant);
 }
 
@@ -440,6 +444,20 @@ bool launch_dw_band(og::Problem p, int64_t planes, int64_t OH, int64_t OW, hipSt
   else
     hipLaunchKernelGGL((og::dw_band_kernel<MODE, 5, 5>), grid, block, lds, s, p);
   return true;
+}
+
+// The grouped direct kernel, R = Cout/G rounded up to 1, 2, 4 or 8 rows per lane.
+template <int MODE>
+void launch_grouped_mode(og::Problem p, hipStream_t s) {
+  const dim3 grid((unsigned)ceil_div((int64_t)p.tiles_m * p.tiles_n, 4)), block(256);
+  if (p.M <= 1)
+    hipLaunchKernelGGL((og::grouped_kernel<MODE, 3, 3, 1>), grid, block, 0, s, p);
+  else if (p.M <= 2)
+    hipLaunchKernelGGL((og::grouped_kernel<MODE, 3, 3, 2>), grid, block, 0, s, p);
+  else if (p.M <= 4)
+    hipLaunchKernelGGL((og::grouped_kernel<MODE, 3, 3, 4>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((og::grouped_kernel<MODE, 3, 3, 8>), grid, block, 0, s, p);
 }
 
 template <int MODE>
@@ -833,6 +851,19 @@ og_status og_conv2d_f32_ex(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t
       launch_dw<og::kExact>(p, per_lane, t_stream);
     else
       launch_dw<og::kFast>(p, per_lane, t_stream);
+    return check_launch("og_conv2d_f32");
+  }
+  if (G > 1 && cin_g >= 2 && cin_g <= 64 && cout_g <= 8 && KH == 3 && KW == 3 &&
+      (t_variant == 0 || t_variant == kGroupedVariant) &&
+      ceil_div(OH * OW, 64) * N * G <= kI32Max - 3) {
+    // grouped, few output channels per group: one wave per 64 output pixels of
+    // an (image, group), all of the group's output channels per lane
+    p.tiles_m = (int)ceil_div(OH * OW, 64);
+    p.tiles_n = (int)(N * G);
+    if (mode == OG_MODE_EXACT)
+      launch_grouped_mode<og::kExact>(p, t_stream);
+    else
+      launch_grouped_mode<og::kFast>(p, t_stream);
     return check_launch("og_conv2d_f32");
   }
   const bool av = aligned16(w) && K % 4 == 0 && (cout_g * K) % 4 == 0;

@@ -1623,6 +1623,95 @@ __global__ void __launch_bounds__(256) dw_band_kernel(Problem p) {
 }
 
 // ---------------------------------------------------------------------------
+// Grouped direct kernel: a grouped 3x3 convolution with few output channels
+// per group (Cout/G <= 8; the grouped, dilated workload; ResNeXt-style
+// blocks).  Each output is the convolution expression of "Exact mode",
+// section "Convolution": its terms in (c, ky, kx) order from +0.  The
+// implicit product would give such a group an 8-row tile; here a wave owns 64
+// consecutive output pixels of one (image, group) and each lane keeps all R
+// (>= Cout/G) output channels of its pixel, so a tap, loaded once (a buffer
+// load at the pixel's offset in channel c's plane, or past the plane for a
+// padding tap, +0), feeds R terms.  Channels are loaded 8 at a time (72 tap
+// loads in flight per lane); their taps, in (c, ky, kx) order, run in chunks
+// of 16 through dpp_steps, two rows at a time, the weights of a row's chunk
+// in one register (lane u of each row of 16 holds tap k0 + u) broadcast by
+// DPP.  Taps past the group (the padding of the last chunk) read +0 on both
+// sides, so their terms leave the sums unchanged; rows past Cout/G read +0
+// weights and are not stored.
+// Launch: tiles_m = waves per (image, group), tiles_n = N*G, 4 waves per block.
+// ---------------------------------------------------------------------------
+template <int MODE, int KH, int KW, int R>
+__global__ void __launch_bounds__(256) grouped_kernel(Problem p) {
+  constexpr int T = KH * KW, CB = 8, NT = CB * T, NQ = (NT + 15) / 16;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(xcd_contiguous(blockIdx.x, gridDim.x) * 4 + (tid >> 6));
+  const int item = wv / p.tiles_m;  // image * G + group
+  if (item >= p.tiles_n) return;    // whole waves past the last (image, group)
+  const int img = item / p.groups, g = item - img * p.groups;
+  const int pix = (wv - item * p.tiles_m) * 64 + lane;
+  const bool valid = pix < p.OHW;
+  const int oy = valid ? pix / p.OW : 0, ox = valid ? pix - oy * p.OW : 0;
+  const int iy0 = oy * p.sH - p.pT, ix0 = ox * p.sW - p.pL;
+  uint32_t voff[T];
+#pragma unroll
+  for (int ky = 0; ky < KH; ++ky)
+#pragma unroll
+    for (int kx = 0; kx < KW; ++kx) {
+      const int iy = iy0 + ky * p.dH, ix = ix0 + kx * p.dW;
+      const bool in = valid & ((unsigned)iy < (unsigned)p.H) & ((unsigned)ix < (unsigned)p.W);
+      voff[ky * KW + kx] = in ? 4u * ((uint32_t)iy * (uint32_t)p.W + (uint32_t)ix) : kOutside;
+    }
+  const float *xg = p.B + img * p.x_img + g * p.x_grp;  // channel 0 of the group
+  const __amdgpu_buffer_rsrc_t rw = buffer_at(p.A + g * p.a_gstride, kRange);  // the group's weights
+  const int cin_g = p.K / T;
+  constexpr int RP = R >= 2 ? R / 2 : 1;  // row pairs (R = 1: one row)
+  float acc[RP][R >= 2 ? 2 : 1];
+#pragma unroll
+  for (int i = 0; i < RP; ++i)
+#pragma unroll
+    for (int j = 0; j < (R >= 2 ? 2 : 1); ++j) acc[i][j] = 0.0f;
+  for (int c0 = 0; c0 < cin_g; c0 += CB) {
+    float v[NQ * 16];
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      const int c = c0 + j;  // a channel past the group reads +0 (empty range)
+      const __amdgpu_buffer_rsrc_t rs =
+          buffer_at(xg + (int64_t)min(c, cin_g - 1) * p.HW, c < cin_g ? 4u * (uint32_t)p.HW : 0u);
+#pragma unroll
+      for (int t = 0; t < T; ++t) v[j * T + t] = load1(rs, voff[t]);
+    }
+#pragma unroll
+    for (int k = NT; k < NQ * 16; ++k) v[k] = 0.0f;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int k = c0 * T + q * 16 + (lane & 15);  // this lane's weight tap in the chunk
+#pragma unroll
+      for (int i = 0; i < RP; ++i) {
+        constexpr int RR = R >= 2 ? 2 : 1;
+        float w[RR];
+#pragma unroll
+        for (int j = 0; j < RR; ++j) {
+          const int row = i * RR + j;
+          const bool ok = row < p.M && k < p.K && q * 16 + (lane & 15) < NT;
+          w[j] = load1(rw, ok ? (uint32_t)(4 * ((int64_t)row * p.lda + k)) : kOutside);
+        }
+        dpp_steps<MODE, RR, 16>(acc[i], w, &v[q * 16]);
+      }
+    }
+  }
+  if (valid) {
+    float *yp = p.C + img * p.y_img + (int64_t)g * p.y_grp + pix;
+#pragma unroll
+    for (int i = 0; i < RP; ++i)
+#pragma unroll
+      for (int j = 0; j < (R >= 2 ? 2 : 1); ++j) {
+        const int row = i * (R >= 2 ? 2 : 1) + j;
+        if (row < p.M) yp[(int64_t)row * p.OHW] = canonical(acc[i][j]);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Row-dot kernel: out_g[r] = sum over p of W_g[r][p] * v_g[p], p increasing,
 // for rows W whose k taps are contiguous.  It serves the single-column
 // products: one row times the transpose of an N x K matrix (m = 1), and,

@@ -163,11 +163,14 @@ void *og_get_stream(void);
  * it like variants 2 and 3); 18 = the depthwise kernel (a convolution with
  * Cin/G = 1, any channel multiplier Cout/G: each output's KH*KW terms run
  * directly, one output per lane; "Matrix product and convolution kernels",
- * section "Convolution"), which is also what 0 picks for such a shape.
+ * section "Convolution"), which is also what 0 picks for such a shape;
+ * 19 = the grouped direct kernel (a grouped 3x3 convolution with
+ * 2 <= Cin/G <= 64 and Cout/G <= 8: one output pixel per lane with all of
+ * its group's output channels), also what 0 picks for such a shape.
  * Every variant runs every shape (a convolution window other than 1x1 or
- * 3x3 runs variants 10..16 as variant 6; variant 18 runs any shape with
- * Cin/G > 1, and any matrix product, as 0 does).  A value outside 0..18
- * returns OG_ERR_INVALID_ARG.
+ * 3x3 runs variants 10..16 as variant 6; variants 18 and 19 run shapes
+ * outside their own, and any matrix product, as 0 does).  A value outside
+ * 0..19 returns OG_ERR_INVALID_ARG.
  */
 og_status og_set_variant(int variant);
 int og_get_variant(void);

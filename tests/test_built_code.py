@@ -27,7 +27,12 @@ LLVM = "/opt/rocm/llvm/bin"
 def _code_object(d):
     bundler = os.path.join(LLVM, "clang-offload-bundler")
     fat, co = os.path.join(d, "fat.bin"), os.path.join(d, "dev.co")
-    subprocess.run(["objcopy", "--dump-section", f".hip_fatbin={fat}", LIB], check=True)
+    # objcopy writes its output over its input when no output file is named:
+    # work on a copy, so the library that this process has loaded is never
+    # rewritten under it
+    lib, scrap = os.path.join(d, "lib.so"), os.path.join(d, "scrap.so")
+    shutil.copyfile(LIB, lib)
+    subprocess.run(["objcopy", "--dump-section", f".hip_fatbin={fat}", lib, scrap], check=True)
     subprocess.run([bundler, "--unbundle", "--type=o",
                     "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--input={fat}",
                     f"--output={co}"], check=True)

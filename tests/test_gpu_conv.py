@@ -80,7 +80,7 @@ def test_random_shapes(orc, mode):
         assert_same_bits(_gpu_conv(x, w, s, mode), _oracle(orc, x, w, s, mode), f"{s} mode {mode}")
 
 
-@pytest.mark.parametrize("variant", list(range(1, 19)))
+@pytest.mark.parametrize("variant", list(range(1, 20)))
 def test_variants_agree(orc, variant):
     rng = np.random.default_rng(300)
     og.set_variant(variant)
@@ -119,6 +119,33 @@ def test_chain_kernel_shapes(orc, variant):
             say(f"conv chain variant {variant} {s} mode {mode}")
             assert_same_bits(_gpu_conv(x, w, s, mode), _oracle(orc, x, w, s, mode),
                              f"chain {variant} {s} mode {mode}")
+
+
+GROUPED_SHAPES = [
+    # the grouped, dilated, strided workload's own form, smaller
+    synth.ConvShape("g8x8", 2, 64, 20, 18, 64, 3, 3, (2, 2), (2, 2, 2, 2), (2, 2), 8),
+    # Cout/G of 1, 3, 5 (rows per lane rounded up), Cin/G from 2 to 20 (two channel blocks)
+    synth.ConvShape("g1", 1, 8, 9, 70, 4, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), 4),
+    synth.ConvShape("g3", 3, 40, 11, 13, 6, 3, 3, (1, 2), (0, 1, 2, 0), (1, 1), 2),
+    synth.ConvShape("g5", 1, 100, 17, 9, 25, 3, 3, (2, 1), (1, 0, 1, 3), (1, 2), 5),
+    synth.ConvShape("g8w", 2, 32, 65, 3, 32, 3, 3, (1, 1), (1, 1, 1, 1), (3, 1), 4),
+]
+
+
+@pytest.mark.parametrize("variant", [0, 3, 7, 19])
+def test_grouped_direct_kernel(orc, variant):
+    """Grouped 3x3 convolutions with few output channels per group run the
+    grouped direct kernel (0 and 19) with the implicit product's bits (3, 7)."""
+    og.set_variant(variant)
+    rng = np.random.default_rng(450)
+    for s in GROUPED_SHAPES:
+        x, w = synth.conv_inputs(s, int(rng.integers(1 << 30)), "uniform")
+        x = _with_specials(x, rng, 0.005)
+        w = _with_specials(w, rng, 0.01)
+        for mode in MODES:
+            say(f"conv grouped variant {variant} {s} mode {mode}")
+            assert_same_bits(_gpu_conv(x, w, s, mode), _oracle(orc, x, w, s, mode),
+                             f"grouped variant {variant} {s} mode {mode}")
 
 
 def test_padding_tap_meets_infinite_weight(orc):
