@@ -86,12 +86,15 @@ struct Tile {
 // 14..16 the chain kernel with matrix-core chains of 4 rows x 64 columns:
 // (compute waves, chains per wave) = (4, 1), (2, 2), (2, 1).
 // 17 the matrix-core kernel with 256x256 tiles and eight waves.
+// 20 the matrix-core kernel with 64x64 tiles of four waves of 16 x 64 outputs
+// (v_mfma_f32_16x16x1_4b_f32), for matrix products in fast mode; exact mode
+// and convolutions run it as variant 4.
 constexpr Tile kTiles[] = {{1, 64, 64, 0},  {2, 128, 256, 4}, {3, 128, 128, 2}, {4, 64, 128, 1},
                            {5, 32, 256, 1}, {6, 4, 64, 1},    {7, 8, 64, 2},    {8, 16, 64, 4},
                            {9, 32, 64, 8},  {10, 4, 64, 1},   {11, 2, 64, 1},   {12, 4, 16, 1},
                            {13, 4, 64, 2},  {14, 16, 64, 1},  {15, 16, 64, 2},  {16, 8, 64, 1},
-                           {17, 256, 256, 4}};
-constexpr int kNumVariants = 19;
+                           {17, 256, 256, 4}, {20, 64, 64, 1}};
+constexpr int kNumVariants = 20;
 // 18 the depthwise kernel (Cin/G = 1, any multiplier): the automatic choice
 // for those shapes; forced on any other shape it runs the automatic choice.
 constexpr int kDepthwiseVariant = 18;
@@ -186,6 +189,10 @@ constexpr Cost kCosts[] = {
     {17, 0, 0, 256, 232.97, 8.57, 0.0, 1, 64, 107.62, 2.42, 0.0},
     {17, 1, 0, 256, 285.99, 9.90, 0.0, 0, 256, 234.57, 12.35, 0.0},
     {17, 2, 1, 256, 246.22, 9.35, 0.0, 0, 64, 113.24, 0.00, 4.5},
+    // variant 20 (matrix products only), fitted to 23 products from 64 x 3136 x 64
+    // to 4096^3 (mean error 4.7 %); its exact fields are variant 4's, which
+    // exact mode runs
+    {20, 0, 0, 384, 27.26, 2.00, 1.0, 1, 512, 107.32, 2.49, 0.0},
 };
 
 // Blocks of a launch of variant t (columns per image where that kernel tiles so).
@@ -317,6 +324,9 @@ void launch_tile(const Tile &t, og::Problem p, hipStream_t s) {
     if (p.KH == 3 && p.KW == 3) return launch_lane_conv<MODE, 3, 3>(t.variant, p, s);
     if (p.KH == 1 && p.KW == 1) return launch_lane_conv<MODE, 1, 1>(t.variant, p, s);
   }
+  // the 16-row matrix-core form: matrix products in fast mode only
+  if (t.variant == 20 && (MODE == og::kExact || KIND != og::kBMatrix))
+    return launch_tile<MODE, KIND, AV, BV>(tile_for_variant(4), p, s);
   // Exact mode keeps two k steps of products beside the accumulators: with
   // two 32x64 blocks per wave (128x256, 128x128 and 256x256 tiles) that no
   // longer fits the registers of two waves per SIMD, so variants 2, 3 and 17
@@ -353,6 +363,10 @@ void launch_tile(const Tile &t, og::Problem p, hipStream_t s) {
       if constexpr (MODE == og::kFast)
         hipLaunchKernelGGL((og::mfma_kernel<MODE, 256, 256, 4, 2, KIND, AV, BV, 2>), grid, dim3(512), 0, s, p);
       break;
+    case 20:  // four waves of 16 x 64 outputs
+      if constexpr (MODE == og::kFast && KIND == og::kBMatrix)
+        hipLaunchKernelGGL((og::mfma_kernel<MODE, 64, 64, 4, 1, KIND, AV, BV, 2, 16>), grid, block, 0, s, p);
+      break;
     // (rings of two chunks: deeper rings cost more in occupancy than they
     // gain in hidden latency, measured on the ResNet-50 layers and products)
     case 6: hipLaunchKernelGGL((og::lane_kernel<MODE, KIND, 1, 4, 2>), grid, block, 0, s, p); break;
@@ -387,8 +401,9 @@ void launch(int mode, bool av, bool bv, const Tile &t, const og::Problem &p, hip
 bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15) == 0; }
 
 const Tile &pick(const Shape &s, int mode) {
-  return t_variant == 0 || t_variant >= kDepthwiseVariant ? choose_tile(s, mode)
-                                                           : tile_for_variant(t_variant);
+  return t_variant == 0 || t_variant == kDepthwiseVariant || t_variant == kGroupedVariant
+             ? choose_tile(s, mode)
+             : tile_for_variant(t_variant);
 }
 
 // The depthwise kernel with its window size compiled in where it is 3x3 or

@@ -45,6 +45,7 @@
 namespace og {
 
 typedef float f32x32 __attribute__((ext_vector_type(32)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 enum Mode { kExact = 0, kFast = 1 };
@@ -395,11 +396,16 @@ __device__ __forceinline__ void run_pipeline(int nchunks, Load &&load, Store &&s
 // one 32x32x1 MFMA pair-of-blocks: lanes 0-31 and 32-63 both carry the 32 A
 // rows, lanes 0-31 carry B columns 0-31 and lanes 32-63 columns 32-63.
 // ---------------------------------------------------------------------------
-template <int MODE, int BM, int BN, int WM, int WN, int KIND, bool AVEC, bool BVEC, int D>
+template <int MODE, int BM, int BN, int WM, int WN, int KIND, bool AVEC, bool BVEC, int D,
+          int MF = 32>
 __global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
   constexpr int NT = 64 * WM * WN, BK = 16;
-  constexpr int TM = BM / WM / 32, TN = BN / WN / 64;
+  constexpr int TM = BM / WM / MF, TN = BN / WN / 64;
   static_assert((WM * WN == 4 || WM * WN == 8) && TM >= 1 && TN >= 1, "tile shape");
+  // MF = 16: blocks of 16 x 64 outputs, one v_mfma_f32_16x16x1_4b_f32 per k
+  // (its four 16x16 blocks share the 16 A rows; fast mode only)
+  static_assert(MF == 32 || (MF == 16 && MODE == kFast), "16-row blocks: fast mode");
+  using acc_t = std::conditional_t<MF == 32, f32x32, f32x16>;
   constexpr int LDA = BM + 1;  // k-major A tile, padded against bank conflicts of the transposing store
   // a transposed B (N x K) is staged like A, its k-major tile padded by 4
   constexpr bool BT = KIND == kBMatrixT;
@@ -423,11 +429,11 @@ __global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
   float ra[D][AS::kRegs];
   float rb[D][BS::kRegs];
 
-  f32x32 acc[TM][TN];
+  acc_t acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x32{};
+    for (int j = 0; j < TN; ++j) acc[i][j] = acc_t{};
   // Exact mode, matrix B and input planes: the rounded products of the last
   // two k steps (k % 2), a step's products added while the next step's are
   // made.  Exact mode with gathered B: the last product made, added one
@@ -444,7 +450,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
       for (int j = 0; j < TN; ++j) prod[u][i][j] = f32x32{};
   f32x32 pend = f32x32{};
 
-  const int a_off = wm * TM * 32 + (lane & 31);
+  const int a_off = wm * TM * MF + (lane & (MF - 1));
   const int b_off = wn * TN * 64 + lane;
 
   run_pipeline<D>(
@@ -532,7 +538,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
         }
         float a[2][TM], b[2][TN];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) a[0][i] = al[a_off + i * 32];
+        for (int i = 0; i < TM; ++i) a[0][i] = al[a_off + i * MF];
 #pragma unroll
         for (int j = 0; j < TN; ++j) b[0][j] = bl[b_off + j * 64];
 #pragma unroll
@@ -540,7 +546,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
           const int u = kk & 1;
           if (kk + 1 < BK) {  // operands of the next k, read while this k's MFMAs run
 #pragma unroll
-            for (int i = 0; i < TM; ++i) a[u ^ 1][i] = al[(kk + 1) * LDA + a_off + i * 32];
+            for (int i = 0; i < TM; ++i) a[u ^ 1][i] = al[(kk + 1) * LDA + a_off + i * MF];
 #pragma unroll
             for (int j = 0; j < TN; ++j) b[u ^ 1][j] = bl[(kk + 1) * LDB + b_off + j * 64];
           }
@@ -548,7 +554,10 @@ __global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
           for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x1f32(a[u][i], b[u][j], acc[i][j], 0, 0, 0);
+              if constexpr (MF == 32)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x1f32(a[u][i], b[u][j], acc[i][j], 0, 0, 0);
+              else
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x1f32(a[u][i], b[u][j], acc[i][j], 0, 0, 0);
         }
       });
   if constexpr (kPend) {
@@ -561,6 +570,21 @@ __global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
       for (int j = 0; j < TN; ++j) acc[i][j] += prod[NPB - 1][i][j];
   }
 
+  if constexpr (MF == 16) {
+    // Epilogue of the 16 x 64 blocks: register r of lane l holds row
+    // 4*(l/16) + r%4 and column 16*(r/4) + l%16 (measured on gfx950).
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int col = n0 + wn * TN * 64 + j * 64 + 16 * (r >> 2) + (lane & 15);
+          const int row = m0 + wm * TM * 16 + i * 16 + 4 * (lane >> 4) + (r & 3);
+          if (col < p.N && row < p.M) *out_ptr<KIND>(p, tc.g, row, col) = canonical(acc[i][j][r]);
+        }
+    return;
+  }
   // Epilogue: accumulator register r of lane l in block pair half h = r/16
   // holds row 8*((r%16)/4) + 4*(l/32) + r%4 and column h*32 + l%32 of the
   // 32 x 64 block.

@@ -80,7 +80,7 @@ def test_random_shapes(orc, mode):
         assert_same_bits(_gpu_conv(x, w, s, mode), _oracle(orc, x, w, s, mode), f"{s} mode {mode}")
 
 
-@pytest.mark.parametrize("variant", list(range(1, 20)))
+@pytest.mark.parametrize("variant", list(range(1, 21)))
 def test_variants_agree(orc, variant):
     rng = np.random.default_rng(300)
     og.set_variant(variant)
