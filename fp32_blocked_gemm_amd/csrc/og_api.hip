@@ -193,6 +193,11 @@ constexpr Cost kCosts[] = {
     // to 4096^3 (mean error 4.7 %); its exact fields are variant 4's, which
     // exact mode runs
     {20, 0, 0, 384, 27.26, 2.00, 1.0, 1, 512, 107.32, 2.49, 0.0},
+    // for convolutions: 1x1 and other windows fitted to the ResNet-50 layers
+    // at batch 1 and 8 (it wins some batch-8 1x1 layers); 3x3 windows never
+    // (its wins there were within the fit's error)
+    {20, 1, 0, 384, 1e9, 0.00, 0.0, 0, 384, 150.49, 2.09, 4.5},
+    {20, 2, 1, 256, 28.25, 0.00, 4.57, 0, 256, 107.39, 0.63, 4.6},
 };
 
 // Blocks of a launch of variant t (columns per image where that kernel tiles so).
@@ -324,8 +329,8 @@ void launch_tile(const Tile &t, og::Problem p, hipStream_t s) {
     if (p.KH == 3 && p.KW == 3) return launch_lane_conv<MODE, 3, 3>(t.variant, p, s);
     if (p.KH == 1 && p.KW == 1) return launch_lane_conv<MODE, 1, 1>(t.variant, p, s);
   }
-  // the 16-row matrix-core form: matrix products in fast mode only
-  if (t.variant == 20 && (MODE == og::kExact || KIND != og::kBMatrix))
+  // the 16-row matrix-core form: fast mode only
+  if (t.variant == 20 && MODE == og::kExact)
     return launch_tile<MODE, KIND, AV, BV>(tile_for_variant(4), p, s);
   // Exact mode keeps two k steps of products beside the accumulators: with
   // two 32x64 blocks per wave (128x256, 128x128 and 256x256 tiles) that no
@@ -364,7 +369,7 @@ void launch_tile(const Tile &t, og::Problem p, hipStream_t s) {
         hipLaunchKernelGGL((og::mfma_kernel<MODE, 256, 256, 4, 2, KIND, AV, BV, 2>), grid, dim3(512), 0, s, p);
       break;
     case 20:  // four waves of 16 x 64 outputs
-      if constexpr (MODE == og::kFast && KIND == og::kBMatrix)
+      if constexpr (MODE == og::kFast)
         hipLaunchKernelGGL((og::mfma_kernel<MODE, 64, 64, 4, 1, KIND, AV, BV, 2, 16>), grid, block, 0, s, p);
       break;
     // (rings of two chunks: deeper rings cost more in occupancy than they
