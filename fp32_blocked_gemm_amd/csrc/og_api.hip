@@ -87,8 +87,7 @@ struct Tile {
 // (compute waves, chains per wave) = (4, 1), (2, 2), (2, 1).
 // 17 the matrix-core kernel with 256x256 tiles and eight waves.
 // 20 the matrix-core kernel with 64x64 tiles of four waves of 16 x 64 outputs
-// (v_mfma_f32_16x16x1_4b_f32), for matrix products in fast mode; exact mode
-// and convolutions run it as variant 4.
+// (v_mfma_f32_16x16x1_4b_f32), both modes.
 constexpr Tile kTiles[] = {{1, 64, 64, 0},  {2, 128, 256, 4}, {3, 128, 128, 2}, {4, 64, 128, 1},
                            {5, 32, 256, 1}, {6, 4, 64, 1},    {7, 8, 64, 2},    {8, 16, 64, 4},
                            {9, 32, 64, 8},  {10, 4, 64, 1},   {11, 2, 64, 1},   {12, 4, 16, 1},
@@ -189,15 +188,16 @@ constexpr Cost kCosts[] = {
     {17, 0, 0, 256, 232.97, 8.57, 0.0, 1, 64, 107.62, 2.42, 0.0},
     {17, 1, 0, 256, 285.99, 9.90, 0.0, 0, 256, 234.57, 12.35, 0.0},
     {17, 2, 1, 256, 246.22, 9.35, 0.0, 0, 64, 113.24, 0.00, 4.5},
-    // variant 20 (matrix products only), fitted to 23 products from 64 x 3136 x 64
-    // to 4096^3 (mean error 4.7 %); its exact fields are variant 4's, which
-    // exact mode runs
-    {20, 0, 0, 384, 27.26, 2.00, 1.0, 1, 512, 107.32, 2.49, 0.0},
+    // variant 20, fitted to 23 products from 64 x 3136 x 64 to 4096^3 (mean
+    // error 4.7 % fast, 4.6 % exact; the exact estimate carries 5 us more,
+    // which keeps it off the products where the other variants' estimates
+    // are too high, e.g. 1000 x 777 x 1531)
+    {20, 0, 0, 384, 27.26, 2.00, 1.0, 1, 512, 60.94, 1.89, 5.93},
     // for convolutions: 1x1 and other windows fitted to the ResNet-50 layers
     // at batch 1 and 8 (it wins some batch-8 1x1 layers); 3x3 windows never
     // (its wins there were within the fit's error)
-    {20, 1, 0, 384, 1e9, 0.00, 0.0, 0, 384, 150.49, 2.09, 4.5},
-    {20, 2, 1, 256, 28.25, 0.00, 4.57, 0, 256, 107.39, 0.63, 4.6},
+    {20, 1, 0, 384, 1e9, 0.00, 0.0, 0, 384, 1e9, 0.00, 0.0},
+    {20, 2, 1, 256, 28.25, 0.00, 4.57, 0, 256, 60.54, 0.00, 5.35},
 };
 
 // Blocks of a launch of variant t (columns per image where that kernel tiles so).
@@ -329,9 +329,6 @@ void launch_tile(const Tile &t, og::Problem p, hipStream_t s) {
     if (p.KH == 3 && p.KW == 3) return launch_lane_conv<MODE, 3, 3>(t.variant, p, s);
     if (p.KH == 1 && p.KW == 1) return launch_lane_conv<MODE, 1, 1>(t.variant, p, s);
   }
-  // the 16-row matrix-core form: fast mode only
-  if (t.variant == 20 && MODE == og::kExact)
-    return launch_tile<MODE, KIND, AV, BV>(tile_for_variant(4), p, s);
   // Exact mode keeps two k steps of products beside the accumulators: with
   // two 32x64 blocks per wave (128x256, 128x128 and 256x256 tiles) that no
   // longer fits the registers of two waves per SIMD, so variants 2, 3 and 17
@@ -369,7 +366,6 @@ void launch_tile(const Tile &t, og::Problem p, hipStream_t s) {
         hipLaunchKernelGGL((og::mfma_kernel<MODE, 256, 256, 4, 2, KIND, AV, BV, 2>), grid, dim3(512), 0, s, p);
       break;
     case 20:  // four waves of 16 x 64 outputs
-      if constexpr (MODE == og::kFast)
         hipLaunchKernelGGL((og::mfma_kernel<MODE, 64, 64, 4, 1, KIND, AV, BV, 2, 16>), grid, block, 0, s, p);
       break;
     // (rings of two chunks: deeper rings cost more in occupancy than they

@@ -396,6 +396,17 @@ __device__ __forceinline__ void run_pipeline(int nchunks, Load &&load, Store &&s
 // one 32x32x1 MFMA pair-of-blocks: lanes 0-31 and 32-63 both carry the 32 A
 // rows, lanes 0-31 carry B columns 0-31 and lanes 32-63 columns 32-63.
 // ---------------------------------------------------------------------------
+// One k step of an MF x 64 block: D = a (x) b + c, one fused multiply-add
+// per element (32x32x1 two-block or 16x16x1 four-block fp32 MFMA).
+template <int MF>
+__device__ __forceinline__ std::conditional_t<MF == 32, f32x32, f32x16> mfma1(
+    float a, float b, std::conditional_t<MF == 32, f32x32, f32x16> c) {
+  if constexpr (MF == 32)
+    return __builtin_amdgcn_mfma_f32_32x32x1f32(a, b, c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x1f32(a, b, c, 0, 0, 0);
+}
+
 template <int MODE, int BM, int BN, int WM, int WN, int KIND, bool AVEC, bool BVEC, int D,
           int MF = 32>
 __global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
@@ -403,8 +414,8 @@ __global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
   constexpr int TM = BM / WM / MF, TN = BN / WN / 64;
   static_assert((WM * WN == 4 || WM * WN == 8) && TM >= 1 && TN >= 1, "tile shape");
   // MF = 16: blocks of 16 x 64 outputs, one v_mfma_f32_16x16x1_4b_f32 per k
-  // (its four 16x16 blocks share the 16 A rows; fast mode only)
-  static_assert(MF == 32 || (MF == 16 && MODE == kFast), "16-row blocks: fast mode");
+  // (its four 16x16 blocks share the 16 A rows)
+  static_assert(MF == 32 || MF == 16, "block rows");
   using acc_t = std::conditional_t<MF == 32, f32x32, f32x16>;
   constexpr int LDA = BM + 1;  // k-major A tile, padded against bank conflicts of the transposing store
   // a transposed B (N x K) is staged like A, its k-major tile padded by 4
@@ -441,14 +452,14 @@ __global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
   // fit two waves per SIMD).
   constexpr bool kPend = MODE == kExact && KIND == kBGather;
   constexpr int NPB = MODE == kExact && !kPend ? 2 : 1;
-  f32x32 prod[NPB][TM][TN];
+  acc_t prod[NPB][TM][TN];
 #pragma unroll
   for (int u = 0; u < NPB; ++u)
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) prod[u][i][j] = f32x32{};
-  f32x32 pend = f32x32{};
+      for (int j = 0; j < TN; ++j) prod[u][i][j] = acc_t{};
+  acc_t pend = acc_t{};
 
   const int a_off = wm * TM * MF + (lane & (MF - 1));
   const int b_off = wn * TN * 64 + lane;
@@ -475,14 +486,14 @@ __global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
           for (int kk = 0; kk < BK; ++kk) {
             float a[TM], b[TN];
 #pragma unroll
-            for (int i = 0; i < TM; ++i) a[i] = al[kk * LDA + a_off + i * 32];
+            for (int i = 0; i < TM; ++i) a[i] = al[kk * LDA + a_off + i * MF];
 #pragma unroll
             for (int j = 0; j < TN; ++j) b[j] = bl[kk * LDB + b_off + j * 64];
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
               for (int j = 0; j < TN; ++j) {
-                const f32x32 pr = __builtin_amdgcn_mfma_f32_32x32x1f32(a[i], b[j], f32x32{}, 0, 0, 0);
+                const acc_t pr = mfma1<MF>(a[i], b[j], acc_t{});
                 const int s = i * TN + j;  // the product before this one: block s - 1
                 const int pi = s == 0 ? TM - 1 : (s - 1) / TN;
                 const int pj = s == 0 ? TN - 1 : (s - 1) % TN;
@@ -505,7 +516,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
           static_for<RA>([&](auto rq) __attribute__((always_inline)) {
             constexpr int R0 = decltype(rq)::value;
 #pragma unroll
-            for (int i = 0; i < TM; ++i) a[R0][i] = al[R0 * LDA + a_off + i * 32];
+            for (int i = 0; i < TM; ++i) a[R0][i] = al[R0 * LDA + a_off + i * MF];
 #pragma unroll
             for (int j = 0; j < TN; ++j) b[R0][j] = bl[R0 * LDB + b_off + j * 64];
           });
@@ -516,10 +527,10 @@ __global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
             for (int i = 0; i < TM; ++i)
 #pragma unroll
               for (int j = 0; j < TN; ++j)
-                prod[U][i][j] = __builtin_amdgcn_mfma_f32_32x32x1f32(a[S][i], b[S][j], f32x32{}, 0, 0, 0);
+                prod[U][i][j] = mfma1<MF>(a[S][i], b[S][j], acc_t{});
             if constexpr (KK + RA < BK) {
 #pragma unroll
-              for (int i = 0; i < TM; ++i) a[SN][i] = al[(KK + RA) * LDA + a_off + i * 32];
+              for (int i = 0; i < TM; ++i) a[SN][i] = al[(KK + RA) * LDA + a_off + i * MF];
 #pragma unroll
               for (int j = 0; j < TN; ++j) b[SN][j] = bl[(KK + RA) * LDB + b_off + j * 64];
             }
@@ -554,10 +565,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
           for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-              if constexpr (MF == 32)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x1f32(a[u][i], b[u][j], acc[i][j], 0, 0, 0);
-              else
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x1f32(a[u][i], b[u][j], acc[i][j], 0, 0, 0);
+              acc[i][j] = mfma1<MF>(a[u][i], b[u][j], acc[i][j]);
         }
       });
   if constexpr (kPend) {

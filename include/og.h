@@ -168,8 +168,7 @@ void *og_get_stream(void);
  * 2 <= Cin/G <= 64 and Cout/G <= 8: one output pixel per lane with all of
  * its group's output channels), also what 0 picks for such a shape;
  * 20 = the matrix-core kernel with 64x64 tiles of four waves of 16x64
- * outputs (v_mfma_f32_16x16x1_4b_f32), for matrix products in fast mode
- * (exact mode and convolutions run it as variant 4).
+ * outputs (v_mfma_f32_16x16x1_4b_f32).
  * Every variant runs every shape (a convolution window other than 1x1 or
  * 3x3 runs variants 10..16 as variant 6; variants 18 and 19 run shapes
  * outside their own, and any matrix product, as 0 does).  A value outside
