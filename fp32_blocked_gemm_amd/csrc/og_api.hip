@@ -557,7 +557,7 @@ bool rowdot_fits(int64_t rows, int64_t ld, int64_t vstride, int64_t groups) {
 
 // The product with a transposed B (N x K) runs the tile kernels that stage B
 // like A: the VALU kernel (variant 1) and the matrix-core kernel (2..5, 17,
-// with exact mode's 64x128 tiles for 2, 3 and 17).
+// 20, with exact mode's 64x128 tiles for 2, 3 and 17).
 template <int MODE, bool AV, bool BV>
 void launch_nt_tile(const Tile &t, og::Problem p, hipStream_t s) {
   constexpr int K = og::kBMatrixT;
@@ -585,6 +585,7 @@ void launch_nt_tile(const Tile &t, og::Problem p, hipStream_t s) {
       if constexpr (MODE == og::kFast)
         hipLaunchKernelGGL((og::mfma_kernel<MODE, 256, 256, 4, 2, K, AV, BV, 2>), grid, dim3(512), 0, s, p);
       break;
+    case 20: hipLaunchKernelGGL((og::mfma_kernel<MODE, 64, 64, 4, 1, K, AV, BV, 2, 16>), grid, block, 0, s, p); break;
     default: hipLaunchKernelGGL((og::mfma_kernel<MODE, 64, 128, 2, 2, K, AV, BV, 4>), grid, block, 0, s, p); break;
   }
 }
@@ -602,14 +603,14 @@ void launch_nt(bool av, bool bv, const Tile &t, const og::Problem &p, hipStream_
 }
 
 // Tile of a product with a transposed B: the forced variant when it has a
-// form for it (1..5, 17), else the cheapest matrix-core tile by the launch
-// model of matrix products.
+// form for it (1..5, 17, 20), else the cheapest matrix-core tile by the
+// launch model of matrix products.
 const Tile &pick_nt(const Shape &sh, int mode) {
   const int v = t_variant;
-  if ((v >= 1 && v <= 5) || v == 17) return tile_for_variant(v);
+  if ((v >= 1 && v <= 5) || v == 17 || v == 20) return tile_for_variant(v);
   int best = 3;
   double best_cost = 1e300;
-  for (int cand : {2, 3, 4, 5, 17}) {
+  for (int cand : {2, 3, 4, 5, 17, 20}) {
     const double e = estimate(tile_for_variant(cand), sh, mode);
     if (e < best_cost) {
       best_cost = e;

@@ -84,7 +84,7 @@ og_status og_gemm_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_t l
  * bit).  Same contract as og_gemm_f32 except that ldb >= max(1,k).  With
  * m == 1 it is a single-row product against the rows of B, streamed once
  * ("Convolution (fast mode)", section "Single-column products").  Every
- * kernel variant 1..5 and 17 has a form for it; other variants run as 0.
+ * kernel variant 1..5, 17 and 20 has a form for it; other variants run as 0.
  */
 og_status og_gemm_nt_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_t lda,
                          const float *B, int64_t ldb, float *C, int64_t ldc, int mode);

@@ -89,7 +89,7 @@ def test_nt_size_sweep_0_to_70(orc, mode):
         _check_gaps(flatC, m, n, ldc, offs[2])
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 5, 9, 17])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 5, 9, 17, 20])
 def test_nt_variants_agree(orc, variant):
     """Every tile with a transposed-B form, aligned (16-byte loads) and not;
     a variant without one (9) runs as the automatic choice."""
