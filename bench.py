@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--only", default=None,
                     help="time one workload only (for profiling): gemm4096_fast, gemm4096_exact, "
                          "resnet_b1, resnet_b8, skinny, prefill, grouped, conv1d, conv1x1, ragged, "
-                         "gemm256, dw_b1, dw_b8, se, single_column, nt_prefill, nt_single_row, nt_rows8, "
+                         "gemm256, dw_b1, dw_b8, se, single_column, nt_prefill, nt_single_row, nt_rows8, model_rows, "
                          "copy (a 1 GiB device copy, to scale the HBM byte counters)")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -171,6 +171,60 @@ def chain_entry_impl(torch, og, synth, timer, shapes, config, seed0):
     ent["per_layer"] = per
     del layers
     return ent
+
+
+def model_rows(torch, og, synth, timer):
+    """Per model: each distinct shape timed alone (20 calls replayed from a HIP
+    graph, 2 warm-ups, >= 20 ms, median of 3), summed as count x time, both
+    modes, and the exact / fast ratio.  Linear layers run as products with
+    N x K weights (og_gemm_nt_f32), A N(0,1), weights N(0, 0.02)."""
+    def timed(call):
+        g = timer.graph(lambda: [call() for _ in range(20)])
+        us = timer.spike(g.replay, min_ms=20.0) / 20 * 1e3
+        del g
+        return us
+
+    def conv_shapes(shapes):
+        groups = {}
+        for s in shapes:
+            key = (s.N, s.Cin, s.H, s.W, s.Cout, s.KH, s.KW, s.stride, s.pad, s.dil, s.groups)
+            groups.setdefault(key, [s, 0])[1] += 1
+        return list(groups.values())
+
+    rows = {}
+    models = {"bert_base_32x128": ("bert_base_4096", []), "bert_base_128": ("bert_base_128", []),
+              "minilm_l6_32x128": ("minilm_l6_4096", []),
+              "whisper_small_encoder_1500": ("whisper_small_enc_1500", synth.whisper_small_frontend()),
+              "resnet50_b1": (None, synth.resnet50_convs(1)),
+              "mobilenetv3_large_b1": (None, synth.mobilenetv3_large_convs(1))}
+    for name, (lin, convs) in models.items():
+        ent = {"shapes": 0, "gflop": 0.0, "fast_us": 0.0, "exact_us": 0.0}
+        for i, (lname, m, n, k, count) in enumerate(synth.transformer_linear_shapes(lin) if lin else []):
+            A = torch.from_numpy(synth.normal((m, k), synth.seed_for(8, 10 * i))).cuda()
+            W = torch.from_numpy(synth.normal((n, k), synth.seed_for(8, 10 * i + 1), 0.02)).cuda()
+            C = torch.empty((m, n), dtype=torch.float32, device="cuda")
+            ent["shapes"] += 1
+            ent["gflop"] += count * 2.0 * m * n * k / 1e9
+            for mode in ("fast", "exact"):
+                ent[f"{mode}_us"] += count * timed(lambda: og.gemm_nt(A, W, mode, out=C))
+            del A, W, C
+        for i, (s, count) in enumerate(conv_shapes(convs)):
+            x, w = synth.conv_inputs(s, synth.seed_for(8, 500 + i))
+            dx, dw = torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda()
+            y = og.conv2d(dx, dw, stride=s.stride, pad=s.pad, dil=s.dil, groups=s.groups)
+            ent["shapes"] += 1
+            ent["gflop"] += count * 2.0 * conv_macs(og, s) / 1e9
+            for mode in ("fast", "exact"):
+                ent[f"{mode}_us"] += count * timed(lambda: og.conv2d(
+                    dx, dw, stride=s.stride, pad=s.pad, dil=s.dil, groups=s.groups, mode=mode, out=y))
+            del dx, dw, y
+        ent["gflop"] = round(ent["gflop"], 3)
+        for mode in ("fast", "exact"):
+            ent[f"{mode}_us"] = round(ent[f"{mode}_us"], 1)
+            ent[f"{mode}_tflops"] = round(ent["gflop"] * 1e3 / ent[f"{mode}_us"], 2)
+        ent["exact_over_fast"] = round(ent["exact_us"] / ent["fast_us"], 3)
+        rows[name] = ent
+    return rows
 
 
 def run_chain(og, layers, mode):
@@ -356,6 +410,11 @@ def extras(torch, og, synth, timer, only=None):
                          "hbm_gbps_hot": round(nbytes / (ms * 1e-3) / 1e9, 1)}
         out[f"gemm_nt_{m}x{n}x4096"] = ent
         del A, Bt, C
+    if want("model_rows"):
+        # the pages' model rows: over the distinct matrix-product and
+        # convolution shapes of one model, count x time summed, exact / fast
+        log("extra: model rows")
+        out["model_rows"] = model_rows(torch, og, synth, timer)
     if want("conv1x1"):
         # the 1x1 layers of the batch-8 chain, hot and cold (HBM-bound shapes)
         log("extra: 1x1 layers of the batch-8 chain")

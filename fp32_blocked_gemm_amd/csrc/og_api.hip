@@ -725,10 +725,12 @@ og_status og_gemm_nt_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_
 
   og::Problem p{};
   p.groups = 1;
-  if (m <= 16 && t_variant == 0 && vt_ok(B, ldb, k) && (m > 1 || k > kStreamMinK)) {
-    // a few rows of A (a single row with a long k, or up to 16) streamed
-    // against the rows of B through the chain kernel, 4 rows x 16 columns
-    // per block
+  // few rows: up to 16, or up to 256 while 64 x 64 tiles would be fewer than
+  // the chip's 256 CUs (each tile would run its whole k chain alone)
+  const bool few_rows = m <= 16 || (m <= 256 && ceil_div(m, 64) * ceil_div(n, 64) < 256);
+  if (few_rows && t_variant == 0 && vt_ok(B, ldb, k) && (m > 1 || k > kStreamMinK)) {
+    // a few rows of A (a single row with a long k, or more) streamed against
+    // the rows of B through the chain kernel, 4 rows x 16 columns per block
     og::Problem q{};
     q.A = A;
     q.lda = lda;

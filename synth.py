@@ -275,3 +275,54 @@ def gemm_single_column() -> GemmCase:
     A = normal((4096, 4096), seed_for(3, 10), 0.02)
     B = normal((4096, 1), seed_for(3, 11))
     return GemmCase("gemm_single_column_4096x1x4096", 4096, 1, 4096, 4096, 1, 1, A, B)
+
+
+def transformer_linear_shapes(model: str) -> list[tuple[str, int, int, int, int]]:
+    """The matrix products of one model's linear layers: (name, m, n, k, count).
+
+    m = token rows, k = input features, n = output features; the weights are
+    stored as n x k (out x in), so these run as products with an N x K operand.
+    Public architecture dimensions: BERT-base (hidden 768, 3072 FFN, 12
+    layers), MiniLM-L6 (hidden 384, 1536 FFN, 6 layers), the Whisper-small
+    encoder (768, 3072, 12 layers); per layer the query, key, value and output
+    projections and the two FFN layers.  Token rows as in the pages' model
+    rows: 32 x 128 (and 128) for BERT and MiniLM, 1500 frames for Whisper.
+    Attention's own products are left out, as on the pages.
+    """
+    dims = {"bert_base_4096": (4096, 768, 3072, 12), "bert_base_128": (128, 768, 3072, 12),
+            "minilm_l6_4096": (4096, 384, 1536, 6), "whisper_small_enc_1500": (1500, 768, 3072, 12)}
+    rows, h, f, layers = dims[model]
+    return [("qkvo", rows, h, h, 4 * layers), ("ffn_up", rows, f, h, layers),
+            ("ffn_down", rows, h, f, layers)]
+
+
+def whisper_small_frontend() -> list[ConvShape]:
+    """The Whisper-small encoder's two 1-D convolutions over 3000 mel frames
+    (80 -> 768, width 3, pad 1; 768 -> 768, width 3, stride 2, pad 1), as H = 1."""
+    return [ConvShape("whisper.conv1", 1, 80, 1, 3000, 768, 1, 3, (1, 1), (0, 1, 0, 1)),
+            ConvShape("whisper.conv2", 1, 768, 1, 3000, 768, 1, 3, (1, 2), (0, 1, 0, 1))]
+
+
+def mobilenetv3_large_convs(batch: int = 1) -> list[ConvShape]:
+    """The convolutions of MobileNetV3-large at 224x224 without the
+    squeeze-and-excitation and classifier layers: the 3x3/2 stem, for each
+    bottleneck its 1x1 expansion (when the expanded width differs from the
+    input), its depthwise convolution and its 1x1 projection, and the last
+    1x1 convolution (160 -> 960) (Howard et al. 2019, table 1)."""
+    layers = [ConvShape("stem", batch, 3, 224, 224, 16, 3, 3, (2, 2), (1, 1, 1, 1))]
+    # (input channels, window, expanded, output channels, stride, input size)
+    spec = ((16, 3, 16, 16, 1, 112), (16, 3, 64, 24, 2, 112), (24, 3, 72, 24, 1, 56),
+            (24, 5, 72, 40, 2, 56), (40, 5, 120, 40, 1, 28), (40, 5, 120, 40, 1, 28),
+            (40, 3, 240, 80, 2, 28), (80, 3, 200, 80, 1, 14), (80, 3, 184, 80, 1, 14),
+            (80, 3, 184, 80, 1, 14), (80, 3, 480, 112, 1, 14), (112, 3, 672, 112, 1, 14),
+            (112, 5, 672, 160, 2, 14), (160, 5, 960, 160, 1, 7), (160, 5, 960, 160, 1, 7))
+    for i, (cin, k, exp, cout, s, hw) in enumerate(spec):
+        tag = f"bneck{i + 1}"
+        if exp != cin:
+            layers.append(ConvShape(tag + ".expand", batch, cin, hw, hw, exp, 1, 1))
+        p = k // 2
+        layers.append(ConvShape(tag + ".dw", batch, exp, hw, hw, exp, k, k, (s, s), (p, p, p, p),
+                                (1, 1), exp))
+        layers.append(ConvShape(tag + ".project", batch, exp, hw // s, hw // s, cout, 1, 1))
+    layers.append(ConvShape("last", batch, 160, 7, 7, 960, 1, 1))
+    return layers

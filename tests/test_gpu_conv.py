@@ -148,6 +148,25 @@ def test_grouped_direct_kernel(orc, variant):
                              f"grouped variant {variant} {s} mode {mode}")
 
 
+@pytest.mark.parametrize("mode", MODES)
+def test_mobilenetv3_large_all_convs(orc, mode):
+    """The 46 convolutions of MobileNetV3-large at batch 1 (stem, 1x1
+    expansions and projections, depthwise, last 1x1), every output."""
+    for i, s in enumerate(synth.mobilenetv3_large_convs(1)):
+        x, w = synth.conv_inputs(s, synth.seed_for(8, 500 + i))
+        say(f"mobilenetv3 conv {s} mode {mode}")
+        assert sha256(_gpu_conv(x, w, s, mode)) == sha256(_oracle(orc, x, w, s, mode)), f"{s}"
+
+
+def test_whisper_frontend_convs(orc):
+    """The Whisper-small encoder's two 1-D convolutions (as H = 1), every output."""
+    for i, s in enumerate(synth.whisper_small_frontend()):
+        x, w = synth.conv_inputs(s, synth.seed_for(8, 600 + i))
+        for mode in MODES:
+            say(f"whisper conv {s} mode {mode}")
+            assert_same_bits(_gpu_conv(x, w, s, mode), _oracle(orc, x, w, s, mode), f"{s} mode {mode}")
+
+
 def test_padding_tap_meets_infinite_weight(orc):
     """An infinite weight on a padding tap gives NaN (padding taps are real products)."""
     s = synth.ConvShape("w8", 1, 1, 1, 1, 1, 3, 3, (1, 1), (1, 1, 1, 1))

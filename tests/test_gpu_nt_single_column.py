@@ -125,6 +125,28 @@ def test_nt_prefill_sampled(orc):
                              f"nt prefill row {r} mode {mode}")
 
 
+@pytest.mark.parametrize("model", ["bert_base_4096", "minilm_l6_4096", "whisper_small_enc_1500"])
+def test_transformer_linear_layers_sampled(orc, model):
+    """The linear layers of the transformer model rows (weights N x K):
+    sampled outputs, corners and one whole row per shape."""
+    rng = np.random.default_rng(900)
+    for i, (name, m, n, k, _) in enumerate(synth.transformer_linear_shapes(model)):
+        A = synth.normal((m, k), synth.seed_for(8, 10 * i))
+        W = synth.normal((n, k), synth.seed_for(8, 10 * i + 1), 0.02)
+        Wc = np.ascontiguousarray(W.T)
+        dA, dW = torch().from_numpy(A).cuda(), torch().from_numpy(W).cuda()
+        for mode in MODES:
+            say(f"{model} {name} {m}x{n}x{k} mode {mode}")
+            got = to_host(og.gemm_nt(dA, dW, mode))
+            rows = np.concatenate([rng.integers(0, m, 1000), [0, 0, m - 1, m - 1]])
+            cols = np.concatenate([rng.integers(0, n, 1000), [0, n - 1, 0, n - 1]])
+            assert_same_bits(got[rows, cols], orc.gemm_at(A, Wc, rows, cols, mode),
+                             f"{model} {name} sampled mode {mode}")
+            r = int(rng.integers(0, m))
+            assert_same_bits(got[r:r + 1], orc.gemm(A[r:r + 1], Wc, mode, rowwise=True),
+                             f"{model} {name} row {r} mode {mode}")
+
+
 @pytest.mark.parametrize("mode", MODES)
 def test_single_row_nt(orc, mode):
     """m = 1: one row against the rows of an n x k matrix, every output."""
@@ -157,11 +179,14 @@ def test_single_row_nt_streamed(orc, mode):
 
 @pytest.mark.parametrize("mode", MODES)
 def test_few_rows_nt_streamed(orc, mode):
-    """2 to 16 rows against an aligned N x K operand (the chain kernel, 4 rows
-    per block): row counts not a multiple of 4, strided A and C."""
+    """2 to 255 rows against an aligned N x K operand, where 64 x 64 tiles
+    would be few (the chain kernel, 4 rows per block): row counts not a
+    multiple of 4, strided A and C."""
     rng = np.random.default_rng(878 + mode)
     for (m, n, k, lda, ldb) in ((2, 33, 64, 64, 64), (3, 100, 260, 263, 264), (5, 16, 128, 130, 132),
-                                (8, 517, 1000, 1000, 1004), (16, 4096, 4096, 4096, 4096)):
+                                (8, 517, 1000, 1000, 1004), (16, 4096, 4096, 4096, 4096),
+                                (37, 300, 128, 128, 132), (128, 768, 768, 768, 768),
+                                (255, 900, 516, 516, 516)):
         A = _mixed(rng, (m, k), 0.01)
         Bt = _mixed(rng, (n, k), 0.001, 0.02)
         say(f"gemm_nt few rows {m}x{n}x{k} lda {lda} ldb {ldb} mode {mode}")
