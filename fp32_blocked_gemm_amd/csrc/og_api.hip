@@ -525,16 +525,27 @@ constexpr int64_t kStreamMinK = 256;
 // through LDS, 16 bytes of one column per load and no transpose.
 // p: A = the row (M = 1), B = the N x K operand (ldb its row stride), C = the
 // n outputs (contiguous), N = n, K = k.
-template <int MODE>
-void launch_chain_vt_mode(og::Problem p, hipStream_t s) {
-  constexpr int BN = 16, CW = 1, R = 1, ROWS = og::chain_rows(CW, BN, R, false);
+template <int MODE, int BN, int CW, int R, bool MF>
+void launch_chain_vt_shape(og::Problem p, hipStream_t s) {
+  constexpr int ROWS = og::chain_rows(CW, BN, R, MF);
   using CS = og::ChainShape<1, BN, ROWS>;
   p.tiles_m = (int)ceil_div(p.M, ROWS);
   p.tiles_n = (int)ceil_div(p.N, BN);
   p.groups = 1;
   const dim3 grid((unsigned)p.tiles_m * (unsigned)p.tiles_n), block(64 * (CW + CS::PW + 1));
-  hipLaunchKernelGGL((og::chain_kernel<MODE, false, og::kLdVecT, 1, 1, BN, CW, R, false>), grid,
+  hipLaunchKernelGGL((og::chain_kernel<MODE, false, og::kLdVecT, 1, 1, BN, CW, R, MF>), grid,
                      block, 0, s, p);
+}
+
+// More than 16 rows in fast mode: the matrix-core chains of variant 14's
+// shape (16 rows x 64 columns per block, the N x K operand streamed once per
+// 16 rows instead of once per 4).
+template <int MODE>
+void launch_chain_vt_mode(og::Problem p, hipStream_t s) {
+  if constexpr (MODE == og::kFast) {
+    if (p.M > 16) return launch_chain_vt_shape<MODE, 64, 4, 1, true>(p, s);
+  }
+  launch_chain_vt_shape<MODE, 16, 1, 1, false>(p, s);
 }
 
 void launch_chain_vt(int mode, og::Problem p, hipStream_t s) {
