@@ -129,6 +129,11 @@ GROUPED_SHAPES = [
     synth.ConvShape("g3", 3, 40, 11, 13, 6, 3, 3, (1, 2), (0, 1, 2, 0), (1, 1), 2),
     synth.ConvShape("g5", 1, 100, 17, 9, 25, 3, 3, (2, 1), (1, 0, 1, 3), (1, 2), 5),
     synth.ConvShape("g8w", 2, 32, 65, 3, 32, 3, 3, (1, 1), (1, 1, 1, 1), (3, 1), 4),
+    # wider planes: stride 2 and dilation 2 across, dilation 2 down, strides
+    # on one axis, two channel blocks (Cin/G = 20), asymmetric padding
+    synth.ConvShape("gb1", 2, 48, 40, 50, 32, 3, 3, (1, 2), (2, 1, 2, 3), (2, 2), 8),
+    synth.ConvShape("gb2", 1, 160, 33, 45, 40, 3, 3, (2, 1), (1, 1, 1, 1), (1, 1), 20),
+    synth.ConvShape("gb3", 1, 80, 20, 30, 20, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), 4),
 ]
 
 
