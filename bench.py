@@ -53,7 +53,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", default=None,
                     help="time one workload only (for profiling): gemm4096_fast, gemm4096_exact, "
-                         "resnet_b1, resnet_b8, skinny, prefill, grouped, conv1d, conv1x1, ragged, "
+                         "resnet_b1, resnet_b8, epilogue, skinny, prefill, grouped, conv1d, conv1x1, ragged, "
                          "gemm256, dw_b1, dw_b8, se, single_column, nt_prefill, nt_single_row, nt_rows8, model_rows, "
                          "copy (a 1 GiB device copy, to scale the HBM byte counters)")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
@@ -371,6 +371,42 @@ def extras(torch, og, synth, timer, only=None):
             ent["pages_cpu_context_ms"] = PAGES_RESNET_CPU_MS
         out[f"resnet50_chain_b{batch}"] = ent
         del layers
+    if want("epilogue"):
+        # the batch-8 chain with each convolution's bias, ReLU and residual:
+        # fused into the convolution's stores, against the same three steps
+        # as separate elementwise passes over the output
+        log("extra: fused epilogue on the resnet50 batch-8 chain")
+        layers = conv_chain(torch, og, synth, 8)
+        epi = []
+        for i, (s, dx, dw, y) in enumerate(layers):
+            b = torch.from_numpy(synth.normal((s.Cout,), synth.seed_for(4, 300 + i), 0.1)).cuda()
+            r = torch.from_numpy(synth.normal(tuple(y.shape), synth.seed_for(4, 400 + i))).cuda()
+            epi.append((b, r))
+        out_bytes = sum(4.0 * y.numel() for *_, y in layers)
+        ent = {"layers": len(layers), "epilogue": "y = relu(conv + bias) + residual",
+               "output_mb": round(out_bytes / 1e6, 1)}
+
+        def fused(mode):
+            for (s, dx, dw, y), (b, r) in zip(layers, epi):
+                og.conv2d(dx, dw, stride=s.stride, pad=s.pad, dil=s.dil, groups=s.groups,
+                          mode=mode, out=y, bias=b, act="relu", residual=r)
+
+        def separate(mode):
+            run_chain(og, layers, mode)
+            for (s, dx, dw, y), (b, r) in zip(layers, epi):
+                y.add_(b.view(1, -1, 1, 1)).relu_().add_(r)
+
+        for mode in ("fast", "exact"):
+            row = {}
+            for key, fn in (("conv_only_ms", lambda: run_chain(og, layers, mode)),
+                            ("fused_ms", lambda: fused(mode)),
+                            ("separate_passes_ms", lambda: separate(mode))):
+                g = timer.graph(fn)
+                row[key] = round(timer.spike(g.replay), 4)
+                del g
+            ent[mode] = row
+        out["resnet50_b8_epilogue"] = ent
+        del layers, epi
     for name, shape_fn, dist in (("grouped", synth.grouped_dilated, "uniform"),
                                  ("conv1d", synth.conv1d_h1, "uniform")):
         if not want(name):

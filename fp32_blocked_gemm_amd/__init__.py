@@ -23,6 +23,9 @@ OG_ERR_TOO_LARGE = -4
 
 EXACT = 0
 FAST = 1
+ACT_NONE = 0
+ACT_RELU = 1
+_ACTS = {None: ACT_NONE, "none": ACT_NONE, "relu": ACT_RELU, ACT_NONE: ACT_NONE, ACT_RELU: ACT_RELU}
 _MODES = {"exact": EXACT, "fast": FAST, EXACT: EXACT, FAST: FAST}
 
 _i64 = ctypes.c_int64
@@ -53,6 +56,8 @@ def lib() -> ctypes.CDLL:
     L.og_gemm_nt_f32.restype = ctypes.c_int
     L.og_conv2d_f32_ex.argtypes = [_i64] * 16 + [_vp, _vp, _vp, ctypes.c_int]
     L.og_conv2d_f32_ex.restype = ctypes.c_int
+    L.og_conv2d_f32_epi.argtypes = [_i64] * 16 + [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int]
+    L.og_conv2d_f32_epi.restype = ctypes.c_int
     L.og_conv2d_f32.argtypes = [_i64] * 11 + [_vp, _vp, _vp, ctypes.c_int]
     L.og_conv2d_f32.restype = ctypes.c_int
     L.og_conv2d_out_size.argtypes = [_i64] * 6
@@ -206,8 +211,10 @@ def gemm_nt(A, B, mode="exact", out=None):
 
 
 def conv2d(x, w, stride=(1, 1), pad=(0, 0, 0, 0), dil=(1, 1), groups=1, mode="exact",
-           out=None):
-    """NCHW convolution; pad = (top, left, bottom, right)."""
+           out=None, bias=None, act=None, residual=None):
+    """NCHW convolution; pad = (top, left, bottom, right).  With bias (Cout),
+    act ('relu') or residual (the output's shape) the epilogue runs in the
+    same kernels: bias, then activation, then residual."""
     torch = _torch()
     if isinstance(stride, int):
         stride = (stride, stride)
@@ -230,9 +237,26 @@ def conv2d(x, w, stride=(1, 1), pad=(0, 0, 0, 0), dil=(1, 1), groups=1, mode="ex
     if tuple(out.shape) != (N, Cout, OH, OW) or not out.is_contiguous():
         raise ValueError("out must be a contiguous [N, Cout, OH, OW] tensor")
     dev = _check_f32_cuda(x, w, out)
+    if act not in _ACTS:
+        raise ValueError(f"act must be None or 'relu', not {act!r}")
+    if bias is not None:
+        _check_f32_cuda(bias, out)
+        if tuple(bias.shape) != (Cout,) or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous tensor of Cout floats")
+    if residual is not None:
+        _check_f32_cuda(residual, out)
+        if tuple(residual.shape) != tuple(out.shape) or not residual.is_contiguous():
+            raise ValueError("residual must be a contiguous tensor of the output's shape")
     with torch.cuda.device(dev):
         _use_stream_of(out)
-        conv2d_f32_ex(N, Cin, H, W, Cout, groups, KH, KW, stride[0], stride[1], pad[0], pad[1],
-                      pad[2], pad[3], dil[0], dil[1], x.data_ptr(), w.data_ptr(), out.data_ptr(),
-                      mode)
+        if bias is None and residual is None and _ACTS[act] == ACT_NONE:
+            conv2d_f32_ex(N, Cin, H, W, Cout, groups, KH, KW, stride[0], stride[1], pad[0],
+                          pad[1], pad[2], pad[3], dil[0], dil[1], x.data_ptr(), w.data_ptr(),
+                          out.data_ptr(), mode)
+        else:
+            _check(lib().og_conv2d_f32_epi(
+                N, Cin, H, W, Cout, groups, KH, KW, stride[0], stride[1], pad[0], pad[1], pad[2],
+                pad[3], dil[0], dil[1], x.data_ptr(), w.data_ptr(),
+                None if bias is None else bias.data_ptr(), _ACTS[act],
+                None if residual is None else residual.data_ptr(), out.data_ptr(), _mode(mode)))
     return out

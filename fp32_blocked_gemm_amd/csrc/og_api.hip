@@ -481,8 +481,8 @@ void launch_dw(og::Problem p, int per_lane, hipStream_t s) {
   const dim3 grid((unsigned)ceil_div((int64_t)p.tiles_m * p.tiles_n, 4));
   if (p.KH == 3 && p.KW == 3)
     launch_dw_window<MODE, 3, 3>(p, per_lane, grid, s);
-  else if (p.KH == 5 && p.KW == 5)
-    launch_dw_window<MODE, 5, 5>(p, per_lane, grid, s);
+  else if (p.KH == 5 && p.KW == 5)  // one output per lane (dw_outputs_per_lane)
+    hipLaunchKernelGGL((og::dw_kernel<MODE, 5, 5, 1>), grid, dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL((og::dw_kernel<MODE, 0, 0, 1>), grid, dim3(256), 0, s, p);
 }
@@ -797,13 +797,23 @@ int64_t og_conv2d_out_size(int64_t size, int64_t k, int64_t stride, int64_t padB
   return span / stride + 1;
 }
 
-og_status og_conv2d_f32_ex(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout,
-                           int64_t G, int64_t KH, int64_t KW, int64_t strideH, int64_t strideW,
-                           int64_t padTop, int64_t padLeft, int64_t padBottom, int64_t padRight,
-                           int64_t dilH, int64_t dilW, const float *x, const float *w, float *y,
-                           int mode) {
+}  // extern "C"
+
+namespace {
+
+// The convolution, with the epilogue (bias, activation, residual) or without
+// (all null / 0).
+og_status conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout, int64_t G, int64_t KH,
+                 int64_t KW, int64_t strideH, int64_t strideW, int64_t padTop, int64_t padLeft,
+                 int64_t padBottom, int64_t padRight, int64_t dilH, int64_t dilW, const float *x,
+                 const float *w, const float *bias, int act, const float *residual, float *y,
+                 int mode) {
   if (mode != OG_MODE_EXACT && mode != OG_MODE_FAST)
     return fail(OG_ERR_INVALID_ARG, "og_conv2d_f32: mode %d is not 0 (exact) or 1 (fast)", mode);
+  if (act != OG_ACT_NONE && act != OG_ACT_RELU)
+    return fail(OG_ERR_INVALID_ARG, "og_conv2d_f32_epi: activation %d is not 0 (none) or 1 (ReLU)",
+                act);
+  const bool epilogue = bias != nullptr || residual != nullptr || act != OG_ACT_NONE;
   if (N < 1 || Cin < 1 || H < 1 || W < 1 || Cout < 1 || G < 1 || KH < 1 || KW < 1)
     return fail(OG_ERR_INVALID_ARG, "og_conv2d_f32: sizes must be >= 1");
   if (strideH < 1 || strideW < 1 || dilH < 1 || dilW < 1)
@@ -838,6 +848,9 @@ og_status og_conv2d_f32_ex(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t
   if (st != OG_OK) return st;
 
   og::Problem p{};
+  p.bias = bias;
+  p.res = residual;
+  p.act = act;
   p.A = w;
   p.lda = K;
   p.a_gstride = cout_g * K;
@@ -898,7 +911,9 @@ og_status og_conv2d_f32_ex(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t
   }
   const bool av = aligned16(w) && K % 4 == 0 && (cout_g * K) % 4 == 0;
   p.a_vec = av ? 1 : 0;
-  const bool stream_se = planes && ncols == 1 && G == 1 && K > kStreamMinK && vt_ok(w, K, K);
+  // (the streamed form's outputs are its columns, not its rows: no epilogue there)
+  const bool stream_se = planes && ncols == 1 && G == 1 && K > kStreamMinK && vt_ok(w, K, K) &&
+                         !epilogue;
   if (planes && ncols == 1 && !stream_se && K <= kRowdotMaxK && t_variant == 0 &&
       rowdot_fits(cout_g, K, 1, G)) {
     // a 1x1 convolution of one 1x1 input: per group, the weight rows against
@@ -930,6 +945,29 @@ og_status og_conv2d_f32_ex(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t
   else
     launch<og::kBGather>(mode, av, false, t, p, t_stream);
   return check_launch("og_conv2d_f32");
+}
+
+}  // namespace
+
+extern "C" {
+
+og_status og_conv2d_f32_ex(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout,
+                           int64_t G, int64_t KH, int64_t KW, int64_t strideH, int64_t strideW,
+                           int64_t padTop, int64_t padLeft, int64_t padBottom, int64_t padRight,
+                           int64_t dilH, int64_t dilW, const float *x, const float *w, float *y,
+                           int mode) {
+  return conv2d(N, Cin, H, W, Cout, G, KH, KW, strideH, strideW, padTop, padLeft, padBottom,
+                padRight, dilH, dilW, x, w, nullptr, OG_ACT_NONE, nullptr, y, mode);
+}
+
+og_status og_conv2d_f32_epi(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout,
+                            int64_t G, int64_t KH, int64_t KW, int64_t strideH, int64_t strideW,
+                            int64_t padTop, int64_t padLeft, int64_t padBottom, int64_t padRight,
+                            int64_t dilH, int64_t dilW, const float *x, const float *w,
+                            const float *bias, int act, const float *residual, float *y,
+                            int mode) {
+  return conv2d(N, Cin, H, W, Cout, G, KH, KW, strideH, strideW, padTop, padLeft, padBottom,
+                padRight, dilH, dilW, x, w, bias, act, residual, y, mode);
 }
 
 og_status og_conv2d_f32(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout, int64_t G,

@@ -77,6 +77,10 @@ struct Problem {
   int64_t y_img, y_grp;  // element strides of y between images and between groups
   int a_vec;             // A rows 16-byte aligned (A, lda and K multiples of 4 floats)
   int bh, ih, iw;        // depthwise band kernel: output rows per band, staged input rows, columns
+  // convolution epilogue (null / 0: none): bias per output channel, then the
+  // activation (1: ReLU), then the residual at the output's own position
+  const float *bias, *res;
+  int act;
 };
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I = 0..N-1.
@@ -125,6 +129,21 @@ __host__ __device__ inline TileCoord tile_of_block(int bid, int nblocks, int til
 
 __device__ inline float canonical(float v) {
   return v != v ? __uint_as_float(0x7FC00000u) : v;
+}
+
+// The value stored for output channel ch at dst: the finished sum, then the
+// convolution epilogue of "Convolution (fast mode)", sections "Tiles and
+// chunks" (bias, then activation) and "Single-column products" (bias,
+// activation and residual) -- each a separately rounded operation after the
+// whole sum, so the sum's bits are those of the plain convolution -- then a
+// NaN made canonical.  ReLU keeps a NaN and turns every other value not
+// above zero into +0.
+__device__ __forceinline__ float finish(const Problem &p, float acc, int64_t ch, const float *dst) {
+  float v = acc;
+  if (p.bias != nullptr) v = v + p.bias[ch];
+  if (p.act == 1) v = v > 0.0f ? v : (v != v ? v : 0.0f);
+  if (p.res != nullptr) v = v + p.res[dst - p.C];
+  return canonical(v);
 }
 
 // ---------------------------------------------------------------------------
@@ -589,7 +608,10 @@ __global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
         for (int r = 0; r < 16; ++r) {
           const int col = n0 + wn * TN * 64 + j * 64 + 16 * (r >> 2) + (lane & 15);
           const int row = m0 + wm * TM * 16 + i * 16 + 4 * (lane >> 4) + (r & 3);
-          if (col < p.N && row < p.M) *out_ptr<KIND>(p, tc.g, row, col) = canonical(acc[i][j][r]);
+          if (col < p.N && row < p.M) {
+            float *d = out_ptr<KIND>(p, tc.g, row, col);
+            *d = finish(p, acc[i][j][r], (int64_t)tc.g * p.M + row, d);
+          }
         }
     return;
   }
@@ -609,7 +631,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = m0 + wm * TM * 32 + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r & 3);
-          if (row < p.M) base[row * rstride] = canonical(acc[i][j][h * 16 + r]);
+          if (row < p.M) base[row * rstride] = finish(p, acc[i][j][h * 16 + r], (int64_t)tc.g * p.M + row, base + row * rstride);
         }
       }
 }
@@ -692,7 +714,7 @@ __global__ void __launch_bounds__(256) valu_kernel(Problem p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = m0 + ty * 4 + i;
-      if (row < p.M) base[row * rstride] = canonical(acc[i][j]);
+      if (row < p.M) base[row * rstride] = finish(p, acc[i][j], (int64_t)tc.g * p.M + row, base + row * rstride);
     }
   }
 }
@@ -799,7 +821,8 @@ __global__ void __launch_bounds__(64 * W) lane_kernel(Problem p) {
     const int64_t rstride = KIND == kBMatrix ? p.ldc : (int64_t)p.OHW;
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      if (row0 + r < p.M) base[(row0 + r) * rstride] = canonical(acc[r]);
+      if (row0 + r < p.M)
+        base[(row0 + r) * rstride] = finish(p, acc[r], (int64_t)tc.g * p.M + row0 + r, base + (row0 + r) * rstride);
   }
 }
 
@@ -912,7 +935,9 @@ __global__ void __launch_bounds__(64 * W) lane_conv_kernel(Problem p) {
     float *base = out_ptr<kBGather>(p, tc.g, 0, img * p.OHW + pix);
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      if (row0 + r < p.M) base[(int64_t)(row0 + r) * p.OHW] = canonical(acc[r]);
+      if (row0 + r < p.M)
+        base[(int64_t)(row0 + r) * p.OHW] =
+            finish(p, acc[r], (int64_t)tc.g * p.M + row0 + r, base + (int64_t)(row0 + r) * p.OHW);
   }
 }
 
@@ -1460,7 +1485,8 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, chain_rows(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = row0 + rb0 + 4 * c + i;
-          if (row < p.M) base[(int64_t)row * rstride] = canonical(acc4[c][i]);
+          if (row < p.M)
+            base[(int64_t)row * rstride] = finish(p, acc4[c][i], (int64_t)tc.g * p.M + row, base + (int64_t)row * rstride);
         }
     }
     return;
@@ -1471,7 +1497,8 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, chain_rows(
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int row = row0 + rb0 + r;
-      if (row < p.M) base[(int64_t)row * rstride] = canonical(acc[r]);
+      if (row < p.M)
+        base[(int64_t)row * rstride] = finish(p, acc[r], (int64_t)tc.g * p.M + row, base + (int64_t)row * rstride);
     }
   }
 }
@@ -1570,7 +1597,7 @@ __global__ void __launch_bounds__(256) dw_kernel(Problem p) {
   float *yp = p.C + img * p.y_img + (int64_t)oc * p.OHW;
 #pragma unroll
   for (int j = 0; j < P; ++j)
-    if (valid[j]) yp[pix0 + 64 * j] = canonical(acc[j]);
+    if (valid[j]) yp[pix0 + 64 * j] = finish(p, acc[j], oc, yp + pix0 + 64 * j);
 }
 
 // ---------------------------------------------------------------------------
@@ -1644,7 +1671,7 @@ __global__ void __launch_bounds__(256) dw_band_kernel(Problem p) {
 #pragma unroll
       for (int kx = 0; kx < KW; ++kx)
         acc = term<MODE>(acc, w[ky * KW + kx], t[ky * p.dH * p.iw + kx * p.dW]);
-    yp[o] = canonical(acc);
+    yp[o] = finish(p, acc, oc, yp + o);
     oyl += qr;
     ox += qc;
     if (ox >= p.OW) {
@@ -1738,7 +1765,8 @@ __global__ void __launch_bounds__(256) grouped_kernel(Problem p) {
 #pragma unroll
       for (int j = 0; j < (R >= 2 ? 2 : 1); ++j) {
         const int row = i * (R >= 2 ? 2 : 1) + j;
-        if (row < p.M) yp[(int64_t)row * p.OHW] = canonical(acc[i][j]);
+        if (row < p.M)
+          yp[(int64_t)row * p.OHW] = finish(p, acc[i][j], (int64_t)g * p.M + row, yp + (int64_t)row * p.OHW);
       }
   }
 }
@@ -1809,7 +1837,10 @@ __global__ void __launch_bounds__(64) rowdot_kernel(Problem p) {
       if (full + (int)decltype(j)::value < nchunks) compute(j);
     });
   }
-  if (ok) p.C[tc.g * p.y_grp + (int64_t)(row0 + lane) * p.ldc] = canonical(acc[0]);
+  if (ok) {
+    float *d = p.C + tc.g * p.y_grp + (int64_t)(row0 + lane) * p.ldc;
+    *d = finish(p, acc[0], (int64_t)tc.g * p.M + row0 + lane, d);
+  }
 }
 
 }  // namespace og

@@ -53,6 +53,9 @@ typedef int og_status;
 #define OG_MODE_EXACT 0 /* separately rounded multiply and add ("Exact mode")              */
 #define OG_MODE_FAST 1  /* one fused multiply-add per term, same order ("Fast mode")        */
 
+#define OG_ACT_NONE 0 /* og_conv2d_f32_epi: no activation                                 */
+#define OG_ACT_RELU 1 /* og_conv2d_f32_epi: v > 0 ? v : +0 (a NaN stays NaN)              */
+
 /*
  * Matrix product, row-major ("Matrix product and convolution kernels",
  * first paragraph; "Exact mode", section "Matrix product"):
@@ -117,6 +120,33 @@ og_status og_conv2d_f32_ex(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t
                            int64_t padTop, int64_t padLeft, int64_t padBottom, int64_t padRight,
                            int64_t dilH, int64_t dilW, const float *x, const float *w, float *y,
                            int mode);
+
+/*
+ * og_conv2d_f32_ex followed by the convolution epilogue ("Convolution (fast
+ * mode)", section "Tiles and chunks": bias, then activation, applied to each
+ * finished output with rows counted from the group's first output channel;
+ * section "Single-column products": the bias, activation and residual
+ * epilogue).  For output (n, oc, oy, ox) with sum s (summed by the mode's
+ * rule, exactly as og_conv2d_f32_ex does):
+ *
+ *     v = s + bias[oc]                       (if bias is not NULL; rounded)
+ *     v = v > 0 ? v : +0, NaN kept           (if act == OG_ACT_RELU)
+ *     v = v + residual[n][oc][oy][ox]        (if residual is not NULL; rounded)
+ *     y[n][oc][oy][ox] = isNaN(v) ? 0x7FC00000 : v
+ *
+ * bias: Cout floats; residual: a contiguous [N, Cout, OutH, OutW] tensor
+ * (it may be y itself: each output reads its own residual before writing);
+ * both device pointers owned by the caller, NULL for none.  act must be
+ * OG_ACT_NONE or OG_ACT_RELU, else OG_ERR_INVALID_ARG; otherwise the contract
+ * of og_conv2d_f32_ex.  With no bias, no activation and no residual the
+ * result equals og_conv2d_f32_ex's.
+ */
+og_status og_conv2d_f32_epi(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout,
+                            int64_t G, int64_t KH, int64_t KW, int64_t strideH, int64_t strideW,
+                            int64_t padTop, int64_t padLeft, int64_t padBottom, int64_t padRight,
+                            int64_t dilH, int64_t dilW, const float *x, const float *w,
+                            const float *bias, int act, const float *residual, float *y,
+                            int mode);
 
 /*
  * The same convolution with one stride, one symmetric padding and one

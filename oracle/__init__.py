@@ -76,11 +76,13 @@ class Oracle:
         L.ogref_conv2d_f32_ex.argtypes = conv_args
         L.ogref_conv2d_im2col_f32_ex.argtypes = conv_args
         L.ogref_conv2d_f32_at.argtypes = [_i64] * 16 + [_fp, _fp, _i64, _fp, _fp, ctypes.c_int]
+        L.ogref_conv_epilogue_f32.argtypes = [_i64, _i64, _i64, _fp, _fp, ctypes.c_int, _fp]
         L.ogref_conv_out_size.argtypes = [_i64] * 6
         L.ogref_conv_out_size.restype = _i64
         for name in ("ogref_gemm_f32", "ogref_gemm_f32_rowwise", "ogref_gemm_f32_at",
                      "ogref_conv2d_f32_ex", "ogref_conv2d_im2col_f32_ex",
-                     "ogref_conv2d_f32_at", "ogref_selftest", "ogref_num_threads",
+                     "ogref_conv2d_f32_at", "ogref_conv_epilogue_f32", "ogref_selftest",
+                     "ogref_num_threads",
                      "ogref_set_num_threads"):
             getattr(L, name).restype = ctypes.c_int
         L.ogref_set_num_threads.argtypes = [ctypes.c_int]
@@ -168,6 +170,23 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle conv2d_at: invalid arguments")
         return out
+
+
+    def conv_epilogue(self, y: np.ndarray, bias=None, act: int = 0, residual=None) -> np.ndarray:
+        """A copy of y [N, Cout, OH, OW] with the convolution epilogue applied:
+        + bias[oc], then ReLU (act 1), then + residual, then canonical NaN."""
+        y = np.ascontiguousarray(y, dtype=np.float32).copy()
+        N, Cout = y.shape[0], y.shape[1]
+        ohw = y.shape[2] * y.shape[3]
+        b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+        r = None if residual is None else np.ascontiguousarray(residual, dtype=np.float32)
+        assert b is None or b.shape == (Cout,)
+        assert r is None or r.shape == y.shape
+        rc = self.L.ogref_conv_epilogue_f32(N, Cout, ohw, _ptr(y), None if b is None else _ptr(b),
+                                            act, None if r is None else _ptr(r))
+        if rc != 0:
+            raise ValueError("oracle conv_epilogue: invalid activation")
+        return y
 
 
 _default: Oracle | None = None

@@ -377,3 +377,28 @@ int ogref_set_num_threads(int n)
     return 1;
 #endif
 }
+
+/* The convolution epilogue: bias of the output channel, then the activation,
+ * then the residual, after the whole sum ("Convolution (fast mode)", section
+ * "Tiles and chunks": bias, then activation; section "Single-column
+ * products": the bias, activation and residual epilogue). */
+int ogref_conv_epilogue_f32(int64_t N, int64_t Cout, int64_t OHW, float *y, const float *bias,
+                            int act, const float *residual)
+{
+    if (act != 0 && act != 1)
+        return -1;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t oc = 0; oc < Cout; ++oc)
+            for (int64_t i = 0; i < OHW; ++i) {
+                const int64_t at = (n * Cout + oc) * OHW + i;
+                float v = y[at];
+                if (bias)
+                    v = v + bias[oc];
+                if (act == 1 && !isnan(v) && !(v > 0.0f))
+                    v = 0.0f;
+                if (residual)
+                    v = v + residual[at];
+                y[at] = store_value(v);
+            }
+    return 0;
+}

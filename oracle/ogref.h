@@ -73,6 +73,15 @@ int ogref_conv2d_f32_at(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Co
                         int64_t dilH, int64_t dilW, const float *x, const float *w,
                         int64_t npts, const int64_t *flat, float *out, int mode);
 
+/* The convolution epilogue, in place on y [N, Cout, OHW] ("Convolution (fast
+ * mode)", sections "Tiles and chunks" and "Single-column products"): per
+ * output, v = y + bias[oc] (if bias), then ReLU (act 1: v > 0 ? v : +0, a NaN
+ * kept), then v + residual (if residual, same position), each operation
+ * rounded on its own, then NaN made canonical.  Returns 0, or -1 for an
+ * activation other than 0 or 1. */
+int ogref_conv_epilogue_f32(int64_t N, int64_t Cout, int64_t OHW, float *y, const float *bias,
+                            int act, const float *residual);
+
 /* Load-time check that the compiled library separates fused from unfused
  * arithmetic:
  * the two-term sum [1+2^-11, -(1+2^-12)] . [1, 1+2^-12] is +0 exactly and

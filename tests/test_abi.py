@@ -116,6 +116,26 @@ def test_conv_rejects_before_launch(L, kw, why):
     assert L.og_last_error()
 
 
+def _conv_epi(L, act=0, bias=NULL, residual=NULL, **kw):
+    a = dict(N=1, Cin=4, H=5, W=5, Cout=4, G=1, KH=3, KW=3, s=(1, 1), p=(0, 0, 0, 0),
+             d=(1, 1), x=P, w=P, y=P, mode=0)
+    a.update(kw)
+    return L.og_conv2d_f32_epi(a["N"], a["Cin"], a["H"], a["W"], a["Cout"], a["G"], a["KH"],
+                               a["KW"], a["s"][0], a["s"][1], a["p"][0], a["p"][1], a["p"][2],
+                               a["p"][3], a["d"][0], a["d"][1], a["x"], a["w"], bias, act,
+                               residual, a["y"], a["mode"])
+
+
+@pytest.mark.parametrize("kw,why", [
+    (dict(act=2), "activation"), (dict(act=-1), "activation"), (dict(act=1, mode=2), "mode"),
+    (dict(bias=P, N=0), "N"), (dict(residual=P, y=NULL), "y null"),
+    (dict(act=1, G=3), "Cin % G"),
+])
+def test_conv_epilogue_rejects_before_launch(L, kw, why):
+    assert _conv_epi(L, **kw) == og.OG_ERR_INVALID_ARG, why
+    assert L.og_last_error()
+
+
 def test_out_size_matches_the_formula():
     orc = oracle.get()
     rng = np.random.default_rng(0)
