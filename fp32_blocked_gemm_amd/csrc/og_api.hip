@@ -422,14 +422,14 @@ int dw_outputs_per_lane(int64_t planes, int64_t ohw, int64_t kh, int64_t kw, int
   return 1;
 }
 
-template <int MODE, int KH, int KW>
+template <int MODE, bool EPI, int KH, int KW>
 void launch_dw_window(og::Problem p, int per_lane, dim3 grid, hipStream_t s) {
   if (per_lane == 4)
-    hipLaunchKernelGGL((og::dw_kernel<MODE, KH, KW, 4>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((og::dw_kernel<MODE, KH, KW, 4, EPI>), grid, dim3(256), 0, s, p);
   else if (per_lane == 2)
-    hipLaunchKernelGGL((og::dw_kernel<MODE, KH, KW, 2>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((og::dw_kernel<MODE, KH, KW, 2, EPI>), grid, dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL((og::dw_kernel<MODE, KH, KW, 1>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((og::dw_kernel<MODE, KH, KW, 1, EPI>), grid, dim3(256), 0, s, p);
 }
 
 // The band form of the depthwise kernel (input rows staged in LDS) for
@@ -437,7 +437,7 @@ void launch_dw_window(og::Problem p, int per_lane, dim3 grid, hipStream_t s) {
 // most 1024 outputs, enough bands for at least 1024 blocks, every band at
 // least 128 outputs, the staged rows within 32 KB.  Returns false (and
 // launches nothing) where the shape does not qualify.
-template <int MODE>
+template <int MODE, bool EPI>
 bool launch_dw_band(og::Problem p, int64_t planes, int64_t OH, int64_t OW, hipStream_t s) {
   const bool w3 = p.KH == 3 && p.KW == 3, w5 = p.KH == 5 && p.KW == 5;
   if (!(w3 || w5) || (w3 && p.sH == 1 && p.sW == 1) || OW < 28) return false;
@@ -456,36 +456,65 @@ bool launch_dw_band(og::Problem p, int64_t planes, int64_t OH, int64_t OW, hipSt
   const dim3 grid((unsigned)(planes * nb)), block(256);
   const size_t lds = (size_t)(4 * ih * iw);
   if (w3)
-    hipLaunchKernelGGL((og::dw_band_kernel<MODE, 3, 3>), grid, block, lds, s, p);
+    hipLaunchKernelGGL((og::dw_band_kernel<MODE, 3, 3, EPI>), grid, block, lds, s, p);
   else
-    hipLaunchKernelGGL((og::dw_band_kernel<MODE, 5, 5>), grid, block, lds, s, p);
+    hipLaunchKernelGGL((og::dw_band_kernel<MODE, 5, 5, EPI>), grid, block, lds, s, p);
   return true;
 }
 
 // The grouped direct kernel, R = Cout/G rounded up to 1, 2, 4 or 8 rows per lane.
-template <int MODE>
+template <int MODE, bool EPI>
 void launch_grouped_mode(og::Problem p, hipStream_t s) {
   const dim3 grid((unsigned)ceil_div((int64_t)p.tiles_m * p.tiles_n, 4)), block(256);
   if (p.M <= 1)
-    hipLaunchKernelGGL((og::grouped_kernel<MODE, 3, 3, 1>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((og::grouped_kernel<MODE, 3, 3, 1, EPI>), grid, block, 0, s, p);
   else if (p.M <= 2)
-    hipLaunchKernelGGL((og::grouped_kernel<MODE, 3, 3, 2>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((og::grouped_kernel<MODE, 3, 3, 2, EPI>), grid, block, 0, s, p);
   else if (p.M <= 4)
-    hipLaunchKernelGGL((og::grouped_kernel<MODE, 3, 3, 4>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((og::grouped_kernel<MODE, 3, 3, 4, EPI>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((og::grouped_kernel<MODE, 3, 3, 8>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((og::grouped_kernel<MODE, 3, 3, 8, EPI>), grid, block, 0, s, p);
 }
 
-template <int MODE>
+template <int MODE, bool EPI>
 void launch_dw(og::Problem p, int per_lane, hipStream_t s) {
   const dim3 grid((unsigned)ceil_div((int64_t)p.tiles_m * p.tiles_n, 4));
   if (p.KH == 3 && p.KW == 3)
-    launch_dw_window<MODE, 3, 3>(p, per_lane, grid, s);
+    launch_dw_window<MODE, EPI, 3, 3>(p, per_lane, grid, s);
   else if (p.KH == 5 && p.KW == 5)  // one output per lane (dw_outputs_per_lane)
-    hipLaunchKernelGGL((og::dw_kernel<MODE, 5, 5, 1>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((og::dw_kernel<MODE, 5, 5, 1, EPI>), grid, dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL((og::dw_kernel<MODE, 0, 0, 1>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((og::dw_kernel<MODE, 0, 0, 1, EPI>), grid, dim3(256), 0, s, p);
 }
+
+// The depthwise and grouped direct kernels are compiled with and without the
+// epilogue (EPI): (mode, epilogue) -> one of four instantiations.
+template <template <int, bool> class L, class... A>
+auto by_mode_epi(int mode, bool epi, A &&...a) {
+  if (mode == OG_MODE_EXACT)
+    return epi ? L<og::kExact, true>::run(a...) : L<og::kExact, false>::run(a...);
+  return epi ? L<og::kFast, true>::run(a...) : L<og::kFast, false>::run(a...);
+}
+template <int MODE, bool EPI>
+struct DwBand {
+  static bool run(og::Problem p, int64_t planes, int64_t OH, int64_t OW, hipStream_t s) {
+    return launch_dw_band<MODE, EPI>(p, planes, OH, OW, s);
+  }
+};
+template <int MODE, bool EPI>
+struct Dw {
+  static int run(og::Problem p, int per_lane, hipStream_t s) {
+    launch_dw<MODE, EPI>(p, per_lane, s);
+    return 0;
+  }
+};
+template <int MODE, bool EPI>
+struct Grouped {
+  static int run(og::Problem p, hipStream_t s) {
+    launch_grouped_mode<MODE, EPI>(p, s);
+    return 0;
+  }
+};
 
 // The row-dot kernel (single-column products): one wave of 64 rows per
 // block, a ring of 8 chunks of 16 taps; VEC: 16-byte loads of the rows.
@@ -832,7 +861,7 @@ og_status conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout, int
   const int64_t cin_g = Cin / G, cout_g = Cout / G;
   const int64_t K = cin_g * KH * KW, ncols = N * OH * OW;
   // every index the kernels form in 32 bits must fit
-  const int64_t dims[] = {K, ncols, cout_g, H, W, OH * OW, KH * KW,
+  const int64_t dims[] = {K, ncols, Cout, H, W, OH * OW, KH * KW,
                           (H + padTop + padBottom) * strideH, (W + padLeft + padRight) * strideW,
                           KH * dilH + H, KW * dilW + W};
   for (int64_t d : dims)
@@ -885,15 +914,11 @@ og_status conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout, int
     const int64_t per_plane = ceil_div(OH * OW, 64 * per_lane), nplanes = N * Cout;
     if (per_plane * nplanes > kI32Max - 3)
       return fail(OG_ERR_TOO_LARGE, "og_conv2d_f32: too many output planes");
-    if (mode == OG_MODE_EXACT ? launch_dw_band<og::kExact>(p, nplanes, OH, OW, t_stream)
-                              : launch_dw_band<og::kFast>(p, nplanes, OH, OW, t_stream))
+    if (by_mode_epi<DwBand>(mode, epilogue, p, nplanes, OH, OW, t_stream))
       return check_launch("og_conv2d_f32");
     p.tiles_m = (int)per_plane;
     p.tiles_n = (int)nplanes;
-    if (mode == OG_MODE_EXACT)
-      launch_dw<og::kExact>(p, per_lane, t_stream);
-    else
-      launch_dw<og::kFast>(p, per_lane, t_stream);
+    by_mode_epi<Dw>(mode, epilogue, p, per_lane, t_stream);
     return check_launch("og_conv2d_f32");
   }
   if (G > 1 && cin_g >= 2 && cin_g <= 64 && cout_g <= 8 && KH == 3 && KW == 3 &&
@@ -903,10 +928,7 @@ og_status conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout, int
     // an (image, group), all of the group's output channels per lane
     p.tiles_m = (int)ceil_div(OH * OW, 64);
     p.tiles_n = (int)(N * G);
-    if (mode == OG_MODE_EXACT)
-      launch_grouped_mode<og::kExact>(p, t_stream);
-    else
-      launch_grouped_mode<og::kFast>(p, t_stream);
+    by_mode_epi<Grouped>(mode, epilogue, p, t_stream);
     return check_launch("og_conv2d_f32");
   }
   const bool av = aligned16(w) && K % 4 == 0 && (cout_g * K) % 4 == 0;

@@ -137,8 +137,15 @@ __device__ inline float canonical(float v) {
 // activation and residual) -- each a separately rounded operation after the
 // whole sum, so the sum's bits are those of the plain convolution -- then a
 // NaN made canonical.  ReLU keeps a NaN and turns every other value not
-// above zero into +0.
-__device__ __forceinline__ float finish(const Problem &p, float acc, int64_t ch, const float *dst) {
+// above zero into +0.  The channel is a 32-bit index: computed in 64 bits
+// (group * M + row) it made the compiler treat the tile bases of the staging
+// loads as divergent, and the main loop read its operands through waterfall
+// loops.
+// EPI false: the plain store (kernels compiled both ways keep their store
+// loops free of the epilogue's tests).
+template <bool EPI = true>
+__device__ __forceinline__ float finish(const Problem &p, float acc, int ch, const float *dst) {
+  if constexpr (!EPI) return canonical(acc);
   float v = acc;
   if (p.bias != nullptr) v = v + p.bias[ch];
   if (p.act == 1) v = v > 0.0f ? v : (v != v ? v : 0.0f);
@@ -610,7 +617,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
           const int row = m0 + wm * TM * 16 + i * 16 + 4 * (lane >> 4) + (r & 3);
           if (col < p.N && row < p.M) {
             float *d = out_ptr<KIND>(p, tc.g, row, col);
-            *d = finish(p, acc[i][j][r], (int64_t)tc.g * p.M + row, d);
+            *d = finish(p, acc[i][j][r], tc.g * p.M + row, d);
           }
         }
     return;
@@ -631,7 +638,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = m0 + wm * TM * 32 + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r & 3);
-          if (row < p.M) base[row * rstride] = finish(p, acc[i][j][h * 16 + r], (int64_t)tc.g * p.M + row, base + row * rstride);
+          if (row < p.M) base[row * rstride] = finish(p, acc[i][j][h * 16 + r], tc.g * p.M + row, base + row * rstride);
         }
       }
 }
@@ -714,7 +721,7 @@ __global__ void __launch_bounds__(256) valu_kernel(Problem p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = m0 + ty * 4 + i;
-      if (row < p.M) base[row * rstride] = finish(p, acc[i][j], (int64_t)tc.g * p.M + row, base + row * rstride);
+      if (row < p.M) base[row * rstride] = finish(p, acc[i][j], tc.g * p.M + row, base + row * rstride);
     }
   }
 }
@@ -752,8 +759,12 @@ __device__ __forceinline__ float step_bcast(float acc, float w, float b) {
 // and a DPP row broadcast hands tap kk to all lanes.  Weights and B tiles
 // are loaded D-1 chunks ahead.
 // ---------------------------------------------------------------------------
+// (Matrix operands with one or two rows per wave: at least 6 waves per SIMD.
+// Left free, the compiler gave the exact two-row form 106 registers and 4
+// waves where 70 registers suffice; the ragged exact product ran 8 % slower.)
 template <int MODE, int KIND, int R, int W, int D>
-__global__ void __launch_bounds__(64 * W) lane_kernel(Problem p) {
+__global__ void __launch_bounds__(64 * W)
+    __attribute__((amdgpu_waves_per_eu(KIND == kBMatrix && R <= 2 ? 6 : 1))) lane_kernel(Problem p) {
   constexpr int NT = 64 * W, BK = 32, BN = 64, WR = BK / 16;
   __shared__ __align__(16) float Bs[2][BK * BN];
   using BS = BStage<BN, BK, NT, KIND, false>;
@@ -822,7 +833,7 @@ __global__ void __launch_bounds__(64 * W) lane_kernel(Problem p) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
       if (row0 + r < p.M)
-        base[(row0 + r) * rstride] = finish(p, acc[r], (int64_t)tc.g * p.M + row0 + r, base + (row0 + r) * rstride);
+        base[(row0 + r) * rstride] = finish(p, acc[r], tc.g * p.M + row0 + r, base + (row0 + r) * rstride);
   }
 }
 
@@ -937,7 +948,7 @@ __global__ void __launch_bounds__(64 * W) lane_conv_kernel(Problem p) {
     for (int r = 0; r < R; ++r)
       if (row0 + r < p.M)
         base[(int64_t)(row0 + r) * p.OHW] =
-            finish(p, acc[r], (int64_t)tc.g * p.M + row0 + r, base + (int64_t)(row0 + r) * p.OHW);
+            finish(p, acc[r], tc.g * p.M + row0 + r, base + (int64_t)(row0 + r) * p.OHW);
   }
 }
 
@@ -1486,7 +1497,7 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, chain_rows(
         for (int i = 0; i < 4; ++i) {
           const int row = row0 + rb0 + 4 * c + i;
           if (row < p.M)
-            base[(int64_t)row * rstride] = finish(p, acc4[c][i], (int64_t)tc.g * p.M + row, base + (int64_t)row * rstride);
+            base[(int64_t)row * rstride] = finish(p, acc4[c][i], tc.g * p.M + row, base + (int64_t)row * rstride);
         }
     }
     return;
@@ -1498,7 +1509,7 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, chain_rows(
     for (int r = 0; r < R; ++r) {
       const int row = row0 + rb0 + r;
       if (row < p.M)
-        base[(int64_t)row * rstride] = finish(p, acc[r], (int64_t)tc.g * p.M + row, base + (int64_t)row * rstride);
+        base[(int64_t)row * rstride] = finish(p, acc[r], tc.g * p.M + row, base + (int64_t)row * rstride);
     }
   }
 }
@@ -1539,7 +1550,7 @@ __device__ __forceinline__ float term(float acc, float w, float v) {
   return acc + prod;
 }
 
-template <int MODE, int KH_, int KW_, int P>
+template <int MODE, int KH_, int KW_, int P, bool EPI>
 __global__ void __launch_bounds__(256) dw_kernel(Problem p) {
   static_assert(P == 1 || (KH_ > 0 && KW_ > 0), "several outputs per lane: compiled windows only");
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1597,7 +1608,7 @@ __global__ void __launch_bounds__(256) dw_kernel(Problem p) {
   float *yp = p.C + img * p.y_img + (int64_t)oc * p.OHW;
 #pragma unroll
   for (int j = 0; j < P; ++j)
-    if (valid[j]) yp[pix0 + 64 * j] = finish(p, acc[j], oc, yp + pix0 + 64 * j);
+    if (valid[j]) yp[pix0 + 64 * j] = finish<EPI>(p, acc[j], oc, yp + pix0 + 64 * j);
 }
 
 // ---------------------------------------------------------------------------
@@ -1614,7 +1625,7 @@ __global__ void __launch_bounds__(256) dw_kernel(Problem p) {
 // Launch: tiles_m = bands per plane, tiles_n = N*Cout planes, dynamic LDS
 // 4*IH*IW bytes.
 // ---------------------------------------------------------------------------
-template <int MODE, int KH, int KW>
+template <int MODE, int KH, int KW, bool EPI>
 __global__ void __launch_bounds__(256) dw_band_kernel(Problem p) {
   extern __shared__ float tile[];
   const int tid = threadIdx.x;
@@ -1671,7 +1682,7 @@ __global__ void __launch_bounds__(256) dw_band_kernel(Problem p) {
 #pragma unroll
       for (int kx = 0; kx < KW; ++kx)
         acc = term<MODE>(acc, w[ky * KW + kx], t[ky * p.dH * p.iw + kx * p.dW]);
-    yp[o] = finish(p, acc, oc, yp + o);
+    yp[o] = finish<EPI>(p, acc, oc, yp + o);
     oyl += qr;
     ox += qc;
     if (ox >= p.OW) {
@@ -1699,7 +1710,7 @@ __global__ void __launch_bounds__(256) dw_band_kernel(Problem p) {
 // weights and are not stored.
 // Launch: tiles_m = waves per (image, group), tiles_n = N*G, 4 waves per block.
 // ---------------------------------------------------------------------------
-template <int MODE, int KH, int KW, int R>
+template <int MODE, int KH, int KW, int R, bool EPI>
 __global__ void __launch_bounds__(256) grouped_kernel(Problem p) {
   constexpr int T = KH * KW, CB = 8, NT = CB * T, NQ = (NT + 15) / 16;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1766,7 +1777,7 @@ __global__ void __launch_bounds__(256) grouped_kernel(Problem p) {
       for (int j = 0; j < (R >= 2 ? 2 : 1); ++j) {
         const int row = i * (R >= 2 ? 2 : 1) + j;
         if (row < p.M)
-          yp[(int64_t)row * p.OHW] = finish(p, acc[i][j], (int64_t)g * p.M + row, yp + (int64_t)row * p.OHW);
+          yp[(int64_t)row * p.OHW] = finish<EPI>(p, acc[i][j], g * p.M + row, yp + (int64_t)row * p.OHW);
       }
   }
 }
@@ -1839,7 +1850,7 @@ __global__ void __launch_bounds__(64) rowdot_kernel(Problem p) {
   }
   if (ok) {
     float *d = p.C + tc.g * p.y_grp + (int64_t)(row0 + lane) * p.ldc;
-    *d = finish(p, acc[0], (int64_t)tc.g * p.M + row0 + lane, d);
+    *d = finish(p, acc[0], tc.g * p.M + row0 + lane, d);
   }
 }
 

@@ -150,3 +150,45 @@ def test_the_scan_finds_a_planted_hazard():
             "\tv_mov_b32_e32 v9, v1\n\ts_nop 1\n"
             "\tv_fmac_f32_dpp v2, v9, v3 row_newbcast:1 row_mask:0xf bank_mask:0xf\n")
     assert len(_hazards(text)) == 1
+
+
+def _waterfalls(text):
+    """Kernels with a buffer access inside a waterfall loop: the descriptor
+    was in vector registers, so the compiler loops over its distinct values
+    (s_and_saveexec, the access, s_xor exec, s_cbranch_execnz)."""
+    kernel, insts, found = None, [], set()
+    for line in text.splitlines():
+        m = re.match(r"^[0-9a-f]+ <(\S+)>:", line)
+        if m:
+            kernel, insts = m.group(1), []
+            continue
+        s = line.split("//")[0].strip()
+        if not s or s.endswith(":") or s.startswith((".", ";")):
+            continue
+        insts.append(s)
+        if s.startswith("s_cbranch_execnz") and len(insts) >= 4:
+            w = insts[-4:-1]
+            if (w[-1].startswith("s_xor_b64 exec, exec") and
+                    any(x.startswith("buffer_") for x in w[:-1]) and
+                    any(x.startswith("s_and_saveexec") for x in insts[-6:-2])):
+                found.add(kernel)
+    return sorted(found)
+
+
+def test_no_buffer_access_in_a_waterfall_loop():
+    """Every staging load's descriptor is wave-uniform and held in scalar
+    registers.  A descriptor the compiler believes divergent is read through
+    a waterfall loop, which slowed the 4096^3 product's main loop by 8 %
+    (a 64-bit channel index in the store epilogue once caused it)."""
+    text = _disassemble()
+    bad = _waterfalls(text)
+    assert not bad, f"{len(bad)} kernels with waterfall buffer accesses, e.g. {bad[:3]}"
+
+
+def test_the_scan_finds_a_planted_waterfall():
+    text = ("0000000000001000 <k>:\n"
+            "\tv_readfirstlane_b32 s8, v2\n\tv_cmp_eq_u64_e64 s[2:3], s[8:9], v[2:3]\n"
+            "\ts_and_saveexec_b64 s[2:3], s[2:3]\n"
+            "\tbuffer_load_dwordx4 v[130:133], v7, s[8:11], 0 offen\n"
+            "\ts_xor_b64 exec, exec, s[2:3]\n\ts_cbranch_execnz 65521\n")
+    assert _waterfalls(text) == ["k"]
