@@ -955,11 +955,19 @@ __global__ void __launch_bounds__(64 * W) lane_conv_kernel(Problem p) {
       });
   if (pix < p.OHW) {
     float *base = out_ptr<kBGather>(p, tc.g, 0, img * p.OHW + pix);
+    // one uniform test picks the store loop with or without the epilogue
+    auto store_all = [&](auto epi) __attribute__((always_inline)) {
+      constexpr bool E = decltype(epi)::value;
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (row0 + r < p.M)
-        base[(int64_t)(row0 + r) * p.OHW] =
-            finish(p, acc[r], tc.g * p.M + row0 + r, base + (int64_t)(row0 + r) * p.OHW);
+      for (int r = 0; r < R; ++r)
+        if (row0 + r < p.M)
+          base[(int64_t)(row0 + r) * p.OHW] =
+              finish<E>(p, acc[r], tc.g * p.M + row0 + r, base + (int64_t)(row0 + r) * p.OHW);
+    };
+    if (p.bias == nullptr && p.res == nullptr && p.act == 0)
+      store_all(std::false_type{});
+    else
+      store_all(std::true_type{});
   }
 }
 
@@ -1498,31 +1506,39 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, chain_rows(
       });
     }
   }
-  if constexpr (MF) {
+  // One uniform test picks the store loop with or without the epilogue.
+  auto store_all = [&](auto epi) __attribute__((always_inline)) {
+    constexpr bool E = decltype(epi)::value;
+    if constexpr (MF) {
+      if (col_ok) {
+        float *base = out_ptr<CONV ? kBGather : kBMatrix>(p, tc.g, 0, CONV ? img * p.OHW + cidx : cidx);
+        const int64_t rstride = CONV ? (int64_t)p.OHW : p.ldc;
+#pragma unroll
+        for (int c = 0; c < R; ++c)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = row0 + rb0 + 4 * c + i;
+            if (row < p.M)
+              base[(int64_t)row * rstride] = finish<E>(p, acc4[c][i], tc.g * p.M + row, base + (int64_t)row * rstride);
+          }
+      }
+      return;
+    }
     if (col_ok) {
       float *base = out_ptr<CONV ? kBGather : kBMatrix>(p, tc.g, 0, CONV ? img * p.OHW + cidx : cidx);
       const int64_t rstride = CONV ? (int64_t)p.OHW : p.ldc;
 #pragma unroll
-      for (int c = 0; c < R; ++c)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = row0 + rb0 + 4 * c + i;
-          if (row < p.M)
-            base[(int64_t)row * rstride] = finish(p, acc4[c][i], tc.g * p.M + row, base + (int64_t)row * rstride);
-        }
+      for (int r = 0; r < R; ++r) {
+        const int row = row0 + rb0 + r;
+        if (row < p.M)
+          base[(int64_t)row * rstride] = finish<E>(p, acc[r], tc.g * p.M + row, base + (int64_t)row * rstride);
+      }
     }
-    return;
-  }
-  if (col_ok) {
-    float *base = out_ptr<CONV ? kBGather : kBMatrix>(p, tc.g, 0, CONV ? img * p.OHW + cidx : cidx);
-    const int64_t rstride = CONV ? (int64_t)p.OHW : p.ldc;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int row = row0 + rb0 + r;
-      if (row < p.M)
-        base[(int64_t)row * rstride] = finish(p, acc[r], tc.g * p.M + row, base + (int64_t)row * rstride);
-    }
-  }
+  };
+  if (p.bias == nullptr && p.res == nullptr && p.act == 0)
+    store_all(std::false_type{});
+  else
+    store_all(std::true_type{});
 }
 
 // ---------------------------------------------------------------------------
