@@ -153,6 +153,23 @@ __device__ __forceinline__ float finish(const Problem &p, float acc, int ch, con
   return canonical(v);
 }
 
+// The epilogue on preloaded operands: b = bias[ch], r = the residual at the
+// output's position, both read before any of the block's stores (a load
+// after a store to a possibly equal address would wait for each in turn).
+__device__ __forceinline__ float finish_with(const Problem &p, float acc, float b, float r) {
+  float v = acc;
+  if (p.bias != nullptr) v = v + b;
+  if (p.act == 1) v = v > 0.0f ? v : (v != v ? v : 0.0f);
+  if (p.res != nullptr) v = v + r;
+  return canonical(v);
+}
+__device__ __forceinline__ float epi_bias(const Problem &p, bool ok, int ch) {
+  return p.bias != nullptr && ok ? p.bias[ch] : 0.0f;
+}
+__device__ __forceinline__ float epi_res(const Problem &p, bool ok, const float *dst) {
+  return p.res != nullptr && ok ? p.res[dst - p.C] : 0.0f;
+}
+
 // ---------------------------------------------------------------------------
 // Loads.  Every staged operand is read with raw buffer loads: a 32-bit byte
 // offset from a base held in scalar registers.  A load whose element lies
@@ -616,15 +633,31 @@ __global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
+        {
+          float pb[16], pr[16];
+          if constexpr (E) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int col = n0 + wn * TN * 64 + j * 64 + 16 * (r >> 2) + (lane & 15);
+              const int row = m0 + wm * TM * 16 + i * 16 + 4 * (lane >> 4) + (r & 3);
+              const bool ok = col < p.N && row < p.M;
+              pb[r] = epi_bias(p, ok, tc.g * p.M + row);
+              pr[r] = epi_res(p, ok, ok ? out_ptr<KIND>(p, tc.g, row, col) : p.C);
+            }
+          }
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int col = n0 + wn * TN * 64 + j * 64 + 16 * (r >> 2) + (lane & 15);
             const int row = m0 + wm * TM * 16 + i * 16 + 4 * (lane >> 4) + (r & 3);
             if (col < p.N && row < p.M) {
               float *d = out_ptr<KIND>(p, tc.g, row, col);
-              *d = finish<E>(p, acc[i][j][r], tc.g * p.M + row, d);
+              if constexpr (E)
+                *d = finish_with(p, acc[i][j][r], pb[r], pr[r]);
+              else
+                *d = finish<false>(p, acc[i][j][r], 0, d);
             }
           }
+        }
       return;
     }
     // Epilogue: accumulator register r of lane l in block pair half h = r/16
@@ -640,11 +673,24 @@ __global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
           if (col >= p.N) continue;
           float *base = out_ptr<KIND>(p, tc.g, 0, col);
           const int64_t rstride = KIND == kBMatrix || KIND == kBMatrixT ? p.ldc : (int64_t)p.OHW;
+          float pb[16], pr[16];
+          if constexpr (E) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int row = m0 + wm * TM * 32 + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r & 3);
+              pb[r] = epi_bias(p, row < p.M, tc.g * p.M + row);
+              pr[r] = epi_res(p, row < p.M, base + (row < p.M ? row : 0) * rstride);
+            }
+          }
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int row = m0 + wm * TM * 32 + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r & 3);
-            if (row < p.M)
-              base[row * rstride] = finish<E>(p, acc[i][j][h * 16 + r], tc.g * p.M + row, base + row * rstride);
+            if (row < p.M) {
+              if constexpr (E)
+                base[row * rstride] = finish_with(p, acc[i][j][h * 16 + r], pb[r], pr[r]);
+              else
+                base[row * rstride] = finish<false>(p, acc[i][j][h * 16 + r], 0, base);
+            }
           }
         }
   };
@@ -958,11 +1004,23 @@ __global__ void __launch_bounds__(64 * W) lane_conv_kernel(Problem p) {
     // one uniform test picks the store loop with or without the epilogue
     auto store_all = [&](auto epi) __attribute__((always_inline)) {
       constexpr bool E = decltype(epi)::value;
+      float pb[R], pr[R];
+      if constexpr (E) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const bool ok = row0 + r < p.M;
+          pb[r] = epi_bias(p, ok, tc.g * p.M + row0 + r);
+          pr[r] = epi_res(p, ok, base + (int64_t)(ok ? row0 + r : 0) * p.OHW);
+        }
+      }
 #pragma unroll
       for (int r = 0; r < R; ++r)
-        if (row0 + r < p.M)
-          base[(int64_t)(row0 + r) * p.OHW] =
-              finish<E>(p, acc[r], tc.g * p.M + row0 + r, base + (int64_t)(row0 + r) * p.OHW);
+        if (row0 + r < p.M) {
+          if constexpr (E)
+            base[(int64_t)(row0 + r) * p.OHW] = finish_with(p, acc[r], pb[r], pr[r]);
+          else
+            base[(int64_t)(row0 + r) * p.OHW] = finish<false>(p, acc[r], 0, base);
+        }
     };
     if (p.bias == nullptr && p.res == nullptr && p.act == 0)
       store_all(std::false_type{});
@@ -1513,13 +1571,28 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, chain_rows(
       if (col_ok) {
         float *base = out_ptr<CONV ? kBGather : kBMatrix>(p, tc.g, 0, CONV ? img * p.OHW + cidx : cidx);
         const int64_t rstride = CONV ? (int64_t)p.OHW : p.ldc;
+        float pb[R][4], pr[R][4];
+        if constexpr (E) {
+#pragma unroll
+          for (int c = 0; c < R; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int row = row0 + rb0 + 4 * c + i;
+              pb[c][i] = epi_bias(p, row < p.M, tc.g * p.M + row);
+              pr[c][i] = epi_res(p, row < p.M, base + (int64_t)(row < p.M ? row : 0) * rstride);
+            }
+        }
 #pragma unroll
         for (int c = 0; c < R; ++c)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int row = row0 + rb0 + 4 * c + i;
-            if (row < p.M)
-              base[(int64_t)row * rstride] = finish<E>(p, acc4[c][i], tc.g * p.M + row, base + (int64_t)row * rstride);
+            if (row < p.M) {
+              if constexpr (E)
+                base[(int64_t)row * rstride] = finish_with(p, acc4[c][i], pb[c][i], pr[c][i]);
+              else
+                base[(int64_t)row * rstride] = finish<false>(p, acc4[c][i], 0, base);
+            }
           }
       }
       return;
@@ -1527,11 +1600,24 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, chain_rows(
     if (col_ok) {
       float *base = out_ptr<CONV ? kBGather : kBMatrix>(p, tc.g, 0, CONV ? img * p.OHW + cidx : cidx);
       const int64_t rstride = CONV ? (int64_t)p.OHW : p.ldc;
+      float pb[R], pr[R];
+      if constexpr (E) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int row = row0 + rb0 + r;
+          pb[r] = epi_bias(p, row < p.M, tc.g * p.M + row);
+          pr[r] = epi_res(p, row < p.M, base + (int64_t)(row < p.M ? row : 0) * rstride);
+        }
+      }
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int row = row0 + rb0 + r;
-        if (row < p.M)
-          base[(int64_t)row * rstride] = finish<E>(p, acc[r], tc.g * p.M + row, base + (int64_t)row * rstride);
+        if (row < p.M) {
+          if constexpr (E)
+            base[(int64_t)row * rstride] = finish_with(p, acc[r], pb[r], pr[r]);
+          else
+            base[(int64_t)row * rstride] = finish<false>(p, acc[r], 0, base);
+        }
       }
     }
   };
