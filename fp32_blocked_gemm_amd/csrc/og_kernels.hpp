@@ -887,10 +887,32 @@ __global__ void __launch_bounds__(64 * W)
   if (col < p.N) {
     float *base = out_ptr<KIND>(p, tc.g, 0, col);
     const int64_t rstride = KIND == kBMatrix ? p.ldc : (int64_t)p.OHW;
+    // one uniform test picks the store loop with or without the epilogue;
+    // with it, the rows' biases and residuals are loaded before the stores
+    auto store_all = [&](auto epi) __attribute__((always_inline)) {
+      constexpr bool E = decltype(epi)::value;
+      float pb[R], pr[R];
+      if constexpr (E) {
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (row0 + r < p.M)
-        base[(row0 + r) * rstride] = finish(p, acc[r], tc.g * p.M + row0 + r, base + (row0 + r) * rstride);
+        for (int r = 0; r < R; ++r) {
+          const bool ok = row0 + r < p.M;
+          pb[r] = epi_bias(p, ok, tc.g * p.M + row0 + r);
+          pr[r] = epi_res(p, ok, base + (ok ? row0 + r : 0) * rstride);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (row0 + r < p.M) {
+          if constexpr (E)
+            base[(row0 + r) * rstride] = finish_with(p, acc[r], pb[r], pr[r]);
+          else
+            base[(row0 + r) * rstride] = finish<false>(p, acc[r], 0, base);
+        }
+    };
+    if (p.bias == nullptr && p.res == nullptr && p.act == 0)
+      store_all(std::false_type{});
+    else
+      store_all(std::true_type{});
   }
 }
 
