@@ -16,8 +16,11 @@
 
 #include "og.h"
 #include "og_kernels.hpp"
+#include "og_launch.hpp"
 
 namespace {
+
+using namespace og::host;
 
 thread_local hipStream_t t_stream = nullptr;
 thread_local int t_variant = 0;
@@ -69,47 +72,6 @@ og_status check_launch(const char *what) {
   return ok();
 }
 
-constexpr int64_t kI32Max = 2147483647;
-
-int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
-// Kernel variants (og_set_variant): 1 VALU 64x64 tile; 2..5 matrix core with
-// (bm, bn) output tiles; 6..9 the lane kernel with R = 1, 2, 4, 8 rows per
-// wave and 4 waves (so bm = 4R, bn = 64).
-struct Tile {
-  int variant, bm, bn;
-  int per_wave;  // matrix core: 32x64 blocks per wave; lane kernel: rows per wave
-};
-// 10..13 the chain kernel: (bn columns, compute waves, rows per lane) =
-// (64, 4, 1), (64, 2, 1), (16, 1, 1) and (64, 2, 2); its 3x3 convolution
-// form of variant 12 has 32 columns.
-// 14..16 the chain kernel with matrix-core chains of 4 rows x 64 columns:
-// (compute waves, chains per wave) = (4, 1), (2, 2), (2, 1).
-// 17 the matrix-core kernel with 256x256 tiles and eight waves.
-// 20 the matrix-core kernel with 64x64 tiles of four waves of 16 x 64 outputs
-// (v_mfma_f32_16x16x1_4b_f32), both modes.
-constexpr Tile kTiles[] = {{1, 64, 64, 0},  {2, 128, 256, 4}, {3, 128, 128, 2}, {4, 64, 128, 1},
-                           {5, 32, 256, 1}, {6, 4, 64, 1},    {7, 8, 64, 2},    {8, 16, 64, 4},
-                           {9, 32, 64, 8},  {10, 4, 64, 1},   {11, 2, 64, 1},   {12, 4, 16, 1},
-                           {13, 4, 64, 2},  {14, 16, 64, 1},  {15, 16, 64, 2},  {16, 8, 64, 1},
-                           {17, 256, 256, 4}, {20, 64, 64, 1}};
-constexpr int kNumVariants = 20;
-// 18 the depthwise kernel (Cin/G = 1, any multiplier): the automatic choice
-// for those shapes; forced on any other shape it runs the automatic choice.
-constexpr int kDepthwiseVariant = 18;
-// 19 the grouped direct kernel (grouped 3x3 convolutions with 2 <= Cin/G <= 64
-// and Cout/G <= 8): the automatic choice for those shapes; forced on any
-// other shape it runs the automatic choice.
-constexpr int kGroupedVariant = 19;
-
-const Tile &tile_for_variant(int v) {
-  for (const Tile &t : kTiles)
-    if (t.variant == v) return t;
-  return kTiles[1];
-}
-
-bool is_lane(const Tile &t) { return t.variant >= 6 && t.variant <= 9; }
-bool is_chain(const Tile &t) { return t.variant >= 10 && t.variant <= 16; }
 
 // The shape the kernel choice sees: a group's product (M x N x K) and, for
 // a convolution, the pixels of one output image and the window size (the
@@ -245,161 +207,15 @@ const Tile &choose_tile(const Shape &s, int mode) {
   return tile_for_variant(best);
 }
 
-// Lane variants of a 3x3 or a 1x1 (strided or padded) convolution run the
-// lane kernel specialised for that kernel size; its column tiles are 64
-// output pixels of one image.
-template <int MODE, int KH, int KW>
-void launch_lane_conv(int variant, og::Problem p, hipStream_t s) {
-  const int tpi = (int)ceil_div(p.OHW, 64);
-  const int rpb = 4 * (variant == 6 ? 1 : variant == 7 ? 2 : variant == 8 ? 4 : 8);
-  p.tiles_m = (int)ceil_div(p.M, rpb);
-  p.tiles_n = (p.N / p.OHW) * tpi;
-  const unsigned blocks = (unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)p.groups;
-  const dim3 grid(blocks), block(256);
-  switch (variant) {
-    case 6: hipLaunchKernelGGL((og::lane_conv_kernel<MODE, KH, KW, 1, 4, 2>), grid, block, 0, s, p); break;
-    case 7: hipLaunchKernelGGL((og::lane_conv_kernel<MODE, KH, KW, 2, 4, 2>), grid, block, 0, s, p); break;
-    case 8: hipLaunchKernelGGL((og::lane_conv_kernel<MODE, KH, KW, 4, 4, 2>), grid, block, 0, s, p); break;
-    default: hipLaunchKernelGGL((og::lane_conv_kernel<MODE, KH, KW, 8, 4, 2>), grid, block, 0, s, p); break;
-  }
-}
-
-// The chain kernel of variant v for a matrix product (CONV false; VEC: B
-// rows 16-byte aligned, read 16 bytes per load) or a KH x KW convolution; its
-// column tiles of a convolution are BN pixels of one image.
-template <int MODE, bool CONV, int LD, int KH, int KW>
-void launch_chain(int v, og::Problem p, hipStream_t s) {
-  // Exact mode of the matrix-core chains (14..16) runs the DPP chains of
-  // the same block shape (10, 13, 11): its products made on the matrix
-  // cores would still need a VALU add each, and the compiler cannot keep
-  // their independent products from piling up in registers.
-  if (MODE == og::kExact && v >= 14) v = v == 14 ? 10 : v == 15 ? 13 : 11;
-  const bool mf = v >= 14;
-  const int bn = v == 12 ? (KH * KW == 1 ? 16 : 32) : 64;
-  const int cw = v == 10 || v == 14 ? 4 : v == 12 ? 1 : 2;  // compute waves
-  const int rows = mf ? cw * 4 * (v == 15 ? 2 : 1) : cw * (64 / bn) * (v == 13 ? 2 : 1);
-  const int pw = 4 * bn / 64;  // B producer waves (and one weight wave)
-  p.tiles_m = (int)ceil_div(p.M, rows);
-  p.tiles_n = CONV ? (int)((p.N / p.OHW) * ceil_div(p.OHW, bn)) : (int)ceil_div(p.N, bn);
-  const unsigned blocks = (unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)p.groups;
-  const dim3 grid(blocks), block(64 * (cw + pw + 1));
-  switch (v) {
-    case 10: hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, LD, KH, KW, 64, 4, 1, false>), grid, block, 0, s, p); break;
-    case 11: hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, LD, KH, KW, 64, 2, 1, false>), grid, block, 0, s, p); break;
-    case 12:
-      if constexpr (KH * KW == 1)
-        hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, LD, KH, KW, 16, 1, 1, false>), grid, block, 0, s, p);
-      else
-        hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, LD, KH, KW, 32, 1, 1, false>), grid, block, 0, s, p);
-      break;
-    case 13: hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, LD, KH, KW, 64, 2, 2, false>), grid, block, 0, s, p); break;
-    default:
-      if constexpr (MODE == og::kFast) {
-        if (v == 14)
-          hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, LD, KH, KW, 64, 4, 1, true>), grid, block, 0, s, p);
-        else if (v == 15)
-          hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, LD, KH, KW, 64, 2, 2, true>), grid, block, 0, s, p);
-        else
-          hipLaunchKernelGGL((og::chain_kernel<MODE, CONV, LD, KH, KW, 64, 2, 1, true>), grid, block, 0, s, p);
-      }
-      break;
-  }
-}
-
-// D: register-ring depth of the staged loads (chunks in flight).
-template <int MODE, int KIND, bool AV, bool BV>
-void launch_tile(const Tile &t, og::Problem p, hipStream_t s) {
-  if (is_chain(t)) {
-    if (KIND == og::kBMatrix) {
-      if (BV) return launch_chain<MODE, false, og::kLdVec, 1, 1>(t.variant, p, s);
-      return launch_chain<MODE, false, og::kLdTap, 1, 1>(t.variant, p, s);
-    }
-    if (p.KH == 3 && p.KW == 3) {
-      // a kernel row's three taps in one load: horizontal dilation 1, the
-      // row at least 3 wide, left and right pads at most 1
-      if (p.dW == 1 && p.W >= 3 && p.pL <= 1 && p.pR <= 1)
-        return launch_chain<MODE, true, og::kLdRow3, 3, 3>(t.variant, p, s);
-      return launch_chain<MODE, true, og::kLdTap, 3, 3>(t.variant, p, s);
-    }
-    if (p.KH == 1 && p.KW == 1) return launch_chain<MODE, true, og::kLdTap, 1, 1>(t.variant, p, s);
-    // other window sizes: the lane kernel with one row per wave
-    return launch_tile<MODE, KIND, AV, BV>(tile_for_variant(6), p, s);
-  }
-  if (KIND == og::kBGather && is_lane(t)) {
-    if (p.KH == 3 && p.KW == 3) return launch_lane_conv<MODE, 3, 3>(t.variant, p, s);
-    if (p.KH == 1 && p.KW == 1) return launch_lane_conv<MODE, 1, 1>(t.variant, p, s);
-  }
-  // Exact mode keeps two k steps of products beside the accumulators: with
-  // two 32x64 blocks per wave (128x256, 128x128 and 256x256 tiles) that no
-  // longer fits the registers of two waves per SIMD, so variants 2, 3 and 17
-  // run 64x128 tiles.  With gathered B it keeps one product and runs 128x128
-  // tiles.
-  const bool big = t.variant == 2 || t.variant == 3 || t.variant == 17;
-  const Tile &tt = (MODE == og::kExact && big) ? tile_for_variant(KIND == og::kBGather ? 3 : 4) : t;
-  p.tiles_m = (int)ceil_div(p.M, tt.bm);
-  p.tiles_n = (int)ceil_div(p.N, tt.bn);
-  const unsigned blocks = (unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)p.groups;
-  const dim3 grid(blocks), block(256);
-  if constexpr (MODE == og::kExact) {
-    if (big) {
-      if constexpr (KIND == og::kBGather)
-        hipLaunchKernelGGL((og::mfma_kernel<MODE, 128, 128, 2, 2, KIND, AV, BV, 2>), grid, block, 0, s, p);
-      else
-        hipLaunchKernelGGL((og::mfma_kernel<MODE, 64, 128, 2, 2, KIND, AV, BV, 4>), grid, block, 0, s, p);
-      return;
-    }
-  }
-  switch (t.variant) {
-    case 1: hipLaunchKernelGGL((og::valu_kernel<MODE, KIND>), grid, block, 0, s, p); break;
-    case 2:
-      if constexpr (MODE == og::kFast)
-        hipLaunchKernelGGL((og::mfma_kernel<MODE, 128, 256, 2, 2, KIND, AV, BV, 2>), grid, block, 0, s, p);
-      break;
-    case 3:
-      if constexpr (MODE == og::kFast)
-        hipLaunchKernelGGL((og::mfma_kernel<MODE, 128, 128, 2, 2, KIND, AV, BV, 2>), grid, block, 0, s, p);
-      break;
-    case 4: hipLaunchKernelGGL((og::mfma_kernel<MODE, 64, 128, 2, 2, KIND, AV, BV, 4>), grid, block, 0, s, p); break;
-    case 5: hipLaunchKernelGGL((og::mfma_kernel<MODE, 32, 256, 1, 4, KIND, AV, BV, 2>), grid, block, 0, s, p); break;
-    case 17:  // eight waves: the B tile (and its gather) serves 256 rows
-      if constexpr (MODE == og::kFast)
-        hipLaunchKernelGGL((og::mfma_kernel<MODE, 256, 256, 4, 2, KIND, AV, BV, 2>), grid, dim3(512), 0, s, p);
-      break;
-    case 20:  // four waves of 16 x 64 outputs
-        hipLaunchKernelGGL((og::mfma_kernel<MODE, 64, 64, 4, 1, KIND, AV, BV, 2, 16>), grid, block, 0, s, p);
-      break;
-    // (rings of two chunks: deeper rings cost more in occupancy than they
-    // gain in hidden latency, measured on the ResNet-50 layers and products)
-    case 6: hipLaunchKernelGGL((og::lane_kernel<MODE, KIND, 1, 4, 2>), grid, block, 0, s, p); break;
-    case 7: hipLaunchKernelGGL((og::lane_kernel<MODE, KIND, 2, 4, 2>), grid, block, 0, s, p); break;
-    case 8: hipLaunchKernelGGL((og::lane_kernel<MODE, KIND, 4, 4, 2>), grid, block, 0, s, p); break;
-    default: hipLaunchKernelGGL((og::lane_kernel<MODE, KIND, 8, 4, 2>), grid, block, 0, s, p); break;
-  }
-}
-
-// AV / BV: 16-byte loads of A rows / B rows (every address and every
-// row length a multiple of 16 bytes, so no load crosses the end of a row).
-template <int MODE, int KIND>
-void launch_vec(bool av, bool bv, const Tile &t, const og::Problem &p, hipStream_t s) {
-  if (av && bv)
-    launch_tile<MODE, KIND, true, true>(t, p, s);
-  else if (av)
-    launch_tile<MODE, KIND, true, false>(t, p, s);
-  else if (bv)
-    launch_tile<MODE, KIND, false, true>(t, p, s);
-  else
-    launch_tile<MODE, KIND, false, false>(t, p, s);
-}
 
 template <int KIND>
 void launch(int mode, bool av, bool bv, const Tile &t, const og::Problem &p, hipStream_t s) {
   if (mode == OG_MODE_EXACT)
-    launch_vec<og::kExact, KIND>(av, bv, t, p, s);
+    launch_kind<og::kExact, KIND>(av, bv, t, p, s);
   else
-    launch_vec<og::kFast, KIND>(av, bv, t, p, s);
+    launch_kind<og::kFast, KIND>(av, bv, t, p, s);
 }
 
-bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15) == 0; }
 
 const Tile &pick(const Shape &s, int mode) {
   return t_variant == 0 || t_variant == kDepthwiseVariant || t_variant == kGroupedVariant
@@ -422,112 +238,7 @@ int dw_outputs_per_lane(int64_t planes, int64_t ohw, int64_t kh, int64_t kw, int
   return 1;
 }
 
-template <int MODE, bool EPI, int KH, int KW>
-void launch_dw_window(og::Problem p, int per_lane, dim3 grid, hipStream_t s) {
-  if (per_lane == 4)
-    hipLaunchKernelGGL((og::dw_kernel<MODE, KH, KW, 4, EPI>), grid, dim3(256), 0, s, p);
-  else if (per_lane == 2)
-    hipLaunchKernelGGL((og::dw_kernel<MODE, KH, KW, 2, EPI>), grid, dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((og::dw_kernel<MODE, KH, KW, 1, EPI>), grid, dim3(256), 0, s, p);
-}
 
-// The band form of the depthwise kernel (input rows staged in LDS) for
-// strided or 5x5 windows on planes at least 28 pixels wide: bands of at
-// most 1024 outputs, enough bands for at least 1024 blocks, every band at
-// least 128 outputs, the staged rows within 32 KB.  Returns false (and
-// launches nothing) where the shape does not qualify.
-template <int MODE, bool EPI>
-bool launch_dw_band(og::Problem p, int64_t planes, int64_t OH, int64_t OW, hipStream_t s) {
-  const bool w3 = p.KH == 3 && p.KW == 3, w5 = p.KH == 5 && p.KW == 5;
-  if (!(w3 || w5) || (w3 && p.sH == 1 && p.sW == 1) || OW < 28) return false;
-  const int64_t iw = (OW - 1) * p.sW + (int64_t)(p.KW - 1) * p.dW + 1;
-  int64_t nb = std::max(ceil_div(OH * OW, 1024), ceil_div(1024, planes));
-  nb = std::min(nb, OH);
-  const int64_t bh = ceil_div(OH, nb);
-  nb = ceil_div(OH, bh);
-  const int64_t ih = (bh - 1) * p.sH + (int64_t)(p.KH - 1) * p.dH + 1;
-  if (planes * nb < 1024 || bh * OW < 128 || ih * iw > 8192 || planes * nb > kI32Max) return false;
-  p.bh = (int)bh;
-  p.ih = (int)ih;
-  p.iw = (int)iw;
-  p.tiles_m = (int)nb;
-  p.tiles_n = (int)planes;
-  const dim3 grid((unsigned)(planes * nb)), block(256);
-  const size_t lds = (size_t)(4 * ih * iw);
-  if (w3)
-    hipLaunchKernelGGL((og::dw_band_kernel<MODE, 3, 3, EPI>), grid, block, lds, s, p);
-  else
-    hipLaunchKernelGGL((og::dw_band_kernel<MODE, 5, 5, EPI>), grid, block, lds, s, p);
-  return true;
-}
-
-// The grouped direct kernel, R = Cout/G rounded up to 1, 2, 4 or 8 rows per lane.
-template <int MODE, bool EPI>
-void launch_grouped_mode(og::Problem p, hipStream_t s) {
-  const dim3 grid((unsigned)ceil_div((int64_t)p.tiles_m * p.tiles_n, 4)), block(256);
-  if (p.M <= 1)
-    hipLaunchKernelGGL((og::grouped_kernel<MODE, 3, 3, 1, EPI>), grid, block, 0, s, p);
-  else if (p.M <= 2)
-    hipLaunchKernelGGL((og::grouped_kernel<MODE, 3, 3, 2, EPI>), grid, block, 0, s, p);
-  else if (p.M <= 4)
-    hipLaunchKernelGGL((og::grouped_kernel<MODE, 3, 3, 4, EPI>), grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((og::grouped_kernel<MODE, 3, 3, 8, EPI>), grid, block, 0, s, p);
-}
-
-template <int MODE, bool EPI>
-void launch_dw(og::Problem p, int per_lane, hipStream_t s) {
-  const dim3 grid((unsigned)ceil_div((int64_t)p.tiles_m * p.tiles_n, 4));
-  if (p.KH == 3 && p.KW == 3)
-    launch_dw_window<MODE, EPI, 3, 3>(p, per_lane, grid, s);
-  else if (p.KH == 5 && p.KW == 5)  // one output per lane (dw_outputs_per_lane)
-    hipLaunchKernelGGL((og::dw_kernel<MODE, 5, 5, 1, EPI>), grid, dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((og::dw_kernel<MODE, 0, 0, 1, EPI>), grid, dim3(256), 0, s, p);
-}
-
-// The depthwise and grouped direct kernels are compiled with and without the
-// epilogue (EPI): (mode, epilogue) -> one of four instantiations.
-template <template <int, bool> class L, class... A>
-auto by_mode_epi(int mode, bool epi, A &&...a) {
-  if (mode == OG_MODE_EXACT)
-    return epi ? L<og::kExact, true>::run(a...) : L<og::kExact, false>::run(a...);
-  return epi ? L<og::kFast, true>::run(a...) : L<og::kFast, false>::run(a...);
-}
-template <int MODE, bool EPI>
-struct DwBand {
-  static bool run(og::Problem p, int64_t planes, int64_t OH, int64_t OW, hipStream_t s) {
-    return launch_dw_band<MODE, EPI>(p, planes, OH, OW, s);
-  }
-};
-template <int MODE, bool EPI>
-struct Dw {
-  static int run(og::Problem p, int per_lane, hipStream_t s) {
-    launch_dw<MODE, EPI>(p, per_lane, s);
-    return 0;
-  }
-};
-template <int MODE, bool EPI>
-struct Grouped {
-  static int run(og::Problem p, hipStream_t s) {
-    launch_grouped_mode<MODE, EPI>(p, s);
-    return 0;
-  }
-};
-
-// The row-dot kernel (single-column products): one wave of 64 rows per
-// block, a ring of 8 chunks of 16 taps; VEC: 16-byte loads of the rows.
-template <int MODE>
-void launch_rowdot_mode(og::Problem p, bool vec, hipStream_t s) {
-  p.tiles_m = (int)ceil_div(p.M, 64);
-  p.tiles_n = 1;
-  const dim3 grid((unsigned)p.tiles_m * (unsigned)p.groups), block(64);
-  if (vec)
-    hipLaunchKernelGGL((og::rowdot_kernel<MODE, true, 8>), grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((og::rowdot_kernel<MODE, false, 8>), grid, block, 0, s, p);
-}
 
 void launch_rowdot(int mode, og::Problem p, bool vec, hipStream_t s) {
   if (mode == OG_MODE_EXACT)
@@ -547,35 +258,6 @@ void launch_rowdot(int mode, og::Problem p, bool vec, hipStream_t s) {
 constexpr int64_t kRowdotMaxK = 512;
 constexpr int64_t kStreamMinK = 256;
 
-// One row against the rows of an N x K matrix (k-contiguous, 16-byte
-// aligned, k a multiple of 4) on the chain kernel in its single-row form
-// (variant 12's shape: blocks of 16 columns, one compute wave of 4 lane rows,
-// one producer wave, one weight wave): the N x K operand streamed once
-// through LDS, 16 bytes of one column per load and no transpose.
-// p: A = the row (M = 1), B = the N x K operand (ldb its row stride), C = the
-// n outputs (contiguous), N = n, K = k.
-template <int MODE, int BN, int CW, int R, bool MF>
-void launch_chain_vt_shape(og::Problem p, hipStream_t s) {
-  constexpr int ROWS = og::chain_rows(CW, BN, R, MF);
-  using CS = og::ChainShape<1, BN, ROWS>;
-  p.tiles_m = (int)ceil_div(p.M, ROWS);
-  p.tiles_n = (int)ceil_div(p.N, BN);
-  p.groups = 1;
-  const dim3 grid((unsigned)p.tiles_m * (unsigned)p.tiles_n), block(64 * (CW + CS::PW + 1));
-  hipLaunchKernelGGL((og::chain_kernel<MODE, false, og::kLdVecT, 1, 1, BN, CW, R, MF>), grid,
-                     block, 0, s, p);
-}
-
-// More than 16 rows in fast mode: the matrix-core chains of variant 14's
-// shape (16 rows x 64 columns per block, the N x K operand streamed once per
-// 16 rows instead of once per 4).
-template <int MODE>
-void launch_chain_vt_mode(og::Problem p, hipStream_t s) {
-  if constexpr (MODE == og::kFast) {
-    if (p.M > 16) return launch_chain_vt_shape<MODE, 64, 4, 1, true>(p, s);
-  }
-  launch_chain_vt_shape<MODE, 16, 1, 1, false>(p, s);
-}
 
 void launch_chain_vt(int mode, og::Problem p, hipStream_t s) {
   if (mode == OG_MODE_EXACT)
@@ -595,52 +277,6 @@ bool rowdot_fits(int64_t rows, int64_t ld, int64_t vstride, int64_t groups) {
          ceil_div(rows, 64) * groups <= kI32Max;
 }
 
-// The product with a transposed B (N x K) runs the tile kernels that stage B
-// like A: the VALU kernel (variant 1) and the matrix-core kernel (2..5, 17,
-// 20, with exact mode's 64x128 tiles for 2, 3 and 17).
-template <int MODE, bool AV, bool BV>
-void launch_nt_tile(const Tile &t, og::Problem p, hipStream_t s) {
-  constexpr int K = og::kBMatrixT;
-  const bool big = t.variant == 2 || t.variant == 3 || t.variant == 17;
-  const Tile &tt = (MODE == og::kExact && big) ? tile_for_variant(4) : t;
-  p.tiles_m = (int)ceil_div(p.M, tt.bm);
-  p.tiles_n = (int)ceil_div(p.N, tt.bn);
-  const dim3 grid((unsigned)p.tiles_m * (unsigned)p.tiles_n), block(256);
-  if (MODE == og::kExact && big) {
-    hipLaunchKernelGGL((og::mfma_kernel<MODE, 64, 128, 2, 2, K, AV, BV, 4>), grid, block, 0, s, p);
-    return;
-  }
-  switch (tt.variant) {
-    case 1: hipLaunchKernelGGL((og::valu_kernel<MODE, K>), grid, block, 0, s, p); break;
-    case 2:
-      if constexpr (MODE == og::kFast)
-        hipLaunchKernelGGL((og::mfma_kernel<MODE, 128, 256, 2, 2, K, AV, BV, 2>), grid, block, 0, s, p);
-      break;
-    case 3:
-      if constexpr (MODE == og::kFast)
-        hipLaunchKernelGGL((og::mfma_kernel<MODE, 128, 128, 2, 2, K, AV, BV, 2>), grid, block, 0, s, p);
-      break;
-    case 5: hipLaunchKernelGGL((og::mfma_kernel<MODE, 32, 256, 1, 4, K, AV, BV, 2>), grid, block, 0, s, p); break;
-    case 17:
-      if constexpr (MODE == og::kFast)
-        hipLaunchKernelGGL((og::mfma_kernel<MODE, 256, 256, 4, 2, K, AV, BV, 2>), grid, dim3(512), 0, s, p);
-      break;
-    case 20: hipLaunchKernelGGL((og::mfma_kernel<MODE, 64, 64, 4, 1, K, AV, BV, 2, 16>), grid, block, 0, s, p); break;
-    default: hipLaunchKernelGGL((og::mfma_kernel<MODE, 64, 128, 2, 2, K, AV, BV, 4>), grid, block, 0, s, p); break;
-  }
-}
-
-template <int MODE>
-void launch_nt(bool av, bool bv, const Tile &t, const og::Problem &p, hipStream_t s) {
-  if (av && bv)
-    launch_nt_tile<MODE, true, true>(t, p, s);
-  else if (av)
-    launch_nt_tile<MODE, true, false>(t, p, s);
-  else if (bv)
-    launch_nt_tile<MODE, false, true>(t, p, s);
-  else
-    launch_nt_tile<MODE, false, false>(t, p, s);
-}
 
 // Tile of a product with a transposed B: the forced variant when it has a
 // form for it (1..5, 17, 20), else the cheapest matrix-core tile by the
@@ -829,6 +465,8 @@ int64_t og_conv2d_out_size(int64_t size, int64_t k, int64_t stride, int64_t padB
 }  // extern "C"
 
 namespace {
+
+using namespace og::host;
 
 // The convolution, with the epilogue (bias, activation, residual) or without
 // (all null / 0).

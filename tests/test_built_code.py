@@ -1,5 +1,6 @@
 """Checks of the built gfx950 code object of libog.so (the library's own
-device code, extracted from the shared library):
+device code, extracted from the shared library, one code object per
+compiled unit):
 
 - the DPP read hazard: a register read through DPP (the source of a
   v_*_dpp instruction) is never written by a VALU instruction fewer than two
@@ -24,19 +25,37 @@ LIB = os.path.join(ROOT, "fp32_blocked_gemm_amd", "libog.so")
 LLVM = "/opt/rocm/llvm/bin"
 
 
-def _code_object(d):
+def _code_objects(d):
+    """The gfx950 code objects of libog.so: its .hip_fatbin section holds one
+    offload bundle per compiled unit, each unbundled on its own."""
     bundler = os.path.join(LLVM, "clang-offload-bundler")
-    fat, co = os.path.join(d, "fat.bin"), os.path.join(d, "dev.co")
+    fat = os.path.join(d, "fat.bin")
     # objcopy writes its output over its input when no output file is named:
     # work on a copy, so the library that this process has loaded is never
     # rewritten under it
     lib, scrap = os.path.join(d, "lib.so"), os.path.join(d, "scrap.so")
     shutil.copyfile(LIB, lib)
     subprocess.run(["objcopy", "--dump-section", f".hip_fatbin={fat}", lib, scrap], check=True)
-    subprocess.run([bundler, "--unbundle", "--type=o",
-                    "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--input={fat}",
-                    f"--output={co}"], check=True)
-    return co
+    with open(fat, "rb") as f:
+        blob = f.read()
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    starts = [m.start() for m in re.finditer(re.escape(magic), blob)]
+    assert starts and starts[0] == 0, "no offload bundle in .hip_fatbin"
+    cos = []
+    for i, (a, b) in enumerate(zip(starts, starts[1:] + [len(blob)])):
+        part, co = os.path.join(d, f"part{i}.bin"), os.path.join(d, f"dev{i}.co")
+        with open(part, "wb") as f:
+            f.write(blob[a:b])
+        subprocess.run([bundler, "--unbundle", "--type=o",
+                        "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--input={part}",
+                        f"--output={co}"], check=True)
+        cos.append(co)
+    return cos
+
+
+def _notes(d):
+    return "".join(subprocess.run([os.path.join(LLVM, "llvm-readelf"), "--notes", co], check=True,
+                                  capture_output=True, text=True).stdout for co in _code_objects(d))
 
 
 def _tools_or_skip():
@@ -50,9 +69,7 @@ def _tools_or_skip():
 def test_no_kernel_spills():
     _tools_or_skip()
     with tempfile.TemporaryDirectory() as d:
-        co = _code_object(d)
-        notes = subprocess.run([os.path.join(LLVM, "llvm-readelf"), "--notes", co], check=True,
-                               capture_output=True, text=True).stdout
+        notes = _notes(d)
     names = re.findall(r"^\s*\.name:\s+(\S+)", notes, flags=re.M)
     spills = [int(v) for v in re.findall(r"\.vgpr_spill_count:\s+(\d+)", notes)]
     sspills = [int(v) for v in re.findall(r"\.sgpr_spill_count:\s+(\d+)", notes)]
@@ -72,9 +89,7 @@ def test_every_host_kernel_has_device_code():
     exist, which the HIP runtime turns into an abort."""
     _tools_or_skip()
     with tempfile.TemporaryDirectory() as d:
-        co = _code_object(d)
-        notes = subprocess.run([os.path.join(LLVM, "llvm-readelf"), "--notes", co], check=True,
-                               capture_output=True, text=True).stdout
+        notes = _notes(d)
     device = set(re.findall(r"^\s*\.name:\s+(\S+)", notes, flags=re.M))
     with open(LIB, "rb") as f:
         blob = f.read()
@@ -89,9 +104,9 @@ def test_every_host_kernel_has_device_code():
 def _disassemble():
     _tools_or_skip()
     with tempfile.TemporaryDirectory() as d:
-        co = _code_object(d)
-        out = subprocess.run([os.path.join(LLVM, "llvm-objdump"), "-d", "--mcpu=gfx950", co],
-                             check=True, capture_output=True, text=True).stdout
+        out = "".join(subprocess.run([os.path.join(LLVM, "llvm-objdump"), "-d", "--mcpu=gfx950", co],
+                                     check=True, capture_output=True, text=True).stdout
+                      for co in _code_objects(d))
     return out
 
 
