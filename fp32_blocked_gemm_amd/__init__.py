@@ -150,12 +150,18 @@ def _use_stream_of(t):
 
 
 def _ld(t) -> int:
-    """Row stride of a 2-D float32 CUDA view with unit column stride."""
+    """Row stride of a 2-D float32 view whose columns are contiguous.
+
+    A view with more than one column must have stride(1) == 1, whatever its
+    number of rows (a single row of a column slice is not contiguous); a
+    single row's stride is never used, so it passes max(1, cols)."""
+    if t.dim() != 2:
+        raise ValueError("expected a 2-D tensor")
     rows, cols = t.shape
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError("columns must be contiguous (stride(1) == 1)")
     if rows <= 1 or cols == 0:
         return max(1, cols)
-    if t.stride(1) != 1 and cols > 1:
-        raise ValueError("columns must be contiguous (stride(1) == 1)")
     return t.stride(0)
 
 

@@ -507,6 +507,10 @@ og_status conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout, int
   // the kernels address the input with 32-bit byte offsets
   if (N * Cin * H * W > (int64_t(1) << 29))
     return fail(OG_ERR_TOO_LARGE, "og_conv2d_f32: the input exceeds 2^29 elements");
+  // and a tile's weight rows (K taps each, the row stride of the weights) too:
+  // the same bound the matrix product puts on lda
+  if (K > (int64_t(1) << 22))
+    return fail(OG_ERR_TOO_LARGE, "og_conv2d_f32: Cin/G*KH*KW = %lld exceeds 2^22", (long long)K);
   const bool planes = KH == 1 && KW == 1 && strideH == 1 && strideW == 1 && padTop == 0 &&
                       padLeft == 0 && padBottom == 0 && padRight == 0;
   const Tile &t = pick(Shape{cout_g, ncols, K, G, OH * OW, KH * KW}, mode);

@@ -48,7 +48,10 @@ typedef int og_status;
 #define OG_ERR_NOT_EXACT (-2)   /* exact mode asked of a kernel variant that has no exact form
                                    ("Exact mode": reported, never approximated)              */
 #define OG_ERR_DEVICE (-3)      /* HIP error, or the current device is not gfx950            */
-#define OG_ERR_TOO_LARGE (-4)   /* a dimension does not fit the kernels' 32-bit counters     */
+#define OG_ERR_TOO_LARGE (-4)   /* a dimension does not fit the kernels' 32-bit offsets and
+                                   counters: m, n or k above 2^31-1, lda or ldb above 2^22, a
+                                   convolution's Cin/G*KH*KW above 2^22 or input above 2^29
+                                   elements (each entry point states its bounds)           */
 
 #define OG_MODE_EXACT 0 /* separately rounded multiply and add ("Exact mode")              */
 #define OG_MODE_FAST 1  /* one fused multiply-add per term, same order ("Fast mode")        */
@@ -112,8 +115,10 @@ og_status og_gemm_nt_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_
  * convolution is H = 1, KH = 1 with padTop = padBottom = 0.
  * Requirements: N, Cin, H, W, Cout, G, KH, KW >= 1; strides and dilations
  * >= 1; pads >= 0; Cin and Cout multiples of G; OH, OW >= 1; pointers
- * non-null.  OG_ERR_TOO_LARGE when the input holds more than 2^29 elements
- * or a size does not fit 31 bits (the kernels form 32-bit offsets).
+ * non-null.  OG_ERR_TOO_LARGE when the input holds more than 2^29 elements,
+ * when K = Cin/G*KH*KW (the taps of one output, the row stride of the
+ * weights) exceeds 2^22, or when a size does not fit 31 bits (the kernels
+ * form 32-bit offsets).
  */
 og_status og_conv2d_f32_ex(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout,
                            int64_t G, int64_t KH, int64_t KW, int64_t strideH, int64_t strideW,

@@ -167,3 +167,42 @@ def test_no_device_is_reported_not_hidden(L):
     except ImportError:
         pass
     assert L.og_gemm_f32(2, 2, 2, P, 2, P, 2, P, 2, 0) == og.OG_ERR_DEVICE
+
+
+def test_conv_too_many_taps_is_too_large(L):
+    """K = Cin/G*KH*KW above 2^22 is refused before any launch: the kernels
+    address a tile's weight rows (row stride K) with 32-bit byte offsets."""
+    # 2^20 channels x 3x3 window: K = 9 * 2^20 > 2^22, the input only 9 * 2^20 elements
+    assert _conv(L, Cin=1 << 20, Cout=2, H=3, W=3) == og.OG_ERR_TOO_LARGE
+    assert b"2^22" in L.og_last_error()
+    # grouped: K per group = 9 * 2^19 > 2^22 too; with four groups 9 * 2^18 fits
+    assert _conv(L, Cin=1 << 20, Cout=4, G=2, H=3, W=3) == og.OG_ERR_TOO_LARGE
+    assert _conv(L, Cin=1 << 20, Cout=4, G=4, H=3, W=3) != og.OG_ERR_TOO_LARGE
+    # K = 2^22 exactly is accepted (with no GPU the call then stops at the device check)
+    try:
+        import torch
+        gpu = torch.cuda.is_available()
+    except ImportError:
+        gpu = False
+    if not gpu:
+        assert _conv(L, Cin=1 << 22, Cout=1, H=1, W=1, KH=1, KW=1) == og.OG_ERR_DEVICE
+
+
+def test_binding_row_stride_of_views():
+    """The binding's row stride: a view with several columns must have unit
+    column stride whatever its number of rows, including a single row taken
+    from a column slice (its columns are a row of the parent apart)."""
+    import torch
+    Y = torch.zeros(8, 6)
+    assert og._ld(Y) == 6
+    assert og._ld(Y[2:3]) == 6                      # one contiguous row
+    assert og._ld(Y[:, 1:4]) == 6                   # rows of a column slice
+    assert og._ld(Y[:, 2:3]) == 6                   # one column: stride(1) unused
+    assert og._ld(Y[:, 2].unsqueeze(1)) == 6
+    assert og._ld(torch.zeros(1, 0)) == 1
+    for bad in (Y[:, 2].unsqueeze(0),               # a column as a (1, 8) row: stride(1) = 6
+                Y.t(),                              # a transposed view
+                Y[:, ::2],                          # every other column
+                Y.t()[:1]):                         # a single row of a transposed view
+        with pytest.raises(ValueError):
+            og._ld(bad)

@@ -239,3 +239,36 @@ def test_stream_is_honoured(orc):
         got = C.cpu().numpy()
     assert og.lib().og_get_stream() == s.cuda_stream
     assert_same_bits(got, orc.gemm(A, B, 1), "gemm on a side stream")
+
+
+def test_single_row_views(orc):
+    """Single-row operands and outputs taken as views: a contiguous row of a
+    larger matrix is used in place; a row whose columns are not adjacent (a
+    column of a matrix viewed as a row) is refused before any launch, and the
+    caller's tensors are left as they were."""
+    t = torch()
+    rng = np.random.default_rng(11)
+    Y = rng.standard_normal((8, 6)).astype(np.float32)
+    Bm = rng.standard_normal((6, 5)).astype(np.float32)
+    dY = t.from_numpy(Y).cuda()
+    dB = t.from_numpy(Bm).cuda()
+    Z = t.full((4, 5), 7.0, device="cuda")
+    for mode in MODES:
+        say(f"gemm single-row views mode {mode}")
+        og.gemm(dY[2:3], dB, mode, out=Z[3:4])
+        got = to_host(Z)
+        assert_same_bits(got[3:4], orc.gemm(np.ascontiguousarray(Y[2:3]), Bm, mode),
+                         f"single row mode {mode}")
+        assert np.all(got[:3] == 7.0), "rows outside the output view were written"
+    before = to_host(Z).copy()
+    col_as_row = dY[:, 2].unsqueeze(0)                   # (1, 8), stride(1) = 6
+    with pytest.raises(ValueError):
+        og.gemm(col_as_row, t.ones((8, 5), device="cuda"), "fast", out=Z[:1])
+    with pytest.raises(ValueError):                      # B (1 x 4) with stride(1) = 5
+        og.gemm(t.ones((2, 1), device="cuda"), Z.t()[:1, :4], "fast",
+                out=t.empty((2, 4), device="cuda"))
+    with pytest.raises(ValueError):                      # out (1 x 4) with stride(1) = 5
+        og.gemm(t.ones((1, 3), device="cuda"), t.ones((3, 4), device="cuda"), "fast",
+                out=Z.t()[1:2, :])
+    t.cuda.synchronize()
+    assert np.array_equal(bits(to_host(Z)), bits(before)), "a refused call wrote its output"
