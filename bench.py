@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--extra-out", default=os.path.join("gpurun_out", "bench_extra.json"),
+                    help="file for the other workloads' numbers (relative to the repository)")
     return ap.parse_args()
 
 
@@ -591,16 +593,58 @@ def main():
                      "wall_s_timed_region": round(wall, 3)},
     }
     del A, B, C
+    extra = {}
     if args.only is None and not args.no_extra:
-        line["extra"] = extras(torch, og, synth, timer)
-        g = line["extra"]
-        g_exact = extras(torch, og, synth, timer, only="gemm4096_exact")["gemm_4096"]["exact"]
-        line["extra"]["gemm_4096_exact"] = g_exact
+        extra = extras(torch, og, synth, timer)
+        extra["gemm_4096_exact"] = extras(torch, og, synth, timer,
+                                          only="gemm4096_exact")["gemm_4096"]["exact"]
+        line["summary"] = summarize(extra)
     if args.only is None and not args.no_cpu:
         log("cpu baseline: oracle on a bounded sample")
         line["cpu_baseline"] = cpu_baseline(synth, args.cpu_seconds)
-        line.setdefault("extra", {})["cpu_oracle"] = cpu_oracle_table(synth)
+        extra["cpu_oracle"] = cpu_oracle_table(synth)
+    if extra:
+        # every workload's numbers: to a file and, as one line, to stderr; the
+        # last line of stdout stays the short record
+        out = os.path.join(ROOT, args.extra_out) if not os.path.isabs(args.extra_out) else args.extra_out
+        try:
+            os.makedirs(os.path.dirname(out), exist_ok=True)
+            with open(out, "w") as f:
+                json.dump(extra, f, indent=1)
+            line["extra_file"] = os.path.relpath(out, ROOT)
+        except OSError as e:
+            log(f"could not write {out}: {e}")
+        print("extra: " + json.dumps(extra), file=sys.stderr, flush=True)
     print(json.dumps(line), flush=True)
+
+
+def summarize(ex):
+    """A few figures of the other workloads for the short record (the full
+    set goes to the extra file)."""
+    def get(*keys):
+        d = ex
+        for k in keys:
+            if not isinstance(d, dict) or k not in d:
+                return None
+            d = d[k]
+        return d
+
+    out = {"gemm_4096_exact": {"ms": None if get("gemm_4096_exact", "us") is None
+                               else round(get("gemm_4096_exact", "us") / 1e3, 4),
+                               "tflops": None if get("gemm_4096_exact", "gflops") is None
+                               else round(get("gemm_4096_exact", "gflops") / 1e3, 2),
+                               "frac_exact_ceiling": get("gemm_4096_exact", "frac_exact_ceiling")}}
+    for b in (1, 8):
+        out[f"resnet50_chain_b{b}_ms"] = {m: get(f"resnet50_chain_b{b}", m, "ms")
+                                          for m in ("fast", "exact", "fast_mfma")
+                                          if get(f"resnet50_chain_b{b}", m, "ms") is not None}
+    for key, name in (("gemm_256", "gemm_256_us"), ("gemm_1000x777x1531_ld13", "ragged_us"),
+                      ("gemm_prefill_512x11008x4096", "prefill_us"),
+                      ("gemm_skinny_1x4096x4096", "skinny_us"),
+                      ("grouped_g32_d2_s2", "grouped_dilated_us"), ("conv1d_w4096_k5", "conv1d_us")):
+        out[name] = {m: get(key, m, "us") for m in ("fast", "exact", "fast_mfma")
+                     if get(key, m, "us") is not None}
+    return out
 
 
 if __name__ == "__main__":
