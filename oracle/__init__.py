@@ -51,7 +51,7 @@ def _ld(a: np.ndarray) -> int:
     """Row stride in elements of a 2-D float32 view with unit column stride."""
     assert a.dtype == np.float32 and a.ndim == 2
     rows, cols = a.shape
-    assert a.strides[1] == 4 or cols <= 1, "columns must be contiguous"
+    assert a.strides[1] == 4 or cols <= 1 or rows == 0, "columns must be contiguous"
     if rows <= 1 or cols == 0:
         return max(1, cols)  # the row stride is never used
     assert a.strides[0] % 4 == 0 and a.strides[0] // 4 >= cols

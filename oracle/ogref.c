@@ -30,7 +30,8 @@
  *  - The im2col route (OneModel "Matrix product and convolution kernels",
  *    section "Convolution"): per image and group a (Cin/G*KH*KW) x (OH*OW)
  *    matrix with rows ordered channel, kernel row, kernel column, multiplied
- *    by the group's weight rows with the matrix product above.
+ *    by the group's weight rows with the matrix product above (in its
+ *    loop-interchanged form, which keeps every output's order).
  */
 #include "ogref.h"
 
@@ -311,6 +312,7 @@ int ogref_conv2d_im2col_f32_ex(int64_t N, int64_t Cin, int64_t H, int64_t W, int
     for (int64_t n = 0; n < s.N; n++)
         for (int64_t g = 0; g < s.G; g++) {
             /* the im2col matrix of image n, group g: row (c, ky, kx), column (oy, ox) */
+#pragma omp parallel for collapse(3) schedule(static)
             for (int64_t c = 0; c < cin_g; c++)
                 for (int64_t ky = 0; ky < s.KH; ky++)
                     for (int64_t kx = 0; kx < s.KW; kx++) {
@@ -325,9 +327,11 @@ int ogref_conv2d_im2col_f32_ex(int64_t N, int64_t Cin, int64_t H, int64_t W, int
                                 col[row * npix + oy * s.OW + ox] = v;
                             }
                     }
-            /* the group's weights [cout_g, K] times the im2col matrix [K, npix] */
-            int rc = ogref_gemm_f32(cout_g, npix, K, w + g * cout_g * K, K, col, npix,
-                                    y + (n * s.Cout + g * cout_g) * npix, npix, mode);
+            /* the group's weights [cout_g, K] times the im2col matrix [K, npix]:
+             * the product's loop-interchanged form (each output still summed
+             * from +0 in increasing k) */
+            int rc = ogref_gemm_f32_rowwise(cout_g, npix, K, w + g * cout_g * K, K, col, npix,
+                                            y + (n * s.Cout + g * cout_g) * npix, npix, mode);
             if (rc != 0) {
                 free(col);
                 return rc;
