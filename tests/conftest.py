@@ -29,3 +29,27 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter):
+    """The parity hash lines (GPU, oracle and stored SHA-256 per full-size
+    workload and mode), shown whatever the verbosity, and kept in
+    gpurun_out/parity_sha256.txt."""
+    mod = sys.modules.get("gpu_util")
+    lines = getattr(mod, "HASH_LINES", None) if mod else None
+    if not lines:
+        return
+    out = ["parity sha256 (workload mode: gpu / oracle / stored)"]
+    for workload, mode, gpu, orc, stored in lines:
+        same = "equal" if gpu == orc == stored else "DIFFER"
+        out.append(f"{workload} {mode}: {gpu} / {orc} / {stored}  {same}")
+    terminalreporter.section("parity hashes")
+    for line in out:
+        terminalreporter.write_line(line)
+    try:
+        d = os.path.join(ROOT, "gpurun_out")
+        os.makedirs(d, exist_ok=True)
+        with open(os.path.join(d, "parity_sha256.txt"), "w") as f:
+            f.write("\n".join(out) + "\n")
+    except OSError:
+        pass

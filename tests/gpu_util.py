@@ -56,3 +56,13 @@ def assert_same_bits(got, want, what: str):
         i = int(bad[0])
         raise AssertionError(f"{what}: {bad.size} of {g.size} outputs differ; first at flat "
                              f"index {i}: got {g[i]:08x} want {w[i]:08x}")
+
+
+# Hash lines of the full-size parity tests: (workload, mode, GPU digest,
+# oracle digest, stored digest), printed at the end of the session.
+HASH_LINES: list[tuple[str, str, str, str, str]] = []
+
+
+def record_hashes(workload: str, mode: str, gpu: str, orc: str, stored: str):
+    HASH_LINES.append((workload, mode, gpu, orc, stored))
+    say(f"sha256 {workload} {mode}: gpu {gpu[:16]} oracle {orc[:16]} stored {stored[:16]}")

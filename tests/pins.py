@@ -367,6 +367,81 @@ def check_identity(orc):
         assert_bits_equal(orc.gemm(eye, B, mode), want.view(np.float32), f"identity mode {mode}")
 
 
+def check_single_outputs(orc):
+    """The one-output helpers (a product's (row, column) outputs, a
+    convolution's outputs at flat indices of y [N, Cout, OH, OW]) equal the
+    whole oracle's outputs at the same places: every output, in shuffled
+    order, of products with row strides and special values, and of
+    convolutions whose four output axes have different lengths (so a flat
+    index decoded with two axes swapped lands on another output)."""
+    rng = np.random.default_rng(21)
+
+    def values(size, special):
+        if special:  # mostly non-finite sums: the classes of the specials
+            return _mixed_values(rng, size).view(np.float32)
+        return rng.standard_normal(size).astype(np.float32)  # exact and fast differ
+
+    for (m, n, k, lda, ldb, special) in ((7, 11, 13, 16, 12, False), (7, 11, 13, 16, 12, True),
+                                         (1, 9, 40, 40, 9, False), (5, 1, 3, 7, 2, True)):
+        for mode in (EXACT, FAST):
+            A = values(m * lda, special).reshape(m, lda)[:, :k]
+            B = values(k * ldb, special).reshape(k, ldb)[:, :n]
+            full = orc.gemm(A, B, mode)
+            order = rng.permutation(m * n)
+            rows, cols = order // n, order % n
+            got = orc.gemm_at(A, B, rows, cols, mode)
+            assert_bits_equal(got, full[rows, cols], f"gemm_at {m}x{n}x{k} mode {mode}")
+    for (N, Cin, H, W, Cout, G, KH, KW, stride, pad, dil, special) in (
+            (2, 4, 9, 6, 6, 2, 3, 2, (2, 1), (1, 0, 2, 1), (1, 2), False),
+            (3, 3, 5, 11, 5, 1, 1, 3, (1, 3), (0, 1, 0, 2), (1, 1), False),
+            (2, 4, 9, 6, 6, 2, 3, 2, (2, 1), (1, 0, 2, 1), (1, 2), True)):
+        for mode in (EXACT, FAST):
+            x = values(N * Cin * H * W, special).reshape(N, Cin, H, W)
+            w = values(Cout * (Cin // G) * KH * KW, special).reshape(Cout, Cin // G, KH, KW)
+            full = orc.conv2d(x, w, mode, groups=G, stride=stride, pad=pad, dil=dil)
+            flat = rng.permutation(full.size)
+            got = orc.conv2d_at(x, w, flat, mode, groups=G, stride=stride, pad=pad, dil=dil)
+            assert_bits_equal(got, full.ravel()[flat], f"conv2d_at {full.shape} mode {mode}")
+
+
+def fused_unfused_family(rng, m: int = 300, n: int = 130):
+    """A and B whose output (i, j) is c_ij * 1 + a_ij * b_j with
+    c_ij = -round(a_ij * b_j) (every other term a product with zero; B's column
+    j is 1 at row 2j and b_j at row 2j+1).  Returns A, B and the fused result,
+    from first principles: rounded separately the two terms cancel to +0;
+    fused, the sum is the rounding error of a*b, exact in float64 (the
+    product of two binary32 values has at most 48 significant bits)."""
+    k = 2 * n
+    a = rng.uniform(1, 2, (m, n)) * np.where(rng.random((m, n)) < .5, 1.0, -1.0)
+    a = (a * 2.0 ** rng.integers(-20, 20, (m, n))).astype(np.float32)
+    b = rng.uniform(1, 2, n).astype(np.float32)
+    exact_prod = a.astype(np.float64) * b.astype(np.float64)
+    prod32 = exact_prod.astype(np.float32)  # round to nearest even
+    A = np.zeros((m, k), np.float32)
+    A[:, 0::2] = -prod32
+    A[:, 1::2] = a
+    B = np.zeros((k, n), np.float32)
+    B[2 * np.arange(n), np.arange(n)] = 1.0
+    B[2 * np.arange(n) + 1, np.arange(n)] = b
+    err = exact_prod - prod32.astype(np.float64)
+    fused = err.astype(np.float32)
+    assert np.all(fused.astype(np.float64) == err), "the error of a binary32 product is exact"
+    return A, B, fused
+
+
+def check_fused_unfused_family(orc):
+    """Exact mode gives +0 for every c + a*b with c = -round(a*b) placed
+    first; fast mode gives the rounding error of a*b ("Exact mode", rule 1:
+    no fused multiply-add; "Matrix product and convolution kernels", section
+    "Fast mode": one fused multiply-add per term)."""
+    A, B, fused = fused_unfused_family(np.random.default_rng(31), 40, 50)
+    assert np.count_nonzero(fused) > 0.9 * fused.size
+    for rowwise in (False, True):
+        assert_bits_equal(orc.gemm(A, B, EXACT, rowwise=rowwise), np.zeros_like(fused),
+                          f"exact, rowwise={rowwise}")
+        assert_bits_equal(orc.gemm(A, B, FAST, rowwise=rowwise), fused, f"fast, rowwise={rowwise}")
+
+
 def check_out_size(orc):
     """The output-size formula against torch's output shapes, and the k = 0 and empty cases."""
     for (N, Cin, H, W, Cout, G, KH, KW, stride, pad, dil) in CONV_INDEX_CASES:
@@ -389,5 +464,6 @@ ALL_CHECKS = [
     check_hand_cases, check_integer_closed_form, check_ieee_emulation, check_conv_ieee_emulation,
     check_transpose, check_split, check_rowwise, check_higham, check_conv_integer_vs_torch,
     check_conv_routes, check_conv_1x1_is_gemm, check_conv_groups_and_batch,
-    check_conv1d_library, check_identity, check_out_size,
+    check_conv1d_library, check_identity, check_out_size, check_single_outputs,
+    check_fused_unfused_family,
 ]

@@ -2,18 +2,20 @@
 against the CPU oracle's direct convolution, bit for bit, exact and fast.
 
 Cases: small random shapes covering stride, asymmetric padding, dilation,
-groups (depthwise included) and batch, with special values; the 53 layers of
-ResNet-50 v1.5 at batch 1 in full and at batch 8 on sampled outputs; the
-grouped dilated strided convolution in full; the 1-D convolution (H = 1) on
-sampled outputs and whole rows.
+groups (depthwise included) and batch, with special values; and every output
+of the full-size workloads: the 53 layers of ResNet-50 v1.5 at batch 1 and 8,
+the grouped dilated strided convolution and the 1-D convolution (H = 1), the
+SHA-256 of the GPU's outputs, the oracle's and the stored ones printed at the
+end of the session and equal.
 """
 import numpy as np
 import pytest
 
 import fp32_blocked_gemm_amd as og
+import full_size
 import oracle
 import synth
-from gpu_util import assert_same_bits, say, sha256, to_host, torch
+from gpu_util import assert_same_bits, record_hashes, say, sha256, to_host, torch
 
 pytestmark = pytest.mark.gpu
 MODES = (og.EXACT, og.FAST)
@@ -183,56 +185,46 @@ def test_padding_tap_meets_infinite_weight(orc):
         assert y.view(np.uint32).ravel()[0] == 0x7FC00000
 
 
+def _full_conv(orc, name):
+    """Every output of every layer of a full-size workload, both modes,
+    against the oracle; the digests of GPU, oracle and stored values equal."""
+    stored = full_size.stored()[name]
+    dig = {m: (full_size.Digest(), full_size.Digest()) for m in full_size.MODES}
+    for i, (s, x, w) in enumerate(full_size.conv_layers(name)):
+        for mname, mode in full_size.MODES.items():
+            say(f"{name} layer {i} {s} mode {mname}")
+            got = _gpu_conv(x, w, s, mode)
+            want = full_size.oracle_conv(orc, s, x, w, mode)
+            assert_same_bits(got, want, f"{name} layer {i} {s.name} mode {mname}")
+            dig[mname][0].add(got)
+            dig[mname][1].add(want)
+    for mname in full_size.MODES:
+        dg, do = dig[mname][0].hex(), dig[mname][1].hex()
+        record_hashes(name, mname, dg, do, stored[mname])
+        assert dg == do == stored[mname], f"{name} {mname}: digests differ"
+
+
 def test_resnet50_batch1_all_layers(orc):
     """All 53 layers of the chain at batch 1, every output, both modes."""
-    for i, s in enumerate(synth.resnet50_convs(1)):
-        x, w = synth.conv_inputs(s, synth.seed_for(4, i))
-        for mode in MODES:
-            say(f"resnet50 b1 layer {i} {s} mode {mode}")
-            got = _gpu_conv(x, w, s, mode)
-            want = _oracle(orc, x, w, s, mode)
-            assert sha256(got) == sha256(want), f"layer {i} {s.name} mode {mode}"
+    _full_conv(orc, "resnet50_b1")
 
 
-def _flat_sample(rng, shape, count):
-    total = int(np.prod(shape))
-    idx = rng.integers(0, total, size=count)
-    return np.concatenate([idx, [0, total - 1]])
-
-
-def test_resnet50_batch8_sampled(orc):
-    rng = np.random.default_rng(8)
-    for i, s in enumerate(synth.resnet50_convs(8)):
-        x, w = synth.conv_inputs(s, synth.seed_for(4, 100 + i))
-        for mode in MODES:
-            say(f"resnet50 b8 layer {i} {s} mode {mode}")
-            got = _gpu_conv(x, w, s, mode)
-            flat = _flat_sample(rng, got.shape, 600)
-            want = orc.conv2d_at(x, w, flat, mode, groups=s.groups, stride=s.stride, pad=s.pad,
-                                 dil=s.dil)
-            assert_same_bits(got.ravel()[flat], want, f"b8 layer {i} {s.name} mode {mode}")
+def test_resnet50_batch8_all_layers(orc):
+    """All 53 layers of the chain at batch 8, every output, both modes."""
+    _full_conv(orc, "resnet50_b8")
 
 
 def test_grouped_dilated_full(orc):
-    s = synth.grouped_dilated()
-    x, w = synth.conv_inputs(s, synth.seed_for(5, 0), "uniform")
-    for mode in MODES:
-        say(f"grouped dilated mode {mode}")
-        assert_same_bits(_gpu_conv(x, w, s, mode), _oracle(orc, x, w, s, mode),
-                         f"grouped mode {mode}")
+    _full_conv(orc, "grouped_dilated")
 
 
-def test_conv1d_h1_sampled(orc):
-    s = synth.conv1d_h1()
-    x, w = synth.conv_inputs(s, synth.seed_for(5, 10), "uniform")
-    rng = np.random.default_rng(10)
+def test_conv1d_h1_full(orc):
+    """The 1-D convolution (8 x 512 -> 512 channels, 4096 wide, KW = 5, pads 2
+    on the width only): every output; and image 0 alone (batch invariance)."""
+    _full_conv(orc, "conv1d_h1")
+    s, x, w = next(full_size.conv_layers("conv1d_h1"))
     for mode in MODES:
-        say(f"conv1d mode {mode}")
-        got = _gpu_conv(x, w, s, mode)
-        assert got.shape == (8, 512, 1, 4096)
-        flat = _flat_sample(rng, got.shape, 3000)
-        want = orc.conv2d_at(x, w, flat, mode, groups=1, stride=s.stride, pad=s.pad, dil=s.dil)
-        assert_same_bits(got.ravel()[flat], want, f"conv1d sampled mode {mode}")
-        # one whole image against the oracle on that image alone (batch invariance)
-        want0 = orc.conv2d(np.ascontiguousarray(x[:1]), w, mode, pad=s.pad)
-        assert_same_bits(got[:1], want0, f"conv1d image 0 mode {mode}")
+        say(f"conv1d image 0 mode {mode}")
+        got = _gpu_conv(np.ascontiguousarray(x[:1]), w, s.with_batch(1), mode)
+        assert_same_bits(got, full_size.oracle_conv(orc, s.with_batch(1), x[:1].copy(), w, mode),
+                         f"conv1d image 0 mode {mode}")

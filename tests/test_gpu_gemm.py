@@ -3,18 +3,23 @@ oracle, bit for bit, in exact and fast mode.
 
 Sizes: every dimension swept over 0..70 with the others fixed (the sweep the
 exact-mode page describes under "Checking it"), random row strides and
-pointer offsets, special values; the 256^3 exact case in full; the ragged
-1000x777x1531 case with row strides dim+13 in full; 4096^3, the prefill
-shape and the skinny m = 1 shape at full size on sampled outputs (and whole
-rows) in the launch configuration the benchmark times.
+pointer offsets, special values; and every full-size workload with every
+output compared, in the launch configuration the benchmark times: 256^3,
+4096^3 and the ragged 1000x777x1531 with row strides dim+13 (each with 0.1 %
+special values and as a clean copy), the prefill shape and the skinny m = 1
+shape.  For those the SHA-256 of the GPU's outputs, of the oracle's and the
+stored one (tests/golden/full_size_sha256.json) are printed at the end of
+the session and must all be equal.
 """
 import numpy as np
 import pytest
 
 import fp32_blocked_gemm_amd as og
+import full_size
 import oracle
 import synth
-from gpu_util import assert_same_bits, bits, say, sha256, to_device_strided, to_host, torch
+from gpu_util import (assert_same_bits, bits, record_hashes, say, to_device_strided, to_host,
+                      torch)
 
 pytestmark = pytest.mark.gpu
 MODES = (og.EXACT, og.FAST)
@@ -61,15 +66,35 @@ def _check_gaps(flatC, m, n, ldc, off):
     assert np.all(u[mask] == synth.GAP_OUT_BITS), "an element outside C was written"
 
 
+def _full_gemm(orc, name):
+    """Every output of a full-size workload, both modes, against the oracle;
+    the gaps of C's row stride untouched; a second run gives the same bits;
+    the digests of GPU, oracle and stored values equal."""
+    c = full_size.gemm_case(name)
+    stored = full_size.stored()[name]
+    dA, _ = to_device_strided(c.A, c.lda)
+    dB, _ = to_device_strided(c.B, c.ldb)
+    for mname, mode in full_size.MODES.items():
+        say(f"gemm {name} {c.m}x{c.n}x{c.k} mode {mname}")
+        fill = np.full((c.m, c.n), synth.GAP_OUT_BITS, np.uint32).view(np.float32)
+        dC, flatC = to_device_strided(fill, c.ldc, 0, gap_bits=synth.GAP_OUT_BITS)
+        og.gemm(dA, dB, mode, out=dC)
+        got = to_host(dC)
+        _check_gaps(to_host(flatC), c.m, c.n, c.ldc, 0)
+        say(f"oracle {name} mode {mname}")
+        want = full_size.oracle_gemm(orc, c, mode)
+        dg, do = full_size.Digest().add(got).hex(), full_size.Digest().add(want).hex()
+        record_hashes(name, mname, dg, do, stored[mname])
+        assert_same_bits(got, want, f"{name} mode {mname}")
+        assert do == stored[mname], f"{name} {mname}: the oracle's digest differs from the stored one"
+        og.gemm(dA, dB, mode, out=dC)
+        assert np.array_equal(bits(to_host(dC)), bits(got)), f"{name} {mname}: second run differs"
+        del dC, flatC
+
+
 def test_square_256_exact_config(orc):
     """m = n = k = 256, uniform[-1,1] from seed 0: bit for bit, exact and fast."""
-    c = synth.gemm_square256()
-    for mode in MODES:
-        say(f"gemm 256^3 mode {mode}")
-        got, _ = _run_gpu(c.A, c.B, mode, 256, 256, 256)
-        want = orc.gemm(c.A, c.B, mode, rowwise=True)
-        assert sha256(got) == sha256(want)
-        assert_same_bits(got, want, f"256^3 mode {mode}")
+    _full_gemm(orc, "gemm_256")
 
 
 SWEEP = [(d, 37, 45) for d in range(71)] + [(19, d, 45) for d in range(71)] + \
@@ -97,13 +122,7 @@ def test_size_sweep_0_to_70(orc, mode):
 @pytest.mark.parametrize("specials", [True, False])
 def test_ragged_ld13_full(orc, specials):
     """1000x777x1531 with row strides dim+13 and 0.1% special values: every output."""
-    c = synth.gemm_ragged(specials)
-    for mode in MODES:
-        say(f"gemm ragged specials={specials} mode {mode}")
-        got, flatC = _run_gpu(c.A, c.B, mode, c.lda, c.ldb, c.ldc)
-        want = orc.gemm(c.A, c.B, mode, rowwise=True)
-        assert_same_bits(got, want, f"ragged mode {mode}")
-        _check_gaps(flatC, c.m, c.n, c.ldc, 0)
+    _full_gemm(orc, "gemm_ragged_" + ("specials" if specials else "clean"))
 
 
 @pytest.mark.parametrize("variant", list(range(1, 21)))
@@ -164,50 +183,18 @@ def test_chain_kernel_lengths(orc, variant):
                              f"chain {variant} A aligned {m}x{n}x{k} mode {mode}")
 
 
-def _sample(rng, m, n, count):
-    rows = rng.integers(0, m, size=count)
-    cols = rng.integers(0, n, size=count)
-    # the four corners and the last row/column, where tile edges are
-    rows = np.concatenate([rows, [0, 0, m - 1, m - 1]])
-    cols = np.concatenate([cols, [0, n - 1, 0, n - 1]])
-    return rows, cols
-
-
-def _full_size(orc, c, whole_rows):
-    rng = np.random.default_rng(5)
-    for mode in MODES:
-        say(f"gemm {c.name} mode {mode}")
-        dA, _ = to_device_strided(c.A, c.lda)
-        dB, _ = to_device_strided(c.B, c.ldb)
-        dC = torch().empty((c.m, c.ldc), dtype=torch().float32, device="cuda")[:, :c.n]
-        og.gemm(dA, dB, mode, out=dC)
-        got = to_host(dC)
-        rows, cols = _sample(rng, c.m, c.n, 3000)
-        want = orc.gemm_at(c.A, c.B, rows, cols, mode)
-        assert_same_bits(got[rows, cols], want, f"{c.name} sampled mode {mode}")
-        for r in whole_rows:
-            wr = orc.gemm(c.A[r:r + 1], c.B, mode, rowwise=True)
-            assert_same_bits(got[r:r + 1], wr, f"{c.name} row {r} mode {mode}")
-        # run twice: the same bits
-        og.gemm(dA, dB, mode, out=dC)
-        assert np.array_equal(bits(to_host(dC)), bits(got)), "second run differs"
-
-
 @pytest.mark.parametrize("specials", [True, False])
-def test_4096_cubed_sampled(orc, specials):
-    _full_size(orc, synth.gemm_4096(specials), whole_rows=[0, 2047, 4095])
+def test_4096_cubed_full(orc, specials):
+    """4096^3 with 0.1 % special values and as a clean copy: every output."""
+    _full_gemm(orc, "gemm_4096_" + ("specials" if specials else "clean"))
 
 
-def test_prefill_sampled(orc):
-    _full_size(orc, synth.gemm_prefill(), whole_rows=[0, 511])
+def test_prefill_full(orc):
+    _full_gemm(orc, "gemm_prefill")
 
 
 def test_skinny_full(orc):
-    c = synth.gemm_skinny()
-    for mode in MODES:
-        say(f"gemm skinny mode {mode}")
-        got, _ = _run_gpu(c.A, c.B, mode, c.lda, c.ldb, c.ldc)
-        assert_same_bits(got, orc.gemm(c.A, c.B, mode, rowwise=True), f"skinny mode {mode}")
+    _full_gemm(orc, "gemm_skinny")
 
 
 def test_k_zero_and_empty():

@@ -106,9 +106,9 @@ def test_nt_variants_agree(orc, variant):
                              f"nt variant {variant} {m}x{n}x{k} mode {mode}")
 
 
-def test_nt_prefill_sampled(orc):
-    """512 tokens x 4096 against 11008 x 4096 weights: sampled outputs and whole rows."""
-    rng = np.random.default_rng(860)
+def test_nt_prefill_full(orc):
+    """512 tokens x 4096 against 11008 x 4096 weights: every output (the
+    oracle multiplies by the transpose of the weights, which it only moves)."""
     A = synth.normal((512, 4096), synth.seed_for(3, 20))
     Bt = synth.normal((11008, 4096), synth.seed_for(3, 21), 0.02)
     Bc = np.ascontiguousarray(Bt.T)
@@ -116,13 +116,7 @@ def test_nt_prefill_sampled(orc):
     for mode in MODES:
         say(f"gemm_nt prefill mode {mode}")
         got = to_host(og.gemm_nt(dA, dB, mode))
-        rows = np.concatenate([rng.integers(0, 512, 3000), [0, 0, 511, 511]])
-        cols = np.concatenate([rng.integers(0, 11008, 3000), [0, 11007, 0, 11007]])
-        assert_same_bits(got[rows, cols], orc.gemm_at(A, Bc, rows, cols, mode),
-                         f"nt prefill sampled mode {mode}")
-        for r in (0, 255, 511):
-            assert_same_bits(got[r:r + 1], orc.gemm(A[r:r + 1], Bc, mode, rowwise=True),
-                             f"nt prefill row {r} mode {mode}")
+        assert_same_bits(got, orc.gemm(A, Bc, mode, rowwise=True), f"nt prefill mode {mode}")
 
 
 @pytest.mark.parametrize("model", ["bert_base_4096", "minilm_l6_4096", "whisper_small_enc_1500"])

@@ -60,6 +60,18 @@ MUTANTS = [
     ("out_size_off_by_one",
      "return floor_div(size + pad_before + pad_after - dil * (k - 1) - 1, stride) + 1;",
      "return floor_div(size + pad_before + pad_after - dil * (k - 1), stride) + 1;"),
+    ("rowwise_from_minus_zero",
+     "                acc[j] = 0.0f;",
+     "                acc[j] = -0.0f;"),
+    ("gemm_at_mode_ignored",
+     "out[t] = gemm_one(k, A + rows[t] * lda, B, ldb, cols[t], mode);",
+     "out[t] = gemm_one(k, A + rows[t] * lda, B, ldb, cols[t], MODE_EXACT);"),
+    ("conv_at_row_and_column_swapped",
+     "out[t] = conv_one(&s, x, w, n, oc, oy, ox, mode);",
+     "out[t] = conv_one(&s, x, w, n, oc, ox, oy, mode);"),
+    ("conv_at_image_and_channel_swapped",
+     "        const int64_t oc = r % s.Cout;\n        const int64_t n = r / s.Cout;",
+     "        const int64_t n = r % s.N;\n        const int64_t oc = r / s.N;"),
     ("im2col_rows_kx_major",
      "const int64_t row = (c * s.KH + ky) * s.KW + kx;",
      "const int64_t row = (c * s.KW + kx) * s.KH + ky;"),
