@@ -29,9 +29,15 @@
 // gather; "Convolution (fast mode)", section "Layout of the work").  The
 // global loads of a chunk are issued D-1 chunks ahead into a ring of
 // registers, so their latency hides behind the products of the chunks in
-// between.  Rows, columns and taps beyond the problem are staged as +0 in
-// BOTH operands, so the extra terms are fma(+0, +0, acc) = acc and
-// acc + round(+0 * +0) = acc.
+// between.  Rows and columns beyond the problem are staged as +0.  Taps
+// beyond k (the last chunk running past the end) read +0 in both operands;
+// in fast mode one operand's padding then gets its sign bit set (an OR with
+// a mask that is zero for real taps, no branch), so each such term adds a
+// product of -0, and x + (-0) = x for every x.  A +0 product would not do:
+// in fast mode a sum can be -0 (a fused multiply-add whose exact result is a
+// negative number too small to represent, added to +0, rounds to -0), and
+// -0 + (+0) = +0.  In exact mode a sum is never -0 (+0 + (-0) = +0, and a
+// rounded sum of non-zero values is never -0), so +0 padding is neutral.
 //
 // All code is compiled with -ffp-contract=off and with fp32 denormals on.
 #pragma once
@@ -129,6 +135,13 @@ __host__ __device__ inline TileCoord tile_of_block(int bid, int nblocks, int til
 
 __device__ inline float canonical(float v) {
   return v != v ? __uint_as_float(0x7FC00000u) : v;
+}
+
+// The sign mask of a staged tap: 0x80000000 for a tap at or beyond k (its
+// padding +0 becomes -0 by an OR), 0 for a real tap.
+__device__ __forceinline__ uint32_t pad_sign(bool past) { return past ? 0x80000000u : 0u; }
+__device__ __forceinline__ float or_sign(float v, uint32_t sign) {
+  return __uint_as_float(__float_as_uint(v) | sign);
 }
 
 // The value stored for output channel ch at dst: the finished sum, then the
@@ -261,6 +274,18 @@ struct AStage {
 #pragma unroll
       for (int e = 0; e < KV; ++e) lds[(kc + e) * LDA + r0 + q * RSTEP] = r[q * KV + e];
   }
+  // The same for the chunk starting at tap k0, this thread's taps at or
+  // beyond K stored as -0 (pad_sign; VEC: K is a multiple of 4, so a load is
+  // wholly inside or wholly past K).
+  template <int LDA>
+  __device__ void store_signed(float *lds, const float (&r)[kRegs], int k0, int K) const {
+    const uint32_t sg = pad_sign(k0 + kc >= K);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+      for (int e = 0; e < KV; ++e)
+        lds[(kc + e) * LDA + r0 + q * RSTEP] = or_sign(r[q * KV + e], sg);
+  }
 };
 
 // ---------------------------------------------------------------------------
@@ -384,6 +409,22 @@ struct BStage {
 #pragma unroll
     for (int q = 0; q < TPG; ++q) lds[(t0 + q) * BN + col] = r[q];
   }
+  // The same for the chunk starting at tap k0, taps at or beyond K stored as
+  // -0 (pad_sign).
+  __device__ void store_signed(float *lds, const float (&r)[kRegs], int k0, int K) const {
+    if (V) {
+#pragma unroll
+      for (int q = 0; q < VNQ; ++q) {
+        const uint32_t sg = pad_sign(k0 + t0 + q * VRSTEP >= K);
+        *reinterpret_cast<float4 *>(&lds[(t0 + q * VRSTEP) * BN + col]) =
+            make_float4(or_sign(r[q * 4 + 0], sg), or_sign(r[q * 4 + 1], sg),
+                        or_sign(r[q * 4 + 2], sg), or_sign(r[q * 4 + 3], sg));
+      }
+      return;
+    }
+#pragma unroll
+    for (int q = 0; q < TPG; ++q) lds[(t0 + q) * BN + col] = or_sign(r[q], pad_sign(k0 + t0 + q >= K));
+  }
 };
 
 // Pointer to output (row, col) of group g.
@@ -398,7 +439,8 @@ __device__ inline float *out_ptr(const Problem &p, int g, int row, int col) {
 // ---------------------------------------------------------------------------
 // The staging pipeline.  Chunk c's loads go to register slot c % D, D-1
 // chunks ahead of its use; at its turn the slot is written to LDS buffer
-// c % 2, one barrier, then the chunk's products.  One barrier per chunk is
+// c % 2 (store(slot, buffer, c)), one barrier, then the chunk's products.
+// One barrier per chunk is
 // enough with two LDS buffers: a wave writing buffer c % 2 has passed the
 // barrier of chunk c-1, so every wave has finished reading chunk c-2 there.
 // The main loop runs whole groups of D chunks and issues every load
@@ -418,7 +460,7 @@ __device__ __forceinline__ void run_pipeline(int nchunks, Load &&load, Store &&s
     static_for<D>([&](auto j) __attribute__((always_inline)) {
       constexpr int J = decltype(j)::value;
       load(min(c0 + J + D - 1, last), std::integral_constant<int, (J + D - 1) % D>{});
-      store(j, std::integral_constant<int, J % 2>{});
+      store(j, std::integral_constant<int, J % 2>{}, c0 + J);
       __syncthreads();
       compute(c0 + J, std::integral_constant<int, J % 2>{}, j);
     });
@@ -426,7 +468,7 @@ __device__ __forceinline__ void run_pipeline(int nchunks, Load &&load, Store &&s
   static_for<D - 1>([&](auto j) __attribute__((always_inline)) {
     constexpr int J = decltype(j)::value;
     if (full + J < nchunks) {
-      store(j, std::integral_constant<int, J % 2>{});
+      store(j, std::integral_constant<int, J % 2>{}, full + J);
       __syncthreads();
       compute(full + J, std::integral_constant<int, J % 2>{}, j);
     }
@@ -513,8 +555,13 @@ __global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
         as.load(p, c * BK, ra[decltype(slot)::value]);
         bs.load(p, c * BK, rb[decltype(slot)::value]);
       },
-      [&](auto slot, auto buf) __attribute__((always_inline)) {
-        as.template store<LDA>(As[decltype(buf)::value], ra[decltype(slot)::value]);
+      [&](auto slot, auto buf, int c) __attribute__((always_inline)) {
+        // fast mode: the A tile's taps past K are -0 (B's are +0)
+        if constexpr (MODE == kFast)
+          as.template store_signed<LDA>(As[decltype(buf)::value], ra[decltype(slot)::value], c * BK,
+                                        p.K);
+        else
+          as.template store<LDA>(As[decltype(buf)::value], ra[decltype(slot)::value]);
         if constexpr (BT)
           bs.template store<LDB>(Bs[decltype(buf)::value], rb[decltype(slot)::value]);
         else
@@ -740,8 +787,13 @@ __global__ void __launch_bounds__(256) valu_kernel(Problem p) {
         as.load(p, c * BK, ra[decltype(slot)::value]);
         bs.load(p, c * BK, rb[decltype(slot)::value]);
       },
-      [&](auto slot, auto buf) __attribute__((always_inline)) {
-        as.template store<LDA>(As[decltype(buf)::value], ra[decltype(slot)::value]);
+      [&](auto slot, auto buf, int c) __attribute__((always_inline)) {
+        // fast mode: the A tile's taps past K are -0 (B's are +0)
+        if constexpr (MODE == kFast)
+          as.template store_signed<LDA>(As[decltype(buf)::value], ra[decltype(slot)::value], c * BK,
+                                        p.K);
+        else
+          as.template store<LDA>(As[decltype(buf)::value], ra[decltype(slot)::value]);
         if constexpr (BT)
           bs.template store<LDB>(Bs[decltype(buf)::value], rb[decltype(slot)::value]);
         else
@@ -863,7 +915,14 @@ __global__ void __launch_bounds__(64 * W)
                                 k0 + t < p.K ? (uint32_t)(4 * t) : kOutside);
           }
       },
-      [&](auto slot, auto buf) __attribute__((always_inline)) { bs.store(Bs[decltype(buf)::value], rb[decltype(slot)::value]); },
+      [&](auto slot, auto buf, int c) __attribute__((always_inline)) {
+        // fast mode: B's taps past K are -0 (the weight registers hold +0
+        // there: they are read through DPP and never written by the VALU)
+        if constexpr (MODE == kFast)
+          bs.store_signed(Bs[decltype(buf)::value], rb[decltype(slot)::value], c * BK, p.K);
+        else
+          bs.store(Bs[decltype(buf)::value], rb[decltype(slot)::value]);
+      },
       [&](int, auto buf, auto slot) __attribute__((always_inline)) {
         constexpr int S = decltype(slot)::value;
         const float *bl = Bs[decltype(buf)::value];
@@ -997,10 +1056,18 @@ __global__ void __launch_bounds__(64 * W) lane_conv_kernel(Problem p) {
                                 k0 + t < p.K ? (uint32_t)(4 * t) : kOutside);
           }
       },
-      [&](auto slot, auto buf) __attribute__((always_inline)) {
+      [&](auto slot, auto buf, int c) __attribute__((always_inline)) {
         float *bl = Bs[decltype(buf)::value];
+        // fast mode: the taps of channels past the group's last are -0 (the
+        // weights there are +0)
 #pragma unroll
-        for (int j = 0; j < PER; ++j) bl[(wave * PER + j) * BN + lane] = rb[decltype(slot)::value][j];
+        for (int cc = 0; cc < CPW; ++cc) {
+          const uint32_t sg = MODE == kFast ? pad_sign(c * CC + wave * CPW + cc >= cin_g) : 0u;
+#pragma unroll
+          for (int k = 0; k < KHW; ++k)
+            bl[(wave * PER + cc * KHW + k) * BN + lane] =
+                or_sign(rb[decltype(slot)::value][cc * KHW + k], sg);
+        }
       },
       [&](int, auto buf, auto slot) __attribute__((always_inline)) {
         constexpr int S = decltype(slot)::value;
@@ -1289,7 +1356,12 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, chain_rows(
         for (int i = 0; i < NW; ++i) rw[S][i] = load1(rs, woffset(i, k0, std::false_type{}));
       }
     };
-    auto store = [&](auto slot, int st) __attribute__((always_inline)) {
+    // chunk c into stage st; in fast mode, in a chunk that runs past K, the
+    // weights of taps at or beyond K are then overwritten with -0 (B's are
+    // +0), so each padded term adds a product of -0 (the lane's own stores:
+    // no barrier between; with 16-byte loads K is a multiple of 4, so a quad
+    // is wholly past or not)
+    auto store = [&](auto slot, int st, int c) __attribute__((always_inline)) {
       constexpr int S = decltype(slot)::value;
       if (wv) {
 #pragma unroll
@@ -1302,9 +1374,20 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, chain_rows(
         for (int i = 0; i < NW; ++i)
           if (i * 64 + lane < ROWS * BK) wstage[st][i * 64 + lane] = rw[S][i];
       }
+      const int k0 = c * BK;
+      if (MODE == kFast && k0 + BK > p.K) {
+        if (wv) {
+          for (int idx = lane; idx < ROWS * BK / 4; idx += 64)
+            if (k0 + 4 * (idx % (BK / 4)) >= p.K)
+              *reinterpret_cast<float4 *>(&wstage[st][4 * idx]) = make_float4(-0.0f, -0.0f, -0.0f, -0.0f);
+        } else {
+          for (int idx = lane; idx < ROWS * BK; idx += 64)
+            if (k0 + idx % BK >= p.K) wstage[st][idx] = -0.0f;
+        }
+      }
     };
     static_for<DW>([&](auto j) __attribute__((always_inline)) { load(min((int)decltype(j)::value, last), j); });
-    store(std::integral_constant<int, 0>{}, 0);
+    store(std::integral_constant<int, 0>{}, 0, 0);
     load(min(DW, last), std::integral_constant<int, 0>{});
     for (int t0 = -1; t0 < nchunks; t0 += U) {
       static_for<U>([&](auto j) __attribute__((always_inline)) {
@@ -1312,7 +1395,7 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, chain_rows(
         const int t = t0 + J;
         if (t < nchunks) {
           const int v = t + 2;  // the chunk stored now (slot (J + 1) % DW holds it)
-          store(std::integral_constant<int, (J + 1) % DW>{}, v % NS);
+          store(std::integral_constant<int, (J + 1) % DW>{}, v % NS, v);
           load(min(v + DW, last), std::integral_constant<int, (J + 1) % DW>{});
           __syncthreads();
         }
@@ -1897,8 +1980,13 @@ __global__ void __launch_bounds__(256) grouped_kernel(Problem p) {
 #pragma unroll
         for (int j = 0; j < RR; ++j) {
           const int row = i * RR + j;
-          const bool ok = row < p.M && k < p.K && q * 16 + (lane & 15) < NT;
+          const bool tap = k < p.K && q * 16 + (lane & 15) < NT;
+          const bool ok = row < p.M && tap;
           w[j] = load1(rw, ok ? (uint32_t)(4 * ((int64_t)row * p.lda + k)) : kOutside);
+          // fast mode, a tap past the group (its input reads +0): weight
+          // -0, so the term adds a product of -0, which leaves any sum
+          // unchanged
+          if (MODE == kFast) w[j] = or_sign(w[j], pad_sign(!tap));
         }
         dpp_steps<MODE, RR, 16>(acc[i], w, &v[q * 16]);
       }
@@ -1964,9 +2052,15 @@ __global__ void __launch_bounds__(64) rowdot_kernel(Problem p) {
     const __amdgpu_buffer_rsrc_t rv = buffer_at(vbase + (int64_t)k0 * p.ldb, kRange);
     vr[S] = load1(rv, k0 + (lane & 15) < p.K ? voff : kOutside);
   };
-  auto compute = [&](auto slot) __attribute__((always_inline)) {
+  // chunk c; in fast mode the row's taps at or beyond K are -0 (v's are +0),
+  // so each padded term adds a product of -0
+  auto compute = [&](auto slot, int c) __attribute__((always_inline)) {
     constexpr int S = decltype(slot)::value;
     const float w1[1] = {vr[S]};
+    if constexpr (MODE == kFast) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) wr[S][t] = or_sign(wr[S][t], pad_sign(c * 16 + t >= p.K));
+    }
     dpp_steps<MODE, 1, 16>(acc, w1, wr[S]);
   };
   if (nchunks > 0) {
@@ -1976,11 +2070,11 @@ __global__ void __launch_bounds__(64) rowdot_kernel(Problem p) {
       static_for<D>([&](auto j) __attribute__((always_inline)) {
         constexpr int J = decltype(j)::value;
         load(min(c0 + J + D - 1, last), std::integral_constant<int, (J + D - 1) % D>{});
-        compute(j);
+        compute(j, c0 + J);
       });
     }
     static_for<D - 1>([&](auto j) __attribute__((always_inline)) {
-      if (full + (int)decltype(j)::value < nchunks) compute(j);
+      if (full + (int)decltype(j)::value < nchunks) compute(j, full + (int)decltype(j)::value);
     });
   }
   if (ok) {

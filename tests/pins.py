@@ -442,6 +442,36 @@ def check_fused_unfused_family(orc):
         assert_bits_equal(orc.gemm(A, B, FAST, rowwise=rowwise), fused, f"fast, rowwise={rowwise}")
 
 
+def underflow_family(rng, m: int, n: int, k: int):
+    """A = 2^-100 and B = +-(1..2) * 2^-60 (negative in odd columns): every
+    product is a non-zero value far below the smallest subnormal.  Rounded
+    on its own (exact mode) a product is a signed zero and +0 + (-0) = +0, so
+    every output is +0.  Fused with the sum (fast mode), the exact result of
+    the first term of an odd column is negative and rounds to -0; every later
+    term adds another negative amount to -0, so those outputs are -0 (even
+    columns +0).  Returns A, B and the fast-mode bits."""
+    A = np.full((m, k), 2.0 ** -100, np.float32)
+    B = (rng.uniform(1, 2, (k, n)) * 2.0 ** -60).astype(np.float32)
+    B[:, 1::2] *= -1
+    fast = np.zeros((m, n), np.uint32)
+    if k > 0:
+        fast[:, 1::2] = 0x80000000
+    return A, B, fast
+
+
+def check_underflow_sign(orc):
+    """IEEE 754 rounding of a fused multiply-add whose exact result is a
+    non-zero negative number too small to represent gives -0; a separately
+    rounded product and sum give +0 ("Exact mode", rules 1 and 3; "Matrix
+    product and convolution kernels", section "Fast mode")."""
+    rng = np.random.default_rng(41)
+    for k in (1, 2, 7):
+        A, B, fast = underflow_family(rng, 3, 6, k)
+        for rowwise in (False, True):
+            assert np.all(bits(orc.gemm(A, B, EXACT, rowwise=rowwise)) == 0), f"exact k={k}"
+            assert np.array_equal(bits(orc.gemm(A, B, FAST, rowwise=rowwise)), fast), f"fast k={k}"
+
+
 def check_out_size(orc):
     """The output-size formula against torch's output shapes, and the k = 0 and empty cases."""
     for (N, Cin, H, W, Cout, G, KH, KW, stride, pad, dil) in CONV_INDEX_CASES:
@@ -465,5 +495,5 @@ ALL_CHECKS = [
     check_transpose, check_split, check_rowwise, check_higham, check_conv_integer_vs_torch,
     check_conv_routes, check_conv_1x1_is_gemm, check_conv_groups_and_batch,
     check_conv1d_library, check_identity, check_out_size, check_single_outputs,
-    check_fused_unfused_family,
+    check_fused_unfused_family, check_underflow_sign,
 ]

@@ -13,6 +13,10 @@ random.  The planted output must equal the case's stored bits, and every
 output the oracle's.
 
 Discriminators:
+  * the sign of an underflowing fused sum: products far below the smallest
+    subnormal, negative in odd columns, with k running past the last whole
+    chunk of every kernel; fast mode gives -0 there and exact mode +0, so a
+    k tail padded with terms that add +0 (turning -0 into +0) would show;
   * fused against unfused: output (i, j) sums c + a*b with c = -round(a*b)
     placed before a*b.  Separately rounded, the sum is +0; fused, it is the
     rounding error of a*b, computed here exactly in float64;
@@ -105,6 +109,35 @@ def test_hand_cases_planted_in_every_variant(orc, variant):
         # W7: k = 0 stores +0 everywhere
         got0 = _gpu_gemm(np.zeros((M, 0), np.float32), np.zeros((0, N), np.float32), mode)
         assert np.all(bits(got0) == 0), f"k = 0 variant {variant} {mname}"
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_underflow_to_minus_zero(orc, variant):
+    """Fast mode keeps the -0 of an underflowing fused sum through the padding
+    of k's last chunk, for k below, at and past each kernel's chunk sizes."""
+    rng = np.random.default_rng(930 + variant)
+    og.set_variant(variant)
+    for m, n, k in ((300, 520, 40), (37, 130, 1), (70, 64, 16), (70, 64, 64), (9, 200, 129),
+                    (5, 300, 300), (1, 4096, 300), (130, 66, 145)):
+        A, B, fast = pins.underflow_family(rng, m, n, k)
+        for mname, mode in MODES.items():
+            say(f"underflow sign variant {variant} {m}x{n}x{k} mode {mname}")
+            got = _gpu_gemm(A, B, mode)
+            want = fast if mode == og.FAST else np.zeros((m, n), np.uint32)
+            assert_same_bits(got, want.view(np.float32), f"underflow {m}x{n}x{k} v{variant} {mname}")
+    # convolutions: channels past a chunk, and padding taps (+0 inputs times
+    # negative weights add -0, which keeps -0)
+    for s in CONV_SHAPES + [synth.ConvShape("u3x3", 1, 37, 6, 7, 20, 3, 3, (1, 1), (1, 1, 1, 1)),
+                            synth.ConvShape("u1x1", 2, 130, 5, 6, 9, 1, 1)]:
+        x = np.full((s.N, s.Cin, s.H, s.W), 2.0 ** -100, np.float32)
+        w = (-rng.uniform(1, 2, (s.Cout, s.Cin // s.groups, s.KH, s.KW)) * 2.0 ** -60).astype(
+            np.float32)
+        for mname, mode in MODES.items():
+            say(f"underflow sign conv variant {variant} {s} mode {mname}")
+            got = _gpu_conv(x, w, s, mode)
+            want = orc.conv2d(x, w, mode, groups=s.groups, stride=s.stride, pad=s.pad, dil=s.dil)
+            assert np.all(bits(want) == (0x80000000 if mode == og.FAST else 0))
+            assert_same_bits(got, want, f"underflow conv {s.name} v{variant} {mname}")
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
