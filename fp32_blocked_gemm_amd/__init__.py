@@ -23,10 +23,12 @@ OG_ERR_TOO_LARGE = -4
 
 EXACT = 0
 FAST = 1
+FAST_MFMA = 2  # fast under a stated tolerance (split k, fp32 matrix cores); see og.h
 ACT_NONE = 0
 ACT_RELU = 1
 _ACTS = {None: ACT_NONE, "none": ACT_NONE, "relu": ACT_RELU, ACT_NONE: ACT_NONE, ACT_RELU: ACT_RELU}
-_MODES = {"exact": EXACT, "fast": FAST, EXACT: EXACT, FAST: FAST}
+_MODES = {"exact": EXACT, "fast": FAST, "fast_mfma": FAST_MFMA, EXACT: EXACT, FAST: FAST,
+          FAST_MFMA: FAST_MFMA}
 
 _i64 = ctypes.c_int64
 _vp = ctypes.c_void_p
@@ -87,7 +89,7 @@ def _mode(mode) -> int:
     try:
         return _MODES[mode]
     except KeyError:
-        raise ValueError(f"mode must be 'exact' or 'fast', not {mode!r}") from None
+        raise ValueError(f"mode must be 'exact', 'fast' or 'fast_mfma', not {mode!r}") from None
 
 
 def version() -> str:

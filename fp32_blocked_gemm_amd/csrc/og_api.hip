@@ -218,7 +218,8 @@ void launch(int mode, bool av, bool bv, const Tile &t, const og::Problem &p, hip
 
 
 const Tile &pick(const Shape &s, int mode) {
-  return t_variant == 0 || t_variant == kDepthwiseVariant || t_variant == kGroupedVariant
+  return t_variant == 0 || t_variant == kDepthwiseVariant || t_variant == kGroupedVariant ||
+                 is_split(t_variant)
              ? choose_tile(s, mode)
              : tile_for_variant(t_variant);
 }
@@ -300,14 +301,72 @@ bool grid_fits(const Tile &t, int64_t M, int64_t N, int64_t groups) {
   return ceil_div(M, t.bm) * ceil_div(N, t.bn) * groups <= kI32Max;
 }
 
+bool valid_mode(int mode) {
+  return mode == OG_MODE_EXACT || mode == OG_MODE_FAST || mode == OG_MODE_FAST_MFMA;
+}
+
+// Launch time of a split-k variant: t = o + rounds * chunks * c microseconds,
+// chunks = a wave's share of the 16-tap chunks of k, rounds = the launch's
+// waves over the waves resident at once, with (cap, c, o) per variant.
+struct SplitCost {
+  int variant;
+  double cap, c, o;
+};
+constexpr SplitCost kSplitCosts[] = {
+    {21, 4096, 0.10, 3.0}, {22, 4096, 0.10, 3.0}, {23, 4096, 0.12, 3.0},
+    {24, 4096, 0.15, 3.0}, {25, 2048, 0.20, 3.0}};
+
+double split_estimate(int v, const Shape &s) {
+  const SplitTile &t = split_tile(v);
+  for (const SplitCost &c : kSplitCosts) {
+    if (c.variant != v) continue;
+    const double blocks = (double)ceil_div(s.M, 16 * t.tm) * (double)ceil_div(s.N, 16 * t.tn) *
+                          (double)s.groups;
+    const double chunks = (double)ceil_div(ceil_div(std::max<int64_t>(s.K, 1), 16), t.ks);
+    const double rounds = std::ceil(blocks * t.ks / c.cap);
+    return c.o + rounds * chunks * c.c;
+  }
+  return 1e300;
+}
+
+// The kernel of a call in mode 2 (fast under tolerance): a split-k variant,
+// or 0 for the fast-mode kernels (which meet the bound): the forced variant,
+// else the lower estimate of the best fast-mode tile and the split-k tiles.
+// fast_estimate < 0: no estimate of the fast path (use the split-k kernels
+// only when forced).
+int mode2_variant(const Shape &s, double fast_estimate) {
+  if (is_split(t_variant)) return t_variant;
+  if (t_variant != 0 || fast_estimate < 0) return 0;
+  int best = 0;
+  double best_cost = fast_estimate;
+  for (const SplitCost &c : kSplitCosts) {
+    const double e = split_estimate(c.variant, s);
+    if (e < best_cost) {
+      best_cost = e;
+      best = c.variant;
+    }
+  }
+  return best;
+}
+
+// A split-k variant forced in exact or fast mode: refused (neither mode's
+// bits can come from it).
+og_status refuse_split(const char *what, int mode) {
+  if (mode != OG_MODE_FAST_MFMA && is_split(t_variant))
+    return fail(OG_ERR_NOT_EXACT, "%s: variant %d has no %s form (split-k kernels run only in "
+                "mode 2)", what, t_variant, mode == OG_MODE_EXACT ? "exact" : "fast");
+  return OG_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 og_status og_gemm_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_t lda,
                       const float *B, int64_t ldb, float *C, int64_t ldc, int mode) {
-  if (mode != OG_MODE_EXACT && mode != OG_MODE_FAST)
-    return fail(OG_ERR_INVALID_ARG, "og_gemm_f32: mode %d is not 0 (exact) or 1 (fast)", mode);
+  if (!valid_mode(mode))
+    return fail(OG_ERR_INVALID_ARG, "og_gemm_f32: mode %d is not 0 (exact), 1 (fast) or 2 (fast "
+                "under tolerance)", mode);
   if (m < 0 || n < 0 || k < 0)
     return fail(OG_ERR_INVALID_ARG, "og_gemm_f32: negative size m=%lld n=%lld k=%lld",
                 (long long)m, (long long)n, (long long)k);
@@ -325,9 +384,19 @@ og_status og_gemm_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_t l
   // the kernels address a tile's rows with 32-bit byte offsets
   if (lda > (int64_t(1) << 22) || ldb > (int64_t(1) << 22))
     return fail(OG_ERR_TOO_LARGE, "og_gemm_f32: lda or ldb exceeds 2^22");
-  const Tile &t = pick(Shape{m, n, k, 1, 0, 0}, mode);
-  if (!grid_fits(t, m, n, 1)) return fail(OG_ERR_TOO_LARGE, "og_gemm_f32: too many tiles");
-  og_status st = check_device();
+  og_status st = refuse_split("og_gemm_f32", mode);
+  if (st != OG_OK) return st;
+  const Shape sh{m, n, k, 1, 0, 0};
+  const int split =
+      mode == OG_MODE_FAST_MFMA
+          ? mode2_variant(sh, estimate(choose_tile(sh, OG_MODE_FAST), sh, OG_MODE_FAST))
+          : 0;
+  if (mode == OG_MODE_FAST_MFMA && !split) mode = OG_MODE_FAST;  // the fast kernels meet the bound
+  const Tile &t = pick(sh, mode);
+  if (!split && !grid_fits(t, m, n, 1)) return fail(OG_ERR_TOO_LARGE, "og_gemm_f32: too many tiles");
+  if (split && ceil_div(m, 16) * ceil_div(n, 16) > kI32Max)
+    return fail(OG_ERR_TOO_LARGE, "og_gemm_f32: too many tiles");
+  st = check_device();
   if (st != OG_OK) return st;
 
   og::Problem p{};
@@ -343,6 +412,10 @@ og_status og_gemm_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_t l
   p.groups = 1;
   const bool av = aligned16(A) && lda % 4 == 0 && k % 4 == 0;
   p.a_vec = av ? 1 : 0;
+  if (split) {
+    launch_splitk_matrix(split, av, false, false, p, t_stream);
+    return check_launch("og_gemm_f32");
+  }
   const bool stream_col = n == 1 && k > kStreamMinK && ldb == 1 && ldc == 1 && vt_ok(A, lda, k);
   if (n == 1 && !stream_col && k <= kRowdotMaxK && t_variant == 0 && rowdot_fits(m, lda, ldb, 1)) {
     // a single column: the rows of A against the column of B
@@ -373,8 +446,9 @@ og_status og_gemm_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_t l
 
 og_status og_gemm_nt_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_t lda,
                          const float *B, int64_t ldb, float *C, int64_t ldc, int mode) {
-  if (mode != OG_MODE_EXACT && mode != OG_MODE_FAST)
-    return fail(OG_ERR_INVALID_ARG, "og_gemm_nt_f32: mode %d is not 0 (exact) or 1 (fast)", mode);
+  if (!valid_mode(mode))
+    return fail(OG_ERR_INVALID_ARG, "og_gemm_nt_f32: mode %d is not 0 (exact), 1 (fast) or 2 "
+                "(fast under tolerance)", mode);
   if (m < 0 || n < 0 || k < 0)
     return fail(OG_ERR_INVALID_ARG, "og_gemm_nt_f32: negative size m=%lld n=%lld k=%lld",
                 (long long)m, (long long)n, (long long)k);
@@ -391,13 +465,40 @@ og_status og_gemm_nt_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_
     return fail(OG_ERR_TOO_LARGE, "og_gemm_nt_f32: a dimension exceeds 2^31-1");
   if (lda > (int64_t(1) << 22) || ldb > (int64_t(1) << 22))
     return fail(OG_ERR_TOO_LARGE, "og_gemm_nt_f32: lda or ldb exceeds 2^22");
+  og_status st = refuse_split("og_gemm_nt_f32", mode);
+  if (st != OG_OK) return st;
   const Shape sh{m, n, k, 1, 0, 0};
+  const int split =
+      mode == OG_MODE_FAST_MFMA
+          ? mode2_variant(sh, estimate(pick_nt(sh, OG_MODE_FAST), sh, OG_MODE_FAST))
+          : 0;
+  if (mode == OG_MODE_FAST_MFMA && !split) mode = OG_MODE_FAST;  // the fast kernels meet the bound
   const bool single_row = m == 1 && t_variant == 0;
   const Tile &t = pick_nt(sh, mode);
-  if (!single_row && !grid_fits(t, m, n, 1))
+  if (!split && !single_row && !grid_fits(t, m, n, 1))
     return fail(OG_ERR_TOO_LARGE, "og_gemm_nt_f32: too many tiles");
-  og_status st = check_device();
+  if (split && ceil_div(m, 16) * ceil_div(n, 16) > kI32Max)
+    return fail(OG_ERR_TOO_LARGE, "og_gemm_nt_f32: too many tiles");
+  st = check_device();
   if (st != OG_OK) return st;
+  if (split) {
+    og::Problem q{};
+    q.A = A;
+    q.lda = lda;
+    q.B = B;
+    q.ldb = ldb;
+    q.C = C;
+    q.ldc = ldc;
+    q.M = (int)m;
+    q.N = (int)n;
+    q.K = (int)k;
+    q.groups = 1;
+    const bool av = aligned16(A) && lda % 4 == 0 && k % 4 == 0;
+    const bool bv = aligned16(B) && ldb % 4 == 0 && k % 4 == 0;
+    q.a_vec = av ? 1 : 0;
+    launch_splitk_matrix(split, av, bv, true, q, t_stream);
+    return check_launch("og_gemm_nt_f32");
+  }
 
   og::Problem p{};
   p.groups = 1;
@@ -475,8 +576,9 @@ og_status conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout, int
                  int64_t padBottom, int64_t padRight, int64_t dilH, int64_t dilW, const float *x,
                  const float *w, const float *bias, int act, const float *residual, float *y,
                  int mode) {
-  if (mode != OG_MODE_EXACT && mode != OG_MODE_FAST)
-    return fail(OG_ERR_INVALID_ARG, "og_conv2d_f32: mode %d is not 0 (exact) or 1 (fast)", mode);
+  if (!valid_mode(mode))
+    return fail(OG_ERR_INVALID_ARG, "og_conv2d_f32: mode %d is not 0 (exact), 1 (fast) or 2 (fast "
+                "under tolerance)", mode);
   if (act != OG_ACT_NONE && act != OG_ACT_RELU)
     return fail(OG_ERR_INVALID_ARG, "og_conv2d_f32_epi: activation %d is not 0 (none) or 1 (ReLU)",
                 act);
@@ -513,9 +615,24 @@ og_status conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout, int
     return fail(OG_ERR_TOO_LARGE, "og_conv2d_f32: Cin/G*KH*KW = %lld exceeds 2^22", (long long)K);
   const bool planes = KH == 1 && KW == 1 && strideH == 1 && strideW == 1 && padTop == 0 &&
                       padLeft == 0 && padBottom == 0 && padRight == 0;
-  const Tile &t = pick(Shape{cout_g, ncols, K, G, OH * OW, KH * KW}, mode);
-  if (!grid_fits(t, cout_g, ncols, G)) return fail(OG_ERR_TOO_LARGE, "og_conv2d_f32: too many tiles");
-  og_status st = check_device();
+  og_status st = refuse_split("og_conv2d_f32", mode);
+  if (st != OG_OK) return st;
+  const Shape sh{cout_g, ncols, K, G, OH * OW, KH * KW};
+  // depthwise, grouped-direct and single-column shapes keep their fast
+  // kernels in mode 2 unless a split-k variant is forced
+  const bool own_kernel = cin_g == 1 || (G > 1 && cin_g <= 64 && cout_g <= 8 && KH == 3 && KW == 3) ||
+                          (planes && ncols == 1);
+  const int split =
+      mode == OG_MODE_FAST_MFMA
+          ? mode2_variant(sh, own_kernel ? -1.0 : estimate(choose_tile(sh, OG_MODE_FAST), sh, OG_MODE_FAST))
+          : 0;
+  if (mode == OG_MODE_FAST_MFMA && !split) mode = OG_MODE_FAST;  // the fast kernels meet the bound
+  const Tile &t = pick(sh, mode);
+  if (!split && !grid_fits(t, cout_g, ncols, G))
+    return fail(OG_ERR_TOO_LARGE, "og_conv2d_f32: too many tiles");
+  if (split && ceil_div(cout_g, 16) * ceil_div(ncols, 16) * G > kI32Max)
+    return fail(OG_ERR_TOO_LARGE, "og_conv2d_f32: too many tiles");
+  st = check_device();
   if (st != OG_OK) return st;
 
   og::Problem p{};
@@ -575,6 +692,10 @@ og_status conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout, int
   }
   const bool av = aligned16(w) && K % 4 == 0 && (cout_g * K) % 4 == 0;
   p.a_vec = av ? 1 : 0;
+  if (split) {
+    launch_splitk_conv(split, av, planes, p, t_stream);
+    return check_launch("og_conv2d_f32");
+  }
   // (the streamed form's outputs are its columns, not its rows: no epilogue there)
   const bool stream_se = planes && ncols == 1 && G == 1 && K > kStreamMinK && vt_ok(w, K, K) &&
                          !epilogue;
@@ -649,8 +770,9 @@ og_status og_set_stream(void *hip_stream) {
 void *og_get_stream(void) { return t_stream; }
 
 og_status og_set_variant(int variant) {
-  if (variant < 0 || variant > kNumVariants)
-    return fail(OG_ERR_INVALID_ARG, "og_set_variant: %d is not in 0..%d", variant, kNumVariants);
+  if (variant < 0 || variant > kLastSplitVariant)
+    return fail(OG_ERR_INVALID_ARG, "og_set_variant: %d is not in 0..%d", variant,
+                kLastSplitVariant);
   t_variant = variant;
   return ok();
 }

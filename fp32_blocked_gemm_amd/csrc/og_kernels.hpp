@@ -2083,4 +2083,217 @@ __global__ void __launch_bounds__(64) rowdot_kernel(Problem p) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Split-k matrix-core kernel: fast mode under a stated tolerance (mode 2).
+// Every output is still one sum over all of k, but the order of its terms is
+// not fixed: v_mfma_f32_16x16x4_f32 adds four products at once (its internal
+// order and roundings are not specified), and the KS waves of a block each
+// sum a contiguous range of k, their partial sums then added in wave order.
+// What is promised instead of bits is the bound |c - r| <= 4e-6 * sqrt(K) *
+// sum |a*b| + 1e-30 against the exact sum r (the sequential-summation bound
+// k*u*sum|a*b| of "Matrix product and convolution kernels", section "Fast
+// mode", in the 4e-6*sqrt(K) form of the dotLLM pull request "F32
+// outer-product tiled GEMM kernel for prefill", section "Tests"), and the
+// class of a non-finite exact result.  Results repeat from run to run: no
+// atomics, and the partial sums are added in a fixed order.
+//
+// A block of KS waves owns a (16 TM) x (16 TN) output tile of one group;
+// wave w sums the chunks of 16 taps [w*per, (w+1)*per).  Operands go from
+// memory straight into registers in the instruction's layout, with no LDS
+// staging and no barrier until the end: lane l brings A row l % 16 and B
+// column l % 16 of each 16 x 16 block for taps 4*(l/16) .. 4*(l/16) + 3 of
+// the chunk (one 16-byte load of an aligned A row), and instruction s of the
+// chunk takes tap 4*(l/16) + s: the chunk's 16 taps in a permuted order, the
+// same on both sides.  Rows, columns and taps beyond the problem read +0.
+// Register r of lane l of a block's accumulator holds row 4*(l/16) + r and
+// column l % 16 (measured on gfx950).  The partial tiles meet in LDS, where
+// each thread adds its outputs' KS partial sums in wave order and stores
+// them through the epilogue.  KH, KW: a gathered convolution's window known
+// at compile time (0: read at run time).
+// ---------------------------------------------------------------------------
+template <int KIND, bool AVEC, bool BVEC, int TM, int TN, int KS, int KH, int KW>
+__global__ void __launch_bounds__(64 * KS) splitk_kernel(Problem p) {
+  // ring of four chunks: three in flight while one is multiplied
+  constexpr int BM = 16 * TM, BN = 16 * TN, D = 4;
+  __shared__ float red[KS * BM * BN];
+  const TileCoord tc = tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n);
+  const int m0 = tc.tm * BM, n0 = tc.tn * BN;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+  const int nch = (p.K + 15) / 16;
+  const int per = (nch + KS - 1) / KS;
+  const int cb = min(nch, wave * per), ce = min(nch, cb + per);  // this wave's chunks
+
+  // A: rows m0 + 16 i + li, byte offsets from the chunk's first tap
+  const float *abase = p.A + tc.g * p.a_gstride + (int64_t)m0 * p.lda;
+  uint32_t aoff[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+    aoff[i] = m0 + 16 * i + li < p.M ? (uint32_t)(4 * ((16 * i + li) * p.lda + 4 * lg)) : kOutside;
+
+  // B: columns n0 + 16 j + li
+  constexpr bool PLANES = KIND == kBPlanes;
+  constexpr bool BT = KIND == kBMatrixT, BM_ = KIND == kBMatrix;
+  uint32_t boff[TN];   // matrix: byte offset of (tap 4 lg, column) from the chunk base;
+                       // planes: of (tap 0, column) from the group's input; past N: kOutside
+  int eimg[TN], iy0[TN], ix0[TN];  // gather: image offset and window origin of the column
+  bool bok[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int col = n0 + 16 * j + li;
+    bok[j] = col < p.N;
+    if constexpr (BM_) {
+      boff[j] = bok[j] ? (uint32_t)(4 * ((int64_t)(4 * lg) * p.ldb + 16 * j + li)) : kOutside;
+    } else if constexpr (BT) {
+      boff[j] = bok[j] ? (uint32_t)(4 * ((int64_t)(16 * j + li) * p.ldb + 4 * lg)) : kOutside;
+    } else {
+      const int cc = bok[j] ? col : 0;
+      const int img = cc / p.OHW, pix = cc - img * p.OHW;
+      if constexpr (PLANES) {
+        boff[j] = (uint32_t)(4 * (img * p.x_img + pix));
+      } else {
+        const int oy = pix / p.OW, ox = pix - oy * p.OW;
+        eimg[j] = (int)(img * p.x_img);
+        iy0[j] = oy * p.sH - p.pT;
+        ix0[j] = ox * p.sW - p.pL;
+      }
+    }
+  }
+  const float *bgrp = p.B + tc.g * p.x_grp;  // convolution: the group's input channels
+  const int khw = KH > 0 ? KH * KW : p.KHW, kw = KH > 0 ? KW : p.KW;
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float ra[D][TM][4], rb[D][TN][4];
+
+  auto load = [&](int c, auto slot) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot)::value;
+    const int k0 = c * 16;
+    const int kleft = p.K - k0;  // taps of the chunk that exist (may be <= 0: reload past the end)
+    // A: four taps of a row, 16 bytes or one by one
+    {
+      const __amdgpu_buffer_rsrc_t rs = buffer_at(abase + k0, kRange);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        if constexpr (AVEC) {
+          load4(rs, 4 * lg < kleft ? aoff[i] : kOutside, ra[S][i]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            ra[S][i][e] = load1(rs, 4 * lg + e < kleft && aoff[i] != kOutside ? aoff[i] + 4 * e : kOutside);
+        }
+      }
+    }
+    if constexpr (BM_) {
+      const __amdgpu_buffer_rsrc_t rs = buffer_at(p.B + (int64_t)k0 * p.ldb + n0, kRange);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          rb[S][j][e] = load1(rs, 4 * lg + e < kleft && bok[j] ? boff[j] + (uint32_t)(4 * e * p.ldb) : kOutside);
+    } else if constexpr (BT) {
+      const __amdgpu_buffer_rsrc_t rs = buffer_at(p.B + (int64_t)n0 * p.ldb + k0, kRange);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        if constexpr (BVEC) {
+          load4(rs, 4 * lg < kleft ? boff[j] : kOutside, rb[S][j]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            rb[S][j][e] = load1(rs, 4 * lg + e < kleft && bok[j] ? boff[j] + 4 * e : kOutside);
+        }
+      }
+    } else if constexpr (PLANES) {
+      const __amdgpu_buffer_rsrc_t rs = buffer_at(bgrp, kRange);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = k0 + 4 * lg + e;  // the input plane of the tap
+          rb[S][j][e] = load1(rs, t < p.K && bok[j] ? boff[j] + (uint32_t)(4 * t * p.HW) : kOutside);
+        }
+    } else {
+      // gather: tap t -> (channel, kernel row, kernel column), then the pixel
+      // the tap reads, +0 in the padding
+      const __amdgpu_buffer_rsrc_t rs = buffer_at(bgrp, kRange);
+      const int t0 = k0 + 4 * lg;
+      int ch = t0 / khw;
+      const int rr = t0 - ch * khw;
+      int ky = rr / kw, kx = rr - (rr / kw) * kw;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = t0 + e;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int iy = iy0[j] + ky * p.dH, ix = ix0[j] + kx * p.dW;
+          const bool in = bok[j] && t < p.K && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
+          rb[S][j][e] = load1(rs, in ? (uint32_t)(4 * (eimg[j] + ch * p.HW + iy * p.W + ix)) : kOutside);
+        }
+        if (++kx == kw) {
+          kx = 0;
+          if (++ky * kw == khw) {
+            ky = 0;
+            ++ch;
+          }
+        }
+      }
+    }
+  };
+  auto compute = [&](auto slot) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot)::value;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[S][i][e], rb[S][j][e], acc[i][j], 0, 0, 0);
+  };
+  // a ring of D chunks in flight; loads past the wave's last chunk reload it
+  // (branch-free, so each wait is for the loads of D-1 chunks earlier)
+  const int n = ce - cb;
+  if (n > 0) {
+    const int last = ce - 1;
+    static_for<D - 1>([&](auto j) __attribute__((always_inline)) { load(min(cb + (int)decltype(j)::value, last), j); });
+    const int full = n - n % D;
+    for (int c = 0; c < full; c += D) {
+      static_for<D>([&](auto j) __attribute__((always_inline)) {
+        constexpr int J = decltype(j)::value;
+        load(min(cb + c + J + D - 1, last), std::integral_constant<int, (J + D - 1) % D>{});
+        compute(j);
+      });
+    }
+    static_for<D - 1>([&](auto j) __attribute__((always_inline)) {
+      if (full + (int)decltype(j)::value < n) compute(j);
+    });
+  }
+
+  // the KS partial tiles meet in LDS: element (row, col) of wave w at
+  // red[w * BM * BN + row * BN + col]
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        red[wave * BM * BN + (16 * i + 4 * lg + r) * BN + 16 * j + li] = acc[i][j][r];
+  __syncthreads();
+  const bool epi = p.bias != nullptr || p.res != nullptr || p.act != 0;
+  for (int o = threadIdx.x; o < BM * BN; o += 64 * KS) {
+    const int row = o / BN, col = o - (o / BN) * BN;
+    const int gr = m0 + row, gc = n0 + col;
+    if (gr >= p.M || gc >= p.N) continue;
+    float v = red[o];
+#pragma unroll
+    for (int w = 1; w < KS; ++w) v += red[w * BM * BN + o];
+    float *d = out_ptr<KIND == kBMatrixT ? kBMatrix : KIND>(p, tc.g, gr, gc);
+    *d = epi ? finish(p, v, tc.g * p.M + gr, d) : canonical(v);
+  }
+}
+
 }  // namespace og

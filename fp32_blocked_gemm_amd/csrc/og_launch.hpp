@@ -423,6 +423,49 @@ void launch_nt(bool av, bool bv, const Tile &t, const og::Problem &p, hipStream_
     launch_nt_tile<MODE, false, false>(t, p, s);
 }
 
+// ---------------------------------------------------------------------------
+// Split-k kernels (OG_MODE_FAST_MFMA): variant -> (16 TM) x (16 TN) output
+// tiles with KS waves sharing k.
+// ---------------------------------------------------------------------------
+struct SplitTile {
+  int variant, tm, tn, ks;
+};
+inline constexpr SplitTile kSplitTiles[] = {
+    {21, 1, 1, 16}, {22, 1, 2, 8}, {23, 2, 2, 8}, {24, 2, 4, 4}, {25, 2, 2, 4}};
+constexpr int kFirstSplitVariant = 21, kLastSplitVariant = 25;
+inline bool is_split(int v) { return v >= kFirstSplitVariant && v <= kLastSplitVariant; }
+
+inline const SplitTile &split_tile(int v) {
+  for (const SplitTile &t : kSplitTiles)
+    if (t.variant == v) return t;
+  return kSplitTiles[0];
+}
+
+template <int KIND, bool AV, bool BV, int KH, int KW>
+void launch_splitk(int variant, og::Problem p, hipStream_t s) {
+  const SplitTile &t = split_tile(variant);
+  p.tiles_m = (int)ceil_div(p.M, 16 * t.tm);
+  p.tiles_n = (int)ceil_div(p.N, 16 * t.tn);
+  const dim3 grid((unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)p.groups),
+      block(64 * t.ks);
+  switch (t.variant) {
+    case 21: hipLaunchKernelGGL((og::splitk_kernel<KIND, AV, BV, 1, 1, 16, KH, KW>), grid, block, 0, s, p); break;
+    case 22: hipLaunchKernelGGL((og::splitk_kernel<KIND, AV, BV, 1, 2, 8, KH, KW>), grid, block, 0, s, p); break;
+    case 23: hipLaunchKernelGGL((og::splitk_kernel<KIND, AV, BV, 2, 2, 8, KH, KW>), grid, block, 0, s, p); break;
+    case 24: hipLaunchKernelGGL((og::splitk_kernel<KIND, AV, BV, 2, 4, 4, KH, KW>), grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL((og::splitk_kernel<KIND, AV, BV, 2, 2, 4, KH, KW>), grid, block, 0, s, p); break;
+  }
+}
+
+// Matrix products: B row-major (bt false) or given as its transpose (bt);
+// av / bv: 16-byte loads of A rows / of the transposed B's rows.
+// (Instantiated in og_units.hip.)
+void launch_splitk_matrix(int variant, bool av, bool bv, bool bt, const og::Problem &p,
+                          hipStream_t s);
+// Convolutions: input planes read in place (1x1, stride 1, no padding) or
+// gathered (3x3 and 1x1 windows compiled in, others read at run time).
+void launch_splitk_conv(int variant, bool av, bool planes, const og::Problem &p, hipStream_t s);
+
 // Entry points of the kernel groups, each instantiated in one compilation
 // of og_units.hip (so the groups compile in parallel) and declared extern
 // here so no other unit instantiates them.

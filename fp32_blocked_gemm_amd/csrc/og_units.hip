@@ -55,6 +55,35 @@ template struct Grouped<og::kExact, false>;
 template struct Grouped<og::kExact, true>;
 template struct Grouped<og::kFast, false>;
 template struct Grouped<og::kFast, true>;
+#elif OG_UNIT == 12
+void launch_splitk_matrix(int variant, bool av, bool bv, bool bt, const og::Problem &p,
+                          hipStream_t s) {
+  if (bt) {
+    if (av && bv) return launch_splitk<og::kBMatrixT, true, true, 0, 0>(variant, p, s);
+    if (av) return launch_splitk<og::kBMatrixT, true, false, 0, 0>(variant, p, s);
+    if (bv) return launch_splitk<og::kBMatrixT, false, true, 0, 0>(variant, p, s);
+    return launch_splitk<og::kBMatrixT, false, false, 0, 0>(variant, p, s);
+  }
+  if (av) return launch_splitk<og::kBMatrix, true, false, 0, 0>(variant, p, s);
+  return launch_splitk<og::kBMatrix, false, false, 0, 0>(variant, p, s);
+}
+#elif OG_UNIT == 13
+void launch_splitk_conv(int variant, bool av, bool planes, const og::Problem &p, hipStream_t s) {
+  if (planes) {
+    if (av) return launch_splitk<og::kBPlanes, true, false, 0, 0>(variant, p, s);
+    return launch_splitk<og::kBPlanes, false, false, 0, 0>(variant, p, s);
+  }
+  if (p.KH == 3 && p.KW == 3) {
+    if (av) return launch_splitk<og::kBGather, true, false, 3, 3>(variant, p, s);
+    return launch_splitk<og::kBGather, false, false, 3, 3>(variant, p, s);
+  }
+  if (p.KH == 1 && p.KW == 1) {
+    if (av) return launch_splitk<og::kBGather, true, false, 1, 1>(variant, p, s);
+    return launch_splitk<og::kBGather, false, false, 1, 1>(variant, p, s);
+  }
+  if (av) return launch_splitk<og::kBGather, true, false, 0, 0>(variant, p, s);
+  return launch_splitk<og::kBGather, false, false, 0, 0>(variant, p, s);
+}
 #else
 #error "unknown OG_UNIT"
 #endif

@@ -15,10 +15,11 @@
  *    accumulator and order with one fused multiply-add per term.  This
  *    library also stores a NaN result of fast mode as 0x7FC00000, so both
  *    modes have exactly one correct bit pattern per output.
- * Results do not depend on tile shapes, kernel variant, stream or device:
- * every output is computed whole by one GPU lane over all of k, and k is
- * never split ("Matrix product and convolution kernels", section "Fixed
- * chunks and thread independence").
+ * In exact and fast mode results do not depend on tile shapes, kernel
+ * variant, stream or device: every output is computed whole by one GPU lane
+ * over all of k, and k is never split ("Matrix product and convolution
+ * kernels", section "Fixed chunks and thread independence").  A third mode,
+ * OG_MODE_FAST_MFMA, trades that order for a stated error bound (below).
  *
  * Conventions of every entry point below:
  *  - All tensor pointers are DEVICE pointers owned by the caller.  The
@@ -45,8 +46,9 @@ typedef int og_status;
 
 #define OG_OK 0
 #define OG_ERR_INVALID_ARG (-1) /* a size, stride, pointer or mode is out of range           */
-#define OG_ERR_NOT_EXACT (-2)   /* exact mode asked of a kernel variant that has no exact form
-                                   ("Exact mode": reported, never approximated)              */
+#define OG_ERR_NOT_EXACT (-2)   /* exact or fast mode asked of a kernel variant that cannot
+                                   give that mode's bits (the split-k variants 21..25):
+                                   reported, never approximated ("Exact mode")             */
 #define OG_ERR_DEVICE (-3)      /* HIP error, or the current device is not gfx950            */
 #define OG_ERR_TOO_LARGE (-4)   /* a dimension does not fit the kernels' 32-bit offsets and
                                    counters: m, n or k above 2^31-1, lda or ldb above 2^22, a
@@ -55,6 +57,25 @@ typedef int og_status;
 
 #define OG_MODE_EXACT 0 /* separately rounded multiply and add ("Exact mode")              */
 #define OG_MODE_FAST 1  /* one fused multiply-add per term, same order ("Fast mode")        */
+/*
+ * OG_MODE_FAST_MFMA: fast mode under a stated tolerance instead of an order.
+ * Every output is the sum over all of k of its products, but the terms may
+ * be grouped and added in any order: k is split among the waves of a
+ * workgroup (never among workgroups) and summed four products at a time by
+ * the fp32 matrix-core instruction v_mfma_f32_16x16x4_f32, whose internal
+ * order is not specified.  For each output with exact sum r (real
+ * arithmetic), S = sum over p of |a_p * b_p| and K terms, a finite result c
+ * satisfies |c - r| <= 4e-6 * sqrt(K) * S + 1e-30 (the accuracy bound of
+ * "Matrix product and convolution kernels", section "Fast mode", k*u*S plus
+ * 1e-30 for subnormals, in the 4e-6*sqrt(K) form of the dotLLM pull request
+ * "F32 outer-product tiled GEMM kernel for prefill", section "Tests"); a
+ * result is NaN (stored as 0x7FC00000) or an infinity of the exact result's
+ * sign exactly when the exact result is.  Results repeat bit for bit from run
+ * to run and do not depend on the stream, but may change with the kernel
+ * variant.  Where the split-k kernels are not expected to be faster the
+ * fast-mode kernels run (they meet the bound).
+ */
+#define OG_MODE_FAST_MFMA 2
 
 #define OG_ACT_NONE 0 /* og_conv2d_f32_epi: no activation                                 */
 #define OG_ACT_RELU 1 /* og_conv2d_f32_epi: v > 0 ? v : +0 (a NaN stays NaN)              */
@@ -204,10 +225,16 @@ void *og_get_stream(void);
  * its group's output channels), also what 0 picks for such a shape;
  * 20 = the matrix-core kernel with 64x64 tiles of four waves of 16x64
  * outputs (v_mfma_f32_16x16x1_4b_f32).
+ * 21..25 = the split-k kernels of OG_MODE_FAST_MFMA, output tiles of
+ * (rows x columns, waves sharing k) = (16 x 16, 16), (16 x 32, 8),
+ * (32 x 32, 8), (32 x 64, 4) and (32 x 32, 4); a compute call in exact or
+ * fast mode with one of them forced returns OG_ERR_NOT_EXACT (neither
+ * mode's bits can come from them).  In OG_MODE_FAST_MFMA a forced variant
+ * 1..20 runs that fast-mode kernel.
  * Every variant runs every shape (a convolution window other than 1x1 or
  * 3x3 runs variants 10..16 as variant 6; variants 18 and 19 run shapes
  * outside their own, and any matrix product, as 0 does).  A value outside
- * 0..20 returns OG_ERR_INVALID_ARG.
+ * 0..25 returns OG_ERR_INVALID_ARG.
  */
 og_status og_set_variant(int variant);
 int og_get_variant(void);

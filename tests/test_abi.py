@@ -61,7 +61,7 @@ def test_gemm_rejects_before_launch(L, args, why):
 
 
 @pytest.mark.parametrize("args,why", [
-    ((4, 4, 4, P, 4, P, 4, P, 4, 2), "mode"),
+    ((4, 4, 4, P, 4, P, 4, P, 4, 3), "mode"),
     ((-1, 4, 4, P, 4, P, 4, P, 4, 0), "negative m"),
     ((4, 4, 5, P, 4, P, 5, P, 4, 0), "lda < k"),
     ((4, 5, 6, P, 6, P, 5, P, 5, 0), "ldb < k (B is n x k)"),
@@ -104,7 +104,7 @@ def _conv(L, N=1, Cin=4, H=5, W=5, Cout=4, G=1, KH=3, KW=3, s=(1, 1), p=(0, 0, 0
 
 
 @pytest.mark.parametrize("kw,why", [
-    (dict(mode=2), "mode"),
+    (dict(mode=3), "mode"),
     (dict(N=0), "N"), (dict(Cin=0), "Cin"), (dict(H=0), "H"), (dict(KW=0), "KW"),
     (dict(G=3), "Cin % G"), (dict(Cin=6, G=3, Cout=4), "Cout % G"),
     (dict(s=(0, 1)), "stride"), (dict(d=(1, 0)), "dilation"), (dict(p=(0, -1, 0, 0)), "pad"),
@@ -127,7 +127,7 @@ def _conv_epi(L, act=0, bias=NULL, residual=NULL, **kw):
 
 
 @pytest.mark.parametrize("kw,why", [
-    (dict(act=2), "activation"), (dict(act=-1), "activation"), (dict(act=1, mode=2), "mode"),
+    (dict(act=2), "activation"), (dict(act=-1), "activation"), (dict(act=1, mode=3), "mode"),
     (dict(bias=P, N=0), "N"), (dict(residual=P, y=NULL), "y null"),
     (dict(act=1, G=3), "Cin % G"),
 ])
@@ -150,7 +150,8 @@ def test_out_size_matches_the_formula():
 
 
 def test_variant_and_stream_state(L):
-    assert L.og_set_variant(21) == og.OG_ERR_INVALID_ARG
+    assert L.og_set_variant(26) == og.OG_ERR_INVALID_ARG
+    assert L.og_set_variant(25) == og.OG_OK
     assert L.og_set_variant(-1) == og.OG_ERR_INVALID_ARG
     assert L.og_set_variant(3) == og.OG_OK and L.og_get_variant() == 3
     assert L.og_set_variant(0) == og.OG_OK
@@ -206,3 +207,28 @@ def test_binding_row_stride_of_views():
                 Y.t()[:1]):                         # a single row of a transposed view
         with pytest.raises(ValueError):
             og._ld(bad)
+
+
+@pytest.mark.parametrize("variant", [21, 22, 23, 24, 25])
+def test_split_variants_refused_in_exact_and_fast(L, variant):
+    """A split-k variant forced in exact or fast mode is reported as
+    OG_ERR_NOT_EXACT before anything is queued ("Exact mode": an operator
+    without an exact kernel says so instead of approximating)."""
+    assert L.og_set_variant(variant) == og.OG_OK
+    try:
+        for mode in (og.EXACT, og.FAST):
+            assert L.og_gemm_f32(4, 4, 4, P, 4, P, 4, P, 4, mode) == og.OG_ERR_NOT_EXACT
+            assert b"split-k" in L.og_last_error()
+            assert L.og_gemm_nt_f32(4, 4, 4, P, 4, P, 4, P, 4, mode) == og.OG_ERR_NOT_EXACT
+            assert _conv(L, mode=mode) == og.OG_ERR_NOT_EXACT
+            assert _conv_epi(L, act=1, mode=mode) == og.OG_ERR_NOT_EXACT
+        # in mode 2 the same call passes the checks (and, with no GPU, stops at the device)
+        try:
+            import torch
+            gpu = torch.cuda.is_available()
+        except ImportError:
+            gpu = False
+        if not gpu:
+            assert L.og_gemm_f32(4, 4, 4, P, 4, P, 4, P, 4, og.FAST_MFMA) == og.OG_ERR_DEVICE
+    finally:
+        L.og_set_variant(0)
