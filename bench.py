@@ -248,7 +248,7 @@ def extras(torch, og, synth, timer, only=None):
         del g
         return ms
 
-    def gemm_entry(case, modes=("fast", "exact"), bytes_moved=None, cold_copies=0):
+    def gemm_entry(case, modes=("fast", "exact", "fast_mfma"), bytes_moved=None, cold_copies=0):
         A, B, C = gemm_workload(torch, og, case)
         # cold: each call reads its own copy of B, the copies together larger
         # than the last-level cache, so B comes from HBM
@@ -283,7 +283,7 @@ def extras(torch, og, synth, timer, only=None):
         nbytes = 4.0 * (x.size + w.size + y.numel())
         xs = [dx.clone() for _ in range(-(-cold_bytes // (4 * x.size)))] if cold_bytes else []
         ent = {"shape": repr(s), "gflop": round(2 * macs / 1e9, 4)}
-        for mode in ("fast", "exact"):
+        for mode in ("fast", "exact", "fast_mfma"):
             call = lambda xx: og.conv2d(xx, dw, stride=s.stride, pad=s.pad, dil=s.dil,
                                         groups=s.groups, mode=mode, out=y)
             ms = graph_ms([lambda: call(dx)] * 20)
@@ -335,7 +335,7 @@ def extras(torch, og, synth, timer, only=None):
         layers = conv_chain(torch, og, synth, batch)
         macs = sum(conv_macs(og, s) for s, *_ in layers)
         ent = {"layers": len(layers), "gflop": round(2 * macs / 1e9, 3)}
-        for mode in ("fast", "exact"):
+        for mode in ("fast", "exact", "fast_mfma"):
             # the 53 launches replayed from one HIP graph (no host time between
             # kernels), and issued one by one from Python
             g = timer.graph(lambda: run_chain(og, layers, mode))
@@ -357,7 +357,7 @@ def extras(torch, og, synth, timer, only=None):
         per = {}
         for (s, dx, dw, y), cnt in shapes.values():
             e = {"count": cnt, "shape": f"{s.Cin}->{s.Cout} {s.H}x{s.W} k{s.KH}x{s.KW} s{s.stride[0]}"}
-            for mode in ("fast", "exact"):
+            for mode in ("fast", "exact", "fast_mfma"):
                 call = (lambda s_, dx_, dw_, y_, m_: lambda: og.conv2d(
                     dx_, dw_, stride=s_.stride, pad=s_.pad, dil=s_.dil, groups=s_.groups, mode=m_,
                     out=y_))(s, dx, dw, y, mode)
@@ -366,7 +366,7 @@ def extras(torch, og, synth, timer, only=None):
                 del g
             per[s.name] = e
         ent["per_shape"] = per
-        for mode in ("fast", "exact"):
+        for mode in ("fast", "exact", "fast_mfma"):
             ent[mode]["sum_count_x_shape_ms"] = round(
                 sum(e["count"] * e[f"{mode}_us"] for e in per.values()) / 1e3, 4)
         if batch == 1:
@@ -441,7 +441,7 @@ def extras(torch, og, synth, timer, only=None):
         C = torch.empty((m, n), dtype=torch.float32, device="cuda")
         flops, nbytes = 2.0 * m * n * 4096, 4.0 * (m * 4096 + n * 4096 + m * n)
         ent = {"m": m, "n": n, "k": 4096, "layout": "B given as n x k (weights N x K)"}
-        for mode in ("fast", "exact"):
+        for mode in ("fast", "exact", "fast_mfma"):
             ms = graph_ms([lambda: og.gemm_nt(A, Bt, mode, out=C)] * 20)
             ent[mode] = {"us": round(ms * 1e3, 2), "gflops": round(flops / (ms * 1e-3) / 1e9, 1),
                          "frac_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4),

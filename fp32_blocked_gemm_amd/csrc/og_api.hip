@@ -306,23 +306,51 @@ bool valid_mode(int mode) {
 }
 
 // Launch time of a split-k variant: t = o + rounds * chunks * c microseconds,
-// chunks = a wave's share of the 16-tap chunks of k, rounds = the launch's
-// waves over the waves resident at once, with (cap, c, o) per variant.
+// chunks = a wave's share of k in chunks of 16 taps, rounds = the launch's
+// waves over cap (waves that run at once), with (cap, c, o) per variant and
+// shape family (0 matrix products, 1 3x3 windows, 2 other windows), fitted
+// to launches of every variant measured on the MI355X over the ResNet-50
+// layers at batch 1 and 8 and a set of products (mean errors 8 to 25 %).
 struct SplitCost {
-  int variant;
+  int variant, fam;
   double cap, c, o;
 };
 constexpr SplitCost kSplitCosts[] = {
-    {21, 4096, 0.10, 3.0}, {22, 4096, 0.10, 3.0}, {23, 4096, 0.12, 3.0},
-    {24, 4096, 0.15, 3.0}, {25, 2048, 0.20, 3.0}};
+    {21, 0, 2048, 0.4625, 3.19},
+    {21, 1, 4096, 1.1671, 2.67},
+    {21, 2, 4096, 1.5103, 2.33},
+    {22, 0, 2048, 0.5760, 2.54},
+    {22, 1, 2048, 0.7839, 3.04},
+    {22, 2, 2048, 0.8099, 2.62},
+    {23, 0, 2048, 0.7633, 3.19},
+    {23, 1, 2048, 1.1932, 3.01},
+    {23, 2, 1024, 0.8410, 2.88},
+    {24, 0, 1024, 0.6900, 4.10},
+    {24, 1, 1024, 0.9317, 5.80},
+    {24, 2, 1024, 1.0097, 4.32},
+    {25, 0, 1024, 0.4058, 3.43},
+    {25, 1, 1024, 0.5304, 4.27},
+    {25, 2, 1024, 0.5466, 3.73},
+};
+// A split-k kernel is taken only when its estimate is below this fraction
+// of the fast-mode kernel's: the two estimates' errors would otherwise pick it
+// where it is slower (measured over the same shapes, with split-k launches
+// of one round only: 8 % less summed time than fast mode and no shape
+// slower, against 12 % less for the best variant of every shape).
+constexpr double kSplitMargin = 0.85;
 
-double split_estimate(int v, const Shape &s) {
+// one_round: only launches whose waves all run at once (the model's error
+// grows with the rounds, and a split-k launch of several rounds was measured
+// slower than the fast-mode kernels where it estimated faster).
+double split_estimate(int v, const Shape &s, bool one_round) {
   const SplitTile &t = split_tile(v);
+  const int fam = s.khw == 0 ? 0 : s.khw == 9 ? 1 : 2;
   for (const SplitCost &c : kSplitCosts) {
-    if (c.variant != v) continue;
+    if (c.variant != v || c.fam != fam) continue;
     const double blocks = (double)ceil_div(s.M, 16 * t.tm) * (double)ceil_div(s.N, 16 * t.tn) *
                           (double)s.groups;
     const double chunks = (double)ceil_div(ceil_div(std::max<int64_t>(s.K, 1), 16), t.ks);
+    if (one_round && blocks * t.ks > c.cap) return 1e300;
     const double rounds = std::ceil(blocks * t.ks / c.cap);
     return c.o + rounds * chunks * c.c;
   }
@@ -338,9 +366,9 @@ int mode2_variant(const Shape &s, double fast_estimate) {
   if (is_split(t_variant)) return t_variant;
   if (t_variant != 0 || fast_estimate < 0) return 0;
   int best = 0;
-  double best_cost = fast_estimate;
-  for (const SplitCost &c : kSplitCosts) {
-    const double e = split_estimate(c.variant, s);
+  double best_cost = kSplitMargin * fast_estimate;
+  for (const SplitTile &c : kSplitTiles) {
+    const double e = split_estimate(c.variant, s, true);
     if (e < best_cost) {
       best_cost = e;
       best = c.variant;

@@ -2084,6 +2084,35 @@ __global__ void __launch_bounds__(64) rowdot_kernel(Problem p) {
 }
 
 
+// The end of a split-k block: the KS partial tiles meet in LDS (element (row,
+// col) of wave w at red[w * BM * BN + row * BN + col]); each thread adds its
+// outputs' partial sums in wave order and stores them through the epilogue.
+template <int KIND, int TM, int TN, int KS>
+__device__ __forceinline__ void splitk_finish(const Problem &p, int g, int m0, int n0, int wave,
+                                              const f32x4 (&acc)[TM][TN], float *red) {
+  constexpr int BM = 16 * TM, BN = 16 * TN;
+  const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        red[wave * BM * BN + (16 * i + 4 * lg + r) * BN + 16 * j + li] = acc[i][j][r];
+  __syncthreads();
+  const bool epi = p.bias != nullptr || p.res != nullptr || p.act != 0;
+  for (int o = threadIdx.x; o < BM * BN; o += 64 * KS) {
+    const int row = o / BN, col = o - (o / BN) * BN;
+    const int gr = m0 + row, gc = n0 + col;
+    if (gr >= p.M || gc >= p.N) continue;
+    float v = red[o];
+#pragma unroll
+    for (int w = 1; w < KS; ++w) v += red[w * BM * BN + o];
+    float *d = out_ptr<KIND == kBMatrixT ? kBMatrix : KIND>(p, g, gr, gc);
+    *d = epi ? finish(p, v, g * p.M + gr, d) : canonical(v);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Split-k matrix-core kernel: fast mode under a stated tolerance (mode 2).
 // Every output is still one sum over all of k, but the order of its terms is
@@ -2273,27 +2302,130 @@ __global__ void __launch_bounds__(64 * KS) splitk_kernel(Problem p) {
     });
   }
 
-  // the KS partial tiles meet in LDS: element (row, col) of wave w at
-  // red[w * BM * BN + row * BN + col]
+  splitk_finish<KIND, TM, TN, KS>(p, tc.g, m0, n0, wave, acc, red);
+}
+
+// ---------------------------------------------------------------------------
+// Split-k kernel for a gathered convolution whose window (KH x KW > 1) is
+// known at compile time, mode 2.  A chunk is four input channels, one per
+// lane group (l / 16), times the KH*KW window positions: instruction e of a
+// chunk multiplies window position e of the four channels, so each output
+// still receives every term once, in an order mode 2 leaves free.  A lane's
+// byte offsets for the window positions of its output pixel, image included
+// (or past the range, for a padding tap), are computed once; a chunk moves
+// only the uniform base of the input and weight buffers by four channels,
+// and a lane whose channel lies past the group's last reads past the range.  A lane's weights for a chunk are the KH*KW
+// consecutive taps of its channel (12-byte loads when KH*KW is a multiple
+// of 3).
+// ---------------------------------------------------------------------------
+template <bool AVEC, int TM, int TN, int KS, int KH, int KW>
+__global__ void __launch_bounds__(64 * KS) splitk_conv_kernel(Problem p) {
+  // ring of three chunks (a chunk is 4 * KHW taps: two in flight keep enough
+  // loads outstanding; two for the largest tiles, for registers)
+  constexpr int KHW = KH * KW, BM = 16 * TM, BN = 16 * TN, D = TM * TN >= 8 ? 2 : 3;
+  static_assert(KHW > 1 && 4 * KHW * 4 <= 256, "windows of more than one tap, offsets past kOutside");
+  __shared__ float red[KS * BM * BN];
+  const TileCoord tc = tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n);
+  const int m0 = tc.tm * BM, n0 = tc.tn * BN;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+  const int cin_g = p.K / KHW;
+  const int nch = (cin_g + 3) / 4;  // chunks of four channels
+  const int per = (nch + KS - 1) / KS;
+  const int cb = min(nch, wave * per), ce = min(nch, cb + per);
+
+  // weights: row m0 + 16 i + li, channel 4 c + lg: KHW taps at this offset
+  // from the chunk's base (rows past M: past the range)
+  const float *abase = p.A + tc.g * p.a_gstride + (int64_t)m0 * p.lda;
+  uint32_t aoff[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+    aoff[i] = m0 + 16 * i + li < p.M ? (uint32_t)(4 * ((16 * i + li) * p.lda + lg * KHW)) : kOutside;
+  // input: column n0 + 16 j + li, window position e: offset of channel lg's
+  // pixel in the column's image (or past the range) from the chunk's first
+  // channel of image 0 (the input holds fewer than 2^29 elements)
+  uint32_t boff[TN][KHW];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int col = n0 + 16 * j + li;
+    const bool ok = col < p.N;
+    const int cc = ok ? col : 0;
+    const int img = cc / p.OHW;
+    const int pix = cc - img * p.OHW;
+    const int oy = pix / p.OW, ox = pix - oy * p.OW;
+    const int iy0 = oy * p.sH - p.pT, ix0 = ox * p.sW - p.pL;
+#pragma unroll
+    for (int ky = 0; ky < KH; ++ky)
+#pragma unroll
+      for (int kx = 0; kx < KW; ++kx) {
+        const int iy = iy0 + ky * p.dH, ix = ix0 + kx * p.dW;
+        const bool in = ok && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
+        boff[j][ky * KW + kx] =
+            in ? (uint32_t)(4 * (img * p.x_img + lg * p.HW + iy * p.W + ix)) : kOutside;
+      }
+  }
+  const float *xg = p.B + tc.g * p.x_grp;
+
+  f32x4 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float ra[D][TM][KHW], rb[D][TN][KHW];
+
+  auto load = [&](int c, auto slot) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot)::value;
+    const int c0 = 4 * c;  // the chunk's first channel
+    // weights: the lane's channel c0 + lg exists, else past the range
+    const __amdgpu_buffer_rsrc_t ra_rs = buffer_at(abase + c0 * KHW, kRange);
+    const bool chok = c0 + lg < cin_g;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      // (kOutside + 4 e stays past the range and below 2^32)
+      const uint32_t o = chok ? aoff[i] : kOutside;
+      if constexpr (KHW % 3 == 0) {
+#pragma unroll
+        for (int e = 0; e < KHW; e += 3) load3(ra_rs, o + 4 * e, &ra[S][i][e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < KHW; ++e) ra[S][i][e] = load1(ra_rs, o + 4 * e);
+      }
+    }
+    // input: a lane whose channel lies past the group's last reads +0
+    const __amdgpu_buffer_rsrc_t rs = buffer_at(xg + (int64_t)c0 * p.HW, kRange);
+#pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        red[wave * BM * BN + (16 * i + 4 * lg + r) * BN + 16 * j + li] = acc[i][j][r];
-  __syncthreads();
-  const bool epi = p.bias != nullptr || p.res != nullptr || p.act != 0;
-  for (int o = threadIdx.x; o < BM * BN; o += 64 * KS) {
-    const int row = o / BN, col = o - (o / BN) * BN;
-    const int gr = m0 + row, gc = n0 + col;
-    if (gr >= p.M || gc >= p.N) continue;
-    float v = red[o];
+      for (int e = 0; e < KHW; ++e) rb[S][j][e] = load1(rs, chok ? boff[j][e] : kOutside);
+  };
+  auto compute = [&](auto slot) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot)::value;
 #pragma unroll
-    for (int w = 1; w < KS; ++w) v += red[w * BM * BN + o];
-    float *d = out_ptr<KIND == kBMatrixT ? kBMatrix : KIND>(p, tc.g, gr, gc);
-    *d = epi ? finish(p, v, tc.g * p.M + gr, d) : canonical(v);
+    for (int e = 0; e < KHW; ++e)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[S][i][e], rb[S][j][e], acc[i][j], 0, 0, 0);
+  };
+  const int n = ce - cb;
+  if (n > 0) {
+    const int last = ce - 1;
+    static_for<D - 1>([&](auto j) __attribute__((always_inline)) { load(min(cb + (int)decltype(j)::value, last), j); });
+    const int full = n - n % D;
+    for (int c = 0; c < full; c += D) {
+      static_for<D>([&](auto j) __attribute__((always_inline)) {
+        constexpr int J = decltype(j)::value;
+        load(min(cb + c + J + D - 1, last), std::integral_constant<int, (J + D - 1) % D>{});
+        compute(j);
+      });
+    }
+    static_for<D - 1>([&](auto j) __attribute__((always_inline)) {
+      if (full + (int)decltype(j)::value < n) compute(j);
+    });
   }
+  splitk_finish<kBGather, TM, TN, KS>(p, tc.g, m0, n0, wave, acc, red);
 }
 
 }  // namespace og

@@ -448,6 +448,17 @@ void launch_splitk(int variant, og::Problem p, hipStream_t s) {
   p.tiles_n = (int)ceil_div(p.N, 16 * t.tn);
   const dim3 grid((unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)p.groups),
       block(64 * t.ks);
+  if constexpr (KIND == og::kBGather && KH * KW > 1) {
+    // a window known at compile time: chunks of four channels by the window
+    switch (t.variant) {
+      case 21: hipLaunchKernelGGL((og::splitk_conv_kernel<AV, 1, 1, 16, KH, KW>), grid, block, 0, s, p); break;
+      case 22: hipLaunchKernelGGL((og::splitk_conv_kernel<AV, 1, 2, 8, KH, KW>), grid, block, 0, s, p); break;
+      case 23: hipLaunchKernelGGL((og::splitk_conv_kernel<AV, 2, 2, 8, KH, KW>), grid, block, 0, s, p); break;
+      case 24: hipLaunchKernelGGL((og::splitk_conv_kernel<AV, 2, 4, 4, KH, KW>), grid, block, 0, s, p); break;
+      default: hipLaunchKernelGGL((og::splitk_conv_kernel<AV, 2, 2, 4, KH, KW>), grid, block, 0, s, p); break;
+    }
+    return;
+  }
   switch (t.variant) {
     case 21: hipLaunchKernelGGL((og::splitk_kernel<KIND, AV, BV, 1, 1, 16, KH, KW>), grid, block, 0, s, p); break;
     case 22: hipLaunchKernelGGL((og::splitk_kernel<KIND, AV, BV, 1, 2, 8, KH, KW>), grid, block, 0, s, p); break;
