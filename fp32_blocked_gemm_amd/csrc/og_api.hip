@@ -219,7 +219,7 @@ void launch(int mode, bool av, bool bv, const Tile &t, const og::Problem &p, hip
 
 const Tile &pick(const Shape &s, int mode) {
   return t_variant == 0 || t_variant == kDepthwiseVariant || t_variant == kGroupedVariant ||
-                 is_split(t_variant)
+                 is_split(t_variant) || is_halo(t_variant)
              ? choose_tile(s, mode)
              : tile_for_variant(t_variant);
 }
@@ -724,6 +724,14 @@ og_status conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout, int
     launch_splitk_conv(split, av, planes, p, t_stream);
     return check_launch("og_conv2d_f32");
   }
+  if (is_halo(t_variant) && mode == OG_MODE_FAST && KH == 3 && KW == 3 && !planes &&
+      ceil_div(cout_g, 16) * N * ceil_div(OH * OW, 64) * G <= kI32Max) {
+    HaloPlan h;
+    if (halo_plan(p, aligned16(x), h)) {
+      launch_halo_conv(t_variant, p, h, t_stream);
+      return check_launch("og_conv2d_f32");
+    }
+  }
   // (the streamed form's outputs are its columns, not its rows: no epilogue there)
   const bool stream_se = planes && ncols == 1 && G == 1 && K > kStreamMinK && vt_ok(w, K, K) &&
                          !epilogue;
@@ -798,9 +806,9 @@ og_status og_set_stream(void *hip_stream) {
 void *og_get_stream(void) { return t_stream; }
 
 og_status og_set_variant(int variant) {
-  if (variant < 0 || variant > kLastSplitVariant)
+  if (variant < 0 || variant > kLastHaloVariant)
     return fail(OG_ERR_INVALID_ARG, "og_set_variant: %d is not in 0..%d", variant,
-                kLastSplitVariant);
+                kLastHaloVariant);
   t_variant = variant;
   return ok();
 }

@@ -83,6 +83,7 @@ struct Problem {
   int64_t y_img, y_grp;  // element strides of y between images and between groups
   int a_vec;             // A rows 16-byte aligned (A, lda and K multiples of 4 floats)
   int bh, ih, iw;        // depthwise band kernel: output rows per band, staged input rows, columns
+  int hrows;             // halo kernel: input rows staged for a tile of 64 output pixels (at most)
   // convolution epilogue (null / 0: none): bias per output channel, then the
   // activation (1: ReLU), then the residual at the output's own position
   const float *bias, *res;
@@ -100,6 +101,22 @@ __device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int
 template <int N, class F>
 __device__ __forceinline__ void static_for(F &&f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// body(t, j) for t = first .. end - 1, j = std::integral_constant of
+// (t - first) % U: a loop over whole groups of U with no branch inside its
+// body, then the last partial group, guarded.  A ring of loads whose slot
+// is (t - first) % U keeps its depth this way: with a guarded body inside
+// the loop, the compiler's count of the loads in flight at each join is the
+// smallest over its paths, and it waits for every load there.
+template <int U, class F>
+__device__ __forceinline__ void ring_loop(int first, int end, F &&body) {
+  int t0 = first;
+  for (; t0 + U <= end; t0 += U)
+    static_for<U>([&](auto j) __attribute__((always_inline)) { body(t0 + decltype(j)::value, j); });
+  static_for<U>([&](auto j) __attribute__((always_inline)) {
+    if (t0 + decltype(j)::value < end) body(t0 + decltype(j)::value, j);
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -1587,16 +1604,19 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, chain_rows(
   // the weight register holds 16 taps of a row, one per lane of a row of 16.
   // Matrix-core form (MF): each of the wave's R chains is 4 rows x 64
   // columns in one v_mfma_f32_4x4x1_16b_f32 per k: its 16 blocks of 4x4
-  // share the 4 rows; lane l gives the B value of column l and the weight of
-  // row l % 4 (four taps per 16-byte read), and holds the 4 rows of column l
-  // (register i = row i).  Each output element of the instruction is one
-  // fused multiply-add, so a chain over increasing k is fast mode (the only
-  // mode this form runs).
+  // share the 4 rows; lane l gives the B value of column l and holds the 4
+  // rows of column l (register i = row i).  The weights come through the
+  // instruction's A broadcast (cbsz 4: every block takes the A values of
+  // block abid): one register holds 16 taps of the chain's 4 rows, lane
+  // 4b + i the weight of row i at tap b, and step u of the 16 broadcasts
+  // block u.  Each output element of the instruction is one fused
+  // multiply-add, so a chain over increasing k is fast mode (the only mode
+  // this form runs).
   const int lr = lane / BN;                 // lane row of the wave (DPP form)
   const int rb0 = MF ? wave * 4 * R : wave * RW * R + lr * R;  // first row of the lane / wave
   float4 bq[RB][4];
   float wq[RB][MF ? 1 : R];
-  float4 wa[RB][MF ? R : 1][4];
+  float wa[RB][MF ? R : 1];
   auto read = [&](auto slot, int st, auto blk) __attribute__((always_inline)) {
     constexpr int S = decltype(slot)::value, B = decltype(blk)::value;
     const float4 *src = stage[st] + 4 * B * BN + cl;
@@ -1604,12 +1624,7 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, chain_rows(
     for (int i = 0; i < 4; ++i) bq[S][i] = src[i * BN];
     if constexpr (MF) {
 #pragma unroll
-      for (int c = 0; c < R; ++c) {
-        const float4 *wrow =
-            reinterpret_cast<const float4 *>(&wstage[st][(rb0 + 4 * c + (lane & 3)) * BK + 16 * B]);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) wa[S][c][q] = wrow[q];
-      }
+      for (int c = 0; c < R; ++c) wa[S][c] = wstage[st][(rb0 + 4 * c + (lane & 3)) * BK + 16 * B + (lane >> 2)];
     } else {
 #pragma unroll
       for (int r = 0; r < R; ++r) wq[S][r] = wstage[st][(rb0 + r) * BK + 16 * B + (lane & 15)];
@@ -1649,8 +1664,8 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, chain_rows(
                 constexpr int u = decltype(uq)::value;
 #pragma unroll
                 for (int c = 0; c < R; ++c) {
-                  const float a = wa[L % RB][c][u / 4][u % 4], b = bq[L % RB][u / 4][u % 4];
-                  acc4[c] = __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, acc4[c], 0, 0, 0);
+                  acc4[c] = __builtin_amdgcn_mfma_f32_4x4x1f32(wa[L % RB][c], bq[L % RB][u / 4][u % 4],
+                                                                acc4[c], 4, u, 0);
                 }
               });
             } else {
@@ -1730,6 +1745,325 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, chain_rows(
     store_all(std::false_type{});
   else
     store_all(std::true_type{});
+}
+
+// ---------------------------------------------------------------------------
+// Halo kernel: fast-mode KH x KW convolutions on the matrix cores, for
+// layers whose outputs split into enough chains of 4 output channels to fill
+// the chip (a batch of images through the middle of a convolution network).
+//
+// A block is CW waves over 64 consecutive output pixels of one image
+// (lane l: pixel l); wave w owns R chains of 4 output channels.  Per tap a
+// chain is one v_mfma_f32_4x4x1_16b_f32: its 16 blocks of 4x4 share the 4
+// rows, lane l gives the input value of its pixel's window at that tap and
+// holds the 4 outputs of its pixel (register i = output channel i of the
+// chain), each a single fused multiply-add -- so a chain over increasing k
+// is the fast mode's ordered sum.  The weights come through the
+// instruction's A broadcast (cbsz 4: every block takes the A values of
+// block abid): one register holds 16 taps of the chain's 4 rows, lane
+// 4b + i the weight of row i at tap b, and tap u of the 16 broadcasts block
+// u.  The rows are the wave's own: it streams them straight from memory
+// into its own ring of three LDS stages, two chunks ahead, and waits for
+// them by count.
+//
+// The input is staged per chunk of CC channels (CC*KHW taps in the order
+// channel, kernel row, kernel column; a multiple of 16).  For each channel
+// the block stages its halo with the padding in place: the rows its windows
+// reach, each as wide as the padded input row, the padding cells +0
+// (written once, before the first chunk) and the input's rows -- contiguous
+// in x, read with 4-byte (HV: 16-byte) loads -- stored in the middle.  A
+// window position is then always a cell of the stage, at a fixed distance
+// from the lane's first cell: a tap is one LDS read through the pointer of
+// its kernel row, the kernel column and the channel in the read's immediate
+// offset (horizontal dilation 1), and two taps of a row are one paired read.
+// LDS holds a chunk as [channel][position]; the channel's distance is added
+// to the three kernel-row pointers once per channel.  Channels past the
+// group's last are staged as +0 (their loads are out of range) and their
+// weights are made -0, so those taps add a product of -0 (fast mode's
+// padding).
+//
+// The staging never stops the matrix cores: chunk c's products run in two
+// halves, and between them each wave stores its part of chunk c+1's halo
+// (loaded during chunk c-1) into the next of three LDS buffers, issues the
+// loads of chunk c+2 and meets the others at the chunk's one barrier; the
+// second half then reads chunk c+1's first taps while it runs.  Buffer
+// (c+1) % 3 was last read in chunk c-2, which every wave finished before the
+// barrier of chunk c-1.  p.hrows: rows a tile stages at most (with its
+// padding rows); the dynamic LDS is 3 buffers of CC channels of
+// hrows * (W + pL + pR) positions.
+// ---------------------------------------------------------------------------
+template <int KH, int KW, int R, int CW, int NI, bool HV, bool AV>
+__global__ void __launch_bounds__(64 * CW) halo_kernel(Problem p) {
+  constexpr int KHW = KH * KW;
+  constexpr int CC = 16;                      // channels per chunk
+  constexpr int BK = CC * KHW, NG = BK / 16;  // taps and 16-tap groups per chunk
+  constexpr int NH = NG / 2;                  // groups before the chunk's barrier
+  constexpr int CPW = CC / CW;                // channels each wave stages
+  constexpr int VW = HV ? 4 : 1;              // floats per halo load
+  constexpr int NBUF = 3;                     // LDS buffers of the halo
+  constexpr int WROWS = 4 * R, WST = WROWS * BK;  // a wave's weight rows; floats of a weight stage
+  constexpr int NWS = 3;                          // weight stages per wave
+  constexpr int WW = AV ? 4 : 1;                  // taps per weight load
+  constexpr int NQ = WST / WW, NIW = (NQ + 63) / 64;  // weight loads per stage, per lane
+  constexpr int NL = CPW * NI;                    // halo loads per chunk, per lane
+  static_assert(BK % 16 == 0 && CC % CW == 0 && NH >= 1, "halo chunk shape");
+  // [NBUF][CC][hrows][W + pL + pR] halo, then per wave [NWS][WROWS][BK] weights
+  extern __shared__ __align__(16) float hs[];
+
+  const TileCoord tc = tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tpi = (p.OHW + 63) / 64;  // pixel tiles per image
+  const int img = tc.tn / tpi;
+  const int pbase = (tc.tn - img * tpi) * 64;
+  const int pix = pbase + lane;
+  const bool valid = pix < p.OHW;
+  const int cin_g = p.K / KHW;
+  const int wp = p.W + p.pL + p.pR;  // a staged row: the padded input row
+  const int cs = p.hrows * wp;       // floats of a staged channel
+  const int bufsz = CC * cs;         // floats of a buffer
+  // the tile's staged rows: input rows ybase .. (padding rows included), of
+  // which r0 .. r1 are the input's
+  const int oy_first = pbase / p.OW, oy_last = min(pbase + 63, p.OHW - 1) / p.OW;
+  const int ybase = oy_first * p.sH - p.pT;
+  const int r0 = max(ybase, 0);
+  const int r1 = min(oy_last * p.sH - p.pT + (KH - 1) * p.dH, p.H - 1);
+  // input floats of a channel (none when every window of the tile lies in
+  // the padding rows)
+  const int hlen = max(r1 - r0 + 1, 0) * p.W;
+
+  // this lane's first cell of each kernel row: pointers into the buffer of
+  // the chunk being run (channel 0), and into the next chunk's
+  const float *tp[KH], *tn[KH];
+  {
+    const int oy = valid ? pix / p.OW : oy_first;
+    const int ox = valid ? pix - oy * p.OW : 0;
+#pragma unroll
+    for (int ky = 0; ky < KH; ++ky)
+      tp[ky] = hs + ((oy - oy_first) * p.sH + ky * p.dH) * wp + ox * p.sW;
+  }
+  // the cell of each halo element this lane stages (the same in every chunk)
+  int hcell[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int q = VW * (lane + 64 * i), rr = q / p.W;
+    hcell[i] = (r0 - ybase + rr) * wp + p.pL + q - rr * p.W;
+  }
+  // +0 everywhere (the padding cells keep it), before the first stores
+  for (int e = threadIdx.x; e < NBUF * bufsz; e += 64 * CW) hs[e] = 0.0f;
+
+  // this wave's weight rows, streamed by the wave itself into its own ring
+  // of LDS stages ([row][tap], WW taps per lane and load, straight from
+  // memory into LDS) two chunks ahead; read back per chunk, lane 4b + i
+  // taking row i of each chain at tap b of each 16-tap group
+  const int wrow0 = tc.tm * (4 * R * CW) + wave * 4 * R;  // first row of the wave
+  const int wbase = min(wrow0, p.M - 1);
+  const __amdgpu_buffer_rsrc_t wrs =
+      buffer_at(p.A + tc.g * p.a_gstride + (int64_t)wbase * p.lda, kRange);
+  float *const wring = hs + NBUF * bufsz + wave * NWS * WST;
+  uint32_t wq[NIW];  // byte offset of the lane's taps of load n in chunk 0, or kOutside
+  int wt[NIW];       // their first tap in a chunk
+#pragma unroll
+  for (int n = 0; n < NIW; ++n) {
+    const int q = n * 64 + lane, r = q / (BK / WW);
+    wt[n] = (q - r * (BK / WW)) * WW;
+    wq[n] = q < NQ && wrow0 + r < p.M
+                ? (uint32_t)((int64_t)(wrow0 + r - wbase) * p.lda * 4 + 4 * wt[n])
+                : kOutside;
+  }
+  const int tb = lane >> 2;  // the lane's tap within a 16-tap group
+
+  const float *xg = p.B + img * p.x_img + tc.g * p.x_grp + (int64_t)r0 * p.W;  // row r0 of channel 0
+  const int nch = (cin_g + CC - 1) / CC, last = nch - 1;
+  float rb[2][CPW][NI * VW];  // halo of chunk c in slot c % 2
+  float wv[2][R][NG];         // weights of chunk c (read from its stage) in slot c % 2
+  float bv[2][16];            // B values of a group, read one group ahead
+  f32x4 acc[R];
+#pragma unroll
+  for (int c = 0; c < R; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto load_halo = [&](int c, auto slot) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot)::value;
+    c = min(c, last);
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+      const int ch = c * CC + wave * CPW + j;  // wave-uniform
+      // a channel past the group's last gets an empty range: +0
+      const __amdgpu_buffer_rsrc_t rs = buffer_at(xg + (int64_t)min(ch, cin_g - 1) * p.HW,
+                                                  ch < cin_g ? (uint32_t)(4 * hlen) : 0u);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const uint32_t off = (uint32_t)(4 * VW * (lane + 64 * i));
+        if constexpr (HV)
+          load4(rs, off, &rb[S][j][4 * i]);
+        else
+          rb[S][j][i] = load1(rs, off);
+      }
+    }
+  };
+  // chunk c's weights into stage c % NWS (loads past the last chunk reload it)
+  auto load_w = [&](int c) __attribute__((always_inline)) {
+    const int k0 = min(c, last) * BK;
+    float *dst = wring + (c % NWS) * WST;
+#pragma unroll
+    for (int n = 0; n < NIW; ++n) {
+      const uint32_t off = wq[n] != kOutside && k0 + wt[n] < p.K ? wq[n] + 4 * k0 : kOutside;
+      if (NQ % 64 == 0 || n + 1 < NIW || lane < NQ % 64) {
+        auto *to = (__attribute__((address_space(3))) void *)(dst + n * 64 * WW);
+        if constexpr (AV)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, to, 16, off, 0, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, to, 4, off, 0, 0, 0);
+      }
+    }
+  };
+  // chunk c's weights from its stage into slot S, once its loads are in:
+  // after them the wave has issued at most `later` loads (a chunk's halo
+  // and weight loads go out in a fixed order), so the wait counts exactly
+  auto read_w = [&](int c, auto slot, auto later) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot)::value, LATER = decltype(later)::value;
+    asm volatile("s_waitcnt vmcnt(%0)" ::"i"(LATER < 63 ? LATER : 63) : "memory");
+    const float *src = wring + (c % NWS) * WST + (lane & 3) * BK + tb;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) wv[S][r][gi] = src[4 * r * BK + 16 * gi];
+  };
+  auto store_halo = [&](auto slot, int buf) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot)::value;
+    float *dst = hs + buf * bufsz + wave * CPW * cs;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      if (VW * (lane + 64 * i) < hlen) {
+        // (16-byte loads: W is a multiple of 4, so the four are in one row)
+#pragma unroll
+        for (int j = 0; j < CPW; ++j)
+#pragma unroll
+          for (int e = 0; e < VW; ++e) dst[j * cs + hcell[i] + e] = rb[S][j][VW * i + e];
+      }
+  };
+  // group G of a chunk through the kernel-row pointers ptr into bv[B]
+  auto read = [&](auto grp, auto into, const float *(&ptr)[KH]) __attribute__((always_inline)) {
+    constexpr int G = decltype(grp)::value, B = decltype(into)::value;
+    static_for<16>([&](auto uq) __attribute__((always_inline)) {
+      constexpr int s = 16 * G + decltype(uq)::value;  // tap of the chunk
+      constexpr int ch = s / KHW, ky = (s % KHW) / KW, kx = s % KW;
+      bv[B][s % 16] = ptr[ky][ch * cs + kx];
+    });
+  };
+  // the products of group G of chunk c (weights in slot S, B values in bv[B])
+  auto products = [&](int c, auto grp, auto slot, auto from) __attribute__((always_inline)) {
+    constexpr int G = decltype(grp)::value, S = decltype(slot)::value, B = decltype(from)::value;
+    float w[R];
+    const uint32_t sg = pad_sign(c * BK + 16 * G + tb >= p.K);  // taps past k: -0
+#pragma unroll
+    for (int r = 0; r < R; ++r) w[r] = or_sign(wv[S][r][G], sg);
+    static_for<16>([&](auto uq) __attribute__((always_inline)) {
+      constexpr int u = decltype(uq)::value;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        acc[r] = __builtin_amdgcn_mfma_f32_4x4x1f32(w[r], bv[B][u], acc[r], 4, u, 0);
+    });
+  };
+
+  // The loads go out in the order weights c, halo c, weights c+1, halo c+1,
+  // ...; each group is fenced so the compiler keeps that order.
+  auto fence = []() __attribute__((always_inline)) { asm volatile("" ::: "memory"); };
+  // The block's barrier: the wave's own LDS stores done, then s_barrier.
+  // (__syncthreads would also wait for the weight loads into LDS, which only
+  // the wave that issued them reads, and drain their ring at every chunk.)
+  auto barrier = []() __attribute__((always_inline)) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  // prologue: chunk 0 in buffer 0 and its weights in registers, chunk 1's
+  // halo and weights in flight, chunk 0's first group read
+  load_w(0);
+  fence();
+  load_halo(0, std::integral_constant<int, 0>{});
+  fence();
+  load_w(1);
+  fence();
+  load_halo(1, std::integral_constant<int, 1>{});
+  fence();
+  barrier();  // the +0 fill before any stage is written
+  store_halo(std::integral_constant<int, 0>{}, 0);
+  read_w(0, std::integral_constant<int, 0>{}, std::integral_constant<int, 2 * NL + NIW>{});
+  barrier();
+  read(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, tp);
+
+  ring_loop<2>(0, nch, [&](int c, auto par) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;  // c % 2
+    fence();
+    load_w(c + 2);
+    fence();
+    // group G of this chunk is read into bv[(P*NG + G) % 2]
+    static_for<NH>([&](auto grp) __attribute__((always_inline)) {
+      constexpr int G = decltype(grp)::value;
+      read(std::integral_constant<int, G + 1>{}, std::integral_constant<int, (P * NG + G + 1) % 2>{}, tp);
+      __builtin_amdgcn_sched_barrier(0);
+      products(c, grp, par, std::integral_constant<int, (P * NG + G) % 2>{});
+    });
+    // chunk c+1 into buffer (c+1) % 3, chunk c+2's loads, the barrier
+    const int nb = (c + 1) % NBUF;
+    store_halo(std::integral_constant<int, 1 - P>{}, nb);
+    fence();
+    load_halo(c + 2, par);
+    fence();
+    // chunk c+1's weights: after them went halo c+1, weights c+2, halo c+2
+    read_w(c + 1, std::integral_constant<int, 1 - P>{}, std::integral_constant<int, 2 * NL + NIW>{});
+    barrier();
+    const int delta = (nb - c % NBUF) * bufsz;
+#pragma unroll
+    for (int t = 0; t < KH; ++t) tn[t] = tp[t] + delta;
+    static_for<NG - NH>([&](auto gq) __attribute__((always_inline)) {
+      constexpr int G = NH + decltype(gq)::value;
+      constexpr int BN = (P * NG + G + 1) % 2;
+      if constexpr (G + 1 < NG)
+        read(std::integral_constant<int, G + 1>{}, std::integral_constant<int, BN>{}, tp);
+      else
+        read(std::integral_constant<int, 0>{}, std::integral_constant<int, BN>{}, tn);
+      __builtin_amdgcn_sched_barrier(0);
+      products(c, std::integral_constant<int, G>{}, par, std::integral_constant<int, (P * NG + G) % 2>{});
+    });
+#pragma unroll
+    for (int t = 0; t < KH; ++t) tp[t] = tn[t];
+  });
+
+  if (valid) {
+    float *base = out_ptr<kBGather>(p, tc.g, 0, img * p.OHW + pix);
+    // one uniform test picks the store loop with or without the epilogue
+    auto store_all = [&](auto epi) __attribute__((always_inline)) {
+      constexpr bool E = decltype(epi)::value;
+      float pb[R][4], pr[R][4];
+      if constexpr (E) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = wrow0 + 4 * r + i;
+            const bool ok = row < p.M;
+            pb[r][i] = epi_bias(p, ok, tc.g * p.M + row);
+            pr[r][i] = epi_res(p, ok, base + (int64_t)(ok ? row : 0) * p.OHW);
+          }
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = wrow0 + 4 * r + i;
+          if (row < p.M) {
+            if constexpr (E)
+              base[(int64_t)row * p.OHW] = finish_with(p, acc[r][i], pb[r][i], pr[r][i]);
+            else
+              base[(int64_t)row * p.OHW] = finish<false>(p, acc[r][i], 0, base);
+          }
+        }
+    };
+    if (p.bias == nullptr && p.res == nullptr && p.act == 0)
+      store_all(std::false_type{});
+    else
+      store_all(std::true_type{});
+  }
 }
 
 // ---------------------------------------------------------------------------

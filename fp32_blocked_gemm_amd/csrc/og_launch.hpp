@@ -477,6 +477,80 @@ void launch_splitk_matrix(int variant, bool av, bool bv, bool bt, const og::Prob
 // gathered (3x3 and 1x1 windows compiled in, others read at run time).
 void launch_splitk_conv(int variant, bool av, bool planes, const og::Problem &p, hipStream_t s);
 
+// ---------------------------------------------------------------------------
+// Halo kernel (fast mode, 3x3 windows) over 64 output pixels of one image:
+// variant 26 four waves of one chain of 4 output channels (16 rows per
+// block), 27 four waves of two chains (32 rows), 28 eight waves of one chain
+// (32 rows, two waves per SIMD).
+// ---------------------------------------------------------------------------
+constexpr int kFirstHaloVariant = 26, kLastHaloVariant = 28;
+inline bool is_halo(int v) { return v >= kFirstHaloVariant && v <= kLastHaloVariant; }
+
+// The staging of a shape: rows a tile of 64 output pixels stages (the
+// output rows 64 consecutive pixels can touch, then the rows their windows
+// reach, padding rows included), halo loads per lane and channel (ni) and
+// their width (16 bytes when every staged input row starts 16-byte
+// aligned), the dynamic LDS: three buffers of 16 channels of rows x padded
+// width positions, then three weight stages of each wave's rows x 144 taps.
+// Horizontal dilation 1 and weight rows of whole 16-byte quads (Cin/G a
+// multiple of 4) only.
+struct HaloPlan {
+  int rows, ni;
+  bool hv;
+  int64_t halo_lds;  // bytes of the halo buffers
+};
+// the weight stages of the largest block (32 rows of 144 taps, three
+// stages), and the LDS a workgroup may hold on gfx950
+constexpr int64_t kHaloWeightLds = 3 * 32 * 144 * 4;
+constexpr int64_t kHaloMaxLds = 160 * 1024;
+inline bool halo_plan(const og::Problem &p, bool x_aligned16, HaloPlan &h) {
+  if (p.dW != 1 || !p.a_vec) return false;
+  const int oh = p.OHW / p.OW;
+  const int orows = std::min(oh, 63 / p.OW + 2);
+  h.rows = (orows - 1) * p.sH + (p.KH - 1) * p.dH + 1;
+  const int64_t hlen = (int64_t)std::min(h.rows, p.H) * p.W;  // input floats of a channel
+  h.hv = x_aligned16 && p.W % 4 == 0 && p.HW % 4 == 0 && p.x_img % 4 == 0 && p.x_grp % 4 == 0;
+  if (h.hv)
+    h.ni = hlen <= 256 ? 1 : hlen <= 512 ? 2 : 0;
+  else
+    h.ni = hlen <= 128 ? 2 : hlen <= 256 ? 4 : hlen <= 512 ? 8 : 0;
+  h.halo_lds = 3 * 16 * (int64_t)h.rows * (p.W + p.pL + p.pR) * 4;
+  return h.ni != 0 && h.halo_lds + kHaloWeightLds <= kHaloMaxLds;
+}
+
+template <int R, int CW, int NI, bool HV, bool AV>
+void launch_halo_shape(og::Problem p, const HaloPlan &h, hipStream_t s) {
+  const auto kernel = og::halo_kernel<3, 3, R, CW, NI, HV, AV>;
+  // more than 64 KB of dynamic LDS must be allowed per kernel, once
+  static const hipError_t allowed =
+      hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kHaloMaxLds);
+  (void)allowed;
+  p.hrows = h.rows;
+  p.tiles_m = (int)ceil_div(p.M, 4 * R * CW);
+  p.tiles_n = (int)((p.N / p.OHW) * ceil_div(p.OHW, 64));
+  const dim3 grid((unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)p.groups), block(64 * CW);
+  const size_t lds = (size_t)h.halo_lds + (size_t)CW * 3 * 4 * R * 144 * 4;
+  hipLaunchKernelGGL(kernel, grid, block, lds, s, p);
+}
+
+template <int R, int CW, bool AV>
+void launch_halo_av(og::Problem p, const HaloPlan &h, hipStream_t s) {
+  if (h.hv) {
+    if (h.ni == 1) return launch_halo_shape<R, CW, 1, true, AV>(p, h, s);
+    return launch_halo_shape<R, CW, 2, true, AV>(p, h, s);
+  }
+  if (h.ni == 2) return launch_halo_shape<R, CW, 2, false, AV>(p, h, s);
+  if (h.ni == 4) return launch_halo_shape<R, CW, 4, false, AV>(p, h, s);
+  return launch_halo_shape<R, CW, 8, false, AV>(p, h, s);
+}
+template <int R, int CW>
+void launch_halo_r(og::Problem p, const HaloPlan &h, hipStream_t s) {
+  launch_halo_av<R, CW, true>(p, h, s);
+}
+
+// A 3x3 convolution (gathered B) on variant 26, 27 or 28, planned by halo_plan.
+void launch_halo_conv(int variant, const og::Problem &p, const HaloPlan &h, hipStream_t s);
+
 // Entry points of the kernel groups, each instantiated in one compilation
 // of og_units.hip (so the groups compile in parallel) and declared extern
 // here so no other unit instantiates them.

@@ -84,6 +84,12 @@ void launch_splitk_conv(int variant, bool av, bool planes, const og::Problem &p,
   if (av) return launch_splitk<og::kBGather, true, false, 0, 0>(variant, p, s);
   return launch_splitk<og::kBGather, false, false, 0, 0>(variant, p, s);
 }
+#elif OG_UNIT == 14
+void launch_halo_conv(int variant, const og::Problem &p, const HaloPlan &h, hipStream_t s) {
+  if (variant == 26) return launch_halo_r<1, 4>(p, h, s);
+  if (variant == 27) return launch_halo_r<2, 4>(p, h, s);
+  return launch_halo_r<1, 8>(p, h, s);
+}
 #else
 #error "unknown OG_UNIT"
 #endif

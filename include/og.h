@@ -231,10 +231,17 @@ void *og_get_stream(void);
  * fast mode with one of them forced returns OG_ERR_NOT_EXACT (neither
  * mode's bits can come from them).  In OG_MODE_FAST_MFMA a forced variant
  * 1..20 runs that fast-mode kernel.
+ * 26, 27, 28 = the halo kernel (fast mode, 3x3 convolutions with horizontal
+ * dilation 1): 64 output pixels of one image per block, the input rows
+ * their windows reach staged in LDS with the padding in place, the k chain
+ * of each 4 output channels on the matrix cores (v_mfma_f32_4x4x1_16b_f32
+ * with the weights broadcast from one block); 4 waves of 4 rows, 4 waves
+ * of 2 x 4 rows and 8 waves of 4 rows.  In exact mode, and on shapes they
+ * do not take, they run as 0 does.
  * Every variant runs every shape (a convolution window other than 1x1 or
  * 3x3 runs variants 10..16 as variant 6; variants 18 and 19 run shapes
  * outside their own, and any matrix product, as 0 does).  A value outside
- * 0..25 returns OG_ERR_INVALID_ARG.
+ * 0..28 returns OG_ERR_INVALID_ARG.
  */
 og_status og_set_variant(int variant);
 int og_get_variant(void);

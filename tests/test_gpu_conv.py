@@ -123,6 +123,47 @@ def test_chain_kernel_shapes(orc, variant):
                              f"chain {variant} {s} mode {mode}")
 
 
+HALO_SHAPES = [
+    # rows past Cout, channels in three chunks (the last one short)
+    synth.ConvShape("h14", 2, 40, 14, 14, 36, 3, 3, (1, 1), (1, 1, 1, 1)),
+    # rows 16 bytes wide: 16-byte halo loads
+    synth.ConvShape("h28", 1, 20, 28, 28, 24, 3, 3, (1, 1), (1, 1, 1, 1)),
+    synth.ConvShape("h56s2", 2, 16, 56, 56, 8, 3, 3, (2, 2), (1, 1, 1, 1)),
+    # 49 pixels per image, three images
+    synth.ConvShape("h7", 3, 36, 7, 7, 70, 3, 3, (1, 1), (1, 1, 1, 1)),
+    # groups, dilation, strides on one axis, asymmetric padding
+    synth.ConvShape("hg", 2, 40, 13, 11, 40, 3, 3, (1, 2), (1, 0, 2, 1), (2, 1), 2),
+    # narrow images: a tile of 64 pixels spans many rows
+    synth.ConvShape("hw3", 1, 20, 70, 3, 12, 3, 3, (1, 1), (1, 1, 1, 1)),
+    synth.ConvShape("hw1", 1, 12, 100, 1, 5, 3, 3, (1, 1), (1, 1, 1, 1)),
+    # pads of 2, four channels
+    synth.ConvShape("hp2", 2, 4, 9, 10, 19, 3, 3, (1, 1), (2, 2, 2, 2)),
+    # a halo too wide to stage, horizontal dilation 2, weight rows not of
+    # whole quads (Cin/G = 9) and a 1x1 window: the automatic choice runs
+    synth.ConvShape("hwide", 1, 8, 9, 300, 6, 3, 3, (1, 1), (1, 1, 1, 1)),
+    synth.ConvShape("hdw2", 1, 16, 9, 12, 20, 3, 3, (1, 1), (1, 2, 1, 2), (1, 2)),
+    synth.ConvShape("hodd", 1, 9, 12, 10, 7, 3, 3, (1, 1), (1, 1, 1, 1)),
+    synth.ConvShape("h1x1", 2, 20, 9, 7, 30, 1, 1),
+]
+
+
+@pytest.mark.parametrize("variant", [26, 27, 28])
+def test_halo_kernel_shapes(orc, variant):
+    """The halo kernel (fast mode, 3x3 windows) bit for bit against the
+    oracle; in exact mode, and on shapes it does not take, the variant runs
+    the automatic choice."""
+    rng = np.random.default_rng(500 + variant)
+    og.set_variant(variant)
+    for s in HALO_SHAPES:
+        x, w = synth.conv_inputs(s, int(rng.integers(1 << 30)), "uniform")
+        x = _with_specials(x, rng, 0.01)
+        w = _with_specials(w, rng, 0.01)
+        for mode in MODES:
+            say(f"conv halo variant {variant} {s} mode {mode}")
+            assert_same_bits(_gpu_conv(x, w, s, mode), _oracle(orc, x, w, s, mode),
+                             f"halo {variant} {s} mode {mode}")
+
+
 GROUPED_SHAPES = [
     # the grouped, dilated, strided workload's own form, smaller
     synth.ConvShape("g8x8", 2, 64, 20, 18, 64, 3, 3, (2, 2), (2, 2, 2, 2), (2, 2), 8),
