@@ -379,6 +379,28 @@ int mode2_variant(const Shape &s, double fast_estimate) {
 
 // A split-k variant forced in exact or fast mode: refused (neither mode's
 // bits can come from it).
+// The halo kernel's time (variants 26 and 27, fast mode), fitted to the
+// ResNet-50 3x3 layers at batch 1 to 16: a round of blocks (one per
+// compute unit) takes c ns per tap of k plus d us; where the LDS holds two
+// or more blocks per compute unit, rounds overlap by kHaloOverlap.  (Within
+// 10 % of the measured times of the stride-1 layers; the stride-2 layers
+// stage taller halos and run up to 30 % over, where the kernel is not the
+// faster one.)
+struct HaloCost {
+  int variant, rows;
+  double c, d;
+};
+constexpr HaloCost kHaloCosts[] = {{26, 16, 10.4, 5.5}, {27, 32, 13.8, 5.6}};
+constexpr double kHaloOverlap = 1.25;
+
+double halo_estimate(const HaloCost &hc, const Shape &s, int64_t images, int64_t halo_lds) {
+  const int64_t blocks = ceil_div(s.M, hc.rows) * images * ceil_div(s.ohw, 64) * s.groups;
+  const int64_t lds = halo_lds + (int64_t)hc.rows * 3 * 144 * 4;  // halo and weight stages
+  const double x = (double)blocks / 256.0;
+  const double rounds = kHaloMaxLds / lds >= 2 ? std::max(1.0, x / kHaloOverlap) : std::ceil(x);
+  return (hc.c * 1e-3 * (double)s.K + hc.d) * rounds;
+}
+
 og_status refuse_split(const char *what, int mode) {
   if (mode != OG_MODE_FAST_MFMA && is_split(t_variant))
     return fail(OG_ERR_NOT_EXACT, "%s: variant %d has no %s form (split-k kernels run only in "
@@ -650,19 +672,6 @@ og_status conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout, int
   // kernels in mode 2 unless a split-k variant is forced
   const bool own_kernel = cin_g == 1 || (G > 1 && cin_g <= 64 && cout_g <= 8 && KH == 3 && KW == 3) ||
                           (planes && ncols == 1);
-  const int split =
-      mode == OG_MODE_FAST_MFMA
-          ? mode2_variant(sh, own_kernel ? -1.0 : estimate(choose_tile(sh, OG_MODE_FAST), sh, OG_MODE_FAST))
-          : 0;
-  if (mode == OG_MODE_FAST_MFMA && !split) mode = OG_MODE_FAST;  // the fast kernels meet the bound
-  const Tile &t = pick(sh, mode);
-  if (!split && !grid_fits(t, cout_g, ncols, G))
-    return fail(OG_ERR_TOO_LARGE, "og_conv2d_f32: too many tiles");
-  if (split && ceil_div(cout_g, 16) * ceil_div(ncols, 16) * G > kI32Max)
-    return fail(OG_ERR_TOO_LARGE, "og_conv2d_f32: too many tiles");
-  st = check_device();
-  if (st != OG_OK) return st;
-
   og::Problem p{};
   p.bias = bias;
   p.res = residual;
@@ -695,6 +704,35 @@ og_status conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout, int
   p.x_grp = cin_g * H * W;
   p.y_img = Cout * OH * OW;
   p.y_grp = cout_g * OH * OW;
+  const bool av = aligned16(w) && K % 4 == 0 && (cout_g * K) % 4 == 0;
+  p.a_vec = av ? 1 : 0;
+  // the halo kernel (fast mode, 3x3 windows): its staging plan and the
+  // variant of the lower estimate, where it takes the shape
+  HaloPlan hplan{};
+  int halo_v = 0;
+  double halo_est = 1e300;
+  if (KH == 3 && KW == 3 && !planes && !own_kernel && halo_plan(p, aligned16(x), hplan) &&
+      ceil_div(cout_g, 16) * N * ceil_div(OH * OW, 64) * G <= kI32Max) {
+    for (const HaloCost &hc : kHaloCosts) {
+      const double e = halo_estimate(hc, sh, N, hplan.halo_lds);
+      if (e < halo_est) halo_est = e, halo_v = hc.variant;
+    }
+  }
+  const int split =
+      mode == OG_MODE_FAST_MFMA
+          ? mode2_variant(sh, own_kernel ? -1.0
+                                         : std::min(estimate(choose_tile(sh, OG_MODE_FAST), sh, OG_MODE_FAST),
+                                                    halo_est))
+          : 0;
+  if (mode == OG_MODE_FAST_MFMA && !split) mode = OG_MODE_FAST;  // the fast kernels meet the bound
+  const Tile &t = pick(sh, mode);
+  if (!split && !grid_fits(t, cout_g, ncols, G))
+    return fail(OG_ERR_TOO_LARGE, "og_conv2d_f32: too many tiles");
+  if (split && ceil_div(cout_g, 16) * ceil_div(ncols, 16) * G > kI32Max)
+    return fail(OG_ERR_TOO_LARGE, "og_conv2d_f32: too many tiles");
+  st = check_device();
+  if (st != OG_OK) return st;
+
   if (cin_g == 1 && (t_variant == 0 || t_variant == kDepthwiseVariant)) {
     // depthwise: one wave per 64 * per_lane output pixels of an (image, output channel) plane
     const int per_lane = dw_outputs_per_lane(N * Cout, OH * OW, KH, KW, strideH, strideW);
@@ -718,17 +756,17 @@ og_status conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout, int
     by_mode_epi<Grouped>(mode, epilogue, p, t_stream);
     return check_launch("og_conv2d_f32");
   }
-  const bool av = aligned16(w) && K % 4 == 0 && (cout_g * K) % 4 == 0;
-  p.a_vec = av ? 1 : 0;
   if (split) {
     launch_splitk_conv(split, av, planes, p, t_stream);
     return check_launch("og_conv2d_f32");
   }
-  if (is_halo(t_variant) && mode == OG_MODE_FAST && KH == 3 && KW == 3 && !planes &&
-      ceil_div(cout_g, 16) * N * ceil_div(OH * OW, 64) * G <= kI32Max) {
-    HaloPlan h;
-    if (halo_plan(p, aligned16(x), h)) {
-      launch_halo_conv(t_variant, p, h, t_stream);
+  // the halo kernel: forced, or chosen where its estimate is below the pick's
+  if (halo_v != 0 && mode == OG_MODE_FAST) {
+    const int hv = is_halo(t_variant) ? t_variant
+                   : t_variant == 0 && halo_est < estimate(t, sh, mode) ? halo_v
+                                                                         : 0;
+    if (hv != 0) {
+      launch_halo_conv(hv, p, hplan, t_stream);
       return check_launch("og_conv2d_f32");
     }
   }
