@@ -219,7 +219,7 @@ void launch(int mode, bool av, bool bv, const Tile &t, const og::Problem &p, hip
 
 const Tile &pick(const Shape &s, int mode) {
   return t_variant == 0 || t_variant == kDepthwiseVariant || t_variant == kGroupedVariant ||
-                 is_split(t_variant) || is_halo(t_variant)
+                 is_split(t_variant) || is_halo(t_variant) || is_panel(t_variant)
              ? choose_tile(s, mode)
              : tile_for_variant(t_variant);
 }
@@ -401,6 +401,30 @@ double halo_estimate(const HaloCost &hc, const Shape &s, int64_t images, int64_t
   return (hc.c * 1e-3 * (double)s.K + hc.d) * rounds;
 }
 
+// The panel kernel's time (variants 29 and 30, fast mode), fitted to the
+// ResNet-50 1x1 layers at batch 1 to 16 and ten products: (c ns per step
+// of k + d us) per round of cap blocks, plus o us; mean error 10 % there
+// and 9 % on held-out shapes (the MobileNetV3-large 1x1 layers at batch 1
+// and 8, twelve seeded random products).
+struct PanelCost {
+  int variant, rows;
+  double cap, c, d, o;
+};
+constexpr PanelCost kPanelCosts[] = {{29, 16, 320, 10.83, 1.38, 2.30}, {30, 32, 320, 16.52, 1.59, 2.23}};
+
+// The lower of the two estimates for a product (images = 0) or a 1x1
+// convolution of `images` images with ohw output pixels each; its variant.
+double panel_estimate(const Shape &s, int64_t images, int *variant) {
+  double best = 1e300;
+  for (const PanelCost &pc : kPanelCosts) {
+    const int64_t cols = images > 0 ? images * ceil_div(s.ohw, 64) : ceil_div(s.N, 64);
+    const double x = (double)(ceil_div(s.M, pc.rows) * cols * s.groups) / pc.cap;
+    const double e = (pc.c * 1e-3 * (double)s.K + pc.d) * std::max(1.0, x) + pc.o;
+    if (e < best) best = e, *variant = pc.variant;
+  }
+  return best;
+}
+
 og_status refuse_split(const char *what, int mode) {
   if (mode != OG_MODE_FAST_MFMA && is_split(t_variant))
     return fail(OG_ERR_NOT_EXACT, "%s: variant %d has no %s form (split-k kernels run only in "
@@ -437,9 +461,13 @@ og_status og_gemm_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_t l
   og_status st = refuse_split("og_gemm_f32", mode);
   if (st != OG_OK) return st;
   const Shape sh{m, n, k, 1, 0, 0};
+  // the panel kernel (fast mode): its variant of the lower estimate
+  int panel_v = 0;
+  const double panel_est =
+      ceil_div(m, 16) * ceil_div(n, 64) <= kI32Max ? panel_estimate(sh, 0, &panel_v) : 1e300;
   const int split =
       mode == OG_MODE_FAST_MFMA
-          ? mode2_variant(sh, estimate(choose_tile(sh, OG_MODE_FAST), sh, OG_MODE_FAST))
+          ? mode2_variant(sh, std::min(estimate(choose_tile(sh, OG_MODE_FAST), sh, OG_MODE_FAST), panel_est))
           : 0;
   if (mode == OG_MODE_FAST_MFMA && !split) mode = OG_MODE_FAST;  // the fast kernels meet the bound
   const Tile &t = pick(sh, mode);
@@ -465,6 +493,17 @@ og_status og_gemm_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_t l
   if (split) {
     launch_splitk_matrix(split, av, false, false, p, t_stream);
     return check_launch("og_gemm_f32");
+  }
+  // the panel kernel: forced, or chosen where its estimate is below the pick's
+  if (panel_v != 0 && mode == OG_MODE_FAST && (n > 1 || is_panel(t_variant))) {
+    const int pv = is_panel(t_variant) ? t_variant
+                   : t_variant == 0 && panel_est < estimate(t, sh, mode) ? panel_v
+                                                                         : 0;
+    if (pv != 0) {
+      const bool bv = aligned16(B) && ldb % 4 == 0 && n % 4 == 0;
+      launch_panel(pv, og::kBMatrix, bv, av, p, t_stream);
+      return check_launch("og_gemm_f32");
+    }
   }
   const bool stream_col = n == 1 && k > kStreamMinK && ldb == 1 && ldc == 1 && vt_ok(A, lda, k);
   if (n == 1 && !stream_col && k <= kRowdotMaxK && t_variant == 0 && rowdot_fits(m, lda, ldb, 1)) {
@@ -718,11 +757,16 @@ og_status conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout, int
       if (e < halo_est) halo_est = e, halo_v = hc.variant;
     }
   }
+  // the panel kernel (fast mode, 1x1 windows): its variant of the lower estimate
+  int panel_v = 0;
+  double panel_est = 1e300;
+  if (KH == 1 && KW == 1 && !own_kernel && ceil_div(cout_g, 16) * N * ceil_div(OH * OW, 64) * G <= kI32Max)
+    panel_est = panel_estimate(sh, N, &panel_v);
   const int split =
       mode == OG_MODE_FAST_MFMA
           ? mode2_variant(sh, own_kernel ? -1.0
-                                         : std::min(estimate(choose_tile(sh, OG_MODE_FAST), sh, OG_MODE_FAST),
-                                                    halo_est))
+                                         : std::min({estimate(choose_tile(sh, OG_MODE_FAST), sh, OG_MODE_FAST),
+                                                     halo_est, panel_est}))
           : 0;
   if (mode == OG_MODE_FAST_MFMA && !split) mode = OG_MODE_FAST;  // the fast kernels meet the bound
   const Tile &t = pick(sh, mode);
@@ -767,6 +811,17 @@ og_status conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout, int
                                                                          : 0;
     if (hv != 0) {
       launch_halo_conv(hv, p, hplan, t_stream);
+      return check_launch("og_conv2d_f32");
+    }
+  }
+  // the panel kernel: forced, or chosen where its estimate is below the pick's
+  if (panel_v != 0 && mode == OG_MODE_FAST) {
+    const int pv = is_panel(t_variant) ? t_variant
+                   : t_variant == 0 && panel_est < estimate(t, sh, mode) ? panel_v
+                                                                         : 0;
+    if (pv != 0) {
+      const bool bv = planes && aligned16(x) && (H * W) % 4 == 0 && p.x_img % 4 == 0 && p.x_grp % 4 == 0;
+      launch_panel(pv, planes ? og::kBPlanes : og::kBGather, bv, av, p, t_stream);
       return check_launch("og_conv2d_f32");
     }
   }
@@ -844,9 +899,9 @@ og_status og_set_stream(void *hip_stream) {
 void *og_get_stream(void) { return t_stream; }
 
 og_status og_set_variant(int variant) {
-  if (variant < 0 || variant > kLastHaloVariant)
+  if (variant < 0 || variant > kLastPanelVariant)
     return fail(OG_ERR_INVALID_ARG, "og_set_variant: %d is not in 0..%d", variant,
-                kLastHaloVariant);
+                kLastPanelVariant);
   t_variant = variant;
   return ok();
 }

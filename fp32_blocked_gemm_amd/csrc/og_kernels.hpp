@@ -1923,7 +1923,15 @@ __global__ void __launch_bounds__(64 * CW) halo_kernel(Problem p) {
   auto read_w = [&](int c, auto slot, auto later) __attribute__((always_inline)) {
     constexpr int S = decltype(slot)::value, LATER = decltype(later)::value;
     asm volatile("s_waitcnt vmcnt(%0)" ::"i"(LATER < 63 ? LATER : 63) : "memory");
-    const float *src = wring + (c % NWS) * WST + (lane & 3) * BK + tb;
+    float *stg = wring + (c % NWS) * WST;
+    // in a chunk running past k (the last one at most) the taps past k get
+    // -0 weights, written over the wave's own stage (its LDS operations run
+    // in order)
+    if ((c + 1) * BK > p.K) {
+      for (int e = lane; e < WST; e += 64)
+        if (c * BK + e % BK >= p.K) stg[e] = -0.0f;
+    }
+    const float *src = stg + (lane & 3) * BK + tb;
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -1952,17 +1960,13 @@ __global__ void __launch_bounds__(64 * CW) halo_kernel(Problem p) {
     });
   };
   // the products of group G of chunk c (weights in slot S, B values in bv[B])
-  auto products = [&](int c, auto grp, auto slot, auto from) __attribute__((always_inline)) {
+  auto products = [&](int, auto grp, auto slot, auto from) __attribute__((always_inline)) {
     constexpr int G = decltype(grp)::value, S = decltype(slot)::value, B = decltype(from)::value;
-    float w[R];
-    const uint32_t sg = pad_sign(c * BK + 16 * G + tb >= p.K);  // taps past k: -0
-#pragma unroll
-    for (int r = 0; r < R; ++r) w[r] = or_sign(wv[S][r][G], sg);
     static_for<16>([&](auto uq) __attribute__((always_inline)) {
       constexpr int u = decltype(uq)::value;
 #pragma unroll
       for (int r = 0; r < R; ++r)
-        acc[r] = __builtin_amdgcn_mfma_f32_4x4x1f32(w[r], bv[B][u], acc[r], 4, u, 0);
+        acc[r] = __builtin_amdgcn_mfma_f32_4x4x1f32(wv[S][r][G], bv[B][u], acc[r], 4, u, 0);
     });
   };
 
@@ -2056,6 +2060,268 @@ __global__ void __launch_bounds__(64 * CW) halo_kernel(Problem p) {
               base[(int64_t)row * p.OHW] = finish_with(p, acc[r][i], pb[r][i], pr[r][i]);
             else
               base[(int64_t)row * p.OHW] = finish<false>(p, acc[r][i], 0, base);
+          }
+        }
+    };
+    if (p.bias == nullptr && p.res == nullptr && p.act == 0)
+      store_all(std::false_type{});
+    else
+      store_all(std::true_type{});
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Panel kernel: fast-mode products whose B rows are read 64 columns at a
+// time -- matrix products (KIND kBMatrix), 1x1 convolutions read in place
+// (kBPlanes) or through a stride and padding (kBGather) -- on the matrix
+// cores, for shapes whose outputs split into enough chains of 4 rows to
+// fill the chip.  The chains are the halo kernel's: CW waves over 64
+// columns (a convolution's: 64 consecutive output pixels of one image),
+// wave w with R chains of 4 rows, one v_mfma_f32_4x4x1_16b_f32 per k step
+// and chain, the weights through the A broadcast from the wave's own ring
+// of LDS stages.
+//
+// B is staged in chunks of CC rows (k steps) x 64 columns, straight
+// from memory into LDS by the load itself ([row][column]): with BV, 16
+// bytes per lane (four columns; a load covers four rows), else 4 bytes (a
+// load covers one row, each lane its own column, its own input pixel
+// through the stride and padding, or an offset past the buffer for a
+// padding tap or a column past the end: +0).  Rows past k are +0 and
+// their weights -0 (fast mode's padding).  A chunk's loads are shared by
+// the waves, a quarter each, so it is in LDS once every wave's own loads
+// are (each waits for its loads by count) and the block has met at a
+// barrier.  That barrier sits before the last 16 steps of each chunk's
+// products: at it every wave has finished the chunk before, whose stage is
+// then reloaded with the chunk NS-1 ahead, so the loads have NS-2 chunks of
+// products to arrive in.  (A barrier stops a wave's matrix cores for some
+// 200 cycles, hidden only by another block's waves on the same compute
+// unit: chunks of 64 steps keep it to about a sixth of the time where one
+// block holds a compute unit; chunks of 32 need less LDS, so that two
+// blocks share one.)
+// ---------------------------------------------------------------------------
+template <int KIND, int R, int CW, int CC, int NS, bool BV, bool AV>
+__global__ void __launch_bounds__(64 * CW) panel_kernel(Problem p) {
+  // CC: k steps per chunk; NS: stages (B and weights)
+  constexpr int NG = CC / 16;             // 16-step groups per chunk
+  constexpr int BST = CC * 64;            // floats of a B stage
+  constexpr int NBL = BV ? CC / 4 / CW : CC / CW;  // B loads per wave and chunk
+  constexpr int WROWS = 4 * R, WST = WROWS * CC;    // a wave's weight rows; floats of its stage
+  constexpr int WW = AV ? 4 : 1;                    // weight taps per lane and load
+  constexpr int NQ = WST / WW, NIW = (NQ + 63) / 64;  // weight loads per wave and chunk
+  constexpr int L = NBL + NIW;                      // loads per wave and chunk
+  constexpr int LATER = (NS - 3) * L;               // loads issued after a chunk's, at its wait
+  static_assert(CC % 16 == 0 && NS >= 3, "panel chunk shape");
+  static_assert(NBL >= 1 && (BV ? (CC / 4) % CW == 0 : CC % CW == 0), "panel chunk shape");
+  static_assert((NS - 2) * L <= 63, "load count");
+  // [NS][CC][64] B, then per wave [NS][WROWS][CC] weights
+  extern __shared__ __align__(16) float ss[];
+
+  const TileCoord tc = tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  constexpr bool CONV = KIND != kBMatrix;
+  // the tile's columns
+  int img = 0, col0;
+  if constexpr (CONV) {
+    const int tpi = (p.OHW + 63) / 64;
+    img = tc.tn / tpi;
+    col0 = (tc.tn - img * tpi) * 64;
+  } else {
+    col0 = tc.tn * 64;
+  }
+  const int ncols = CONV ? p.OHW : p.N;
+  const bool valid = col0 + lane < ncols;
+  // B: rows of the chunk at bbase + row * rstride (floats)
+  const float *bbase = CONV ? p.B + img * p.x_img + tc.g * p.x_grp : p.B;
+  const int64_t rstride = CONV ? (int64_t)p.HW : p.ldb;
+  uint32_t boff[BV ? NBL : 1];  // BV: byte offset of each load's quad within the chunk (or kOutside)
+  int brow[BV ? NBL : 1];       // BV: its row within the chunk
+  uint32_t coff = kOutside;     // 4-byte loads: the lane's column within a row
+  const uint32_t rstep = (uint32_t)(rstride * 4);  // bytes between rows
+  if constexpr (BV) {
+#pragma unroll
+    for (int j = 0; j < NBL; ++j) {
+      const int qd = (wave * NBL + j) * 64 + lane;  // quad of the chunk: row qd / 16, columns 4 (qd % 16)
+      brow[j] = qd / 16;
+      const int c = col0 + 4 * (qd % 16);
+      boff[j] = c < ncols ? (uint32_t)(((int64_t)brow[j] * rstride + c) * 4) : kOutside;
+    }
+  } else if constexpr (KIND == kBGather) {
+    const int oy = valid ? (col0 + lane) / p.OW : 0;
+    const int ox = valid ? col0 + lane - oy * p.OW : 0;
+    const int iy = oy * p.sH - p.pT, ix = ox * p.sW - p.pL;
+    if (valid && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W)
+      coff = (uint32_t)(4 * (iy * p.W + ix));
+  } else {
+    if (valid) coff = (uint32_t)(4 * (col0 + lane));
+  }
+  const bool col_in = coff != kOutside;
+
+  // the wave's weight rows, as in the halo kernel
+  const int wrow0 = tc.tm * (4 * R * CW) + wave * 4 * R;
+  const int wbase = min(wrow0, p.M - 1);
+  const __amdgpu_buffer_rsrc_t wrs =
+      buffer_at(p.A + tc.g * p.a_gstride + (int64_t)wbase * p.lda, kRange);
+  float *const wring = ss + NS * BST + wave * NS * WST;
+  uint32_t wq[NIW];
+  int wt[NIW];
+#pragma unroll
+  for (int n = 0; n < NIW; ++n) {
+    const int q = n * 64 + lane, r = q / (CC / WW);
+    wt[n] = (q - r * (CC / WW)) * WW;
+    wq[n] = q < NQ && wrow0 + r < p.M
+                ? (uint32_t)((int64_t)(wrow0 + r - wbase) * p.lda * 4 + 4 * wt[n])
+                : kOutside;
+  }
+  const int tb = lane >> 2;  // the lane's tap within a 16-step group
+  const int nch = (p.K + CC - 1) / CC, last = nch - 1;
+  typedef __attribute__((address_space(3))) void lds_t;
+
+  // chunk c's B (this wave's share) and weights into stage c % NS
+  auto load = [&](int c) __attribute__((always_inline)) {
+    const int k0 = min(c, last) * CC, st = c % NS;
+    if constexpr (BV) {
+      const __amdgpu_buffer_rsrc_t rs = buffer_at(bbase + (int64_t)k0 * rstride, kRange);
+#pragma unroll
+      for (int j = 0; j < NBL; ++j) {
+        const uint32_t off = k0 + brow[j] < p.K ? boff[j] : kOutside;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_t *)(ss + st * BST + (wave * NBL + j) * 256),
+                                                 16, off, 0, 0, 0);
+      }
+    } else {
+      // the wave's rows from row0 of the chunk: the lane's offset advances by
+      // one row per load (carried in one register; used only where the
+      // lane's column is inside, so it never wraps into range)
+      const int row0 = wave * NBL, rows_left = p.K - k0 - row0;  // uniform
+      const __amdgpu_buffer_rsrc_t rs = buffer_at(bbase + ((int64_t)k0 + row0) * rstride, kRange);
+      uint32_t vo = coff;
+#pragma unroll
+      for (int j = 0; j < NBL; ++j) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_t *)(ss + st * BST + (row0 + j) * 64), 4,
+                                                 col_in && j < rows_left ? vo : kOutside, 0, 0, 0);
+        vo += rstep;
+      }
+    }
+    float *dst = wring + st * WST;
+#pragma unroll
+    for (int n = 0; n < NIW; ++n) {
+      const uint32_t off = wq[n] != kOutside && k0 + wt[n] < p.K ? wq[n] + 4 * k0 : kOutside;
+      if (NQ % 64 == 0 || n + 1 < NIW || lane < NQ % 64) {
+        auto *to = (lds_t *)(dst + n * 64 * WW);
+        if constexpr (AV)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, to, 16, off, 0, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, to, 4, off, 0, 0, 0);
+      }
+    }
+  };
+  auto fence = []() __attribute__((always_inline)) { asm volatile("" ::: "memory"); };
+  auto wait_and_meet = [&]() __attribute__((always_inline)) {
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(LATER) : "memory");
+  };
+
+  float wv[2][R][NG];  // weights of chunk c in slot c % 2
+  float bv[2][16];     // B values of a group, read one group ahead
+  f32x4 acc[R];
+#pragma unroll
+  for (int c = 0; c < R; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // chunk c's weights into slot S; in a chunk running past k (the last one
+  // at most) the wave first writes -0 over its stage's steps past k (its own
+  // stage: its LDS operations run in order, no wait)
+  auto read_w = [&](int c, auto slot) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot)::value;
+    float *stg = wring + (c % NS) * WST;
+    if ((c + 1) * CC > p.K) {
+      for (int e = lane; e < WST; e += 64)
+        if (c * CC + e % CC >= p.K) stg[e] = -0.0f;
+    }
+    const float *src = stg + (lane & 3) * CC + tb;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int g = 0; g < NG; ++g) wv[S][r][g] = src[4 * r * CC + 16 * g];
+  };
+  auto read = [&](int c, auto grp, auto into) __attribute__((always_inline)) {
+    constexpr int G = decltype(grp)::value, B = decltype(into)::value;
+    const float *src = ss + (c % NS) * BST + lane;
+    static_for<16>([&](auto uq) __attribute__((always_inline)) {
+      constexpr int u = decltype(uq)::value;
+      bv[B][u] = src[(16 * G + u) * 64];
+    });
+  };
+  auto products = [&](auto grp, auto slot, auto from) __attribute__((always_inline)) {
+    constexpr int G = decltype(grp)::value, S = decltype(slot)::value, B = decltype(from)::value;
+    static_for<16>([&](auto uq) __attribute__((always_inline)) {
+      constexpr int u = decltype(uq)::value;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        acc[r] = __builtin_amdgcn_mfma_f32_4x4x1f32(wv[S][r][G], bv[B][u], acc[r], 4, u, 0);
+    });
+  };
+
+  // k = 0: no chunk, nothing to load (chunk indices below would be negative)
+  if (nch > 0) {
+  // prologue: chunks 0 .. NS-2 in flight, then chunk 0 in
+#pragma unroll
+  for (int c = 0; c < NS - 1; ++c) {
+    fence();
+    load(c);
+  }
+  fence();
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"((NS - 2) * L) : "memory");
+  read_w(0, std::integral_constant<int, 0>{});
+  read(0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+
+  // group G of chunk c is read into bv[(P*NG + G) % 2], P = c % 2
+  ring_loop<2>(0, nch, [&](int c, auto par) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;
+    static_for<NG - 1>([&](auto grp) __attribute__((always_inline)) {
+      constexpr int G = decltype(grp)::value;
+      read(c, std::integral_constant<int, G + 1>{}, std::integral_constant<int, (P * NG + G + 1) % 2>{});
+      __builtin_amdgcn_sched_barrier(0);
+      products(grp, par, std::integral_constant<int, (P * NG + G) % 2>{});
+    });
+    // chunk c+1: this wave's loads of it in (after them went chunks
+    // c+2 .. c+NS-2), then the block's barrier; chunk c-1's stage is free
+    fence();
+    wait_and_meet();
+    load(c + NS - 1);
+    fence();
+    read_w(c + 1, std::integral_constant<int, 1 - P>{});
+    constexpr int G = NG - 1;
+    read(c + 1, std::integral_constant<int, 0>{}, std::integral_constant<int, (P * NG + G + 1) % 2>{});
+    __builtin_amdgcn_sched_barrier(0);
+    products(std::integral_constant<int, G>{}, par, std::integral_constant<int, (P * NG + G) % 2>{});
+  });
+  }
+
+  if (valid) {
+    float *base = out_ptr<KIND>(p, tc.g, 0, CONV ? img * p.OHW + col0 + lane : col0 + lane);
+    const int64_t rs = CONV ? (int64_t)p.OHW : p.ldc;
+    auto store_all = [&](auto epi) __attribute__((always_inline)) {
+      constexpr bool E = decltype(epi)::value;
+      float pb[R][4], pr[R][4];
+      if constexpr (E) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = wrow0 + 4 * r + i;
+            const bool ok = row < p.M;
+            pb[r][i] = epi_bias(p, ok, tc.g * p.M + row);
+            pr[r][i] = epi_res(p, ok, base + (int64_t)(ok ? row : 0) * rs);
+          }
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = wrow0 + 4 * r + i;
+          if (row < p.M) {
+            if constexpr (E)
+              base[(int64_t)row * rs] = finish_with(p, acc[r][i], pb[r][i], pr[r][i]);
+            else
+              base[(int64_t)row * rs] = finish<false>(p, acc[r][i], 0, base);
           }
         }
     };

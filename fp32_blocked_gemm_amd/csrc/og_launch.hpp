@@ -551,6 +551,37 @@ void launch_halo_r(og::Problem p, const HaloPlan &h, hipStream_t s) {
 // A 3x3 convolution (gathered B) on variant 26, 27 or 28, planned by halo_plan.
 void launch_halo_conv(int variant, const og::Problem &p, const HaloPlan &h, hipStream_t s);
 
+// ---------------------------------------------------------------------------
+// Panel kernel (fast mode: 1x1 convolutions, any stride and padding, and
+// matrix products): four waves over 64 columns, variant 29 one chain of 4
+// rows per wave (16 rows per block) in chunks of 64 steps and four stages
+// (96 KB of LDS), 30 two chains (32 rows) in chunks of 32 steps and five
+// stages (60 KB, two blocks per compute unit).  B rows are read 16 bytes
+// per lane (bv) where every row of the panel starts 16-byte aligned and the
+// column count is a multiple of 4.
+// ---------------------------------------------------------------------------
+constexpr int kFirstPanelVariant = 29, kLastPanelVariant = 30;
+inline bool is_panel(int v) { return v >= kFirstPanelVariant && v <= kLastPanelVariant; }
+
+template <int KIND, int R, bool BV, bool AV>
+void launch_panel_shape(og::Problem p, hipStream_t s) {
+  constexpr int CW = 4, CC = R == 1 ? 64 : 32, NS = R == 1 ? 4 : 5;
+  const auto kernel = og::panel_kernel<KIND, R, CW, CC, NS, BV, AV>;
+  p.tiles_m = (int)ceil_div(p.M, 4 * R * CW);
+  p.tiles_n = KIND == og::kBMatrix ? (int)ceil_div(p.N, 64) : (int)((p.N / p.OHW) * ceil_div(p.OHW, 64));
+  const dim3 grid((unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)p.groups), block(64 * CW);
+  const size_t lds = (size_t)(NS * CC * 64 + CW * NS * 4 * R * CC) * 4;  // B stages, weight stages
+  // more than 64 KB of dynamic LDS must be allowed per kernel, once
+  static const hipError_t allowed =
+      hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  (void)allowed;
+  hipLaunchKernelGGL(kernel, grid, block, lds, s, p);
+}
+
+// A matrix product (kind kBMatrix) or a 1x1 convolution (kBPlanes, kBGather)
+// on variant 29 or 30.
+void launch_panel(int variant, int kind, bool bv, bool av, const og::Problem &p, hipStream_t s);
+
 // Entry points of the kernel groups, each instantiated in one compilation
 // of og_units.hip (so the groups compile in parallel) and declared extern
 // here so no other unit instantiates them.

@@ -90,6 +90,28 @@ void launch_halo_conv(int variant, const og::Problem &p, const HaloPlan &h, hipS
   if (variant == 27) return launch_halo_r<2, 4>(p, h, s);
   return launch_halo_r<1, 8>(p, h, s);
 }
+#elif OG_UNIT == 15
+template <int R>
+static void launch_panel_r(int kind, bool bv, bool av, const og::Problem &p, hipStream_t s) {
+  if (kind == og::kBMatrix) {
+    if (bv && av) return launch_panel_shape<og::kBMatrix, R, true, true>(p, s);
+    if (bv) return launch_panel_shape<og::kBMatrix, R, true, false>(p, s);
+    if (av) return launch_panel_shape<og::kBMatrix, R, false, true>(p, s);
+    return launch_panel_shape<og::kBMatrix, R, false, false>(p, s);
+  }
+  if (kind == og::kBPlanes) {
+    if (bv && av) return launch_panel_shape<og::kBPlanes, R, true, true>(p, s);
+    if (bv) return launch_panel_shape<og::kBPlanes, R, true, false>(p, s);
+    if (av) return launch_panel_shape<og::kBPlanes, R, false, true>(p, s);
+    return launch_panel_shape<og::kBPlanes, R, false, false>(p, s);
+  }
+  if (av) return launch_panel_shape<og::kBGather, R, false, true>(p, s);
+  return launch_panel_shape<og::kBGather, R, false, false>(p, s);
+}
+void launch_panel(int variant, int kind, bool bv, bool av, const og::Problem &p, hipStream_t s) {
+  if (variant == 29) return launch_panel_r<1>(kind, bv, av, p, s);
+  return launch_panel_r<2>(kind, bv, av, p, s);
+}
 #else
 #error "unknown OG_UNIT"
 #endif

@@ -164,6 +164,38 @@ def test_halo_kernel_shapes(orc, variant):
                              f"halo {variant} {s} mode {mode}")
 
 
+PANEL_SHAPES = [
+    # 1x1 read in place, 16-byte rows (64 pixels) and not (49), channels
+    # ending inside a 32-step chunk, rows past Cout
+    synth.ConvShape("p8", 2, 40, 8, 8, 36, 1, 1),
+    synth.ConvShape("p7", 3, 70, 7, 7, 20, 1, 1),
+    synth.ConvShape("p3", 1, 3, 9, 12, 5, 1, 1),
+    # strided and padded 1x1: the gathered form
+    synth.ConvShape("p14s2", 2, 64, 14, 14, 33, 1, 1, (2, 2)),
+    synth.ConvShape("ppad", 2, 20, 6, 9, 17, 1, 1, (1, 2), (1, 0, 2, 1)),
+    # groups
+    synth.ConvShape("pg", 2, 64, 10, 10, 48, 1, 1, (1, 1), (0, 0, 0, 0), (1, 1), 4),
+    # a 3x3 window: the automatic choice runs
+    synth.ConvShape("p3x3", 1, 16, 9, 9, 8, 3, 3, (1, 1), (1, 1, 1, 1)),
+]
+
+
+@pytest.mark.parametrize("variant", [29, 30])
+def test_panel_kernel_shapes(orc, variant):
+    """The panel kernel (fast mode, 1x1 windows) bit for bit against the
+    oracle; in exact mode, and on other windows, the automatic choice."""
+    rng = np.random.default_rng(600 + variant)
+    og.set_variant(variant)
+    for s in PANEL_SHAPES:
+        x, w = synth.conv_inputs(s, int(rng.integers(1 << 30)), "uniform")
+        x = _with_specials(x, rng, 0.01)
+        w = _with_specials(w, rng, 0.01)
+        for mode in MODES:
+            say(f"conv panel variant {variant} {s} mode {mode}")
+            assert_same_bits(_gpu_conv(x, w, s, mode), _oracle(orc, x, w, s, mode),
+                             f"panel {variant} {s} mode {mode}")
+
+
 GROUPED_SHAPES = [
     # the grouped, dilated, strided workload's own form, smaller
     synth.ConvShape("g8x8", 2, 64, 20, 18, 64, 3, 3, (2, 2), (2, 2, 2, 2), (2, 2), 8),

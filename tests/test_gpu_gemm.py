@@ -183,6 +183,36 @@ def test_chain_kernel_lengths(orc, variant):
                              f"chain {variant} A aligned {m}x{n}x{k} mode {mode}")
 
 
+@pytest.mark.parametrize("variant", [29, 30])
+def test_panel_kernel_products(orc, variant):
+    """The panel kernel (fast mode) over k from 0 to many 32-step chunks with
+    ragged tails, rows and columns ending inside a block, row strides,
+    misaligned and aligned rows of A and B, and special values; in exact
+    mode the variant runs the automatic choice."""
+    rng = np.random.default_rng(90 + variant)
+    og.set_variant(variant)
+    # rows of A and B not 16-byte aligned: 4-byte loads
+    for m, n, k in ((5, 70, 0), (5, 70, 1), (9, 33, 31), (9, 33, 32), (9, 33, 33), (17, 64, 64),
+                    (70, 130, 517), (1, 301, 300), (131, 301, 97)):
+        A = _mixed(rng, (m, k), 0.01)
+        B = _mixed(rng, (k, n), 0.01)
+        for mode in MODES:
+            say(f"gemm panel variant {variant} {m}x{n}x{k} mode {mode}")
+            got, flat = _run_gpu(A, B, mode, k + 1, n + 3, n + 2, (0, 1, 1))
+            _check_gaps(flat, m, n, n + 2, 1)
+            assert_same_bits(got, orc.gemm(A, B, mode), f"panel {variant} {m}x{n}x{k} mode {mode}")
+    # B rows 16-byte aligned (16-byte panel loads), A rows too or not
+    for m, n, k, lda, ldb in ((5, 64, 200, 200, 68), (33, 132, 517, 520, 136),
+                              (64, 128, 96, 96, 128), (7, 64, 1100, 1101, 64), (40, 4, 36, 36, 4)):
+        A = _mixed(rng, (m, k), 0.01)
+        B = _mixed(rng, (k, n), 0.01)
+        for mode in MODES:
+            say(f"gemm panel variant {variant} aligned {m}x{n}x{k} lda {lda} ldb {ldb} mode {mode}")
+            got, _ = _run_gpu(A, B, mode, lda, ldb, n + 1, (0, 4, 0))
+            assert_same_bits(got, orc.gemm(A, B, mode),
+                             f"panel {variant} aligned {m}x{n}x{k} mode {mode}")
+
+
 @pytest.mark.parametrize("specials", [True, False])
 def test_4096_cubed_full(orc, specials):
     """4096^3 with 0.1 % special values and as a clean copy: every output."""
