@@ -36,9 +36,10 @@ COLD_BYTES = 600 << 20  # rotated input copies beyond the 256 MB last-level cach
 # HBM bytes per launch of the headline kernel, from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs scaled by a 1 GiB copy (the summary under profiles/ gives
 # the commands and counts).  Valid only for the kernel build it was measured
-# on: None until the counters are taken again on the current one.
+# on (None until the counters are taken again after a change to it):
+# FETCH_SIZE 196 767.1 KiB x 2.00 + WRITE_SIZE 65 536.0 KiB x 1.00.
 HEADLINE_TRAFFIC = {"kernel": "og::mfma_kernel<1, 256, 256, 4, 2, 0, true, true, 2, 32>",
-                    "bytes": None}
+                    "bytes": 470087885}
 PAGES_RESNET_CPU_MS = {"16 threads": 12.3, "32 threads": 11.1}  # 16-core Zen 4, fast mode
 
 
@@ -55,7 +56,15 @@ def parse():
                     help="time one workload only (for profiling): gemm4096_fast, gemm4096_exact, "
                          "resnet_b1, resnet_b8, epilogue, skinny, prefill, grouped, conv1d, conv1x1, ragged, "
                          "gemm256, dw_b1, dw_b8, se, single_column, nt_prefill, nt_single_row, nt_rows8, model_rows, "
-                         "copy (a 1 GiB device copy, to scale the HBM byte counters)")
+                         "copy (a 1 GiB device copy, to scale the HBM byte counters), "
+                         "layer (one ResNet-50 layer: --layer, --batch, --variant, --mode; "
+                         "--warmup then --steps calls)")
+    ap.add_argument("--layer", default="layer3.1.c2",
+                    help="with --only layer: the ResNet-50 layer to time (e.g. layer3.1.c2)")
+    ap.add_argument("--batch", type=int, default=8, help="with --only layer: the batch")
+    ap.add_argument("--variant", type=int, default=0,
+                    help="with --only layer: the kernel variant forced (0: the automatic choice)")
+    ap.add_argument("--mode", default="fast", help="with --only layer: exact, fast or fast_mfma")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -551,6 +560,36 @@ def main():
     og.lib()
     timer = Timer(torch)
 
+    if args.only == "layer":
+        # one layer, its calls issued back to back (for profiling a kernel)
+        s = [c for c in synth.resnet50_convs(args.batch) if c.name == args.layer]
+        if not s:
+            print(f"no ResNet-50 layer {args.layer}", file=sys.stderr)
+            sys.exit(2)
+        s = s[0]
+        x, w = synth.conv_inputs(s, 1)
+        dx, dw = torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda()
+        og.set_variant(args.variant)
+        call = lambda: og.conv2d(dx, dw, stride=s.stride, pad=s.pad, dil=s.dil, groups=s.groups,
+                                 mode=args.mode)
+        y = call()
+        for _ in range(args.warmup):
+            og.conv2d(dx, dw, stride=s.stride, pad=s.pad, dil=s.dil, groups=s.groups,
+                      mode=args.mode, out=y)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            og.conv2d(dx, dw, stride=s.stride, pad=s.pad, dil=s.dil, groups=s.groups,
+                      mode=args.mode, out=y)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / max(args.steps, 1) * 1e3
+        print(json.dumps({"only": "layer", "layer": args.layer, "batch": args.batch,
+                          "variant": args.variant, "mode": args.mode, "shape": repr(s),
+                          "us_per_call": round(us, 2),
+                          "gflops": round(2 * conv_macs(og, s) / (us * 1e-6) / 1e9, 1)}), flush=True)
+        return
     if args.only not in (None, "gemm4096_fast"):
         log(f"only: {args.only}")
         res = extras(torch, og, synth, timer, only=args.only)

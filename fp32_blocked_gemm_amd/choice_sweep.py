@@ -1,0 +1,158 @@
+"""Measures the regret of libog's automatic kernel choice in fast mode: for
+each shape of a set, the time of the automatic choice (variant 0) over the
+best time of every variant that runs the shape, each forced with
+og_set_variant.  Needs a GPU.
+
+Two sets of shapes.  "fit": the shapes the fast-mode launch-time table was
+fitted to -- ResNet-50's convolutions at batch 1, 2, 3, 4, 5, 6, 8, 12 and
+16, MobileNetV3-large's ungrouped convolutions at batch 1, 2, 4, 6 and 8,
+twelve 3x3 convolutions of other widths and 72 seeded random matrix
+products.  "heldout": shapes the fit did not see -- ResNet-50 at batch 7
+and 10, MobileNetV3-large at batch 3 and 5, four more 3x3 convolutions and
+24 random products of another seed.
+
+    python3 -m fp32_blocked_gemm_amd.choice_sweep [--set fit|heldout] [--out FILE] [--quick]
+
+prints one JSON line per shape (times in us) and a summary line.
+"""
+import argparse
+import json
+import random
+import sys
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--out", default=None, help="also write the lines to this file")
+    ap.add_argument("--set", default="heldout", choices=("fit", "heldout"))
+    ap.add_argument("--quick", action="store_true", help="the first ResNet-50 batch only, 6 products")
+    args = ap.parse_args()
+    import torch
+
+    import synth
+    import bench
+    import fp32_blocked_gemm_amd as og
+
+    timer = bench.Timer(torch)
+    out = open(args.out, "w") if args.out else None
+
+    def emit(e):
+        line = json.dumps(e)
+        print(line, flush=True)
+        if out:
+            out.write(line + "\n")
+            out.flush()
+
+    def t_of(call):
+        g = timer.graph(lambda: [call() for _ in range(10)])
+        ms = timer.spike(g.replay, min_ms=10.0, reps=3) / 10
+        del g
+        return round(ms * 1e3, 2)
+
+    # variants that run a shape in fast mode: every tile variant, and the
+    # kernels of their own forms where the shape is theirs
+    tiles = list(range(1, 18)) + [20]
+
+    def conv_variants(s):
+        if s.Cin // s.groups == 1:
+            return None  # depthwise: its own kernel only
+        v = list(tiles)
+        if s.KH == 3 and s.KW == 3:
+            v += [26, 27, 28]
+        if s.KH == 1 and s.KW == 1:
+            v += [29, 30]
+        return v
+
+    regrets = []
+
+    def run_conv(s, tag):
+        vs = conv_variants(s)
+        if vs is None:
+            return
+        x, w = synth.conv_inputs(s, 1)
+        dx, dw = torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda()
+        y = og.conv2d(dx, dw, stride=s.stride, pad=s.pad, dil=s.dil, groups=s.groups)
+        e = {"set": tag, "kind": "conv", "shape": repr(s),
+             "dims": [s.N, s.Cin, s.H, s.W, s.Cout, s.KH, s.KW, list(s.stride), list(s.pad), list(s.dil), s.groups]}
+        for v in [0] + vs:
+            og.set_variant(v)
+            e[str(v)] = t_of(lambda: og.conv2d(dx, dw, stride=s.stride, pad=s.pad, dil=s.dil,
+                                               groups=s.groups, mode="fast", out=y))
+        og.set_variant(0)
+        best = min(e[str(v)] for v in [0] + vs)
+        e["best"] = min(([0] + vs), key=lambda v: e[str(v)])
+        e["regret"] = round(e["0"] / best, 4)
+        regrets.append(e["regret"])
+        emit(e)
+
+    def run_gemm(m, n, k, ld, tag):
+        A = torch.randn(m, k + ld, device="cuda")[:, :k]
+        B = torch.randn(k, n + ld, device="cuda")[:, :n]
+        C = torch.empty(m, n + ld, device="cuda")[:, :n]
+        vs = tiles + [29, 30]
+        e = {"set": tag, "kind": "gemm", "shape": f"{m}x{n}x{k} row strides +{ld}", "dims": [m, n, k, ld]}
+        for v in [0] + vs:
+            og.set_variant(v)
+            e[str(v)] = t_of(lambda: og.gemm(A, B, "fast", out=C))
+        og.set_variant(0)
+        best = min(e[str(v)] for v in [0] + vs)
+        e["best"] = min(([0] + vs), key=lambda v: e[str(v)])
+        e["regret"] = round(e["0"] / best, 4)
+        regrets.append(e["regret"])
+        emit(e)
+
+    if args.set == "fit":
+        resnet_b, mobile_b, seeds = (1, 2, 3, 4, 5, 6, 8, 12, 16), (1, 2, 4, 6, 8), ((7, 48), (23, 24))
+        other = (synth.ConvShape("inc96_35", 8, 96, 35, 35, 96, 3, 3, (1, 1), (1, 1, 1, 1)),
+                 synth.ConvShape("inc192_17", 8, 192, 17, 17, 192, 3, 3, (1, 1), (1, 1, 1, 1)),
+                 synth.ConvShape("vgg64_112", 1, 64, 112, 112, 64, 3, 3, (1, 1), (1, 1, 1, 1)),
+                 synth.ConvShape("u128_32_b4", 4, 128, 32, 32, 128, 3, 3, (1, 1), (1, 1, 1, 1)),
+                 synth.ConvShape("vgg128_56_b2", 2, 128, 56, 56, 128, 3, 3, (1, 1), (1, 1, 1, 1)),
+                 synth.ConvShape("u256_16_b8", 8, 256, 16, 16, 256, 3, 3, (1, 1), (1, 1, 1, 1)),
+                 synth.ConvShape("s2_96_40_b4", 4, 96, 40, 40, 192, 3, 3, (2, 2), (1, 1, 1, 1)),
+                 synth.ConvShape("u384_10_b16", 16, 384, 10, 10, 384, 3, 3, (1, 1), (1, 1, 1, 1)),
+                 synth.ConvShape("u160_20_b4", 4, 160, 20, 20, 160, 3, 3, (1, 1), (1, 1, 1, 1)),
+                 synth.ConvShape("u48_64_b2", 2, 48, 64, 64, 96, 3, 3, (1, 1), (1, 1, 1, 1)),
+                 synth.ConvShape("s2_320_24_b8", 8, 320, 24, 24, 320, 3, 3, (2, 2), (1, 1, 1, 1)),
+                 synth.ConvShape("u512_12_b2", 2, 512, 12, 12, 256, 3, 3, (1, 1), (1, 1, 1, 1)))
+    else:
+        resnet_b, mobile_b, seeds = (7, 10), (3, 5), ((31, 24),)
+        other = (synth.ConvShape("u80_30_b6", 6, 80, 30, 30, 80, 3, 3, (1, 1), (1, 1, 1, 1)),
+                 synth.ConvShape("u224_14_b4", 4, 224, 14, 14, 448, 3, 3, (1, 1), (1, 1, 1, 1)),
+                 synth.ConvShape("s2_64_80_b2", 2, 64, 80, 80, 128, 3, 3, (2, 2), (1, 1, 1, 1)),
+                 synth.ConvShape("u32_96_b1", 1, 32, 96, 96, 32, 3, 3, (1, 1), (1, 1, 1, 1)))
+    if args.quick:
+        resnet_b, mobile_b, other, seeds = resnet_b[:1], (), (), ((seeds[0][0], 6),)
+    seen = set()
+    for b in resnet_b:
+        for s in synth.resnet50_convs(b):
+            key = (s.N, s.Cin, s.H, s.Cout, s.KH, s.stride)
+            if key not in seen:
+                seen.add(key)
+                run_conv(s, f"resnet50_b{b}")
+    for b in mobile_b:
+        for s in synth.mobilenetv3_large_convs(b):
+            key = (s.N, s.Cin, s.H, s.Cout, s.KH, s.stride, s.groups)
+            if key not in seen:
+                seen.add(key)
+                run_conv(s, f"mobilenetv3_b{b}")
+    for s in other:
+        run_conv(s, "other3x3")
+    for seed, nprod in seeds:
+        rng = random.Random(seed)
+        for _ in range(nprod):
+            run_gemm(rng.choice([48, 96, 200, 333, 640, 1200, 2048]), rng.choice([100, 250, 700, 1500, 2900]),
+                     rng.choice([64, 300, 777, 1500, 2300]), rng.choice([0, 1, 4]), "random_products")
+    regrets.sort()
+    n = len(regrets)
+    summ = {"summary": True, "shapes": n, "mean_regret": round(sum(regrets) / n, 4),
+            "median_regret": regrets[n // 2], "max_regret": regrets[-1],
+            "over_5pct": sum(r > 1.05 for r in regrets), "over_10pct": sum(r > 1.10 for r in regrets)}
+    emit(summ)
+    if out:
+        out.close()
+
+
+if __name__ == "__main__":
+    sys.path.insert(0, __import__("os").path.dirname(__import__("os").path.dirname(__import__("os").path.abspath(__file__))))
+    main()

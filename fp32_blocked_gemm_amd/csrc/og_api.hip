@@ -80,86 +80,193 @@ struct Shape {
   int64_t M, N, K, groups;
   int64_t ohw;  // output pixels per image; 0 for a matrix product
   int64_t khw;  // KH * KW; 0 for a matrix product
+  int ffam = 0;        // family of the fast-mode model (fast_family)
+  double bytes = 0;    // bytes of the operands and the result, each counted once
+  double halo_x = 0;   // halo kernel: thousands of input floats staged per block over its k
 };
 
-// Launch time model, fitted to launches of every variant measured on MI355X
-// over the ResNet-50 layers at batch 1 and 8 and the matrix products the library
-// is benchmarked on: t = (c * K + d) * rounds + o microseconds, rounds =
-// ceil(blocks / cap) or max(1, blocks / cap), whichever fits that variant
-// better, with (cap, c in ns per k step, d per round, o) per variant, mode
-// and family: matrix products, 3x3 windows (whose gathers cost more) and
-// other windows.  Among fits of nearly equal error, the one whose choices
-// add up to the least measured time was kept.  The chain
-// kernel's step cost is held at >= 2.5 ns when fitting (about six cycles:
-// its dependent chain cannot run faster), so the model does not extrapolate
-// a chain to no cost.  (The exact-mode fields of variants 14..16 are not
-// used: exact mode runs them as 10, 13 and 11.)
-struct Cost {
+// Family of a convolution in the fast-mode launch model: 1 a 3x3 window at
+// stride 1, 4 a strided 3x3 window, 2 a 1x1 window read in place (stride 1,
+// no padding), 3 any other window or a strided or padded 1x1 (gathered
+// taps); matrix products are family 0.
+int fast_family(int64_t KH, int64_t KW, bool planes, int64_t strideH, int64_t strideW) {
+  if (KH == 3 && KW == 3) return strideH == 1 && strideW == 1 ? 1 : 4;
+  return planes ? 2 : 3;
+}
+
+// Launch time models, t in microseconds.  Fast mode: t = (c * K / 1000 + d
+// + e * X) * rounds + o + b * bytes / 1e6, rounds = max(1, (1 - q) * x + q *
+// ceil(x)) with x = blocks / cap, bytes those of the operands and the result
+// each counted once, X (halo kernel only) the thousands of input floats a
+// block stages over its k; (q, cap, c, d, o, b, e) per variant and family
+// (fast_family), cap a multiple of 256 blocks (one or more per compute
+// unit), fitted by least squares on the relative error to 401 shapes, each
+// launched on every variant on the MI355X (ResNet-50's convolutions at
+// batch 1, 2, 3, 4, 5, 6, 8, 12 and 16, MobileNetV3-large's ungrouped ones
+// at batch 1, 2, 4, 6 and 8, twelve 3x3 convolutions of other widths, 72
+// seeded random matrix products): mean error 4.8 %.  Variants 26..28 are the
+// halo kernel, 29 and 30 the panel kernel.
+struct FastCost {
   int variant, fam;
-  int q_fast;  // 1: whole rounds of cap blocks, ceil(blocks / cap); 0: max(1, blocks / cap)
-  double cap_fast, c_fast, d_fast, o_fast;
-  int q_exact;
-  double cap_exact, c_exact, d_exact, o_exact;
+  double q, cap, c, d, o, b, e;
 };
-constexpr Cost kCosts[] = {
-    {2, 0, 0, 256, 125.31, 0.00, 9.4, 1, 128, 107.50, 2.46, 0.0},
-    {2, 1, 0, 256, 197.45, 0.00, 9.6, 0, 256, 234.52, 12.36, 0.0},
-    {2, 2, 0, 128, 131.95, 0.00, 10.2, 1, 128, 117.10, 5.28, 0.0},
-    {3, 0, 1, 256, 63.76, 0.00, 7.1, 1, 256, 107.61, 2.45, 0.0},
-    {3, 1, 1, 384, 103.58, 2.92, 3.9, 1, 384, 237.74, 0.13, 7.3},
-    {3, 2, 1, 256, 76.89, 3.56, 2.3, 1, 384, 117.04, 5.18, 0.0},
-    {4, 0, 1, 384, 41.11, 3.52, 0.0, 1, 512, 107.32, 2.49, 0.0},
-    {4, 1, 1, 384, 73.95, 1.87, 4.4, 0, 384, 150.49, 2.09, 4.5},
-    {4, 2, 1, 256, 47.75, 0.80, 3.6, 0, 256, 107.39, 0.63, 4.6},
-    {5, 0, 1, 384, 45.55, 4.49, 0.0, 1, 512, 114.71, 2.63, 0.0},
-    {5, 1, 0, 384, 115.18, 5.91, 0.0, 0, 384, 215.93, 0.45, 5.7},
-    {5, 2, 1, 256, 58.70, 0.37, 3.6, 0, 256, 122.63, 0.00, 4.9},
-    {6, 0, 1, 768, 13.57, 3.45, 0.1, 1, 768, 15.27, 1.87, 2.2},
-    {6, 1, 0, 512, 13.48, 0.00, 8.7, 0, 512, 14.85, 0.00, 8.9},
-    {6, 2, 1, 512, 12.49, 0.06, 4.5, 0, 512, 13.11, 0.04, 6.0},
-    {7, 0, 1, 768, 16.14, 0.00, 3.9, 1, 768, 20.41, 0.00, 3.8},
-    {7, 1, 1, 768, 17.58, 0.80, 3.8, 1, 768, 21.17, 0.00, 5.9},
-    {7, 2, 1, 512, 14.55, 0.04, 4.5, 1, 512, 18.33, 0.00, 4.6},
-    {8, 0, 1, 768, 21.41, 2.69, 0.8, 1, 768, 32.08, 0.70, 2.0},
-    {8, 1, 0, 384, 21.34, 0.00, 3.3, 0, 384, 30.40, 0.00, 2.7},
-    {8, 2, 1, 512, 22.65, 0.00, 3.4, 0, 768, 37.84, 1.55, 1.8},
-    {9, 0, 1, 384, 23.24, 0.00, 5.1, 0, 512, 53.02, 0.00, 3.8},
-    {9, 1, 0, 384, 32.64, 0.07, 3.2, 0, 384, 55.57, 0.00, 0.9},
-    {9, 2, 0, 384, 31.67, 0.23, 3.6, 0, 384, 50.09, 0.00, 4.4},
-    {10, 0, 0, 256, 6.81, 1.78, 3.5, 1, 256, 7.76, 2.24, 2.8},
-    {10, 1, 0, 256, 4.14, 5.33, 5.0, 0, 256, 4.79, 5.58, 5.3},
-    {10, 2, 1, 256, 6.54, 3.48, 1.7, 1, 256, 7.81, 3.55, 1.5},
-    {11, 0, 0, 256, 5.38, 1.94, 3.3, 0, 256, 6.73, 2.13, 3.3},
-    {11, 1, 0, 256, 3.92, 4.48, 5.0, 0, 256, 4.80, 4.58, 5.5},
-    {11, 2, 1, 128, 2.60, 1.59, 1.8, 1, 128, 3.33, 1.64, 1.8},
-    {12, 0, 0, 768, 4.06, 4.23, 0.0, 0, 768, 5.37, 2.80, 2.4},
-    {12, 1, 0, 384, 3.18, 2.49, 7.0, 0, 384, 4.14, 2.68, 6.9},
-    {12, 2, 0, 384, 2.83, 0.88, 5.0, 0, 256, 2.50, 0.54, 5.0},
-    {13, 0, 0, 256, 6.79, 2.74, 2.5, 1, 256, 9.99, 2.14, 2.3},
-    {13, 1, 0, 256, 4.95, 5.29, 4.3, 0, 256, 7.66, 5.79, 4.6},
-    {13, 2, 0, 256, 6.68, 3.45, 2.6, 1, 256, 9.85, 3.39, 1.2},
-    {14, 0, 1, 256, 13.53, 2.85, 2.7, 1, 32, 3.88, 1.08, 2.9},
-    {14, 1, 0, 256, 9.41, 7.59, 0.0, 1, 64, 5.91, 3.57, 3.5},
-    {14, 2, 1, 256, 11.72, 4.56, 1.6, 1, 64, 7.77, 3.56, 1.4},
-    {15, 0, 1, 256, 12.32, 2.71, 3.1, 1, 64, 9.80, 2.52, 3.0},
-    {15, 1, 0, 256, 10.21, 7.46, 0.0, 1, 64, 9.17, 3.22, 2.9},
-    {15, 2, 1, 256, 11.18, 4.34, 1.5, 1, 64, 9.87, 3.39, 1.3},
-    {16, 0, 1, 256, 8.88, 2.21, 3.5, 1, 32, 3.36, 1.04, 3.4},
-    {16, 1, 0, 256, 7.64, 6.56, 1.6, 0, 64, 4.78, 4.57, 6.3},
-    {16, 2, 1, 256, 8.58, 3.51, 1.5, 1, 32, 3.32, 1.64, 2.0},
-    {17, 0, 0, 256, 232.97, 8.57, 0.0, 1, 64, 107.62, 2.42, 0.0},
-    {17, 1, 0, 256, 285.99, 9.90, 0.0, 0, 256, 234.57, 12.35, 0.0},
-    {17, 2, 1, 256, 246.22, 9.35, 0.0, 0, 64, 113.24, 0.00, 4.5},
-    // variant 20, fitted to 23 products from 64 x 3136 x 64 to 4096^3 (mean
-    // error 4.7 % fast, 4.6 % exact; the exact estimate carries 5 us more,
-    // which keeps it off the products where the other variants' estimates
-    // are too high, e.g. 1000 x 777 x 1531)
-    {20, 0, 0, 384, 27.26, 2.00, 1.0, 1, 512, 60.94, 1.89, 5.93},
-    // for convolutions: 1x1 and other windows fitted to the ResNet-50 layers
-    // at batch 1 and 8 (it wins some batch-8 1x1 layers); 3x3 windows never
-    // (its wins there were within the fit's error)
-    {20, 1, 0, 384, 1e9, 0.00, 0.0, 0, 384, 1e9, 0.00, 0.0},
-    {20, 2, 1, 256, 28.25, 0.00, 4.57, 0, 256, 60.54, 0.00, 5.35},
+constexpr FastCost kFastCosts[] = {
+    {2, 0, 0, 256, 132.150, 9.037, 0.000, 0.0790, 0.0000},
+    {2, 1, 0, 256, 200.488, 0.000, 9.607, 0.0977, 0.0000},
+    {2, 2, 0.75, 256, 135.149, 0.000, 8.754, 0.0683, 0.0000},
+    {2, 3, 0.75, 256, 191.331, 4.963, 9.518, 0.0000, 0.0000},
+    {2, 4, 1, 256, 198.851, 0.829, 9.278, 0.0386, 0.0000},
+    {3, 0, 0.75, 256, 71.315, 5.603, 0.000, 0.0910, 0.0000},
+    {3, 1, 0.5, 256, 106.661, 1.239, 5.154, 0.0499, 0.0000},
+    {3, 2, 0.75, 256, 74.927, 0.448, 5.102, 0.0654, 0.0000},
+    {3, 3, 0.75, 256, 103.345, 0.178, 8.299, 0.0000, 0.0000},
+    {3, 4, 0.25, 256, 106.345, 2.227, 3.966, 0.0247, 0.0000},
+    {4, 0, 0.25, 256, 39.923, 2.435, 1.643, 0.0526, 0.0000},
+    {4, 1, 0.5, 256, 76.180, 0.000, 5.792, 0.0000, 0.0000},
+    {4, 2, 0.5, 256, 44.865, 0.483, 3.795, 0.0623, 0.0000},
+    {4, 3, 0.5, 256, 72.451, 0.000, 7.765, 0.0000, 0.0000},
+    {4, 4, 0.75, 256, 76.090, 0.714, 4.108, 0.0483, 0.0000},
+    {5, 0, 0.25, 256, 46.179, 2.100, 2.042, 0.0183, 0.0000},
+    {5, 1, 0.5, 256, 117.752, 0.000, 5.240, 0.0000, 0.0000},
+    {5, 2, 0.5, 256, 54.768, 0.387, 3.801, 0.0375, 0.0000},
+    {5, 3, 0.5, 256, 107.044, 0.000, 8.889, 0.0000, 0.0000},
+    {5, 4, 0.75, 256, 116.785, 1.327, 4.345, 0.0067, 0.0000},
+    {6, 0, 0.5, 768, 14.608, 0.242, 2.335, 0.8409, 0.0000},
+    {6, 1, 0.75, 768, 16.692, 0.000, 1.079, 0.0000, 0.0000},
+    {6, 2, 0.5, 768, 14.497, 0.741, 2.710, 0.1789, 0.0000},
+    {6, 3, 0.25, 768, 20.135, 4.491, 2.202, 0.0000, 0.0000},
+    {6, 4, 0.5, 512, 17.816, 0.000, 3.089, 0.5236, 0.0000},
+    {7, 0, 0.5, 768, 17.177, 0.117, 2.491, 0.5768, 0.0000},
+    {7, 1, 0.5, 768, 19.233, 0.000, 3.427, 0.0000, 0.0000},
+    {7, 2, 0.5, 768, 17.275, 0.730, 2.542, 0.1325, 0.0000},
+    {7, 3, 0.5, 512, 15.281, 2.631, 5.843, 0.0000, 0.0000},
+    {7, 4, 0.75, 512, 20.614, 0.000, 3.038, 0.2773, 0.0000},
+    {8, 0, 0.25, 512, 21.492, 0.000, 2.990, 0.3116, 0.0000},
+    {8, 1, 0.25, 512, 23.173, 0.000, 4.585, 0.0000, 0.0000},
+    {8, 2, 0.75, 768, 23.794, 0.559, 2.533, 0.1622, 0.0000},
+    {8, 3, 0.75, 512, 20.253, 2.175, 5.834, 0.0000, 0.0000},
+    {8, 4, 0.5, 512, 26.950, 0.000, 3.092, 0.1817, 0.0000},
+    {9, 0, 1, 512, 31.340, 0.000, 3.312, 0.3016, 0.0000},
+    {9, 1, 0, 2048, 29.070, 0.000, 0.000, 2.2430, 0.0000},
+    {9, 2, 0.25, 512, 32.850, 0.000, 3.493, 0.1880, 0.0000},
+    {9, 3, 0.5, 512, 32.239, 2.823, 4.915, 0.0000, 0.0000},
+    {9, 4, 1, 512, 33.842, 0.000, 3.167, 0.3262, 0.0000},
+    {10, 0, 1, 256, 5.957, 3.489, 1.632, 0.0000, 0.0000},
+    {10, 1, 1, 256, 4.901, 3.893, 1.728, 0.0000, 0.0000},
+    {10, 2, 1, 256, 5.242, 3.517, 1.783, 0.0000, 0.0000},
+    {10, 3, 0.5, 512, 15.291, 13.569, 0.000, 0.4646, 0.0000},
+    {10, 4, 1, 256, 3.995, 5.910, 1.106, 0.2118, 0.0000},
+    {11, 0, 1, 256, 5.058, 2.842, 1.530, 0.0000, 0.0000},
+    {11, 1, 1, 256, 4.670, 3.157, 1.395, 0.0388, 0.0000},
+    {11, 2, 1, 256, 4.418, 3.151, 1.633, 0.0748, 0.0000},
+    {11, 3, 0.25, 1024, 25.793, 26.188, 0.000, 0.6820, 0.0000},
+    {11, 4, 0.25, 256, 4.151, 4.723, 2.500, 0.0000, 0.0000},
+    {12, 0, 0.5, 512, 3.208, 1.246, 3.032, 0.4526, 0.0000},
+    {12, 1, 1, 256, 2.418, 1.180, 3.373, 0.2280, 0.0000},
+    {12, 2, 0.25, 512, 3.202, 1.303, 3.748, 0.0000, 0.0000},
+    {12, 3, 0.25, 2048, 19.515, 11.629, 3.561, 0.0000, 0.0000},
+    {12, 4, 0, 256, 2.172, 1.702, 5.833, 0.0851, 0.0000},
+    {13, 0, 1, 256, 6.535, 3.427, 1.654, 0.0000, 0.0000},
+    {13, 1, 1, 256, 6.099, 3.497, 1.653, 0.0184, 0.0000},
+    {13, 2, 1, 256, 6.283, 3.381, 1.657, 0.0000, 0.0000},
+    {13, 3, 0.25, 512, 13.675, 13.472, 0.000, 0.3762, 0.0000},
+    {13, 4, 0.75, 256, 4.884, 5.693, 2.003, 0.2918, 0.0000},
+    {14, 0, 0.75, 256, 9.352, 5.193, 1.938, 0.1295, 0.0000},
+    {14, 1, 1, 256, 9.956, 5.491, 1.711, 0.0059, 0.0000},
+    {14, 2, 1, 256, 7.045, 4.813, 1.979, 0.0000, 0.0000},
+    {14, 3, 1, 256, 9.661, 7.993, 1.251, 0.1966, 0.0000},
+    {14, 4, 0.5, 256, 7.366, 12.874, 1.225, 0.0000, 0.0000},
+    {15, 0, 0.75, 256, 10.260, 5.226, 1.886, 0.0770, 0.0000},
+    {15, 1, 1, 256, 10.682, 4.264, 1.699, 0.0083, 0.0000},
+    {15, 2, 1, 256, 8.417, 4.706, 1.838, 0.0000, 0.0000},
+    {15, 3, 1, 256, 9.672, 7.894, 1.268, 0.1412, 0.0000},
+    {15, 4, 0.5, 256, 7.929, 11.879, 1.208, 0.0000, 0.0000},
+    {16, 0, 1, 256, 7.681, 4.247, 1.716, 0.0000, 0.0000},
+    {16, 1, 1, 256, 8.624, 3.982, 1.709, 0.0000, 0.0000},
+    {16, 2, 1, 256, 6.525, 4.078, 1.922, 0.0000, 0.0000},
+    {16, 3, 0.75, 256, 7.535, 7.375, 0.000, 0.2893, 0.0000},
+    {16, 4, 0.75, 256, 6.736, 7.941, 1.861, 0.1315, 0.0000},
+    {17, 0, 0, 256, 236.744, 9.817, 0.000, 0.1532, 0.0000},
+    {17, 1, 0, 256, 289.559, 0.000, 10.965, 0.1087, 0.0000},
+    {17, 2, 0.5, 256, 238.070, 9.250, 0.336, 0.0620, 0.0000},
+    {17, 3, 1, 256, 282.211, 15.870, 0.221, 0.0000, 0.0000},
+    {17, 4, 1, 256, 289.389, 8.416, 1.934, 0.0936, 0.0000},
+    {20, 0, 1, 512, 29.176, 0.000, 3.255, 0.2359, 0.0000},
+    {20, 1, 0.25, 256, 45.603, 0.000, 5.908, 0.0000, 0.0000},
+    {20, 2, 0.25, 256, 28.724, 0.412, 4.546, 0.0276, 0.0000},
+    {20, 3, 0.5, 256, 36.809, 0.000, 8.740, 0.0000, 0.0000},
+    {20, 4, 0.25, 256, 46.385, 0.497, 4.725, 0.0000, 0.0000},
+    {26, 1, 1, 256, 4.430, 0.000, 3.796, 1.6826, 0.1950},
+    {26, 4, 1, 256, 10.586, 0.000, 2.851, 2.0567, 0.0000},
+    {27, 1, 1, 256, 10.657, 3.122, 3.082, 0.6114, 0.0660},
+    {27, 4, 1, 256, 15.740, 1.461, 2.964, 0.4300, 0.0000},
+    {28, 1, 1, 256, 15.630, 2.860, 2.724, 0.0000, 0.0707},
+    {28, 4, 1, 256, 22.280, 0.000, 1.458, 0.7435, 0.0000},
+    {29, 0, 0.25, 256, 9.776, 0.493, 3.298, 0.1214, 0.0000},
+    {29, 2, 0.5, 256, 8.419, 1.002, 3.144, 0.0000, 0.0000},
+    {29, 3, 0.75, 256, 9.878, 1.438, 4.119, 0.3371, 0.0000},
+    {30, 0, 0.25, 256, 15.907, 0.442, 3.476, 0.0498, 0.0000},
+    {30, 2, 0.25, 256, 14.384, 1.044, 3.014, 0.0000, 0.0000},
+    {30, 3, 0.75, 256, 13.387, 0.000, 4.620, 0.3017, 0.0000},
+};
+
+// Exact mode: t = (c * K / 1000 + d) * rounds + o, rounds = ceil(blocks /
+// cap) (q = 1) or max(1, blocks / cap) (q = 0), per variant and family (0
+// matrix products, 1 3x3 windows, 2 other windows), fitted to launches of
+// every variant over the ResNet-50 layers at batch 1 and 8 and the
+// benchmarked products; among fits of nearly equal error the one whose
+// choices add up to the least measured time was kept.  The chain kernel's
+// step cost is held at >= 2.5 ns (about six cycles: its dependent chain
+// cannot run faster).  Variant 20's entries carry 5 us more than its fit,
+// which keeps it off products where the other variants' estimates are too
+// high (1000 x 777 x 1531), and none for 3x3 windows.
+struct ExactCost {
+  int variant, fam, q;
+  double cap, c, d, o;
+};
+constexpr ExactCost kExactCosts[] = {
+    {2, 0, 1, 128, 107.50, 2.46, 0.0},
+    {2, 1, 0, 256, 234.52, 12.36, 0.0},
+    {2, 2, 1, 128, 117.10, 5.28, 0.0},
+    {3, 0, 1, 256, 107.61, 2.45, 0.0},
+    {3, 1, 1, 384, 237.74, 0.13, 7.3},
+    {3, 2, 1, 384, 117.04, 5.18, 0.0},
+    {4, 0, 1, 512, 107.32, 2.49, 0.0},
+    {4, 1, 0, 384, 150.49, 2.09, 4.5},
+    {4, 2, 0, 256, 107.39, 0.63, 4.6},
+    {5, 0, 1, 512, 114.71, 2.63, 0.0},
+    {5, 1, 0, 384, 215.93, 0.45, 5.7},
+    {5, 2, 0, 256, 122.63, 0.00, 4.9},
+    {6, 0, 1, 768, 15.27, 1.87, 2.2},
+    {6, 1, 0, 512, 14.85, 0.00, 8.9},
+    {6, 2, 0, 512, 13.11, 0.04, 6.0},
+    {7, 0, 1, 768, 20.41, 0.00, 3.8},
+    {7, 1, 1, 768, 21.17, 0.00, 5.9},
+    {7, 2, 1, 512, 18.33, 0.00, 4.6},
+    {8, 0, 1, 768, 32.08, 0.70, 2.0},
+    {8, 1, 0, 384, 30.40, 0.00, 2.7},
+    {8, 2, 0, 768, 37.84, 1.55, 1.8},
+    {9, 0, 0, 512, 53.02, 0.00, 3.8},
+    {9, 1, 0, 384, 55.57, 0.00, 0.9},
+    {9, 2, 0, 384, 50.09, 0.00, 4.4},
+    {10, 0, 1, 256, 7.76, 2.24, 2.8},
+    {10, 1, 0, 256, 4.79, 5.58, 5.3},
+    {10, 2, 1, 256, 7.81, 3.55, 1.5},
+    {11, 0, 0, 256, 6.73, 2.13, 3.3},
+    {11, 1, 0, 256, 4.80, 4.58, 5.5},
+    {11, 2, 1, 128, 3.33, 1.64, 1.8},
+    {12, 0, 0, 768, 5.37, 2.80, 2.4},
+    {12, 1, 0, 384, 4.14, 2.68, 6.9},
+    {12, 2, 0, 256, 2.50, 0.54, 5.0},
+    {13, 0, 1, 256, 9.99, 2.14, 2.3},
+    {13, 1, 0, 256, 7.66, 5.79, 4.6},
+    {13, 2, 1, 256, 9.85, 3.39, 1.2},
+    {17, 0, 1, 64, 107.62, 2.42, 0.0},
+    {17, 1, 0, 256, 234.57, 12.35, 0.0},
+    {17, 2, 0, 64, 113.24, 0.00, 4.5},
+    {20, 0, 1, 512, 60.94, 1.89, 5.93},
+    {20, 1, 0, 384, 1e9, 0.00, 0.0},
+    {20, 2, 0, 256, 60.54, 0.00, 5.35},
 };
 
 // Blocks of a launch of variant t (columns per image where that kernel tiles so).
@@ -171,37 +278,48 @@ int64_t launch_blocks(const Tile &t, const Shape &s) {
   return ceil_div(s.M, bm) * ncol * s.groups;
 }
 
-double estimate(const Tile &t, const Shape &s, int mode) {
-  // family of the shape: 0 matrix product, 1 3x3 window, 2 other windows
-  const int fam = s.khw == 0 ? 0 : s.khw == 9 ? 1 : 2;
-  for (const Cost &c : kCosts) {
-    if (c.variant != t.variant || c.fam != fam) continue;
-    const bool ex = mode == OG_MODE_EXACT;
-    const double cap = ex ? c.cap_exact : c.cap_fast;
-    const double per = (ex ? c.c_exact : c.c_fast) * 1e-3;
-    const double d = ex ? c.d_exact : c.d_fast, o = ex ? c.o_exact : c.o_fast;
+// Fast-mode estimate of `variant` on a launch of `blocks` blocks; 1e300
+// where the variant has no entry for the shape's family.
+double fast_estimate(int variant, const Shape &s, int64_t blocks) {
+  for (const FastCost &c : kFastCosts) {
+    if (c.variant != variant || c.fam != s.ffam) continue;
     const double k = (double)(s.K > 0 ? s.K : 1);
-    const double x = (double)launch_blocks(t, s) / cap;
-    const double rounds = (ex ? c.q_exact : c.q_fast) ? std::ceil(x) : std::max(1.0, x);
-    return (per * k + d) * rounds + o;
+    const double x = (double)blocks / c.cap;
+    const double rounds = std::max(1.0, (1.0 - c.q) * x + c.q * std::ceil(x));
+    return (c.c * 1e-3 * k + c.d + c.e * s.halo_x) * rounds + c.o + c.b * 1e-6 * s.bytes;
   }
   return 1e300;
 }
 
-// The kernel chosen from the shape alone: the lowest estimate.
+double estimate(const Tile &t, const Shape &s, int mode) {
+  if (mode != OG_MODE_EXACT) return fast_estimate(t.variant, s, launch_blocks(t, s));
+  // family of the shape: 0 matrix product, 1 3x3 window, 2 other windows
+  const int fam = s.khw == 0 ? 0 : s.khw == 9 ? 1 : 2;
+  for (const ExactCost &c : kExactCosts) {
+    if (c.variant != t.variant || c.fam != fam) continue;
+    const double k = (double)(s.K > 0 ? s.K : 1);
+    const double x = (double)launch_blocks(t, s) / c.cap;
+    const double rounds = c.q ? std::ceil(x) : std::max(1.0, x);
+    return (c.c * 1e-3 * k + c.d) * rounds + c.o;
+  }
+  return 1e300;
+}
+
+// The kernel chosen from the shape alone: the tile variant of the lowest
+// estimate.
 const Tile &choose_tile(const Shape &s, int mode) {
   int best = 3;
   double best_cost = 1e300;
-  for (const Cost &c : kCosts) {
-    if (c.fam) continue;  // each variant once
+  for (const Tile &t : kTiles) {
+    if (t.variant == 1) continue;  // the VALU kernel: for the tests only
     // the chain kernel runs windows other than 1x1 and 3x3 as variant 6
-    if (is_chain(tile_for_variant(c.variant)) && s.khw != 0 && s.khw != 1 && s.khw != 9) continue;
-    if (c.variant == 9 && mode == OG_MODE_EXACT) continue;  // eight rows per lane: VALU-bound in exact mode
-    if (c.variant >= 14 && c.variant <= 16 && mode == OG_MODE_EXACT) continue;  // run as 10, 13, 11
-    const double e = estimate(tile_for_variant(c.variant), s, mode);
+    if (is_chain(t) && s.khw != 0 && s.khw != 1 && s.khw != 9) continue;
+    if (t.variant == 9 && mode == OG_MODE_EXACT) continue;  // eight rows per lane: VALU-bound in exact mode
+    if (t.variant >= 14 && t.variant <= 16 && mode == OG_MODE_EXACT) continue;  // run as 10, 13, 11
+    const double e = estimate(t, s, mode);
     if (e < best_cost) {
       best_cost = e;
-      best = c.variant;
+      best = t.variant;
     }
   }
   return tile_for_variant(best);
@@ -377,54 +495,33 @@ int mode2_variant(const Shape &s, double fast_estimate) {
   return best;
 }
 
-// A split-k variant forced in exact or fast mode: refused (neither mode's
-// bits can come from it).
-// The halo kernel's time (variants 26 and 27, fast mode), fitted to the
-// ResNet-50 3x3 layers at batch 1 to 16: a round of blocks (one per
-// compute unit) takes c ns per tap of k plus d us; where the LDS holds two
-// or more blocks per compute unit, rounds overlap by kHaloOverlap.  (Within
-// 10 % of the measured times of the stride-1 layers; the stride-2 layers
-// stage taller halos and run up to 30 % over, where the kernel is not the
-// faster one.)
-struct HaloCost {
-  int variant, rows;
-  double c, d;
-};
-constexpr HaloCost kHaloCosts[] = {{26, 16, 10.4, 5.5}, {27, 32, 13.8, 5.6}};
-constexpr double kHaloOverlap = 1.25;
-
-double halo_estimate(const HaloCost &hc, const Shape &s, int64_t images, int64_t halo_lds) {
-  const int64_t blocks = ceil_div(s.M, hc.rows) * images * ceil_div(s.ohw, 64) * s.groups;
-  const int64_t lds = halo_lds + (int64_t)hc.rows * 3 * 144 * 4;  // halo and weight stages
-  const double x = (double)blocks / 256.0;
-  const double rounds = kHaloMaxLds / lds >= 2 ? std::max(1.0, x / kHaloOverlap) : std::ceil(x);
-  return (hc.c * 1e-3 * (double)s.K + hc.d) * rounds;
-}
-
-// The panel kernel's time (variants 29 and 30, fast mode), fitted to the
-// ResNet-50 1x1 layers at batch 1 to 16 and ten products: (c ns per step
-// of k + d us) per round of cap blocks, plus o us; mean error 10 % there
-// and 9 % on held-out shapes (the MobileNetV3-large 1x1 layers at batch 1
-// and 8, twelve seeded random products).
-struct PanelCost {
-  int variant, rows;
-  double cap, c, d, o;
-};
-constexpr PanelCost kPanelCosts[] = {{29, 16, 320, 10.83, 1.38, 2.30}, {30, 32, 320, 16.52, 1.59, 2.23}};
-
-// The lower of the two estimates for a product (images = 0) or a 1x1
-// convolution of `images` images with ohw output pixels each; its variant.
-double panel_estimate(const Shape &s, int64_t images, int *variant) {
+// The halo kernel's estimate for a 3x3 convolution of `images` images
+// (variants 26, 27 and 28: 16, 32 and 32 rows per block, blocks of 64
+// output pixels of one image); the variant of the lowest.
+double halo_estimate(const Shape &s, int64_t images, int *variant) {
   double best = 1e300;
-  for (const PanelCost &pc : kPanelCosts) {
-    const int64_t cols = images > 0 ? images * ceil_div(s.ohw, 64) : ceil_div(s.N, 64);
-    const double x = (double)(ceil_div(s.M, pc.rows) * cols * s.groups) / pc.cap;
-    const double e = (pc.c * 1e-3 * (double)s.K + pc.d) * std::max(1.0, x) + pc.o;
-    if (e < best) best = e, *variant = pc.variant;
+  for (const auto [v, rows] : {std::pair<int, int64_t>{26, 16}, {27, 32}, {28, 32}}) {
+    const double e = fast_estimate(v, s, ceil_div(s.M, rows) * images * ceil_div(s.ohw, 64) * s.groups);
+    if (e < best) best = e, *variant = v;
   }
   return best;
 }
 
+// The panel kernel's estimate for a product (images = 0) or a 1x1
+// convolution of `images` images with ohw output pixels each (variants 29
+// and 30: 16 and 32 rows per block, 64 columns); the variant of the lower.
+double panel_estimate(const Shape &s, int64_t images, int *variant) {
+  double best = 1e300;
+  for (const auto [v, rows] : {std::pair<int, int64_t>{29, 16}, {30, 32}}) {
+    const int64_t cols = images > 0 ? images * ceil_div(s.ohw, 64) : ceil_div(s.N, 64);
+    const double e = fast_estimate(v, s, ceil_div(s.M, rows) * cols * s.groups);
+    if (e < best) best = e, *variant = v;
+  }
+  return best;
+}
+
+// A split-k variant forced in exact or fast mode: refused (neither mode's
+// bits can come from it).
 og_status refuse_split(const char *what, int mode) {
   if (mode != OG_MODE_FAST_MFMA && is_split(t_variant))
     return fail(OG_ERR_NOT_EXACT, "%s: variant %d has no %s form (split-k kernels run only in "
@@ -460,7 +557,7 @@ og_status og_gemm_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_t l
     return fail(OG_ERR_TOO_LARGE, "og_gemm_f32: lda or ldb exceeds 2^22");
   og_status st = refuse_split("og_gemm_f32", mode);
   if (st != OG_OK) return st;
-  const Shape sh{m, n, k, 1, 0, 0};
+  const Shape sh{m, n, k, 1, 0, 0, 0, 4.0 * ((double)m * k + (double)k * n + (double)m * n)};
   // the panel kernel (fast mode): its variant of the lower estimate
   int panel_v = 0;
   const double panel_est =
@@ -556,7 +653,7 @@ og_status og_gemm_nt_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_
     return fail(OG_ERR_TOO_LARGE, "og_gemm_nt_f32: lda or ldb exceeds 2^22");
   og_status st = refuse_split("og_gemm_nt_f32", mode);
   if (st != OG_OK) return st;
-  const Shape sh{m, n, k, 1, 0, 0};
+  const Shape sh{m, n, k, 1, 0, 0, 0, 4.0 * ((double)m * k + (double)k * n + (double)m * n)};
   const int split =
       mode == OG_MODE_FAST_MFMA
           ? mode2_variant(sh, estimate(pick_nt(sh, OG_MODE_FAST), sh, OG_MODE_FAST))
@@ -706,7 +803,8 @@ og_status conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout, int
                       padLeft == 0 && padBottom == 0 && padRight == 0;
   og_status st = refuse_split("og_conv2d_f32", mode);
   if (st != OG_OK) return st;
-  const Shape sh{cout_g, ncols, K, G, OH * OW, KH * KW};
+  Shape sh{cout_g, ncols, K, G, OH * OW, KH * KW, fast_family(KH, KW, planes, strideH, strideW),
+           4.0 * ((double)N * Cin * H * W + (double)Cout * K + (double)Cout * ncols)};
   // depthwise, grouped-direct and single-column shapes keep their fast
   // kernels in mode 2 unless a split-k variant is forced
   const bool own_kernel = cin_g == 1 || (G > 1 && cin_g <= 64 && cout_g <= 8 && KH == 3 && KW == 3) ||
@@ -752,10 +850,10 @@ og_status conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout, int
   double halo_est = 1e300;
   if (KH == 3 && KW == 3 && !planes && !own_kernel && halo_plan(p, aligned16(x), hplan) &&
       ceil_div(cout_g, 16) * N * ceil_div(OH * OW, 64) * G <= kI32Max) {
-    for (const HaloCost &hc : kHaloCosts) {
-      const double e = halo_estimate(hc, sh, N, hplan.halo_lds);
-      if (e < halo_est) halo_est = e, halo_v = hc.variant;
-    }
+    // the input floats a block stages over its k: 16 channels of hplan.rows
+    // padded rows per chunk of 144 taps
+    sh.halo_x = (double)K / 144.0 * (double)(hplan.halo_lds / 12) * 1e-3;
+    halo_est = halo_estimate(sh, N, &halo_v);
   }
   // the panel kernel (fast mode, 1x1 windows): its variant of the lower estimate
   int panel_v = 0;

@@ -238,10 +238,16 @@ void *og_get_stream(void);
  * with the weights broadcast from one block); 4 waves of 4 rows, 4 waves
  * of 2 x 4 rows and 8 waves of 4 rows.  In exact mode, and on shapes they
  * do not take, they run as 0 does.
+ * 29, 30 = the panel kernel (fast mode, og_gemm_f32 products and 1x1
+ * convolutions): panels of 64 columns of B (input pixels) loaded straight
+ * into LDS stages, the weight rows of each wave through its own LDS
+ * stages, the k chain of each 4 rows on the matrix cores as in 26..28;
+ * 4 waves of 4 rows and 4 waves of 2 x 4 rows.  In exact mode, and on
+ * shapes they do not take (other windows), they run as 0 does.
  * Every variant runs every shape (a convolution window other than 1x1 or
  * 3x3 runs variants 10..16 as variant 6; variants 18 and 19 run shapes
  * outside their own, and any matrix product, as 0 does).  A value outside
- * 0..28 returns OG_ERR_INVALID_ARG.
+ * 0..30 returns OG_ERR_INVALID_ARG.
  */
 og_status og_set_variant(int variant);
 int og_get_variant(void);
