@@ -1,4 +1,4 @@
-"""Measures the regret of libog's automatic kernel choice in fast mode: for
+"""Measures the regret of libog's automatic kernel choice (fast or exact mode): for
 each shape of a set, the time of the automatic choice (variant 0) over the
 best time of every variant that runs the shape, each forced with
 og_set_variant.  Needs a GPU.
@@ -11,7 +11,8 @@ products.  "heldout": shapes the fit did not see -- ResNet-50 at batch 7
 and 10, MobileNetV3-large at batch 3 and 5, four more 3x3 convolutions and
 24 random products of another seed.
 
-    python3 -m fp32_blocked_gemm_amd.choice_sweep [--set fit|heldout] [--out FILE] [--quick]
+    python3 -m fp32_blocked_gemm_amd.choice_sweep [--set fit|heldout] [--mode fast|exact]
+        [--only3x3] [--variants 26,27,28] [--out FILE] [--quick]
 
 prints one JSON line per shape (times in us) and a summary line.
 """
@@ -26,7 +27,12 @@ def main() -> None:
     ap.add_argument("--out", default=None, help="also write the lines to this file")
     ap.add_argument("--set", default="heldout", choices=("fit", "heldout"))
     ap.add_argument("--quick", action="store_true", help="the first ResNet-50 batch only, 6 products")
+    ap.add_argument("--mode", default="fast", choices=("fast", "exact"))
+    ap.add_argument("--only3x3", action="store_true", help="3x3 convolutions only")
+    ap.add_argument("--variants", default=None,
+                    help="comma-separated variants to time besides 0 (default: every one that runs the shape)")
     args = ap.parse_args()
+    only = [int(v) for v in args.variants.split(",")] if args.variants else None
     import torch
 
     import synth
@@ -49,19 +55,28 @@ def main() -> None:
         del g
         return round(ms * 1e3, 2)
 
-    # variants that run a shape in fast mode: every tile variant, and the
-    # kernels of their own forms where the shape is theirs
+    # variants that run a shape: every tile variant (exact mode runs 14..16
+    # as others and refuses none), and the kernels of their own forms where
+    # the shape is theirs (the panel kernel in fast mode only)
     tiles = list(range(1, 18)) + [20]
+    if args.mode == "exact":
+        tiles = [v for v in tiles if v not in (14, 15, 16)]
+    panel = [29, 30] if args.mode == "fast" else []
+
+    def keep(vs):
+        return [v for v in vs if only is None or v in only]
 
     def conv_variants(s):
         if s.Cin // s.groups == 1:
             return None  # depthwise: its own kernel only
+        if args.only3x3 and not (s.KH == 3 and s.KW == 3):
+            return None
         v = list(tiles)
         if s.KH == 3 and s.KW == 3:
             v += [26, 27, 28]
         if s.KH == 1 and s.KW == 1:
-            v += [29, 30]
-        return v
+            v += panel
+        return keep(v)
 
     regrets = []
 
@@ -77,7 +92,7 @@ def main() -> None:
         for v in [0] + vs:
             og.set_variant(v)
             e[str(v)] = t_of(lambda: og.conv2d(dx, dw, stride=s.stride, pad=s.pad, dil=s.dil,
-                                               groups=s.groups, mode="fast", out=y))
+                                               groups=s.groups, mode=args.mode, out=y))
         og.set_variant(0)
         best = min(e[str(v)] for v in [0] + vs)
         e["best"] = min(([0] + vs), key=lambda v: e[str(v)])
@@ -89,11 +104,13 @@ def main() -> None:
         A = torch.randn(m, k + ld, device="cuda")[:, :k]
         B = torch.randn(k, n + ld, device="cuda")[:, :n]
         C = torch.empty(m, n + ld, device="cuda")[:, :n]
-        vs = tiles + [29, 30]
+        if args.only3x3:
+            return
+        vs = keep(tiles + panel)
         e = {"set": tag, "kind": "gemm", "shape": f"{m}x{n}x{k} row strides +{ld}", "dims": [m, n, k, ld]}
         for v in [0] + vs:
             og.set_variant(v)
-            e[str(v)] = t_of(lambda: og.gemm(A, B, "fast", out=C))
+            e[str(v)] = t_of(lambda: og.gemm(A, B, args.mode, out=C))
         og.set_variant(0)
         best = min(e[str(v)] for v in [0] + vs)
         e["best"] = min(([0] + vs), key=lambda v: e[str(v)])

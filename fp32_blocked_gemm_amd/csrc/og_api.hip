@@ -104,13 +104,13 @@ int fast_family(int64_t KH, int64_t KW, bool planes, int64_t strideH, int64_t st
 // launched on every variant on the MI355X (ResNet-50's convolutions at
 // batch 1, 2, 3, 4, 5, 6, 8, 12 and 16, MobileNetV3-large's ungrouped ones
 // at batch 1, 2, 4, 6 and 8, twelve 3x3 convolutions of other widths, 72
-// seeded random matrix products): mean error 4.8 %.  Variants 26..28 are the
+// seeded random matrix products): mean error 4.5 %.  Variants 26..28 are the
 // halo kernel, 29 and 30 the panel kernel.
-struct FastCost {
+struct ModelCost {
   int variant, fam;
   double q, cap, c, d, o, b, e;
 };
-constexpr FastCost kFastCosts[] = {
+constexpr ModelCost kFastCosts[] = {
     {2, 0, 0, 256, 132.150, 9.037, 0.000, 0.0790, 0.0000},
     {2, 1, 0, 256, 200.488, 0.000, 9.607, 0.0977, 0.0000},
     {2, 2, 0.75, 256, 135.149, 0.000, 8.754, 0.0683, 0.0000},
@@ -196,12 +196,12 @@ constexpr FastCost kFastCosts[] = {
     {20, 2, 0.25, 256, 28.724, 0.412, 4.546, 0.0276, 0.0000},
     {20, 3, 0.5, 256, 36.809, 0.000, 8.740, 0.0000, 0.0000},
     {20, 4, 0.25, 256, 46.385, 0.497, 4.725, 0.0000, 0.0000},
-    {26, 1, 1, 256, 4.430, 0.000, 3.796, 1.6826, 0.1950},
-    {26, 4, 1, 256, 10.586, 0.000, 2.851, 2.0567, 0.0000},
-    {27, 1, 1, 256, 10.657, 3.122, 3.082, 0.6114, 0.0660},
-    {27, 4, 1, 256, 15.740, 1.461, 2.964, 0.4300, 0.0000},
-    {28, 1, 1, 256, 15.630, 2.860, 2.724, 0.0000, 0.0707},
-    {28, 4, 1, 256, 22.280, 0.000, 1.458, 0.7435, 0.0000},
+    {26, 1, 1, 256, 1.671, 0.443, 4.021, 1.4895, 0.2057},
+    {26, 4, 1, 256, 6.547, 3.368, 2.024, 0.0114, 0.0700},
+    {27, 1, 0.75, 256, 7.114, 3.167, 2.203, 0.3561, 0.1637},
+    {27, 4, 1, 256, 9.472, 3.278, 2.821, 0.1519, 0.0605},
+    {28, 1, 1, 256, 9.616, 3.367, 1.820, 0.1295, 0.1170},
+    {28, 4, 1, 256, 13.012, 0.728, 5.132, 0.3597, 0.0000},
     {29, 0, 0.25, 256, 9.776, 0.493, 3.298, 0.1214, 0.0000},
     {29, 2, 0.5, 256, 8.419, 1.002, 3.144, 0.0000, 0.0000},
     {29, 3, 0.75, 256, 9.878, 1.438, 4.119, 0.3371, 0.0000},
@@ -210,63 +210,86 @@ constexpr FastCost kFastCosts[] = {
     {30, 3, 0.75, 256, 13.387, 0.000, 4.620, 0.3017, 0.0000},
 };
 
-// Exact mode: t = (c * K / 1000 + d) * rounds + o, rounds = ceil(blocks /
-// cap) (q = 1) or max(1, blocks / cap) (q = 0), per variant and family (0
-// matrix products, 1 3x3 windows, 2 other windows), fitted to launches of
-// every variant over the ResNet-50 layers at batch 1 and 8 and the
-// benchmarked products; among fits of nearly equal error the one whose
-// choices add up to the least measured time was kept.  The chain kernel's
-// step cost is held at >= 2.5 ns (about six cycles: its dependent chain
-// cannot run faster).  Variant 20's entries carry 5 us more than its fit,
-// which keeps it off products where the other variants' estimates are too
-// high (1000 x 777 x 1531), and none for 3x3 windows.
-struct ExactCost {
-  int variant, fam, q;
-  double cap, c, d, o;
-};
-constexpr ExactCost kExactCosts[] = {
-    {2, 0, 1, 128, 107.50, 2.46, 0.0},
-    {2, 1, 0, 256, 234.52, 12.36, 0.0},
-    {2, 2, 1, 128, 117.10, 5.28, 0.0},
-    {3, 0, 1, 256, 107.61, 2.45, 0.0},
-    {3, 1, 1, 384, 237.74, 0.13, 7.3},
-    {3, 2, 1, 384, 117.04, 5.18, 0.0},
-    {4, 0, 1, 512, 107.32, 2.49, 0.0},
-    {4, 1, 0, 384, 150.49, 2.09, 4.5},
-    {4, 2, 0, 256, 107.39, 0.63, 4.6},
-    {5, 0, 1, 512, 114.71, 2.63, 0.0},
-    {5, 1, 0, 384, 215.93, 0.45, 5.7},
-    {5, 2, 0, 256, 122.63, 0.00, 4.9},
-    {6, 0, 1, 768, 15.27, 1.87, 2.2},
-    {6, 1, 0, 512, 14.85, 0.00, 8.9},
-    {6, 2, 0, 512, 13.11, 0.04, 6.0},
-    {7, 0, 1, 768, 20.41, 0.00, 3.8},
-    {7, 1, 1, 768, 21.17, 0.00, 5.9},
-    {7, 2, 1, 512, 18.33, 0.00, 4.6},
-    {8, 0, 1, 768, 32.08, 0.70, 2.0},
-    {8, 1, 0, 384, 30.40, 0.00, 2.7},
-    {8, 2, 0, 768, 37.84, 1.55, 1.8},
-    {9, 0, 0, 512, 53.02, 0.00, 3.8},
-    {9, 1, 0, 384, 55.57, 0.00, 0.9},
-    {9, 2, 0, 384, 50.09, 0.00, 4.4},
-    {10, 0, 1, 256, 7.76, 2.24, 2.8},
-    {10, 1, 0, 256, 4.79, 5.58, 5.3},
-    {10, 2, 1, 256, 7.81, 3.55, 1.5},
-    {11, 0, 0, 256, 6.73, 2.13, 3.3},
-    {11, 1, 0, 256, 4.80, 4.58, 5.5},
-    {11, 2, 1, 128, 3.33, 1.64, 1.8},
-    {12, 0, 0, 768, 5.37, 2.80, 2.4},
-    {12, 1, 0, 384, 4.14, 2.68, 6.9},
-    {12, 2, 0, 256, 2.50, 0.54, 5.0},
-    {13, 0, 1, 256, 9.99, 2.14, 2.3},
-    {13, 1, 0, 256, 7.66, 5.79, 4.6},
-    {13, 2, 1, 256, 9.85, 3.39, 1.2},
-    {17, 0, 1, 64, 107.62, 2.42, 0.0},
-    {17, 1, 0, 256, 234.57, 12.35, 0.0},
-    {17, 2, 0, 64, 113.24, 0.00, 4.5},
-    {20, 0, 1, 512, 60.94, 1.89, 5.93},
-    {20, 1, 0, 384, 1e9, 0.00, 0.0},
-    {20, 2, 0, 256, 60.54, 0.00, 5.35},
+// Exact mode: the same form and families, fitted the same way to the same
+// shapes launched in exact mode (variants 14..16 run as 10, 13 and 11 there;
+// the panel kernel has no exact form).
+constexpr ModelCost kExactCosts[] = {
+    {2, 0, 0, 256, 101.213, 5.867, 0.000, 0.3088, 0.0000},
+    {2, 1, 0, 256, 235.881, 0.000, 0.000, 1.6945, 0.0000},
+    {2, 2, 1, 256, 104.747, 0.000, 4.018, 0.2369, 0.0000},
+    {2, 3, 1, 256, 218.297, 14.892, 0.000, 0.1956, 0.0000},
+    {2, 4, 0.75, 256, 234.074, 6.003, 0.000, 0.6898, 0.0000},
+    {3, 0, 1, 256, 101.045, 6.017, 0.000, 0.2697, 0.0000},
+    {3, 1, 0, 256, 237.329, 0.000, 7.556, 0.0000, 0.0000},
+    {3, 2, 1, 256, 104.433, 0.000, 4.625, 0.0646, 0.0000},
+    {3, 3, 0, 256, 227.422, 0.000, 10.802, 0.0000, 0.0000},
+    {3, 4, 0, 256, 237.574, 2.833, 4.089, 0.0000, 0.0000},
+    {4, 0, 0, 256, 99.514, 0.000, 6.835, 0.0000, 0.0000},
+    {4, 1, 0, 256, 151.018, 0.000, 6.039, 0.0000, 0.0000},
+    {4, 2, 0, 256, 103.386, 0.000, 4.837, 0.0349, 0.0000},
+    {4, 3, 0.5, 512, 141.624, 2.887, 5.247, 0.3364, 0.0000},
+    {4, 4, 0, 256, 151.080, 0.736, 4.422, 0.0532, 0.0000},
+    {5, 0, 1, 512, 109.297, 0.000, 6.162, 0.2407, 0.0000},
+    {5, 1, 0, 512, 216.461, 0.000, 1.328, 0.8328, 0.0000},
+    {5, 2, 1, 512, 118.186, 0.028, 4.241, 0.1464, 0.0000},
+    {5, 3, 0.25, 512, 203.916, 0.489, 10.213, 0.2272, 0.0000},
+    {5, 4, 0.5, 256, 215.736, 0.000, 6.273, 0.0000, 0.0000},
+    {6, 0, 0.5, 768, 15.469, 0.083, 2.504, 0.7430, 0.0000},
+    {6, 1, 0.25, 768, 19.610, 0.000, 4.462, 0.0000, 0.0000},
+    {6, 2, 0.5, 768, 14.674, 0.586, 2.825, 0.1742, 0.0000},
+    {6, 3, 0.5, 768, 20.707, 4.075, 1.083, 0.0000, 0.0000},
+    {6, 4, 0.5, 512, 18.571, 0.000, 2.904, 0.6610, 0.0000},
+    {7, 0, 0.5, 768, 20.004, 0.000, 2.505, 0.4969, 0.0000},
+    {7, 1, 0.5, 768, 22.475, 0.000, 4.213, 0.0000, 0.0000},
+    {7, 2, 0.5, 768, 20.429, 0.557, 2.781, 0.1081, 0.0000},
+    {7, 3, 0.25, 512, 15.714, 2.626, 6.937, 0.0000, 0.0000},
+    {7, 4, 0.25, 512, 23.841, 0.000, 3.332, 0.2151, 0.0000},
+    {8, 0, 0.5, 512, 30.410, 0.000, 3.035, 0.1666, 0.0000},
+    {8, 1, 0.5, 512, 31.168, 0.000, 5.015, 0.0000, 0.0000},
+    {8, 2, 0.75, 768, 32.286, 0.373, 2.846, 0.1809, 0.0000},
+    {8, 3, 0.5, 768, 31.659, 6.956, 0.922, 0.0000, 0.0000},
+    {8, 4, 0.5, 512, 34.199, 0.000, 3.295, 0.1827, 0.0000},
+    {9, 0, 1, 512, 51.502, 0.000, 3.381, 0.2339, 0.0000},
+    {9, 1, 0.25, 512, 52.140, 0.000, 4.045, 0.7324, 0.0000},
+    {9, 2, 0.25, 512, 51.023, 0.269, 3.673, 0.1550, 0.0000},
+    {9, 3, 0, 512, 39.133, 9.928, 3.916, 0.0000, 0.0000},
+    {9, 4, 0.5, 512, 54.581, 0.000, 3.270, 0.3806, 0.0000},
+    {10, 0, 1, 256, 7.285, 3.324, 1.735, 0.0000, 0.0000},
+    {10, 1, 1, 256, 5.908, 3.806, 1.812, 0.0693, 0.0000},
+    {10, 2, 1, 256, 6.559, 3.584, 1.781, 0.0000, 0.0000},
+    {10, 3, 0.5, 512, 15.522, 13.777, 0.000, 0.4231, 0.0000},
+    {10, 4, 0.75, 256, 5.230, 5.068, 2.269, 0.1950, 0.0000},
+    {11, 0, 1, 256, 6.521, 2.895, 1.708, 0.0000, 0.0000},
+    {11, 1, 1, 256, 5.729, 3.097, 1.304, 0.0581, 0.0000},
+    {11, 2, 1, 256, 5.866, 3.245, 1.705, 0.0724, 0.0000},
+    {11, 3, 0.25, 1024, 25.921, 26.732, 0.000, 0.5407, 0.0000},
+    {11, 4, 0.5, 256, 5.239, 4.136, 2.964, 0.0246, 0.0000},
+    {12, 0, 0.25, 512, 3.835, 1.173, 3.536, 0.6924, 0.0000},
+    {12, 1, 1, 256, 3.152, 1.188, 3.755, 0.0733, 0.0000},
+    {12, 2, 0.25, 512, 3.691, 1.351, 3.962, 0.0759, 0.0000},
+    {12, 3, 0.25, 1024, 9.803, 5.836, 5.034, 0.0000, 0.0000},
+    {12, 4, 0.5, 256, 2.971, 1.611, 4.888, 0.0190, 0.0000},
+    {13, 0, 1, 256, 9.622, 3.339, 1.801, 0.0000, 0.0000},
+    {13, 1, 1, 256, 9.141, 3.439, 1.583, 0.0192, 0.0000},
+    {13, 2, 1, 256, 8.833, 3.567, 1.709, 0.0000, 0.0000},
+    {13, 3, 0.25, 512, 16.051, 13.456, 0.000, 0.3438, 0.0000},
+    {13, 4, 0.75, 256, 8.159, 5.185, 2.304, 0.2008, 0.0000},
+    {17, 0, 0, 256, 101.175, 5.864, 0.000, 0.3118, 0.0000},
+    {17, 1, 0, 256, 235.908, 0.000, 0.000, 1.6983, 0.0000},
+    {17, 2, 0.25, 256, 104.334, 0.000, 3.960, 0.2632, 0.0000},
+    {17, 3, 1, 256, 218.246, 14.904, 0.000, 0.1962, 0.0000},
+    {17, 4, 0.75, 256, 234.144, 6.004, 0.000, 0.6884, 0.0000},
+    {20, 0, 1, 512, 58.722, 0.000, 3.245, 0.2239, 0.0000},
+    {20, 1, 0.25, 512, 92.985, 0.000, 2.441, 0.9360, 0.0000},
+    {20, 2, 1, 512, 58.484, 0.412, 4.382, 0.1826, 0.0000},
+    {20, 3, 0.5, 512, 90.270, 0.106, 8.587, 0.0740, 0.0000},
+    {20, 4, 0.75, 768, 91.113, 0.549, 3.833, 0.7017, 0.0000},
+    {26, 1, 0.75, 512, 6.259, 2.194, 0.000, 3.1981, 0.5083},
+    {26, 4, 1, 256, 16.267, 3.462, 2.003, 0.0199, 0.0627},
+    {27, 1, 0.5, 256, 24.327, 1.948, 3.724, 0.8510, 0.2805},
+    {27, 4, 1, 256, 29.868, 4.052, 2.266, 0.1788, 0.0566},
+    {28, 1, 1, 256, 19.777, 3.068, 1.932, 0.2230, 0.0829},
+    {28, 4, 1, 256, 20.855, 2.529, 3.680, 0.3044, 0.0361},
 };
 
 // Blocks of a launch of variant t (columns per image where that kernel tiles so).
@@ -278,31 +301,25 @@ int64_t launch_blocks(const Tile &t, const Shape &s) {
   return ceil_div(s.M, bm) * ncol * s.groups;
 }
 
-// Fast-mode estimate of `variant` on a launch of `blocks` blocks; 1e300
-// where the variant has no entry for the shape's family.
-double fast_estimate(int variant, const Shape &s, int64_t blocks) {
-  for (const FastCost &c : kFastCosts) {
-    if (c.variant != variant || c.fam != s.ffam) continue;
-    const double k = (double)(s.K > 0 ? s.K : 1);
-    const double x = (double)blocks / c.cap;
-    const double rounds = std::max(1.0, (1.0 - c.q) * x + c.q * std::ceil(x));
-    return (c.c * 1e-3 * k + c.d + c.e * s.halo_x) * rounds + c.o + c.b * 1e-6 * s.bytes;
-  }
-  return 1e300;
+// Estimate of `variant` on a launch of `blocks` blocks in exact or fast mode
+// (mode 2 uses the fast one); 1e300 where the variant has no entry for the
+// shape's family.
+double model_estimate(int mode, int variant, const Shape &s, int64_t blocks) {
+  auto scan = [&](const auto &table) {
+    for (const ModelCost &c : table) {
+      if (c.variant != variant || c.fam != s.ffam) continue;
+      const double k = (double)(s.K > 0 ? s.K : 1);
+      const double x = (double)blocks / c.cap;
+      const double rounds = std::max(1.0, (1.0 - c.q) * x + c.q * std::ceil(x));
+      return (c.c * 1e-3 * k + c.d + c.e * s.halo_x) * rounds + c.o + c.b * 1e-6 * s.bytes;
+    }
+    return 1e300;
+  };
+  return mode == OG_MODE_EXACT ? scan(kExactCosts) : scan(kFastCosts);
 }
 
 double estimate(const Tile &t, const Shape &s, int mode) {
-  if (mode != OG_MODE_EXACT) return fast_estimate(t.variant, s, launch_blocks(t, s));
-  // family of the shape: 0 matrix product, 1 3x3 window, 2 other windows
-  const int fam = s.khw == 0 ? 0 : s.khw == 9 ? 1 : 2;
-  for (const ExactCost &c : kExactCosts) {
-    if (c.variant != t.variant || c.fam != fam) continue;
-    const double k = (double)(s.K > 0 ? s.K : 1);
-    const double x = (double)launch_blocks(t, s) / c.cap;
-    const double rounds = c.q ? std::ceil(x) : std::max(1.0, x);
-    return (c.c * 1e-3 * k + c.d) * rounds + c.o;
-  }
-  return 1e300;
+  return model_estimate(mode, t.variant, s, launch_blocks(t, s));
 }
 
 // The kernel chosen from the shape alone: the tile variant of the lowest
@@ -314,7 +331,6 @@ const Tile &choose_tile(const Shape &s, int mode) {
     if (t.variant == 1) continue;  // the VALU kernel: for the tests only
     // the chain kernel runs windows other than 1x1 and 3x3 as variant 6
     if (is_chain(t) && s.khw != 0 && s.khw != 1 && s.khw != 9) continue;
-    if (t.variant == 9 && mode == OG_MODE_EXACT) continue;  // eight rows per lane: VALU-bound in exact mode
     if (t.variant >= 14 && t.variant <= 16 && mode == OG_MODE_EXACT) continue;  // run as 10, 13, 11
     const double e = estimate(t, s, mode);
     if (e < best_cost) {
@@ -495,13 +511,15 @@ int mode2_variant(const Shape &s, double fast_estimate) {
   return best;
 }
 
-// The halo kernel's estimate for a 3x3 convolution of `images` images
-// (variants 26, 27 and 28: 16, 32 and 32 rows per block, blocks of 64
-// output pixels of one image); the variant of the lowest.
-double halo_estimate(const Shape &s, int64_t images, int *variant) {
+// The halo kernel's estimate for a 3x3 convolution whose images hold
+// `tiles` tiles of 64 lanes in all (variants 26, 27 and 28: 16, 32 and 32
+// rows per block; those whose block fits the LDS), in exact or fast mode;
+// the variant of the lowest.
+double halo_estimate(int mode, const Shape &s, const HaloPlan &h, int64_t tiles, int *variant) {
   double best = 1e300;
   for (const auto [v, rows] : {std::pair<int, int64_t>{26, 16}, {27, 32}, {28, 32}}) {
-    const double e = fast_estimate(v, s, ceil_div(s.M, rows) * images * ceil_div(s.ohw, 64) * s.groups);
+    if (!halo_fits(h, v)) continue;
+    const double e = model_estimate(mode, v, s, ceil_div(s.M, rows) * tiles * s.groups);
     if (e < best) best = e, *variant = v;
   }
   return best;
@@ -514,7 +532,7 @@ double panel_estimate(const Shape &s, int64_t images, int *variant) {
   double best = 1e300;
   for (const auto [v, rows] : {std::pair<int, int64_t>{29, 16}, {30, 32}}) {
     const int64_t cols = images > 0 ? images * ceil_div(s.ohw, 64) : ceil_div(s.N, 64);
-    const double e = fast_estimate(v, s, ceil_div(s.M, rows) * cols * s.groups);
+    const double e = model_estimate(OG_MODE_FAST, v, s, ceil_div(s.M, rows) * cols * s.groups);
     if (e < best) best = e, *variant = v;
   }
   return best;
@@ -846,14 +864,17 @@ og_status conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout, int
   // the halo kernel (fast mode, 3x3 windows): its staging plan and the
   // variant of the lower estimate, where it takes the shape
   HaloPlan hplan{};
-  int halo_v = 0;
-  double halo_est = 1e300;
+  bool halo_ok = false;
+  int halo_v = 0, halo_xv = 0;  // the fast and the exact variant of the lowest estimate
+  double halo_est = 1e300, halo_xest = 1e300;
   if (KH == 3 && KW == 3 && !planes && !own_kernel && halo_plan(p, aligned16(x), hplan) &&
-      ceil_div(cout_g, 16) * N * ceil_div(OH * OW, 64) * G <= kI32Max) {
+      ceil_div(cout_g, 16) * N * hplan.tiles * G <= kI32Max) {
+    halo_ok = true;
     // the input floats a block stages over its k: 16 channels of hplan.rows
     // padded rows per chunk of 144 taps
-    sh.halo_x = (double)K / 144.0 * (double)(hplan.halo_lds / 12) * 1e-3;
-    halo_est = halo_estimate(sh, N, &halo_v);
+    sh.halo_x = (double)K / 144.0 * 16.0 * hplan.rows * (double)(W + padLeft + padRight) * 1e-3;
+    halo_est = halo_estimate(OG_MODE_FAST, sh, hplan, N * hplan.tiles, &halo_v);
+    halo_xest = halo_estimate(OG_MODE_EXACT, sh, hplan, N * hplan.tiles, &halo_xv);
   }
   // the panel kernel (fast mode, 1x1 windows): its variant of the lower estimate
   int panel_v = 0;
@@ -903,12 +924,17 @@ og_status conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout, int
     return check_launch("og_conv2d_f32");
   }
   // the halo kernel: forced, or chosen where its estimate is below the pick's
-  if (halo_v != 0 && mode == OG_MODE_FAST) {
-    const int hv = is_halo(t_variant) ? t_variant
-                   : t_variant == 0 && halo_est < estimate(t, sh, mode) ? halo_v
-                                                                         : 0;
+  if (halo_ok && (mode == OG_MODE_FAST || mode == OG_MODE_EXACT)) {
+    const int best_v = mode == OG_MODE_EXACT ? halo_xv : halo_v;
+    const double best_est = mode == OG_MODE_EXACT ? halo_xest : halo_est;
+    // (a forced variant whose block does not fit the LDS runs as 0 does)
+    const bool forced = is_halo(t_variant) && halo_fits(hplan, t_variant);
+    const bool automatic = t_variant == 0 || (is_halo(t_variant) && !forced);
+    const int hv = forced ? t_variant
+                   : automatic && best_v != 0 && best_est < estimate(t, sh, mode) ? best_v
+                                                                                  : 0;
     if (hv != 0) {
-      launch_halo_conv(hv, p, hplan, t_stream);
+      launch_halo_conv(hv, mode, p, hplan, t_stream);
       return check_launch("og_conv2d_f32");
     }
   }

@@ -84,6 +84,7 @@ struct Problem {
   int a_vec;             // A rows 16-byte aligned (A, lda and K multiples of 4 floats)
   int bh, ih, iw;        // depthwise band kernel: output rows per band, staged input rows, columns
   int hrows;             // halo kernel: input rows staged for a tile of 64 output pixels (at most)
+  int vpitch;            // halo kernel: > 0, lanes take consecutive cells of output rows this wide
   // convolution epilogue (null / 0: none): bias per output channel, then the
   // activation (1: ReLU), then the residual at the output's own position
   const float *bias, *res;
@@ -1752,79 +1753,104 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, chain_rows(
 // layers whose outputs split into enough chains of 4 output channels to fill
 // the chip (a batch of images through the middle of a convolution network).
 //
-// A block is CW waves over 64 consecutive output pixels of one image
-// (lane l: pixel l); wave w owns R chains of 4 output channels.  Per tap a
-// chain is one v_mfma_f32_4x4x1_16b_f32: its 16 blocks of 4x4 share the 4
-// rows, lane l gives the input value of its pixel's window at that tap and
-// holds the 4 outputs of its pixel (register i = output channel i of the
-// chain), each a single fused multiply-add -- so a chain over increasing k
-// is the fast mode's ordered sum.  The weights come through the
-// instruction's A broadcast (cbsz 4: every block takes the A values of
-// block abid): one register holds 16 taps of the chain's 4 rows, lane
-// 4b + i the weight of row i at tap b, and tap u of the 16 broadcasts block
-// u.  The rows are the wave's own: it streams them straight from memory
-// into its own ring of three LDS stages, two chunks ahead, and waits for
-// them by count.
+// A block is CW waves over 64 lanes of one image; wave w owns R chains of 4
+// output channels.  Per tap a chain is one v_mfma_f32_4x4x1_16b_f32: its 16
+// blocks of 4x4 share the 4 rows, lane l gives the input value of its
+// pixel's window at that tap and holds the 4 outputs of its pixel (register
+// i = output channel i of the chain), each a single fused multiply-add -- so
+// a chain over increasing k is the fast mode's ordered sum.  The weights come
+// through the instruction's A broadcast (cbsz 4: every block takes the A
+// values of block abid): one register holds 16 taps of the chain's 4 rows,
+// lane 4b + i the weight of row i at tap b, and tap u of the 16 broadcasts
+// block u.  The rows are the wave's own: it streams them straight from
+// memory into its own ring of NWS LDS stages, NWS-1 chunks ahead, and reads
+// them into registers before the chunk's last quad (every lane of every load
+// has a place in the stage, so the loads are unconditional and the waits
+// count them exactly).
 //
-// The input is staged per chunk of CC channels (CC*KHW taps in the order
-// channel, kernel row, kernel column; a multiple of 16).  For each channel
-// the block stages its halo with the padding in place: the rows its windows
-// reach, each as wide as the padded input row, the padding cells +0
-// (written once, before the first chunk) and the input's rows -- contiguous
-// in x, read with 4-byte (HV: 16-byte) loads -- stored in the middle.  A
-// window position is then always a cell of the stage, at a fixed distance
-// from the lane's first cell: a tap is one LDS read through the pointer of
-// its kernel row, the kernel column and the channel in the read's immediate
-// offset (horizontal dilation 1), and two taps of a row are one paired read.
-// LDS holds a chunk as [channel][position]; the channel's distance is added
-// to the three kernel-row pointers once per channel.  Channels past the
-// group's last are staged as +0 (their loads are out of range) and their
-// weights are made -0, so those taps add a product of -0 (fast mode's
-// padding).
+// Lanes and pixels: at stride 1 (p.vpitch = W + pL + pR, the padded row)
+// the 64 lanes take 64 consecutive cells of the output rows laid out as
+// wide as the padded input row, the last pL + pR cells of each row being no
+// pixel (computed, not stored), so the 64 lanes' reads of a tap are 64
+// consecutive cells of the stage; otherwise (p.vpitch = 0) they take 64
+// consecutive output pixels.
+//
+// The input is staged per chunk of CC = 16 channels (CC*KHW taps in the
+// order channel, kernel row, kernel column).  The block stages the halo of
+// its lanes' windows with the padding in place: the rows they reach, each
+// as wide as the padded input row, the padding cells +0 (written once,
+// before the first chunk) and the input's rows -- contiguous in x, read with
+// 4-byte (HV: 16-byte) loads, wave w loading channels w*CPW.. -- stored in
+// the middle.  LDS holds a chunk as [cell][channel]: a cell is the CC
+// channels of one input position and 4 floats of padding (80 bytes, so 8
+// lanes reading 16 bytes of 8 consecutive cells meet 8 different groups of
+// banks).  A window position is then always a cell at a fixed distance from
+// the lane's first cell of its kernel row, and one 16-byte read brings 4
+// channels of one tap position: with the kernel row's pointer, the kernel
+// column and the channel quad sit in the read's immediate offset (no
+// address arithmetic per tap).  Taps run in k order: quad q of a chunk is
+// its channels 4q..4q+3, each over the KHW window positions, read as KHW
+// 16-byte reads (one per position) and run as 4*KHW chain steps.  A wave
+// stores its CPW channels of an input position as one 16-byte (CPW = 2:
+// 8-byte) write.  Lanes past the input's part of the halo write a spare cell
+// past the rows.  Channels past the group's last are staged as +0 (their
+// loads are out of range) and their weights are made -0, so those taps add a
+// product of -0 (fast mode's padding).
 //
 // The staging never stops the matrix cores: chunk c's products run in two
 // halves, and between them each wave stores its part of chunk c+1's halo
 // (loaded during chunk c-1) into the next of three LDS buffers, issues the
 // loads of chunk c+2 and meets the others at the chunk's one barrier; the
-// second half then reads chunk c+1's first taps while it runs.  Buffer
+// second half then reads chunk c+1's first quad while it runs.  Buffer
 // (c+1) % 3 was last read in chunk c-2, which every wave finished before the
 // barrier of chunk c-1.  p.hrows: rows a tile stages at most (with its
-// padding rows); the dynamic LDS is 3 buffers of CC channels of
-// hrows * (W + pL + pR) positions.
+// padding rows); a buffer is hrows * (W + pL + pR) + 3 cells (two cells read
+// past the rows by lanes of no pixel, one spare written by idle lanes).
 // ---------------------------------------------------------------------------
-template <int KH, int KW, int R, int CW, int NI, bool HV, bool AV>
+template <int MODE, int KH, int KW, int R, int CW, int NI, bool HV, bool AV, int NWS>
 __global__ void __launch_bounds__(64 * CW) halo_kernel(Problem p) {
   constexpr int KHW = KH * KW;
-  constexpr int CC = 16;                      // channels per chunk
-  constexpr int BK = CC * KHW, NG = BK / 16;  // taps and 16-tap groups per chunk
-  constexpr int NH = NG / 2;                  // groups before the chunk's barrier
-  constexpr int CPW = CC / CW;                // channels each wave stages
-  constexpr int VW = HV ? 4 : 1;              // floats per halo load
-  constexpr int NBUF = 3;                     // LDS buffers of the halo
+  constexpr int CC = 16;                 // channels per chunk
+  constexpr int BK = CC * KHW;           // taps per chunk
+  constexpr int NG = BK / 16;            // 16-tap weight groups per chunk
+  constexpr int NQC = CC / 4;            // channel quads per chunk
+  constexpr int QT = 4 * KHW;            // taps per quad
+  constexpr int CSTR = CC + 4;           // floats of a staged cell
+  constexpr int C4 = CSTR / 4;           // its 16-byte units
+  constexpr int CPW = CC / CW;           // channels each wave stages
+  constexpr int VW = HV ? 4 : 1;         // floats per halo load
+  constexpr int NBUF = 3;                // LDS buffers of the halo
   constexpr int WROWS = 4 * R, WST = WROWS * BK;  // a wave's weight rows; floats of a weight stage
-  constexpr int NWS = 3;                          // weight stages per wave
   constexpr int WW = AV ? 4 : 1;                  // taps per weight load
-  constexpr int NQ = WST / WW, NIW = (NQ + 63) / 64;  // weight loads per stage, per lane
+  constexpr int NQW = WST / WW, NIW = (NQW + 63) / 64;  // weight loads per stage, per lane
+  constexpr int WSTP = NIW * 64 * WW;             // floats of a stage, every lane's place included
   constexpr int NL = CPW * NI;                    // halo loads per chunk, per lane
-  static_assert(BK % 16 == 0 && CC % CW == 0 && NH >= 1, "halo chunk shape");
-  // [NBUF][CC][hrows][W + pL + pR] halo, then per wave [NWS][WROWS][BK] weights
+  static_assert(BK % 16 == 0 && (CPW == 4 || CPW == 2) && NQC % 2 == 0, "halo chunk shape");
+  static_assert(NWS == 2 || NWS == 3, "two or three weight stages per wave");
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  // [NBUF][cells][CSTR] halo, then per wave [NWS][WSTP] weights
   extern __shared__ __align__(16) float hs[];
 
   const TileCoord tc = tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tpi = (p.OHW + 63) / 64;  // pixel tiles per image
+  // the lanes' cells: rows of vw cells, of which the first OW are pixels
+  const int vw = p.vpitch > 0 ? p.vpitch : p.OW;
+  const int ncell = p.OHW / p.OW * vw;  // cells of an image
+  const int tpi = (ncell + 63) / 64;    // tiles per image
   const int img = tc.tn / tpi;
   const int pbase = (tc.tn - img * tpi) * 64;
-  const int pix = pbase + lane;
-  const bool valid = pix < p.OHW;
+  const int cell = pbase + lane;
+  const int cy = cell / vw, cx = cell - cy * vw;
+  const bool valid = cell < ncell && cx < p.OW;
+  const int pix = cy * p.OW + cx;  // the lane's output pixel, where valid
   const int cin_g = p.K / KHW;
-  const int wp = p.W + p.pL + p.pR;  // a staged row: the padded input row
-  const int cs = p.hrows * wp;       // floats of a staged channel
-  const int bufsz = CC * cs;         // floats of a buffer
+  const int wp = p.W + p.pL + p.pR;       // a staged row: the padded input row
+  const int spare = p.hrows * wp + 2;     // the cell idle lanes write
+  const int bufsz = (spare + 1) * CSTR;   // floats of a buffer
   // the tile's staged rows: input rows ybase .. (padding rows included), of
   // which r0 .. r1 are the input's
-  const int oy_first = pbase / p.OW, oy_last = min(pbase + 63, p.OHW - 1) / p.OW;
+  const int oy_first = pbase / vw, oy_last = min(pbase + 63, ncell - 1) / vw;
   const int ybase = oy_first * p.sH - p.pT;
   const int r0 = max(ybase, 0);
   const int r1 = min(oy_last * p.sH - p.pT + (KH - 1) * p.dH, p.H - 1);
@@ -1832,42 +1858,49 @@ __global__ void __launch_bounds__(64 * CW) halo_kernel(Problem p) {
   // the padding rows)
   const int hlen = max(r1 - r0 + 1, 0) * p.W;
 
-  // this lane's first cell of each kernel row: pointers into the buffer of
-  // the chunk being run (channel 0), and into the next chunk's
-  const float *tp[KH], *tn[KH];
+  // this lane's first cell of each kernel row, in the buffer of the chunk
+  // being run, and in the next chunk's
+  const f32x4 *tp[KH], *tn[KH];
   {
-    const int oy = valid ? pix / p.OW : oy_first;
-    const int ox = valid ? pix - oy * p.OW : 0;
+    // (lanes of no pixel read the cells of their own place in the rows: at
+    // stride 1, within hrows rows of the stage plus two cells, which only
+    // they read; past an image's last row, the first pixel's cells)
+    const bool in_rows = cell < ncell || p.vpitch > 0;
+    const int oy = in_rows ? cy : oy_first;
+    const int ox = in_rows ? cx : 0;
+    const f32x4 *hs4 = reinterpret_cast<const f32x4 *>(hs);
 #pragma unroll
     for (int ky = 0; ky < KH; ++ky)
-      tp[ky] = hs + ((oy - oy_first) * p.sH + ky * p.dH) * wp + ox * p.sW;
+      tp[ky] = hs4 + (((oy - oy_first) * p.sH + ky * p.dH) * wp + ox * p.sW) * C4;
   }
-  // the cell of each halo element this lane stages (the same in every chunk)
+  // the cell each halo element of this lane goes to (the same in every
+  // chunk; the spare cell for lanes past the halo)
   int hcell[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int q = VW * (lane + 64 * i), rr = q / p.W;
-    hcell[i] = (r0 - ybase + rr) * wp + p.pL + q - rr * p.W;
+    hcell[i] = q < hlen ? (r0 - ybase + rr) * wp + p.pL + q - rr * p.W : spare;
   }
   // +0 everywhere (the padding cells keep it), before the first stores
-  for (int e = threadIdx.x; e < NBUF * bufsz; e += 64 * CW) hs[e] = 0.0f;
+  for (int e = threadIdx.x; e < NBUF * bufsz / 4; e += 64 * CW)
+    reinterpret_cast<f32x4 *>(hs)[e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // this wave's weight rows, streamed by the wave itself into its own ring
+  // this wave's weight rows, streamed by the wave itself into its own pair
   // of LDS stages ([row][tap], WW taps per lane and load, straight from
-  // memory into LDS) two chunks ahead; read back per chunk, lane 4b + i
+  // memory into LDS) one chunk ahead; read back per chunk, lane 4b + i
   // taking row i of each chain at tap b of each 16-tap group
   const int wrow0 = tc.tm * (4 * R * CW) + wave * 4 * R;  // first row of the wave
   const int wbase = min(wrow0, p.M - 1);
   const __amdgpu_buffer_rsrc_t wrs =
       buffer_at(p.A + tc.g * p.a_gstride + (int64_t)wbase * p.lda, kRange);
-  float *const wring = hs + NBUF * bufsz + wave * NWS * WST;
+  float *const wring = hs + NBUF * bufsz + wave * NWS * WSTP;
   uint32_t wq[NIW];  // byte offset of the lane's taps of load n in chunk 0, or kOutside
   int wt[NIW];       // their first tap in a chunk
 #pragma unroll
   for (int n = 0; n < NIW; ++n) {
     const int q = n * 64 + lane, r = q / (BK / WW);
     wt[n] = (q - r * (BK / WW)) * WW;
-    wq[n] = q < NQ && wrow0 + r < p.M
+    wq[n] = q < NQW && wrow0 + r < p.M
                 ? (uint32_t)((int64_t)(wrow0 + r - wbase) * p.lda * 4 + 4 * wt[n])
                 : kOutside;
   }
@@ -1877,7 +1910,7 @@ __global__ void __launch_bounds__(64 * CW) halo_kernel(Problem p) {
   const int nch = (cin_g + CC - 1) / CC, last = nch - 1;
   float rb[2][CPW][NI * VW];  // halo of chunk c in slot c % 2
   float wv[2][R][NG];         // weights of chunk c (read from its stage) in slot c % 2
-  float bv[2][16];            // B values of a group, read one group ahead
+  f32x4 qb[2][KHW];           // a quad's input values (4 channels per position), read one quad ahead
   f32x4 acc[R];
 #pragma unroll
   for (int c = 0; c < R; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -1904,26 +1937,24 @@ __global__ void __launch_bounds__(64 * CW) halo_kernel(Problem p) {
   // chunk c's weights into stage c % NWS (loads past the last chunk reload it)
   auto load_w = [&](int c) __attribute__((always_inline)) {
     const int k0 = min(c, last) * BK;
-    float *dst = wring + (c % NWS) * WST;
+    float *dst = wring + (c % NWS) * WSTP;
 #pragma unroll
     for (int n = 0; n < NIW; ++n) {
       const uint32_t off = wq[n] != kOutside && k0 + wt[n] < p.K ? wq[n] + 4 * k0 : kOutside;
-      if (NQ % 64 == 0 || n + 1 < NIW || lane < NQ % 64) {
-        auto *to = (__attribute__((address_space(3))) void *)(dst + n * 64 * WW);
-        if constexpr (AV)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, to, 16, off, 0, 0, 0);
-        else
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, to, 4, off, 0, 0, 0);
-      }
+      auto *to = (__attribute__((address_space(3))) void *)(dst + n * 64 * WW);
+      if constexpr (AV)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, to, 16, off, 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, to, 4, off, 0, 0, 0);
     }
   };
   // chunk c's weights from its stage into slot S, once its loads are in:
-  // after them the wave has issued at most `later` loads (a chunk's halo
-  // and weight loads go out in a fixed order), so the wait counts exactly
+  // after them the wave has issued exactly `later` loads (a chunk's halo
+  // and weight loads go out in a fixed order)
   auto read_w = [&](int c, auto slot, auto later) __attribute__((always_inline)) {
     constexpr int S = decltype(slot)::value, LATER = decltype(later)::value;
     asm volatile("s_waitcnt vmcnt(%0)" ::"i"(LATER < 63 ? LATER : 63) : "memory");
-    float *stg = wring + (c % NWS) * WST;
+    float *stg = wring + (c % NWS) * WSTP;
     // in a chunk running past k (the last one at most) the taps past k get
     // -0 weights, written over the wave's own stage (its LDS operations run
     // in order)
@@ -1937,37 +1968,83 @@ __global__ void __launch_bounds__(64 * CW) halo_kernel(Problem p) {
 #pragma unroll
       for (int gi = 0; gi < NG; ++gi) wv[S][r][gi] = src[4 * r * BK + 16 * gi];
   };
+  // the wave's CPW channels of each of its halo elements, one write per
+  // input position
   auto store_halo = [&](auto slot, int buf) __attribute__((always_inline)) {
     constexpr int S = decltype(slot)::value;
-    float *dst = hs + buf * bufsz + wave * CPW * cs;
+    float *dst = hs + buf * bufsz + wave * CPW;
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      if (VW * (lane + 64 * i) < hlen) {
+#pragma unroll
+      for (int e = 0; e < VW; ++e) {
         // (16-byte loads: W is a multiple of 4, so the four are in one row)
-#pragma unroll
-        for (int j = 0; j < CPW; ++j)
-#pragma unroll
-          for (int e = 0; e < VW; ++e) dst[j * cs + hcell[i] + e] = rb[S][j][VW * i + e];
+        const int at = (hcell[i] + (hcell[i] == spare ? 0 : e)) * CSTR;
+        if constexpr (CPW == 4)
+          *reinterpret_cast<f32x4 *>(dst + at) =
+              f32x4{rb[S][0][VW * i + e], rb[S][1][VW * i + e], rb[S][2][VW * i + e], rb[S][3][VW * i + e]};
+        else
+          *reinterpret_cast<f32x2 *>(dst + at) = f32x2{rb[S][0][VW * i + e], rb[S][1][VW * i + e]};
       }
   };
-  // group G of a chunk through the kernel-row pointers ptr into bv[B]
-  auto read = [&](auto grp, auto into, const float *(&ptr)[KH]) __attribute__((always_inline)) {
-    constexpr int G = decltype(grp)::value, B = decltype(into)::value;
-    static_for<16>([&](auto uq) __attribute__((always_inline)) {
-      constexpr int s = 16 * G + decltype(uq)::value;  // tap of the chunk
-      constexpr int ch = s / KHW, ky = (s % KHW) / KW, kx = s % KW;
-      bv[B][s % 16] = ptr[ky][ch * cs + kx];
+  // quad Q of a chunk (4 channels at each window position) through the
+  // kernel-row pointers ptr into qb[B]
+  auto read = [&](auto quad, auto into, const f32x4 *(&ptr)[KH]) __attribute__((always_inline)) {
+    constexpr int Q = decltype(quad)::value, B = decltype(into)::value;
+    static_for<KHW>([&](auto pq) __attribute__((always_inline)) {
+      constexpr int pos = decltype(pq)::value, ky = pos / KW, kx = pos % KW;
+      qb[B][pos] = ptr[ky][kx * C4 + Q];
     });
   };
-  // the products of group G of chunk c (weights in slot S, B values in bv[B])
-  auto products = [&](int, auto grp, auto slot, auto from) __attribute__((always_inline)) {
-    constexpr int G = decltype(grp)::value, S = decltype(slot)::value, B = decltype(from)::value;
-    static_for<16>([&](auto uq) __attribute__((always_inline)) {
-      constexpr int u = decltype(uq)::value;
+  // the products of quad Q of chunk c (weights in slot S, inputs in qb[B]):
+  // its taps in k order, channel 4Q + ci at window position pos.  Fast
+  // mode: the chain step itself, one fused multiply-add per output.  Exact
+  // mode: the matrix core forms the rounded products (C = +0: fma(w, x, +0)
+  // is round(w * x), but +0 for an exact -0 product, which cannot change a
+  // sum that is never -0) and separately rounded adds take them into the
+  // sums in k order, two taps at a time, the products of the next two taps
+  // issued before the adds of these.  Empty asm statements order the steps
+  // (an input passes through one before its products, the sums through one
+  // after their adds): the products do not depend on the sums, and the
+  // compiler would otherwise issue every product of the quad first and run
+  // out of registers.
+  auto products = [&](auto quad, auto slot, auto from) __attribute__((always_inline)) {
+    constexpr int Q = decltype(quad)::value, S = decltype(slot)::value, B = decltype(from)::value;
+    if constexpr (MODE == kFast) {
+      static_for<QT>([&](auto tq) __attribute__((always_inline)) {
+        constexpr int t = decltype(tq)::value, s = QT * Q + t, ci = t / KHW, pos = t % KHW;
 #pragma unroll
-      for (int r = 0; r < R; ++r)
-        acc[r] = __builtin_amdgcn_mfma_f32_4x4x1f32(wv[S][r][G], bv[B][u], acc[r], 4, u, 0);
-    });
+        for (int r = 0; r < R; ++r)
+          acc[r] = __builtin_amdgcn_mfma_f32_4x4x1f32(wv[S][r][s / 16], qb[B][pos][ci], acc[r], 4, s % 16, 0);
+      });
+    } else {
+      static_assert(QT % 2 == 0, "exact steps go in pairs of taps");
+      constexpr int NP = QT / 2;
+      f32x4 pr[2][2][R];  // the products of a pair of taps, by the pair's parity
+      auto issue = [&](auto pair) __attribute__((always_inline)) {
+        constexpr int PI = decltype(pair)::value;
+        static_for<2>([&](auto hq) __attribute__((always_inline)) {
+          constexpr int h = decltype(hq)::value, t = 2 * PI + h;
+          constexpr int s = QT * Q + t, ci = t / KHW, pos = t % KHW;
+          float x = qb[B][pos][ci];
+          asm volatile("" : "+v"(x));
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+            pr[PI % 2][h][r] = __builtin_amdgcn_mfma_f32_4x4x1f32(wv[S][r][s / 16], x,
+                                                                  f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 4, s % 16, 0);
+        });
+      };
+      issue(std::integral_constant<int, 0>{});
+      static_for<NP>([&](auto pn) __attribute__((always_inline)) {
+        constexpr int n = decltype(pn)::value;
+        if constexpr (n + 1 < NP) issue(std::integral_constant<int, n + 1>{});
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int r = 0; r < R; ++r) acc[r] = acc[r] + pr[n % 2][h][r];
+#pragma unroll
+        for (int r = 0; r < R; ++r) asm volatile("" : "+v"(acc[r]));
+      });
+    }
   };
 
   // The loads go out in the order weights c, halo c, weights c+1, halo c+1,
@@ -1980,32 +2057,35 @@ __global__ void __launch_bounds__(64 * CW) halo_kernel(Problem p) {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
   // prologue: chunk 0 in buffer 0 and its weights in registers, chunk 1's
-  // halo and weights in flight, chunk 0's first group read
+  // halo (and with three stages its weights) in flight, chunk 0's first
+  // quad read
   load_w(0);
   fence();
   load_halo(0, std::integral_constant<int, 0>{});
   fence();
-  load_w(1);
-  fence();
+  if constexpr (NWS == 3) {
+    load_w(1);
+    fence();
+  }
   load_halo(1, std::integral_constant<int, 1>{});
   fence();
   barrier();  // the +0 fill before any stage is written
   store_halo(std::integral_constant<int, 0>{}, 0);
-  read_w(0, std::integral_constant<int, 0>{}, std::integral_constant<int, 2 * NL + NIW>{});
+  read_w(0, std::integral_constant<int, 0>{}, std::integral_constant<int, 2 * NL + (NWS - 2) * NIW>{});
   barrier();
   read(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, tp);
 
   ring_loop<2>(0, nch, [&](int c, auto par) __attribute__((always_inline)) {
     constexpr int P = decltype(par)::value;  // c % 2
     fence();
-    load_w(c + 2);
+    load_w(c + NWS - 1);
     fence();
-    // group G of this chunk is read into bv[(P*NG + G) % 2]
-    static_for<NH>([&](auto grp) __attribute__((always_inline)) {
-      constexpr int G = decltype(grp)::value;
-      read(std::integral_constant<int, G + 1>{}, std::integral_constant<int, (P * NG + G + 1) % 2>{}, tp);
+    // quad Q of a chunk is in qb[Q % 2] (a chunk has an even number of quads)
+    static_for<NQC / 2>([&](auto quad) __attribute__((always_inline)) {
+      constexpr int Q = decltype(quad)::value;
+      read(std::integral_constant<int, Q + 1>{}, std::integral_constant<int, (Q + 1) % 2>{}, tp);
       __builtin_amdgcn_sched_barrier(0);
-      products(c, grp, par, std::integral_constant<int, (P * NG + G) % 2>{});
+      products(quad, par, std::integral_constant<int, Q % 2>{});
     });
     // chunk c+1 into buffer (c+1) % 3, chunk c+2's loads, the barrier
     const int nb = (c + 1) % NBUF;
@@ -2013,21 +2093,23 @@ __global__ void __launch_bounds__(64 * CW) halo_kernel(Problem p) {
     fence();
     load_halo(c + 2, par);
     fence();
-    // chunk c+1's weights: after them went halo c+1, weights c+2, halo c+2
-    read_w(c + 1, std::integral_constant<int, 1 - P>{}, std::integral_constant<int, 2 * NL + NIW>{});
     barrier();
-    const int delta = (nb - c % NBUF) * bufsz;
+    const int delta = (nb - c % NBUF) * (bufsz / 4);
 #pragma unroll
     for (int t = 0; t < KH; ++t) tn[t] = tp[t] + delta;
-    static_for<NG - NH>([&](auto gq) __attribute__((always_inline)) {
-      constexpr int G = NH + decltype(gq)::value;
-      constexpr int BN = (P * NG + G + 1) % 2;
-      if constexpr (G + 1 < NG)
-        read(std::integral_constant<int, G + 1>{}, std::integral_constant<int, BN>{}, tp);
+    static_for<NQC - NQC / 2>([&](auto qq) __attribute__((always_inline)) {
+      constexpr int Q = NQC / 2 + decltype(qq)::value;
+      if constexpr (Q + 1 < NQC)
+        read(std::integral_constant<int, Q + 1>{}, std::integral_constant<int, (Q + 1) % 2>{}, tp);
       else
-        read(std::integral_constant<int, 0>{}, std::integral_constant<int, BN>{}, tn);
+        read(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, tn);
+      // chunk c+1's weights, before the last quad: after them went halo c+2
+      // (three stages: halo c+1, weights c+2 and halo c+2)
+      if constexpr (Q + 1 == NQC)
+        read_w(c + 1, std::integral_constant<int, 1 - P>{},
+               std::integral_constant<int, NWS == 2 ? NL : 2 * NL + NIW>{});
       __builtin_amdgcn_sched_barrier(0);
-      products(c, std::integral_constant<int, G>{}, par, std::integral_constant<int, (P * NG + G) % 2>{});
+      products(std::integral_constant<int, Q>{}, par, std::integral_constant<int, Q % 2>{});
     });
 #pragma unroll
     for (int t = 0; t < KH; ++t) tp[t] = tn[t];

@@ -497,16 +497,29 @@ inline bool is_halo(int v) { return v >= kFirstHaloVariant && v <= kLastHaloVari
 struct HaloPlan {
   int rows, ni;
   bool hv;
+  int vpitch;        // stride 1: the lanes' rows of cells, as wide as the padded input row; else 0
+  int64_t tiles;     // tiles of 64 lanes per image
   int64_t halo_lds;  // bytes of the halo buffers
 };
-// the weight stages of the largest block (32 rows of 144 taps, three
-// stages), and the LDS a workgroup may hold on gfx950
-constexpr int64_t kHaloWeightLds = 3 * 32 * 144 * 4;
+// a wave's weight stage in floats (4 * R rows of 144 taps, padded to whole
+// loads of 64 lanes x 16 bytes), the weight stages of a block of variant v
+// in bytes (two per wave), and the LDS a workgroup may hold on gfx950
+constexpr int64_t halo_weight_stage(int R) { return (4 * R * 144 / 4 + 63) / 64 * 64 * 4; }
+constexpr int64_t halo_weight_lds(int v) {
+  return v == 26 ? 4 * 2 * halo_weight_stage(1) * 4
+       : v == 27 ? 4 * 2 * halo_weight_stage(2) * 4
+                 : 8 * 2 * halo_weight_stage(1) * 4;
+}
 constexpr int64_t kHaloMaxLds = 160 * 1024;
 inline bool halo_plan(const og::Problem &p, bool x_aligned16, HaloPlan &h) {
   if (p.dW != 1 || !p.a_vec) return false;
   const int oh = p.OHW / p.OW;
-  const int orows = std::min(oh, 63 / p.OW + 2);
+  // at stride 1 the lanes take cells of rows as wide as the padded input row
+  // (a tile's lanes span at most 63 / vpitch + 2 such rows, those past the
+  // image included); else 64 consecutive pixels
+  h.vpitch = p.sH == 1 && p.sW == 1 ? p.W + p.pL + p.pR : 0;
+  const int orows = h.vpitch > 0 ? 63 / h.vpitch + 2 : std::min(oh, 63 / p.OW + 2);
+  h.tiles = h.vpitch > 0 ? ceil_div((int64_t)oh * h.vpitch, 64) : ceil_div(p.OHW, 64);
   h.rows = (orows - 1) * p.sH + (p.KH - 1) * p.dH + 1;
   const int64_t hlen = (int64_t)std::min(h.rows, p.H) * p.W;  // input floats of a channel
   h.hv = x_aligned16 && p.W % 4 == 0 && p.HW % 4 == 0 && p.x_img % 4 == 0 && p.x_grp % 4 == 0;
@@ -514,42 +527,50 @@ inline bool halo_plan(const og::Problem &p, bool x_aligned16, HaloPlan &h) {
     h.ni = hlen <= 256 ? 1 : hlen <= 512 ? 2 : 0;
   else
     h.ni = hlen <= 128 ? 2 : hlen <= 256 ? 4 : hlen <= 512 ? 8 : 0;
-  h.halo_lds = 3 * 16 * (int64_t)h.rows * (p.W + p.pL + p.pR) * 4;
-  return h.ni != 0 && h.halo_lds + kHaloWeightLds <= kHaloMaxLds;
+  // three buffers of rows * (W + pL + pR) + 3 cells of 20 floats (16
+  // channels and 4 of padding)
+  h.halo_lds = 3 * ((int64_t)h.rows * (p.W + p.pL + p.pR) + 3) * 20 * 4;
+  return h.ni != 0 && h.halo_lds + halo_weight_lds(26) <= kHaloMaxLds;
 }
+// whether variant v's block (its halo and weight stages) fits the LDS
+inline bool halo_fits(const HaloPlan &h, int v) { return h.halo_lds + halo_weight_lds(v) <= kHaloMaxLds; }
 
-template <int R, int CW, int NI, bool HV, bool AV>
+// (two weight stages per wave: measured over 80 3x3 convolutions, three
+// stages, which hide more of the weight loads' latency, took 2 % more time
+// in all, the LDS they hold costing blocks per compute unit)
+template <int MODE, int R, int CW, int NI, bool HV, bool AV>
 void launch_halo_shape(og::Problem p, const HaloPlan &h, hipStream_t s) {
-  const auto kernel = og::halo_kernel<3, 3, R, CW, NI, HV, AV>;
+  constexpr int NWS = 2;
+  const auto kernel = og::halo_kernel<MODE, 3, 3, R, CW, NI, HV, AV, NWS>;
   // more than 64 KB of dynamic LDS must be allowed per kernel, once
   static const hipError_t allowed =
       hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kHaloMaxLds);
   (void)allowed;
   p.hrows = h.rows;
+  p.vpitch = h.vpitch;
   p.tiles_m = (int)ceil_div(p.M, 4 * R * CW);
-  p.tiles_n = (int)((p.N / p.OHW) * ceil_div(p.OHW, 64));
+  p.tiles_n = (int)((p.N / p.OHW) * h.tiles);
   const dim3 grid((unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)p.groups), block(64 * CW);
-  const size_t lds = (size_t)h.halo_lds + (size_t)CW * 3 * 4 * R * 144 * 4;
+  const size_t lds = (size_t)h.halo_lds + (size_t)CW * NWS * halo_weight_stage(R) * 4;
   hipLaunchKernelGGL(kernel, grid, block, lds, s, p);
 }
 
-template <int R, int CW, bool AV>
-void launch_halo_av(og::Problem p, const HaloPlan &h, hipStream_t s) {
-  if (h.hv) {
-    if (h.ni == 1) return launch_halo_shape<R, CW, 1, true, AV>(p, h, s);
-    return launch_halo_shape<R, CW, 2, true, AV>(p, h, s);
-  }
-  if (h.ni == 2) return launch_halo_shape<R, CW, 2, false, AV>(p, h, s);
-  if (h.ni == 4) return launch_halo_shape<R, CW, 4, false, AV>(p, h, s);
-  return launch_halo_shape<R, CW, 8, false, AV>(p, h, s);
-}
-template <int R, int CW>
+template <int MODE, int R, int CW>
 void launch_halo_r(og::Problem p, const HaloPlan &h, hipStream_t s) {
-  launch_halo_av<R, CW, true>(p, h, s);
+  if (h.hv) {
+    if (h.ni == 1) return launch_halo_shape<MODE, R, CW, 1, true, true>(p, h, s);
+    return launch_halo_shape<MODE, R, CW, 2, true, true>(p, h, s);
+  }
+  if (h.ni == 2) return launch_halo_shape<MODE, R, CW, 2, false, true>(p, h, s);
+  if (h.ni == 4) return launch_halo_shape<MODE, R, CW, 4, false, true>(p, h, s);
+  return launch_halo_shape<MODE, R, CW, 8, false, true>(p, h, s);
 }
 
-// A 3x3 convolution (gathered B) on variant 26, 27 or 28, planned by halo_plan.
-void launch_halo_conv(int variant, const og::Problem &p, const HaloPlan &h, hipStream_t s);
+// A 3x3 convolution (gathered B) on variant 26, 27 or 28, planned by
+// halo_plan, in exact (0) or fast (1) mode.
+void launch_halo_conv(int variant, int mode, const og::Problem &p, const HaloPlan &h, hipStream_t s);
+// (its exact-mode kernels, in their own group)
+void launch_halo_exact(int variant, const og::Problem &p, const HaloPlan &h, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Panel kernel (fast mode: 1x1 convolutions, any stride and padding, and

@@ -85,10 +85,17 @@ void launch_splitk_conv(int variant, bool av, bool planes, const og::Problem &p,
   return launch_splitk<og::kBGather, false, false, 0, 0>(variant, p, s);
 }
 #elif OG_UNIT == 14
-void launch_halo_conv(int variant, const og::Problem &p, const HaloPlan &h, hipStream_t s) {
-  if (variant == 26) return launch_halo_r<1, 4>(p, h, s);
-  if (variant == 27) return launch_halo_r<2, 4>(p, h, s);
-  return launch_halo_r<1, 8>(p, h, s);
+void launch_halo_conv(int variant, int mode, const og::Problem &p, const HaloPlan &h, hipStream_t s) {
+  if (mode == OG_MODE_EXACT) return launch_halo_exact(variant, p, h, s);
+  if (variant == 26) return launch_halo_r<og::kFast, 1, 4>(p, h, s);
+  if (variant == 27) return launch_halo_r<og::kFast, 2, 4>(p, h, s);
+  return launch_halo_r<og::kFast, 1, 8>(p, h, s);
+}
+#elif OG_UNIT == 16
+void launch_halo_exact(int variant, const og::Problem &p, const HaloPlan &h, hipStream_t s) {
+  if (variant == 26) return launch_halo_r<og::kExact, 1, 4>(p, h, s);
+  if (variant == 27) return launch_halo_r<og::kExact, 2, 4>(p, h, s);
+  return launch_halo_r<og::kExact, 1, 8>(p, h, s);
 }
 #elif OG_UNIT == 15
 template <int R>

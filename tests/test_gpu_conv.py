@@ -149,9 +149,10 @@ HALO_SHAPES = [
 
 @pytest.mark.parametrize("variant", [26, 27, 28])
 def test_halo_kernel_shapes(orc, variant):
-    """The halo kernel (fast mode, 3x3 windows) bit for bit against the
-    oracle; in exact mode, and on shapes it does not take, the variant runs
-    the automatic choice."""
+    """The halo kernel (3x3 windows; exact mode's products on the matrix
+    cores and its sums on the VALU, fast mode's chains on the matrix cores)
+    bit for bit against the oracle; on shapes it does not take the variant
+    runs the automatic choice."""
     rng = np.random.default_rng(500 + variant)
     og.set_variant(variant)
     for s in HALO_SHAPES:
