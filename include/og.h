@@ -231,13 +231,15 @@ void *og_get_stream(void);
  * fast mode with one of them forced returns OG_ERR_NOT_EXACT (neither
  * mode's bits can come from them).  In OG_MODE_FAST_MFMA a forced variant
  * 1..20 runs that fast-mode kernel.
- * 26, 27, 28 = the halo kernel (fast mode, 3x3 convolutions with horizontal
- * dilation 1): 64 output pixels of one image per block, the input rows
- * their windows reach staged in LDS with the padding in place, the k chain
- * of each 4 output channels on the matrix cores (v_mfma_f32_4x4x1_16b_f32
- * with the weights broadcast from one block); 4 waves of 4 rows, 4 waves
- * of 2 x 4 rows and 8 waves of 4 rows.  In exact mode, and on shapes they
- * do not take, they run as 0 does.
+ * 26, 27, 28 = the halo kernel (3x3 convolutions with horizontal dilation
+ * 1): 64 output pixels of one image per block, the input rows their
+ * windows reach staged in LDS with the padding in place, each 4 output
+ * channels on the matrix cores (v_mfma_f32_4x4x1_16b_f32 with the weights
+ * broadcast from one block; fast mode: the k chain itself, exact mode: the
+ * rounded products, summed by separately rounded adds in k order); 4
+ * waves of 4 rows, 4 waves of 2 x 4 rows and 8 waves of 4 rows.  On shapes
+ * they do not take (or whose block does not fit the LDS) they run as 0
+ * does.
  * 29, 30 = the panel kernel (fast mode, og_gemm_f32 products and 1x1
  * convolutions): panels of 64 columns of B (input pixels) loaded straight
  * into LDS stages, the weight rows of each wave through its own LDS
