@@ -37,7 +37,7 @@ from gpu_util import assert_same_bits, bits, say, to_device_strided, to_host, to
 
 pytestmark = pytest.mark.gpu
 MODES = {"exact": og.EXACT, "fast": og.FAST}
-VARIANTS = list(range(0, 21))
+VARIANTS = list(range(0, 21)) + [26, 27, 28, 29, 30]  # tiles, then the halo and panel kernels
 M, N, K = 300, 520, 40  # several tiles of the largest tile shapes, each ending inside
 
 
@@ -128,6 +128,9 @@ def test_underflow_to_minus_zero(orc, variant):
     # convolutions: channels past a chunk, and padding taps (+0 inputs times
     # negative weights add -0, which keeps -0)
     for s in CONV_SHAPES + [synth.ConvShape("u3x3", 1, 37, 6, 7, 20, 3, 3, (1, 1), (1, 1, 1, 1)),
+                            # weight rows of whole quads: the halo kernel's shapes
+                            synth.ConvShape("u3x3q", 2, 36, 6, 7, 20, 3, 3, (1, 1), (1, 1, 1, 1)),
+                            synth.ConvShape("u3x3s2", 1, 20, 9, 8, 12, 3, 3, (2, 2), (1, 1, 1, 1)),
                             synth.ConvShape("u1x1", 2, 130, 5, 6, 9, 1, 1)]:
         x = np.full((s.N, s.Cin, s.H, s.W), 2.0 ** -100, np.float32)
         w = (-rng.uniform(1, 2, (s.Cout, s.Cin // s.groups, s.KH, s.KW)) * 2.0 ** -60).astype(
