@@ -1803,11 +1803,15 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, chain_rows(
 // loads of chunk c+2 and meets the others at the chunk's one barrier; the
 // second half then reads chunk c+1's first quad while it runs.  Buffer
 // (c+1) % 3 was last read in chunk c-2, which every wave finished before the
-// barrier of chunk c-1.  p.hrows: rows a tile stages at most (with its
-// padding rows); a buffer is hrows * (W + pL + pR) + 3 cells (two cells read
-// past the rows by lanes of no pixel, one spare written by idle lanes).
+// barrier of chunk c-1.  With two buffers (NBUF = 2, for halos whose three
+// buffers would not leave LDS for as many blocks per compute unit) the store
+// waits for that barrier, and a second barrier before the chunk's last quad
+// makes chunk c+1's halo visible to the reads of its first.  p.hrows: rows a
+// tile stages at most (with its padding rows); a buffer is
+// hrows * (W + pL + pR) + 3 cells (two cells read past the rows by lanes of
+// no pixel, one spare written by idle lanes).
 // ---------------------------------------------------------------------------
-template <int MODE, int KH, int KW, int R, int CW, int NI, bool HV, bool AV, int NWS>
+template <int MODE, int KH, int KW, int R, int CW, int NI, bool HV, bool AV, int NWS, int NBUF>
 __global__ void __launch_bounds__(64 * CW) halo_kernel(Problem p) {
   constexpr int KHW = KH * KW;
   constexpr int CC = 16;                 // channels per chunk
@@ -1819,7 +1823,6 @@ __global__ void __launch_bounds__(64 * CW) halo_kernel(Problem p) {
   constexpr int C4 = CSTR / 4;           // its 16-byte units
   constexpr int CPW = CC / CW;           // channels each wave stages
   constexpr int VW = HV ? 4 : 1;         // floats per halo load
-  constexpr int NBUF = 3;                // LDS buffers of the halo
   constexpr int WROWS = 4 * R, WST = WROWS * BK;  // a wave's weight rows; floats of a weight stage
   constexpr int WW = AV ? 4 : 1;                  // taps per weight load
   constexpr int NQW = WST / WW, NIW = (NQW + 63) / 64;  // weight loads per stage, per lane
@@ -1827,6 +1830,7 @@ __global__ void __launch_bounds__(64 * CW) halo_kernel(Problem p) {
   constexpr int NL = CPW * NI;                    // halo loads per chunk, per lane
   static_assert(BK % 16 == 0 && (CPW == 4 || CPW == 2) && NQC % 2 == 0, "halo chunk shape");
   static_assert(NWS == 2 || NWS == 3, "two or three weight stages per wave");
+  static_assert(NBUF == 2 || NBUF == 3, "two or three halo buffers");
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   // [NBUF][cells][CSTR] halo, then per wave [NWS][WSTP] weights
   extern __shared__ __align__(16) float hs[];
@@ -2087,27 +2091,41 @@ __global__ void __launch_bounds__(64 * CW) halo_kernel(Problem p) {
       __builtin_amdgcn_sched_barrier(0);
       products(quad, par, std::integral_constant<int, Q % 2>{});
     });
-    // chunk c+1 into buffer (c+1) % 3, chunk c+2's loads, the barrier
     const int nb = (c + 1) % NBUF;
-    store_halo(std::integral_constant<int, 1 - P>{}, nb);
-    fence();
-    load_halo(c + 2, par);
-    fence();
-    barrier();
     const int delta = (nb - c % NBUF) * (bufsz / 4);
+    if constexpr (NBUF == 3) {
+      // chunk c+1 into buffer (c+1) % 3 (last read in chunk c-2, which every
+      // wave finished before the barrier of chunk c-1), chunk c+2's loads,
+      // the barrier
+      store_halo(std::integral_constant<int, 1 - P>{}, nb);
+      fence();
+      load_halo(c + 2, par);
+      fence();
+      barrier();
+    } else {
+      // two buffers: buffer (c+1) % 2 was read in chunk c-1, which every wave
+      // has finished at this barrier; a second barrier before the last quad
+      // makes chunk c+1's halo visible to its first quad's reads
+      barrier();
+      store_halo(std::integral_constant<int, 1 - P>{}, nb);
+      fence();
+      load_halo(c + 2, par);
+      fence();
+    }
 #pragma unroll
     for (int t = 0; t < KH; ++t) tn[t] = tp[t] + delta;
     static_for<NQC - NQC / 2>([&](auto qq) __attribute__((always_inline)) {
       constexpr int Q = NQC / 2 + decltype(qq)::value;
-      if constexpr (Q + 1 < NQC)
+      if constexpr (Q + 1 < NQC) {
         read(std::integral_constant<int, Q + 1>{}, std::integral_constant<int, (Q + 1) % 2>{}, tp);
-      else
+      } else {
+        if constexpr (NBUF == 2) barrier();
         read(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, tn);
-      // chunk c+1's weights, before the last quad: after them went halo c+2
-      // (three stages: halo c+1, weights c+2 and halo c+2)
-      if constexpr (Q + 1 == NQC)
+        // chunk c+1's weights, before the last quad: after them went halo c+2
+        // (three stages: halo c+1, weights c+2 and halo c+2)
         read_w(c + 1, std::integral_constant<int, 1 - P>{},
                std::integral_constant<int, NWS == 2 ? NL : 2 * NL + NIW>{});
+      }
       __builtin_amdgcn_sched_barrier(0);
       products(std::integral_constant<int, Q>{}, par, std::integral_constant<int, Q % 2>{});
     });

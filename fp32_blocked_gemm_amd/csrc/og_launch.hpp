@@ -497,9 +497,9 @@ inline bool is_halo(int v) { return v >= kFirstHaloVariant && v <= kLastHaloVari
 struct HaloPlan {
   int rows, ni;
   bool hv;
-  int vpitch;        // stride 1: the lanes' rows of cells, as wide as the padded input row; else 0
-  int64_t tiles;     // tiles of 64 lanes per image
-  int64_t halo_lds;  // bytes of the halo buffers
+  int vpitch;       // stride 1: the lanes' rows of cells, as wide as the padded input row; else 0
+  int64_t tiles;    // tiles of 64 lanes per image
+  int64_t buf_lds;  // bytes of one halo buffer
 };
 // a wave's weight stage in floats (4 * R rows of 144 taps, padded to whole
 // loads of 64 lanes x 16 bytes), the weight stages of a block of variant v
@@ -515,44 +515,64 @@ inline bool halo_plan(const og::Problem &p, bool x_aligned16, HaloPlan &h) {
   if (p.dW != 1 || !p.a_vec) return false;
   const int oh = p.OHW / p.OW;
   // at stride 1 the lanes take cells of rows as wide as the padded input row
-  // (a tile's lanes span at most 63 / vpitch + 2 such rows, those past the
-  // image included); else 64 consecutive pixels
+  // (a tile's lanes past the image included); else 64 consecutive pixels
   h.vpitch = p.sH == 1 && p.sW == 1 ? p.W + p.pL + p.pR : 0;
-  const int orows = h.vpitch > 0 ? 63 / h.vpitch + 2 : std::min(oh, 63 / p.OW + 2);
-  h.tiles = h.vpitch > 0 ? ceil_div((int64_t)oh * h.vpitch, 64) : ceil_div(p.OHW, 64);
-  h.rows = (orows - 1) * p.sH + (p.KH - 1) * p.dH + 1;
+  const int64_t vw = h.vpitch > 0 ? h.vpitch : p.OW, ncell = (int64_t)oh * vw;
+  h.tiles = ceil_div(ncell, 64);
+  // the most rows of cells a tile's lanes span
+  int64_t orows = 1;
+  for (int64_t t = 0; t < h.tiles; ++t) {
+    const int64_t lastc = h.vpitch > 0 ? 64 * t + 63 : std::min(64 * t + 63, ncell - 1);
+    orows = std::max(orows, lastc / vw - 64 * t / vw + 1);
+  }
+  h.rows = (int)((orows - 1) * p.sH + (p.KH - 1) * p.dH + 1);
   const int64_t hlen = (int64_t)std::min(h.rows, p.H) * p.W;  // input floats of a channel
   h.hv = x_aligned16 && p.W % 4 == 0 && p.HW % 4 == 0 && p.x_img % 4 == 0 && p.x_grp % 4 == 0;
   if (h.hv)
     h.ni = hlen <= 256 ? 1 : hlen <= 512 ? 2 : 0;
   else
     h.ni = hlen <= 128 ? 2 : hlen <= 256 ? 4 : hlen <= 512 ? 8 : 0;
-  // three buffers of rows * (W + pL + pR) + 3 cells of 20 floats (16
-  // channels and 4 of padding)
-  h.halo_lds = 3 * ((int64_t)h.rows * (p.W + p.pL + p.pR) + 3) * 20 * 4;
-  return h.ni != 0 && h.halo_lds + halo_weight_lds(26) <= kHaloMaxLds;
+  // a buffer: rows * (W + pL + pR) + 3 cells of 20 floats (16 channels and
+  // 4 of padding)
+  h.buf_lds = ((int64_t)h.rows * (p.W + p.pL + p.pR) + 3) * 20 * 4;
+  return h.ni != 0 && 2 * h.buf_lds + halo_weight_lds(26) <= kHaloMaxLds;
 }
-// whether variant v's block (its halo and weight stages) fits the LDS
-inline bool halo_fits(const HaloPlan &h, int v) { return h.halo_lds + halo_weight_lds(v) <= kHaloMaxLds; }
+// whether variant v's block (two halo buffers and its weight stages) fits the LDS
+inline bool halo_fits(const HaloPlan &h, int v) { return 2 * h.buf_lds + halo_weight_lds(v) <= kHaloMaxLds; }
 
-// (two weight stages per wave: measured over 80 3x3 convolutions, three
-// stages, which hide more of the weight loads' latency, took 2 % more time
-// in all, the LDS they hold costing blocks per compute unit)
-template <int MODE, int R, int CW, int NI, bool HV, bool AV>
-void launch_halo_shape(og::Problem p, const HaloPlan &h, hipStream_t s) {
+template <int MODE, int R, int CW, int NI, bool HV, bool AV, int NBUF>
+void launch_halo_nbuf(const og::Problem &p, const HaloPlan &h, hipStream_t s) {
   constexpr int NWS = 2;
-  const auto kernel = og::halo_kernel<MODE, 3, 3, R, CW, NI, HV, AV, NWS>;
+  const auto kernel = og::halo_kernel<MODE, 3, 3, R, CW, NI, HV, AV, NWS, NBUF>;
   // more than 64 KB of dynamic LDS must be allowed per kernel, once
   static const hipError_t allowed =
       hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kHaloMaxLds);
   (void)allowed;
+  const dim3 grid((unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)p.groups), block(64 * CW);
+  const size_t lds = (size_t)(NBUF * h.buf_lds) + (size_t)CW * NWS * halo_weight_stage(R) * 4;
+  hipLaunchKernelGGL(kernel, grid, block, lds, s, p);
+}
+
+// Two weight stages per wave (measured over 80 3x3 convolutions, three
+// stages, which hide more of the weight loads' latency, took 2 % more time
+// in all, the LDS they hold costing blocks per compute unit); three halo
+// buffers where they fit and the launch's blocks need no more compute-unit
+// slots than three buffers leave (the kernels use over 128 registers: at
+// most two waves per SIMD), else two (a second barrier per chunk).
+template <int MODE, int R, int CW, int NI, bool HV, bool AV>
+void launch_halo_shape(og::Problem p, const HaloPlan &h, hipStream_t s) {
   p.hrows = h.rows;
   p.vpitch = h.vpitch;
   p.tiles_m = (int)ceil_div(p.M, 4 * R * CW);
   p.tiles_n = (int)((p.N / p.OHW) * h.tiles);
-  const dim3 grid((unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)p.groups), block(64 * CW);
-  const size_t lds = (size_t)h.halo_lds + (size_t)CW * NWS * halo_weight_stage(R) * 4;
-  hipLaunchKernelGGL(kernel, grid, block, lds, s, p);
+  auto per_cu = [&](int nbuf) {
+    const int64_t lds = nbuf * h.buf_lds + (int64_t)CW * 2 * halo_weight_stage(R) * 4;
+    return lds > kHaloMaxLds ? 0 : std::min<int64_t>(kHaloMaxLds / lds, 8 / CW);
+  };
+  const int64_t blocks = (int64_t)p.tiles_m * p.tiles_n * p.groups;
+  if (per_cu(3) > 0 && (per_cu(3) >= per_cu(2) || blocks <= 256 * per_cu(3)))
+    return launch_halo_nbuf<MODE, R, CW, NI, HV, AV, 3>(p, h, s);
+  launch_halo_nbuf<MODE, R, CW, NI, HV, AV, 2>(p, h, s);
 }
 
 template <int MODE, int R, int CW>

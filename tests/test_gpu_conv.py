@@ -129,6 +129,8 @@ HALO_SHAPES = [
     # rows 16 bytes wide: 16-byte halo loads
     synth.ConvShape("h28", 1, 20, 28, 28, 24, 3, 3, (1, 1), (1, 1, 1, 1)),
     synth.ConvShape("h56s2", 2, 16, 56, 56, 8, 3, 3, (2, 2), (1, 1, 1, 1)),
+    # wide rows: halos of two buffers (two barriers per chunk)
+    synth.ConvShape("h56", 1, 36, 56, 56, 20, 3, 3, (1, 1), (1, 1, 1, 1)),
     # 49 pixels per image, three images
     synth.ConvShape("h7", 3, 36, 7, 7, 70, 3, 3, (1, 1), (1, 1, 1, 1)),
     # groups, dilation, strides on one axis, asymmetric padding
