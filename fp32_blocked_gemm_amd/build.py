@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libog.so")
 OBJDIR = os.path.join(HERE, "_build")
 API = os.path.join(CSRC, "og_api.hip")
 UNITS = os.path.join(CSRC, "og_units.hip")
-N_UNITS = 16  # kernel groups of og_units.hip, compiled in parallel
+N_UNITS = 17  # kernel groups of og_units.hip, compiled in parallel
 SOURCES = [API, UNITS]
 HEADERS = [os.path.join(CSRC, "og_kernels.hpp"), os.path.join(CSRC, "og_launch.hpp"),
            os.path.join(INCLUDE, "og.h")]

@@ -73,7 +73,7 @@ def main() -> None:
             return None
         v = list(tiles)
         if s.KH == 3 and s.KW == 3:
-            v += [26, 27, 28]
+            v += [26, 27, 28, 31, 32, 33]
         if s.KH == 1 and s.KW == 1:
             v += panel
         return keep(v)

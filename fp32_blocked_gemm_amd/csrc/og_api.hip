@@ -196,18 +196,24 @@ constexpr ModelCost kFastCosts[] = {
     {20, 2, 0.25, 256, 28.724, 0.412, 4.546, 0.0276, 0.0000},
     {20, 3, 0.5, 256, 36.809, 0.000, 8.740, 0.0000, 0.0000},
     {20, 4, 0.25, 256, 46.385, 0.497, 4.725, 0.0000, 0.0000},
-    {26, 1, 1, 256, 3.880, 0.000, 5.343, 0.9813, 0.0996},
-    {26, 4, 1, 256, 4.824, 2.872, 3.466, 0.3856, 0.0792},
-    {27, 1, 0.5, 256, 6.924, 1.636, 3.201, 0.4855, 0.1859},
-    {27, 4, 1, 256, 9.031, 4.793, 2.384, 0.1186, 0.0588},
-    {28, 1, 1, 256, 9.809, 3.440, 1.811, 0.1227, 0.1035},
-    {28, 4, 1, 256, 11.778, 5.403, 2.846, 0.3072, 0.0213},
+    {26, 1, 1, 256, 3.851, 0.000, 5.334, 0.9905, 0.0996},
+    {26, 4, 1, 256, 4.864, 2.845, 3.406, 0.3862, 0.0789},
+    {27, 1, 0.5, 256, 6.921, 1.587, 3.198, 0.4847, 0.1870},
+    {27, 4, 1, 256, 9.054, 4.701, 2.449, 0.1241, 0.0583},
+    {28, 1, 1, 256, 9.804, 3.408, 1.789, 0.1367, 0.1023},
+    {28, 4, 1, 256, 11.834, 5.310, 2.876, 0.3160, 0.0204},
     {29, 0, 0.25, 256, 9.776, 0.493, 3.298, 0.1214, 0.0000},
     {29, 2, 0.5, 256, 8.419, 1.002, 3.144, 0.0000, 0.0000},
     {29, 3, 0.75, 256, 9.878, 1.438, 4.119, 0.3371, 0.0000},
     {30, 0, 0.25, 256, 15.907, 0.442, 3.476, 0.0498, 0.0000},
     {30, 2, 0.25, 256, 14.384, 1.044, 3.014, 0.0000, 0.0000},
     {30, 3, 0.75, 256, 13.387, 0.000, 4.620, 0.3017, 0.0000},
+    {31, 1, 0.75, 256, 1.398, 1.006, 5.167, 1.3164, 0.0990},
+    {31, 4, 1, 256, 1.436, 2.956, 0.011, 2.2745, 0.0854},
+    {32, 1, 1, 256, 5.531, 3.008, 1.193, 0.3708, 0.1009},
+    {32, 4, 1, 256, 9.695, 6.701, 1.730, 0.8313, 0.0000},
+    {33, 1, 0.5, 256, 3.929, 0.000, 6.217, 1.3628, 0.0856},
+    {33, 4, 1, 256, 0.904, 1.573, 2.845, 2.8047, 0.0995},
 };
 
 // Exact mode: the same form and families, fitted the same way to the same
@@ -284,12 +290,18 @@ constexpr ModelCost kExactCosts[] = {
     {20, 2, 1, 512, 58.484, 0.412, 4.382, 0.1826, 0.0000},
     {20, 3, 0.5, 512, 90.270, 0.106, 8.587, 0.0740, 0.0000},
     {20, 4, 0.75, 768, 91.113, 0.549, 3.833, 0.7017, 0.0000},
-    {26, 1, 1, 512, 12.712, 0.000, 3.448, 1.3250, 0.2802},
-    {26, 4, 1, 256, 8.418, 0.000, 7.610, 1.5286, 0.1345},
-    {27, 1, 0.25, 256, 24.125, 0.000, 6.923, 1.1436, 0.1877},
-    {27, 4, 1, 256, 29.940, 4.297, 2.490, 0.1617, 0.0537},
-    {28, 1, 1, 256, 19.962, 3.054, 1.932, 0.2556, 0.0722},
-    {28, 4, 1, 256, 19.494, 5.578, 2.600, 0.3863, 0.0550},
+    {26, 1, 1, 512, 12.688, 0.000, 3.411, 1.3181, 0.2810},
+    {26, 4, 1, 256, 8.422, 0.000, 7.430, 1.5041, 0.1361},
+    {27, 1, 0.25, 256, 24.060, 0.000, 6.895, 1.1480, 0.1870},
+    {27, 4, 1, 256, 29.871, 4.356, 2.579, 0.1697, 0.0508},
+    {28, 1, 1, 256, 19.915, 3.055, 1.923, 0.2576, 0.0705},
+    {28, 4, 1, 256, 19.400, 5.357, 2.877, 0.4001, 0.0545},
+    {31, 1, 0.75, 256, 2.623, 0.872, 5.827, 1.4970, 0.0902},
+    {31, 4, 1, 256, 0.838, 2.716, 0.108, 2.7199, 0.1151},
+    {32, 1, 1, 256, 8.928, 2.576, 1.874, 0.1531, 0.0968},
+    {32, 4, 1, 256, 11.020, 7.444, 2.139, 0.4554, 0.0000},
+    {33, 1, 0.75, 256, 6.808, 0.000, 6.582, 1.4772, 0.0548},
+    {33, 4, 1, 256, 1.900, 0.269, 2.809, 3.4030, 0.1332},
 };
 
 // Blocks of a launch of variant t (columns per image where that kernel tiles so).
@@ -468,10 +480,10 @@ constexpr SplitCost kSplitCosts[] = {
 };
 // A split-k kernel is taken only when its estimate is below this fraction
 // of the fast-mode kernel's: the two estimates' errors would otherwise pick it
-// where it is slower (measured over the same shapes, with split-k launches
-// of one round only: 8 % less summed time than fast mode and no shape
-// slower, against 12 % less for the best variant of every shape).
-constexpr double kSplitMargin = 0.85;
+// where it is slower (with split-k launches of one round only; 0.85 with the
+// earlier fast-mode table, 0.9 since the refitted one, whose estimates err
+// less: ResNet-50 at batch 1 keeps its split-k layers).
+constexpr double kSplitMargin = 0.9;
 
 // one_round: only launches whose waves all run at once (the model's error
 // grows with the rounds, and a split-k launch of several rounds was measured
@@ -512,14 +524,13 @@ int mode2_variant(const Shape &s, double fast_estimate) {
 }
 
 // The halo kernel's estimate for a 3x3 convolution whose images hold
-// `tiles` tiles of 64 lanes in all (variants 26, 27 and 28: 16, 32 and 32
-// rows per block; those whose block fits the LDS), in exact or fast mode;
-// the variant of the lowest.
+// `tiles` tiles of 64 lanes in all (variants 26..28 and 31..33, those whose
+// block fits the LDS), in exact or fast mode; the variant of the lowest.
 double halo_estimate(int mode, const Shape &s, const HaloPlan &h, int64_t tiles, int *variant) {
   double best = 1e300;
-  for (const auto [v, rows] : {std::pair<int, int64_t>{26, 16}, {27, 32}, {28, 32}}) {
+  for (const int v : {26, 27, 28, 31, 32, 33}) {
     if (!halo_fits(h, v)) continue;
-    const double e = model_estimate(mode, v, s, ceil_div(s.M, rows) * tiles * s.groups);
+    const double e = model_estimate(mode, v, s, ceil_div(s.M, (int64_t)halo_block_rows(v)) * tiles * s.groups);
     if (e < best) best = e, *variant = v;
   }
   return best;
@@ -1023,9 +1034,9 @@ og_status og_set_stream(void *hip_stream) {
 void *og_get_stream(void) { return t_stream; }
 
 og_status og_set_variant(int variant) {
-  if (variant < 0 || variant > kLastPanelVariant)
+  if (variant < 0 || variant > kLastHaloDppVariant)
     return fail(OG_ERR_INVALID_ARG, "og_set_variant: %d is not in 0..%d", variant,
-                kLastPanelVariant);
+                kLastHaloDppVariant);
   t_variant = variant;
   return ok();
 }

@@ -1151,6 +1151,7 @@ __global__ void __launch_bounds__(64 * W) lane_conv_kernel(Problem p) {
 #define OG_DPP(u) " row_newbcast:" #u " row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
 // fast, one row: %0 acc, %1 weights, %2.. B values
 #define OG_F1(u, b) "v_fmac_f32_dpp %0, %1, %" #b OG_DPP(u)
+#define OG_FAST1_4 "s_nop 1\n" OG_F1(0, 2) OG_F1(1, 3) OG_F1(2, 4) OG_F1(3, 5)
 #define OG_FAST1_8                                                                     \
   "s_nop 1\n" OG_F1(0, 2) OG_F1(1, 3) OG_F1(2, 4) OG_F1(3, 5) OG_F1(4, 6) OG_F1(5, 7) \
       OG_F1(6, 8) OG_F1(7, 9)
@@ -1159,6 +1160,7 @@ __global__ void __launch_bounds__(64 * W) lane_conv_kernel(Problem p) {
       OG_F1(13, 15) OG_F1(14, 16) OG_F1(15, 17)
 // fast, two rows: %0 %1 acc, %2 %3 weights, %4.. B values
 #define OG_F2(u, b) "v_fmac_f32_dpp %0, %2, %" #b OG_DPP(u) "v_fmac_f32_dpp %1, %3, %" #b OG_DPP(u)
+#define OG_FAST2_4 "s_nop 1\n" OG_F2(0, 4) OG_F2(1, 5) OG_F2(2, 6) OG_F2(3, 7)
 #define OG_FAST2_8                                                                      \
   "s_nop 1\n" OG_F2(0, 4) OG_F2(1, 5) OG_F2(2, 6) OG_F2(3, 7) OG_F2(4, 8) OG_F2(5, 9) \
       OG_F2(6, 10) OG_F2(7, 11)
@@ -1174,6 +1176,8 @@ __global__ void __launch_bounds__(64 * W) lane_conv_kernel(Problem p) {
       OG_A1(1) OG_M1(1, 4, 8) OG_A1(2) OG_M1(2, 5, 9) OG_A1(1) OG_M1(1, 6, 10) OG_A1(2)     \
           OG_M1(2, 7, 11) OG_A1(1)
 #define OG_EXACT1_8 OG_EXACT1_HEAD OG_A1(2)
+#define OG_EXACT1_4 \
+  "s_nop 1\n" OG_M1(1, 0, 4) OG_M1(2, 1, 5) OG_A1(1) OG_M1(1, 2, 6) OG_A1(2) OG_M1(2, 3, 7) OG_A1(1) OG_A1(2)
 #define OG_EXACT1_16                                                                      \
   OG_EXACT1_HEAD OG_M1(1, 8, 12) OG_A1(2) OG_M1(2, 9, 13) OG_A1(1) OG_M1(1, 10, 14) OG_A1(2) \
       OG_M1(2, 11, 15) OG_A1(1) OG_M1(1, 12, 16) OG_A1(2) OG_M1(2, 13, 17) OG_A1(1)          \
@@ -1189,12 +1193,16 @@ __global__ void __launch_bounds__(64 * W) lane_conv_kernel(Problem p) {
           OG_M2(4, 5, 5, 13) OG_A2(2, 3) OG_M2(2, 3, 6, 14) OG_A2(4, 5) OG_M2(4, 5, 7, 15) \
               OG_A2(2, 3)
 #define OG_EXACT2_8 OG_EXACT2_HEAD OG_A2(4, 5)
+#define OG_EXACT2_4                                                                          \
+  "s_nop 1\n" OG_M2(2, 3, 0, 8) OG_M2(4, 5, 1, 9) OG_A2(2, 3) OG_M2(2, 3, 2, 10) OG_A2(4, 5) \
+      OG_M2(4, 5, 3, 11) OG_A2(2, 3) OG_A2(4, 5)
 #define OG_EXACT2_16                                                                     \
   OG_EXACT2_HEAD OG_M2(2, 3, 8, 16) OG_A2(4, 5) OG_M2(4, 5, 9, 17) OG_A2(2, 3)           \
       OG_M2(2, 3, 10, 18) OG_A2(4, 5) OG_M2(4, 5, 11, 19) OG_A2(2, 3) OG_M2(2, 3, 12, 20) \
           OG_A2(4, 5) OG_M2(4, 5, 13, 21) OG_A2(2, 3) OG_M2(2, 3, 14, 22) OG_A2(4, 5)     \
               OG_M2(4, 5, 15, 23) OG_A2(2, 3) OG_A2(4, 5)
 
+#define OG_B4(b) "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3])
 #define OG_B8(b) "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]), "v"(b[4]), "v"(b[5]), "v"(b[6]), "v"(b[7])
 #define OG_B16(b)                                                                            \
   OG_B8(b), "v"(b[8]), "v"(b[9]), "v"(b[10]), "v"(b[11]), "v"(b[12]), "v"(b[13]), "v"(b[14]), \
@@ -1204,24 +1212,34 @@ __global__ void __launch_bounds__(64 * W) lane_conv_kernel(Problem p) {
 // weights of row r in w[r] (lane u of each row of 16 holds step u's weight).
 template <int MODE, int R, int N>
 __device__ __forceinline__ void dpp_steps(float (&acc)[R], const float (&w)[R], const float *b) {
-  static_assert((R == 1 || R == 2) && (N == 8 || N == 16), "dpp_steps shape");
-  if constexpr (MODE == kFast && R == 1 && N == 8)
+  static_assert((R == 1 || R == 2) && (N == 4 || N == 8 || N == 16), "dpp_steps shape");
+  if constexpr (MODE == kFast && R == 1 && N == 4)
+    asm(OG_FAST1_4 : "+v"(acc[0]) : "v"(w[0]), OG_B4(b));
+  else if constexpr (MODE == kFast && R == 1 && N == 8)
     asm(OG_FAST1_8 : "+v"(acc[0]) : "v"(w[0]), OG_B8(b));
   else if constexpr (MODE == kFast && R == 1)
     asm(OG_FAST1_16 : "+v"(acc[0]) : "v"(w[0]), OG_B16(b));
+  else if constexpr (MODE == kFast && N == 4)
+    asm(OG_FAST2_4 : "+v"(acc[0]), "+v"(acc[1]) : "v"(w[0]), "v"(w[1]), OG_B4(b));
   else if constexpr (MODE == kFast && N == 8)
     asm(OG_FAST2_8 : "+v"(acc[0]), "+v"(acc[1]) : "v"(w[0]), "v"(w[1]), OG_B8(b));
   else if constexpr (MODE == kFast)
     asm(OG_FAST2_16 : "+v"(acc[0]), "+v"(acc[1]) : "v"(w[0]), "v"(w[1]), OG_B16(b));
   else if constexpr (R == 1) {
     float t0, t1;
-    if constexpr (N == 8)
+    if constexpr (N == 4)
+      asm(OG_EXACT1_4 : "+v"(acc[0]), "=&v"(t0), "=&v"(t1) : "v"(w[0]), OG_B4(b));
+    else if constexpr (N == 8)
       asm(OG_EXACT1_8 : "+v"(acc[0]), "=&v"(t0), "=&v"(t1) : "v"(w[0]), OG_B8(b));
     else
       asm(OG_EXACT1_16 : "+v"(acc[0]), "=&v"(t0), "=&v"(t1) : "v"(w[0]), OG_B16(b));
   } else {
     float t0, t1, t2, t3;
-    if constexpr (N == 8)
+    if constexpr (N == 4)
+      asm(OG_EXACT2_4
+          : "+v"(acc[0]), "+v"(acc[1]), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)
+          : "v"(w[0]), "v"(w[1]), OG_B4(b));
+    else if constexpr (N == 8)
       asm(OG_EXACT2_8
           : "+v"(acc[0]), "+v"(acc[1]), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)
           : "v"(w[0]), "v"(w[1]), OG_B8(b));
@@ -1811,7 +1829,7 @@ __global__ void __launch_bounds__(64 * (CW + ChainShape<KH * KW, BN, chain_rows(
 // hrows * (W + pL + pR) + 3 cells (two cells read past the rows by lanes of
 // no pixel, one spare written by idle lanes).
 // ---------------------------------------------------------------------------
-template <int MODE, int KH, int KW, int R, int CW, int NI, bool HV, bool AV, int NWS, int NBUF>
+template <int MODE, int KH, int KW, int R, int CW, int NI, bool HV, bool AV, int NWS, int NBUF, bool DPP>
 __global__ void __launch_bounds__(64 * CW) halo_kernel(Problem p) {
   constexpr int KHW = KH * KW;
   constexpr int CC = 16;                 // channels per chunk
@@ -1823,7 +1841,8 @@ __global__ void __launch_bounds__(64 * CW) halo_kernel(Problem p) {
   constexpr int C4 = CSTR / 4;           // its 16-byte units
   constexpr int CPW = CC / CW;           // channels each wave stages
   constexpr int VW = HV ? 4 : 1;         // floats per halo load
-  constexpr int WROWS = 4 * R, WST = WROWS * BK;  // a wave's weight rows; floats of a weight stage
+  constexpr int RA = DPP ? 1 : 4;                 // rows per chain: a lane's own (DPP), 4 (matrix cores)
+  constexpr int WROWS = RA * R, WST = WROWS * BK;  // a wave's weight rows; floats of a weight stage
   constexpr int WW = AV ? 4 : 1;                  // taps per weight load
   constexpr int NQW = WST / WW, NIW = (NQW + 63) / 64;  // weight loads per stage, per lane
   constexpr int WSTP = NIW * 64 * WW;             // floats of a stage, every lane's place included
@@ -1893,7 +1912,7 @@ __global__ void __launch_bounds__(64 * CW) halo_kernel(Problem p) {
   // of LDS stages ([row][tap], WW taps per lane and load, straight from
   // memory into LDS) one chunk ahead; read back per chunk, lane 4b + i
   // taking row i of each chain at tap b of each 16-tap group
-  const int wrow0 = tc.tm * (4 * R * CW) + wave * 4 * R;  // first row of the wave
+  const int wrow0 = tc.tm * (WROWS * CW) + wave * WROWS;  // first row of the wave
   const int wbase = min(wrow0, p.M - 1);
   const __amdgpu_buffer_rsrc_t wrs =
       buffer_at(p.A + tc.g * p.a_gstride + (int64_t)wbase * p.lda, kRange);
@@ -1913,11 +1932,16 @@ __global__ void __launch_bounds__(64 * CW) halo_kernel(Problem p) {
   const float *xg = p.B + img * p.x_img + tc.g * p.x_grp + (int64_t)r0 * p.W;  // row r0 of channel 0
   const int nch = (cin_g + CC - 1) / CC, last = nch - 1;
   float rb[2][CPW][NI * VW];  // halo of chunk c in slot c % 2
-  float wv[2][R][NG];         // weights of chunk c (read from its stage) in slot c % 2
+  // weights of chunk c (read from its stage) in slot c % 2: matrix cores,
+  // 16-tap groups of the chunk; DPP, per quad its runs of 16, 16 and 4 taps
+  constexpr int NGW = DPP ? 3 * NQC : NG;
+  static_assert(!DPP || QT == 36, "DPP runs of a quad: 16, 16, 4 taps");
+  float wv[2][R][NGW];
   f32x4 qb[2][KHW];           // a quad's input values (4 channels per position), read one quad ahead
-  f32x4 acc[R];
+  f32x4 acc[R];   // matrix cores: the 4 rows of chain r at the lane's pixel
+  float accd[R];  // DPP: row r at the lane's pixel
 #pragma unroll
-  for (int c = 0; c < R; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int c = 0; c < R; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f}, accd[c] = 0.0f;
 
   auto load_halo = [&](int c, auto slot) __attribute__((always_inline)) {
     constexpr int S = decltype(slot)::value;
@@ -1966,11 +1990,24 @@ __global__ void __launch_bounds__(64 * CW) halo_kernel(Problem p) {
       for (int e = lane; e < WST; e += 64)
         if (c * BK + e % BK >= p.K) stg[e] = -0.0f;
     }
-    const float *src = stg + (lane & 3) * BK + tb;
+    if constexpr (DPP) {
+      // lane u of each row of 16 holds tap u of the run (for row_newbcast);
+      // a quad's third run has 4 taps (lanes past them read taps of the next
+      // quad or the stage's padding, unused)
+      const float *src = stg + (lane & 15);
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+      for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int gi = 0; gi < NG; ++gi) wv[S][r][gi] = src[4 * r * BK + 16 * gi];
+        for (int q = 0; q < NQC; ++q)
+#pragma unroll
+          for (int j = 0; j < 3; ++j) wv[S][r][3 * q + j] = src[r * BK + QT * q + 16 * j];
+    } else {
+      const float *src = stg + (lane & 3) * BK + tb;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) wv[S][r][gi] = src[4 * r * BK + 16 * gi];
+    }
   };
   // the wave's CPW channels of each of its halo elements, one write per
   // input position
@@ -2013,7 +2050,23 @@ __global__ void __launch_bounds__(64 * CW) halo_kernel(Problem p) {
   // out of registers.
   auto products = [&](auto quad, auto slot, auto from) __attribute__((always_inline)) {
     constexpr int Q = decltype(quad)::value, S = decltype(slot)::value, B = decltype(from)::value;
-    if constexpr (MODE == kFast) {
+    if constexpr (DPP) {
+      // runs of 16, 16 and 4 taps, each one asm block of DPP steps (weights
+      // broadcast from lane u of the run; exact mode's products and sums
+      // interleaved inside the block)
+      static_for<3>([&](auto jq) __attribute__((always_inline)) {
+        constexpr int j = decltype(jq)::value, n = j < 2 ? 16 : 4;
+        float b[n];
+        static_for<n>([&](auto uq) __attribute__((always_inline)) {
+          constexpr int t = 16 * j + decltype(uq)::value, ci = t / KHW, pos = t % KHW;
+          b[decltype(uq)::value] = qb[B][pos][ci];
+        });
+        float w[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) w[r] = wv[S][r][3 * Q + j];
+        dpp_steps<MODE, R, n>(accd, w, b);
+      });
+    } else if constexpr (MODE == kFast) {
       static_for<QT>([&](auto tq) __attribute__((always_inline)) {
         constexpr int t = decltype(tq)::value, s = QT * Q + t, ci = t / KHW, pos = t % KHW;
 #pragma unroll
@@ -2138,13 +2191,13 @@ __global__ void __launch_bounds__(64 * CW) halo_kernel(Problem p) {
     // one uniform test picks the store loop with or without the epilogue
     auto store_all = [&](auto epi) __attribute__((always_inline)) {
       constexpr bool E = decltype(epi)::value;
-      float pb[R][4], pr[R][4];
+      float pb[R][RA], pr[R][RA];
       if constexpr (E) {
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = wrow0 + 4 * r + i;
+          for (int i = 0; i < RA; ++i) {
+            const int row = wrow0 + RA * r + i;
             const bool ok = row < p.M;
             pb[r][i] = epi_bias(p, ok, tc.g * p.M + row);
             pr[r][i] = epi_res(p, ok, base + (int64_t)(ok ? row : 0) * p.OHW);
@@ -2153,13 +2206,14 @@ __global__ void __launch_bounds__(64 * CW) halo_kernel(Problem p) {
 #pragma unroll
       for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = wrow0 + 4 * r + i;
+        for (int i = 0; i < RA; ++i) {
+          const int row = wrow0 + RA * r + i;
+          const float v = DPP ? accd[r] : acc[r][i];
           if (row < p.M) {
             if constexpr (E)
-              base[(int64_t)row * p.OHW] = finish_with(p, acc[r][i], pb[r][i], pr[r][i]);
+              base[(int64_t)row * p.OHW] = finish_with(p, v, pb[r][i], pr[r][i]);
             else
-              base[(int64_t)row * p.OHW] = finish<false>(p, acc[r][i], 0, base);
+              base[(int64_t)row * p.OHW] = finish<false>(p, v, 0, base);
           }
         }
     };

@@ -478,13 +478,40 @@ void launch_splitk_matrix(int variant, bool av, bool bv, bool bt, const og::Prob
 void launch_splitk_conv(int variant, bool av, bool planes, const og::Problem &p, hipStream_t s);
 
 // ---------------------------------------------------------------------------
-// Halo kernel (fast mode, 3x3 windows) over 64 output pixels of one image:
-// variant 26 four waves of one chain of 4 output channels (16 rows per
-// block), 27 four waves of two chains (32 rows), 28 eight waves of one chain
-// (32 rows, two waves per SIMD).
+// Halo kernel (3x3 windows) over 64 lanes of one image.  Matrix-core
+// chains: variant 26 four waves of one chain of 4 output channels (16 rows
+// per block), 27 four waves of two chains (32 rows), 28 eight waves of one
+// chain (32 rows, two waves per SIMD).  DPP steps (a lane's own rows, the
+// weights broadcast within rows of 16 lanes; for latency-bound shapes):
+// variant 31 four waves of one row (4 rows per block), 32 eight waves of one
+// row (8 rows), 33 four waves of two rows (8 rows).
 // ---------------------------------------------------------------------------
 constexpr int kFirstHaloVariant = 26, kLastHaloVariant = 28;
-inline bool is_halo(int v) { return v >= kFirstHaloVariant && v <= kLastHaloVariant; }
+constexpr int kFirstHaloDppVariant = 31, kLastHaloDppVariant = 33;
+inline bool is_halo(int v) {
+  return (v >= kFirstHaloVariant && v <= kLastHaloVariant) ||
+         (v >= kFirstHaloDppVariant && v <= kLastHaloDppVariant);
+}
+// shape of a halo variant: rows per chain set R, waves CW, DPP steps
+struct HaloShape {
+  int r, cw;
+  bool dpp;
+};
+inline HaloShape halo_shape(int v) {
+  switch (v) {
+    case 26: return {1, 4, false};
+    case 27: return {2, 4, false};
+    case 28: return {1, 8, false};
+    case 31: return {1, 4, true};
+    case 32: return {1, 8, true};
+    default: return {2, 4, true};
+  }
+}
+// output rows per block
+inline int halo_block_rows(int v) {
+  const HaloShape h = halo_shape(v);
+  return (h.dpp ? 1 : 4) * h.r * h.cw;
+}
 
 // The staging of a shape: rows a tile of 64 output pixels stages (the
 // output rows 64 consecutive pixels can touch, then the rows their windows
@@ -501,14 +528,14 @@ struct HaloPlan {
   int64_t tiles;    // tiles of 64 lanes per image
   int64_t buf_lds;  // bytes of one halo buffer
 };
-// a wave's weight stage in floats (4 * R rows of 144 taps, padded to whole
-// loads of 64 lanes x 16 bytes), the weight stages of a block of variant v
-// in bytes (two per wave), and the LDS a workgroup may hold on gfx950
-constexpr int64_t halo_weight_stage(int R) { return (4 * R * 144 / 4 + 63) / 64 * 64 * 4; }
-constexpr int64_t halo_weight_lds(int v) {
-  return v == 26 ? 4 * 2 * halo_weight_stage(1) * 4
-       : v == 27 ? 4 * 2 * halo_weight_stage(2) * 4
-                 : 8 * 2 * halo_weight_stage(1) * 4;
+// a wave's weight stage in floats (its rows of 144 taps -- 4 * R on the
+// matrix cores, R with DPP steps -- padded to whole loads of 64 lanes x 16
+// bytes), the weight stages of a block of variant v in bytes (two per wave),
+// and the LDS a workgroup may hold on gfx950
+constexpr int64_t halo_weight_stage(int R, bool dpp) { return ((dpp ? 1 : 4) * R * 144 / 4 + 63) / 64 * 64 * 4; }
+inline int64_t halo_weight_lds(int v) {
+  const HaloShape h = halo_shape(v);
+  return (int64_t)h.cw * 2 * halo_weight_stage(h.r, h.dpp) * 4;
 }
 constexpr int64_t kHaloMaxLds = 160 * 1024;
 inline bool halo_plan(const og::Problem &p, bool x_aligned16, HaloPlan &h) {
@@ -540,16 +567,16 @@ inline bool halo_plan(const og::Problem &p, bool x_aligned16, HaloPlan &h) {
 // whether variant v's block (two halo buffers and its weight stages) fits the LDS
 inline bool halo_fits(const HaloPlan &h, int v) { return 2 * h.buf_lds + halo_weight_lds(v) <= kHaloMaxLds; }
 
-template <int MODE, int R, int CW, int NI, bool HV, bool AV, int NBUF>
+template <int MODE, int R, int CW, bool DPP, int NI, bool HV, bool AV, int NBUF>
 void launch_halo_nbuf(const og::Problem &p, const HaloPlan &h, hipStream_t s) {
   constexpr int NWS = 2;
-  const auto kernel = og::halo_kernel<MODE, 3, 3, R, CW, NI, HV, AV, NWS, NBUF>;
+  const auto kernel = og::halo_kernel<MODE, 3, 3, R, CW, NI, HV, AV, NWS, NBUF, DPP>;
   // more than 64 KB of dynamic LDS must be allowed per kernel, once
   static const hipError_t allowed =
       hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kHaloMaxLds);
   (void)allowed;
   const dim3 grid((unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)p.groups), block(64 * CW);
-  const size_t lds = (size_t)(NBUF * h.buf_lds) + (size_t)CW * NWS * halo_weight_stage(R) * 4;
+  const size_t lds = (size_t)(NBUF * h.buf_lds) + (size_t)CW * NWS * halo_weight_stage(R, DPP) * 4;
   hipLaunchKernelGGL(kernel, grid, block, lds, s, p);
 }
 
@@ -559,38 +586,39 @@ void launch_halo_nbuf(const og::Problem &p, const HaloPlan &h, hipStream_t s) {
 // buffers where they fit and the launch's blocks need no more compute-unit
 // slots than three buffers leave (the kernels use over 128 registers: at
 // most two waves per SIMD), else two (a second barrier per chunk).
-template <int MODE, int R, int CW, int NI, bool HV, bool AV>
+template <int MODE, int R, int CW, bool DPP, int NI, bool HV, bool AV>
 void launch_halo_shape(og::Problem p, const HaloPlan &h, hipStream_t s) {
   p.hrows = h.rows;
   p.vpitch = h.vpitch;
-  p.tiles_m = (int)ceil_div(p.M, 4 * R * CW);
+  p.tiles_m = (int)ceil_div(p.M, (DPP ? 1 : 4) * R * CW);
   p.tiles_n = (int)((p.N / p.OHW) * h.tiles);
   auto per_cu = [&](int nbuf) {
-    const int64_t lds = nbuf * h.buf_lds + (int64_t)CW * 2 * halo_weight_stage(R) * 4;
+    const int64_t lds = nbuf * h.buf_lds + (int64_t)CW * 2 * halo_weight_stage(R, DPP) * 4;
     return lds > kHaloMaxLds ? 0 : std::min<int64_t>(kHaloMaxLds / lds, 8 / CW);
   };
   const int64_t blocks = (int64_t)p.tiles_m * p.tiles_n * p.groups;
   if (per_cu(3) > 0 && (per_cu(3) >= per_cu(2) || blocks <= 256 * per_cu(3)))
-    return launch_halo_nbuf<MODE, R, CW, NI, HV, AV, 3>(p, h, s);
-  launch_halo_nbuf<MODE, R, CW, NI, HV, AV, 2>(p, h, s);
+    return launch_halo_nbuf<MODE, R, CW, DPP, NI, HV, AV, 3>(p, h, s);
+  launch_halo_nbuf<MODE, R, CW, DPP, NI, HV, AV, 2>(p, h, s);
 }
 
-template <int MODE, int R, int CW>
+template <int MODE, int R, int CW, bool DPP>
 void launch_halo_r(og::Problem p, const HaloPlan &h, hipStream_t s) {
   if (h.hv) {
-    if (h.ni == 1) return launch_halo_shape<MODE, R, CW, 1, true, true>(p, h, s);
-    return launch_halo_shape<MODE, R, CW, 2, true, true>(p, h, s);
+    if (h.ni == 1) return launch_halo_shape<MODE, R, CW, DPP, 1, true, true>(p, h, s);
+    return launch_halo_shape<MODE, R, CW, DPP, 2, true, true>(p, h, s);
   }
-  if (h.ni == 2) return launch_halo_shape<MODE, R, CW, 2, false, true>(p, h, s);
-  if (h.ni == 4) return launch_halo_shape<MODE, R, CW, 4, false, true>(p, h, s);
-  return launch_halo_shape<MODE, R, CW, 8, false, true>(p, h, s);
+  if (h.ni == 2) return launch_halo_shape<MODE, R, CW, DPP, 2, false, true>(p, h, s);
+  if (h.ni == 4) return launch_halo_shape<MODE, R, CW, DPP, 4, false, true>(p, h, s);
+  return launch_halo_shape<MODE, R, CW, DPP, 8, false, true>(p, h, s);
 }
 
-// A 3x3 convolution (gathered B) on variant 26, 27 or 28, planned by
-// halo_plan, in exact (0) or fast (1) mode.
+// A 3x3 convolution (gathered B) on a halo variant (26..28, 31..33),
+// planned by halo_plan, in exact (0) or fast (1) mode.
 void launch_halo_conv(int variant, int mode, const og::Problem &p, const HaloPlan &h, hipStream_t s);
-// (its exact-mode kernels, in their own group)
+// (its kernels by group: matrix-core fast, matrix-core exact, DPP both modes)
 void launch_halo_exact(int variant, const og::Problem &p, const HaloPlan &h, hipStream_t s);
+void launch_halo_dpp(int variant, int mode, const og::Problem &p, const HaloPlan &h, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Panel kernel (fast mode: 1x1 convolutions, any stride and padding, and

@@ -86,16 +86,28 @@ void launch_splitk_conv(int variant, bool av, bool planes, const og::Problem &p,
 }
 #elif OG_UNIT == 14
 void launch_halo_conv(int variant, int mode, const og::Problem &p, const HaloPlan &h, hipStream_t s) {
+  if (halo_shape(variant).dpp) return launch_halo_dpp(variant, mode, p, h, s);
   if (mode == OG_MODE_EXACT) return launch_halo_exact(variant, p, h, s);
-  if (variant == 26) return launch_halo_r<og::kFast, 1, 4>(p, h, s);
-  if (variant == 27) return launch_halo_r<og::kFast, 2, 4>(p, h, s);
-  return launch_halo_r<og::kFast, 1, 8>(p, h, s);
+  if (variant == 26) return launch_halo_r<og::kFast, 1, 4, false>(p, h, s);
+  if (variant == 27) return launch_halo_r<og::kFast, 2, 4, false>(p, h, s);
+  return launch_halo_r<og::kFast, 1, 8, false>(p, h, s);
 }
 #elif OG_UNIT == 16
 void launch_halo_exact(int variant, const og::Problem &p, const HaloPlan &h, hipStream_t s) {
-  if (variant == 26) return launch_halo_r<og::kExact, 1, 4>(p, h, s);
-  if (variant == 27) return launch_halo_r<og::kExact, 2, 4>(p, h, s);
-  return launch_halo_r<og::kExact, 1, 8>(p, h, s);
+  if (variant == 26) return launch_halo_r<og::kExact, 1, 4, false>(p, h, s);
+  if (variant == 27) return launch_halo_r<og::kExact, 2, 4, false>(p, h, s);
+  return launch_halo_r<og::kExact, 1, 8, false>(p, h, s);
+}
+#elif OG_UNIT == 17
+template <int MODE>
+static void launch_halo_dpp_mode(int variant, const og::Problem &p, const HaloPlan &h, hipStream_t s) {
+  if (variant == 31) return launch_halo_r<MODE, 1, 4, true>(p, h, s);
+  if (variant == 32) return launch_halo_r<MODE, 1, 8, true>(p, h, s);
+  return launch_halo_r<MODE, 2, 4, true>(p, h, s);
+}
+void launch_halo_dpp(int variant, int mode, const og::Problem &p, const HaloPlan &h, hipStream_t s) {
+  if (mode == OG_MODE_EXACT) return launch_halo_dpp_mode<og::kExact>(variant, p, h, s);
+  launch_halo_dpp_mode<og::kFast>(variant, p, h, s);
 }
 #elif OG_UNIT == 15
 template <int R>

@@ -246,10 +246,16 @@ void *og_get_stream(void);
  * stages, the k chain of each 4 rows on the matrix cores as in 26..28;
  * 4 waves of 4 rows and 4 waves of 2 x 4 rows.  In exact mode, and on
  * shapes they do not take (other windows), they run as 0 does.
+ * 31, 32, 33 = the halo kernel with DPP steps in place of the matrix
+ * cores (for latency-bound 3x3 convolutions, a small batch): a lane's own
+ * output channels, each step one v_fmac_f32 (exact: v_mul_f32 then a
+ * separately rounded add) with the weight broadcast within rows of 16
+ * lanes; 4 waves of 1 row, 8 waves of 1 row and 4 waves of 2 rows.  On
+ * shapes they do not take they run as 0 does.
  * Every variant runs every shape (a convolution window other than 1x1 or
  * 3x3 runs variants 10..16 as variant 6; variants 18 and 19 run shapes
  * outside their own, and any matrix product, as 0 does).  A value outside
- * 0..30 returns OG_ERR_INVALID_ARG.
+ * 0..33 returns OG_ERR_INVALID_ARG.
  */
 og_status og_set_variant(int variant);
 int og_get_variant(void);

@@ -150,8 +150,8 @@ def test_out_size_matches_the_formula():
 
 
 def test_variant_and_stream_state(L):
-    assert L.og_set_variant(31) == og.OG_ERR_INVALID_ARG
-    assert L.og_set_variant(30) == og.OG_OK
+    assert L.og_set_variant(34) == og.OG_ERR_INVALID_ARG
+    assert L.og_set_variant(33) == og.OG_OK
     assert L.og_set_variant(-1) == og.OG_ERR_INVALID_ARG
     assert L.og_set_variant(3) == og.OG_OK and L.og_get_variant() == 3
     assert L.og_set_variant(0) == og.OG_OK

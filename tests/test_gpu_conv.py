@@ -149,12 +149,12 @@ HALO_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("variant", [26, 27, 28])
+@pytest.mark.parametrize("variant", [26, 27, 28, 31, 32, 33])
 def test_halo_kernel_shapes(orc, variant):
-    """The halo kernel (3x3 windows; exact mode's products on the matrix
-    cores and its sums on the VALU, fast mode's chains on the matrix cores)
-    bit for bit against the oracle; on shapes it does not take the variant
-    runs the automatic choice."""
+    """The halo kernel (3x3 windows; on the matrix cores, exact mode's
+    products there and its sums on the VALU, fast mode's chains there; or
+    in DPP steps on the VALU) bit for bit against the oracle; on shapes it
+    does not take the variant runs the automatic choice."""
     rng = np.random.default_rng(500 + variant)
     og.set_variant(variant)
     for s in HALO_SHAPES:

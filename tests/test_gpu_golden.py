@@ -37,7 +37,7 @@ from gpu_util import assert_same_bits, bits, say, to_device_strided, to_host, to
 
 pytestmark = pytest.mark.gpu
 MODES = {"exact": og.EXACT, "fast": og.FAST}
-VARIANTS = list(range(0, 21)) + [26, 27, 28, 29, 30]  # tiles, then the halo and panel kernels
+VARIANTS = list(range(0, 21)) + [26, 27, 28, 29, 30, 31, 32, 33]  # tiles, then the halo and panel kernels
 M, N, K = 300, 520, 40  # several tiles of the largest tile shapes, each ending inside
 
 
