@@ -9,9 +9,14 @@ fitted to -- ResNet-50's convolutions at batch 1, 2, 3, 4, 5, 6, 8, 12 and
 twelve 3x3 convolutions of other widths and 72 seeded random matrix
 products.  "heldout": shapes the fit did not see -- ResNet-50 at batch 7
 and 10, MobileNetV3-large at batch 3 and 5, four more 3x3 convolutions and
-24 random products of another seed.
+24 random products of another seed.  "large" (fitted too) and
+"large_heldout": products of the sizes of a language model's layers, m from
+1 to 4096 rows against n = 1024 to 11008 columns and k = 1024 to 8192 -- the
+4096^3, prefill 512x11008x4096 and single-row 1x4096x4096 products and 33
+seeded ones in the first; 8x4096x4096, 2048x11008x4096 and 16 of another
+seed, with no size of the first, in the second.
 
-    python3 -m fp32_blocked_gemm_amd.choice_sweep [--set fit|heldout] [--mode fast|exact]
+    python3 -m fp32_blocked_gemm_amd.choice_sweep [--set fit|heldout|large|large_heldout] [--mode fast|exact]
         [--only3x3] [--variants 26,27,28] [--out FILE] [--quick]
 
 prints one JSON line per shape (times in us) and a summary line.
@@ -22,10 +27,31 @@ import random
 import sys
 
 
+def large_products(which):
+    """(m, n, k, row-stride padding) of the "large" or "large_heldout" set:
+    products of at most 2 * 4096^3 multiply-adds, none of the second in the
+    first."""
+    def draw(seed, count, first):
+        rng, out = random.Random(seed), list(first)
+        while len(out) < count:
+            m, n, k = (rng.choice([1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 3072, 4096]),
+                       rng.choice([1024, 2048, 4096, 8192, 11008]), rng.choice([1024, 2048, 4096, 8192]))
+            p = (m, n, k, rng.choice([0, 4]))
+            if m * n * k <= 2 * 4096 ** 3 and p not in out:
+                out.append(p)
+        return out
+
+    fit = draw(41, 36, [(4096, 4096, 4096, 0), (512, 11008, 4096, 0), (1, 4096, 4096, 0)])
+    if which == "large":
+        return fit
+    held = draw(43, 40, [(8, 4096, 4096, 0), (2048, 11008, 4096, 0)])
+    return [p for p in held if p[:3] not in {q[:3] for q in fit}][:18]
+
+
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--out", default=None, help="also write the lines to this file")
-    ap.add_argument("--set", default="heldout", choices=("fit", "heldout"))
+    ap.add_argument("--set", default="heldout", choices=("fit", "heldout", "large", "large_heldout"))
     ap.add_argument("--quick", action="store_true", help="the first ResNet-50 batch only, 6 products")
     ap.add_argument("--mode", default="fast", choices=("fast", "exact"))
     ap.add_argument("--only3x3", action="store_true", help="3x3 convolutions only")
@@ -118,7 +144,11 @@ def main() -> None:
         regrets.append(e["regret"])
         emit(e)
 
-    if args.set == "fit":
+    products = []
+    if args.set in ("large", "large_heldout"):
+        resnet_b, mobile_b, other, seeds = (), (), (), ()
+        products = large_products(args.set)
+    elif args.set == "fit":
         resnet_b, mobile_b, seeds = (1, 2, 3, 4, 5, 6, 8, 12, 16), (1, 2, 4, 6, 8), ((7, 48), (23, 24))
         other = (synth.ConvShape("inc96_35", 8, 96, 35, 35, 96, 3, 3, (1, 1), (1, 1, 1, 1)),
                  synth.ConvShape("inc192_17", 8, 192, 17, 17, 192, 3, 3, (1, 1), (1, 1, 1, 1)),
@@ -139,7 +169,8 @@ def main() -> None:
                  synth.ConvShape("s2_64_80_b2", 2, 64, 80, 80, 128, 3, 3, (2, 2), (1, 1, 1, 1)),
                  synth.ConvShape("u32_96_b1", 1, 32, 96, 96, 32, 3, 3, (1, 1), (1, 1, 1, 1)))
     if args.quick:
-        resnet_b, mobile_b, other, seeds = resnet_b[:1], (), (), ((seeds[0][0], 6),)
+        resnet_b, mobile_b, other = resnet_b[:1], (), ()
+        seeds, products = ((seeds[0][0], 6),) if seeds else (), products[:3]
     seen = set()
     for b in resnet_b:
         for s in synth.resnet50_convs(b):
@@ -155,6 +186,8 @@ def main() -> None:
                 run_conv(s, f"mobilenetv3_b{b}")
     for s in other:
         run_conv(s, "other3x3")
+    for m, n, k, ld in products:
+        run_gemm(m, n, k, ld, args.set + "_products")
     for seed, nprod in seeds:
         rng = random.Random(seed)
         for _ in range(nprod):

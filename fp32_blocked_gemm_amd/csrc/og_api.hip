@@ -80,18 +80,26 @@ struct Shape {
   int64_t M, N, K, groups;
   int64_t ohw;  // output pixels per image; 0 for a matrix product
   int64_t khw;  // KH * KW; 0 for a matrix product
-  int ffam = 0;        // family of the fast-mode model (fast_family)
+  int ffam = 0;        // a convolution's family in the launch model (fast_family)
   double bytes = 0;    // bytes of the operands and the result, each counted once
   double halo_x = 0;   // halo kernel: thousands of input floats staged per block over its k
 };
 
-// Family of a convolution in the fast-mode launch model: 1 a 3x3 window at
-// stride 1, 4 a strided 3x3 window, 2 a 1x1 window read in place (stride 1,
-// no padding), 3 any other window or a strided or padded 1x1 (gathered
-// taps); matrix products are family 0.
+// Family of a convolution in the launch model: 1 a 3x3 window at stride 1,
+// 4 a strided 3x3 window, 2 a 1x1 window read in place (stride 1, no
+// padding), 3 any other window or a strided or padded 1x1 (gathered taps).
 int fast_family(int64_t KH, int64_t KW, bool planes, int64_t strideH, int64_t strideW) {
   if (KH == 3 && KW == 3) return strideH == 1 && strideW == 1 ? 1 : 4;
   return planes ? 2 : 3;
+}
+// Family of a matrix product in the model of `mode`: 5 from 2^32
+// multiply-adds up in fast mode and 2^30 in exact mode (sizes where the
+// large tiles' time per block decides; one fit over all sizes overrated the
+// 64 x 64 tile there, and these bounds gave the least regret on the fitted
+// and held-out products), else 0.
+int product_family(int mode, const Shape &s) {
+  const double macs = (double)s.M * (double)s.N * (double)s.K;
+  return macs >= (mode == OG_MODE_EXACT ? 1073741824.0 : 4294967296.0) ? 5 : 0;
 }
 
 // Launch time models, t in microseconds.  Fast mode: t = (c * K / 1000 + d
@@ -99,115 +107,137 @@ int fast_family(int64_t KH, int64_t KW, bool planes, int64_t strideH, int64_t st
 // ceil(x)) with x = blocks / cap, bytes those of the operands and the result
 // each counted once, X (halo kernel only) the thousands of input floats a
 // block stages over its k; (q, cap, c, d, o, b, e) per variant and family
-// (fast_family), cap a multiple of 256 blocks (one or more per compute
-// unit), fitted by least squares on the relative error to 401 shapes, each
-// launched on every variant on the MI355X (ResNet-50's convolutions at
-// batch 1, 2, 3, 4, 5, 6, 8, 12 and 16, MobileNetV3-large's ungrouped ones
-// at batch 1, 2, 4, 6 and 8, twelve 3x3 convolutions of other widths, 72
-// seeded random matrix products): mean error 4.5 % (exact 4.3 %).  Variants 26..28 are the
-// halo kernel, 29 and 30 the panel kernel.
+// (fast_family, product_family), cap a multiple of 256 blocks (one or more
+// per compute unit), fitted by least squares on the relative error to 437
+// shapes, each launched on every variant on the MI355X (ResNet-50's
+// convolutions at batch 1, 2, 3, 4, 5, 6, 8, 12 and 16, MobileNetV3-large's
+// ungrouped ones at batch 1, 2, 4, 6 and 8, twelve 3x3 convolutions of other
+// widths, 72 seeded random matrix products up to 2048 x 2900 x 2300, and 36
+// products of a language model's sizes: 4096^3, 512 x 11008 x 4096,
+// 1 x 4096 x 4096 and 33 seeded ones of m = 1..4096, n = 1024..11008,
+// k = 1024..8192): mean error 4.1 % (exact 4.9 %).  Variants 26..28 and
+// 31..33 are the halo kernel, 29 and 30 the panel kernel.
 struct ModelCost {
   int variant, fam;
   double q, cap, c, d, o, b, e;
 };
 constexpr ModelCost kFastCosts[] = {
-    {2, 0, 0, 256, 132.150, 9.037, 0.000, 0.0790, 0.0000},
+    {2, 0, 0, 256, 130.323, 9.416, 0.000, 0.0239, 0.0000},
     {2, 1, 0, 256, 200.488, 0.000, 9.607, 0.0977, 0.0000},
     {2, 2, 0.75, 256, 135.149, 0.000, 8.754, 0.0683, 0.0000},
     {2, 3, 0.75, 256, 191.331, 4.963, 9.518, 0.0000, 0.0000},
     {2, 4, 1, 256, 198.851, 0.829, 9.278, 0.0386, 0.0000},
-    {3, 0, 0.75, 256, 71.315, 5.603, 0.000, 0.0910, 0.0000},
+    {2, 5, 0.75, 256, 128.304, 2.595, 17.525, 0.0000, 0.0000},
+    {3, 0, 0, 256, 70.055, 5.914, 0.000, 0.0390, 0.0000},
     {3, 1, 0.5, 256, 106.661, 1.239, 5.154, 0.0499, 0.0000},
     {3, 2, 0.75, 256, 74.927, 0.448, 5.102, 0.0654, 0.0000},
     {3, 3, 0.75, 256, 103.345, 0.178, 8.299, 0.0000, 0.0000},
     {3, 4, 0.25, 256, 106.345, 2.227, 3.966, 0.0247, 0.0000},
-    {4, 0, 0.25, 256, 39.923, 2.435, 1.643, 0.0526, 0.0000},
+    {3, 5, 0.75, 256, 67.837, 0.000, 11.640, 0.0000, 0.0000},
+    {4, 0, 0.5, 256, 39.546, 2.475, 1.766, 0.0000, 0.0000},
     {4, 1, 0.5, 256, 76.180, 0.000, 5.792, 0.0000, 0.0000},
     {4, 2, 0.5, 256, 44.865, 0.483, 3.795, 0.0623, 0.0000},
     {4, 3, 0.5, 256, 72.451, 0.000, 7.765, 0.0000, 0.0000},
     {4, 4, 0.75, 256, 76.090, 0.714, 4.108, 0.0483, 0.0000},
-    {5, 0, 0.25, 256, 46.179, 2.100, 2.042, 0.0183, 0.0000},
+    {4, 5, 0.5, 256, 34.477, 0.000, 12.049, 0.1135, 0.0000},
+    {5, 0, 0.25, 256, 45.745, 2.829, 1.379, 0.0000, 0.0000},
     {5, 1, 0.5, 256, 117.752, 0.000, 5.240, 0.0000, 0.0000},
     {5, 2, 0.5, 256, 54.768, 0.387, 3.801, 0.0375, 0.0000},
     {5, 3, 0.5, 256, 107.044, 0.000, 8.889, 0.0000, 0.0000},
     {5, 4, 0.75, 256, 116.785, 1.327, 4.345, 0.0067, 0.0000},
-    {6, 0, 0.5, 768, 14.608, 0.242, 2.335, 0.8409, 0.0000},
+    {5, 5, 0.5, 256, 36.621, 0.000, 10.466, 0.1963, 0.0000},
+    {6, 0, 0.75, 768, 15.713, 0.884, 1.995, 0.0458, 0.0000},
     {6, 1, 0.75, 768, 16.692, 0.000, 1.079, 0.0000, 0.0000},
     {6, 2, 0.5, 768, 14.497, 0.741, 2.710, 0.1789, 0.0000},
     {6, 3, 0.25, 768, 20.135, 4.491, 2.202, 0.0000, 0.0000},
     {6, 4, 0.5, 512, 17.816, 0.000, 3.089, 0.5236, 0.0000},
-    {7, 0, 0.5, 768, 17.177, 0.117, 2.491, 0.5768, 0.0000},
+    {6, 5, 0.25, 1536, 31.162, 0.200, 0.309, 0.1142, 0.0000},
+    {7, 0, 0.75, 768, 18.099, 0.981, 1.964, 0.0518, 0.0000},
     {7, 1, 0.5, 768, 19.233, 0.000, 3.427, 0.0000, 0.0000},
     {7, 2, 0.5, 768, 17.275, 0.730, 2.542, 0.1325, 0.0000},
     {7, 3, 0.5, 512, 15.281, 2.631, 5.843, 0.0000, 0.0000},
     {7, 4, 0.75, 512, 20.614, 0.000, 3.038, 0.2773, 0.0000},
-    {8, 0, 0.25, 512, 21.492, 0.000, 2.990, 0.3116, 0.0000},
+    {7, 5, 0.25, 768, 18.305, 0.000, 2.165, 0.1467, 0.0000},
+    {8, 0, 0.5, 512, 22.278, 0.478, 2.801, 0.0205, 0.0000},
     {8, 1, 0.25, 512, 23.173, 0.000, 4.585, 0.0000, 0.0000},
     {8, 2, 0.75, 768, 23.794, 0.559, 2.533, 0.1622, 0.0000},
     {8, 3, 0.75, 512, 20.253, 2.175, 5.834, 0.0000, 0.0000},
     {8, 4, 0.5, 512, 26.950, 0.000, 3.092, 0.1817, 0.0000},
-    {9, 0, 1, 512, 31.340, 0.000, 3.312, 0.3016, 0.0000},
+    {8, 5, 0.25, 768, 27.693, 0.000, 3.876, 0.0769, 0.0000},
+    {9, 0, 1, 512, 31.443, 0.555, 3.053, 0.1385, 0.0000},
     {9, 1, 0, 2048, 29.070, 0.000, 0.000, 2.2430, 0.0000},
     {9, 2, 0.25, 512, 32.850, 0.000, 3.493, 0.1880, 0.0000},
     {9, 3, 0.5, 512, 32.239, 2.823, 4.915, 0.0000, 0.0000},
     {9, 4, 1, 512, 33.842, 0.000, 3.167, 0.3262, 0.0000},
-    {10, 0, 1, 256, 5.957, 3.489, 1.632, 0.0000, 0.0000},
+    {9, 5, 0.25, 768, 46.021, 1.159, 16.829, 0.0000, 0.0000},
+    {10, 0, 1, 256, 6.029, 3.464, 1.564, 0.0388, 0.0000},
     {10, 1, 1, 256, 4.901, 3.893, 1.728, 0.0000, 0.0000},
     {10, 2, 1, 256, 5.242, 3.517, 1.783, 0.0000, 0.0000},
     {10, 3, 0.5, 512, 15.291, 13.569, 0.000, 0.4646, 0.0000},
     {10, 4, 1, 256, 3.995, 5.910, 1.106, 0.2118, 0.0000},
-    {11, 0, 1, 256, 5.058, 2.842, 1.530, 0.0000, 0.0000},
+    {10, 5, 0.75, 512, 13.361, 5.341, 0.000, 0.0877, 0.0000},
+    {11, 0, 1, 256, 5.120, 2.830, 1.475, 0.0196, 0.0000},
     {11, 1, 1, 256, 4.670, 3.157, 1.395, 0.0388, 0.0000},
     {11, 2, 1, 256, 4.418, 3.151, 1.633, 0.0748, 0.0000},
     {11, 3, 0.25, 1024, 25.793, 26.188, 0.000, 0.6820, 0.0000},
     {11, 4, 0.25, 256, 4.151, 4.723, 2.500, 0.0000, 0.0000},
-    {12, 0, 0.5, 512, 3.208, 1.246, 3.032, 0.4526, 0.0000},
+    {11, 5, 1, 1024, 21.637, 9.818, 0.000, 0.0945, 0.0000},
+    {12, 0, 1, 512, 3.361, 1.286, 2.651, 0.0427, 0.0000},
     {12, 1, 1, 256, 2.418, 1.180, 3.373, 0.2280, 0.0000},
     {12, 2, 0.25, 512, 3.202, 1.303, 3.748, 0.0000, 0.0000},
     {12, 3, 0.25, 2048, 19.515, 11.629, 3.561, 0.0000, 0.0000},
     {12, 4, 0, 256, 2.172, 1.702, 5.833, 0.0851, 0.0000},
-    {13, 0, 1, 256, 6.535, 3.427, 1.654, 0.0000, 0.0000},
+    {12, 5, 1, 2048, 12.993, 4.877, 0.000, 0.2869, 0.0000},
+    {13, 0, 1, 256, 6.537, 3.431, 1.563, 0.0122, 0.0000},
     {13, 1, 1, 256, 6.099, 3.497, 1.653, 0.0184, 0.0000},
     {13, 2, 1, 256, 6.283, 3.381, 1.657, 0.0000, 0.0000},
     {13, 3, 0.25, 512, 13.675, 13.472, 0.000, 0.3762, 0.0000},
     {13, 4, 0.75, 256, 4.884, 5.693, 2.003, 0.2918, 0.0000},
-    {14, 0, 0.75, 256, 9.352, 5.193, 1.938, 0.1295, 0.0000},
+    {13, 5, 0.5, 512, 13.553, 5.992, 2.127, 0.0387, 0.0000},
+    {14, 0, 1, 256, 9.051, 5.091, 2.106, 0.0000, 0.0000},
     {14, 1, 1, 256, 9.956, 5.491, 1.711, 0.0059, 0.0000},
     {14, 2, 1, 256, 7.045, 4.813, 1.979, 0.0000, 0.0000},
     {14, 3, 1, 256, 9.661, 7.993, 1.251, 0.1966, 0.0000},
     {14, 4, 0.5, 256, 7.366, 12.874, 1.225, 0.0000, 0.0000},
-    {15, 0, 0.75, 256, 10.260, 5.226, 1.886, 0.0770, 0.0000},
+    {14, 5, 0.5, 512, 17.904, 8.537, 9.580, 0.0000, 0.0000},
+    {15, 0, 1, 256, 9.844, 5.089, 2.029, 0.0000, 0.0000},
     {15, 1, 1, 256, 10.682, 4.264, 1.699, 0.0083, 0.0000},
     {15, 2, 1, 256, 8.417, 4.706, 1.838, 0.0000, 0.0000},
     {15, 3, 1, 256, 9.672, 7.894, 1.268, 0.1412, 0.0000},
     {15, 4, 0.5, 256, 7.929, 11.879, 1.208, 0.0000, 0.0000},
-    {16, 0, 1, 256, 7.681, 4.247, 1.716, 0.0000, 0.0000},
+    {15, 5, 0.5, 512, 19.903, 8.240, 7.554, 0.0000, 0.0000},
+    {16, 0, 1, 256, 7.558, 4.265, 1.610, 0.0101, 0.0000},
     {16, 1, 1, 256, 8.624, 3.982, 1.709, 0.0000, 0.0000},
     {16, 2, 1, 256, 6.525, 4.078, 1.922, 0.0000, 0.0000},
     {16, 3, 0.75, 256, 7.535, 7.375, 0.000, 0.2893, 0.0000},
     {16, 4, 0.75, 256, 6.736, 7.941, 1.861, 0.1315, 0.0000},
-    {17, 0, 0, 256, 236.744, 9.817, 0.000, 0.1532, 0.0000},
+    {16, 5, 0.25, 1024, 31.425, 14.504, 6.658, 0.0101, 0.0000},
+    {17, 0, 0, 256, 234.886, 10.173, 0.000, 0.1016, 0.0000},
     {17, 1, 0, 256, 289.559, 0.000, 10.965, 0.1087, 0.0000},
     {17, 2, 0.5, 256, 238.070, 9.250, 0.336, 0.0620, 0.0000},
     {17, 3, 1, 256, 282.211, 15.870, 0.221, 0.0000, 0.0000},
     {17, 4, 1, 256, 289.389, 8.416, 1.934, 0.0936, 0.0000},
-    {20, 0, 1, 512, 29.176, 0.000, 3.255, 0.2359, 0.0000},
+    {17, 5, 1, 256, 235.543, 2.906, 3.549, 0.1560, 0.0000},
+    {20, 0, 0.5, 256, 27.886, 0.000, 3.846, 0.0000, 0.0000},
     {20, 1, 0.25, 256, 45.603, 0.000, 5.908, 0.0000, 0.0000},
     {20, 2, 0.25, 256, 28.724, 0.412, 4.546, 0.0276, 0.0000},
     {20, 3, 0.5, 256, 36.809, 0.000, 8.740, 0.0000, 0.0000},
     {20, 4, 0.25, 256, 46.385, 0.497, 4.725, 0.0000, 0.0000},
+    {20, 5, 0, 256, 18.735, 0.000, 19.760, 0.1959, 0.0000},
     {26, 1, 1, 256, 3.851, 0.000, 5.334, 0.9905, 0.0996},
     {26, 4, 1, 256, 4.864, 2.845, 3.406, 0.3862, 0.0789},
     {27, 1, 0.5, 256, 6.921, 1.587, 3.198, 0.4847, 0.1870},
     {27, 4, 1, 256, 9.054, 4.701, 2.449, 0.1241, 0.0583},
     {28, 1, 1, 256, 9.804, 3.408, 1.789, 0.1367, 0.1023},
     {28, 4, 1, 256, 11.834, 5.310, 2.876, 0.3160, 0.0204},
-    {29, 0, 0.25, 256, 9.776, 0.493, 3.298, 0.1214, 0.0000},
+    {29, 0, 0.25, 256, 9.927, 0.600, 3.310, 0.0004, 0.0000},
     {29, 2, 0.5, 256, 8.419, 1.002, 3.144, 0.0000, 0.0000},
     {29, 3, 0.75, 256, 9.878, 1.438, 4.119, 0.3371, 0.0000},
-    {30, 0, 0.25, 256, 15.907, 0.442, 3.476, 0.0498, 0.0000},
+    {29, 5, 0, 768, 21.665, 2.872, 15.191, 0.0000, 0.0000},
+    {30, 0, 0.25, 256, 15.926, 0.543, 3.436, 0.0000, 0.0000},
     {30, 2, 0.25, 256, 14.384, 1.044, 3.014, 0.0000, 0.0000},
     {30, 3, 0.75, 256, 13.387, 0.000, 4.620, 0.3017, 0.0000},
+    {30, 5, 0.25, 256, 11.824, 0.674, 13.275, 0.0178, 0.0000},
     {31, 1, 0.75, 256, 1.398, 1.006, 5.167, 1.3164, 0.0990},
     {31, 4, 1, 256, 1.436, 2.956, 0.011, 2.2745, 0.0854},
     {32, 1, 1, 256, 5.531, 3.008, 1.193, 0.3708, 0.1009},
@@ -220,76 +250,90 @@ constexpr ModelCost kFastCosts[] = {
 // shapes launched in exact mode (variants 14..16 run as 10, 13 and 11 there;
 // the panel kernel has no exact form).
 constexpr ModelCost kExactCosts[] = {
-    {2, 0, 0, 256, 101.213, 5.867, 0.000, 0.3088, 0.0000},
+    {2, 0, 0, 256, 99.073, 6.610, 0.000, 0.1468, 0.0000},
     {2, 1, 0, 256, 235.881, 0.000, 0.000, 1.6945, 0.0000},
     {2, 2, 1, 256, 104.747, 0.000, 4.018, 0.2369, 0.0000},
     {2, 3, 1, 256, 218.297, 14.892, 0.000, 0.1956, 0.0000},
     {2, 4, 0.75, 256, 234.074, 6.003, 0.000, 0.6898, 0.0000},
-    {3, 0, 1, 256, 101.045, 6.017, 0.000, 0.2697, 0.0000},
+    {2, 5, 1, 256, 98.477, 0.899, 0.000, 0.9550, 0.0000},
+    {3, 0, 0, 256, 99.082, 6.605, 0.000, 0.1482, 0.0000},
     {3, 1, 0, 256, 237.329, 0.000, 7.556, 0.0000, 0.0000},
     {3, 2, 1, 256, 104.433, 0.000, 4.625, 0.0646, 0.0000},
     {3, 3, 0, 256, 227.422, 0.000, 10.802, 0.0000, 0.0000},
     {3, 4, 0, 256, 237.574, 2.833, 4.089, 0.0000, 0.0000},
-    {4, 0, 0, 256, 99.514, 0.000, 6.835, 0.0000, 0.0000},
+    {3, 5, 1, 256, 110.687, 4.624, 0.000, 0.0000, 0.0000},
+    {4, 0, 0, 256, 100.336, 0.998, 5.696, 0.0000, 0.0000},
     {4, 1, 0, 256, 151.018, 0.000, 6.039, 0.0000, 0.0000},
     {4, 2, 0, 256, 103.386, 0.000, 4.837, 0.0349, 0.0000},
     {4, 3, 0.5, 512, 141.624, 2.887, 5.247, 0.3364, 0.0000},
     {4, 4, 0, 256, 151.080, 0.736, 4.422, 0.0532, 0.0000},
-    {5, 0, 1, 512, 109.297, 0.000, 6.162, 0.2407, 0.0000},
+    {4, 5, 0, 256, 62.170, 0.000, 31.153, 0.7418, 0.0000},
+    {5, 0, 0, 256, 108.455, 0.177, 6.583, 0.0000, 0.0000},
     {5, 1, 0, 512, 216.461, 0.000, 1.328, 0.8328, 0.0000},
     {5, 2, 1, 512, 118.186, 0.028, 4.241, 0.1464, 0.0000},
     {5, 3, 0.25, 512, 203.916, 0.489, 10.213, 0.2272, 0.0000},
     {5, 4, 0.5, 256, 215.736, 0.000, 6.273, 0.0000, 0.0000},
-    {6, 0, 0.5, 768, 15.469, 0.083, 2.504, 0.7430, 0.0000},
+    {5, 5, 0.75, 512, 121.189, 1.093, 0.000, 0.0000, 0.0000},
+    {6, 0, 0.75, 768, 16.610, 0.655, 2.163, 0.0335, 0.0000},
     {6, 1, 0.25, 768, 19.610, 0.000, 4.462, 0.0000, 0.0000},
     {6, 2, 0.5, 768, 14.674, 0.586, 2.825, 0.1742, 0.0000},
     {6, 3, 0.5, 768, 20.707, 4.075, 1.083, 0.0000, 0.0000},
     {6, 4, 0.5, 512, 18.571, 0.000, 2.904, 0.6610, 0.0000},
-    {7, 0, 0.5, 768, 20.004, 0.000, 2.505, 0.4969, 0.0000},
+    {6, 5, 0.25, 1536, 32.567, 0.250, 3.386, 0.1161, 0.0000},
+    {7, 0, 0.5, 512, 19.645, 0.011, 2.869, 0.0217, 0.0000},
     {7, 1, 0.5, 768, 22.475, 0.000, 4.213, 0.0000, 0.0000},
     {7, 2, 0.5, 768, 20.429, 0.557, 2.781, 0.1081, 0.0000},
     {7, 3, 0.25, 512, 15.714, 2.626, 6.937, 0.0000, 0.0000},
     {7, 4, 0.25, 512, 23.841, 0.000, 3.332, 0.2151, 0.0000},
-    {8, 0, 0.5, 512, 30.410, 0.000, 3.035, 0.1666, 0.0000},
+    {7, 5, 0.25, 768, 22.054, 0.000, 4.938, 0.1787, 0.0000},
+    {8, 0, 0.5, 512, 31.513, 0.180, 2.950, 0.0048, 0.0000},
     {8, 1, 0.5, 512, 31.168, 0.000, 5.015, 0.0000, 0.0000},
     {8, 2, 0.75, 768, 32.286, 0.373, 2.846, 0.1809, 0.0000},
     {8, 3, 0.5, 768, 31.659, 6.956, 0.922, 0.0000, 0.0000},
     {8, 4, 0.5, 512, 34.199, 0.000, 3.295, 0.1827, 0.0000},
-    {9, 0, 1, 512, 51.502, 0.000, 3.381, 0.2339, 0.0000},
+    {8, 5, 0.25, 768, 37.529, 0.271, 7.665, 0.1582, 0.0000},
+    {9, 0, 0.5, 512, 51.108, 0.531, 3.148, 0.1163, 0.0000},
     {9, 1, 0.25, 512, 52.140, 0.000, 4.045, 0.7324, 0.0000},
     {9, 2, 0.25, 512, 51.023, 0.269, 3.673, 0.1550, 0.0000},
     {9, 3, 0, 512, 39.133, 9.928, 3.916, 0.0000, 0.0000},
     {9, 4, 0.5, 512, 54.581, 0.000, 3.270, 0.3806, 0.0000},
-    {10, 0, 1, 256, 7.285, 3.324, 1.735, 0.0000, 0.0000},
+    {9, 5, 0.25, 512, 46.904, 0.000, 19.598, 0.2909, 0.0000},
+    {10, 0, 1, 256, 7.233, 3.293, 1.738, 0.0183, 0.0000},
     {10, 1, 1, 256, 5.908, 3.806, 1.812, 0.0693, 0.0000},
     {10, 2, 1, 256, 6.559, 3.584, 1.781, 0.0000, 0.0000},
     {10, 3, 0.5, 512, 15.522, 13.777, 0.000, 0.4231, 0.0000},
     {10, 4, 0.75, 256, 5.230, 5.068, 2.269, 0.1950, 0.0000},
-    {11, 0, 1, 256, 6.521, 2.895, 1.708, 0.0000, 0.0000},
+    {10, 5, 1, 256, 7.269, 3.744, 0.000, 0.0607, 0.0000},
+    {11, 0, 1, 256, 6.495, 2.881, 1.683, 0.0128, 0.0000},
     {11, 1, 1, 256, 5.729, 3.097, 1.304, 0.0581, 0.0000},
     {11, 2, 1, 256, 5.866, 3.245, 1.705, 0.0724, 0.0000},
     {11, 3, 0.25, 1024, 25.921, 26.732, 0.000, 0.5407, 0.0000},
     {11, 4, 0.5, 256, 5.239, 4.136, 2.964, 0.0246, 0.0000},
-    {12, 0, 0.25, 512, 3.835, 1.173, 3.536, 0.6924, 0.0000},
+    {11, 5, 0.5, 512, 12.929, 6.224, 1.801, 0.1119, 0.0000},
+    {12, 0, 0.75, 512, 4.157, 1.237, 3.162, 0.0632, 0.0000},
     {12, 1, 1, 256, 3.152, 1.188, 3.755, 0.0733, 0.0000},
     {12, 2, 0.25, 512, 3.691, 1.351, 3.962, 0.0759, 0.0000},
     {12, 3, 0.25, 1024, 9.803, 5.836, 5.034, 0.0000, 0.0000},
     {12, 4, 0.5, 256, 2.971, 1.611, 4.888, 0.0190, 0.0000},
-    {13, 0, 1, 256, 9.622, 3.339, 1.801, 0.0000, 0.0000},
+    {12, 5, 0.5, 1024, 7.651, 2.296, 12.358, 0.0753, 0.0000},
+    {13, 0, 1, 256, 9.516, 3.329, 1.788, 0.0033, 0.0000},
     {13, 1, 1, 256, 9.141, 3.439, 1.583, 0.0192, 0.0000},
     {13, 2, 1, 256, 8.833, 3.567, 1.709, 0.0000, 0.0000},
     {13, 3, 0.25, 512, 16.051, 13.456, 0.000, 0.3438, 0.0000},
     {13, 4, 0.75, 256, 8.159, 5.185, 2.304, 0.2008, 0.0000},
-    {17, 0, 0, 256, 101.175, 5.864, 0.000, 0.3118, 0.0000},
+    {13, 5, 0.75, 256, 9.302, 3.901, 5.738, 0.0518, 0.0000},
+    {17, 0, 0, 256, 99.039, 6.607, 0.000, 0.1497, 0.0000},
     {17, 1, 0, 256, 235.908, 0.000, 0.000, 1.6983, 0.0000},
     {17, 2, 0.25, 256, 104.334, 0.000, 3.960, 0.2632, 0.0000},
     {17, 3, 1, 256, 218.246, 14.904, 0.000, 0.1962, 0.0000},
     {17, 4, 0.75, 256, 234.144, 6.004, 0.000, 0.6884, 0.0000},
-    {20, 0, 1, 512, 58.722, 0.000, 3.245, 0.2239, 0.0000},
+    {17, 5, 1, 256, 68.173, 8.685, 0.000, 1.9127, 0.0000},
+    {20, 0, 0, 256, 58.360, 0.000, 3.513, 0.0000, 0.0000},
     {20, 1, 0.25, 512, 92.985, 0.000, 2.441, 0.9360, 0.0000},
     {20, 2, 1, 512, 58.484, 0.412, 4.382, 0.1826, 0.0000},
     {20, 3, 0.5, 512, 90.270, 0.106, 8.587, 0.0740, 0.0000},
     {20, 4, 0.75, 768, 91.113, 0.549, 3.833, 0.7017, 0.0000},
+    {20, 5, 0.5, 512, 63.415, 3.964, 7.301, 0.0000, 0.0000},
     {26, 1, 1, 512, 12.688, 0.000, 3.411, 1.3181, 0.2810},
     {26, 4, 1, 256, 8.422, 0.000, 7.430, 1.5041, 0.1361},
     {27, 1, 0.25, 256, 24.060, 0.000, 6.895, 1.1480, 0.1870},
@@ -317,9 +361,10 @@ int64_t launch_blocks(const Tile &t, const Shape &s) {
 // (mode 2 uses the fast one); 1e300 where the variant has no entry for the
 // shape's family.
 double model_estimate(int mode, int variant, const Shape &s, int64_t blocks) {
+  const int fam = s.khw == 0 ? product_family(mode, s) : s.ffam;
   auto scan = [&](const auto &table) {
     for (const ModelCost &c : table) {
-      if (c.variant != variant || c.fam != s.ffam) continue;
+      if (c.variant != variant || c.fam != fam) continue;
       const double k = (double)(s.K > 0 ? s.K : 1);
       const double x = (double)blocks / c.cap;
       const double rounds = std::max(1.0, (1.0 - c.q) * x + c.q * std::ceil(x));
