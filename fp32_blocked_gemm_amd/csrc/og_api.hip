@@ -92,14 +92,11 @@ int fast_family(int64_t KH, int64_t KW, bool planes, int64_t strideH, int64_t st
   if (KH == 3 && KW == 3) return strideH == 1 && strideW == 1 ? 1 : 4;
   return planes ? 2 : 3;
 }
-// Family of a matrix product in the model of `mode`: 5 from 2^32
-// multiply-adds up in fast mode and 2^30 in exact mode (sizes where the
+// Family of a matrix product: 5 from 2^32 multiply-adds up (sizes where the
 // large tiles' time per block decides; one fit over all sizes overrated the
-// 64 x 64 tile there, and these bounds gave the least regret on the fitted
-// and held-out products), else 0.
-int product_family(int mode, const Shape &s) {
-  const double macs = (double)s.M * (double)s.N * (double)s.K;
-  return macs >= (mode == OG_MODE_EXACT ? 1073741824.0 : 4294967296.0) ? 5 : 0;
+// 64 x 64 tile there), else 0.
+int product_family(const Shape &s) {
+  return (double)s.M * (double)s.N * (double)s.K >= 4294967296.0 ? 5 : 0;
 }
 
 // Launch time models, t in microseconds.  Fast mode: t = (c * K / 1000 + d
@@ -115,7 +112,7 @@ int product_family(int mode, const Shape &s) {
 // widths, 72 seeded random matrix products up to 2048 x 2900 x 2300, and 36
 // products of a language model's sizes: 4096^3, 512 x 11008 x 4096,
 // 1 x 4096 x 4096 and 33 seeded ones of m = 1..4096, n = 1024..11008,
-// k = 1024..8192): mean error 4.1 % (exact 4.9 %).  Variants 26..28 and
+// k = 1024..8192): mean error 4.1 % (exact 3.8 %).  Variants 26..28 and
 // 31..33 are the halo kernel, 29 and 30 the panel kernel.
 struct ModelCost {
   int variant, fam;
@@ -247,93 +244,89 @@ constexpr ModelCost kFastCosts[] = {
 };
 
 // Exact mode: the same form and families, fitted the same way to the same
-// shapes launched in exact mode (variants 14..16 run as 10, 13 and 11 there;
-// the panel kernel has no exact form).
+// shapes launched in exact mode (variants 14..16 run as 10, 13 and 11 there,
+// and 2, 3 and 17 on the 64 x 128 or 128 x 128 tile, whose blocks their
+// entries count; the panel kernel has no exact form; variant 9, whose eight
+// rows per lane are VALU-bound in exact mode, is left out of the choice).
 constexpr ModelCost kExactCosts[] = {
-    {2, 0, 0, 256, 99.073, 6.610, 0.000, 0.1468, 0.0000},
-    {2, 1, 0, 256, 235.881, 0.000, 0.000, 1.6945, 0.0000},
-    {2, 2, 1, 256, 104.747, 0.000, 4.018, 0.2369, 0.0000},
-    {2, 3, 1, 256, 218.297, 14.892, 0.000, 0.1956, 0.0000},
-    {2, 4, 0.75, 256, 234.074, 6.003, 0.000, 0.6898, 0.0000},
-    {2, 5, 1, 256, 98.477, 0.899, 0.000, 0.9550, 0.0000},
-    {3, 0, 0, 256, 99.082, 6.605, 0.000, 0.1482, 0.0000},
+    {2, 0, 0, 256, 100.157, 0.605, 6.110, 0.0000, 0.0000},
+    {2, 1, 0, 256, 237.327, 0.000, 7.563, 0.0000, 0.0000},
+    {2, 2, 0, 256, 103.383, 0.000, 4.836, 0.0342, 0.0000},
+    {2, 3, 0, 256, 227.415, 0.000, 10.788, 0.0000, 0.0000},
+    {2, 4, 0, 256, 237.609, 2.834, 4.086, 0.0000, 0.0000},
+    {2, 5, 0, 256, 58.375, 0.000, 30.472, 0.9348, 0.0000},
+    {3, 0, 0, 256, 100.177, 0.624, 6.090, 0.0000, 0.0000},
     {3, 1, 0, 256, 237.329, 0.000, 7.556, 0.0000, 0.0000},
-    {3, 2, 1, 256, 104.433, 0.000, 4.625, 0.0646, 0.0000},
+    {3, 2, 0, 256, 103.364, 0.000, 4.839, 0.0350, 0.0000},
     {3, 3, 0, 256, 227.422, 0.000, 10.802, 0.0000, 0.0000},
     {3, 4, 0, 256, 237.574, 2.833, 4.089, 0.0000, 0.0000},
-    {3, 5, 1, 256, 110.687, 4.624, 0.000, 0.0000, 0.0000},
-    {4, 0, 0, 256, 100.336, 0.998, 5.696, 0.0000, 0.0000},
+    {3, 5, 0, 256, 58.559, 0.000, 29.973, 0.9301, 0.0000},
+    {4, 0, 0, 256, 100.175, 0.598, 6.125, 0.0000, 0.0000},
     {4, 1, 0, 256, 151.018, 0.000, 6.039, 0.0000, 0.0000},
     {4, 2, 0, 256, 103.386, 0.000, 4.837, 0.0349, 0.0000},
     {4, 3, 0.5, 512, 141.624, 2.887, 5.247, 0.3364, 0.0000},
     {4, 4, 0, 256, 151.080, 0.736, 4.422, 0.0532, 0.0000},
-    {4, 5, 0, 256, 62.170, 0.000, 31.153, 0.7418, 0.0000},
-    {5, 0, 0, 256, 108.455, 0.177, 6.583, 0.0000, 0.0000},
+    {4, 5, 0, 256, 58.658, 0.000, 29.888, 0.9283, 0.0000},
+    {5, 0, 0, 256, 108.137, 0.000, 6.790, 0.0000, 0.0000},
     {5, 1, 0, 512, 216.461, 0.000, 1.328, 0.8328, 0.0000},
     {5, 2, 1, 512, 118.186, 0.028, 4.241, 0.1464, 0.0000},
     {5, 3, 0.25, 512, 203.916, 0.489, 10.213, 0.2272, 0.0000},
     {5, 4, 0.5, 256, 215.736, 0.000, 6.273, 0.0000, 0.0000},
-    {5, 5, 0.75, 512, 121.189, 1.093, 0.000, 0.0000, 0.0000},
-    {6, 0, 0.75, 768, 16.610, 0.655, 2.163, 0.0335, 0.0000},
+    {5, 5, 0, 256, 63.828, 0.000, 0.000, 1.1038, 0.0000},
+    {6, 0, 0.75, 768, 16.419, 0.645, 2.214, 0.0419, 0.0000},
     {6, 1, 0.25, 768, 19.610, 0.000, 4.462, 0.0000, 0.0000},
     {6, 2, 0.5, 768, 14.674, 0.586, 2.825, 0.1742, 0.0000},
     {6, 3, 0.5, 768, 20.707, 4.075, 1.083, 0.0000, 0.0000},
     {6, 4, 0.5, 512, 18.571, 0.000, 2.904, 0.6610, 0.0000},
-    {6, 5, 0.25, 1536, 32.567, 0.250, 3.386, 0.1161, 0.0000},
-    {7, 0, 0.5, 512, 19.645, 0.011, 2.869, 0.0217, 0.0000},
+    {6, 5, 0.25, 1536, 32.813, 0.003, 0.000, 0.1111, 0.0000},
+    {7, 0, 0.75, 768, 20.607, 0.714, 2.117, 0.0372, 0.0000},
     {7, 1, 0.5, 768, 22.475, 0.000, 4.213, 0.0000, 0.0000},
     {7, 2, 0.5, 768, 20.429, 0.557, 2.781, 0.1081, 0.0000},
     {7, 3, 0.25, 512, 15.714, 2.626, 6.937, 0.0000, 0.0000},
     {7, 4, 0.25, 512, 23.841, 0.000, 3.332, 0.2151, 0.0000},
-    {7, 5, 0.25, 768, 22.054, 0.000, 4.938, 0.1787, 0.0000},
-    {8, 0, 0.5, 512, 31.513, 0.180, 2.950, 0.0048, 0.0000},
+    {7, 5, 0.5, 768, 22.349, 0.000, 0.000, 0.0533, 0.0000},
+    {8, 0, 0.5, 512, 31.006, 0.120, 3.090, 0.0111, 0.0000},
     {8, 1, 0.5, 512, 31.168, 0.000, 5.015, 0.0000, 0.0000},
     {8, 2, 0.75, 768, 32.286, 0.373, 2.846, 0.1809, 0.0000},
     {8, 3, 0.5, 768, 31.659, 6.956, 0.922, 0.0000, 0.0000},
     {8, 4, 0.5, 512, 34.199, 0.000, 3.295, 0.1827, 0.0000},
-    {8, 5, 0.25, 768, 37.529, 0.271, 7.665, 0.1582, 0.0000},
-    {9, 0, 0.5, 512, 51.108, 0.531, 3.148, 0.1163, 0.0000},
-    {9, 1, 0.25, 512, 52.140, 0.000, 4.045, 0.7324, 0.0000},
-    {9, 2, 0.25, 512, 51.023, 0.269, 3.673, 0.1550, 0.0000},
-    {9, 3, 0, 512, 39.133, 9.928, 3.916, 0.0000, 0.0000},
-    {9, 4, 0.5, 512, 54.581, 0.000, 3.270, 0.3806, 0.0000},
-    {9, 5, 0.25, 512, 46.904, 0.000, 19.598, 0.2909, 0.0000},
-    {10, 0, 1, 256, 7.233, 3.293, 1.738, 0.0183, 0.0000},
+    {8, 5, 0.25, 768, 38.080, 0.000, 1.375, 0.1186, 0.0000},
+    {10, 0, 1, 256, 7.301, 3.324, 1.656, 0.0150, 0.0000},
     {10, 1, 1, 256, 5.908, 3.806, 1.812, 0.0693, 0.0000},
     {10, 2, 1, 256, 6.559, 3.584, 1.781, 0.0000, 0.0000},
     {10, 3, 0.5, 512, 15.522, 13.777, 0.000, 0.4231, 0.0000},
     {10, 4, 0.75, 256, 5.230, 5.068, 2.269, 0.1950, 0.0000},
-    {10, 5, 1, 256, 7.269, 3.744, 0.000, 0.0607, 0.0000},
-    {11, 0, 1, 256, 6.495, 2.881, 1.683, 0.0128, 0.0000},
+    {10, 5, 0.5, 1024, 29.988, 11.778, 0.000, 0.0617, 0.0000},
+    {11, 0, 1, 256, 6.524, 2.895, 1.634, 0.0114, 0.0000},
     {11, 1, 1, 256, 5.729, 3.097, 1.304, 0.0581, 0.0000},
     {11, 2, 1, 256, 5.866, 3.245, 1.705, 0.0724, 0.0000},
     {11, 3, 0.25, 1024, 25.921, 26.732, 0.000, 0.5407, 0.0000},
     {11, 4, 0.5, 256, 5.239, 4.136, 2.964, 0.0246, 0.0000},
-    {11, 5, 0.5, 512, 12.929, 6.224, 1.801, 0.1119, 0.0000},
-    {12, 0, 0.75, 512, 4.157, 1.237, 3.162, 0.0632, 0.0000},
+    {11, 5, 0.25, 2048, 52.987, 20.691, 0.000, 0.1080, 0.0000},
+    {12, 0, 0.75, 512, 4.088, 1.238, 3.219, 0.0669, 0.0000},
     {12, 1, 1, 256, 3.152, 1.188, 3.755, 0.0733, 0.0000},
     {12, 2, 0.25, 512, 3.691, 1.351, 3.962, 0.0759, 0.0000},
     {12, 3, 0.25, 1024, 9.803, 5.836, 5.034, 0.0000, 0.0000},
     {12, 4, 0.5, 256, 2.971, 1.611, 4.888, 0.0190, 0.0000},
-    {12, 5, 0.5, 1024, 7.651, 2.296, 12.358, 0.0753, 0.0000},
-    {13, 0, 1, 256, 9.516, 3.329, 1.788, 0.0033, 0.0000},
+    {12, 5, 1, 1536, 11.528, 3.147, 0.000, 0.1019, 0.0000},
+    {13, 0, 1, 256, 9.581, 3.356, 1.719, 0.0000, 0.0000},
     {13, 1, 1, 256, 9.141, 3.439, 1.583, 0.0192, 0.0000},
     {13, 2, 1, 256, 8.833, 3.567, 1.709, 0.0000, 0.0000},
     {13, 3, 0.25, 512, 16.051, 13.456, 0.000, 0.3438, 0.0000},
     {13, 4, 0.75, 256, 8.159, 5.185, 2.304, 0.2008, 0.0000},
-    {13, 5, 0.75, 256, 9.302, 3.901, 5.738, 0.0518, 0.0000},
-    {17, 0, 0, 256, 99.039, 6.607, 0.000, 0.1497, 0.0000},
-    {17, 1, 0, 256, 235.908, 0.000, 0.000, 1.6983, 0.0000},
-    {17, 2, 0.25, 256, 104.334, 0.000, 3.960, 0.2632, 0.0000},
-    {17, 3, 1, 256, 218.246, 14.904, 0.000, 0.1962, 0.0000},
-    {17, 4, 0.75, 256, 234.144, 6.004, 0.000, 0.6884, 0.0000},
-    {17, 5, 1, 256, 68.173, 8.685, 0.000, 1.9127, 0.0000},
-    {20, 0, 0, 256, 58.360, 0.000, 3.513, 0.0000, 0.0000},
+    {13, 5, 0.25, 1024, 38.282, 12.294, 6.192, 0.0324, 0.0000},
+    {17, 0, 0, 256, 100.161, 0.681, 6.035, 0.0000, 0.0000},
+    {17, 1, 0, 256, 237.316, 0.000, 7.630, 0.0000, 0.0000},
+    {17, 2, 0, 256, 103.369, 0.000, 4.827, 0.0371, 0.0000},
+    {17, 3, 0, 256, 227.411, 0.000, 10.801, 0.0000, 0.0000},
+    {17, 4, 0, 256, 237.674, 2.833, 4.082, 0.0000, 0.0000},
+    {17, 5, 0, 256, 58.654, 0.000, 29.703, 0.9287, 0.0000},
+    {20, 0, 1, 512, 58.025, 0.261, 3.343, 0.1207, 0.0000},
     {20, 1, 0.25, 512, 92.985, 0.000, 2.441, 0.9360, 0.0000},
     {20, 2, 1, 512, 58.484, 0.412, 4.382, 0.1826, 0.0000},
     {20, 3, 0.5, 512, 90.270, 0.106, 8.587, 0.0740, 0.0000},
     {20, 4, 0.75, 768, 91.113, 0.549, 3.833, 0.7017, 0.0000},
-    {20, 5, 0.5, 512, 63.415, 3.964, 7.301, 0.0000, 0.0000},
+    {20, 5, 0.75, 512, 66.107, 0.000, 0.000, 0.0000, 0.0000},
     {26, 1, 1, 512, 12.688, 0.000, 3.411, 1.3181, 0.2810},
     {26, 4, 1, 256, 8.422, 0.000, 7.430, 1.5041, 0.1361},
     {27, 1, 0.25, 256, 24.060, 0.000, 6.895, 1.1480, 0.1870},
@@ -361,7 +354,7 @@ int64_t launch_blocks(const Tile &t, const Shape &s) {
 // (mode 2 uses the fast one); 1e300 where the variant has no entry for the
 // shape's family.
 double model_estimate(int mode, int variant, const Shape &s, int64_t blocks) {
-  const int fam = s.khw == 0 ? product_family(mode, s) : s.ffam;
+  const int fam = s.khw == 0 ? product_family(s) : s.ffam;
   auto scan = [&](const auto &table) {
     for (const ModelCost &c : table) {
       if (c.variant != variant || c.fam != fam) continue;
@@ -376,6 +369,12 @@ double model_estimate(int mode, int variant, const Shape &s, int64_t blocks) {
 }
 
 double estimate(const Tile &t, const Shape &s, int mode) {
+  // exact mode runs variants 2, 3 and 17 on the 64 x 128 tile (128 x 128
+  // with gathered taps; launch_kind): their launches have that tile's blocks
+  if (mode == OG_MODE_EXACT && (t.variant == 2 || t.variant == 3 || t.variant == 17)) {
+    const bool gathered = s.khw != 0 && s.ffam != 2;
+    return model_estimate(mode, t.variant, s, launch_blocks(tile_for_variant(gathered ? 3 : 4), s));
+  }
   return model_estimate(mode, t.variant, s, launch_blocks(t, s));
 }
 
@@ -389,6 +388,7 @@ const Tile &choose_tile(const Shape &s, int mode) {
     // the chain kernel runs windows other than 1x1 and 3x3 as variant 6
     if (is_chain(t) && s.khw != 0 && s.khw != 1 && s.khw != 9) continue;
     if (t.variant >= 14 && t.variant <= 16 && mode == OG_MODE_EXACT) continue;  // run as 10, 13, 11
+    if (t.variant == 9 && mode == OG_MODE_EXACT) continue;  // eight rows per lane: VALU-bound in exact mode
     const double e = estimate(t, s, mode);
     if (e < best_cost) {
       best_cost = e;
