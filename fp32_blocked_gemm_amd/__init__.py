@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
     L.og_set_variant.restype = ctypes.c_int
     L.og_get_variant.argtypes = []
     L.og_get_variant.restype = ctypes.c_int
+    L.og_gemm_choice.argtypes = [_i64, _i64, _i64, ctypes.c_int]
+    L.og_gemm_choice.restype = ctypes.c_int
     L.og_last_error.argtypes = []
     L.og_last_error.restype = ctypes.c_char_p
     L.og_version.argtypes = []
@@ -113,6 +115,14 @@ def get_variant() -> int:
 # ---------------------------------------------------------------------------
 # Raw entry points: device pointers and sizes, exactly the C ABI.
 # ---------------------------------------------------------------------------
+
+def gemm_choice(m: int, n: int, k: int, mode="fast") -> int:
+    """The variant og_gemm_f32's automatic choice runs for an m x n x k
+    product (n >= 2) in `mode` (og_gemm_choice)."""
+    v = lib().og_gemm_choice(m, n, k, _mode(mode))
+    _check(min(v, 0))
+    return v
+
 
 def set_stream(stream_handle: int | None):
     _check(lib().og_set_stream(stream_handle))

@@ -594,6 +594,25 @@ double panel_estimate(const Shape &s, int64_t images, int *variant) {
   return best;
 }
 
+// The automatic choice for a matrix product, in pieces og_gemm_f32 and
+// og_gemm_choice share: the shape, the panel kernel's estimate and variant,
+// the split-k variant of mode 2 (0: none), and whether the panel kernel
+// beats the tile pick t (fast mode, n > 1).
+Shape product_shape(int64_t m, int64_t n, int64_t k) {
+  return Shape{m, n, k, 1, 0, 0, 0, 4.0 * ((double)m * k + (double)k * n + (double)m * n)};
+}
+double product_panel_estimate(const Shape &sh, int *panel_v) {
+  *panel_v = 0;
+  return ceil_div(sh.M, 16) * ceil_div(sh.N, 64) <= kI32Max ? panel_estimate(sh, 0, panel_v) : 1e300;
+}
+int product_split(const Shape &sh, int mode, double panel_est) {
+  if (mode != OG_MODE_FAST_MFMA) return 0;
+  return mode2_variant(sh, std::min(estimate(choose_tile(sh, OG_MODE_FAST), sh, OG_MODE_FAST), panel_est));
+}
+bool product_takes_panel(const Shape &sh, const Tile &t, double panel_est) {
+  return panel_est < estimate(t, sh, OG_MODE_FAST);
+}
+
 // A split-k variant forced in exact or fast mode: refused (neither mode's
 // bits can come from it).
 og_status refuse_split(const char *what, int mode) {
@@ -631,15 +650,10 @@ og_status og_gemm_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_t l
     return fail(OG_ERR_TOO_LARGE, "og_gemm_f32: lda or ldb exceeds 2^22");
   og_status st = refuse_split("og_gemm_f32", mode);
   if (st != OG_OK) return st;
-  const Shape sh{m, n, k, 1, 0, 0, 0, 4.0 * ((double)m * k + (double)k * n + (double)m * n)};
-  // the panel kernel (fast mode): its variant of the lower estimate
+  const Shape sh = product_shape(m, n, k);
   int panel_v = 0;
-  const double panel_est =
-      ceil_div(m, 16) * ceil_div(n, 64) <= kI32Max ? panel_estimate(sh, 0, &panel_v) : 1e300;
-  const int split =
-      mode == OG_MODE_FAST_MFMA
-          ? mode2_variant(sh, std::min(estimate(choose_tile(sh, OG_MODE_FAST), sh, OG_MODE_FAST), panel_est))
-          : 0;
+  const double panel_est = product_panel_estimate(sh, &panel_v);
+  const int split = product_split(sh, mode, panel_est);
   if (mode == OG_MODE_FAST_MFMA && !split) mode = OG_MODE_FAST;  // the fast kernels meet the bound
   const Tile &t = pick(sh, mode);
   if (!split && !grid_fits(t, m, n, 1)) return fail(OG_ERR_TOO_LARGE, "og_gemm_f32: too many tiles");
@@ -667,9 +681,9 @@ og_status og_gemm_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_t l
   }
   // the panel kernel: forced, or chosen where its estimate is below the pick's
   if (panel_v != 0 && mode == OG_MODE_FAST && (n > 1 || is_panel(t_variant))) {
-    const int pv = is_panel(t_variant) ? t_variant
-                   : t_variant == 0 && panel_est < estimate(t, sh, mode) ? panel_v
-                                                                         : 0;
+    const int pv = is_panel(t_variant)                                      ? t_variant
+                   : t_variant == 0 && product_takes_panel(sh, t, panel_est) ? panel_v
+                                                                            : 0;
     if (pv != 0) {
       const bool bv = aligned16(B) && ldb % 4 == 0 && n % 4 == 0;
       launch_panel(pv, og::kBMatrix, bv, av, p, t_stream);
@@ -727,7 +741,7 @@ og_status og_gemm_nt_f32(int64_t m, int64_t n, int64_t k, const float *A, int64_
     return fail(OG_ERR_TOO_LARGE, "og_gemm_nt_f32: lda or ldb exceeds 2^22");
   og_status st = refuse_split("og_gemm_nt_f32", mode);
   if (st != OG_OK) return st;
-  const Shape sh{m, n, k, 1, 0, 0, 0, 4.0 * ((double)m * k + (double)k * n + (double)m * n)};
+  const Shape sh = product_shape(m, n, k);
   const int split =
       mode == OG_MODE_FAST_MFMA
           ? mode2_variant(sh, estimate(pick_nt(sh, OG_MODE_FAST), sh, OG_MODE_FAST))
@@ -1087,6 +1101,28 @@ og_status og_set_variant(int variant) {
 }
 
 int og_get_variant(void) { return t_variant; }
+
+int og_gemm_choice(int64_t m, int64_t n, int64_t k, int mode) {
+  if (!valid_mode(mode))
+    return fail(OG_ERR_INVALID_ARG, "og_gemm_choice: mode %d is not 0, 1 or 2", mode);
+  if (m < 1 || n < 2 || k < 1)
+    return fail(OG_ERR_INVALID_ARG, "og_gemm_choice: needs m >= 1, n >= 2, k >= 1 (m=%lld n=%lld k=%lld)",
+                (long long)m, (long long)n, (long long)k);
+  if (m > kI32Max || n > kI32Max || k > kI32Max)
+    return fail(OG_ERR_TOO_LARGE, "og_gemm_choice: a dimension exceeds 2^31-1");
+  const Shape sh = product_shape(m, n, k);
+  int panel_v = 0;
+  const double panel_est = product_panel_estimate(sh, &panel_v);
+  const int split = product_split(sh, mode, panel_est);
+  if (split) {
+    ok();
+    return split;
+  }
+  if (mode == OG_MODE_FAST_MFMA) mode = OG_MODE_FAST;
+  const Tile &t = choose_tile(sh, mode);
+  ok();
+  return panel_v != 0 && mode == OG_MODE_FAST && product_takes_panel(sh, t, panel_est) ? panel_v : t.variant;
+}
 
 const char *og_last_error(void) { return t_error.c_str(); }
 

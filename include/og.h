@@ -260,6 +260,23 @@ void *og_get_stream(void);
 og_status og_set_variant(int variant);
 int og_get_variant(void);
 
+/*
+ * The kernel variant (numbered as for og_set_variant) that og_gemm_f32
+ * runs under the automatic choice (variant 0) for an m x n x k product with
+ * n >= 2 in `mode`: a tile variant (2..17 or 20), a panel variant (29, 30;
+ * fast mode) or a split-k variant (21..25; OG_MODE_FAST_MFMA).  The choice
+ * depends on the shape and mode alone, never on the data or the device
+ * ("Matrix product and convolution kernels", section "Fixed chunks and
+ * thread independence"), so callers that report which kernel ran
+ * (benchmarks) and tests of the choice can ask for it; exact mode runs
+ * variants 2, 3 and 17 on the 64x128 tile (see og_set_variant).  Queues
+ * nothing and needs no device.  Returns OG_ERR_INVALID_ARG for a mode
+ * other than 0, 1 or 2 or for m < 1, n < 2 or k < 1 (a single column takes
+ * the row-dot or streamed-column form, which has no number), and
+ * OG_ERR_TOO_LARGE for a dimension above 2^31-1.
+ */
+int og_gemm_choice(int64_t m, int64_t n, int64_t k, int mode);
+
 /* Description of the calling thread's last error ("" after a success). */
 const char *og_last_error(void);
 

@@ -232,3 +232,38 @@ def test_split_variants_refused_in_exact_and_fast(L, variant):
             assert L.og_gemm_f32(4, 4, 4, P, 4, P, 4, P, 4, og.FAST_MFMA) == og.OG_ERR_DEVICE
     finally:
         L.og_set_variant(0)
+
+
+# The automatic choice for a product depends on the shape and mode alone, so
+# it is host logic: og_gemm_choice reports it without a device.
+def test_gemm_choice_of_the_4096_product(L):
+    # the 256 x 256 tile with eight waves: the kernel whose launch time and
+    # HBM counters the 4096^3 fast-mode measurement reports
+    assert og.gemm_choice(4096, 4096, 4096, "fast") == 17
+
+
+@pytest.mark.parametrize("m,n,k", [(512, 11008, 4096), (1, 4096, 4096), (8, 4096, 4096),
+                                   (1000, 777, 1531), (256, 256, 256), (64, 3136, 64),
+                                   (2048, 8192, 8192)])
+def test_gemm_choice_is_a_variant_of_its_mode(L, m, n, k):
+    tiles = set(range(2, 18)) | {20}
+    assert og.gemm_choice(m, n, k, "fast") in tiles | {29, 30}
+    assert og.gemm_choice(m, n, k, "exact") in tiles - {9, 14, 15, 16}
+    assert og.gemm_choice(m, n, k, "fast_mfma") in tiles | {21, 22, 23, 24, 25, 29, 30}
+
+
+def test_gemm_choice_mode2_splits_a_short_product(L):
+    # 256^3 is bound by its k chain: mode 2 splits k
+    assert og.gemm_choice(256, 256, 256, "fast_mfma") in (21, 22, 23, 24, 25)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((4, 4, 4, 7), og.OG_ERR_INVALID_ARG),
+    ((0, 4, 4, 0), og.OG_ERR_INVALID_ARG),
+    ((4, 1, 4, 1), og.OG_ERR_INVALID_ARG),
+    ((4, 4, 0, 1), og.OG_ERR_INVALID_ARG),
+    ((2 ** 31, 4, 4, 1), og.OG_ERR_TOO_LARGE),
+])
+def test_gemm_choice_rejects(L, args, status):
+    assert L.og_gemm_choice(*args) == status
+    assert L.og_last_error()
