@@ -14,7 +14,11 @@ and 10, MobileNetV3-large at batch 3 and 5, four more 3x3 convolutions and
 1 to 4096 rows against n = 1024 to 11008 columns and k = 1024 to 8192 -- the
 4096^3, prefill 512x11008x4096 and single-row 1x4096x4096 products and 33
 seeded ones in the first; 8x4096x4096, 2048x11008x4096 and 16 of another
-seed, with no size of the first, in the second.
+seed, with no size of the first, in the second.  "extra" (fitted too) and
+"extra_heldout" (both fitted too) and "extra_heldout2": 1-D convolutions
+(H = 1, windows 1x3, 1x5 and 1x7) and products whose rows are not 16-byte
+aligned (odd k, row strides + 13), ten of each per set from three seeds,
+none of the sizes the benchmark times.
 
     python3 -m fp32_blocked_gemm_amd.choice_sweep [--set fit|heldout|large|large_heldout] [--mode fast|exact]
         [--only3x3] [--variants 26,27,28] [--out FILE] [--quick]
@@ -48,10 +52,30 @@ def large_products(which):
     return [p for p in held if p[:3] not in {q[:3] for q in fit}][:18]
 
 
+def extra_shapes(which, synth):
+    """1-D convolutions and unaligned products of the "extra" or
+    "extra_heldout" set (none of the benchmark's own sizes)."""
+    rng = random.Random({"extra": 51, "extra_heldout": 53}.get(which, 57))
+    convs, prods = [], []
+    while len(convs) < 10:
+        n, c, co = rng.choice([1, 2, 4, 8]), rng.choice([64, 128, 256, 384, 512]), rng.choice([64, 128, 256, 512])
+        w, kw = rng.choice([512, 1024, 2048, 3000, 8192]), rng.choice([3, 5, 7])
+        if (n, c, w, co, kw) == (8, 512, 4096, 512, 5) or n * c * w * co * kw > 2 ** 34:
+            continue
+        convs.append(synth.ConvShape(f"c1d_{n}_{c}_{w}_{co}_{kw}", n, c, 1, w, co, 1, kw, (1, 1),
+                                     (0, kw // 2, 0, kw // 2)))
+    while len(prods) < 10:
+        m, n, k = rng.choice([100, 333, 700, 1000, 1500, 2500]), rng.choice([250, 777, 1200, 2000]), \
+            rng.choice([301, 777, 1531, 2047, 3001])
+        if (m, n, k) != (1000, 777, 1531):
+            prods.append((m, n, k, 13))
+    return convs, prods
+
+
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--out", default=None, help="also write the lines to this file")
-    ap.add_argument("--set", default="heldout", choices=("fit", "heldout", "large", "large_heldout"))
+    ap.add_argument("--set", default="heldout", choices=("fit", "heldout", "large", "large_heldout", "extra", "extra_heldout", "extra_heldout2"))
     ap.add_argument("--quick", action="store_true", help="the first ResNet-50 batch only, 6 products")
     ap.add_argument("--mode", default="fast", choices=("fast", "exact"))
     ap.add_argument("--only3x3", action="store_true", help="3x3 convolutions only")
@@ -145,7 +169,10 @@ def main() -> None:
         emit(e)
 
     products = []
-    if args.set in ("large", "large_heldout"):
+    if args.set.startswith("extra"):
+        resnet_b, mobile_b, seeds = (), (), ()
+        other, products = extra_shapes(args.set, synth)
+    elif args.set in ("large", "large_heldout"):
         resnet_b, mobile_b, other, seeds = (), (), (), ()
         products = large_products(args.set)
     elif args.set == "fit":
@@ -185,7 +212,7 @@ def main() -> None:
                 seen.add(key)
                 run_conv(s, f"mobilenetv3_b{b}")
     for s in other:
-        run_conv(s, "other3x3")
+        run_conv(s, "conv1d" if args.set.startswith("extra") else "other3x3")
     for m, n, k, ld in products:
         run_gemm(m, n, k, ld, args.set + "_products")
     for seed, nprod in seeds:

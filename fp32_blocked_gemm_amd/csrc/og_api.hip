@@ -87,9 +87,11 @@ struct Shape {
 
 // Family of a convolution in the launch model: 1 a 3x3 window at stride 1,
 // 4 a strided 3x3 window, 2 a 1x1 window read in place (stride 1, no
-// padding), 3 any other window or a strided or padded 1x1 (gathered taps).
+// padding), 6 a 1 x k window (k > 1: the 1-D convolutions), 3 any other
+// window or a strided or padded 1x1 (gathered taps).
 int fast_family(int64_t KH, int64_t KW, bool planes, int64_t strideH, int64_t strideW) {
   if (KH == 3 && KW == 3) return strideH == 1 && strideW == 1 ? 1 : 4;
+  if (KH == 1 && KW > 1) return 6;
   return planes ? 2 : 3;
 }
 // Family of a matrix product: 5 from 2^32 multiply-adds up (sizes where the
@@ -105,14 +107,15 @@ int product_family(const Shape &s) {
 // each counted once, X (halo kernel only) the thousands of input floats a
 // block stages over its k; (q, cap, c, d, o, b, e) per variant and family
 // (fast_family, product_family), cap a multiple of 256 blocks (one or more
-// per compute unit), fitted by least squares on the relative error to 437
+// per compute unit), fitted by least squares on the relative error to 457
 // shapes, each launched on every variant on the MI355X (ResNet-50's
 // convolutions at batch 1, 2, 3, 4, 5, 6, 8, 12 and 16, MobileNetV3-large's
 // ungrouped ones at batch 1, 2, 4, 6 and 8, twelve 3x3 convolutions of other
-// widths, 72 seeded random matrix products up to 2048 x 2900 x 2300, and 36
-// products of a language model's sizes: 4096^3, 512 x 11008 x 4096,
+// widths, 72 seeded random matrix products up to 2048 x 2900 x 2300, 36
+// products of a language model's sizes (4096^3, 512 x 11008 x 4096,
 // 1 x 4096 x 4096 and 33 seeded ones of m = 1..4096, n = 1024..11008,
-// k = 1024..8192): mean error 4.1 % (exact 3.8 %).  Variants 26..28 and
+// k = 1024..8192) and 20 seeded 1-D convolutions): mean error 4.2 %
+// (exact 3.8 %).  Variants 26..28 and
 // 31..33 are the halo kernel, 29 and 30 the panel kernel.
 struct ModelCost {
   int variant, fam;
@@ -125,48 +128,56 @@ constexpr ModelCost kFastCosts[] = {
     {2, 3, 0.75, 256, 191.331, 4.963, 9.518, 0.0000, 0.0000},
     {2, 4, 1, 256, 198.851, 0.829, 9.278, 0.0386, 0.0000},
     {2, 5, 0.75, 256, 128.304, 2.595, 17.525, 0.0000, 0.0000},
+    {2, 6, 0.75, 256, 201.719, 0.000, 9.362, 0.0000, 0.0000},
     {3, 0, 0, 256, 70.055, 5.914, 0.000, 0.0390, 0.0000},
     {3, 1, 0.5, 256, 106.661, 1.239, 5.154, 0.0499, 0.0000},
     {3, 2, 0.75, 256, 74.927, 0.448, 5.102, 0.0654, 0.0000},
     {3, 3, 0.75, 256, 103.345, 0.178, 8.299, 0.0000, 0.0000},
     {3, 4, 0.25, 256, 106.345, 2.227, 3.966, 0.0247, 0.0000},
     {3, 5, 0.75, 256, 67.837, 0.000, 11.640, 0.0000, 0.0000},
+    {3, 6, 0, 256, 102.707, 0.000, 7.815, 0.0000, 0.0000},
     {4, 0, 0.5, 256, 39.546, 2.475, 1.766, 0.0000, 0.0000},
     {4, 1, 0.5, 256, 76.180, 0.000, 5.792, 0.0000, 0.0000},
     {4, 2, 0.5, 256, 44.865, 0.483, 3.795, 0.0623, 0.0000},
     {4, 3, 0.5, 256, 72.451, 0.000, 7.765, 0.0000, 0.0000},
     {4, 4, 0.75, 256, 76.090, 0.714, 4.108, 0.0483, 0.0000},
     {4, 5, 0.5, 256, 34.477, 0.000, 12.049, 0.1135, 0.0000},
+    {4, 6, 0.5, 256, 66.137, 0.000, 10.942, 0.0000, 0.0000},
     {5, 0, 0.25, 256, 45.745, 2.829, 1.379, 0.0000, 0.0000},
     {5, 1, 0.5, 256, 117.752, 0.000, 5.240, 0.0000, 0.0000},
     {5, 2, 0.5, 256, 54.768, 0.387, 3.801, 0.0375, 0.0000},
     {5, 3, 0.5, 256, 107.044, 0.000, 8.889, 0.0000, 0.0000},
     {5, 4, 0.75, 256, 116.785, 1.327, 4.345, 0.0067, 0.0000},
     {5, 5, 0.5, 256, 36.621, 0.000, 10.466, 0.1963, 0.0000},
+    {5, 6, 1, 512, 123.158, 0.000, 0.000, 0.5882, 0.0000},
     {6, 0, 0.75, 768, 15.713, 0.884, 1.995, 0.0458, 0.0000},
     {6, 1, 0.75, 768, 16.692, 0.000, 1.079, 0.0000, 0.0000},
     {6, 2, 0.5, 768, 14.497, 0.741, 2.710, 0.1789, 0.0000},
     {6, 3, 0.25, 768, 20.135, 4.491, 2.202, 0.0000, 0.0000},
     {6, 4, 0.5, 512, 17.816, 0.000, 3.089, 0.5236, 0.0000},
     {6, 5, 0.25, 1536, 31.162, 0.200, 0.309, 0.1142, 0.0000},
+    {6, 6, 0, 512, 26.780, 0.000, 7.047, 2.3461, 0.0000},
     {7, 0, 0.75, 768, 18.099, 0.981, 1.964, 0.0518, 0.0000},
     {7, 1, 0.5, 768, 19.233, 0.000, 3.427, 0.0000, 0.0000},
     {7, 2, 0.5, 768, 17.275, 0.730, 2.542, 0.1325, 0.0000},
     {7, 3, 0.5, 512, 15.281, 2.631, 5.843, 0.0000, 0.0000},
     {7, 4, 0.75, 512, 20.614, 0.000, 3.038, 0.2773, 0.0000},
     {7, 5, 0.25, 768, 18.305, 0.000, 2.165, 0.1467, 0.0000},
+    {7, 6, 0, 512, 29.051, 0.000, 7.635, 0.9218, 0.0000},
     {8, 0, 0.5, 512, 22.278, 0.478, 2.801, 0.0205, 0.0000},
     {8, 1, 0.25, 512, 23.173, 0.000, 4.585, 0.0000, 0.0000},
     {8, 2, 0.75, 768, 23.794, 0.559, 2.533, 0.1622, 0.0000},
     {8, 3, 0.75, 512, 20.253, 2.175, 5.834, 0.0000, 0.0000},
     {8, 4, 0.5, 512, 26.950, 0.000, 3.092, 0.1817, 0.0000},
     {8, 5, 0.25, 768, 27.693, 0.000, 3.876, 0.0769, 0.0000},
+    {8, 6, 0, 512, 33.282, 0.000, 6.818, 0.3850, 0.0000},
     {9, 0, 1, 512, 31.443, 0.555, 3.053, 0.1385, 0.0000},
     {9, 1, 0, 2048, 29.070, 0.000, 0.000, 2.2430, 0.0000},
     {9, 2, 0.25, 512, 32.850, 0.000, 3.493, 0.1880, 0.0000},
     {9, 3, 0.5, 512, 32.239, 2.823, 4.915, 0.0000, 0.0000},
     {9, 4, 1, 512, 33.842, 0.000, 3.167, 0.3262, 0.0000},
     {9, 5, 0.25, 768, 46.021, 1.159, 16.829, 0.0000, 0.0000},
+    {9, 6, 0.75, 768, 52.487, 0.000, 0.000, 0.5941, 0.0000},
     {10, 0, 1, 256, 6.029, 3.464, 1.564, 0.0388, 0.0000},
     {10, 1, 1, 256, 4.901, 3.893, 1.728, 0.0000, 0.0000},
     {10, 2, 1, 256, 5.242, 3.517, 1.783, 0.0000, 0.0000},
@@ -215,12 +226,14 @@ constexpr ModelCost kFastCosts[] = {
     {17, 3, 1, 256, 282.211, 15.870, 0.221, 0.0000, 0.0000},
     {17, 4, 1, 256, 289.389, 8.416, 1.934, 0.0936, 0.0000},
     {17, 5, 1, 256, 235.543, 2.906, 3.549, 0.1560, 0.0000},
+    {17, 6, 0, 256, 290.399, 10.880, 0.000, 0.0609, 0.0000},
     {20, 0, 0.5, 256, 27.886, 0.000, 3.846, 0.0000, 0.0000},
     {20, 1, 0.25, 256, 45.603, 0.000, 5.908, 0.0000, 0.0000},
     {20, 2, 0.25, 256, 28.724, 0.412, 4.546, 0.0276, 0.0000},
     {20, 3, 0.5, 256, 36.809, 0.000, 8.740, 0.0000, 0.0000},
     {20, 4, 0.25, 256, 46.385, 0.497, 4.725, 0.0000, 0.0000},
     {20, 5, 0, 256, 18.735, 0.000, 19.760, 0.1959, 0.0000},
+    {20, 6, 0.5, 512, 45.669, 0.000, 6.827, 0.4091, 0.0000},
     {26, 1, 1, 256, 3.851, 0.000, 5.334, 0.9905, 0.0996},
     {26, 4, 1, 256, 4.864, 2.845, 3.406, 0.3862, 0.0789},
     {27, 1, 0.5, 256, 6.921, 1.587, 3.198, 0.4847, 0.1870},
@@ -255,42 +268,49 @@ constexpr ModelCost kExactCosts[] = {
     {2, 3, 0, 256, 227.415, 0.000, 10.788, 0.0000, 0.0000},
     {2, 4, 0, 256, 237.609, 2.834, 4.086, 0.0000, 0.0000},
     {2, 5, 0, 256, 58.375, 0.000, 30.472, 0.9348, 0.0000},
+    {2, 6, 0.75, 512, 239.827, 0.000, 2.032, 0.5130, 0.0000},
     {3, 0, 0, 256, 100.177, 0.624, 6.090, 0.0000, 0.0000},
     {3, 1, 0, 256, 237.329, 0.000, 7.556, 0.0000, 0.0000},
     {3, 2, 0, 256, 103.364, 0.000, 4.839, 0.0350, 0.0000},
     {3, 3, 0, 256, 227.422, 0.000, 10.802, 0.0000, 0.0000},
     {3, 4, 0, 256, 237.574, 2.833, 4.089, 0.0000, 0.0000},
     {3, 5, 0, 256, 58.559, 0.000, 29.973, 0.9301, 0.0000},
+    {3, 6, 0.5, 512, 239.132, 0.000, 2.159, 0.5582, 0.0000},
     {4, 0, 0, 256, 100.175, 0.598, 6.125, 0.0000, 0.0000},
     {4, 1, 0, 256, 151.018, 0.000, 6.039, 0.0000, 0.0000},
     {4, 2, 0, 256, 103.386, 0.000, 4.837, 0.0349, 0.0000},
     {4, 3, 0.5, 512, 141.624, 2.887, 5.247, 0.3364, 0.0000},
     {4, 4, 0, 256, 151.080, 0.736, 4.422, 0.0532, 0.0000},
     {4, 5, 0, 256, 58.658, 0.000, 29.888, 0.9283, 0.0000},
+    {4, 6, 1, 512, 156.699, 0.000, 1.624, 0.3594, 0.0000},
     {5, 0, 0, 256, 108.137, 0.000, 6.790, 0.0000, 0.0000},
     {5, 1, 0, 512, 216.461, 0.000, 1.328, 0.8328, 0.0000},
     {5, 2, 1, 512, 118.186, 0.028, 4.241, 0.1464, 0.0000},
     {5, 3, 0.25, 512, 203.916, 0.489, 10.213, 0.2272, 0.0000},
     {5, 4, 0.5, 256, 215.736, 0.000, 6.273, 0.0000, 0.0000},
     {5, 5, 0, 256, 63.828, 0.000, 0.000, 1.1038, 0.0000},
+    {5, 6, 0.5, 768, 217.771, 0.441, 1.019, 0.5805, 0.0000},
     {6, 0, 0.75, 768, 16.419, 0.645, 2.214, 0.0419, 0.0000},
     {6, 1, 0.25, 768, 19.610, 0.000, 4.462, 0.0000, 0.0000},
     {6, 2, 0.5, 768, 14.674, 0.586, 2.825, 0.1742, 0.0000},
     {6, 3, 0.5, 768, 20.707, 4.075, 1.083, 0.0000, 0.0000},
     {6, 4, 0.5, 512, 18.571, 0.000, 2.904, 0.6610, 0.0000},
     {6, 5, 0.25, 1536, 32.813, 0.003, 0.000, 0.1111, 0.0000},
+    {6, 6, 0, 512, 26.770, 0.021, 8.432, 2.1005, 0.0000},
     {7, 0, 0.75, 768, 20.607, 0.714, 2.117, 0.0372, 0.0000},
     {7, 1, 0.5, 768, 22.475, 0.000, 4.213, 0.0000, 0.0000},
     {7, 2, 0.5, 768, 20.429, 0.557, 2.781, 0.1081, 0.0000},
     {7, 3, 0.25, 512, 15.714, 2.626, 6.937, 0.0000, 0.0000},
     {7, 4, 0.25, 512, 23.841, 0.000, 3.332, 0.2151, 0.0000},
     {7, 5, 0.5, 768, 22.349, 0.000, 0.000, 0.0533, 0.0000},
+    {7, 6, 0, 512, 32.147, 0.232, 8.262, 0.6587, 0.0000},
     {8, 0, 0.5, 512, 31.006, 0.120, 3.090, 0.0111, 0.0000},
     {8, 1, 0.5, 512, 31.168, 0.000, 5.015, 0.0000, 0.0000},
     {8, 2, 0.75, 768, 32.286, 0.373, 2.846, 0.1809, 0.0000},
     {8, 3, 0.5, 768, 31.659, 6.956, 0.922, 0.0000, 0.0000},
     {8, 4, 0.5, 512, 34.199, 0.000, 3.295, 0.1827, 0.0000},
     {8, 5, 0.25, 768, 38.080, 0.000, 1.375, 0.1186, 0.0000},
+    {8, 6, 1, 512, 49.443, 0.000, 0.000, 1.4596, 0.0000},
     {10, 0, 1, 256, 7.301, 3.324, 1.656, 0.0150, 0.0000},
     {10, 1, 1, 256, 5.908, 3.806, 1.812, 0.0693, 0.0000},
     {10, 2, 1, 256, 6.559, 3.584, 1.781, 0.0000, 0.0000},
@@ -321,12 +341,14 @@ constexpr ModelCost kExactCosts[] = {
     {17, 3, 0, 256, 227.411, 0.000, 10.801, 0.0000, 0.0000},
     {17, 4, 0, 256, 237.674, 2.833, 4.082, 0.0000, 0.0000},
     {17, 5, 0, 256, 58.654, 0.000, 29.703, 0.9287, 0.0000},
+    {17, 6, 0.5, 512, 238.988, 0.000, 2.174, 0.5598, 0.0000},
     {20, 0, 1, 512, 58.025, 0.261, 3.343, 0.1207, 0.0000},
     {20, 1, 0.25, 512, 92.985, 0.000, 2.441, 0.9360, 0.0000},
     {20, 2, 1, 512, 58.484, 0.412, 4.382, 0.1826, 0.0000},
     {20, 3, 0.5, 512, 90.270, 0.106, 8.587, 0.0740, 0.0000},
     {20, 4, 0.75, 768, 91.113, 0.549, 3.833, 0.7017, 0.0000},
     {20, 5, 0.75, 512, 66.107, 0.000, 0.000, 0.0000, 0.0000},
+    {20, 6, 0.75, 768, 95.802, 0.000, 4.013, 0.5598, 0.0000},
     {26, 1, 1, 512, 12.688, 0.000, 3.411, 1.3181, 0.2810},
     {26, 4, 1, 256, 8.422, 0.000, 7.430, 1.5041, 0.1361},
     {27, 1, 0.25, 256, 24.060, 0.000, 6.895, 1.1480, 0.1870},
