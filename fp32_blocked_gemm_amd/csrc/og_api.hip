@@ -108,7 +108,8 @@ int product_family(const Shape &s) {
 // block stages over its k; (q, cap, c, d, o, b, e) per variant and family
 // (fast_family, product_family), cap a multiple of 256 blocks (one or more
 // per compute unit), fitted by least squares on the relative error to 457
-// shapes, each launched on every variant on the MI355X (ResNet-50's
+// shapes (477 in exact mode), each launched on every variant on the MI355X
+// (ResNet-50's
 // convolutions at batch 1, 2, 3, 4, 5, 6, 8, 12 and 16, MobileNetV3-large's
 // ungrouped ones at batch 1, 2, 4, 6 and 8, twelve 3x3 convolutions of other
 // widths, 72 seeded random matrix products up to 2048 x 2900 x 2300, 36
