@@ -577,11 +577,12 @@ __global__ void __launch_bounds__(64 * WM * WN) mfma_kernel(Problem p) {
       [&](auto slot, auto buf, int c) __attribute__((always_inline)) {
         // fast mode: the A tile's taps past K are -0 (B's are +0).  Only the
         // chunk that runs past K has such taps: a uniform test skips the sign
-        // fix elsewhere, except on the 256 x 256 tile, whose branch-free form
-        // measured faster (4096^3: 0.986 ms against 0.999 with the test,
-        // while the test made the 64 x 128 tile's 512 x 11008 x 4096 launch
-        // 416 -> 408 us)
-        constexpr bool kSignTest = !(BM == 256 && BN == 256);
+        // fix elsewhere, except where a wave holds 2 x 2 blocks (the 128 x 256
+        // and 256 x 256 tiles), whose branch-free form measured faster
+        // (4096^3 on 256 x 256: 0.986 ms against 0.999 with the test;
+        // 2048 x 11008 x 4096 on 128 x 256: 1.54 against 1.99 ms), while the
+        // test made the 64 x 128 tile's 512 x 11008 x 4096 launch 416 -> 408 us
+        constexpr bool kSignTest = TM * TN < 4;
         if (MODE == kFast && (!kSignTest || (c + 1) * BK > p.K))
           as.template store_signed<LDA>(As[decltype(buf)::value], ra[decltype(slot)::value], c * BK,
                                         p.K);
